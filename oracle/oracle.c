@@ -1,0 +1,269 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct fp64 CPU reference for rotary
+ * position embedding (RoPE) and for softmax attention over rotated queries
+ * and keys.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load or call this file.  It shares no
+ * code, header, table or constant with the HIP library, and the HIP library
+ * never calls it.
+ *
+ * Sources (cited by page title and section):
+ *   [RF] "RoPE and FlashAttention: relative positions and online softmax"
+ *        section 1 (RoPE from a relative-position requirement: pair rotation,
+ *        frequency schedule, Q and K rotated but never V), section 2
+ *        (offset-aware RoPE: absolute positions, fp64 angle construction),
+ *        section 4 (naive attention S = QK^T/sqrt(d), P = softmax(S), O = PV),
+ *        section 5 (masked rows; a row with no valid key is rejected).
+ *   [TR] "Write Triton Rope Kernel", sections "Inputs the agent should gather
+ *        first" (GPT-NeoX half-split vs GPT-J adjacent-pair layout, partial
+ *        RoPE on the first rot_dim dims, per-token positions) and
+ *        "Required reasoning process" steps 1, 6 and 8 (the rotation formulas
+ *        and their sign convention).
+ *
+ * Readings where the pages are silent or disagree (each stated once here):
+ *   - Frequency denominator under partial RoPE is rot_dim, not head_dim:
+ *     theta_i = base^(-2 i / rot_dim), i in [0, rot_dim/2).
+ *   - Half-split partial RoPE pairs (i, i + rot_dim/2) for i < rot_dim/2; the
+ *     dims [rot_dim, head_dim) are copied unchanged.
+ *   - Angles and trig are carried in fp64 here; no rounding to the input type.
+ *   - Softmax scale defaults to 1/sqrt(head_dim) (head_dim, not rot_dim).
+ *   - Offset mask: query i sits at q_off + i, key j at k_off + j; with causal
+ *     set, key j is visible to query i iff k_off + j <= q_off + i.
+ *
+ * Build: gcc -O2 -std=c99 -fopenmp -ffp-contract=off -shared -fPIC -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_NEOX = 0, OR_GPTJ = 1 };
+enum { OR_OK = 0, OR_ERR_ARG = 1, OR_ERR_EMPTY_ROW = 2, OR_ERR_NOMEM = 3 };
+
+/* theta_i = base^(-2i/rot_dim): one frequency per rotated pair; the first
+ * frequency is 1 for every base.  [RF] section 1; [TR] "Correctness
+ * requirements" (table build). */
+static double pair_frequency(double base, int i, int rot_dim)
+{
+    return pow(base, -2.0 * (double)i / (double)rot_dim);
+}
+
+/* The two coordinates that form pair i.  GPT-J rotates adjacent pairs
+ * (2i, 2i+1); GPT-NeoX rotates the halves (i, i + rot_dim/2).  [TR] "Inputs
+ * the agent should gather first", item 1; [RF] section 1. */
+static void pair_slots(int layout, int i, int rot_dim, int *a, int *b)
+{
+    if (layout == OR_GPTJ) {
+        *a = 2 * i;
+        *b = 2 * i + 1;
+    } else {
+        *a = i;
+        *b = i + rot_dim / 2;
+    }
+}
+
+/* Rotate one row of head_dim values sitting at absolute position pos.
+ * Each pair (xa, xb) becomes (xa cos - xb sin, xa sin + xb cos) with angle
+ * pos * theta_i.  Dims at or past rot_dim pass through.  [TR] "Required
+ * reasoning process" steps 1 and 6; [RF] section 1. */
+static void rotate_row(const double *x, double *y, int head_dim, int rot_dim,
+                       double pos, double base, int layout)
+{
+    for (int d = rot_dim; d < head_dim; ++d)
+        y[d] = x[d];
+    for (int i = 0; i < rot_dim / 2; ++i) {
+        double ang = pos * pair_frequency(base, i, rot_dim);
+        double c = cos(ang), s = sin(ang);
+        int a, b;
+        pair_slots(layout, i, rot_dim, &a, &b);
+        double xa = x[a], xb = x[b];
+        y[a] = xa * c - xb * s;
+        y[b] = xa * s + xb * c;
+    }
+}
+
+static int rope_args_ok(int head_dim, int rot_dim, double base, int layout)
+{
+    if (head_dim <= 0 || head_dim % 2 != 0) return 0;
+    if (rot_dim < 0 || rot_dim % 2 != 0 || rot_dim > head_dim) return 0;
+    if (!(base > 0.0)) return 0;
+    if (layout != OR_NEOX && layout != OR_GPTJ) return 0;
+    return 1;
+}
+
+/* Rotate n_rows rows of x ([n_rows, head_dim], contiguous) at the given
+ * per-row positions.  rot_dim == 0 copies.  Per-token positions come from the
+ * caller, never from the row index: [TR] "Required reasoning process" step 3. */
+int oracle_rope(const double *x, double *y, int64_t n_rows, int head_dim,
+                int rot_dim, const double *positions, double base, int layout)
+{
+    if (!rope_args_ok(head_dim, rot_dim, base, layout) || n_rows < 0) return OR_ERR_ARG;
+    if (n_rows > 0 && (!x || !y || !positions)) return OR_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r)
+        rotate_row(x + r * head_dim, y + r * head_dim, head_dim, rot_dim,
+                   positions[r], base, layout);
+    return OR_OK;
+}
+
+/* The exact trig a cos/sin table approximates: cos_out[p][i] = cos(p theta_i),
+ * sin_out[p][i] = sin(p theta_i), rows of rot_dim/2 values.  [RF] section 2
+ * (angles formed in fp64); [TR] "Correctness requirements" (table build). */
+int oracle_trig(double base, int rot_dim, int64_t n_pos, double *cos_out, double *sin_out)
+{
+    if (rot_dim <= 0 || rot_dim % 2 != 0 || !(base > 0.0) || n_pos < 0) return OR_ERR_ARG;
+    if (n_pos > 0 && (!cos_out || !sin_out)) return OR_ERR_ARG;
+    const int half = rot_dim / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < n_pos; ++p)
+        for (int i = 0; i < half; ++i) {
+            double ang = (double)p * pair_frequency(base, i, rot_dim);
+            cos_out[p * half + i] = cos(ang);
+            sin_out[p * half + i] = sin(ang);
+        }
+    return OR_OK;
+}
+
+/* Number of keys query i may attend to.  Keys sit at contiguous positions, so
+ * the visible set is a prefix [0, n) of the key rows. */
+static int64_t visible_keys(int64_t i, int64_t Sk, int64_t q_off, int64_t k_off, int causal)
+{
+    if (!causal) return Sk;
+    int64_t last = q_off + i - k_off;    /* largest visible key index */
+    if (last < 0) return 0;
+    return last + 1 < Sk ? last + 1 : Sk;
+}
+
+/* One output row of naive attention over n visible keys:
+ * s_j = scale * (qr . kr_j), p = softmax(s), out = sum_j p_j v_j.
+ * [RF] section 4 (S = QK^T/sqrt(d), P = softmax(S), O = PV). */
+static void attend_row(const double *qr, const double *kr, const double *v,
+                       int64_t n, int D, int Dv, double scale, double *scores,
+                       double *out)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        double s = 0.0;
+        for (int d = 0; d < D; ++d) s += qr[d] * kr[j * D + d];
+        s *= scale;
+        scores[j] = s;
+        if (s > m) m = s;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        scores[j] = exp(scores[j] - m);
+        l += scores[j];
+    }
+    for (int e = 0; e < Dv; ++e) out[e] = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        for (int e = 0; e < Dv; ++e) out[e] += scores[j] * v[j * Dv + e];
+    for (int e = 0; e < Dv; ++e) out[e] /= l;
+}
+
+static int attn_args_ok(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int D, int Dv,
+                        int rot_dim, double base, int layout)
+{
+    if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || Dv <= 0) return 0;
+    if (rot_dim == 0) return D > 0 && D % 2 == 0;
+    return rope_args_ok(D, rot_dim, base, layout);
+}
+
+/* Full attention forward.  q [B,H,Sq,D], k [B,H,Sk,D], v [B,H,Sk,Dv],
+ * o [B,H,Sq,Dv], all contiguous fp64.  Query i has position q_off + i and key
+ * j position k_off + j; Q and K are rotated at those positions (rot_dim == 0:
+ * no rotation), V is never rotated ([RF] section 1).  scale <= 0 selects
+ * 1/sqrt(D).  A query with no visible key is rejected ([RF] section 5). */
+int oracle_attention(const double *q, const double *k, const double *v, double *o,
+                     int64_t B, int64_t H, int64_t Sq, int64_t Sk, int D, int Dv,
+                     int64_t q_off, int64_t k_off, int rot_dim, double base,
+                     int layout, int causal, double scale)
+{
+    if (!attn_args_ok(B, H, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!q || !k || !v || !o) return OR_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int64_t i = 0; i < Sq; ++i)
+        if (visible_keys(i, Sk, q_off, k_off, causal) == 0) return OR_ERR_EMPTY_ROW;
+
+    const int64_t nq = B * H * Sq, nk = B * H * Sk;
+    double *qr = malloc(sizeof(double) * (size_t)(nq * D));
+    double *kr = malloc(sizeof(double) * (size_t)(nk * D));
+    if (!qr || !kr) { free(qr); free(kr); return OR_ERR_NOMEM; }
+
+    /* Rotate every Q and K row once, at its absolute position. */
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nq; ++r)
+        rotate_row(q + r * D, qr + r * D, D, rot_dim, (double)(q_off + r % Sq), base, layout);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nk; ++r)
+        rotate_row(k + r * D, kr + r * D, D, rot_dim, (double)(k_off + r % Sk), base, layout);
+
+    int status = OR_OK;
+#pragma omp parallel
+    {
+        double *scores = malloc(sizeof(double) * (size_t)Sk);
+        if (!scores) {
+#pragma omp atomic write
+            status = OR_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nq; ++r) {
+                int64_t bh = r / Sq, i = r % Sq;
+                int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
+                attend_row(qr + r * D, kr + bh * Sk * D, v + bh * Sk * Dv, n, D, Dv,
+                           scale, scores, o + r * Dv);
+            }
+            free(scores);
+        }
+    }
+    free(qr);
+    free(kr);
+    return status;
+}
+
+/* Selected rows of the same forward, for spot checks at sizes the full
+ * oracle cannot finish quickly.  rows holds n_rows (b, h, i) triples; row r of
+ * o_rows ([n_rows, Dv]) receives output row (b, h, i).  Each selected row
+ * rotates its own query and visible keys. */
+int oracle_attention_rows(const double *q, const double *k, const double *v,
+                          int64_t B, int64_t H, int64_t Sq, int64_t Sk, int D, int Dv,
+                          int64_t q_off, int64_t k_off, int rot_dim, double base,
+                          int layout, int causal, double scale,
+                          const int64_t *rows, int64_t n_rows, double *o_rows)
+{
+    if (!attn_args_ok(B, H, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!q || !k || !v || (n_rows > 0 && (!rows || !o_rows)) || n_rows < 0) return OR_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Sq) return OR_ERR_ARG;
+        if (visible_keys(i, Sk, q_off, k_off, causal) == 0) return OR_ERR_EMPTY_ROW;
+    }
+    int status = OR_OK;
+#pragma omp parallel
+    {
+        double *qr = malloc(sizeof(double) * (size_t)D);
+        double *kr = malloc(sizeof(double) * (size_t)(Sk * D));
+        double *scores = malloc(sizeof(double) * (size_t)Sk);
+        if (!qr || !kr || !scores) {
+#pragma omp atomic write
+            status = OR_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+                int64_t bh = b * H + h;
+                int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
+                rotate_row(q + (bh * Sq + i) * D, qr, D, rot_dim, (double)(q_off + i), base, layout);
+                for (int64_t j = 0; j < n; ++j)
+                    rotate_row(k + (bh * Sk + j) * D, kr + j * D, D, rot_dim,
+                               (double)(k_off + j), base, layout);
+                attend_row(qr, kr, v + bh * Sk * Dv, n, D, Dv, scale, scores, o_rows + r * Dv);
+            }
+        }
+        free(qr);
+        free(kr);
+        free(scores);
+    }
+    return status;
+}

@@ -1,0 +1,186 @@
+"""Seeded synthetic inputs for the fused attention and the standalone RoPE op.
+
+This module holds none of the method's arithmetic: it only draws random
+numbers, rounds them to the storage type and describes the workload shapes.
+Both the GPU path (through the tests and the benchmark) and the fp64 oracle
+consume what it produces.
+
+Recipe (the pages fix shapes but neither a generator nor seeds):
+  * ``numpy.random.default_rng(seed)`` (PCG64), drawing ``standard_normal`` in
+    fp64 in the order q, k, v at full shape, as the worked tests of "RoPE and
+    FlashAttention: relative positions and online softmax" (section 5) do with
+    ``default_rng``.
+  * Values are rounded fp64 -> fp32 (round to nearest even), then fp32 -> bf16
+    (round to nearest even) for bf16 workloads.
+  * The ragged continuous-batching workload ("Write Triton Rope Kernel",
+    "Inputs the agent should gather first", item 6) draws, in this order:
+    request lengths from distinct cut points, per-token positions iid uniform
+    over the table, then Q, then K.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# storage-type rounding (round to nearest even), no method arithmetic
+
+
+def bf16_bits(x) -> np.ndarray:
+    """uint16 bit patterns of ``x`` rounded fp32 -> bf16 to nearest even."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """Exact fp32 values of uint16 bf16 bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    """fp32 array holding ``x`` rounded to ``dtype`` ('f32' or 'bf16')."""
+    f = np.asarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return np.ascontiguousarray(f)
+    if dtype == "bf16":
+        return bf16_to_f32(bf16_bits(f))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# workload descriptions
+
+
+@dataclass(frozen=True)
+class AttentionWorkload:
+    """One fused RoPE + attention forward: q [B,H,Sq,D], k/v [B,H,Sk,D]."""
+
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    dtype: str            # 'f32' or 'bf16'
+    seed: int
+    layout: str           # 'neox' or 'gptj'
+    base: float = 10000.0
+    rot_dim: int | None = None
+    q_off: int = 0
+    k_off: int = 0
+    causal: bool = True
+
+    @property
+    def rot(self) -> int:
+        return self.D if self.rot_dim is None else self.rot_dim
+
+    @property
+    def table_rows(self) -> int:
+        return max(self.q_off + self.Sq, self.k_off + self.Sk)
+
+    def visible_pairs(self) -> int:
+        """Number of (query, key) pairs the mask allows, over all heads."""
+        if not self.causal:
+            return self.B * self.H * self.Sq * self.Sk
+        i = np.arange(self.Sq, dtype=np.int64)
+        n = np.clip(self.q_off + i - self.k_off + 1, 0, self.Sk)
+        return int(self.B * self.H * n.sum())
+
+    def flops(self) -> int:
+        """Algorithmic flops: 4*D per visible pair (QK^T and PV, 2 each)."""
+        return 4 * self.D * self.visible_pairs()
+
+    def label(self) -> str:
+        return f"{self.B}x{self.H}x{self.Sq}x{self.Sk}x{self.D}"
+
+
+@dataclass(frozen=True)
+class RopeApplyWorkload:
+    """Standalone in-place RoPE over a ragged continuous batch."""
+
+    name: str
+    n_tokens: int
+    n_requests: int
+    table_rows: int
+    H_q: int
+    H_kv: int
+    D: int
+    rot_dim: int
+    layout: str
+    dtype: str
+    seed: int
+    base: float = 10000.0
+    positions: str = "uniform"   # 'uniform' (iid over the table) or 'contiguous'
+    start_positions: tuple = field(default=())
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the op must move: rotated span read+written for every head,
+        one cos and one sin row per token, one int32 position per token."""
+        elt = 2 if self.dtype == "bf16" else 4
+        per_tok = 2 * (self.H_q + self.H_kv) * self.rot_dim * elt + 2 * (self.rot_dim // 2) * 4 + 4
+        return self.n_tokens * per_tok
+
+
+# The parity / benchmark workloads.
+TINY_F32 = AttentionWorkload("causal_gptj_f32_1x2x128x64", 1, 2, 128, 128, 64, "f32", 0, "gptj")
+SMALL_BF16 = AttentionWorkload("causal_gptj_bf16_1x8x512x64", 1, 8, 512, 512, 64, "bf16", 1, "gptj")
+SWEEP_BF16 = tuple(
+    AttentionWorkload(f"causal_neox_bf16_{b}x8x{s}x64", b, 8, s, s, 64, "bf16", seed, "neox")
+    for (b, s), seed in zip(((1, 1024), (1, 2048), (1, 4096), (2, 1024), (4, 1024)), range(2, 7))
+)
+HEADLINE = SWEEP_BF16[2]   # 1x8x4096x64 bf16 NeoX causal
+PREFILL_OFFSET = AttentionWorkload("chunked_prefill_neox_bf16_1x32x2048q_16384k_128", 1, 32, 2048,
+                                   16384, 128, "bf16", 7, "neox", base=500000.0,
+                                   q_off=14336, k_off=0)
+RAGGED_ROPE = RopeApplyWorkload("ragged_rope_neox_bf16_8192tok_32q8kv_rot64of128", 8192, 16,
+                                32768, 32, 8, 128, 64, "neox", "bf16", 8)
+
+ATTENTION_WORKLOADS = (TINY_F32, SMALL_BF16) + SWEEP_BF16 + (PREFILL_OFFSET,)
+
+
+# ---------------------------------------------------------------------------
+# generators
+
+
+def attention_inputs(w: AttentionWorkload):
+    """(q, k, v) as fp32 arrays holding values exact in ``w.dtype``."""
+    rng = np.random.default_rng(w.seed)
+    q = rng.standard_normal((w.B, w.H, w.Sq, w.D))
+    k = rng.standard_normal((w.B, w.H, w.Sk, w.D))
+    v = rng.standard_normal((w.B, w.H, w.Sk, w.D))
+    return tuple(round_to(a.astype(np.float32), w.dtype) for a in (q, k, v))
+
+
+def ragged_lengths(rng: np.random.Generator, total: int, n_requests: int) -> np.ndarray:
+    """``n_requests`` positive lengths summing to ``total`` from distinct cut points."""
+    if n_requests < 1 or n_requests > total:
+        raise ValueError("need 1 <= n_requests <= total")
+    cuts = np.sort(rng.choice(np.arange(1, total), size=n_requests - 1, replace=False))
+    edges = np.concatenate([[0], cuts, [total]])
+    return np.diff(edges).astype(np.int64)
+
+
+def rope_apply_inputs(w: RopeApplyWorkload):
+    """dict with 'lengths', 'positions' (int32), 'q' [T,H_q,D], 'k' [T,H_kv,D]
+    (fp32 arrays exact in ``w.dtype``)."""
+    rng = np.random.default_rng(w.seed)
+    lengths = ragged_lengths(rng, w.n_tokens, w.n_requests)
+    if w.positions == "uniform":
+        positions = rng.integers(0, w.table_rows, size=w.n_tokens)
+    elif w.positions == "contiguous":
+        starts = list(w.start_positions) or [0] * w.n_requests
+        positions = np.concatenate([s + np.arange(n) for s, n in zip(starts, lengths)])
+    else:
+        raise ValueError(w.positions)
+    q = rng.standard_normal((w.n_tokens, w.H_q, w.D)).astype(np.float32)
+    k = rng.standard_normal((w.n_tokens, w.H_kv, w.D)).astype(np.float32)
+    return {
+        "lengths": lengths,
+        "positions": positions.astype(np.int32),
+        "q": round_to(q, w.dtype),
+        "k": round_to(k, w.dtype),
+    }

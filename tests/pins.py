@@ -1,0 +1,354 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics
+fix, never against the oracle's own formulas retyped.
+
+Each pin takes an ``oracle.Oracle`` and raises ``AssertionError`` when the
+oracle disagrees.  ``tests/test_oracle_pins.py`` runs every pin on the real
+oracle, and runs the whole set on copies of the oracle with a planted mistake
+to show that each such mistake fails at least one pin.
+
+Pages cited:
+  [RF] "RoPE and FlashAttention: relative positions and online softmax"
+  [TR] "Write Triton Rope Kernel"
+"""
+from __future__ import annotations
+
+import math
+from pathlib import Path
+
+import numpy as np
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ---------------------------------------------------------------------------
+# independent constructions used as references
+
+
+def rotation_matrix(head_dim: int, rot_dim: int, pos: float, base: float, layout: str) -> np.ndarray:
+    """Explicit block rotation matrix R(pos): each pair's plane gets the
+    textbook 2x2 rotation [[c, -s], [s, c]] by pos * base**(-2i/rot_dim).
+    Built as a dense matrix and applied with a matmul, so it shares no
+    per-pair indexing code with the oracle's loop."""
+    R = np.eye(head_dim)
+    half = rot_dim // 2
+    for i in range(half):
+        a, b = (2 * i, 2 * i + 1) if layout == "gptj" else (i, i + half)
+        ang = pos * np.power(base, -2.0 * i / rot_dim)
+        c, s = np.cos(ang), np.sin(ang)
+        R[a, a], R[a, b], R[b, a], R[b, b] = c, -s, s, c
+    return R
+
+
+def rope_complex(x: np.ndarray, positions, base: float, rot_dim: int, layout: str) -> np.ndarray:
+    """RoPE as complex multiplication: pair i is the complex number
+    x_a + j x_b, multiplied by exp(j * pos * theta_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    half = rot_dim // 2
+    if layout == "gptj":
+        z = x[..., 0:rot_dim:2] + 1j * x[..., 1:rot_dim:2]
+    else:
+        z = x[..., :half] + 1j * x[..., half:rot_dim]
+    theta = np.power(base, -2.0 * np.arange(half) / rot_dim)
+    pos = np.asarray(positions, dtype=np.float64)[..., None]
+    w = z * np.exp(1j * pos * theta)
+    y = x.copy()
+    if layout == "gptj":
+        y[..., 0:rot_dim:2], y[..., 1:rot_dim:2] = w.real, w.imag
+    else:
+        y[..., :half], y[..., half:rot_dim] = w.real, w.imag
+    return y
+
+
+def dense_reference(qr, kr, v, allowed, scale):
+    """softmax(scale * qr kr^T + mask) v with scipy's softmax."""
+    from scipy.special import softmax
+    s = np.where(allowed, scale * (qr @ kr.T), -np.inf)
+    return softmax(s, axis=-1) @ v
+
+
+def offset_mask(Sq: int, Sk: int, q_off: int, k_off: int) -> np.ndarray:
+    return (k_off + np.arange(Sk))[None, :] <= (q_off + np.arange(Sq))[:, None]
+
+
+# ---------------------------------------------------------------------------
+# RoPE pins
+
+
+def pin_worked_example(orc):
+    """[RF] section 2, practice solution (tests/golden/worked_example.txt)."""
+    rows = []
+    for line in (GOLDEN / "worked_example.txt").read_text().splitlines():
+        if line.strip() and not line.startswith("#"):
+            m, n, val, sym = line.split()
+            rows.append((int(m), int(n), float(val), sym))
+    x = np.array([[1.0, 0.0]])
+    for layout in ("gptj", "neox"):
+        for m, n, val, sym in rows:
+            arg = float(sym[len("cos("):-1])
+            assert abs(val - math.cos(arg)) < 1e-16, "fixture value disagrees with its own formula"
+            q = orc.rope(x, [m], base=10000.0, layout=layout)
+            k = orc.rope(x, [n], base=10000.0, layout=layout)
+            score = float(q[0] @ k[0])
+            assert abs(score - val) <= 1e-15, (layout, m, n, score, val)
+
+
+def pin_relative_shift_p2(orc):
+    """All-pairs relative-shift invariance with the shapes of [RF] section 2's
+    test: q [2,3,7,8] at 4..10, k [2,3,9,8] at 2..10, shift 23, 1e-11."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((2, 3, 7, 8))
+    k = rng.standard_normal((2, 3, 9, 8))
+    qp, kp = np.arange(4, 11), np.arange(2, 11)
+    for layout in ("gptj", "neox"):
+        a = orc.rope(q, qp, layout=layout) @ np.swapaxes(orc.rope(k, kp, layout=layout), -1, -2)
+        b = orc.rope(q, qp + 23, layout=layout) @ np.swapaxes(orc.rope(k, kp + 23, layout=layout), -1, -2)
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11)
+        wrong = orc.rope(q, qp, layout=layout) @ np.swapaxes(orc.rope(k, kp + 1, layout=layout), -1, -2)
+        assert not np.allclose(a, wrong), "shifting only k must change the scores"
+
+
+def pin_relative_shift_long(orc):
+    """Relative-shift invariance at the long-context settings: D=128, base
+    500000, positions near 14336..16383, shift 10000.  Tolerance scales with
+    the largest angle times fp64 epsilon times D."""
+    rng = np.random.default_rng(5)
+    D = 128
+    q = rng.standard_normal((6, D))
+    k = rng.standard_normal((9, D))
+    qp, kp = 14336 + np.arange(6) * 300, np.arange(9) * 1800
+    shift = 10000
+    tol = (16384 + shift) * 2.0 ** -52 * D * 64
+    for layout in ("gptj", "neox"):
+        a = orc.rope(q, qp, base=5e5, layout=layout) @ orc.rope(k, kp, base=5e5, layout=layout).T
+        b = orc.rope(q, qp + shift, base=5e5, layout=layout) @ orc.rope(k, kp + shift, base=5e5, layout=layout).T
+        np.testing.assert_allclose(a, b, rtol=0, atol=tol)
+
+
+def pin_norm_preserved(orc):
+    """Rotations preserve norms ([RF] section 1)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 64))
+    pos = rng.integers(0, 32768, size=5)
+    for layout in ("gptj", "neox"):
+        for rot in (64, 32):
+            y = orc.rope(x, pos, rot_dim=rot, layout=layout)
+            np.testing.assert_allclose((y ** 2).sum(-1), (x ** 2).sum(-1), rtol=1e-13)
+
+
+def pin_chunked_equals_full(orc):
+    """Rotating K in two chunks with their true positions equals rotating it
+    whole, bit for bit; restarting the positions of the second chunk at 0
+    must differ ([RF] section 2)."""
+    rng = np.random.default_rng(43)
+    k = rng.standard_normal((2, 3, 9, 8))
+    kp = np.arange(2, 11)
+    for layout in ("gptj", "neox"):
+        full = orc.rope(k, kp, layout=layout)
+        chunked = np.concatenate([orc.rope(k[..., :4, :], kp[:4], layout=layout),
+                                  orc.rope(k[..., 4:, :], kp[4:], layout=layout)], axis=-2)
+        assert np.array_equal(full, chunked)
+        restarted = orc.rope(k[..., 4:, :], np.arange(5), layout=layout)
+        assert not np.allclose(full[..., 4:, :], restarted)
+
+
+def pin_position_zero_identity(orc):
+    """cos 0 = 1 and sin 0 = 0 exactly: position 0 leaves a row unchanged."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 128))
+    for layout in ("gptj", "neox"):
+        for rot in (128, 64):
+            assert np.array_equal(orc.rope(x, 0, rot_dim=rot, layout=layout), x)
+
+
+def pin_complex_multiplication(orc):
+    """RoPE equals multiplying each pair, read as a complex number, by
+    exp(i * pos * theta_i); checked for both pairings, partial and full
+    rotation, and several bases."""
+    rng = np.random.default_rng(17)
+    for D, rot, base in ((8, 8, 10000.0), (64, 64, 10000.0), (128, 64, 10000.0),
+                         (128, 128, 500000.0), (12, 4, 100.0)):
+        x = rng.standard_normal((7, D))
+        pos = rng.integers(0, 40000, size=7)
+        for layout in ("gptj", "neox"):
+            got = orc.rope(x, pos, base=base, rot_dim=rot, layout=layout)
+            want = rope_complex(x, pos, base, rot, layout)
+            np.testing.assert_allclose(got, want, rtol=0, atol=1e-11)
+
+
+def pin_brute_force_matrices(orc):
+    """On tiny rows (D <= 8) the oracle equals the explicit block rotation
+    matrix R(pos) applied by matmul."""
+    rng = np.random.default_rng(19)
+    for D, rot in ((2, 2), (4, 4), (6, 4), (8, 8), (8, 2)):
+        x = rng.standard_normal((5, D))
+        pos = [0, 1, 7, 300, 12345]
+        for layout in ("gptj", "neox"):
+            got = orc.rope(x, pos, base=100.0, rot_dim=rot, layout=layout)
+            want = np.stack([rotation_matrix(D, rot, p, 100.0, layout) @ x[r] for r, p in enumerate(pos)])
+            np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def pin_layout_permutation(orc):
+    """GPT-J and NeoX are the same functions after permuting the rotated dims
+    (slot 2i -> i, 2i+1 -> i + rot/2), bit for bit ([RF] section 2;
+    [TR] "Common failure modes")."""
+    rng = np.random.default_rng(23)
+    for D, rot in ((64, 64), (128, 64)):
+        x = rng.standard_normal((6, D))
+        pos = rng.integers(0, 32768, size=6)
+        half = rot // 2
+        perm = np.arange(D)
+        perm[:half] = np.arange(0, rot, 2)
+        perm[half:rot] = np.arange(1, rot, 2)
+        gptj = orc.rope(x, pos, rot_dim=rot, layout="gptj")
+        neox = orc.rope(x[:, perm], pos, rot_dim=rot, layout="neox")
+        assert np.array_equal(neox, gptj[:, perm])
+
+
+def pin_partial_tail(orc):
+    """Partial RoPE leaves dims >= rot_dim bit-identical, and its first rot_dim
+    dims equal a full rotation of those dims alone: the frequency schedule
+    depends on rot_dim only ([TR] "Correctness requirements")."""
+    rng = np.random.default_rng(29)
+    x = rng.standard_normal((8, 128))
+    pos = rng.integers(0, 32768, size=8)
+    for layout in ("gptj", "neox"):
+        y = orc.rope(x, pos, rot_dim=64, layout=layout)
+        assert np.array_equal(y[:, 64:], x[:, 64:])
+        head = orc.rope(np.ascontiguousarray(x[:, :64]), pos, rot_dim=64, layout=layout)
+        assert np.array_equal(y[:, :64], head)
+
+
+def pin_trig_table(orc):
+    """The exact table: row 0 is (1, 0); column 0 is (cos p, sin p) because the
+    first frequency is 1 ([RF] section 3); everything matches numpy's trig of
+    p * base**(-2i/rot_dim)."""
+    for base, rot, n in ((10000.0, 64, 4096), (500000.0, 128, 512)):
+        c, s = orc.trig(base, rot, n)
+        assert np.array_equal(c[0], np.ones(rot // 2)) and np.array_equal(s[0], np.zeros(rot // 2))
+        p = np.arange(n, dtype=np.float64)
+        np.testing.assert_allclose(c[:, 0], np.cos(p), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(s[:, 0], np.sin(p), rtol=0, atol=1e-15)
+        ang = p[:, None] * np.power(base, -2.0 * np.arange(rot // 2) / rot)[None, :]
+        np.testing.assert_allclose(c, np.cos(ang), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(s, np.sin(ang), rtol=0, atol=1e-12)
+
+
+def pin_token_permutation(orc):
+    """Per-token positions: permuting the tokens (with their positions)
+    commutes with the rotation ([TR] "Required reasoning process" step 3)."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((20, 3, 16))
+    pos = rng.integers(0, 32768, size=20)
+    perm = rng.permutation(20)
+    for layout in ("gptj", "neox"):
+        y = orc.rope(x, pos[:, None], rot_dim=8, layout=layout)
+        yp = orc.rope(x[perm], pos[perm][:, None], rot_dim=8, layout=layout)
+        assert np.array_equal(yp, y[perm])
+
+
+# ---------------------------------------------------------------------------
+# attention pins
+
+
+def pin_attention_p2_example(orc):
+    """[RF] section 5's example: Q [7,4], K [9,4], V [9,5] from default_rng(43),
+    keys j <= 2 + i visible (query offset 2), scale 1/2, no rotation; equals
+    scipy's dense softmax at 1e-12."""
+    rng = np.random.default_rng(43)
+    Q, K, V = rng.normal(size=(7, 4)), rng.normal(size=(9, 4)), rng.normal(size=(9, 5))
+    mask = np.arange(9)[None, :] <= (2 + np.arange(7))[:, None]
+    want = dense_reference(Q, K, V, mask, 0.5)
+    got = orc.attention(Q, K, V, q_off=2, k_off=0, rot_dim=0, causal=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_vs_scipy_rotated(orc):
+    """RoPE attention with offsets equals rotating with the explicit matrices,
+    then scipy's dense masked softmax (1e-12)."""
+    rng = np.random.default_rng(37)
+    for (Sq, Sk, q_off, k_off, D, rot, layout, causal) in (
+            (7, 9, 2, 0, 8, 8, "gptj", True), (9, 9, 0, 0, 8, 8, "neox", True),
+            (5, 12, 20, 13, 8, 4, "neox", True), (6, 4, 0, 0, 6, 6, "gptj", False)):
+        q, k, v = rng.standard_normal((Sq, D)), rng.standard_normal((Sk, D)), rng.standard_normal((Sk, D))
+        qr = np.stack([rotation_matrix(D, rot, q_off + i, 10000.0, layout) @ q[i] for i in range(Sq)])
+        kr = np.stack([rotation_matrix(D, rot, k_off + j, 10000.0, layout) @ k[j] for j in range(Sk)])
+        allowed = offset_mask(Sq, Sk, q_off, k_off) if causal else np.ones((Sq, Sk), bool)
+        want = dense_reference(qr, kr, v, allowed, 1.0 / math.sqrt(D))
+        got = orc.attention(q, k, v, q_off=q_off, k_off=k_off, rot_dim=rot, layout=layout, causal=causal)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_vs_torch_sdpa(orc):
+    """torch's scaled_dot_product_attention in fp64 on the CPU with an
+    explicit boolean mask ([RF] sections 5 and 6) agrees at 1e-12."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(41)
+    B, H, Sq, Sk, D = 2, 3, 6, 10, 8
+    q, k, v = (rng.standard_normal(s) for s in ((B, H, Sq, D), (B, H, Sk, D), (B, H, Sk, D)))
+    q_off, k_off = 4, 0
+    qr = orc.rope(q, q_off + np.arange(Sq), layout="neox")
+    kr = orc.rope(k, k_off + np.arange(Sk), layout="neox")
+    mask = torch.tensor(offset_mask(Sq, Sk, q_off, k_off))
+    want = F.scaled_dot_product_attention(torch.tensor(qr), torch.tensor(kr), torch.tensor(v),
+                                          attn_mask=mask, dropout_p=0.0).numpy()
+    got = orc.attention(q, k, v, q_off=q_off, k_off=k_off, layout="neox")
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_closed_forms(orc):
+    """Closed forms: zero queries give uniform weights, so causal output row i
+    is the mean of V[0..i]; row 0 of a square causal forward is V[0]; a single
+    key returns V; all-ones V gives all-ones output (softmax rows sum to 1)."""
+    rng = np.random.default_rng(47)
+    S, D = 12, 8
+    k, v = rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    got = orc.attention(np.zeros((S, D)), k, v, layout="gptj")
+    want = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+    q = rng.standard_normal((S, D))
+    got = orc.attention(q, k, v, layout="neox")
+    np.testing.assert_allclose(got[0], v[0], rtol=0, atol=1e-15)
+    got = orc.attention(q[:1], k[:1], v[:1], layout="neox", causal=False)
+    np.testing.assert_allclose(got, v[:1], rtol=0, atol=1e-15)
+    got = orc.attention(q, k, np.ones((S, D)), q_off=3, k_off=1, layout="gptj")
+    np.testing.assert_allclose(got, np.ones((S, D)), rtol=0, atol=1e-14)
+
+
+def pin_attention_translation(orc):
+    """Moving queries and keys together by the same offset leaves the output
+    unchanged up to rounding (the relative-position identity, [RF] section 1)."""
+    rng = np.random.default_rng(53)
+    q, k, v = (rng.standard_normal((1, 2, 16, 16)) for _ in range(3))
+    a = orc.attention(q, k, v, q_off=0, k_off=0, layout="neox")
+    b = orc.attention(q, k, v, q_off=777, k_off=777, layout="neox")
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+    c = orc.attention(q, k, v, q_off=1, k_off=0, layout="neox")
+    assert not np.allclose(a, c), "changing only the query offset must change the output"
+
+
+def pin_empty_row_rejected(orc):
+    """A query that sees no key is rejected ([RF] section 5)."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(59)
+    q, k, v = (rng.standard_normal((4, 8)) for _ in range(3))
+    try:
+        orc.attention(q, k, v, q_off=0, k_off=1, layout="gptj")
+    except oracle_pkg.OracleError as e:
+        assert e.status == oracle_pkg.ERR_EMPTY_ROW
+    else:
+        raise AssertionError("empty row accepted")
+
+
+def pin_rows_match_full(orc):
+    """The sampled-row entry point reproduces the full forward bit for bit."""
+    rng = np.random.default_rng(61)
+    q, k, v = rng.standard_normal((2, 2, 9, 8)), rng.standard_normal((2, 2, 11, 8)), rng.standard_normal((2, 2, 11, 8))
+    full = orc.attention(q, k, v, q_off=5, k_off=3, layout="gptj")
+    rows = [(0, 0, 0), (1, 1, 8), (0, 1, 4), (1, 0, 2)]
+    got = orc.attention_rows(q, k, v, rows, q_off=5, k_off=3, layout="gptj")
+    assert np.array_equal(got, np.stack([full[b, h, i] for b, h, i in rows]))
+
+
+ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

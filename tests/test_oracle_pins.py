@@ -1,0 +1,56 @@
+"""The fp64 oracle against its pins, and the pins against planted mistakes.
+
+A planted mistake lives only in a temporary copy of the oracle's C source;
+each one must make at least one pin fail.
+"""
+import pytest
+
+import oracle
+import pins
+
+MUTATIONS = {
+    # name: (text in oracle.c, replacement)
+    "sin_sign_first": ("y[a] = xa * c - xb * s;", "y[a] = xa * c + xb * s;"),
+    "sin_sign_second": ("y[b] = xa * s + xb * c;", "y[b] = -xa * s + xb * c;"),
+    "second_uses_cos_twice": ("y[b] = xa * s + xb * c;", "y[b] = xa * c + xb * c;"),
+    "frequency_denominator": ("-2.0 * (double)i / (double)rot_dim", "-2.0 * (double)i / (double)(rot_dim + 2)"),
+    "frequency_no_factor_two": ("-2.0 * (double)i / (double)rot_dim", "-1.0 * (double)i / (double)rot_dim"),
+    "layouts_swapped": ("if (layout == OR_GPTJ) {", "if (layout != OR_GPTJ) {"),
+    "neox_partner_off_by_one": ("*b = i + rot_dim / 2;", "*b = (i + rot_dim / 2 + 1) % rot_dim;"),
+    "tail_dropped": ("        y[d] = x[d];", "        y[d] = 0.0;"),
+    "row_index_as_position": ("positions[r], base, layout);", "(double)r, base, layout);"),
+    "query_offset_ignored": ("(double)(q_off + r % Sq)", "(double)(r % Sq)"),
+    "key_offset_ignored": ("(double)(k_off + r % Sk)", "(double)(r % Sk)"),
+    "mask_off_by_one": ("int64_t last = q_off + i - k_off;", "int64_t last = q_off + i - k_off - 1;"),
+    "mask_sees_future": ("int64_t last = q_off + i - k_off;", "int64_t last = q_off + i - k_off + 1;"),
+    "scale_uses_d": ("scale = 1.0 / sqrt((double)D);", "scale = 1.0 / (double)D;"),
+    "dot_index": ("s += qr[d] * kr[j * D + d];", "s += qr[d] * kr[j + d];"),
+    "pv_index": ("out[e] += scores[j] * v[j * Dv + e];", "out[e] += scores[j] * v[j * Dv];"),
+    "not_normalised": ("for (int e = 0; e < Dv; ++e) out[e] /= l;", ""),
+    "query_rotated_at_key_offset": ("(double)(q_off + r % Sq)", "(double)(k_off + r % Sq)"),
+}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTATIONS[name]
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found in oracle.c"
+    mutant = oracle.load_variant(src.replace(old, new), name)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, oracle.OracleError):
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name!r} passed every pin"
