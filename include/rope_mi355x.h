@@ -1,0 +1,163 @@
+/*
+ * rope_mi355x.h -- C ABI of the MI355X (gfx950) rotary position embedding
+ * library: a cos/sin table build, a standalone in-place RoPE for ragged
+ * continuous batches, and a fused RoPE + softmax attention forward with an
+ * offset-causal mask.
+ *
+ * Pages cited (by title and section):
+ *   [RF] "RoPE and FlashAttention: relative positions and online softmax"
+ *   [TR] "Write Triton Rope Kernel"
+ *   [PK] "RoPE + PoPE Attention Kernels" (README of pope-memory-optimal)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer, allocated, owned and freed
+ *     by the caller.  The library allocates no memory and keeps no state
+ *     beyond a per-device cache of device properties; it is thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; no call synchronises.
+ *   - Each call returns ROPE_OK (0) or an error status.  Every host-visible
+ *     argument is validated before any HIP call is made, so argument errors
+ *     are reported without a device and nothing is enqueued on error.
+ *     ROPE_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ *   - Element types: ROPE_BF16 (bfloat16 storage) or ROPE_F32.  All rotation
+ *     and softmax arithmetic is fp32; cos/sin tables are always fp32
+ *     ([TR] "Kernel design rules": fp32 trig, upcast after load, cast at store).
+ *   - Pairing layouts ([TR] "Inputs the agent should gather first", item 1):
+ *       ROPE_NEOX: half split, pair (i, i + rot_dim/2), i < rot_dim/2;
+ *       ROPE_GPTJ: adjacent pairs (2i, 2i+1), i < rot_dim/2.
+ *     Pair i at position p is rotated by angle p * theta_i with
+ *     theta_i = base^(-2i/rot_dim):  a' = a cos - b sin,  b' = a sin + b cos
+ *     ([RF] sections 1-2; [TR] "Required reasoning process", steps 1 and 6).
+ *     Dims at or past rot_dim are never modified ([TR] "Correctness
+ *     requirements": the unrotated tail is bit-identical).
+ *   - cos/sin tables: fp32 [table_rows, rot_dim/2], row stride rot_dim/2,
+ *     row p holds cos(p theta_i) / sin(p theta_i).
+ */
+#ifndef ROPE_MI355X_H
+#define ROPE_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* pairing layouts */
+#define ROPE_NEOX 0
+#define ROPE_GPTJ 1
+
+/* element types */
+#define ROPE_BF16 0
+#define ROPE_F32 1
+
+/* status codes */
+#define ROPE_OK 0
+#define ROPE_ERR_NULL 1          /* a required pointer is NULL */
+#define ROPE_ERR_SHAPE 2         /* odd or out-of-range dims, non-positive sizes, bad strides */
+#define ROPE_ERR_BASE 3          /* base <= 0 (or not finite) */
+#define ROPE_ERR_UNSUPPORTED 4   /* dtype / head_dim / rot_dim / layout combination not built */
+#define ROPE_ERR_EMPTY_ROW 5     /* causal with q_pos_offset < k_pos_offset: a query sees no key */
+#define ROPE_ERR_TABLE_RANGE 6   /* table_rows too small for the positions the call uses */
+#define ROPE_ERR_HIP 7           /* a HIP launch failed */
+#define ROPE_ERR_ALIGN 8         /* a pointer or stride breaks the required alignment */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *rope_status_str(int status);
+
+/*
+ * rope_tables_build -- fill fp32 cos/sin tables for positions 0..max_pos-1.
+ *
+ * Defines the table of [TR] "Correctness requirements" (theta_i =
+ * base^(-2i/rot_dim), angle = position * theta_i, fp32 storage) with the
+ * angle formed in fp64 as [RF] section 2 does, then each of cos and sin
+ * rounded once to fp32.  The frequency denominator is rot_dim, so the table
+ * of a partial RoPE has rot_dim/2 columns.
+ *
+ *   base        > 0, finite                          (else ROPE_ERR_BASE)
+ *   rot_dim     even, 2..1024                        (else ROPE_ERR_SHAPE)
+ *   max_pos     1..2^31-1 rows                       (else ROPE_ERR_SHAPE)
+ *   cos_out,    device fp32 [max_pos, rot_dim/2] each, written whole
+ *   sin_out
+ * Off the hot path: build once per (base, rot_dim, max_pos) and keep the
+ * tables as device buffers ([RF] section 2).
+ */
+int rope_tables_build(double base, int rot_dim, int64_t max_pos,
+                      float *cos_out, float *sin_out, void *stream);
+
+/*
+ * rope_apply -- standalone RoPE on Q and K of a ragged continuous batch, in
+ * place, both tensors in one launch ([TR] "Required reasoning process"
+ * steps 2-10 and "Performance requirements": per-token positions, GQA head
+ * counts, partial rot_dim, combined Q+K launch; [TR] "Kernel design rules":
+ * in-place is race-free because each pair is loaded before it is stored).
+ *
+ *   q           [n_tokens, h_q heads, head_dim] elements of `dtype`, element
+ *               (t, h, d) at q[t*q_stride_tok + h*q_stride_head + d]; the
+ *               first rot_dim dims of every (t, h) row are rotated in place.
+ *               May be NULL when h_q == 0.
+ *   k           same for the h_kv key heads (may be NULL when h_kv == 0).
+ *               V is never passed: it is not rotated ([RF] section 1).
+ *   strides     in elements; need stride_head >= head_dim and
+ *               stride_tok >= heads * stride_head (rows do not overlap).
+ *   positions   int32 [n_tokens]: absolute position of each token, read per
+ *               token, never derived from the token index ([TR] step 3).
+ *               Values outside [0, table_rows) are clamped into that range on
+ *               the device (no access leaves the table); such tokens receive
+ *               the rotation of the clamped position.
+ *   cos_tab,    fp32 [table_rows, rot_dim/2] (see rope_tables_build).
+ *   sin_tab
+ *   head_dim    even, 2..1024; rot_dim even, 2..head_dim.
+ *   layout      ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16 or ROPE_F32.
+ * n_tokens == 0, or h_q == h_kv == 0, is a no-op returning ROPE_OK.
+ * Any alignment is accepted; 16-byte-aligned rows whose rotated span is a
+ * whole number of 16-byte vectors take the vectorised path.
+ */
+int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
+               void *k, int64_t k_stride_tok, int64_t k_stride_head, int h_kv,
+               const int32_t *positions, int64_t n_tokens,
+               const float *cos_tab, const float *sin_tab, int64_t table_rows,
+               int head_dim, int rot_dim, int layout, int dtype, void *stream);
+
+/*
+ * rope_flash_attn_fwd -- fused RoPE + softmax attention forward.
+ *
+ * Computes O = softmax(scale * rope(Q) rope(K)^T + mask) V per (batch, head)
+ * ([RF] section 4 for the operation, section 5 for the online-softmax
+ * recurrence it is evaluated with, section 2 for offset positions).  Query i
+ * sits at position q_pos_offset + i and key j at k_pos_offset + j; Q and K
+ * rows are rotated at those positions inside the kernel (each K tile once as
+ * it is staged, no rotated copy written to memory: [PK] "Why
+ * memory_optimized_pope is much slower but uses much less memory"); V is
+ * never rotated.  With causal != 0, key j is visible to query i iff
+ * k_pos_offset + j <= q_pos_offset + i (the offset mask of [RF] section 6
+ * for cached/chunked queries); causal == 0 shows every key to every query.
+ *
+ *   q, o        [B, H, Sq, head_dim], contiguous, element type `dtype`;
+ *               o is written whole and must not alias q, k or v.
+ *   k, v        [B, H, Sk, head_dim], contiguous.
+ *   cos_tab,    fp32 [table_rows, rot_dim/2]; need
+ *   sin_tab     table_rows >= max(q_pos_offset + Sq, k_pos_offset + Sk)
+ *               (else ROPE_ERR_TABLE_RANGE).
+ *   rot_dim     0 (no rotation: plain attention; tables may be NULL) or a
+ *               multiple of 32 up to head_dim.
+ *   head_dim    64 or 128.
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
+ *   offsets     >= 0.  With causal != 0, q_pos_offset < k_pos_offset would
+ *               leave query 0 with no visible key: ROPE_ERR_EMPTY_ROW
+ *               ([RF] section 5 rejects such rows).
+ * Requires 16-byte-aligned q, k, v, o (else ROPE_ERR_ALIGN).
+ * Accumulation and softmax are fp32; for ROPE_BF16 the rotated Q/K and the
+ * probabilities enter the matrix cores rounded to bf16.
+ */
+int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
+                        int B, int H, int64_t Sq, int64_t Sk, int head_dim,
+                        int64_t q_pos_offset, int64_t k_pos_offset,
+                        const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                        int rot_dim, int layout, int causal, float softmax_scale,
+                        int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_MI355X_H */

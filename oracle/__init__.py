@@ -77,10 +77,15 @@ class Oracle:
         lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, i64, i64, i64, i64, i32, i32,
                                               i64, i64, i32, dbl, i32, i32, dbl,
                                               _i64p, i64, _dp]
+        lib.oracle_threads.argtypes = []
         for fn in (lib.oracle_rope, lib.oracle_trig, lib.oracle_attention,
-                   lib.oracle_attention_rows):
+                   lib.oracle_attention_rows, lib.oracle_threads):
             fn.restype = ctypes.c_int
         self._lib = lib
+
+    def threads(self) -> int:
+        """OpenMP threads the oracle's parallel regions use."""
+        return int(self._lib.oracle_threads())
 
     @staticmethod
     def _check(status: int) -> None:

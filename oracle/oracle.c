@@ -34,12 +34,16 @@
  * Build: gcc -O2 -std=c99 -fopenmp -ffp-contract=off -shared -fPIC -lm
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { OR_NEOX = 0, OR_GPTJ = 1 };
 enum { OR_OK = 0, OR_ERR_ARG = 1, OR_ERR_EMPTY_ROW = 2, OR_ERR_NOMEM = 3 };
+
+/* Threads an OpenMP region of the oracle uses (reported with its timings). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* theta_i = base^(-2i/rot_dim): one frequency per rotated pair; the first
  * frequency is 1 for every base.  [RF] section 1; [TR] "Correctness

@@ -1,0 +1,193 @@
+"""Python binding of the C ABI over torch tensors.
+
+Argument marshalling only: each function checks tensor devices/dtypes/shapes
+that ctypes cannot see, passes data pointers and the current HIP stream to
+the library, and raises ``RopeError`` on a non-zero status.  All computation
+happens in the HIP kernels; there is no CPU or eager fallback.  torch provides
+device memory and streams.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+
+class RopeError(ValueError):
+    """Non-zero status from the C library."""
+
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.status_str(status)} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.OK:
+        raise RopeError(status, where)
+
+
+_LAYOUT = {"neox": _lib.NEOX, "gptj": _lib.GPTJ}
+
+
+def _layout(layout) -> int:
+    if isinstance(layout, str):
+        return _LAYOUT[layout.lower()]
+    return int(layout)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32 expected")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require_cuda(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def tables_build(base: float, rot_dim: int, max_pos: int, device="cuda"):
+    """fp32 (cos, sin) tables ``[max_pos, rot_dim/2]`` built on the device."""
+    lib = _lib.load()
+    cos = torch.empty((max_pos, rot_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check(lib.rope_tables_build(float(base), int(rot_dim), int(max_pos), cos.data_ptr(),
+                                 sin.data_ptr(), _stream(cos)), "rope_tables_build")
+    return cos, sin
+
+
+def rope_apply(q: torch.Tensor | None, k: torch.Tensor | None, positions: torch.Tensor,
+               cos: torch.Tensor, sin: torch.Tensor, rot_dim: int | None = None,
+               layout="neox") -> None:
+    """Rotate ``q`` ``[T, H_q, D]`` and ``k`` ``[T, H_kv, D]`` in place at
+    ``positions`` (int32 ``[T]``); either may be None.  One kernel launch."""
+    lib = _lib.load()
+    ref = q if q is not None else k
+    if ref is None:
+        raise ValueError("need q or k")
+    _require_cuda(q, k, positions, cos, sin)
+    if positions.dtype != torch.int32 or positions.dim() != 1 or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int32 vector")
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32:
+        raise ValueError("cos/sin tables must be float32")
+    if not (cos.is_contiguous() and sin.is_contiguous() and cos.shape == sin.shape):
+        raise ValueError("cos/sin must be contiguous tables of equal shape")
+    T, D = ref.shape[0], ref.shape[-1]
+    rot = D if rot_dim is None else int(rot_dim)
+    if cos.dim() != 2 or cos.shape[1] != rot // 2:
+        raise ValueError("table rows must hold rot_dim/2 values")
+    args = []
+    for t in (q, k):
+        if t is None:
+            args += [None, 0, 0, 0]
+            continue
+        if t.dim() != 3 or t.shape[0] != T or t.shape[2] != D or t.stride(2) != 1:
+            raise ValueError("q/k must be [tokens, heads, head_dim] with contiguous head_dim")
+        if t.dtype != ref.dtype:
+            raise ValueError("q and k must share a dtype")
+        args += [t.data_ptr(), t.stride(0), t.stride(1), t.shape[1]]
+    if positions.numel() != T:
+        raise ValueError("one position per token")
+    _check(lib.rope_apply(*args, positions.data_ptr(), T, cos.data_ptr(), sin.data_ptr(),
+                          cos.shape[0], D, rot, _layout(layout), _dtype(ref), _stream(ref)),
+           "rope_apply")
+
+
+def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,
+                   q_pos_offset: int = 0, k_pos_offset: int = 0, rot_dim: int | None = None,
+                   layout="neox", causal: bool = True, softmax_scale: float = 0.0,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused RoPE + attention forward on ``[B, H, S, D]`` tensors.
+
+    ``rot_dim=0`` (or no tables) runs plain attention.  Returns ``out``
+    (allocated like ``q`` when not given)."""
+    lib = _lib.load()
+    _require_cuda(q, k, v, cos, sin)
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous [B, H, S, D] tensors of one dtype")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Sk, D] matching q")
+    if rot_dim is None:
+        rot_dim = D if cos is not None else 0
+    if rot_dim > 0:
+        if cos is None or sin is None:
+            raise ValueError("rotation needs cos/sin tables")
+        if cos.dtype != torch.float32 or not cos.is_contiguous() or cos.shape != sin.shape \
+                or not sin.is_contiguous() or cos.dim() != 2 or cos.shape[1] != rot_dim // 2:
+            raise ValueError("cos/sin must be contiguous float32 [rows, rot_dim/2]")
+        cp, sp, rows = cos.data_ptr(), sin.data_ptr(), cos.shape[0]
+    else:
+        cp, sp, rows = None, None, 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    _check(lib.rope_flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   B, H, Sq, Sk, D, int(q_pos_offset), int(k_pos_offset),
+                                   cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),
+                                   float(softmax_scale), _dtype(q), _stream(q)),
+           "rope_flash_attn_fwd")
+    return out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int = 0,
+                           k_pos_offset: int = 0, rot_dim: int | None = None, layout="neox",
+                           causal: bool = True, softmax_scale: float = 0.0):
+    """Validate once and return a zero-argument callable that enqueues the
+    fused forward on fixed buffers (for repeated launches in timing loops;
+    the buffers must stay alive and unchanged in shape)."""
+    flash_attn_fwd(q, k, v, cos, sin, q_pos_offset, k_pos_offset, rot_dim, layout, causal,
+                   softmax_scale, out)   # validates and runs once
+    lib = _lib.load()
+    B, H, Sq, D = q.shape
+    rot = (D if cos is not None else 0) if rot_dim is None else int(rot_dim)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, k.shape[2], D,
+            int(q_pos_offset), int(k_pos_offset), cos.data_ptr() if rot else None,
+            sin.data_ptr() if rot else None, cos.shape[0] if rot else 0, rot, _layout(layout),
+            int(bool(causal)), float(softmax_scale), _dtype(q), _stream(q))
+    fn = lib.rope_flash_attn_fwd
+
+    def launch():
+        status = fn(*args)
+        if status != _lib.OK:
+            raise RopeError(status, "rope_flash_attn_fwd")
+    return launch
+
+
+def prepare_rope_apply(q, k, positions, cos, sin, rot_dim: int | None = None, layout="neox"):
+    """Validate once and return a zero-argument callable that enqueues
+    rope_apply on fixed buffers (in place)."""
+    rope_apply(q, k, positions, cos, sin, rot_dim, layout)
+    lib = _lib.load()
+    ref = q if q is not None else k
+    T, D = ref.shape[0], ref.shape[-1]
+    rot = D if rot_dim is None else int(rot_dim)
+    args = []
+    for t in (q, k):
+        args += [None, 0, 0, 0] if t is None else [t.data_ptr(), t.stride(0), t.stride(1), t.shape[1]]
+    args += [positions.data_ptr(), T, cos.data_ptr(), sin.data_ptr(), cos.shape[0], D, rot,
+             _layout(layout), _dtype(ref), _stream(ref)]
+    fn = lib.rope_apply
+
+    def launch():
+        status = fn(*args)
+        if status != _lib.OK:
+            raise RopeError(status, "rope_apply")
+    return launch

@@ -1,0 +1,149 @@
+// abi.cpp -- the extern "C" entry points of include/rope_mi355x.h.
+//
+// Every entry point validates all host-visible arguments first and returns a
+// status without touching HIP when one is wrong; only then does it pick a
+// kernel instantiation and enqueue it on the caller's stream.  Nothing here
+// allocates device memory or synchronises.
+#include <cmath>
+#include <cstdint>
+
+#include "common.hpp"
+#include "rope_mi355x.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 2147483647;   // blocks per 1-D grid
+
+bool aligned(const void *p, unsigned bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+int elt_size(int dtype) { return dtype == ROPE_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dtype) { return dtype == ROPE_BF16 || dtype == ROPE_F32; }
+bool valid_layout(int layout) { return layout == ROPE_NEOX || layout == ROPE_GPTJ; }
+
+// Rows (t, h) of one tensor must not overlap: stride_head >= head_dim when
+// there is more than one head, and a token's heads fit inside stride_tok
+// when there is more than one token.
+bool strides_ok(int64_t st_tok, int64_t st_head, int heads, int head_dim, int64_t n_tokens)
+{
+    if (heads == 0) return true;
+    if (heads > 1 && st_head < head_dim) return false;
+    if (st_head < 0 || st_tok < 0) return false;
+    const int64_t row_span = (int64_t)(heads - 1) * st_head + head_dim;
+    if (n_tokens > 1 && st_tok < row_span) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rope_status_str(int status)
+{
+    switch (status) {
+    case ROPE_OK: return "ok";
+    case ROPE_ERR_NULL: return "a required pointer is NULL";
+    case ROPE_ERR_SHAPE: return "invalid shape, dimension, offset or stride";
+    case ROPE_ERR_BASE: return "base must be positive and finite";
+    case ROPE_ERR_UNSUPPORTED: return "unsupported dtype / head_dim / rot_dim / layout combination";
+    case ROPE_ERR_EMPTY_ROW: return "a query row sees no key (causal with q_pos_offset < k_pos_offset)";
+    case ROPE_ERR_TABLE_RANGE: return "cos/sin table has too few rows for the positions used";
+    case ROPE_ERR_HIP: return "HIP kernel launch failed";
+    case ROPE_ERR_ALIGN: return "pointer or stride breaks the required alignment";
+    default: return "unknown status";
+    }
+}
+
+int rope_tables_build(double base, int rot_dim, int64_t max_pos, float *cos_out,
+                      float *sin_out, void *stream)
+{
+    if (!(base > 0.0) || !std::isfinite(base)) return ROPE_ERR_BASE;
+    if (rot_dim < 2 || rot_dim > 1024 || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (max_pos < 1 || max_pos > 2147483647) return ROPE_ERR_SHAPE;
+    if (!cos_out || !sin_out) return ROPE_ERR_NULL;
+    if (!aligned(cos_out, 4) || !aligned(sin_out, 4)) return ROPE_ERR_ALIGN;
+    return rope_launch_tables(base, rot_dim, max_pos, cos_out, sin_out,
+                              static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK
+               ? ROPE_OK
+               : ROPE_ERR_HIP;
+}
+
+int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
+               void *k, int64_t k_stride_tok, int64_t k_stride_head, int h_kv,
+               const int32_t *positions, int64_t n_tokens,
+               const float *cos_tab, const float *sin_tab, int64_t table_rows,
+               int head_dim, int rot_dim, int layout, int dtype, void *stream)
+{
+    if (head_dim < 2 || head_dim > 1024 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (rot_dim < 2 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (n_tokens < 0 || n_tokens > 2147483647 || h_q < 0 || h_kv < 0 || h_q + h_kv > 65536)
+        return ROPE_ERR_SHAPE;
+    if (!valid_layout(layout) || !valid_dtype(dtype)) return ROPE_ERR_UNSUPPORTED;
+    if (!strides_ok(q_stride_tok, q_stride_head, h_q, head_dim, n_tokens) ||
+        !strides_ok(k_stride_tok, k_stride_head, h_kv, head_dim, n_tokens))
+        return ROPE_ERR_SHAPE;
+    if (n_tokens == 0 || h_q + h_kv == 0) return ROPE_OK;
+    if ((h_q > 0 && !q) || (h_kv > 0 && !k) || !positions || !cos_tab || !sin_tab)
+        return ROPE_ERR_NULL;
+    if (table_rows < 1) return ROPE_ERR_TABLE_RANGE;
+    const unsigned es = (unsigned)elt_size(dtype);
+    if ((h_q > 0 && !aligned(q, es)) || (h_kv > 0 && !aligned(k, es)) || !aligned(positions, 4) ||
+        !aligned(cos_tab, 4) || !aligned(sin_tab, 4))
+        return ROPE_ERR_ALIGN;
+
+    RopeApplyArgs a;
+    a.q = q; a.q_stride_tok = q_stride_tok; a.q_stride_head = q_stride_head; a.h_q = h_q;
+    a.k = k; a.k_stride_tok = k_stride_tok; a.k_stride_head = k_stride_head; a.h_kv = h_kv;
+    a.positions = positions; a.n_tokens = n_tokens;
+    a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.table_rows = table_rows;
+    a.head_dim = head_dim; a.rot_dim = rot_dim; a.layout = layout; a.dtype = dtype;
+    return rope_launch_apply(a, static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK ? ROPE_OK
+                                                                                     : ROPE_ERR_HIP;
+}
+
+int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
+                        int B, int H, int64_t Sq, int64_t Sk, int head_dim,
+                        int64_t q_pos_offset, int64_t k_pos_offset,
+                        const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                        int rot_dim, int layout, int causal, float softmax_scale,
+                        int dtype, void *stream)
+{
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ROPE_ERR_SHAPE;
+    if (Sq > 2147483647 || Sk > 2147483647) return ROPE_ERR_SHAPE;
+    if (head_dim < 2 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (q_pos_offset < 0 || k_pos_offset < 0) return ROPE_ERR_SHAPE;
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return ROPE_ERR_SHAPE;
+    if (!valid_dtype(dtype) || !valid_layout(layout)) return ROPE_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return ROPE_ERR_UNSUPPORTED;
+    if (rot_dim % 32 != 0) return ROPE_ERR_UNSUPPORTED;
+    // grid size: one block per (batch*head, query tile); the fp32 kernel uses
+    // 64-query tiles, the bf16 kernel 128.
+    const int64_t tiles = (Sq + 63) / 64;
+    if ((int64_t)B * H > kMaxGrid || (int64_t)B * H * tiles > kMaxGrid) return ROPE_ERR_SHAPE;
+    if (!q || !k || !v || !o) return ROPE_ERR_NULL;
+    if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
+    if (o == q || o == k || o == v) return ROPE_ERR_SHAPE;
+    if (causal && q_pos_offset < k_pos_offset) return ROPE_ERR_EMPTY_ROW;
+    if (rot_dim > 0) {
+        const int64_t need_q = q_pos_offset + Sq, need_k = k_pos_offset + Sk;
+        if (table_rows < need_q || table_rows < need_k) return ROPE_ERR_TABLE_RANGE;
+        if (!aligned(cos_tab, 16) || !aligned(sin_tab, 16)) return ROPE_ERR_ALIGN;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return ROPE_ERR_ALIGN;
+
+    FlashArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
+    a.q_off = q_pos_offset; a.k_off = k_pos_offset;
+    a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.table_rows = table_rows;
+    a.rot_dim = rot_dim; a.layout = layout; a.causal = causal ? 1 : 0;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    a.dtype = dtype;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rc = dtype == ROPE_BF16 ? rope_launch_flash_bf16(a, s) : rope_launch_flash_f32(a, s);
+    return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+}  // extern "C"

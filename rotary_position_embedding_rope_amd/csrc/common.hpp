@@ -1,0 +1,73 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of this library:
+// bf16 <-> fp32 conversion, vector types for 16-byte accesses, and the
+// launcher interface that abi.cpp calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rope {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 storage is handled as raw uint16 bit patterns; widening is exact.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two fp32 values rounded to nearest-even bf16 (v_cvt_pk_bf16_f32), packed
+// low | high << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+}  // namespace rope
+
+// Status values returned by the launchers (mirror include/rope_mi355x.h).
+#define ROPE_LAUNCH_OK 0
+#define ROPE_LAUNCH_ERR 7
+
+// Host launchers, one per kernel family.  Arguments are validated by abi.cpp
+// before these are called; each returns ROPE_LAUNCH_OK or ROPE_LAUNCH_ERR.
+int rope_launch_tables(double base, int rot_dim, int64_t max_pos, float *cos_out,
+                       float *sin_out, hipStream_t stream);
+
+struct RopeApplyArgs {
+    void *q;
+    int64_t q_stride_tok, q_stride_head;
+    int h_q;
+    void *k;
+    int64_t k_stride_tok, k_stride_head;
+    int h_kv;
+    const int32_t *positions;
+    int64_t n_tokens;
+    const float *cos_tab, *sin_tab;
+    int64_t table_rows;
+    int head_dim, rot_dim, layout, dtype;
+};
+int rope_launch_apply(const RopeApplyArgs &a, hipStream_t stream);
+
+struct FlashArgs {
+    const void *q, *k, *v;
+    void *o;
+    int B, H;
+    int64_t Sq, Sk;
+    int head_dim;
+    int64_t q_off, k_off;
+    const float *cos_tab, *sin_tab;
+    int64_t table_rows;
+    int rot_dim, layout, causal;
+    float scale;   // already resolved (> 0)
+    int dtype;
+};
+int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream);
+int rope_launch_flash_f32(const FlashArgs &a, hipStream_t stream);

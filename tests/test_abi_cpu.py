@@ -1,0 +1,173 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and turns every invalid argument into its status code before any
+HIP call (so these run without a GPU; no compute call is made)."""
+import re
+from pathlib import Path
+
+import pytest
+
+from rotary_position_embedding_rope_amd import _lib
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "rope_mi355x.h"
+
+FAKE = 0x10000          # a 16-byte-aligned non-NULL address; never dereferenced
+FAKE2 = 0x20000
+FAKE3 = 0x30000
+FAKE4 = 0x40000
+MISALIGNED = 0x10002
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    body = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rope_[a-z_0-9]+)\s*\(", body)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_header():
+    text = HEADER.read_text()
+    codes = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"#define (ROPE_\w+) (\d+)", text))
+    assert codes["ROPE_OK"] == _lib.OK and codes["ROPE_ERR_NULL"] == _lib.ERR_NULL
+    assert codes["ROPE_ERR_SHAPE"] == _lib.ERR_SHAPE and codes["ROPE_ERR_BASE"] == _lib.ERR_BASE
+    assert codes["ROPE_ERR_UNSUPPORTED"] == _lib.ERR_UNSUPPORTED
+    assert codes["ROPE_ERR_EMPTY_ROW"] == _lib.ERR_EMPTY_ROW
+    assert codes["ROPE_ERR_TABLE_RANGE"] == _lib.ERR_TABLE_RANGE
+    assert codes["ROPE_ERR_HIP"] == _lib.ERR_HIP and codes["ROPE_ERR_ALIGN"] == _lib.ERR_ALIGN
+    assert codes["ROPE_NEOX"] == _lib.NEOX and codes["ROPE_GPTJ"] == _lib.GPTJ
+    assert codes["ROPE_BF16"] == _lib.BF16 and codes["ROPE_F32"] == _lib.F32
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert _lib.status_str(s)
+    assert _lib.status_str(99) == "unknown status"
+
+
+# --------------------------------------------------------------------------
+# rope_tables_build
+
+
+@pytest.mark.parametrize("base,rot,maxpos,c,s,want", [
+    (0.0, 64, 10, FAKE, FAKE2, _lib.ERR_BASE),
+    (-1.0, 64, 10, FAKE, FAKE2, _lib.ERR_BASE),
+    (float("inf"), 64, 10, FAKE, FAKE2, _lib.ERR_BASE),
+    (float("nan"), 64, 10, FAKE, FAKE2, _lib.ERR_BASE),
+    (1e4, 63, 10, FAKE, FAKE2, _lib.ERR_SHAPE),
+    (1e4, 0, 10, FAKE, FAKE2, _lib.ERR_SHAPE),
+    (1e4, 2048, 10, FAKE, FAKE2, _lib.ERR_SHAPE),
+    (1e4, 64, 0, FAKE, FAKE2, _lib.ERR_SHAPE),
+    (1e4, 64, 1 << 40, FAKE, FAKE2, _lib.ERR_SHAPE),
+    (1e4, 64, 10, None, FAKE2, _lib.ERR_NULL),
+    (1e4, 64, 10, FAKE, None, _lib.ERR_NULL),
+    (1e4, 64, 10, MISALIGNED, FAKE2, _lib.ERR_ALIGN),
+])
+def test_tables_build_rejects(lib, base, rot, maxpos, c, s, want):
+    assert lib.rope_tables_build(base, rot, maxpos, c, s, None) == want
+
+
+# --------------------------------------------------------------------------
+# rope_apply
+
+
+def apply_args(**over):
+    a = dict(q=FAKE, qst=40 * 128, qsh=128, hq=32, k=FAKE2, kst=8 * 128, ksh=128, hkv=8,
+             pos=FAKE3, n=8192, cos=FAKE4, sin=FAKE4 + 0x1000, rows=32768, D=128, rot=64,
+             layout=_lib.NEOX, dtype=_lib.BF16)
+    a.update(over)
+    return [a["q"], a["qst"], a["qsh"], a["hq"], a["k"], a["kst"], a["ksh"], a["hkv"], a["pos"],
+            a["n"], a["cos"], a["sin"], a["rows"], a["D"], a["rot"], a["layout"], a["dtype"], None]
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(D=127), _lib.ERR_SHAPE),
+    (dict(D=0), _lib.ERR_SHAPE),
+    (dict(D=2048, rot=64), _lib.ERR_SHAPE),
+    (dict(rot=130), _lib.ERR_SHAPE),
+    (dict(rot=63), _lib.ERR_SHAPE),
+    (dict(rot=0), _lib.ERR_SHAPE),
+    (dict(n=-1), _lib.ERR_SHAPE),
+    (dict(hq=-1), _lib.ERR_SHAPE),
+    (dict(qsh=64), _lib.ERR_SHAPE),            # head rows overlap
+    (dict(qst=31 * 128), _lib.ERR_SHAPE),      # token rows overlap
+    (dict(layout=2), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=5), _lib.ERR_UNSUPPORTED),
+    (dict(q=None), _lib.ERR_NULL),
+    (dict(k=None), _lib.ERR_NULL),
+    (dict(pos=None), _lib.ERR_NULL),
+    (dict(cos=None), _lib.ERR_NULL),
+    (dict(rows=0), _lib.ERR_TABLE_RANGE),
+    (dict(q=FAKE + 1), _lib.ERR_ALIGN),
+    (dict(pos=FAKE3 + 2), _lib.ERR_ALIGN),
+    (dict(cos=FAKE4 + 2), _lib.ERR_ALIGN),
+])
+def test_rope_apply_rejects(lib, over, want):
+    assert lib.rope_apply(*apply_args(**over)) == want
+
+
+@pytest.mark.parametrize("over", [dict(n=0), dict(hq=0, hkv=0, q=None, k=None)])
+def test_rope_apply_noop_needs_no_device(lib, over):
+    # an empty batch is a no-op: OK without any HIP call
+    assert lib.rope_apply(*apply_args(**over)) == _lib.OK
+
+
+# --------------------------------------------------------------------------
+# rope_flash_attn_fwd
+
+
+def fwd_args(**over):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, B=1, H=8, Sq=4096, Sk=4096, D=64, qo=0, ko=0,
+             cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX, causal=1,
+             scale=0.0, dtype=_lib.BF16)
+    a.update(over)
+    return [a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qo"],
+            a["ko"], a["cos"], a["sin"], a["rows"], a["rot"], a["layout"], a["causal"], a["scale"],
+            a["dtype"], None]
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(B=0), _lib.ERR_SHAPE),
+    (dict(H=-1), _lib.ERR_SHAPE),
+    (dict(Sq=0), _lib.ERR_SHAPE),
+    (dict(Sk=0), _lib.ERR_SHAPE),
+    (dict(D=63), _lib.ERR_SHAPE),
+    (dict(rot=66), _lib.ERR_SHAPE),
+    (dict(rot=-2), _lib.ERR_SHAPE),
+    (dict(qo=-1), _lib.ERR_SHAPE),
+    (dict(scale=float("nan")), _lib.ERR_SHAPE),
+    (dict(scale=float("inf")), _lib.ERR_SHAPE),
+    (dict(o=FAKE), _lib.ERR_SHAPE),             # o aliases q
+    (dict(D=192, rot=192), _lib.ERR_UNSUPPORTED),   # D/2 = 96 is not a power of two
+    (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
+    (dict(rot=48), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=3), _lib.ERR_UNSUPPORTED),
+    (dict(layout=7), _lib.ERR_UNSUPPORTED),
+    (dict(q=None), _lib.ERR_NULL),
+    (dict(v=None), _lib.ERR_NULL),
+    (dict(cos=None), _lib.ERR_NULL),
+    (dict(qo=0, ko=1, rows=8192), _lib.ERR_EMPTY_ROW),
+    (dict(rows=4095), _lib.ERR_TABLE_RANGE),
+    (dict(qo=14336, Sq=2048, Sk=16384, rows=16383), _lib.ERR_TABLE_RANGE),
+    (dict(cos=FAKE4 + 0x1004), _lib.ERR_ALIGN),
+    (dict(k=FAKE2 + 8), _lib.ERR_ALIGN),
+])
+def test_flash_rejects(lib, over, want):
+    assert lib.rope_flash_attn_fwd(*fwd_args(**over)) == want
+
+
+def test_flash_without_rotation_needs_no_table(lib):
+    # rot_dim = 0: tables may be NULL; a bad shape is still reported first
+    assert lib.rope_flash_attn_fwd(*fwd_args(rot=0, cos=None, sin=None, rows=0, B=0)) == _lib.ERR_SHAPE
+    # non-causal with q_off < k_off is legal (every key is visible); shape error first
+    assert lib.rope_flash_attn_fwd(*fwd_args(causal=0, qo=0, ko=5, rows=8192, H=0)) == _lib.ERR_SHAPE

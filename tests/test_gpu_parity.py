@@ -1,0 +1,353 @@
+"""GPU parity: the HIP kernels through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Bars (stated per test): fp32 fused forward max |err| <= 1e-5; bf16 fused
+forward max |err| <= 2e-2; rope_apply bf16 within one bf16 ulp of the exact
+rotation and bit-identical outside the rotated span; the table within one fp32
+ulp of the exact trig.  Outputs are poisoned with NaN before each call so an
+unwritten element cannot pass.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rotary_position_embedding_rope_amd import api
+from rotary_position_embedding_rope_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).to(DEV)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def tables(base, rot, rows):
+    return api.tables_build(base, rot, rows, device=DEV)
+
+
+def ulp_f32(x):
+    return np.spacing(np.abs(x).astype(np.float32)).astype(np.float64)
+
+
+def ulp_bf16(x):
+    # bf16 keeps 8 significant bits: spacing = 2^(e - 7) for |x| in [2^e, 2^(e+1))
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+# --------------------------------------------------------------------------
+# table build
+
+
+@pytest.mark.parametrize("base,rot,rows", [(1e4, 64, 32768), (5e5, 128, 16384), (1e4, 64, 4096),
+                                           (1e4, 2, 7), (100.0, 96, 1000)])
+def test_tables_within_one_ulp_of_exact(orc, base, rot, rows):
+    """Each entry within one fp32 ulp of the fp64 trig, plus the fp64 angle's
+    own rounding: p * theta_i is formed with two fp64 roundings (pow and the
+    product, on either side), which moves cos/sin by up to ~4 * 2^-53 * |angle|
+    absolutely -- visible only where the value is near zero.  At least 99.9%
+    of entries must be the correctly rounded fp32 value."""
+    c, s = tables(base, rot, rows)
+    torch.cuda.synchronize()
+    ce, se = orc.trig(base, rot, rows)
+    angle = np.arange(rows)[:, None] * np.power(base, -2.0 * np.arange(rot // 2) / rot)[None, :]
+    for got, exact in ((to64(c), ce), (to64(s), se)):
+        err = np.abs(got - exact)
+        bound = ulp_f32(exact) + 8 * 2.0 ** -53 * angle
+        assert (err <= bound).all(), float((err / bound).max())
+        assert np.mean(got == exact.astype(np.float32)) > 0.999
+    assert (to64(c)[0] == 1.0).all() and (to64(s)[0] == 0.0).all()
+
+
+# --------------------------------------------------------------------------
+# standalone rope_apply
+
+
+def pair_magnitude(x, rot, layout):
+    """|x_a| + |x_b| of the pair each rotated element belongs to."""
+    a = np.abs(x[..., :rot])
+    if layout == "gptj":
+        partner = a.reshape(a.shape[:-1] + (rot // 2, 2))[..., ::-1].reshape(a.shape)
+    else:
+        partner = np.concatenate([a[..., rot // 2:], a[..., :rot // 2]], axis=-1)
+    return a + partner
+
+
+def check_rope_apply_result(orc, x_in, x_out, positions, base, rot, layout, dtype):
+    """x_in/x_out: [T, H, D] fp64 arrays (input and GPU output).
+
+    Bar: the tail is bit-identical; each rotated element is within one ulp of
+    the storage type at the exact value, plus the fp32 evaluation error of
+    a*cos - b*sin with an fp32 table (at most ~4 * 2^-24 * (|a| + |b|)), which
+    only matters where the result cancels to near zero; for bf16 at least 99%
+    of elements are the correctly rounded exact value."""
+    pos = np.broadcast_to(positions[:, None], x_in.shape[:2])
+    want = orc.rope(x_in, pos, base=base, rot_dim=rot, layout=layout)
+    assert np.array_equal(x_out[..., rot:], x_in[..., rot:]), "tail must be bit-identical"
+    err = np.abs(x_out[..., :rot] - want[..., :rot])
+    fp32_eval = 4 * 2.0 ** -24 * pair_magnitude(x_in, rot, layout)
+    if dtype == "bf16":
+        bound = ulp_bf16(want[..., :rot]) + fp32_eval
+        assert (err <= bound).all(), float((err / bound).max())
+        exact = wl.round_to(want[..., :rot].astype(np.float32), "bf16")
+        assert np.mean(x_out[..., :rot] == exact) > 0.99
+    else:
+        bound = ulp_f32(want[..., :rot]) + fp32_eval
+        assert (err <= bound).all(), float((err / bound).max())
+    return float(err.max())
+
+
+def test_rope_apply_ragged_workload(orc):
+    """The ragged continuous-batching workload at full size: 8192 tokens from
+    16 requests, positions uniform over a 32768-row table, Q 32 heads, K 8
+    heads, NeoX, rot 64 of 128, bf16, in place, one launch."""
+    w = wl.RAGGED_ROPE
+    d = wl.rope_apply_inputs(w)
+    c, s = tables(w.base, w.rot_dim, w.table_rows)
+    q, k = to_dev(d["q"], "bf16"), to_dev(d["k"], "bf16")
+    pos = torch.from_numpy(d["positions"]).to(DEV)
+    api.rope_apply(q, k, pos, c, s, rot_dim=w.rot_dim, layout=w.layout)
+    torch.cuda.synchronize()
+    eq = check_rope_apply_result(orc, d["q"].astype(np.float64), to64(q), d["positions"], w.base,
+                                 w.rot_dim, w.layout, "bf16")
+    ek = check_rope_apply_result(orc, d["k"].astype(np.float64), to64(k), d["positions"], w.base,
+                                 w.rot_dim, w.layout, "bf16")
+    assert max(eq, ek) <= BF16_TOL
+
+
+@pytest.mark.parametrize("layout", ["neox", "gptj"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D,rot", [(128, 128), (128, 64), (64, 64), (64, 32), (80, 48), (64, 36), (8, 2)])
+def test_rope_apply_variants(orc, layout, dtype, D, rot):
+    """Both pairings, both storage types, full and partial rotation, vector
+    and scalar paths (36 and 48 are not whole 16-byte chunks for some
+    cases), GQA head counts."""
+    rng = np.random.default_rng(D * 1000 + rot)
+    T, Hq, Hkv, rows = 333, 6, 2, 5000
+    xq = wl.round_to(rng.standard_normal((T, Hq, D)), dtype)
+    xk = wl.round_to(rng.standard_normal((T, Hkv, D)), dtype)
+    positions = rng.integers(0, rows, size=T).astype(np.int32)
+    c, s = tables(10000.0, rot, rows)
+    q, k = to_dev(xq, dtype), to_dev(xk, dtype)
+    api.rope_apply(q, k, torch.from_numpy(positions).to(DEV), c, s, rot_dim=rot, layout=layout)
+    torch.cuda.synchronize()
+    check_rope_apply_result(orc, xq.astype(np.float64), to64(q), positions, 1e4, rot, layout, dtype)
+    check_rope_apply_result(orc, xk.astype(np.float64), to64(k), positions, 1e4, rot, layout, dtype)
+
+
+def test_rope_apply_packed_qkv_strides(orc):
+    """Q and K as views into one packed [T, Hq + 2*Hkv, D] QKV buffer: token
+    stride covers all heads; V heads must stay untouched."""
+    rng = np.random.default_rng(99)
+    T, Hq, Hkv, D, rot = 257, 8, 2, 128, 64
+    qkv = wl.round_to(rng.standard_normal((T, Hq + 2 * Hkv, D)), "bf16")
+    positions = rng.integers(0, 4096, size=T).astype(np.int32)
+    c, s = tables(1e4, rot, 4096)
+    buf = to_dev(qkv, "bf16")
+    q, k = buf[:, :Hq], buf[:, Hq:Hq + Hkv]
+    api.rope_apply(q, k, torch.from_numpy(positions).to(DEV), c, s, rot_dim=rot, layout="neox")
+    torch.cuda.synchronize()
+    out = to64(buf)
+    check_rope_apply_result(orc, qkv[:, :Hq].astype(np.float64), out[:, :Hq], positions, 1e4, rot, "neox", "bf16")
+    check_rope_apply_result(orc, qkv[:, Hq:Hq + Hkv].astype(np.float64), out[:, Hq:Hq + Hkv], positions, 1e4,
+                            rot, "neox", "bf16")
+    assert np.array_equal(out[:, Hq + Hkv:], qkv[:, Hq + Hkv:]), "V must never be rotated"
+
+
+def test_rope_apply_contiguous_requests_nonzero_starts(orc):
+    """Three requests of different lengths with non-zero start positions,
+    packed back to back ("Write Triton Rope Kernel", output format item 5)."""
+    w = wl.RopeApplyWorkload("three_requests", 300, 3, 8192, 4, 2, 64, 64, "gptj", "bf16", 12,
+                             positions="contiguous", start_positions=(17, 4000, 1))
+    d = wl.rope_apply_inputs(w)
+    assert d["positions"][0] == 17
+    c, s = tables(w.base, w.rot_dim, w.table_rows)
+    q, k = to_dev(d["q"], "bf16"), to_dev(d["k"], "bf16")
+    api.rope_apply(q, k, torch.from_numpy(d["positions"]).to(DEV), c, s, layout=w.layout)
+    torch.cuda.synchronize()
+    check_rope_apply_result(orc, d["q"].astype(np.float64), to64(q), d["positions"], w.base, 64, "gptj", "bf16")
+    # the token index is not the position: rotating at the index must differ
+    wrong = orc.rope(d["q"].astype(np.float64), np.arange(300)[:, None], rot_dim=64, layout="gptj")
+    assert not np.allclose(to64(q), wrong, atol=1e-2)
+
+
+def test_rope_apply_position_zero_and_single_side(orc):
+    """Position 0 is the identity, bit for bit; Q-only and K-only calls."""
+    rng = np.random.default_rng(5)
+    x = wl.round_to(rng.standard_normal((64, 4, 128)), "bf16")
+    c, s = tables(1e4, 128, 16)
+    q = to_dev(x, "bf16")
+    api.rope_apply(q, None, torch.zeros(64, dtype=torch.int32, device=DEV), c, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(to64(q), x)
+    k = to_dev(x, "bf16")
+    pos = rng.integers(0, 16, size=64).astype(np.int32)
+    api.rope_apply(None, k, torch.from_numpy(pos).to(DEV), c, s)
+    torch.cuda.synchronize()
+    check_rope_apply_result(orc, x.astype(np.float64), to64(k), pos, 1e4, 128, "neox", "bf16")
+
+
+def test_rope_apply_out_of_range_positions_are_clamped(orc):
+    """Positions outside the table are clamped into it (documented), never
+    read out of bounds."""
+    rng = np.random.default_rng(6)
+    x = wl.round_to(rng.standard_normal((4, 2, 64)), "bf16")
+    c, s = tables(1e4, 64, 100)
+    q = to_dev(x, "bf16")
+    pos = np.array([-5, 0, 99, 1000], dtype=np.int32)
+    api.rope_apply(q, None, torch.from_numpy(pos).to(DEV), c, s, layout="gptj")
+    torch.cuda.synchronize()
+    check_rope_apply_result(orc, x.astype(np.float64), to64(q), np.clip(pos, 0, 99), 1e4, 64, "gptj", "bf16")
+
+
+# --------------------------------------------------------------------------
+# fused forward
+
+
+def run_fused(w: wl.AttentionWorkload, q, k, v, rot=None):
+    rot = w.rot if rot is None else rot
+    c = s = None
+    if rot > 0:
+        c, s = tables(w.base, rot, w.table_rows)
+    out = torch.full_like(q, float("nan"))
+    api.flash_attn_fwd(q, k, v, c, s, q_pos_offset=w.q_off, k_pos_offset=w.k_off, rot_dim=rot,
+                       layout=w.layout, causal=w.causal, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def sample_rows(w: wl.AttentionWorkload, n_random=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(w.B):
+        for h in sorted({0, w.H - 1, w.H // 2}):
+            for i in (0, 1, 31, 32, 63, 64, 127, 128, w.Sq // 2, w.Sq - 2, w.Sq - 1):
+                if 0 <= i < w.Sq:
+                    rows.add((b, h, i))
+    for _ in range(n_random):
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.Sq))))
+    return sorted(rows)
+
+
+def oracle_rows(orc, w, q, k, v, rows, rot=None):
+    """Oracle output for each (b, h, i) in ``rows``, one oracle call per head."""
+    rot = w.rot if rot is None else rot
+    out = {}
+    heads = sorted({(b, h) for b, h, _ in rows})
+    for b, h in heads:
+        idx = [i for bb, hh, i in rows if (bb, hh) == (b, h)]
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        res = orc.attention_rows(q[sl], k[sl], v[sl], [(0, 0, i) for i in idx], q_off=w.q_off,
+                                 k_off=w.k_off, rot_dim=rot, base=w.base, layout=w.layout,
+                                 causal=w.causal)
+        for i, r in zip(idx, res):
+            out[(b, h, i)] = r
+    return np.stack([out[r] for r in rows])
+
+
+def test_fused_tiny_f32_full(orc):
+    """fp32 workload 1x2x128x64, GPT-J, causal: every output vs the oracle,
+    max |err| <= 1e-5."""
+    w = wl.TINY_F32
+    q, k, v = wl.attention_inputs(w)
+    got = to64(run_fused(w, to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")))
+    want = orc.attention(q, k, v, q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot, base=w.base,
+                         layout=w.layout, causal=w.causal)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= F32_TOL
+
+
+@pytest.mark.parametrize("w", [wl.SMALL_BF16, wl.SWEEP_BF16[0]], ids=lambda w: w.name)
+def test_fused_bf16_full(orc, w):
+    """Every output of the 1x8x512x64 GPT-J and 1x8x1024x64 NeoX workloads vs
+    the oracle, max |err| <= 2e-2; query 0 sees only key 0, so its output is
+    V[0] exactly."""
+    q, k, v = wl.attention_inputs(w)
+    out = run_fused(w, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"))
+    got = to64(out)
+    want = orc.attention(q, k, v, q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot, base=w.base,
+                         layout=w.layout, causal=w.causal)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= BF16_TOL
+    assert np.array_equal(got[:, :, 0], v[:, :, 0].astype(np.float64))
+
+
+@pytest.mark.parametrize("w", list(wl.SWEEP_BF16) + [wl.PREFILL_OFFSET], ids=lambda w: w.name)
+def test_fused_full_size_sampled(orc, w):
+    """Full-size workloads in the benchmark's launch configuration: sampled
+    output rows (first/last rows, tile edges, random) vs the oracle row by
+    row, max |err| <= 2e-2; every output finite."""
+    q, k, v = wl.attention_inputs(w)
+    out = run_fused(w, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"))
+    assert bool(torch.isfinite(out).all())
+    rows = sample_rows(w)
+    got = np.stack([to64(out[b, h, i]) for (b, h, i) in rows])
+    want = oracle_rows(orc, w, q, k, v, rows)
+    assert np.abs(got - want).max() <= BF16_TOL
+
+
+EDGE_CASES = [
+    # (B, H, Sq, Sk, D, dtype, layout, rot, q_off, k_off, causal)
+    (2, 3, 200, 200, 64, "bf16", "neox", 64, 0, 0, True),       # ragged tails, several tiles
+    (1, 2, 77, 333, 64, "bf16", "gptj", 64, 0, 0, False),       # non-causal, rectangular
+    (1, 2, 150, 220, 128, "bf16", "neox", 128, 100, 30, True),  # offset mask, D=128
+    (1, 1, 1, 1, 64, "bf16", "gptj", 64, 0, 0, True),           # one query, one key
+    (1, 2, 1, 300, 128, "bf16", "neox", 128, 299, 0, True),     # decode-like single query
+    (1, 2, 130, 130, 64, "bf16", "neox", 32, 0, 0, True),       # partial rotation NeoX
+    (1, 2, 130, 130, 128, "bf16", "gptj", 64, 5, 5, True),      # partial rotation GPT-J
+    (1, 2, 190, 190, 64, "bf16", "neox", 0, 0, 0, True),        # no rotation
+    (1, 2, 100, 257, 128, "f32", "neox", 128, 300, 0, True),    # fp32, offset
+    (2, 2, 70, 70, 64, "f32", "gptj", 32, 0, 0, True),          # fp32 partial
+    (1, 1, 65, 65, 128, "f32", "gptj", 0, 0, 0, False),         # fp32, no rotation
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_edge_cases_full(orc, case):
+    B, H, Sq, Sk, D, dtype, layout, rot, qo, ko, causal = case
+    w = wl.AttentionWorkload("edge", B, H, Sq, Sk, D, dtype, 1234 + Sq, layout, base=1e4,
+                             rot_dim=rot, q_off=qo, k_off=ko, causal=causal)
+    q, k, v = wl.attention_inputs(w)
+    got = to64(run_fused(w, to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)))
+    want = orc.attention(q, k, v, q_off=qo, k_off=ko, rot_dim=rot, base=w.base, layout=layout,
+                         causal=causal)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= (BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
+def test_fused_deterministic_and_unfused_agree():
+    """Two runs are bit-identical; the fused kernel agrees with the unfused
+    path (rope_apply on copies of Q and K, then the kernel with rotation
+    off) within the bf16 bar."""
+    w = wl.SWEEP_BF16[0]
+    q, k, v = (to_dev(a, "bf16") for a in wl.attention_inputs(w))
+    a = run_fused(w, q, k, v)
+    b = run_fused(w, q, k, v)
+    assert torch.equal(a, b)
+    c, s = tables(w.base, w.rot, w.table_rows)
+    T = w.Sq
+    qr = q.clone().permute(0, 2, 1, 3).reshape(T, w.H, w.D).contiguous()
+    kr = k.clone().permute(0, 2, 1, 3).reshape(T, w.H, w.D).contiguous()
+    pos = torch.arange(T, dtype=torch.int32, device=DEV)
+    api.rope_apply(qr, kr, pos, c, s, layout=w.layout)
+    qr = qr.reshape(1, T, w.H, w.D).permute(0, 2, 1, 3).contiguous()
+    kr = kr.reshape(1, T, w.H, w.D).permute(0, 2, 1, 3).contiguous()
+    u = run_fused(w, qr, kr, v, rot=0)
+    assert float((a.float() - u.float()).abs().max()) <= BF16_TOL
