@@ -90,15 +90,21 @@ def recorded_traffic(profile: str, source: str):
 def time_launches(torch, launch, steps, warmup, stream, rotate=None):
     """Warm up, then time `steps` launches: wall time between device
     synchronisations and per-launch HIP event durations on `stream`."""
+    def run(i):
+        if rotate:
+            rotate(i)
+        else:
+            launch()
+
     for i in range(warmup):
-        (rotate(i) if rotate else launch)()
+        run(i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0 = time.perf_counter()
     for i, (a, b) in enumerate(evs):
         a.record(stream)
-        (rotate(i) if rotate else launch)()
+        run(i)
         b.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
