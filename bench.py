@@ -65,6 +65,8 @@ def parse_args():
                     help="restrict the timed kernels (for profiler runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every attention workload (printed to stderr)")
+    ap.add_argument("--balance", action="store_true",
+                    help="pass a workspace: balanced (split query tile) schedule")
     return ap.parse_args()
 
 
@@ -112,13 +114,13 @@ def time_launches(torch, launch, steps, warmup, stream, rotate=None):
     return wall_ms / steps, sum(durs) / len(durs), durs
 
 
-def bench_fused(torch, api, wl, w, steps, warmup):
+def bench_fused(torch, api, wl, w, steps, warmup, balance=False):
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in wl.attention_inputs(w))
     cos, sin = api.tables_build(w.base, w.rot, w.table_rows, device=dev)
     out = torch.empty_like(q)
     launch = api.prepare_flash_attn_fwd(q, k, v, out, cos, sin, w.q_off, w.k_off, w.rot, w.layout,
-                                        w.causal)
+                                        w.causal, workspace="auto" if balance else None)
     stream = torch.cuda.current_stream(dev)
     ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
     return dict(q=q, k=k, v=v, cos=cos, sin=sin, out=out, ms_step=ms_step, kernel_ms=kernel_ms,
@@ -245,7 +247,7 @@ def main():
                          "accumulate": "fp32", "device": torch.cuda.get_device_name(0)}}
 
     if args.only in ("all", "fused"):
-        r = bench_fused(torch, api, wl, w, args.steps, args.warmup)
+        r = bench_fused(torch, api, wl, w, args.steps, args.warmup, balance=args.balance)
         flops = w.flops()
         value = flops / (r["ms_step"] * 1e-3) / 1e12
         achieved = flops / (r["kernel_ms"] * 1e-3) / 1e12
@@ -272,7 +274,7 @@ def main():
         for x in wl.ATTENTION_WORKLOADS:
             if x.dtype != "bf16":
                 continue
-            rx = bench_fused(torch, api, wl, x, args.steps, args.warmup)
+            rx = bench_fused(torch, api, wl, x, args.steps, args.warmup, balance=args.balance)
             tf = x.flops() / (rx["kernel_ms"] * 1e-3) / 1e12
             sys.stderr.write(f"sweep {x.name:55s} kernel {rx['kernel_ms'] * 1e3:9.2f} us  "
                              f"{tf:8.1f} TFLOP/s  {tf / PEAK_BF16_TFLOPS * 100:5.1f}% of peak\n")

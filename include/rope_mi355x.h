@@ -148,13 +148,35 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  * Requires 16-byte-aligned q, k, v, o (else ROPE_ERR_ALIGN).
  * Accumulation and softmax are fp32; for ROPE_BF16 the rotated Q/K and the
  * probabilities enter the matrix cores rounded to bf16.
+ *
+ *   workspace   optional device scratch, workspace_bytes long, 16-byte
+ *               aligned, contents irrelevant.  With at least
+ *               rope_flash_attn_workspace_size() bytes, causal workloads
+ *               whose query tiles see very unequal key counts are cut into
+ *               equal shares of work across the GPU; a query tile cut
+ *               between shares leaves fp32 partial states (output rows,
+ *               running max and sum) in the workspace, and a second kernel
+ *               enqueued right after on the same stream merges them.  Calls
+ *               that share one workspace must not run concurrently.
+ *               NULL / too small: one workgroup per query tile (same
+ *               result up to floating-point rounding order).
  */
 int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
                         int B, int H, int64_t Sq, int64_t Sk, int head_dim,
                         int64_t q_pos_offset, int64_t k_pos_offset,
                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
                         int rot_dim, int layout, int causal, float softmax_scale,
-                        int dtype, void *stream);
+                        int dtype, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * rope_flash_attn_workspace_size -- bytes of workspace rope_flash_attn_fwd
+ * can use for these shapes on the current device (0: it would use none).
+ * Returns minus a status code for arguments rope_flash_attn_fwd would reject
+ * on shape grounds.  Makes no device allocation.
+ */
+int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int head_dim,
+                                       int64_t q_pos_offset, int64_t k_pos_offset, int causal,
+                                       int dtype);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,8 @@ BF16, F32 = 0, 1
 OK, ERR_NULL, ERR_SHAPE, ERR_BASE, ERR_UNSUPPORTED, ERR_EMPTY_ROW, ERR_TABLE_RANGE, ERR_HIP, ERR_ALIGN = range(9)
 
 # every symbol include/rope_mi355x.h declares
-EXPORTS = ("rope_status_str", "rope_tables_build", "rope_apply", "rope_flash_attn_fwd")
+EXPORTS = ("rope_status_str", "rope_tables_build", "rope_apply", "rope_flash_attn_fwd",
+           "rope_flash_attn_workspace_size")
 
 _lib = None
 
@@ -38,8 +39,10 @@ def load() -> ctypes.CDLL:
                                i32, i32, i32, i32, vp]
     lib.rope_apply.restype = i32
     lib.rope_flash_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i32, i64, i64,
-                                        vp, vp, i64, i32, i32, i32, f32, i32, vp]
+                                        vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     lib.rope_flash_attn_fwd.restype = i32
+    lib.rope_flash_attn_workspace_size.argtypes = [i32, i32, i64, i64, i32, i64, i64, i32, i32]
+    lib.rope_flash_attn_workspace_size.restype = i64
     _lib = lib
     return lib
 

@@ -102,15 +102,42 @@ def rope_apply(q: torch.Tensor | None, k: torch.Tensor | None, positions: torch.
            "rope_apply")
 
 
+_WORKSPACES: dict = {}
+
+
+def workspace_for(q: torch.Tensor, Sk: int, q_pos_offset: int, k_pos_offset: int,
+                  causal: bool) -> torch.Tensor | None:
+    """Workspace for the balanced schedule of this forward, cached per device
+    and grown on demand (None when the library would use none).  Calls
+    sharing it must be serialised, which holds on one stream."""
+    lib = _lib.load()
+    B, H, Sq, D = q.shape
+    need = lib.rope_flash_attn_workspace_size(B, H, Sq, Sk, D, int(q_pos_offset), int(k_pos_offset),
+                                              int(bool(causal)), _dtype(q))
+    if need < 0:
+        raise RopeError(-need, "rope_flash_attn_workspace_size")
+    if need == 0:
+        return None
+    key = q.device
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,
                    q_pos_offset: int = 0, k_pos_offset: int = 0, rot_dim: int | None = None,
                    layout="neox", causal: bool = True, softmax_scale: float = 0.0,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
+                   out: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
     """Fused RoPE + attention forward on ``[B, H, S, D]`` tensors.
 
     ``rot_dim=0`` (or no tables) runs plain attention.  Returns ``out``
-    (allocated like ``q`` when not given)."""
+    (allocated like ``q`` when not given).  ``workspace``: None (one
+    workgroup per query tile, the default), "auto" (the balanced schedule
+    with a cached buffer sized by the library) or a uint8 tensor of at least
+    the library's requested size."""
     lib = _lib.load()
     _require_cuda(q, k, v, cos, sin)
     for t in (q, k, v):
@@ -135,10 +162,14 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    if isinstance(workspace, str):
+        workspace = workspace_for(q, Sk, q_pos_offset, k_pos_offset, causal)
+    wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (None, 0)
     _check(lib.rope_flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    B, H, Sq, Sk, D, int(q_pos_offset), int(k_pos_offset),
                                    cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),
-                                   float(softmax_scale), _dtype(q), _stream(q)),
+                                   float(softmax_scale), _dtype(q), wp, wb, _stream(q)),
            "rope_flash_attn_fwd")
     return out
 
@@ -149,19 +180,23 @@ def default_scale(head_dim: int) -> float:
 
 def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int = 0,
                            k_pos_offset: int = 0, rot_dim: int | None = None, layout="neox",
-                           causal: bool = True, softmax_scale: float = 0.0):
+                           causal: bool = True, softmax_scale: float = 0.0, workspace=None):
     """Validate once and return a zero-argument callable that enqueues the
     fused forward on fixed buffers (for repeated launches in timing loops;
     the buffers must stay alive and unchanged in shape)."""
+    if isinstance(workspace, str):
+        workspace = workspace_for(q, k.shape[2], q_pos_offset, k_pos_offset, causal)
     flash_attn_fwd(q, k, v, cos, sin, q_pos_offset, k_pos_offset, rot_dim, layout, causal,
-                   softmax_scale, out)   # validates and runs once
+                   softmax_scale, out, workspace)   # validates and runs once
     lib = _lib.load()
     B, H, Sq, D = q.shape
     rot = (D if cos is not None else 0) if rot_dim is None else int(rot_dim)
+    wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (None, 0)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, k.shape[2], D,
             int(q_pos_offset), int(k_pos_offset), cos.data_ptr() if rot else None,
             sin.data_ptr() if rot else None, cos.shape[0] if rot else 0, rot, _layout(layout),
-            int(bool(causal)), float(softmax_scale), _dtype(q), _stream(q))
+            int(bool(causal)), float(softmax_scale), _dtype(q), wp, wb, _stream(q))
     fn = lib.rope_flash_attn_fwd
 
     def launch():

@@ -101,12 +101,45 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
                                                                                      : ROPE_ERR_HIP;
 }
 
+namespace {
+
+// Shape checks shared by the forward and its workspace query.
+int check_fwd_shape(int B, int H, int64_t Sq, int64_t Sk, int head_dim, int64_t q_pos_offset,
+                    int64_t k_pos_offset, int causal, int dtype)
+{
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ROPE_ERR_SHAPE;
+    if (Sq > 2147483647 || Sk > 2147483647) return ROPE_ERR_SHAPE;
+    if (head_dim < 2 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (q_pos_offset < 0 || k_pos_offset < 0) return ROPE_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return ROPE_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return ROPE_ERR_UNSUPPORTED;
+    const int64_t tiles = (Sq + 63) / 64;
+    if ((int64_t)B * H > kMaxGrid || (int64_t)B * H * tiles > kMaxGrid) return ROPE_ERR_SHAPE;
+    if (causal && q_pos_offset < k_pos_offset) return ROPE_ERR_EMPTY_ROW;
+    return ROPE_OK;
+}
+
+}  // namespace
+
+int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int head_dim,
+                                       int64_t q_pos_offset, int64_t k_pos_offset, int causal,
+                                       int dtype)
+{
+    const int st = check_fwd_shape(B, H, Sq, Sk, head_dim, q_pos_offset, k_pos_offset, causal, dtype);
+    if (st != ROPE_OK) return -st;
+    if (dtype != ROPE_BF16) return 0;
+    FlashArgs a = {};
+    a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
+    a.q_off = q_pos_offset; a.k_off = k_pos_offset; a.causal = causal ? 1 : 0; a.dtype = dtype;
+    return rope_flash_bf16_workspace_bytes(a);
+}
+
 int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
                         int B, int H, int64_t Sq, int64_t Sk, int head_dim,
                         int64_t q_pos_offset, int64_t k_pos_offset,
                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
                         int rot_dim, int layout, int causal, float softmax_scale,
-                        int dtype, void *stream)
+                        int dtype, void *workspace, int64_t workspace_bytes, void *stream)
 {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ROPE_ERR_SHAPE;
     if (Sq > 2147483647 || Sk > 2147483647) return ROPE_ERR_SHAPE;
@@ -132,6 +165,8 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
     }
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
         return ROPE_ERR_ALIGN;
+    if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return ROPE_ERR_SHAPE;
+    if (workspace && !aligned(workspace, 16)) return ROPE_ERR_ALIGN;
 
     FlashArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
@@ -141,6 +176,8 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
     a.rot_dim = rot_dim; a.layout = layout; a.causal = causal ? 1 : 0;
     a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     a.dtype = dtype;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace ? workspace_bytes : 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int rc = dtype == ROPE_BF16 ? rope_launch_flash_bf16(a, s) : rope_launch_flash_f32(a, s);
     return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;

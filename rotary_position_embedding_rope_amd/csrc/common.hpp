@@ -68,6 +68,11 @@ struct FlashArgs {
     int rot_dim, layout, causal;
     float scale;   // already resolved (> 0)
     int dtype;
+    void *workspace;           // zero-filled scratch for the balanced schedule, or NULL
+    int64_t workspace_bytes;
 };
 int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream);
+// Workspace bytes the bf16 launch would use for these shapes on the current
+// device (0: the launch needs none).
+int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a);
 int rope_launch_flash_f32(const FlashArgs &a, hipStream_t stream);

@@ -11,36 +11,47 @@
 // (section 6's offset mask).  Rotation pairs and formula: "Write Triton Rope
 // Kernel", "Required reasoning process" steps 1 and 6.
 //
-// Work decomposition (FlashAttention-2 style, section 7 of the same page: a
+// Work decomposition (FlashAttention-2 style, the same page's section 7: a
 // query-block outer loop, key/value inner loop, output written once):
-//   * one 256-thread workgroup per (batch*head, 128-query tile); each of its
-//     4 waves owns 32 query rows;
-//   * the key loop walks 64-key tiles, stopping at the last tile a query of
-//     the workgroup can see; tiles past a wave's last query are skipped by
-//     that wave; the element mask runs only on tiles straddling the diagonal
-//     or the ragged end;
-//   * heaviest query tiles are dispatched first and all tiles of one head are
-//     issued to the same XCD (block index modulo the head count), so a head's
-//     K/V stay in one L2.
+//   * a workgroup owns a 128-query tile of one (batch, head); NG key groups
+//     of 4 waves each (NG = 1 or 2) walk interleaved 64-key tiles of that
+//     query tile and are merged through LDS at the end.  With NG = 2 every
+//     SIMD runs two waves, so one wave's softmax overlaps the other's
+//     matrix-core work;
+//   * in each group a wave owns 32 query rows; the key loop stops at the
+//     last tile a query of the workgroup can see, tiles past a wave's last
+//     query are skipped by that wave, and the element mask runs only on
+//     tiles straddling the diagonal or the ragged end;
+//   * heaviest query tiles are dispatched first, and all tiles of one head
+//     go to one XCD (block index modulo the head count), so a head's K/V
+//     stay in one L2.
 //
-// Data path per workgroup:
+// Data path of a group:
 //   * Q: each lane loads its query row's dims straight into the matrix-core
-//     operand layout, rotates in fp32 at q_off + i, rounds to bf16 and keeps
-//     the tile in registers for the whole key loop.
-//   * K: every visited tile is loaded once from HBM by all 256 threads,
-//     rotated in fp32 at its key positions, rounded to bf16 and written to
-//     LDS -- each key tile is rotated once per staging and no rotated copy
-//     ever reaches HBM ("RoPE + PoPE Attention Kernels": recompute instead
-//     of materialising rotated [B,H,S,D] tensors).  V is staged unrotated,
-//     transposed, into LDS.  Two LDS buffers: tile t+1 is fetched into
-//     registers while tile t is consumed, then written to the other buffer;
-//     one barrier per tile.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane owns one query column,
-//     so the row max / row sum of the softmax are 32 in-lane values plus one
-//     exchange with the lane 32 apart.  The probabilities come out of the
-//     accumulator already in the B-operand layout of the next product:
-//     O^T = V^T P^T needs no LDS round trip for P.
-//   * Softmax in base 2 with scale*log2(e) applied to the fp32 scores.
+//     operand layout, rotates them in fp32 at q_off + i, multiplies by
+//     scale*log2(e), rounds to bf16 and keeps the tile in registers.
+//   * K: every visited tile is loaded from HBM once, rotated in fp32 at its
+//     key positions, rounded to bf16 and written to LDS -- rotated once per
+//     staging, never written back to HBM ("RoPE + PoPE Attention Kernels":
+//     recompute instead of materialising rotated [B,H,S,D] tensors).  V is
+//     copied unrotated, row-major, to LDS.  Two LDS buffers per group: tile
+//     t+NG is fetched into registers while tile t is consumed, then written
+//     to the other buffer; one barrier per tile.
+//   * S' = K Q'^T - m on v_mfma_f32_32x32x16_bf16, the accumulator seeded
+//     with the running max: a lane owns one query column, so row max / row
+//     sum are in-lane plus one v_permlane32_swap, and the exponent needs no
+//     per-score arithmetic: P = exp2(S').
+//   * The max is lazily refreshed: only when a row's new scores exceed its
+//     reference by more than 2^8 (or on its first visible key) is the
+//     reference raised and O, l rescaled -- exact in real arithmetic since
+//     numerator and denominator share the reference.
+//   * P is rounded to bf16; its row sums use v_dot2_f32_bf16 on those same
+//     bf16 values, so numerator and denominator see identical weights.  P
+//     leaves the accumulator already in the B-operand layout of
+//     O^T = V^T P^T; the V^T operand comes from ds_read_b64_tr_b16
+//     transposing reads of the row-major V tile.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace {
@@ -49,11 +60,14 @@ using rope::bf16x8_t;
 using rope::f32x16_t;
 using rope::pack_bf16x2;
 
-constexpr int NWAVES = 4;
-constexpr int BM = 32 * NWAVES;   // queries per workgroup
-constexpr int BN = 64;            // keys per tile
-constexpr int KPAD = 8;           // K LDS row pitch = D + KPAD bf16 (16-byte aligned rows)
-constexpr int VPAD = 4;           // V^T LDS row pitch = BN + VPAD bf16 (8-byte aligned rows)
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int WAVES_PER_GROUP = 4;
+constexpr int BM = 32 * WAVES_PER_GROUP;   // queries per workgroup
+constexpr int KPAD = 8;                     // K LDS row pitch = D + 8 bf16
+constexpr int VP = 160;                     // V LDS row pitch (bf16): 80 dwords, == 16 mod 64 banks
+constexpr float LAZY_THRESHOLD = 8.0f;      // log2 headroom before the reference max is raised
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -64,8 +78,83 @@ struct Params {
     int rot_dim;
     float sl2;          // softmax scale * log2(e)
     int causal;
-    int n_qtiles;
+    int64_t n_qtiles;
+    int64_t n_kt;       // key tiles
+    // Key tiles visited by query tile t: causal and t < n_qtiles - 1:
+    // min(n_kt, va * t + vb); the last query tile: v_last; non-causal: n_kt.
+    int64_t va, vb, v_last;
+    // Balanced schedule (sk_G > 0): the BH * u_head (query tile, key tile)
+    // visits are cut into sk_G equal contiguous shares, one per workgroup.
+    int sk_G;
+    int64_t u_head;     // visits per (batch, head)
+    // xcd_order: heads are laid out XCD by XCD in the visit order (head
+    // slot hs = (bh % 8) * (BH / 8) + bh / 8) and block b takes share
+    // (b % 8) * (sk_G / 8) + b / 8, so blocks that the dispatcher sends to one
+    // XCD (b mod 8) work on that XCD's heads and their K/V share one L2.
+    int xcd_order;
+    float *ws_part;     // partial states: [sk_G][2 slots][4 waves][NC][64 lanes]
 };
+
+// ---- schedule arithmetic (host and device) ----
+
+__host__ __device__ inline int64_t tile_visits(const Params &p, int64_t t)
+{
+    if (!p.causal) return p.n_kt;
+    if (t == p.n_qtiles - 1) return p.v_last;
+    const int64_t v = p.va * t + p.vb;
+    return v < p.n_kt ? v : p.n_kt;
+}
+
+// Sum of tile_visits(t) over t < T, in closed form (T <= n_qtiles).
+__host__ __device__ inline int64_t visits_before(const Params &p, int64_t T)
+{
+    if (!p.causal) return T * p.n_kt;
+    const int64_t tf = T < p.n_qtiles - 1 ? T : p.n_qtiles - 1;   // tiles on the linear law
+    const int64_t ts = p.n_kt <= p.vb ? 0 : (p.n_kt - p.vb + p.va - 1) / p.va;  // first saturated tile
+    const int64_t m = tf < ts ? tf : ts;
+    int64_t s = p.va * m * (m - 1) / 2 + p.vb * m + (tf - m) * p.n_kt;
+    if (T == p.n_qtiles) s += p.v_last;
+    return s;
+}
+
+// Largest query tile T with visits_before(T) <= r (r < u_head).
+__device__ inline int64_t find_tile(const Params &p, int64_t r)
+{
+    int64_t lo = 0, hi = p.n_qtiles - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (visits_before(p, mid) <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ inline int64_t share_start(int64_t w, int64_t U, int G) { return (w * U) / G; }
+
+__device__ inline int head_of_slot(const Params &p, int64_t hs)
+{
+    if (!p.xcd_order) return (int)hs;
+    const int per = p.BH / 8;
+    return (int)((hs % per) * 8 + hs / per);
+}
+__device__ inline int64_t slot_of_head(const Params &p, int bh)
+{
+    if (!p.xcd_order) return bh;
+    return (int64_t)(bh % 8) * (p.BH / 8) + bh / 8;
+}
+__device__ inline int64_t share_of_block(const Params &p, int64_t b)
+{
+    if (!p.xcd_order) return b;
+    return (b % 8) * (p.sk_G / 8) + b / 8;
+}
+
+// The workgroup whose share contains visit x.
+__device__ inline int64_t share_of(int64_t x, int64_t U, int G)
+{
+    int64_t w = (x * G) / U;   // share_start(w) <= x
+    while (w + 1 < G && share_start(w + 1, U, G) <= x) ++w;
+    return w;
+}
 
 __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8])
 {
@@ -83,8 +172,7 @@ __device__ __forceinline__ uint4 pack8(const float (&x)[8])
 }
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
-// Rotate the pair (a[i], b[i]) by (c[i], s[i]) for i < N: a' = a c - b s,
-// b' = a s + b c.
+// Rotate pairs (a[i], b[i]) by (c[i], s[i]): a' = a c - b s, b' = a s + b c.
 template <int N>
 __device__ __forceinline__ void rotate_pairs(float *a, float *b, const float *c, const float *s)
 {
@@ -96,368 +184,681 @@ __device__ __forceinline__ void rotate_pairs(float *a, float *b, const float *c,
     }
 }
 
+// Reductions with the lane 32 apart (the other half of the same query
+// column).  v_permlane32_swap leaves {own, partner} in its two results on
+// every lane, so the symmetric max / sum is the same on both halves.
+__device__ __forceinline__ float max_with_partner(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Per-thread staging plan for K tiles (fixed across tiles).
-//   NeoX: a slot is two 8-dim chunks -- either a rotated pair of chunks
-//         (lo at 8c, hi at 8c + rot/2) or two copied chunks past rot_dim.
-//         D/16 slots per key row.
+//   NeoX: a slot is two 8-dim chunks -- a rotated pair of chunks (lo at 8c,
+//         hi at 8c + rot/2) or two copied chunks past rot_dim.  D/16 slots
+//         per key row.
 //   GPT-J / no rotation: a slot is one 8-dim chunk, rotated (whole pairs)
 //         or copied.  D/8 slots per key row.
-template <int D, int LAYOUT, bool ROT>
+template <int D, int LAYOUT, bool ROT, int BN>
 struct KPlan {
     static constexpr bool NEOX_SLOT = ROT && LAYOUT == 0;
     static constexpr int SLOTS_PER_ROW = NEOX_SLOT ? D / 16 : D / 8;
-    static constexpr int ITEMS = BN * SLOTS_PER_ROW / (NWAVES * 64);
+    static constexpr int SLOTS = BN * SLOTS_PER_ROW;
+    static constexpr int ITEMS = (SLOTS + 255) / 256;   // per thread (the last may be empty)
 };
 
-template <int D, int LAYOUT, bool ROT>
-__global__ __launch_bounds__(256) void flash_fwd_bf16_kernel(Params p)
+template <int D, int BN>
+struct Lds {
+    static constexpr int KP = D + KPAD;
+    static constexpr int K_ELEMS = BN * KP;
+    static constexpr int V_ELEMS = BN * VP;
+    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;   // one K + one V tile
+};
+
+// D: head dim; BN: keys per tile (32 or 64); NG: key groups per workgroup.
+template <int D, int LAYOUT, bool ROT, int NG, int BN>
+__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2)))
+void flash_fwd_bf16_kernel(Params p)
 {
-    using Plan = KPlan<D, LAYOUT, ROT>;
-    constexpr int KP = D + KPAD;
-    constexpr int VP = BN + VPAD;
+    using Plan = KPlan<D, LAYOUT, ROT, BN>;
+    using L = Lds<D, BN>;
+    constexpr int NKB = BN / 32;                    // 32-key blocks per tile
+    constexpr int KP = L::KP;
     constexpr int KI = Plan::ITEMS;                 // K slots per thread per tile
-    constexpr int VI = (BN / 2) * (D / 8) / 256;    // V items per thread per tile
+    constexpr int VSLOTS = BN * (D / 8);            // V 16-byte chunks per tile
+    constexpr int VI = (VSLOTS + 255) / 256;        // per thread (the last may be empty)
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
+    constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+    // [group][buffer][K tile | V tile]
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NG * 2 * L::BUF_ELEMS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int group = tid >> 8;
+    const int gtid = tid & 255;                     // thread index inside the group
+    const int lane = tid & 63;
+    const int wave = gtid >> 6;                     // wave inside the group
     const int l32 = lane & 31, hh = lane >> 5;
-
-    const int bh = blockIdx.x % p.BH;
-    const int rank = blockIdx.x / p.BH;
-    const int qtile = p.causal ? p.n_qtiles - 1 - rank : rank;
-    const int64_t q0 = (int64_t)qtile * BM;
-    const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
-    const uint16_t *kh = p.k + (int64_t)bh * p.Sk * D;
-    const uint16_t *vh = p.v + (int64_t)bh * p.Sk * D;
     const int rh = p.rot_dim / 2;   // table row stride
 
-    // ---------------- Q: load, rotate, keep as MFMA B operand ----------------
-    const int64_t qrow = q0 + wave * 32 + l32;
-    const bool qvalid = qrow < p.Sq;
-    bf16x8_t qf[DT];
-    {
-        float qv[DT][8];
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (qvalid) w = *reinterpret_cast<const uint4 *>(qh + qrow * D + 16 * t + 8 * hh);
-            unpack8(w, qv[t]);
-        }
-        if constexpr (ROT) {
-            if (qvalid) {
-                const int64_t pos = p.q_off + qrow;
-                const float *crow = p.cos_tab + pos * rh;
-                const float *srow = p.sin_tab + pos * rh;
-                if constexpr (LAYOUT == 0) {
-                    // lane holds dims 16t + 8hh + s; partner of 16t+8hh+s is
-                    // 16(t + rot/32) + 8hh + s, in the same lane.
-                    // (rot_dim is a multiple of 32, so tr = rot_dim/32 <= DT/2.)
-                    const int tr = p.rot_dim / 32;
-#pragma unroll
-                    for (int t = 0; t < DT / 2; ++t) {
-                        if (t < tr) {
-                            const int f0 = 16 * t + 8 * hh;
-                            float c[8], s[8];
-                            *reinterpret_cast<float4 *>(c) = ld4(crow + f0);
-                            *reinterpret_cast<float4 *>(c + 4) = ld4(crow + f0 + 4);
-                            *reinterpret_cast<float4 *>(s) = ld4(srow + f0);
-                            *reinterpret_cast<float4 *>(s + 4) = ld4(srow + f0 + 4);
-                            // the partner chunk is t + tr; registers are only
-                            // indexed with compile-time constants
-#pragma unroll
-                            for (int u = 1; u <= DT / 2; ++u)
-                                if (u == tr) rotate_pairs<8>(qv[t], qv[t + u], c, s);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int t = 0; t < DT; ++t) {
-                        if (16 * t < p.rot_dim) {
-                            const int f0 = 8 * t + 4 * hh;
-                            float c[4], s[4], a[4], b[4];
-                            *reinterpret_cast<float4 *>(c) = ld4(crow + f0);
-                            *reinterpret_cast<float4 *>(s) = ld4(srow + f0);
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) { a[u] = qv[t][2 * u]; b[u] = qv[t][2 * u + 1]; }
-                            rotate_pairs<4>(a, b, c, s);
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) { qv[t][2 * u] = a[u]; qv[t][2 * u + 1] = b[u]; }
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) qf[t][s] = (__bf16)qv[t][s];
-        }
-    }
-
-    // ---------------- key loop bounds ----------------
-    const int64_t q_valid = p.Sq - q0 < BM ? p.Sq - q0 : BM;
-    const int64_t n_kt = (p.Sk + BN - 1) / BN;
-    int64_t kt_end = n_kt;
-    if (p.causal) {
-        const int64_t jmax = p.q_off + q0 + q_valid - 1 - p.k_off;
-        kt_end = jmax / BN + 1 < n_kt ? jmax / BN + 1 : n_kt;
-    }
-    // this wave's query range
-    const int64_t wq0 = q0 + wave * 32;
-    const int64_t wq_last = (wq0 + 31 < p.Sq ? wq0 + 31 : p.Sq - 1);
-    const bool wave_has_rows = wq0 < p.Sq;
-
-    // ---------------- staging plan ----------------
-    int k_row[KI], k_mode[KI], k_d0[KI], k_d1[KI];
+    // ---------------- staging plan (fixed for the whole launch) ----------------
+    // k_mode: -1 no slot, 0 copy, 1 NeoX rotate (lo, hi), 2 GPT-J rotate.
+    // k_o0/k_o1 = element offsets of the two chunks inside a K tile, k_to =
+    // offset of the cos/sin slice inside the tile's block of table rows.
+    int k_row[KI], k_mode[KI], k_o0[KI], k_o1[KI], k_to[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-        const int item = tid + 256 * i;
+        const int item = gtid + 256 * i;
         const int row = item / Plan::SLOTS_PER_ROW;
         const int slot = item % Plan::SLOTS_PER_ROW;
+        int d0 = 0, d1 = 0;
         k_row[i] = row;
-        if constexpr (Plan::NEOX_SLOT) {
+        if (item >= Plan::SLOTS) {
+            k_mode[i] = -1;
+        } else if constexpr (Plan::NEOX_SLOT) {
             const int rslots = p.rot_dim / 16;
             if (slot < rslots) {
                 k_mode[i] = 1;                            // rotate (lo, hi)
-                k_d0[i] = 8 * slot;
-                k_d1[i] = 8 * slot + rh;
+                d0 = 8 * slot;
+                d1 = 8 * slot + rh;
             } else {
                 k_mode[i] = 0;                            // copy two chunks
-                k_d0[i] = p.rot_dim + 16 * (slot - rslots);
-                k_d1[i] = k_d0[i] + 8;
+                d0 = p.rot_dim + 16 * (slot - rslots);
+                d1 = d0 + 8;
             }
         } else {
             k_mode[i] = (ROT && 8 * slot < p.rot_dim) ? 2 : 0;
-            k_d0[i] = 8 * slot;
-            k_d1[i] = 0;
+            d0 = 8 * slot;
         }
+        k_o0[i] = row * D + d0;
+        k_o1[i] = row * D + d1;
+        k_to[i] = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
     }
-    int v_kp[VI], v_c[VI];
+    int v_row[VI], v_o[VI], v_l[VI];
+    bool v_ok[VI];
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
-        const int item = tid + 256 * i;
-        v_kp[i] = item / (D / 8);
-        v_c[i] = item % (D / 8);
+        const int item = gtid + 256 * i;
+        v_ok[i] = item < VSLOTS;
+        v_row[i] = item / (D / 8);
+        v_o[i] = v_row[i] * D + 8 * (item % (D / 8));     // global offset inside the tile
+        v_l[i] = v_row[i] * VP + 8 * (item % (D / 8));    // LDS offset
     }
 
-    // prefetch registers
-    uint4 kr0[KI], kr1[KI];
-    float kc[KI][8], ks[KI][8];
-    uint4 vr0[VI], vr1[VI];
+    // V^T operand addressing for ds_read_b64_tr_b16: in each 16-lane group
+    // the source lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving
+    // lane l' then holds V[key0 .. key0+3][dim0 + l'].
+    const int g16 = lane >> 4, lp = lane & 15;
+    const int tr_row = lp >> 2, tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
+    const int tr_key = 4 * (g16 >> 1) + tr_row;   // + 32kb + 16mm (+ 8)
+    const rope::bf16x2_t ones = __builtin_bit_cast(rope::bf16x2_t, 0x3f803f80u);   // (1, 1)
 
-    auto fetch = [&](int64_t kt) {
-        const int64_t j0 = kt * BN;
+    // One segment: key tiles [kb, ke) of query tile `qtile` of head `bh`.
+    // `full` when the segment covers all key tiles the query tile visits;
+    // otherwise its state is merged with the other segments of that query
+    // tile through the workspace (seg_v: global index of its first visit,
+    // w: this workgroup's share index).
+    auto segment = [&](int bh, int64_t qtile, int64_t kb, int64_t ke, bool full, int64_t seg_v,
+                       int64_t w) {
+        const int64_t q0 = qtile * BM;
+        const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
+        const uint16_t *kh = p.k + (int64_t)bh * p.Sk * D;
+        const uint16_t *vh = p.v + (int64_t)bh * p.Sk * D;
+
+        // ---- Q: load, rotate, scale, keep as MFMA B operand ----
+        const int64_t qrow = q0 + wave * 32 + l32;
+        const bool qvalid = qrow < p.Sq;
+        bf16x8_t qf[DT];
+        {
+            float qv[DT][8];
 #pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            const int64_t j = j0 + k_row[i];
-            const bool ok = j < p.Sk;
-            const uint16_t *src = kh + j * D;
-            kr0[i] = ok ? *reinterpret_cast<const uint4 *>(src + k_d0[i]) : make_uint4(0, 0, 0, 0);
-            if constexpr (Plan::NEOX_SLOT)
-                kr1[i] = ok ? *reinterpret_cast<const uint4 *>(src + k_d1[i]) : make_uint4(0, 0, 0, 0);
+            for (int t = 0; t < DT; ++t) {
+                uint4 wv = make_uint4(0, 0, 0, 0);
+                if (qvalid) wv = *reinterpret_cast<const uint4 *>(qh + qrow * D + 16 * t + 8 * hh);
+                unpack8(wv, qv[t]);
+            }
             if constexpr (ROT) {
-                if (ok && k_mode[i] != 0) {
-                    const int64_t pos = p.k_off + j;
-                    const int f0 = LAYOUT == 0 ? k_d0[i] : k_d0[i] / 2;
-                    const float *cr = p.cos_tab + pos * rh + f0;
-                    const float *sr = p.sin_tab + pos * rh + f0;
-                    *reinterpret_cast<float4 *>(kc[i]) = ld4(cr);
-                    *reinterpret_cast<float4 *>(ks[i]) = ld4(sr);
+                if (qvalid) {
+                    const int64_t pos = p.q_off + qrow;
+                    const float *crow = p.cos_tab + pos * rh;
+                    const float *srow = p.sin_tab + pos * rh;
                     if constexpr (LAYOUT == 0) {
-                        *reinterpret_cast<float4 *>(kc[i] + 4) = ld4(cr + 4);
-                        *reinterpret_cast<float4 *>(ks[i] + 4) = ld4(sr + 4);
+                        // lane holds dims 16t + 8hh + s; the partner of
+                        // 16t+8hh+s is 16(t + rot/32) + 8hh + s, in the same
+                        // lane (rot_dim is a multiple of 32: tr <= DT/2).
+                        const int tr = p.rot_dim / 32;
+#pragma unroll
+                        for (int t = 0; t < DT / 2; ++t) {
+                            if (t < tr) {
+                                const int f0 = 16 * t + 8 * hh;
+                                float c[8], s[8];
+                                *reinterpret_cast<float4 *>(c) = ld4(crow + f0);
+                                *reinterpret_cast<float4 *>(c + 4) = ld4(crow + f0 + 4);
+                                *reinterpret_cast<float4 *>(s) = ld4(srow + f0);
+                                *reinterpret_cast<float4 *>(s + 4) = ld4(srow + f0 + 4);
+                                // registers are only indexed with compile-time constants
+#pragma unroll
+                                for (int u = 1; u <= DT / 2; ++u)
+                                    if (u == tr) rotate_pairs<8>(qv[t], qv[t + u], c, s);
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < DT; ++t) {
+                            if (16 * t < p.rot_dim) {
+                                const int f0 = 8 * t + 4 * hh;
+                                float c[4], s[4], a[4], b[4];
+                                *reinterpret_cast<float4 *>(c) = ld4(crow + f0);
+                                *reinterpret_cast<float4 *>(s) = ld4(srow + f0);
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) { a[u] = qv[t][2 * u]; b[u] = qv[t][2 * u + 1]; }
+                                rotate_pairs<4>(a, b, c, s);
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) { qv[t][2 * u] = a[u]; qv[t][2 * u + 1] = b[u]; }
+                            }
+                        }
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < VI; ++i) {
-            const int64_t j = j0 + 2 * v_kp[i];
-            const uint16_t *src = vh + j * D + 8 * v_c[i];
-            vr0[i] = j < p.Sk ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
-            vr1[i] = j + 1 < p.Sk ? *reinterpret_cast<const uint4 *>(src + D) : make_uint4(0, 0, 0, 0);
-        }
-    };
-
-    auto stage = [&](int buf) {
-        uint16_t *kdst = Ks[buf];
+            for (int t = 0; t < DT; ++t) {
 #pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            uint16_t *row = kdst + k_row[i] * KP;
-            if (k_mode[i] == 1) {
-                float lo[8], hi[8];
-                unpack8(kr0[i], lo);
-                unpack8(kr1[i], hi);
-                rotate_pairs<8>(lo, hi, kc[i], ks[i]);
-                *reinterpret_cast<uint4 *>(row + k_d0[i]) = pack8(lo);
-                *reinterpret_cast<uint4 *>(row + k_d1[i]) = pack8(hi);
-            } else if (k_mode[i] == 2) {
-                float x[8], a[4], b[4];
-                unpack8(kr0[i], x);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) { a[u] = x[2 * u]; b[u] = x[2 * u + 1]; }
-                rotate_pairs<4>(a, b, kc[i], ks[i]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) { x[2 * u] = a[u]; x[2 * u + 1] = b[u]; }
-                *reinterpret_cast<uint4 *>(row + k_d0[i]) = pack8(x);
-            } else {
-                *reinterpret_cast<uint4 *>(row + k_d0[i]) = kr0[i];
-                if constexpr (Plan::NEOX_SLOT) *reinterpret_cast<uint4 *>(row + k_d1[i]) = kr1[i];
+                for (int s = 0; s < 8; ++s) qf[t][s] = (__bf16)(qv[t][s] * p.sl2);
             }
         }
-        // V^T: element (dim d, key j) at Vt[d * VP + j]; a thread writes the
-        // two keys (2kp, 2kp+1) of 8 dims as 8 packed dwords.
-        uint16_t *vdst = Vt[buf];
+
+        const int64_t wq0 = q0 + wave * 32;
+        const int64_t wq_last = (wq0 + 31 < p.Sq ? wq0 + 31 : p.Sq - 1);
+        const bool wave_has_rows = wq0 < p.Sq;
+
+        uint4 kr0[KI], kr1[KI];
+        float kc[KI][8], ks[KI][8];
+        uint4 vr[VI];
+
+        // Global loads of one key tile into registers: uniform per-tile base
+        // pointers, fixed 32-bit per-thread offsets; row bounds are checked
+        // only on the ragged last tile.
+        auto fetch = [&](int64_t kt) {
+            const int64_t j0 = kt * BN;
+            const uint16_t *kbase = kh + j0 * D;
+            const uint16_t *vbase = vh + j0 * D;
+            const int64_t left = p.Sk - j0;
+            const int rows = left < BN ? (int)left : BN;
+            const bool fullt = rows == BN;
 #pragma unroll
-        for (int i = 0; i < VI; ++i) {
-            const uint32_t a[4] = {vr0[i].x, vr0[i].y, vr0[i].z, vr0[i].w};
-            const uint32_t b[4] = {vr1[i].x, vr1[i].y, vr1[i].z, vr1[i].w};
-            uint16_t *col = vdst + (8 * v_c[i]) * VP + 2 * v_kp[i];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                *reinterpret_cast<uint32_t *>(col + (2 * u) * VP) = (a[u] & 0xffffu) | (b[u] << 16);
-                *reinterpret_cast<uint32_t *>(col + (2 * u + 1) * VP) = (a[u] >> 16) | (b[u] & 0xffff0000u);
+            for (int i = 0; i < KI; ++i) {
+                if (k_mode[i] < 0) continue;
+                const bool ok = fullt || k_row[i] < rows;
+                kr0[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + k_o0[i]) : make_uint4(0, 0, 0, 0);
+                if constexpr (Plan::NEOX_SLOT)
+                    kr1[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + k_o1[i]) : make_uint4(0, 0, 0, 0);
+                if constexpr (ROT) {
+                    if (ok && k_mode[i] != 0) {
+                        const float *cr = p.cos_tab + (p.k_off + j0) * rh + k_to[i];
+                        const float *sr = p.sin_tab + (p.k_off + j0) * rh + k_to[i];
+                        *reinterpret_cast<float4 *>(kc[i]) = ld4(cr);
+                        *reinterpret_cast<float4 *>(ks[i]) = ld4(sr);
+                        if constexpr (LAYOUT == 0) {
+                            *reinterpret_cast<float4 *>(kc[i] + 4) = ld4(cr + 4);
+                            *reinterpret_cast<float4 *>(ks[i] + 4) = ld4(sr + 4);
+                        }
+                    }
+                }
             }
-        }
-    };
-
-    // ---------------- running state ----------------
-    f32x16_t oacc[DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) oacc[b] = (f32x16_t){};
-    float m_run = -INFINITY;   // running max (scaled, base 2), same in lanes l and l^32
-    float l_part = 0.f;        // this lane's share of the running denominator
+            for (int i = 0; i < VI; ++i) {
+                const bool ok = v_ok[i] && (fullt || v_row[i] < rows);
+                vr[i] = ok ? *reinterpret_cast<const uint4 *>(vbase + v_o[i]) : make_uint4(0, 0, 0, 0);
+            }
+        };
 
-    fetch(0);
-    stage(0);
-
-    for (int64_t kt = 0; kt < kt_end; ++kt) {
-        const int buf = (int)(kt & 1);
-        __syncthreads();   // tile kt staged; tile kt-1 fully consumed
-        const bool more = kt + 1 < kt_end;
-        if (more) fetch(kt + 1);
-
-        const int64_t j0 = kt * BN;
-        const bool wave_active =
-            wave_has_rows && (!p.causal || p.k_off + j0 <= p.q_off + wq_last);
-        if (wave_active) {
-            const uint16_t *kb_lds = Ks[buf];
-            const uint16_t *vt_lds = Vt[buf];
-            // S^T = K Q^T: two 32-key blocks x 32 queries.
-            f32x16_t sacc[2];
+        // Rotate the fetched K tile, round to bf16 and write K and V to LDS.
+        auto stage = [&](int buf) {
+            uint16_t *kdst = lds + (group * 2 + buf) * L::BUF_ELEMS;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sacc[kb] = (f32x16_t){};
+            for (int i = 0; i < KI; ++i) {
+                if (k_mode[i] < 0) continue;
+                // LDS rows have pitch KP; the chunk offsets inside a row are
+                // k_o - k_row * D.
+                uint16_t *row = kdst + k_row[i] * KP - k_row[i] * D;
+                if (k_mode[i] == 1) {
+                    float lo[8], hi[8];
+                    unpack8(kr0[i], lo);
+                    unpack8(kr1[i], hi);
+                    rotate_pairs<8>(lo, hi, kc[i], ks[i]);
+                    *reinterpret_cast<uint4 *>(row + k_o0[i]) = pack8(lo);
+                    *reinterpret_cast<uint4 *>(row + k_o1[i]) = pack8(hi);
+                } else if (k_mode[i] == 2) {
+                    float x[8], a[4], b[4];
+                    unpack8(kr0[i], x);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { a[u] = x[2 * u]; b[u] = x[2 * u + 1]; }
+                    rotate_pairs<4>(a, b, kc[i], ks[i]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { x[2 * u] = a[u]; x[2 * u + 1] = b[u]; }
+                    *reinterpret_cast<uint4 *>(row + k_o0[i]) = pack8(x);
+                } else {
+                    *reinterpret_cast<uint4 *>(row + k_o0[i]) = kr0[i];
+                    if constexpr (Plan::NEOX_SLOT) *reinterpret_cast<uint4 *>(row + k_o1[i]) = kr1[i];
+                }
+            }
+            uint16_t *vdst = kdst + L::K_ELEMS;
+#pragma unroll
+            for (int i = 0; i < VI; ++i)
+                if (v_ok[i]) *reinterpret_cast<uint4 *>(vdst + v_l[i]) = vr[i];
+        };
+
+        // ---- running state ----
+        f32x16_t oacc[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) oacc[b] = (f32x16_t){};
+        // Reference max of this lane's query row (base 2, scaled scores),
+        // equal in lanes l and l^32; m_set is false until the row has seen a
+        // visible key.
+        float m_ref = 0.f;
+        bool m_set = false;
+        float l_acc[4] = {0.f, 0.f, 0.f, 0.f};   // partial row sums (this lane's keys)
+        // accumulator seed: -m_ref in every element, refreshed when m_ref moves
+        f32x16_t cinit = (f32x16_t){};
+
+        // One key tile of this group: S', softmax update, O += V^T P^T.
+        auto compute = [&](int64_t kt, int buf) {
+            const int64_t j0 = kt * BN;
+            const bool wave_active =
+                wave_has_rows && (!p.causal || p.k_off + j0 <= p.q_off + wq_last);
+            if (!wave_active) return;
+            const uint16_t *kb_lds = lds + (group * 2 + buf) * L::BUF_ELEMS;
+            const uint16_t *v_lds = kb_lds + L::K_ELEMS;
+            // S' = K Q'^T - m_ref: NKB 32-key blocks x 32 queries.
+            f32x16_t sacc[NKB];
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2) {
+                sacc[kb2] = cinit;
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
                     const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                        kb_lds + (kb * 32 + l32) * KP + 16 * t + 8 * hh);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
+                        kb_lds + (kb2 * 32 + l32) * KP + 16 * t + 8 * hh);
+                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb2], 0, 0, 0);
                 }
             }
-            // accumulator element r of block kb <-> key j0 + 32kb + 8(r/4) + 4hh + r%4
+            // accumulator element r of block kb2 <-> key j0 + 32kb2 + 8(r/4) + 4hh + r%4
             const bool need_mask = (j0 + BN > p.Sk) ||
                                    (p.causal && p.k_off + j0 + BN - 1 > p.q_off + wq0);
             if (need_mask) {
+                // key j0 + kk is visible iff kk <= lim (kk: index inside the tile)
+                int64_t lim64 = p.Sk - 1 - j0;
+                if (p.causal) {
+                    const int64_t c = p.q_off + qrow - p.k_off - j0;
+                    lim64 = c < lim64 ? c : lim64;
+                }
+                const int lim = lim64 < -1 ? -1 : (lim64 > BN ? BN : (int)lim64);
+                const int lim_h = lim - 4 * hh;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int64_t j = j0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-                        const bool ok = j < p.Sk && (!p.causal || p.k_off + j <= p.q_off + qrow);
-                        if (!ok) sacc[kb][r] = -INFINITY;
+                        const int kk = 32 * kb2 + 8 * (r / 4) + (r % 4);
+                        if (kk > lim_h) sacc[kb2][r] = -INFINITY;
                     }
             }
-            float mx = -INFINITY;
+            // row max of S' (tree), combined with the other half of the column
+            float mx[4 * NKB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int u = 0; u < 4 * NKB; ++u)
+                mx[u] = fmaxf(fmaxf(sacc[u >> 2][4 * (u & 3)], sacc[u >> 2][4 * (u & 3) + 1]),
+                              fmaxf(sacc[u >> 2][4 * (u & 3) + 2], sacc[u >> 2][4 * (u & 3) + 3]));
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * p.sl2);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            float lsum = 0.f;
+            for (int wd = 2 * NKB; wd >= 1; wd >>= 1)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int u = 0; u < wd; ++u) mx[u] = fmaxf(mx[u], mx[u + wd]);
+            const float rmax = max_with_partner(mx[0]);
+            // raise the reference on a row's first visible key, or when its
+            // scores exceed the reference by more than the lazy threshold
+            const bool need = (!m_set && rmax > -INFINITY) || rmax > LAZY_THRESHOLD;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float delta = need ? rmax : 0.f;
+                const float alpha = m_set ? __builtin_amdgcn_exp2f(-delta) : 1.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.sl2, -m_use));
-                    sacc[kb][r] = pr;
-                    lsum += pr;
+                for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[kb2][r] -= delta;
+#pragma unroll
+                for (int b = 0; b < DB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) l_acc[u] *= alpha;
+                m_ref += delta;
+                m_set = m_set || need;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cinit[r] = -m_ref;
+            }
+            // P = exp2(S'), rounded to bf16 in the B-operand layout of
+            // O^T += V^T P^T.  For key sub-step mm of block kb2, slot s holds
+            // accumulator element 8mm + s, i.e. key 32kb2 + 16mm + 8(s/4) +
+            // 4hh + s%4.
+            bf16x8_t pb[NKB][2];
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    uint32_t wv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        wv[u] = pack_bf16x2(__builtin_amdgcn_exp2f(sacc[kb2][8 * mm + 2 * u]),
+                                            __builtin_amdgcn_exp2f(sacc[kb2][8 * mm + 2 * u + 1]));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        l_acc[u] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(rope::bf16x2_t, wv[u]), ones, l_acc[u], false);
+                    pb[kb2][mm] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
                 }
-            l_part = l_part * alpha + lsum;
-            m_run = m_new;
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                    for (int b = 0; b < DB; ++b) {
+                        const int key0 = 32 * kb2 + 16 * mm + tr_key;
+                        const uint16_t *src = v_lds + key0 * VP + 32 * b + tr_col;
+                        const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
+                        const s16x4_t x1 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * VP));
+                        const bf16x8_t a = __builtin_bit_cast(
+                            bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+                                          x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+                        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb2][mm], oacc[b], 0, 0, 0);
+                    }
+        };
+
+        // Group g takes tiles kb + g, kb + g + NG, ...  Group 0 computes then
+        // stages its next tile; group 1 runs one tile ahead, staging first
+        // and computing second, so within an iteration the two waves sharing
+        // a SIMD are in different phases (matrix-core work against
+        // rotation/softmax VALU work).
+        const int64_t n_iter = (ke - kb + NG - 1) / NG;
+        if (kb + group < ke) {
+            fetch(kb + group);
+            stage(0);
+        }
+        if (group == 1 && kb + group + NG < ke) fetch(kb + group + NG);
+
+        for (int64_t it = 0; it < n_iter; ++it) {
+            const int buf = (int)(it & 1);
+            __syncthreads();   // this iteration's tiles staged; the previous ones consumed
+            const int64_t kt = kb + it * NG + group;
+            if (group == 0) {
+                const bool more = kt + NG < ke;
+                if (more) fetch(kt + NG);
+                if (kt < ke) compute(kt, buf);
+                if (more) stage(buf ^ 1);
+            } else {
+                if (kt + NG < ke) stage(buf ^ 1);
+                if (kt + 2 * NG < ke) fetch(kt + 2 * NG);
+                if (kt < ke) compute(kt, buf);
+            }
+        }
+
+        // ---- per-segment epilogue ----
+        float l_tot = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
+        float m_fin = m_set ? m_ref : -INFINITY;
+        float *xfer = reinterpret_cast<float *>(lds);
+        __syncthreads();   // all tiles consumed; LDS reusable
+        if constexpr (NG == 2) {
+            // group 1 hands its state to group 0 through LDS: per wave, per
+            // lane, DB*16 accumulators + m + l, component-major.
+            if (group == 1) {
+                float *dst = xfer + wave * NC * 64 + lane;
+#pragma unroll
+                for (int b = 0; b < DB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[(b * 16 + r) * 64] = oacc[b][r];
+                dst[(DB * 16) * 64] = m_fin;
+                dst[(DB * 16 + 1) * 64] = l_tot;
+            }
+            __syncthreads();
+            if (group == 0) {
+                const float *src = xfer + wave * NC * 64 + lane;
+                const float mB = src[(DB * 16) * 64], lB = src[(DB * 16 + 1) * 64];
+                const float m = fmaxf(m_fin, mB);
+                const float aA = m_fin == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_fin - m);
+                const float aB = mB == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mB - m);
+#pragma unroll
+                for (int b = 0; b < DB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[b][r] = oacc[b][r] * aA + src[(b * 16 + r) * 64] * aB;
+                l_tot = l_tot * aA + lB * aB;
+                m_fin = m;
+            }
+        }
+
+        auto write_out = [&]() {
+            if (!qvalid) return;
+            const float inv = 1.f / l_tot;
+            uint16_t *orow = p.o + ((int64_t)bh * p.Sq + qrow) * D;
 #pragma unroll
             for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-
-            // O^T += V^T P^T.  For key sub-step mm of block kb, B-operand slot
-            // s holds accumulator element 8mm + s, i.e. key
-            // 32kb + 16mm + 8(s/4) + 4hh + s%4; the A operand takes the same
-            // keys from V^T row d: two runs of 4 contiguous keys.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    bf16x8_t pb;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) pb[s] = (__bf16)sacc[kb][8 * mm + s];
-#pragma unroll
-                    for (int b = 0; b < DB; ++b) {
-                        const uint16_t *vrow = vt_lds + (32 * b + l32) * VP + 32 * kb + 16 * mm + 4 * hh;
-                        const uint2 x0 = *reinterpret_cast<const uint2 *>(vrow);
-                        const uint2 x1 = *reinterpret_cast<const uint2 *>(vrow + 8);
-                        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y));
-                        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[b], 0, 0, 0);
-                    }
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * b + 8 * g + 4 * hh;
+                    uint2 wv;
+                    wv.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
+                    wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+                    *reinterpret_cast<uint2 *>(orow + d0) = wv;
                 }
-        }
-        if (more) stage(buf ^ 1);
-    }
+        };
 
-    // ---------------- epilogue: O = O_acc / l ----------------
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
-    if (qvalid) {
-        const float inv = 1.f / l_tot;
-        uint16_t *orow = p.o + ((int64_t)bh * p.Sq + qrow) * D;
+        if (full) {
+            if (group == 0) write_out();
+        } else if (group == 0) {
+            // Split query tile: publish this segment's state; the merge
+            // kernel that follows on the stream combines the segments.
+            const int64_t U = (int64_t)p.BH * p.u_head;
+            const int my_slot = seg_v == share_start(w, U, p.sk_G) ? 0 : 1;
+            float *dst = p.ws_part + (((w * 2 + my_slot) * 4 + wave) * NC) * 64 + lane;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[(b * 16 + r) * 64] = oacc[b][r];
+            dst[(DB * 16) * 64] = m_fin;
+            dst[(DB * 16 + 1) * 64] = l_tot;
+        }
+        __syncthreads();   // LDS is reused by the next segment
+    };
+
+    if (p.sk_G == 0) {
+        // one workgroup per query tile, heaviest tiles first, a head's tiles
+        // on one XCD (block index modulo the head count)
+        const int bh = blockIdx.x % p.BH;
+        const int64_t rank = blockIdx.x / p.BH;
+        const int64_t qtile = p.causal ? p.n_qtiles - 1 - rank : rank;
+        segment(bh, qtile, 0, tile_visits(p, qtile), true, 0, 0);
+    } else {
+        // balanced share [v0, v1) of the (batch*head, query tile, key tile) visits
+        const int64_t U = (int64_t)p.BH * p.u_head;
+        const int64_t w = share_of_block(p, blockIdx.x);
+        const int64_t v1 = share_start(w + 1, U, p.sk_G);
+        for (int64_t v = share_start(w, U, p.sk_G); v < v1;) {
+            const int64_t hs = v / p.u_head;
+            const int bh = head_of_slot(p, hs);
+            const int64_t r = v - hs * p.u_head;
+            const int64_t qtile = find_tile(p, r);
+            const int64_t base = visits_before(p, qtile);
+            const int64_t nt = tile_visits(p, qtile);
+            const int64_t kb = r - base;
+            const int64_t ke = (nt < kb + (v1 - v)) ? nt : kb + (v1 - v);
+            segment(bh, qtile, kb, ke, kb == 0 && ke == nt, v, w);
+            v += ke - kb;
+        }
+    }
+}
+
+// Combines the segments of every split query tile, in share order, and
+// writes its output rows.  One 4-wave workgroup per (batch*head, query tile);
+// tiles that were not split return at once.  Runs after the main kernel on
+// the same stream, so every partial state is visible.
+template <int D>
+__global__ __launch_bounds__(256) void flash_merge_kernel(Params p)
+{
+    constexpr int DB = D / 32, NC = DB * 16 + 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.x / p.n_qtiles;
+    const int64_t qtile = blockIdx.x % p.n_qtiles;
+    const int64_t U = (int64_t)p.BH * p.u_head;
+    const int64_t X0 = slot_of_head(p, bh) * p.u_head + visits_before(p, qtile);
+    const int64_t X1 = X0 + tile_visits(p, qtile);
+    const int64_t w_first = share_of(X0, U, p.sk_G), w_last = share_of(X1 - 1, U, p.sk_G);
+    if (w_first == w_last) return;   // written by the main kernel
+    const int64_t qrow = qtile * BM + wave * 32 + l32;
+    f32x16_t oacc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) oacc[b] = (f32x16_t){};
+    float m_acc = -INFINITY, l_sum = 0.f;
+    for (int64_t w2 = w_first; w2 <= w_last; ++w2) {
+        const int slot2 = share_start(w2, U, p.sk_G) >= X0 ? 0 : 1;
+        const float *src = p.ws_part + (((w2 * 2 + slot2) * 4 + wave) * NC) * 64 + lane;
+        const float m2 = src[(DB * 16) * 64], l2 = src[(DB * 16 + 1) * 64];
+        const float m = fmaxf(m_acc, m2);
+        const float a1 = m_acc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_acc - m);
+        const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * b + 8 * g + 4 * hh;
-                uint2 w;
-                w.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-                w.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-                *reinterpret_cast<uint2 *>(orow + d0) = w;
-            }
+            for (int r = 0; r < 16; ++r) oacc[b][r] = oacc[b][r] * a1 + src[(b * 16 + r) * 64] * a2;
+        l_sum = l_sum * a1 + l2 * a2;
+        m_acc = m;
     }
+    if (qrow >= p.Sq) return;
+    const float inv = 1.f / l_sum;
+    uint16_t *orow = p.o + ((int64_t)bh * p.Sq + qrow) * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * b + 8 * g + 4 * hh;
+            uint2 wv;
+            wv.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
+            wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+            *reinterpret_cast<uint2 *>(orow + d0) = wv;
+        }
+}
+
+#ifndef ROPE_FLASH_D64_NG
+#define ROPE_FLASH_D64_NG 2
+#endif
+#ifndef ROPE_FLASH_D64_BN
+#define ROPE_FLASH_D64_BN 64
+#endif
+#ifndef ROPE_FLASH_D128_NG
+#define ROPE_FLASH_D128_NG 1
+#endif
+#ifndef ROPE_FLASH_D128_BN
+#define ROPE_FLASH_D128_BN 32
+#endif
+
+// Tile shape per head dim: key groups per workgroup and keys per tile.
+// D = 64: two groups (8 waves, two per SIMD) of 64-key tiles.  D = 128: one
+// group of 32-key tiles (within 256 registers per wave), two workgroups per
+// CU.
+template <int D> struct Shape;
+template <> struct Shape<64> {
+    static constexpr int NG = ROPE_FLASH_D64_NG, BN = ROPE_FLASH_D64_BN;
+};
+template <> struct Shape<128> {
+    static constexpr int NG = ROPE_FLASH_D128_NG, BN = ROPE_FLASH_D128_BN;
+};
+
+std::atomic<int> g_cu_count[64];
+
+int device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Host half of the schedule: visit-law coefficients, and the balanced
+// share count (0 = one workgroup per query tile).
+template <int D>
+void plan(const FlashArgs &a, Params &p)
+{
+    constexpr int BN = Shape<D>::BN, NG = Shape<D>::NG;
+    p.BH = a.B * a.H;
+    p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
+    p.causal = a.causal;
+    p.n_qtiles = (a.Sq + BM - 1) / BM;
+    p.n_kt = (a.Sk + BN - 1) / BN;
+    const int64_t delta = a.q_off - a.k_off;   // >= 0 when causal (validated)
+    p.va = BM / BN;
+    p.vb = (BM - 1 + delta) / BN + 1;
+    {
+        const int64_t je = a.q_off + a.Sq - 1 - a.k_off;
+        p.v_last = a.causal ? (je / BN + 1 < p.n_kt ? je / BN + 1 : p.n_kt) : p.n_kt;
+    }
+    p.u_head = visits_before(p, p.n_qtiles);
+    p.sk_G = 0;
+    p.xcd_order = 0;
+    p.ws_part = nullptr;
+    if (!a.causal) return;
+    // balance only when the largest query tile does clearly more than the
+    // average and there is enough work to share
+    const int cus = device_cu_count();
+    const int G = cus * (NG == 2 ? 1 : 2);
+    const int64_t U = (int64_t)p.BH * p.u_head;
+    const int64_t vmax = tile_visits(p, p.n_qtiles - 1) > tile_visits(p, 0) ? tile_visits(p, p.n_qtiles - 1)
+                                                                            : tile_visits(p, 0);
+    if (G <= 0 || U < 4 * (int64_t)G || vmax * p.n_qtiles * 10 < p.u_head * 11) return;
+    p.sk_G = G;
+    p.xcd_order = (p.BH % 8 == 0 && G % 8 == 0) ? 1 : 0;
+}
+
+template <int D>
+int64_t workspace_bytes(const Params &p)
+{
+    if (p.sk_G == 0) return 0;
+    constexpr int NC = (D / 32) * 16 + 2;
+    return (int64_t)p.sk_G * 2 * 4 * NC * 64 * 4;   // two partial states per share
 }
 
 template <int D, int LAYOUT, bool ROT>
 int launch(const FlashArgs &a, hipStream_t stream)
 {
+    constexpr int NG = Shape<D>::NG, BN = Shape<D>::BN;
     Params p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
     p.v = static_cast<const uint16_t *>(a.v);
     p.o = static_cast<uint16_t *>(a.o);
-    p.BH = a.B * a.H;
-    p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
     p.cos_tab = a.cos_tab; p.sin_tab = a.sin_tab; p.rot_dim = a.rot_dim;
     p.sl2 = a.scale * 1.4426950408889634f;
-    p.causal = a.causal;
-    p.n_qtiles = (int)((a.Sq + BM - 1) / BM);
-    const int64_t blocks = (int64_t)p.BH * p.n_qtiles;
-    hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT>), dim3((unsigned)blocks), dim3(256),
-                       0, stream, p);
-    return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
+    plan<D>(a, p);
+    const int64_t need = workspace_bytes<D>(p);
+    if (need == 0 || a.workspace == nullptr || a.workspace_bytes < need)
+        p.sk_G = 0;   // no (or too small a) workspace: one workgroup per query tile
+    else
+        p.ws_part = static_cast<float *>(a.workspace);
+    const int64_t blocks = p.sk_G > 0 ? p.sk_G : (int64_t)p.BH * p.n_qtiles;
+    hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, NG, BN>), dim3((unsigned)blocks),
+                       dim3(256 * NG), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
+    if (p.sk_G > 0) {
+        hipLaunchKernelGGL((flash_merge_kernel<D>), dim3((unsigned)(p.BH * p.n_qtiles)), dim3(256), 0,
+                           stream, p);
+        if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
+    }
+    return ROPE_LAUNCH_OK;
 }
 
 }  // namespace
@@ -471,4 +872,15 @@ int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream)
     }
     if (!rot) return launch<128, 1, false>(a, stream);
     return a.layout == 0 ? launch<128, 0, true>(a, stream) : launch<128, 1, true>(a, stream);
+}
+
+int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a)
+{
+    Params p;
+    if (a.head_dim == 64) {
+        plan<64>(a, p);
+        return workspace_bytes<64>(p);
+    }
+    plan<128>(a, p);
+    return workspace_bytes<128>(p);
 }

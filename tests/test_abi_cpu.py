@@ -129,11 +129,11 @@ def test_rope_apply_noop_needs_no_device(lib, over):
 def fwd_args(**over):
     a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, B=1, H=8, Sq=4096, Sk=4096, D=64, qo=0, ko=0,
              cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX, causal=1,
-             scale=0.0, dtype=_lib.BF16)
+             scale=0.0, dtype=_lib.BF16, ws=None, wsb=0)
     a.update(over)
     return [a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qo"],
             a["ko"], a["cos"], a["sin"], a["rows"], a["rot"], a["layout"], a["causal"], a["scale"],
-            a["dtype"], None]
+            a["dtype"], a["ws"], a["wsb"], None]
 
 
 @pytest.mark.parametrize("over,want", [
@@ -161,6 +161,9 @@ def fwd_args(**over):
     (dict(qo=14336, Sq=2048, Sk=16384, rows=16383), _lib.ERR_TABLE_RANGE),
     (dict(cos=FAKE4 + 0x1004), _lib.ERR_ALIGN),
     (dict(k=FAKE2 + 8), _lib.ERR_ALIGN),
+    (dict(ws=None, wsb=1024), _lib.ERR_SHAPE),        # bytes without a buffer
+    (dict(ws=FAKE4 + 0x8000, wsb=-1), _lib.ERR_SHAPE),
+    (dict(ws=FAKE4 + 0x8004, wsb=4096), _lib.ERR_ALIGN),
 ])
 def test_flash_rejects(lib, over, want):
     assert lib.rope_flash_attn_fwd(*fwd_args(**over)) == want
@@ -171,3 +174,21 @@ def test_flash_without_rotation_needs_no_table(lib):
     assert lib.rope_flash_attn_fwd(*fwd_args(rot=0, cos=None, sin=None, rows=0, B=0)) == _lib.ERR_SHAPE
     # non-causal with q_off < k_off is legal (every key is visible); shape error first
     assert lib.rope_flash_attn_fwd(*fwd_args(causal=0, qo=0, ko=5, rows=8192, H=0)) == _lib.ERR_SHAPE
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 8, 4096, 4096, 64, 0, 0, 1, _lib.BF16), _lib.ERR_SHAPE),
+    ((1, 8, 4096, 4096, 63, 0, 0, 1, _lib.BF16), _lib.ERR_SHAPE),
+    ((1, 8, 4096, 4096, 96, 0, 0, 1, _lib.BF16), _lib.ERR_UNSUPPORTED),
+    ((1, 8, 4096, 4096, 64, 0, 0, 1, 7), _lib.ERR_UNSUPPORTED),
+    ((1, 8, 4096, 4096, 64, 0, 3, 1, _lib.BF16), _lib.ERR_EMPTY_ROW),
+    ((1, 8, 4096, 4096, 64, -1, 0, 1, _lib.BF16), _lib.ERR_SHAPE),
+])
+def test_workspace_size_rejects(lib, args, want):
+    """Invalid shapes come back as minus the status code, before any HIP call."""
+    assert lib.rope_flash_attn_workspace_size(*args) == -want
+
+
+def test_workspace_size_fp32_needs_none(lib):
+    # the fp32 kernel has no balanced schedule: no device query, zero bytes
+    assert lib.rope_flash_attn_workspace_size(1, 2, 128, 128, 64, 0, 0, 1, _lib.F32) == 0

@@ -351,3 +351,56 @@ def test_fused_deterministic_and_unfused_agree():
     kr = kr.reshape(1, T, w.H, w.D).permute(0, 2, 1, 3).contiguous()
     u = run_fused(w, qr, kr, v, rot=0)
     assert float((a.float() - u.float()).abs().max()) <= BF16_TOL
+
+
+# --------------------------------------------------------------------------
+# balanced (split query tile) schedule
+
+
+BALANCED = [
+    wl.AttentionWorkload("balanced_neox_1x8x2048x64", 1, 8, 2048, 2048, 64, "bf16", 21, "neox"),
+    wl.AttentionWorkload("balanced_gptj_2x4x2000x64", 2, 4, 2000, 2000, 64, "bf16", 22, "gptj"),
+    wl.AttentionWorkload("balanced_neox_1x8x2048x128", 1, 8, 2048, 2048, 128, "bf16", 23, "neox"),
+    wl.AttentionWorkload("balanced_offset_gptj_1x8x1500x2600x128", 1, 8, 1500, 2600, 128, "bf16", 24,
+                         "gptj", q_off=1100, k_off=0),
+]
+
+
+def test_balanced_schedule_is_used():
+    """The square causal workloads above request a workspace (the split
+    schedule runs); a balanced one (chunked prefill) does not."""
+    from rotary_position_embedding_rope_amd import _lib
+    lib = _lib.load()
+    for w in BALANCED[:3] + [wl.HEADLINE]:
+        assert lib.rope_flash_attn_workspace_size(w.B, w.H, w.Sq, w.Sk, w.D, w.q_off, w.k_off, 1,
+                                                  _lib.BF16) > 0, w.name
+    w = wl.PREFILL_OFFSET
+    assert lib.rope_flash_attn_workspace_size(w.B, w.H, w.Sq, w.Sk, w.D, w.q_off, w.k_off, 1,
+                                              _lib.BF16) == 0
+
+
+@pytest.mark.parametrize("w", BALANCED, ids=lambda w: w.name)
+def test_balanced_schedule_full(orc, w):
+    """Split query tiles merged through the workspace: every output vs the
+    oracle (2e-2), the same with no workspace (one workgroup per query
+    tile), two calls in a row bit-identical (the merge order is fixed)."""
+    q, k, v = wl.attention_inputs(w)
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    c, s = tables(w.base, w.rot, w.table_rows)
+    ws = api.workspace_for(tq, w.Sk, w.q_off, w.k_off, True)
+    assert ws is not None
+    ws.fill_(0x7f)   # contents are irrelevant: stale bytes must not matter
+    outs = []
+    for use_ws in (ws, ws, None):
+        out = torch.full_like(tq, float("nan"))
+        api.flash_attn_fwd(tq, tk, tv, c, s, w.q_off, w.k_off, w.rot, w.layout, True, out=out,
+                           workspace=use_ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    want = orc.attention(q, k, v, q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot, base=w.base,
+                         layout=w.layout, causal=True)
+    for out in outs:
+        got = to64(out)
+        assert np.isfinite(got).all()
+        assert np.abs(got - want).max() <= BF16_TOL
