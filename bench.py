@@ -8,13 +8,15 @@ W untimed warmup steps, then exactly K timed steps between two device
 synchronisations; rank 0 prints ONE JSON line.
 
   value          whole-job TFLOP/s = algorithmic flops / wall time per step
-                 (algorithmic flops: 4*D per query/key pair the mask allows)
-  roofline       the fused kernel: flops per launch / mean kernel duration
-                 from HIP events on the launch stream, against 2500 TFLOP/s
+                 (algorithmic flops: 4*D per query/key pair the mask allows);
+                 the K steps run back to back between two synchronisations
+  roofline       the fused kernel: flops per launch / mean launch duration,
+                 from one HIP event pair on the launch stream around the K
+                 launches, against 2500 TFLOP/s
   rope_apply     the ragged RoPE workload (8192 tokens, 32 Q + 8 K heads,
-                 rot 64 of 128): algorithmic bytes / mean kernel duration,
-                 cycling through enough buffer sets to defeat the 256 MB
-                 last-level cache, against 8 TB/s
+                 rot 64 of 128): algorithmic bytes / mean launch duration
+                 (measured the same way), cycling through enough buffer sets
+                 to defeat the 256 MB last-level cache, against 8 TB/s
   cpu_baseline   the fp64 CPU oracle on the same workload (whole heads),
                  timed on this host's cores
   comparators    context rows mirroring "RoPE + PoPE Attention Kernels"'
@@ -90,8 +92,12 @@ def recorded_traffic(profile: str, source: str):
 
 
 def time_launches(torch, launch, steps, warmup, stream, rotate=None):
-    """Warm up, then time `steps` launches: wall time between device
-    synchronisations and per-launch HIP event durations on `stream`."""
+    """Warm up, then the timed region: `steps` launches back to back on
+    `stream`, between device synchronisations, with one HIP event pair on the
+    stream around them.  A second, untimed-for-value pass puts an event pair
+    around each launch for the spread of single-launch durations.  Returns
+    (wall ms per launch, event ms per launch in the timed region, sorted
+    single-launch event ms)."""
     def run(i):
         if rotate:
             rotate(i)
@@ -100,18 +106,25 @@ def time_launches(torch, launch, steps, warmup, stream, rotate=None):
 
     for i in range(warmup):
         run(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
     t0 = time.perf_counter()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
+    a.record(stream)
+    for i in range(steps):
         run(i)
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    durs = sorted(a.elapsed_time(b) for a, b in evs)
-    return wall_ms / steps, sum(durs) / len(durs), durs
+    event_ms = a.elapsed_time(b)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (x, y) in enumerate(evs):
+        x.record(stream)
+        run(i)
+        y.record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(x.elapsed_time(y) for x, y in evs)
+    return wall_ms / steps, event_ms / steps, durs
 
 
 def bench_fused(torch, api, wl, w, steps, warmup, balance=False):
@@ -146,7 +159,8 @@ def bench_rope_apply(torch, api, wl, steps, sets):
     return {
         "workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
         "ms_per_launch": round(kernel_ms, 5), "wall_ms_per_launch": round(ms_step, 5),
-        "p10_ms": round(durs[len(durs) // 10], 5), "p90_ms": round(durs[(9 * len(durs)) // 10], 5),
+        "single_launch_p10_ms": round(durs[len(durs) // 10], 5),
+        "single_launch_p90_ms": round(durs[(9 * len(durs)) // 10], 5),
         "buffer_sets": sets, "cycled_mib": round(set_mb * sets, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -253,8 +267,10 @@ def main():
         achieved = flops / (r["kernel_ms"] * 1e-3) / 1e12
         result["value"] = round(value, 2)
         result["ms_per_step"] = round(r["ms_step"], 5)
-        result["kernel_ms"] = {"mean": round(r["kernel_ms"], 5), "p10": round(r["p10"], 5),
-                               "p50": round(r["p50"], 5), "p90": round(r["p90"], 5)}
+        result["kernel_ms"] = {"mean": round(r["kernel_ms"], 5),
+                               "single_launch_p10": round(r["p10"], 5),
+                               "single_launch_p50": round(r["p50"], 5),
+                               "single_launch_p90": round(r["p90"], 5)}
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                               "traffic": recorded_traffic(f"flash_fwd_bf16_{w.name}_traffic.md",

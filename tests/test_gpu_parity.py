@@ -152,6 +152,28 @@ def test_rope_apply_variants(orc, layout, dtype, D, rot):
     check_rope_apply_result(orc, xk.astype(np.float64), to64(k), positions, 1e4, rot, layout, dtype)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (40, 0), (64, 8), (128, 16)])
+@pytest.mark.parametrize("dtype,rot", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("layout", ["neox", "gptj"])
+def test_rope_apply_head_counts(orc, Hq, Hkv, dtype, rot, layout):
+    """Head counts from a few heads per token (several tokens share a wave)
+    to 144 (a token spans several waves, or the launch falls back to the
+    chunk-column kernel), Q-only included; ragged token count."""
+    rng = np.random.default_rng(Hq * 100 + Hkv + rot)
+    T, D, rows = 97, 128, 3000
+    xq = wl.round_to(rng.standard_normal((T, Hq, D)), dtype)
+    xk = wl.round_to(rng.standard_normal((T, Hkv, D)), dtype) if Hkv else None
+    positions = rng.integers(0, rows, size=T).astype(np.int32)
+    c, s = tables(10000.0, rot, rows)
+    q = to_dev(xq, dtype)
+    k = to_dev(xk, dtype) if Hkv else None
+    api.rope_apply(q, k, torch.from_numpy(positions).to(DEV), c, s, rot_dim=rot, layout=layout)
+    torch.cuda.synchronize()
+    check_rope_apply_result(orc, xq.astype(np.float64), to64(q), positions, 1e4, rot, layout, dtype)
+    if Hkv:
+        check_rope_apply_result(orc, xk.astype(np.float64), to64(k), positions, 1e4, rot, layout, dtype)
+
+
 def test_rope_apply_packed_qkv_strides(orc):
     """Q and K as views into one packed [T, Hq + 2*Hkv, D] QKV buffer: token
     stride covers all heads; V heads must stay untouched."""
