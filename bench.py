@@ -63,8 +63,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
-    ap.add_argument("--only", choices=["all", "fused", "rope_apply"], default="all",
-                    help="restrict the timed kernels (for profiler runs)")
+    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "copy"], default="all",
+                    help="restrict the timed kernels (for profiler runs); 'copy' runs only a "
+                         "plain 256 MiB device copy, the calibration for HBM byte counters")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every attention workload (printed to stderr)")
     ap.add_argument("--balance", action="store_true",
@@ -212,6 +213,18 @@ def comparators(torch, api, wl, w, r, steps, warmup):
             "extra_mem_mib": {"fused": fused_mem, "unfused": unfused_mem}}
 
 
+def copy_calibration(torch, steps, nbytes=256 * 2 ** 20):
+    """A plain device-to-device copy of known size: the reference that scales
+    the profiler's FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_per_launch": nbytes, "launches": steps}
+
+
 def cpu_baseline(wl, w, seconds):
     """The oracle on whole heads of the workload, cycled until `seconds` pass."""
     import numpy as np
@@ -251,6 +264,9 @@ def main():
     from rotary_position_embedding_rope_amd import api
     from rotary_position_embedding_rope_amd import workloads as wl
 
+    if args.only == "copy":
+        print(json.dumps(copy_calibration(torch, args.steps)), flush=True)
+        return
     w = {x.name: x for x in wl.ATTENTION_WORKLOADS}[args.workload]
     result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
