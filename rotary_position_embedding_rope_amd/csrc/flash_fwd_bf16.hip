@@ -13,18 +13,23 @@
 //
 // Work decomposition (FlashAttention-2 style, the same page's section 7: a
 // query-block outer loop, key/value inner loop, output written once):
-//   * a workgroup owns a 128-query tile of one (batch, head); NG key groups
-//     of 4 waves each (NG = 1 or 2) walk interleaved 64-key tiles of that
-//     query tile and are merged through LDS at the end.  With NG = 2 every
-//     SIMD runs two waves, so one wave's softmax overlaps the other's
-//     matrix-core work;
+//   * a workgroup owns 128 query rows of one (batch, head): two 64-row
+//     halves.  With the causal mask these are half-tiles r and n - 1 - r of
+//     the query range, a light and a heavy one, so all workgroups see about
+//     the same number of key tiles (the causal triangle is folded instead of
+//     leaving the last query tiles as the critical path); otherwise they are
+//     128 consecutive rows.  NG key groups of 4 waves each (NG = 1 or 2) walk
+//     interleaved key tiles and are merged through LDS at the end.  With
+//     NG = 2 every SIMD runs two waves, one per half, so one wave's softmax
+//     overlaps the other's matrix-core work and the heavy half's tiles are
+//     spread over all four SIMDs;
 //   * in each group a wave owns 32 query rows; the key loop stops at the
 //     last tile a query of the workgroup can see, tiles past a wave's last
-//     query are skipped by that wave, and the element mask runs only on
-//     tiles straddling the diagonal or the ragged end;
-//   * heaviest query tiles are dispatched first, and all tiles of one head
-//     go to one XCD (block index modulo the head count), so a head's K/V
-//     stay in one L2.
+//     query are skipped by that wave (it keeps staging for the others), and
+//     the element mask runs only on tiles straddling the diagonal or the
+//     ragged end;
+//   * all workgroups of one head go to one XCD (block index modulo the head
+//     count), so a head's K/V stay in one L2.
 //
 // Data path of a group:
 //   * Q: each lane loads its query row's dims straight into the matrix-core
@@ -79,10 +84,12 @@ struct Params {
     float sl2;          // softmax scale * log2(e)
     int causal;
     int64_t n_qtiles;
+    int64_t n_half;     // 64-row halves of the query range
     int64_t n_kt;       // key tiles
     // Key tiles visited by query tile t: causal and t < n_qtiles - 1:
     // min(n_kt, va * t + vb); the last query tile: v_last; non-causal: n_kt.
     int64_t va, vb, v_last;
+    int tile_n;         // keys per tile
     // Balanced schedule (sk_G > 0): the BH * u_head (query tile, key tile)
     // visits are cut into sk_G equal contiguous shares, one per workgroup.
     int sk_G;
@@ -102,6 +109,14 @@ __host__ __device__ inline int64_t tile_visits(const Params &p, int64_t t)
     if (!p.causal) return p.n_kt;
     if (t == p.n_qtiles - 1) return p.v_last;
     const int64_t v = p.va * t + p.vb;
+    return v < p.n_kt ? v : p.n_kt;
+}
+
+// Key tiles seen by query rows up to `last` (all key tiles when not causal).
+__host__ __device__ inline int64_t row_visits(const Params &p, int64_t last)
+{
+    if (!p.causal) return p.n_kt;
+    const int64_t v = (p.q_off + last - p.k_off) / p.tile_n + 1;
     return v < p.n_kt ? v : p.n_kt;
 }
 
@@ -220,8 +235,10 @@ struct Lds {
     static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;   // one K + one V tile
 };
 
-// D: head dim; BN: keys per tile (32 or 64); NG: key groups per workgroup.
-template <int D, int LAYOUT, bool ROT, int NG, int BN>
+// D: head dim; BN: keys per tile (32 or 64); NG: key groups per workgroup;
+// BAL: the balanced schedule (a separate instantiation, so the default
+// kernel does not carry its share-walking code).
+template <int D, int LAYOUT, bool ROT, int NG, int BN, bool BAL>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_bf16_kernel(Params p)
 {
@@ -299,20 +316,25 @@ void flash_fwd_bf16_kernel(Params p)
     const int tr_key = 4 * (g16 >> 1) + tr_row;   // + 32kb + 16mm (+ 8)
     const rope::bf16x2_t ones = __builtin_bit_cast(rope::bf16x2_t, 0x3f803f80u);   // (1, 1)
 
-    // One segment: key tiles [kb, ke) of query tile `qtile` of head `bh`.
-    // `full` when the segment covers all key tiles the query tile visits;
-    // otherwise its state is merged with the other segments of that query
-    // tile through the workspace (seg_v: global index of its first visit,
-    // w: this workgroup's share index).
-    auto segment = [&](int bh, int64_t qtile, int64_t kb, int64_t ke, bool full, int64_t seg_v,
-                       int64_t w) {
-        const int64_t q0 = qtile * BM;
+    // One segment: key tiles [kb, ke) of the 128 query rows made of two
+    // 64-row halves starting at rowA and rowB (rowB >= Sq: no second half)
+    // of head `bh`.  `full` when the segment covers every key tile those rows
+    // see; otherwise (balanced schedule, rowB = rowA + 64) its state is merged
+    // with the other segments of that query tile through the workspace
+    // (seg_v: global index of its first visit, w: this workgroup's share).
+    // Wave w of group 0 takes half (w >> 1) & 1, rows 32 (w & 1) of it; group
+    // 1 takes the other half on each SIMD, so a SIMD's two waves work on
+    // different halves.
+    auto segment = [&](int bh, int64_t rowA, int64_t rowB, int64_t kb, int64_t ke, bool full,
+                       int64_t seg_v, int64_t w) {
+        const int half = ((wave >> 1) ^ (NG == 2 ? group : 0)) & 1;
+        const int64_t wq0 = (half ? rowB : rowA) + 32 * (wave & 1);   // first row of this wave
         const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
         const uint16_t *kh = p.k + (int64_t)bh * p.Sk * D;
         const uint16_t *vh = p.v + (int64_t)bh * p.Sk * D;
 
         // ---- Q: load, rotate, scale, keep as MFMA B operand ----
-        const int64_t qrow = q0 + wave * 32 + l32;
+        const int64_t qrow = wq0 + l32;
         const bool qvalid = qrow < p.Sq;
         bf16x8_t qf[DT];
         {
@@ -373,7 +395,6 @@ void flash_fwd_bf16_kernel(Params p)
             }
         }
 
-        const int64_t wq0 = q0 + wave * 32;
         const int64_t wq_last = (wq0 + 31 < p.Sq ? wq0 + 31 : p.Sq - 1);
         const bool wave_has_rows = wq0 < p.Sq;
 
@@ -614,7 +635,7 @@ void flash_fwd_bf16_kernel(Params p)
             // group 1 hands its state to group 0 through LDS: per wave, per
             // lane, DB*16 accumulators + m + l, component-major.
             if (group == 1) {
-                float *dst = xfer + wave * NC * 64 + lane;
+                float *dst = xfer + (wave ^ 2) * NC * 64 + lane;   // the rows of group 0's wave ^ 2
 #pragma unroll
                 for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -672,13 +693,24 @@ void flash_fwd_bf16_kernel(Params p)
         __syncthreads();   // LDS is reused by the next segment
     };
 
-    if (p.sk_G == 0) {
-        // one workgroup per query tile, heaviest tiles first, a head's tiles
-        // on one XCD (block index modulo the head count)
+    if constexpr (!BAL) {
+        // A head's workgroups share an XCD (block index modulo the head
+        // count).  Causal: workgroup r takes 64-row half-tiles r and
+        // n_half - 1 - r, a light and a heavy one, so every workgroup sees
+        // about the same number of key tiles.  Otherwise: 128 consecutive rows.
         const int bh = blockIdx.x % p.BH;
         const int64_t rank = blockIdx.x / p.BH;
-        const int64_t qtile = p.causal ? p.n_qtiles - 1 - rank : rank;
-        segment(bh, qtile, 0, tile_visits(p, qtile), true, 0, 0);
+        int64_t rowA, rowB;
+        if (p.causal) {
+            const int64_t hb = p.n_half - 1 - rank;
+            rowA = 64 * rank;
+            rowB = hb > rank ? 64 * hb : p.Sq;
+        } else {
+            rowA = rank * BM;
+            rowB = rowA + 64;
+        }
+        const int64_t last = (rowB < p.Sq ? rowB : rowA) + 63;
+        segment(bh, rowA, rowB, 0, row_visits(p, last < p.Sq ? last : p.Sq - 1), true, 0, 0);
     } else {
         // balanced share [v0, v1) of the (batch*head, query tile, key tile) visits
         const int64_t U = (int64_t)p.BH * p.u_head;
@@ -693,7 +725,7 @@ void flash_fwd_bf16_kernel(Params p)
             const int64_t nt = tile_visits(p, qtile);
             const int64_t kb = r - base;
             const int64_t ke = (nt < kb + (v1 - v)) ? nt : kb + (v1 - v);
-            segment(bh, qtile, kb, ke, kb == 0 && ke == nt, v, w);
+            segment(bh, qtile * BM, qtile * BM + 64, kb, ke, kb == 0 && ke == nt, v, w);
             v += ke - kb;
         }
     }
@@ -799,6 +831,8 @@ void plan(const FlashArgs &a, Params &p)
     p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
     p.causal = a.causal;
     p.n_qtiles = (a.Sq + BM - 1) / BM;
+    p.n_half = (a.Sq + 63) / 64;
+    p.tile_n = BN;
     p.n_kt = (a.Sk + BN - 1) / BN;
     const int64_t delta = a.q_off - a.k_off;   // >= 0 when causal (validated)
     p.va = BM / BN;
@@ -849,9 +883,14 @@ int launch(const FlashArgs &a, hipStream_t stream)
         p.sk_G = 0;   // no (or too small a) workspace: one workgroup per query tile
     else
         p.ws_part = static_cast<float *>(a.workspace);
-    const int64_t blocks = p.sk_G > 0 ? p.sk_G : (int64_t)p.BH * p.n_qtiles;
-    hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, NG, BN>), dim3((unsigned)blocks),
-                       dim3(256 * NG), 0, stream, p);
+    const int64_t blocks = p.sk_G > 0 ? p.sk_G
+                           : (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
+    if (p.sk_G > 0)
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, NG, BN, true>), dim3((unsigned)blocks),
+                           dim3(256 * NG), 0, stream, p);
+    else
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, NG, BN, false>), dim3((unsigned)blocks),
+                           dim3(256 * NG), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     if (p.sk_G > 0) {
         hipLaunchKernelGGL((flash_merge_kernel<D>), dim3((unsigned)(p.BH * p.n_qtiles)), dim3(256), 0,

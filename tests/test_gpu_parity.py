@@ -338,6 +338,8 @@ EDGE_CASES = [
     (1, 2, 100, 257, 128, "f32", "neox", 128, 300, 0, True),    # fp32, offset
     (2, 2, 70, 70, 64, "f32", "gptj", 32, 0, 0, True),          # fp32 partial
     (1, 1, 65, 65, 128, "f32", "gptj", 0, 0, 0, False),         # fp32, no rotation
+    (1, 2, 320, 320, 64, "bf16", "neox", 64, 0, 0, True),       # odd number of 64-row halves
+    (1, 1, 448, 600, 64, "bf16", "gptj", 64, 152, 0, True),     # offset mask, D=64, paired halves
 ]
 
 
