@@ -213,16 +213,17 @@ __device__ __forceinline__ float sum_with_partner(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Per-thread staging plan for K tiles (fixed across tiles).
-//   NeoX: a slot is two 8-dim chunks -- a rotated pair of chunks (lo at 8c,
-//         hi at 8c + rot/2) or two copied chunks past rot_dim.  D/16 slots
-//         per key row.
-//   GPT-J / no rotation: a slot is one 8-dim chunk, rotated (whole pairs)
-//         or copied.  D/8 slots per key row.
+// Per-thread staging plan for K tiles (fixed across tiles).  A slot is two
+// 8-dim chunks of one key row, D/16 slots per row:
+//   NeoX: a rotated pair of chunks (lo at 8c, hi at 8c + rot/2), or two
+//         copied chunks past rot_dim;
+//   GPT-J: 16 consecutive dims (8 whole pairs), rotated or copied (rot_dim
+//         is a multiple of 32, so a slot is never split);
+//   no rotation: 16 consecutive dims, copied.
 template <int D, int LAYOUT, bool ROT, int BN>
 struct KPlan {
     static constexpr bool NEOX_SLOT = ROT && LAYOUT == 0;
-    static constexpr int SLOTS_PER_ROW = NEOX_SLOT ? D / 16 : D / 8;
+    static constexpr int SLOTS_PER_ROW = D / 16;
     static constexpr int SLOTS = BN * SLOTS_PER_ROW;
     static constexpr int ITEMS = (SLOTS + 255) / 256;   // per thread (the last may be empty)
 };
@@ -233,6 +234,14 @@ struct Lds {
     static constexpr int K_ELEMS = BN * KP;
     static constexpr int V_ELEMS = BN * VP;
     static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;   // one K + one V tile
+};
+
+struct KItem {
+    int row, mode, o0, o1, to;
+};
+struct VItem {
+    int row, o, l;
+    bool ok;
 };
 
 // D: head dim; BN: keys per tile (32 or 64); NG: key groups per workgroup;
@@ -252,6 +261,7 @@ void flash_fwd_bf16_kernel(Params p)
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
     constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
+    constexpr int NFK = 8;                          // cos/sin values per K item
 
     // [group][buffer][K tile | V tile]
     __shared__ __attribute__((aligned(16))) uint16_t lds[NG * 2 * L::BUF_ELEMS];
@@ -264,49 +274,55 @@ void flash_fwd_bf16_kernel(Params p)
     const int l32 = lane & 31, hh = lane >> 5;
     const int rh = p.rot_dim / 2;   // table row stride
 
-    // ---------------- staging plan (fixed for the whole launch) ----------------
-    // k_mode: -1 no slot, 0 copy, 1 NeoX rotate (lo, hi), 2 GPT-J rotate.
-    // k_o0/k_o1 = element offsets of the two chunks inside a K tile, k_to =
-    // offset of the cos/sin slice inside the tile's block of table rows.
-    int k_row[KI], k_mode[KI], k_o0[KI], k_o1[KI], k_to[KI];
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-        const int item = gtid + 256 * i;
+    // ---------------- staging plans ----------------
+    // A K item is one slot of a key row: mode -1 no slot, 0 copy, 1 NeoX
+    // rotate (lo, hi), 2 GPT-J rotate; o0/o1 = element offsets of its two
+    // chunks inside a K tile, to = offset of its cos/sin slice inside the
+    // tile's block of table rows.  A V item is one 16-byte chunk.
+    auto k_item = [&](int item) {
+        KItem it;
         const int row = item / Plan::SLOTS_PER_ROW;
         const int slot = item % Plan::SLOTS_PER_ROW;
         int d0 = 0, d1 = 0;
-        k_row[i] = row;
+        it.row = row;
         if (item >= Plan::SLOTS) {
-            k_mode[i] = -1;
+            it.mode = -1;
         } else if constexpr (Plan::NEOX_SLOT) {
             const int rslots = p.rot_dim / 16;
             if (slot < rslots) {
-                k_mode[i] = 1;                            // rotate (lo, hi)
+                it.mode = 1;                            // rotate (lo, hi)
                 d0 = 8 * slot;
                 d1 = 8 * slot + rh;
             } else {
-                k_mode[i] = 0;                            // copy two chunks
+                it.mode = 0;                            // copy two chunks
                 d0 = p.rot_dim + 16 * (slot - rslots);
                 d1 = d0 + 8;
             }
         } else {
-            k_mode[i] = (ROT && 8 * slot < p.rot_dim) ? 2 : 0;
-            d0 = 8 * slot;
+            it.mode = (ROT && 16 * slot < p.rot_dim) ? 2 : 0;
+            d0 = 16 * slot;
+            d1 = d0 + 8;
         }
-        k_o0[i] = row * D + d0;
-        k_o1[i] = row * D + d1;
-        k_to[i] = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
-    }
-    int v_row[VI], v_o[VI], v_l[VI];
-    bool v_ok[VI];
+        it.o0 = row * D + d0;
+        it.o1 = row * D + d1;
+        it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
+        return it;
+    };
+    auto v_item = [&](int item) {
+        VItem it;
+        it.ok = item < VSLOTS;
+        it.row = item / (D / 8);
+        it.o = it.row * D + 8 * (item % (D / 8));     // global offset inside the tile
+        it.l = it.row * VP + 8 * (item % (D / 8));    // LDS offset
+        return it;
+    };
+    // Plan A: the 256 threads of a group share a tile.
+    KItem kpa[KI];
+    VItem vpa[VI];
 #pragma unroll
-    for (int i = 0; i < VI; ++i) {
-        const int item = gtid + 256 * i;
-        v_ok[i] = item < VSLOTS;
-        v_row[i] = item / (D / 8);
-        v_o[i] = v_row[i] * D + 8 * (item % (D / 8));     // global offset inside the tile
-        v_l[i] = v_row[i] * VP + 8 * (item % (D / 8));    // LDS offset
-    }
+    for (int i = 0; i < KI; ++i) kpa[i] = k_item(gtid + 256 * i);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) vpa[i] = v_item(gtid + 256 * i);
 
     // V^T operand addressing for ds_read_b64_tr_b16: in each 16-lane group
     // the source lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving
@@ -398,14 +414,13 @@ void flash_fwd_bf16_kernel(Params p)
         const int64_t wq_last = (wq0 + 31 < p.Sq ? wq0 + 31 : p.Sq - 1);
         const bool wave_has_rows = wq0 < p.Sq;
 
-        uint4 kr0[KI], kr1[KI];
-        float kc[KI][8], ks[KI][8];
-        uint4 vr[VI];
-
-        // Global loads of one key tile into registers: uniform per-tile base
-        // pointers, fixed 32-bit per-thread offsets; row bounds are checked
-        // only on the ragged last tile.
-        auto fetch = [&](int64_t kt) {
+        // Global loads of one key tile's items into registers: uniform
+        // per-tile base pointers, fixed per-thread offsets; row bounds are
+        // checked only on the ragged last tile.
+        auto fetch_items = [&](int64_t kt, const auto &ki, const auto &vi, auto &r0, auto &r1, auto &kc,
+                               auto &ks, auto &vr) {
+            constexpr int NK = sizeof(ki) / sizeof(ki[0]);
+            constexpr int NV = sizeof(vi) / sizeof(vi[0]);
             const int64_t j0 = kt * BN;
             const uint16_t *kbase = kh + j0 * D;
             const uint16_t *vbase = vh + j0 * D;
@@ -413,67 +428,101 @@ void flash_fwd_bf16_kernel(Params p)
             const int rows = left < BN ? (int)left : BN;
             const bool fullt = rows == BN;
 #pragma unroll
-            for (int i = 0; i < KI; ++i) {
-                if (k_mode[i] < 0) continue;
-                const bool ok = fullt || k_row[i] < rows;
-                kr0[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + k_o0[i]) : make_uint4(0, 0, 0, 0);
-                if constexpr (Plan::NEOX_SLOT)
-                    kr1[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + k_o1[i]) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < NK; ++i) {
+                if (ki[i].mode < 0) continue;
+                const bool ok = fullt || ki[i].row < rows;
+                r0[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + ki[i].o0) : make_uint4(0, 0, 0, 0);
+                r1[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + ki[i].o1) : make_uint4(0, 0, 0, 0);
                 if constexpr (ROT) {
-                    if (ok && k_mode[i] != 0) {
-                        const float *cr = p.cos_tab + (p.k_off + j0) * rh + k_to[i];
-                        const float *sr = p.sin_tab + (p.k_off + j0) * rh + k_to[i];
+                    if (ok && ki[i].mode != 0) {
+                        const float *cr = p.cos_tab + (p.k_off + j0) * rh + ki[i].to;
+                        const float *sr = p.sin_tab + (p.k_off + j0) * rh + ki[i].to;
                         *reinterpret_cast<float4 *>(kc[i]) = ld4(cr);
                         *reinterpret_cast<float4 *>(ks[i]) = ld4(sr);
-                        if constexpr (LAYOUT == 0) {
-                            *reinterpret_cast<float4 *>(kc[i] + 4) = ld4(cr + 4);
-                            *reinterpret_cast<float4 *>(ks[i] + 4) = ld4(sr + 4);
-                        }
+                        *reinterpret_cast<float4 *>(kc[i] + 4) = ld4(cr + 4);
+                        *reinterpret_cast<float4 *>(ks[i] + 4) = ld4(sr + 4);
                     }
                 }
             }
 #pragma unroll
-            for (int i = 0; i < VI; ++i) {
-                const bool ok = v_ok[i] && (fullt || v_row[i] < rows);
-                vr[i] = ok ? *reinterpret_cast<const uint4 *>(vbase + v_o[i]) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < NV; ++i) {
+                const bool ok = vi[i].ok && (fullt || vi[i].row < rows);
+                vr[i] = ok ? *reinterpret_cast<const uint4 *>(vbase + vi[i].o) : make_uint4(0, 0, 0, 0);
             }
         };
 
-        // Rotate the fetched K tile, round to bf16 and write K and V to LDS.
-        auto stage = [&](int buf) {
+        // Rotate fetched K items, round to bf16 and write K and V to LDS.
+        auto stage_items = [&](int buf, const auto &ki, const auto &vi, const auto &r0, const auto &r1,
+                               const auto &kc, const auto &ks, const auto &vr) {
+            constexpr int NK = sizeof(ki) / sizeof(ki[0]);
+            constexpr int NV = sizeof(vi) / sizeof(vi[0]);
             uint16_t *kdst = lds + (group * 2 + buf) * L::BUF_ELEMS;
 #pragma unroll
-            for (int i = 0; i < KI; ++i) {
-                if (k_mode[i] < 0) continue;
+            for (int i = 0; i < NK; ++i) {
+                if (ki[i].mode < 0) continue;
                 // LDS rows have pitch KP; the chunk offsets inside a row are
-                // k_o - k_row * D.
-                uint16_t *row = kdst + k_row[i] * KP - k_row[i] * D;
-                if (k_mode[i] == 1) {
-                    float lo[8], hi[8];
-                    unpack8(kr0[i], lo);
-                    unpack8(kr1[i], hi);
-                    rotate_pairs<8>(lo, hi, kc[i], ks[i]);
-                    *reinterpret_cast<uint4 *>(row + k_o0[i]) = pack8(lo);
-                    *reinterpret_cast<uint4 *>(row + k_o1[i]) = pack8(hi);
-                } else if (k_mode[i] == 2) {
-                    float x[8], a[4], b[4];
-                    unpack8(kr0[i], x);
+                // o - row * D.
+                uint16_t *row = kdst + ki[i].row * KP - ki[i].row * D;
+                if (ROT && LAYOUT == 0 && ki[i].mode == 1) {
+                    float lo[8], hi[8], c[8], sn[8];
+                    unpack8(r0[i], lo);
+                    unpack8(r1[i], hi);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) { a[u] = x[2 * u]; b[u] = x[2 * u + 1]; }
-                    rotate_pairs<4>(a, b, kc[i], ks[i]);
+                    for (int u = 0; u < 8; ++u) { c[u] = kc[i][u]; sn[u] = ks[i][u]; }
+                    rotate_pairs<8>(lo, hi, c, sn);
+                    *reinterpret_cast<uint4 *>(row + ki[i].o0) = pack8(lo);
+                    *reinterpret_cast<uint4 *>(row + ki[i].o1) = pack8(hi);
+                } else if (ROT && LAYOUT == 1 && ki[i].mode == 2) {
+                    // chunk h holds pairs 4h .. 4h+3 of the slot's 8
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) { x[2 * u] = a[u]; x[2 * u + 1] = b[u]; }
-                    *reinterpret_cast<uint4 *>(row + k_o0[i]) = pack8(x);
+                    for (int h = 0; h < 2; ++h) {
+                        float x[8], a[4], b[4], c[4], sn[4];
+                        unpack8(h ? r1[i] : r0[i], x);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            a[u] = x[2 * u]; b[u] = x[2 * u + 1]; c[u] = kc[i][4 * h + u]; sn[u] = ks[i][4 * h + u];
+                        }
+                        rotate_pairs<4>(a, b, c, sn);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) { x[2 * u] = a[u]; x[2 * u + 1] = b[u]; }
+                        *reinterpret_cast<uint4 *>(row + (h ? ki[i].o1 : ki[i].o0)) = pack8(x);
+                    }
                 } else {
-                    *reinterpret_cast<uint4 *>(row + k_o0[i]) = kr0[i];
-                    if constexpr (Plan::NEOX_SLOT) *reinterpret_cast<uint4 *>(row + k_o1[i]) = kr1[i];
+                    *reinterpret_cast<uint4 *>(row + ki[i].o0) = r0[i];
+                    *reinterpret_cast<uint4 *>(row + ki[i].o1) = r1[i];
                 }
             }
             uint16_t *vdst = kdst + L::K_ELEMS;
 #pragma unroll
-            for (int i = 0; i < VI; ++i)
-                if (v_ok[i]) *reinterpret_cast<uint4 *>(vdst + v_l[i]) = vr[i];
+            for (int i = 0; i < NV; ++i)
+                if (vi[i].ok) *reinterpret_cast<uint4 *>(vdst + vi[i].l) = vr[i];
         };
+
+        // Plan A registers: one tile of this group in flight.
+        uint4 kr0[KI], kr1[KI];
+        float kc[KI][NFK], ks[KI][NFK];
+        uint4 vr[VI];
+        auto fetch = [&](int64_t kt) { fetch_items(kt, kpa, vpa, kr0, kr1, kc, ks, vr); };
+        auto stage = [&](int buf) { stage_items(buf, kpa, vpa, kr0, kr1, kc, ks, vr); };
+
+        // Plan B (tiles only the heavy half's rows see): the light half's two
+        // waves of this group fetch, rotate and stage whole tiles alone, one
+        // tile ahead, so the heavy half's waves spend those iterations on
+        // matrix-core work.  Items are split over the light pair's 128 threads.
+        const int ltid = (wave & 1) * 64 + lane;
+        constexpr int KIB = (Plan::SLOTS + 127) / 128, VIB = (VSLOTS + 127) / 128;
+        KItem kpb[KIB];
+        VItem vpb[VIB];
+        uint4 b0[KIB], b1[KIB], bv[VIB];
+        float bc[KIB][NFK], bs[KIB][NFK];
+        auto fetch_light = [&](int64_t kt) {
+#pragma unroll
+            for (int i = 0; i < KIB; ++i) kpb[i] = k_item(ltid + 128 * i);
+#pragma unroll
+            for (int i = 0; i < VIB; ++i) vpb[i] = v_item(ltid + 128 * i);
+            fetch_items(kt, kpb, vpb, b0, b1, bc, bs, bv);
+        };
+        auto stage_light = [&](int buf) { stage_items(buf, kpb, vpb, b0, b1, bc, bs, bv); };
 
         // ---- running state ----
         f32x16_t oacc[DB];
@@ -604,25 +653,61 @@ void flash_fwd_bf16_kernel(Params p)
         // a SIMD are in different phases (matrix-core work against
         // rotation/softmax VALU work).
         const int64_t n_iter = (ke - kb + NG - 1) / NG;
+        // Tiles from x_light on are seen by the heavy half's rows only (the
+        // light half's last visible tile is below x_light - NG, so its waves
+        // have stopped computing by the time they stage them).
+        const bool light = half == 0;
+        int64_t x_light = ke + NG;   // no light-only staging
+        // (the two-group shape only: with one key group at D = 128 the light
+        // waves' extra registers would spill)
+        constexpr bool OFFLOAD = NG == 2 && !BAL;
+        if (OFFLOAD && rowB < p.Sq) {
+            const int64_t lastA = rowA + 63 < p.Sq ? rowA + 63 : p.Sq - 1;
+            x_light = row_visits(p, lastA) + NG;
+        }
         if (kb + group < ke) {
             fetch(kb + group);
             stage(0);
         }
-        if (group == 1 && kb + group + NG < ke) fetch(kb + group + NG);
+        if (group == 1 && kb + group + NG < ke && kb + group + NG < x_light) fetch(kb + group + NG);
 
-        for (int64_t it = 0; it < n_iter; ++it) {
+
+        // Phase 1: every wave of the group fetches and stages its share of
+        // the next tile (plan A).  Phase 2 (the group's next tile is at or
+        // past x_light): the light waves stage whole tiles alone (plan B) and
+        // the heavy waves only compute.  Both phases run one barrier per
+        // iteration, so every wave reaches the same barrier count whatever
+        // its split point.
+        int64_t it = 0;
+        for (; it < n_iter; ++it) {
+            const int64_t kt = kb + it * NG + group;
+            const int64_t nxt = kt + NG;              // the tile this group stages now
+            if (nxt < ke && nxt >= x_light) break;
             const int buf = (int)(it & 1);
             __syncthreads();   // this iteration's tiles staged; the previous ones consumed
-            const int64_t kt = kb + it * NG + group;
             if (group == 0) {
-                const bool more = kt + NG < ke;
-                if (more) fetch(kt + NG);
+                const bool more = nxt < ke;
+                if (more) fetch(nxt);
                 if (kt < ke) compute(kt, buf);
                 if (more) stage(buf ^ 1);
             } else {
-                if (kt + NG < ke) stage(buf ^ 1);
-                if (kt + 2 * NG < ke) fetch(kt + 2 * NG);
+                if (nxt < ke) stage(buf ^ 1);
+                if (nxt + NG < ke && nxt + NG < x_light) fetch(nxt + NG);
                 if (kt < ke) compute(kt, buf);
+            }
+        }
+        if constexpr (OFFLOAD) {
+            if (light && it < n_iter && kb + it * NG + group + NG < ke) fetch_light(kb + it * NG + group + NG);
+            for (; it < n_iter; ++it) {
+                const int64_t kt = kb + it * NG + group;
+                const int buf = (int)(it & 1);
+                __syncthreads();
+                if (light) {   // these rows see none of the remaining tiles
+                    if (kt + NG < ke) stage_light(buf ^ 1);
+                    if (kt + 2 * NG < ke) fetch_light(kt + 2 * NG);
+                } else if (kt < ke) {
+                    compute(kt, buf);
+                }
             }
         }
 
