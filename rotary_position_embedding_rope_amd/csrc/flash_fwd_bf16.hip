@@ -413,6 +413,24 @@ void flash_fwd_bf16_kernel(Params p)
 
         const int64_t wq_last = (wq0 + 31 < p.Sq ? wq0 + 31 : p.Sq - 1);
         const bool wave_has_rows = wq0 < p.Sq;
+        // Per-wave tile bounds, so the tile loop needs no 64-bit position
+        // arithmetic: this wave computes tiles [0, kt_end) and masks tiles
+        // from kt_mask on (the one straddling its diagonal, or the ragged
+        // last tile); lane key limit: key j is visible iff j <= lim_base.
+        const int kt_end = wave_has_rows ? (int)row_visits(p, wq_last) : 0;
+        int kt_mask = (int)(p.Sk / BN);            // the ragged tile, or n_kt if none
+        int lim_base = (int)(p.Sk - 1);
+        if (p.causal) {
+            const int64_t delta = p.q_off - p.k_off;   // >= 0
+            const int64_t x = delta + wq0 + 1 - BN;
+            const int64_t kc = x < 0 ? 0 : x / BN + 1;
+            if (kc < kt_mask) kt_mask = (int)kc;
+            const int64_t c = delta + qrow;
+            if (c < lim_base) lim_base = (int)c;
+        }
+        // cos/sin rows of this segment's keys start at position k_off
+        const float *ctab = ROT ? p.cos_tab + p.k_off * rh : nullptr;
+        const float *stab = ROT ? p.sin_tab + p.k_off * rh : nullptr;
 
         // Global loads of one key tile's items into registers: uniform
         // per-tile base pointers, fixed per-thread offsets; row bounds are
@@ -421,11 +439,11 @@ void flash_fwd_bf16_kernel(Params p)
                                auto &ks, auto &vr) {
             constexpr int NK = sizeof(ki) / sizeof(ki[0]);
             constexpr int NV = sizeof(vi) / sizeof(vi[0]);
-            const int64_t j0 = kt * BN;
-            const uint16_t *kbase = kh + j0 * D;
-            const uint16_t *vbase = vh + j0 * D;
-            const int64_t left = p.Sk - j0;
-            const int rows = left < BN ? (int)left : BN;
+            const int j0 = (int)kt * BN;
+            const uint16_t *kbase = kh + (int64_t)j0 * D;
+            const uint16_t *vbase = vh + (int64_t)j0 * D;
+            const int left = (int)p.Sk - j0;
+            const int rows = left < BN ? left : BN;
             const bool fullt = rows == BN;
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
@@ -435,8 +453,8 @@ void flash_fwd_bf16_kernel(Params p)
                 r1[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + ki[i].o1) : make_uint4(0, 0, 0, 0);
                 if constexpr (ROT) {
                     if (ok && ki[i].mode != 0) {
-                        const float *cr = p.cos_tab + (p.k_off + j0) * rh + ki[i].to;
-                        const float *sr = p.sin_tab + (p.k_off + j0) * rh + ki[i].to;
+                        const float *cr = ctab + (int64_t)j0 * rh + ki[i].to;
+                        const float *sr = stab + (int64_t)j0 * rh + ki[i].to;
                         *reinterpret_cast<float4 *>(kc[i]) = ld4(cr);
                         *reinterpret_cast<float4 *>(ks[i]) = ld4(sr);
                         *reinterpret_cast<float4 *>(kc[i] + 4) = ld4(cr + 4);
@@ -538,11 +556,10 @@ void flash_fwd_bf16_kernel(Params p)
         f32x16_t cinit = (f32x16_t){};
 
         // One key tile of this group: S', softmax update, O += V^T P^T.
-        auto compute = [&](int64_t kt, int buf) {
-            const int64_t j0 = kt * BN;
-            const bool wave_active =
-                wave_has_rows && (!p.causal || p.k_off + j0 <= p.q_off + wq_last);
-            if (!wave_active) return;
+        auto compute = [&](int64_t kt64, int buf) {
+            const int kt = (int)kt64;
+            const int j0 = kt * BN;
+            if (kt >= kt_end) return;   // no row of this wave sees the tile
             const uint16_t *kb_lds = lds + (group * 2 + buf) * L::BUF_ELEMS;
             const uint16_t *v_lds = kb_lds + L::K_ELEMS;
             // S' = K Q'^T - m_ref: NKB 32-key blocks x 32 queries.
@@ -558,16 +575,10 @@ void flash_fwd_bf16_kernel(Params p)
                 }
             }
             // accumulator element r of block kb2 <-> key j0 + 32kb2 + 8(r/4) + 4hh + r%4
-            const bool need_mask = (j0 + BN > p.Sk) ||
-                                   (p.causal && p.k_off + j0 + BN - 1 > p.q_off + wq0);
-            if (need_mask) {
+            if (kt >= kt_mask) {
                 // key j0 + kk is visible iff kk <= lim (kk: index inside the tile)
-                int64_t lim64 = p.Sk - 1 - j0;
-                if (p.causal) {
-                    const int64_t c = p.q_off + qrow - p.k_off - j0;
-                    lim64 = c < lim64 ? c : lim64;
-                }
-                const int lim = lim64 < -1 ? -1 : (lim64 > BN ? BN : (int)lim64);
+                const int lim0 = lim_base - j0;
+                const int lim = lim0 < -1 ? -1 : (lim0 > BN ? BN : lim0);
                 const int lim_h = lim - 4 * hh;
 #pragma unroll
                 for (int kb2 = 0; kb2 < NKB; ++kb2)
