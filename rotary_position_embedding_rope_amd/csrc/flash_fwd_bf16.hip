@@ -528,7 +528,7 @@ void flash_fwd_bf16_kernel(Params p)
         // tile ahead, so the heavy half's waves spend those iterations on
         // matrix-core work.  Items are split over the light pair's 128 threads.
         const int ltid = (wave & 1) * 64 + lane;
-        constexpr int KIB = (Plan::SLOTS + 127) / 128, VIB = (VSLOTS + 127) / 128;
+        constexpr int KIB = (Plan::SLOTS + 127) / 128, VIB = (VSLOTS / 2 + 127) / 128;
         KItem kpb[KIB];
         VItem vpb[VIB];
         uint4 b0[KIB], b1[KIB], bv[VIB];
@@ -541,6 +541,18 @@ void flash_fwd_bf16_kernel(Params p)
             fetch_items(kt, kpb, vpb, b0, b1, bc, bs, bv);
         };
         auto stage_light = [&](int buf) { stage_items(buf, kpb, vpb, b0, b1, bc, bs, bv); };
+        // the other half of the V chunks: the heavy pair, one tile ahead
+        KItem knone[1];
+        knone[0].mode = -1; knone[0].row = 0; knone[0].o0 = 0; knone[0].o1 = 0; knone[0].to = 0;
+        VItem vph[VIB];
+        uint4 hv[VIB], hk0[1], hk1[1];
+        float hkc[1][NFK], hks[1][NFK];
+        auto fetch_heavy = [&](int64_t kt) {
+#pragma unroll
+            for (int i = 0; i < VIB; ++i) vph[i] = v_item(VSLOTS / 2 + ltid + 128 * i);
+            fetch_items(kt, knone, vph, hk0, hk1, hkc, hks, hv);
+        };
+        auto stage_heavy = [&](int buf) { stage_items(buf, knone, vph, hk0, hk1, hkc, hks, hv); };
 
         // ---- running state ----
         f32x16_t oacc[DB];
@@ -708,7 +720,10 @@ void flash_fwd_bf16_kernel(Params p)
             }
         }
         if constexpr (OFFLOAD) {
-            if (light && it < n_iter && kb + it * NG + group + NG < ke) fetch_light(kb + it * NG + group + NG);
+            if (it < n_iter && kb + it * NG + group + NG < ke) {
+                if (light) fetch_light(kb + it * NG + group + NG);
+                else fetch_heavy(kb + it * NG + group + NG);
+            }
             for (; it < n_iter; ++it) {
                 const int64_t kt = kb + it * NG + group;
                 const int buf = (int)(it & 1);
@@ -716,8 +731,10 @@ void flash_fwd_bf16_kernel(Params p)
                 if (light) {   // these rows see none of the remaining tiles
                     if (kt + NG < ke) stage_light(buf ^ 1);
                     if (kt + 2 * NG < ke) fetch_light(kt + 2 * NG);
-                } else if (kt < ke) {
-                    compute(kt, buf);
+                } else {
+                    if (kt + NG < ke) stage_heavy(buf ^ 1);
+                    if (kt + 2 * NG < ke) fetch_heavy(kt + 2 * NG);
+                    if (kt < ke) compute(kt, buf);
                 }
             }
         }
