@@ -80,6 +80,7 @@ struct Params {
     int BH;
     int64_t Sq, Sk, q_off, k_off;
     const float *cos_tab, *sin_tab;
+    int64_t table_rows;
     int rot_dim;
     float sl2;          // softmax scale * log2(e)
     int causal;
@@ -213,6 +214,30 @@ __device__ __forceinline__ float sum_with_partner(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Raw buffer access: one descriptor per tensor slice, carrying the slice's
+// exact byte length.  A load at or past that length returns zeros, so a
+// ragged last tile needs no per-lane row checks and no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;   // untyped 32-bit buffer (gfx9 family)
+
+// `rows` rows of `row_bytes` bytes from `base` (rows <= 0: empty; lengths
+// past 4 GiB are capped, far beyond the few KiB one tile addresses).
+template <int ROW_BYTES>
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int rows)
+{
+    constexpr int MAX_ROWS = (int)(0xffffffffu / ROW_BYTES);
+    const uint32_t n = rows <= 0 ? 0u : (rows >= MAX_ROWS ? 0xffffffffu : (uint32_t)rows * ROW_BYTES);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, RSRC_FLAGS);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, int byte_off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float4 bload16f(rsrc_t r, int byte_off)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // Per-thread staging plan for K tiles (fixed across tiles).  A slot is two
 // 8-dim chunks of one key row, D/16 slots per row:
 //   NeoX: a rotated pair of chunks (lo at 8c, hi at 8c + rot/2), or two
@@ -228,59 +253,68 @@ struct KPlan {
     static constexpr int ITEMS = (SLOTS + 255) / 256;   // per thread (the last may be empty)
 };
 
-template <int D, int BN>
-struct Lds {
-    static constexpr int KP = D + KPAD;
-    static constexpr int K_ELEMS = BN * KP;
-    static constexpr int V_ELEMS = BN * VP;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;   // one K + one V tile
-};
-
 struct KItem {
     int row, mode, o0, o1, to;
 };
 struct VItem {
-    int row, o, l;
+    int o, l;
     bool ok;
 };
 
+// Row sums of one tile's probabilities (this lane's keys) up to this bound
+// are taken without looking at the row max: every probability is then at
+// most 2^13, far from fp32/bf16 overflow, and the reference the scores are
+// measured against only ever rises.  A larger sum sends the tile to the
+// exact path (true row max, lazy rescale).
+constexpr float FAST_SUM_LIMIT = 8192.0f;
+
 // D: head dim; BN: keys per tile (32 or 64); NG: key groups per workgroup;
-// BAL: the balanced schedule (a separate instantiation, so the default
-// kernel does not carry its share-walking code).
-template <int D, int LAYOUT, bool ROT, int NG, int BN, bool BAL>
+// FULL: rot_dim == D (every K slot rotates); BAL: the balanced schedule (a
+// separate instantiation, so the default kernel does not carry its
+// share-walking code).
+template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, bool BAL>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_bf16_kernel(Params p)
 {
     using Plan = KPlan<D, LAYOUT, ROT, BN>;
-    using L = Lds<D, BN>;
     constexpr int NKB = BN / 32;                    // 32-key blocks per tile
-    constexpr int KP = L::KP;
+    constexpr int KP = D + KPAD;                    // K LDS row pitch
+    constexpr int K_ELEMS = BN * KP, V_ELEMS = BN * VP;
     constexpr int KI = Plan::ITEMS;                 // K slots per thread per tile
     constexpr int VSLOTS = BN * (D / 8);            // V 16-byte chunks per tile
     constexpr int VI = (VSLOTS + 255) / 256;        // per thread (the last may be empty)
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
     constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
-    constexpr int NFK = 8;                          // cos/sin values per K item
 
-    // [group][buffer][K tile | V tile]
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NG * 2 * L::BUF_ELEMS];
+    // [group][buffer] K tiles, then [group][buffer] V tiles.  K runs one tile
+    // ahead of V: while tile t's probabilities are formed, the scores of
+    // tile t+NG are computed from the other K buffer.
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NG * 2 * (K_ELEMS + V_ELEMS)];
 
     const int tid = threadIdx.x;
-    const int group = tid >> 8;
+    // group and wave are uniform across a wave; saying so keeps every
+    // tile-level quantity (and the buffer descriptors) in scalar registers
+    const int group = __builtin_amdgcn_readfirstlane(tid >> 8);
     const int gtid = tid & 255;                     // thread index inside the group
     const int lane = tid & 63;
-    const int wave = gtid >> 6;                     // wave inside the group
+    const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);   // wave inside the group
     const int l32 = lane & 31, hh = lane >> 5;
     const int rh = p.rot_dim / 2;   // table row stride
+    auto kbuf = [&](int b) { return lds + (group * 2 + b) * K_ELEMS; };
+    auto vbuf = [&](int b) { return lds + NG * 2 * K_ELEMS + (group * 2 + b) * V_ELEMS; };
 
     // ---------------- staging plans ----------------
     // A K item is one slot of a key row: mode -1 no slot, 0 copy, 1 NeoX
     // rotate (lo, hi), 2 GPT-J rotate; o0/o1 = element offsets of its two
     // chunks inside a K tile, to = offset of its cos/sin slice inside the
     // tile's block of table rows.  A V item is one 16-byte chunk.
-    auto k_item = [&](int item) {
-        KItem it;
+    KItem kpa[KI];
+    VItem vpa[VI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int item = gtid + 256 * i;
+        KItem &it = kpa[i];
         const int row = item / Plan::SLOTS_PER_ROW;
         const int slot = item % Plan::SLOTS_PER_ROW;
         int d0 = 0, d1 = 0;
@@ -306,23 +340,15 @@ void flash_fwd_bf16_kernel(Params p)
         it.o0 = row * D + d0;
         it.o1 = row * D + d1;
         it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
-        return it;
-    };
-    auto v_item = [&](int item) {
-        VItem it;
-        it.ok = item < VSLOTS;
-        it.row = item / (D / 8);
-        it.o = it.row * D + 8 * (item % (D / 8));     // global offset inside the tile
-        it.l = it.row * VP + 8 * (item % (D / 8));    // LDS offset
-        return it;
-    };
-    // Plan A: the 256 threads of a group share a tile.
-    KItem kpa[KI];
-    VItem vpa[VI];
+    }
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kpa[i] = k_item(gtid + 256 * i);
-#pragma unroll
-    for (int i = 0; i < VI; ++i) vpa[i] = v_item(gtid + 256 * i);
+    for (int i = 0; i < VI; ++i) {
+        const int item = gtid + 256 * i;
+        const int row = item / (D / 8);
+        vpa[i].ok = item < VSLOTS;
+        vpa[i].o = row * D + 8 * (item % (D / 8));     // element offset inside the tile
+        vpa[i].l = row * VP + 8 * (item % (D / 8));    // LDS offset
+    }
 
     // V^T operand addressing for ds_read_b64_tr_b16: in each 16-lane group
     // the source lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving
@@ -431,128 +457,104 @@ void flash_fwd_bf16_kernel(Params p)
         // cos/sin rows of this segment's keys start at position k_off
         const float *ctab = ROT ? p.cos_tab + p.k_off * rh : nullptr;
         const float *stab = ROT ? p.sin_tab + p.k_off * rh : nullptr;
+        const int sk32 = (int)p.Sk;
+        // table rows from position k_off on (k_off + Sk <= table_rows < 2^31
+        // is not required: the count is capped at the int range)
+        const int64_t trk = p.table_rows - p.k_off;
+        const int tab_rows_k = (int)(trk < 0x7fffffffLL ? trk : 0x7fffffffLL);
 
-        // Global loads of one key tile's items into registers: uniform
-        // per-tile base pointers, fixed per-thread offsets; row bounds are
-        // checked only on the ragged last tile.
-        auto fetch_items = [&](int64_t kt, const auto &ki, const auto &vi, auto &r0, auto &r1, auto &kc,
-                               auto &ks, auto &vr) {
-            constexpr int NK = sizeof(ki) / sizeof(ki[0]);
-            constexpr int NV = sizeof(vi) / sizeof(vi[0]);
-            const int j0 = (int)kt * BN;
-            const uint16_t *kbase = kh + (int64_t)j0 * D;
-            const uint16_t *vbase = vh + (int64_t)j0 * D;
-            const int left = (int)p.Sk - j0;
-            const int rows = left < BN ? left : BN;
-            const bool fullt = rows == BN;
+        // ---- K/V pipeline registers (one K tile and one V tile in flight) ----
+        uint4 kr0[KI], kr1[KI];
+        float kc[KI][8], ks[KI][8];
+        uint4 vr[VI];
+        // Global loads of key tile kt's K items (with their table rows) and
+        // of value tile kt's V items.  Rows past Sk (and table rows past the
+        // table) read as zeros.
+        auto fetch_k = [&](int kt) {
+            const int j0 = kt * BN;
+            const rsrc_t krs = make_rsrc<2 * D>(kh + (int64_t)j0 * D, sk32 - j0);
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                if (ki[i].mode < 0) continue;
-                const bool ok = fullt || ki[i].row < rows;
-                r0[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + ki[i].o0) : make_uint4(0, 0, 0, 0);
-                r1[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + ki[i].o1) : make_uint4(0, 0, 0, 0);
-                if constexpr (ROT) {
-                    if (ok && ki[i].mode != 0) {
-                        const float *cr = ctab + (int64_t)j0 * rh + ki[i].to;
-                        const float *sr = stab + (int64_t)j0 * rh + ki[i].to;
-                        *reinterpret_cast<float4 *>(kc[i]) = ld4(cr);
-                        *reinterpret_cast<float4 *>(ks[i]) = ld4(sr);
-                        *reinterpret_cast<float4 *>(kc[i] + 4) = ld4(cr + 4);
-                        *reinterpret_cast<float4 *>(ks[i] + 4) = ld4(sr + 4);
-                    }
+            for (int i = 0; i < KI; ++i) {
+                if (kpa[i].mode < 0) continue;
+                kr0[i] = bload16(krs, 2 * kpa[i].o0);
+                kr1[i] = bload16(krs, 2 * kpa[i].o1);
+            }
+            if constexpr (ROT) {
+                // table rows are rot_dim/2 floats: descriptors count
+                // 16-byte units (rh is a multiple of 16)
+                const int left = tab_rows_k - j0;   // a tile reads at most BN of them
+                const int trows = (left < BN ? left : BN) * (rh / 4);
+                const rsrc_t crs = make_rsrc<16>(ctab + (int64_t)j0 * rh, trows);
+                const rsrc_t srs = make_rsrc<16>(stab + (int64_t)j0 * rh, trows);
+#pragma unroll
+                for (int i = 0; i < KI; ++i) {
+                    if (kpa[i].mode < 0) continue;
+                    const int to = 4 * kpa[i].to;
+                    *reinterpret_cast<float4 *>(kc[i]) = bload16f(crs, to);
+                    *reinterpret_cast<float4 *>(ks[i]) = bload16f(srs, to);
+                    *reinterpret_cast<float4 *>(kc[i] + 4) = bload16f(crs, to + 16);
+                    *reinterpret_cast<float4 *>(ks[i] + 4) = bload16f(srs, to + 16);
                 }
             }
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const bool ok = vi[i].ok && (fullt || vi[i].row < rows);
-                vr[i] = ok ? *reinterpret_cast<const uint4 *>(vbase + vi[i].o) : make_uint4(0, 0, 0, 0);
-            }
         };
-
-        // Rotate fetched K items, round to bf16 and write K and V to LDS.
-        auto stage_items = [&](int buf, const auto &ki, const auto &vi, const auto &r0, const auto &r1,
-                               const auto &kc, const auto &ks, const auto &vr) {
-            constexpr int NK = sizeof(ki) / sizeof(ki[0]);
-            constexpr int NV = sizeof(vi) / sizeof(vi[0]);
-            uint16_t *kdst = lds + (group * 2 + buf) * L::BUF_ELEMS;
+        auto fetch_v = [&](int kt) {
+            const int j0 = kt * BN;
+            const rsrc_t vrs = make_rsrc<2 * D>(vh + (int64_t)j0 * D, sk32 - j0);
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                if (ki[i].mode < 0) continue;
+            for (int i = 0; i < VI; ++i)
+                if (vpa[i].ok) vr[i] = bload16(vrs, 2 * vpa[i].o);
+        };
+        // Rotate the fetched K items in fp32 at their key positions, round to
+        // bf16 and write them to K buffer b.
+        auto stage_k = [&](int b) {
+            uint16_t *kdst = kbuf(b);
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                if (kpa[i].mode < 0) continue;
                 // LDS rows have pitch KP; the chunk offsets inside a row are
                 // o - row * D.
-                uint16_t *row = kdst + ki[i].row * KP - ki[i].row * D;
-                if (ROT && LAYOUT == 0 && ki[i].mode == 1) {
-                    float lo[8], hi[8], c[8], sn[8];
-                    unpack8(r0[i], lo);
-                    unpack8(r1[i], hi);
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) { c[u] = kc[i][u]; sn[u] = ks[i][u]; }
-                    rotate_pairs<8>(lo, hi, c, sn);
-                    *reinterpret_cast<uint4 *>(row + ki[i].o0) = pack8(lo);
-                    *reinterpret_cast<uint4 *>(row + ki[i].o1) = pack8(hi);
-                } else if (ROT && LAYOUT == 1 && ki[i].mode == 2) {
+                uint16_t *row = kdst + kpa[i].row * (KP - D);
+                uint4 w0 = kr0[i], w1 = kr1[i];
+                if constexpr (ROT && LAYOUT == 0) {
+                    float lo[8], hi[8];
+                    unpack8(kr0[i], lo);
+                    unpack8(kr1[i], hi);
+                    rotate_pairs<8>(lo, hi, kc[i], ks[i]);
+                    w0 = pack8(lo);
+                    w1 = pack8(hi);
+                } else if constexpr (ROT && LAYOUT == 1) {
                     // chunk h holds pairs 4h .. 4h+3 of the slot's 8
+                    float x[2][8];
+                    unpack8(kr0[i], x[0]);
+                    unpack8(kr1[i], x[1]);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        float x[8], a[4], b[4], c[4], sn[4];
-                        unpack8(h ? r1[i] : r0[i], x);
+                        float a[4], bb[4];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            a[u] = x[2 * u]; b[u] = x[2 * u + 1]; c[u] = kc[i][4 * h + u]; sn[u] = ks[i][4 * h + u];
-                        }
-                        rotate_pairs<4>(a, b, c, sn);
+                        for (int u = 0; u < 4; ++u) { a[u] = x[h][2 * u]; bb[u] = x[h][2 * u + 1]; }
+                        rotate_pairs<4>(a, bb, kc[i] + 4 * h, ks[i] + 4 * h);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) { x[2 * u] = a[u]; x[2 * u + 1] = b[u]; }
-                        *reinterpret_cast<uint4 *>(row + (h ? ki[i].o1 : ki[i].o0)) = pack8(x);
+                        for (int u = 0; u < 4; ++u) { x[h][2 * u] = a[u]; x[h][2 * u + 1] = bb[u]; }
                     }
-                } else {
-                    *reinterpret_cast<uint4 *>(row + ki[i].o0) = r0[i];
-                    *reinterpret_cast<uint4 *>(row + ki[i].o1) = r1[i];
+                    w0 = pack8(x[0]);
+                    w1 = pack8(x[1]);
                 }
+                if constexpr (ROT && !FULL) {
+                    // slots past rot_dim keep their input bits
+                    const bool rot_slot = kpa[i].mode != 0;
+                    w0 = rot_slot ? w0 : kr0[i];
+                    w1 = rot_slot ? w1 : kr1[i];
+                }
+                *reinterpret_cast<uint4 *>(row + kpa[i].o0) = w0;
+                *reinterpret_cast<uint4 *>(row + kpa[i].o1) = w1;
             }
-            uint16_t *vdst = kdst + L::K_ELEMS;
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (vi[i].ok) *reinterpret_cast<uint4 *>(vdst + vi[i].l) = vr[i];
         };
-
-        // Plan A registers: one tile of this group in flight.
-        uint4 kr0[KI], kr1[KI];
-        float kc[KI][NFK], ks[KI][NFK];
-        uint4 vr[VI];
-        auto fetch = [&](int64_t kt) { fetch_items(kt, kpa, vpa, kr0, kr1, kc, ks, vr); };
-        auto stage = [&](int buf) { stage_items(buf, kpa, vpa, kr0, kr1, kc, ks, vr); };
-
-        // Plan B (tiles only the heavy half's rows see): the light half's two
-        // waves of this group fetch, rotate and stage whole tiles alone, one
-        // tile ahead, so the heavy half's waves spend those iterations on
-        // matrix-core work.  Items are split over the light pair's 128 threads.
-        const int ltid = (wave & 1) * 64 + lane;
-        constexpr int KIB = (Plan::SLOTS + 127) / 128, VIB = (VSLOTS / 2 + 127) / 128;
-        KItem kpb[KIB];
-        VItem vpb[VIB];
-        uint4 b0[KIB], b1[KIB], bv[VIB];
-        float bc[KIB][NFK], bs[KIB][NFK];
-        auto fetch_light = [&](int64_t kt) {
+        auto stage_v = [&](int b) {
+            uint16_t *vdst = vbuf(b);
 #pragma unroll
-            for (int i = 0; i < KIB; ++i) kpb[i] = k_item(ltid + 128 * i);
-#pragma unroll
-            for (int i = 0; i < VIB; ++i) vpb[i] = v_item(ltid + 128 * i);
-            fetch_items(kt, kpb, vpb, b0, b1, bc, bs, bv);
+            for (int i = 0; i < VI; ++i)
+                if (vpa[i].ok) *reinterpret_cast<uint4 *>(vdst + vpa[i].l) = vr[i];
         };
-        auto stage_light = [&](int buf) { stage_items(buf, kpb, vpb, b0, b1, bc, bs, bv); };
-        // the other half of the V chunks: the heavy pair, one tile ahead
-        KItem knone[1];
-        knone[0].mode = -1; knone[0].row = 0; knone[0].o0 = 0; knone[0].o1 = 0; knone[0].to = 0;
-        VItem vph[VIB];
-        uint4 hv[VIB], hk0[1], hk1[1];
-        float hkc[1][NFK], hks[1][NFK];
-        auto fetch_heavy = [&](int64_t kt) {
-#pragma unroll
-            for (int i = 0; i < VIB; ++i) vph[i] = v_item(VSLOTS / 2 + ltid + 128 * i);
-            fetch_items(kt, knone, vph, hk0, hk1, hkc, hks, hv);
-        };
-        auto stage_heavy = [&](int buf) { stage_items(buf, knone, vph, hk0, hk1, hkc, hks, hv); };
 
         // ---- running state ----
         f32x16_t oacc[DB];
@@ -560,36 +562,60 @@ void flash_fwd_bf16_kernel(Params p)
         for (int b = 0; b < DB; ++b) oacc[b] = (f32x16_t){};
         // Reference max of this lane's query row (base 2, scaled scores),
         // equal in lanes l and l^32; m_set is false until the row has seen a
-        // visible key.
+        // visible key; all_set: every row of the wave has.
         float m_ref = 0.f;
-        bool m_set = false;
+        bool m_set = false, all_set = false;
         float l_acc[4] = {0.f, 0.f, 0.f, 0.f};   // partial row sums (this lane's keys)
         // accumulator seed: -m_ref in every element, refreshed when m_ref moves
         f32x16_t cinit = (f32x16_t){};
 
-        // One key tile of this group: S', softmax update, O += V^T P^T.
-        auto compute = [&](int64_t kt64, int buf) {
-            const int kt = (int)kt64;
-            const int j0 = kt * BN;
-            if (kt >= kt_end) return;   // no row of this wave sees the tile
-            const uint16_t *kb_lds = lds + (group * 2 + buf) * L::BUF_ELEMS;
-            const uint16_t *v_lds = kb_lds + L::K_ELEMS;
-            // S' = K Q'^T - m_ref: NKB 32-key blocks x 32 queries.
-            f32x16_t sacc[NKB];
+        // S' = K Q'^T - m_ref of the tile in K buffer b: NKB 32-key blocks x
+        // 32 queries.  Accumulator element r of block kb2 <-> key
+        // 32kb2 + 8(r/4) + 4hh + r%4 of the tile.
+        auto qk = [&](int b, f32x16_t (&s)[NKB]) {
+            const uint16_t *kl = kbuf(b);
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2) {
-                sacc[kb2] = cinit;
+                s[kb2] = cinit;
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
                     const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                        kb_lds + (kb2 * 32 + l32) * KP + 16 * t + 8 * hh);
-                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb2], 0, 0, 0);
+                        kl + (kb2 * 32 + l32) * KP + 16 * t + 8 * hh);
+                    s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb2], 0, 0, 0);
                 }
             }
-            // accumulator element r of block kb2 <-> key j0 + 32kb2 + 8(r/4) + 4hh + r%4
+        };
+        // P = exp2(S'), rounded to bf16 in the B-operand layout of
+        // O^T += V^T P^T, and this lane's partial row sums of those bf16
+        // values.  For key sub-step mm of block kb2, slot s holds accumulator
+        // element 8mm + s.
+        auto probs = [&](const f32x16_t (&s)[NKB], bf16x8_t (&pb)[NKB][2], float (&lt)[4]) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lt[u] = 0.f;
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    uint32_t wv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        wv[u] = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb2][8 * mm + 2 * u]),
+                                            __builtin_amdgcn_exp2f(s[kb2][8 * mm + 2 * u + 1]));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        lt[u] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(rope::bf16x2_t, wv[u]), ones, lt[u], false);
+                    pb[kb2][mm] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+                }
+        };
+        // The exact path for tile kt: element mask (diagonal or ragged
+        // tile), row max, lazy rescale of the reference (shifting the scores
+        // of this tile and of the next one, already computed), probabilities.
+        auto exact = [&](int kt, f32x16_t (&s)[NKB], f32x16_t (&sn)[NKB], bf16x8_t (&pb)[NKB][2],
+                         float (&lt)[4]) {
             if (kt >= kt_mask) {
-                // key j0 + kk is visible iff kk <= lim (kk: index inside the tile)
-                const int lim0 = lim_base - j0;
+                // key kt*BN + kk is visible iff kk <= lim (kk: index inside the tile)
+                const int lim0 = lim_base - kt * BN;
                 const int lim = lim0 < -1 ? -1 : (lim0 > BN ? BN : lim0);
                 const int lim_h = lim - 4 * hh;
 #pragma unroll
@@ -597,15 +623,15 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kk = 32 * kb2 + 8 * (r / 4) + (r % 4);
-                        if (kk > lim_h) sacc[kb2][r] = -INFINITY;
+                        if (kk > lim_h) s[kb2][r] = -INFINITY;
                     }
             }
             // row max of S' (tree), combined with the other half of the column
             float mx[4 * NKB];
 #pragma unroll
             for (int u = 0; u < 4 * NKB; ++u)
-                mx[u] = fmaxf(fmaxf(sacc[u >> 2][4 * (u & 3)], sacc[u >> 2][4 * (u & 3) + 1]),
-                              fmaxf(sacc[u >> 2][4 * (u & 3) + 2], sacc[u >> 2][4 * (u & 3) + 3]));
+                mx[u] = fmaxf(fmaxf(s[u >> 2][4 * (u & 3)], s[u >> 2][4 * (u & 3) + 1]),
+                              fmaxf(s[u >> 2][4 * (u & 3) + 2], s[u >> 2][4 * (u & 3) + 3]));
 #pragma unroll
             for (int wd = 2 * NKB; wd >= 1; wd >>= 1)
 #pragma unroll
@@ -620,7 +646,10 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                 for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[kb2][r] -= delta;
+                    for (int r = 0; r < 16; ++r) {
+                        s[kb2][r] -= delta;
+                        sn[kb2][r] -= delta;
+                    }
 #pragma unroll
                 for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -632,111 +661,113 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) cinit[r] = -m_ref;
             }
-            // P = exp2(S'), rounded to bf16 in the B-operand layout of
-            // O^T += V^T P^T.  For key sub-step mm of block kb2, slot s holds
-            // accumulator element 8mm + s, i.e. key 32kb2 + 16mm + 8(s/4) +
-            // 4hh + s%4.
-            bf16x8_t pb[NKB][2];
-#pragma unroll
-            for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    uint32_t wv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        wv[u] = pack_bf16x2(__builtin_amdgcn_exp2f(sacc[kb2][8 * mm + 2 * u]),
-                                            __builtin_amdgcn_exp2f(sacc[kb2][8 * mm + 2 * u + 1]));
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        l_acc[u] = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(rope::bf16x2_t, wv[u]), ones, l_acc[u], false);
-                    pb[kb2][mm] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-                }
+            all_set = __builtin_amdgcn_ballot_w64(!m_set) == 0;
+            probs(s, pb, lt);
+        };
+        // O^T += V^T P^T with V from V buffer b.
+        auto pv = [&](const bf16x8_t (&pb)[NKB][2], int b) {
+            const uint16_t *v_lds = vbuf(b);
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
                 for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-                    for (int b = 0; b < DB; ++b) {
+                    for (int bd = 0; bd < DB; ++bd) {
                         const int key0 = 32 * kb2 + 16 * mm + tr_key;
-                        const uint16_t *src = v_lds + key0 * VP + 32 * b + tr_col;
+                        const uint16_t *src = v_lds + key0 * VP + 32 * bd + tr_col;
                         const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
                         const s16x4_t x1 =
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * VP));
                         const bf16x8_t a = __builtin_bit_cast(
                             bf16x8_t, (short __attribute__((ext_vector_type(8)))){
                                           x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-                        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb2][mm], oacc[b], 0, 0, 0);
+                        oacc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb2][mm], oacc[bd], 0, 0, 0);
                     }
         };
 
-        // Group g takes tiles kb + g, kb + g + NG, ...  Group 0 computes then
-        // stages its next tile; group 1 runs one tile ahead, staging first
-        // and computing second, so within an iteration the two waves sharing
-        // a SIMD are in different phases (matrix-core work against
-        // rotation/softmax VALU work).
-        const int64_t n_iter = (ke - kb + NG - 1) / NG;
-        // Tiles from x_light on are seen by the heavy half's rows only (the
-        // light half's last visible tile is below x_light - NG, so its waves
-        // have stopped computing by the time they stage them).
-        const bool light = half == 0;
-        int64_t x_light = ke + NG;   // no light-only staging
-        // (the two-group shape only: with one key group at D = 128 the light
-        // waves' extra registers would spill)
-        constexpr bool OFFLOAD = NG == 2 && !BAL;
-        if (OFFLOAD && rowB < p.Sq) {
-            const int64_t lastA = rowA + 63 < p.Sq ? rowA + 63 : p.Sq - 1;
-            x_light = row_visits(p, lastA) + NG;
+        // Group g takes tiles kb + g, kb + g + NG, ...: iteration j of the
+        // group handles tile T(j) = kb + j NG + g, whose K sits in K buffer
+        // j & 1 and whose V sits in V buffer j & 1.  Iteration j: fetch
+        // K(j+2) and V(j+1) from HBM; compute the scores of tile j+1 (its K
+        // was staged one iteration earlier) while forming tile j's
+        // probabilities from the scores computed one iteration earlier; add
+        // tile j's P V while rotating and staging K(j+2) and V(j+1) into the
+        // buffers iteration j-1 finished reading.  One barrier per
+        // iteration; every wave of the workgroup runs the same number of
+        // iterations, the first j_end of them computing (a wave's tiles end
+        // at kt_end), the rest only staging.
+        const int n_iter = (int)((ke - kb + NG - 1) / NG);
+        const int t0 = (int)kb + group;
+        const int tend = (int)ke;
+        auto T = [&](int j) { return t0 + j * NG; };
+        const int c_end = kt_end < tend ? kt_end : tend;   // computed tiles: [t0, c_end)
+        int j_end = c_end > t0 ? (c_end - t0 + NG - 1) / NG : 0;
+        if (j_end > n_iter) j_end = n_iter;
+        if (T(0) < tend) {
+            fetch_k(T(0));
+            fetch_v(T(0));
+            stage_k(0);
+            stage_v(0);
         }
-        if (kb + group < ke) {
-            fetch(kb + group);
-            stage(0);
+        if (T(1) < tend) {
+            fetch_k(T(1));
+            stage_k(1);
         }
-        if (group == 1 && kb + group + NG < ke && kb + group + NG < x_light) fetch(kb + group + NG);
+        __syncthreads();
+        f32x16_t S0[NKB], S1[NKB];
+        if (j_end > 0) qk(0, S0);
 
-
-        // Phase 1: every wave of the group fetches and stages its share of
-        // the next tile (plan A).  Phase 2 (the group's next tile is at or
-        // past x_light): the light waves stage whole tiles alone (plan B) and
-        // the heavy waves only compute.  Both phases run one barrier per
-        // iteration, so every wave reaches the same barrier count whatever
-        // its split point.
-        int64_t it = 0;
-        for (; it < n_iter; ++it) {
-            const int64_t kt = kb + it * NG + group;
-            const int64_t nxt = kt + NG;              // the tile this group stages now
-            if (nxt < ke && nxt >= x_light) break;
-            const int buf = (int)(it & 1);
-            __syncthreads();   // this iteration's tiles staged; the previous ones consumed
-            if (group == 0) {
-                const bool more = nxt < ke;
-                if (more) fetch(nxt);
-                if (kt < ke) compute(kt, buf);
-                if (more) stage(buf ^ 1);
-            } else {
-                if (nxt < ke) stage(buf ^ 1);
-                if (nxt + NG < ke && nxt + NG < x_light) fetch(nxt + NG);
-                if (kt < ke) compute(kt, buf);
+        auto fetch_next = [&](int j) {
+            if (T(j + 2) < tend) fetch_k(T(j + 2));
+            if (T(j + 1) < tend) fetch_v(T(j + 1));
+        };
+        auto step = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
+            __syncthreads();   // K(j+1), V(j) staged; buffers of iteration j-1 free
+            const int kt = T(j);
+            fetch_next(j);
+            // scores of tile j+1 (unused past the last tile) on the matrix
+            // cores, interleaved with tile j's probabilities on the vector ALU
+            qk((j + 1) & 1, sn);
+            bf16x8_t pb[NKB][2];
+            float lt[4];
+            probs(sc, pb, lt);
+            const float lmax = fmaxf(fmaxf(lt[0], lt[1]), fmaxf(lt[2], lt[3]));
+#pragma unroll
+            for (int i = 0; i < NKB * DT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 64 / (NKB * DT) + 1, 0);   // vector ALU
             }
+            // the fast path's values exist before the branch on them
+            asm volatile("" ::"v"(lmax));
+            const bool big = !(lmax <= FAST_SUM_LIMIT);
+            if (!all_set || kt >= kt_mask || __builtin_amdgcn_ballot_w64(big) != 0)
+                exact(kt, sc, sn, pb, lt);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) l_acc[u] += lt[u];
+            // tile j's P V on the matrix cores, interleaved with staging
+            pv(pb, j & 1);
+            stage_k(j & 1);
+            stage_v((j + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < 2 * NKB * DB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 64 / (2 * NKB * DB), 0);   // vector ALU
+            }
+        };
+        int j = 0;
+        for (; j + 1 < j_end; j += 2) {
+            step(j, S0, S1);
+            step(j + 1, S1, S0);
         }
-        if constexpr (OFFLOAD) {
-            if (it < n_iter && kb + it * NG + group + NG < ke) {
-                if (light) fetch_light(kb + it * NG + group + NG);
-                else fetch_heavy(kb + it * NG + group + NG);
-            }
-            for (; it < n_iter; ++it) {
-                const int64_t kt = kb + it * NG + group;
-                const int buf = (int)(it & 1);
-                __syncthreads();
-                if (light) {   // these rows see none of the remaining tiles
-                    if (kt + NG < ke) stage_light(buf ^ 1);
-                    if (kt + 2 * NG < ke) fetch_light(kt + 2 * NG);
-                } else {
-                    if (kt + NG < ke) stage_heavy(buf ^ 1);
-                    if (kt + 2 * NG < ke) fetch_heavy(kt + 2 * NG);
-                    if (kt < ke) compute(kt, buf);
-                }
-            }
+        if (j < j_end) {
+            step(j, S0, S1);
+            ++j;
+        }
+        for (; j < n_iter; ++j) {
+            __syncthreads();
+            fetch_next(j);
+            stage_k(j & 1);
+            stage_v((j + 1) & 1);
         }
 
         // ---- per-segment epilogue ----
@@ -979,7 +1010,7 @@ int64_t workspace_bytes(const Params &p)
     return (int64_t)p.sk_G * 2 * 4 * NC * 64 * 4;   // two partial states per share
 }
 
-template <int D, int LAYOUT, bool ROT>
+template <int D, int LAYOUT, bool ROT, bool FULL>
 int launch(const FlashArgs &a, hipStream_t stream)
 {
     constexpr int NG = Shape<D>::NG, BN = Shape<D>::BN;
@@ -989,6 +1020,7 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.v = static_cast<const uint16_t *>(a.v);
     p.o = static_cast<uint16_t *>(a.o);
     p.cos_tab = a.cos_tab; p.sin_tab = a.sin_tab; p.rot_dim = a.rot_dim;
+    p.table_rows = a.table_rows;
     p.sl2 = a.scale * 1.4426950408889634f;
     plan<D>(a, p);
     const int64_t need = workspace_bytes<D>(p);
@@ -999,10 +1031,10 @@ int launch(const FlashArgs &a, hipStream_t stream)
     const int64_t blocks = p.sk_G > 0 ? p.sk_G
                            : (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
     if (p.sk_G > 0)
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, NG, BN, true>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true>), dim3((unsigned)blocks),
                            dim3(256 * NG), 0, stream, p);
     else
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, NG, BN, false>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, false>), dim3((unsigned)blocks),
                            dim3(256 * NG), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     if (p.sk_G > 0) {
@@ -1013,17 +1045,21 @@ int launch(const FlashArgs &a, hipStream_t stream)
     return ROPE_LAUNCH_OK;
 }
 
+template <int D>
+int launch_d(const FlashArgs &a, hipStream_t stream)
+{
+    if (a.rot_dim == 0) return launch<D, 1, false, false>(a, stream);
+    const bool full = a.rot_dim == D;
+    if (a.layout == 0)
+        return full ? launch<D, 0, true, true>(a, stream) : launch<D, 0, true, false>(a, stream);
+    return full ? launch<D, 1, true, true>(a, stream) : launch<D, 1, true, false>(a, stream);
+}
+
 }  // namespace
 
 int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream)
 {
-    const bool rot = a.rot_dim > 0;
-    if (a.head_dim == 64) {
-        if (!rot) return launch<64, 1, false>(a, stream);
-        return a.layout == 0 ? launch<64, 0, true>(a, stream) : launch<64, 1, true>(a, stream);
-    }
-    if (!rot) return launch<128, 1, false>(a, stream);
-    return a.layout == 0 ? launch<128, 0, true>(a, stream) : launch<128, 1, true>(a, stream);
+    return a.head_dim == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
 }
 
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a)
