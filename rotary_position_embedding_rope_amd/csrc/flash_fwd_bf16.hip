@@ -56,6 +56,7 @@
 //     O^T = V^T P^T; the V^T operand comes from ds_read_b64_tr_b16
 //     transposing reads of the row-major V tile.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -186,7 +187,6 @@ __device__ __forceinline__ uint4 pack8(const float (&x)[8])
     return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                       pack_bf16x2(x[6], x[7]));
 }
-__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
 // Rotate pairs (a[i], b[i]) by (c[i], s[i]): a' = a c - b s, b' = a s + b c.
 template <int N>
@@ -197,6 +197,23 @@ __device__ __forceinline__ void rotate_pairs(float *a, float *b, const float *c,
         const float x = a[i], y = b[i];
         a[i] = x * c[i] - y * s[i];
         b[i] = x * s[i] + y * c[i];
+    }
+}
+
+// Instruction order of one iteration's block for the scheduler: matrix op
+// I, then the LDS reads of the matrix op two further on (two for a P V op,
+// one for a score op), then NVA vector-ALU instructions.
+template <int I, int NPV, int NMF, int NVA>
+__device__ __forceinline__ void sched_mix()
+{
+    if constexpr (I < NMF) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+        if constexpr (I + 2 < NPV)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS reads
+        else if constexpr (I + 2 < NMF)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NVA, 0);       // vector ALU
+        sched_mix<I + 1, NPV, NMF, NVA>();
     }
 }
 
@@ -286,6 +303,10 @@ void flash_fwd_bf16_kernel(Params p)
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
     constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
+    // the light half's waves stage the heavy half's exclusive tiles alone
+    // (two key groups only: with one group at D = 128 there are no spare
+    // registers for the deeper loads)
+    constexpr bool OFFLOAD = NG == 2 && !BAL;
 
     // [group][buffer] K tiles, then [group][buffer] V tiles.  K runs one tile
     // ahead of V: while tile t's probabilities are formed, the scores of
@@ -309,12 +330,8 @@ void flash_fwd_bf16_kernel(Params p)
     // rotate (lo, hi), 2 GPT-J rotate; o0/o1 = element offsets of its two
     // chunks inside a K tile, to = offset of its cos/sin slice inside the
     // tile's block of table rows.  A V item is one 16-byte chunk.
-    KItem kpa[KI];
-    VItem vpa[VI];
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-        const int item = gtid + 256 * i;
-        KItem &it = kpa[i];
+    auto k_item = [&](int item) {
+        KItem it;
         const int row = item / Plan::SLOTS_PER_ROW;
         const int slot = item % Plan::SLOTS_PER_ROW;
         int d0 = 0, d1 = 0;
@@ -340,15 +357,23 @@ void flash_fwd_bf16_kernel(Params p)
         it.o0 = row * D + d0;
         it.o1 = row * D + d1;
         it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-        const int item = gtid + 256 * i;
+        return it;
+    };
+    auto v_item = [&](int item) {
+        VItem it;
         const int row = item / (D / 8);
-        vpa[i].ok = item < VSLOTS;
-        vpa[i].o = row * D + 8 * (item % (D / 8));     // element offset inside the tile
-        vpa[i].l = row * VP + 8 * (item % (D / 8));    // LDS offset
-    }
+        it.ok = item < VSLOTS;
+        it.o = row * D + 8 * (item % (D / 8));     // element offset inside the tile
+        it.l = row * VP + 8 * (item % (D / 8));    // LDS offset
+        return it;
+    };
+    // Plan A: the 256 threads of a group share the staging of a tile.
+    KItem kpa[KI];
+    VItem vpa[VI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) kpa[i] = k_item(gtid + 256 * i);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) vpa[i] = v_item(gtid + 256 * i);
 
     // V^T operand addressing for ds_read_b64_tr_b16: in each 16-lane group
     // the source lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving
@@ -374,58 +399,185 @@ void flash_fwd_bf16_kernel(Params p)
         const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
         const uint16_t *kh = p.k + (int64_t)bh * p.Sk * D;
         const uint16_t *vh = p.v + (int64_t)bh * p.Sk * D;
+        const int sk32 = (int)p.Sk;
+        // cos/sin rows of this segment's keys start at position k_off; table
+        // rows from there on, capped at the int range
+        const float *ctab = ROT ? p.cos_tab + p.k_off * rh : nullptr;
+        const float *stab = ROT ? p.sin_tab + p.k_off * rh : nullptr;
+        const int64_t trk = p.table_rows - p.k_off;
+        const int tab_rows_k = (int)(trk < 0x7fffffffLL ? trk : 0x7fffffffLL);
 
-        // ---- Q: load, rotate, scale, keep as MFMA B operand ----
-        const int64_t qrow = wq0 + l32;
-        const bool qvalid = qrow < p.Sq;
-        bf16x8_t qf[DT];
-        {
-            float qv[DT][8];
+        // Group g takes tiles kb + g, kb + g + NG, ...: iteration j of the
+        // group handles tile T(j) = kb + j NG + g, whose K sits in K buffer
+        // j & 1 and whose V sits in V buffer j & 1.
+        const int n_iter = (int)((ke - kb + NG - 1) / NG);
+        const int t0 = (int)kb + group;
+        const int tend = (int)ke;
+        auto T = [&](int j) { return t0 + j * NG; };
+
+        // ---- K/V loads and staging ----
+        // Global loads of key tile kt's K items (with their table rows) and
+        // of value tile kt's V items into the given registers.  Rows past Sk
+        // (and table rows past the table) read as zeros.
+        auto fetch_k = [&](int kt, const auto &ki, auto &r0, auto &r1, auto &c, auto &s) {
+            constexpr int N = sizeof(ki) / sizeof(ki[0]);
+            const int j0 = kt * BN;
+            const rsrc_t krs = make_rsrc<2 * D>(kh + (int64_t)j0 * D, sk32 - j0);
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                uint4 wv = make_uint4(0, 0, 0, 0);
-                if (qvalid) wv = *reinterpret_cast<const uint4 *>(qh + qrow * D + 16 * t + 8 * hh);
-                unpack8(wv, qv[t]);
+            for (int i = 0; i < N; ++i) {
+                if (ki[i].mode < 0) continue;
+                r0[i] = bload16(krs, 2 * ki[i].o0);
+                r1[i] = bload16(krs, 2 * ki[i].o1);
             }
             if constexpr (ROT) {
-                if (qvalid) {
-                    const int64_t pos = p.q_off + qrow;
-                    const float *crow = p.cos_tab + pos * rh;
-                    const float *srow = p.sin_tab + pos * rh;
-                    if constexpr (LAYOUT == 0) {
-                        // lane holds dims 16t + 8hh + s; the partner of
-                        // 16t+8hh+s is 16(t + rot/32) + 8hh + s, in the same
-                        // lane (rot_dim is a multiple of 32: tr <= DT/2).
-                        const int tr = p.rot_dim / 32;
+                // table rows are rot_dim/2 floats; descriptors count 16-byte
+                // units (rh is a multiple of 16)
+                const int left = tab_rows_k - j0;   // a tile reads at most BN of them
+                const int trows = (left < BN ? left : BN) * (rh / 4);
+                const rsrc_t crs = make_rsrc<16>(ctab + (int64_t)j0 * rh, trows);
+                const rsrc_t srs = make_rsrc<16>(stab + (int64_t)j0 * rh, trows);
 #pragma unroll
-                        for (int t = 0; t < DT / 2; ++t) {
-                            if (t < tr) {
-                                const int f0 = 16 * t + 8 * hh;
-                                float c[8], s[8];
-                                *reinterpret_cast<float4 *>(c) = ld4(crow + f0);
-                                *reinterpret_cast<float4 *>(c + 4) = ld4(crow + f0 + 4);
-                                *reinterpret_cast<float4 *>(s) = ld4(srow + f0);
-                                *reinterpret_cast<float4 *>(s + 4) = ld4(srow + f0 + 4);
-                                // registers are only indexed with compile-time constants
+                for (int i = 0; i < N; ++i) {
+                    if (ki[i].mode < 0) continue;
+                    const int to = 4 * ki[i].to;
+                    *reinterpret_cast<float4 *>(c[i]) = bload16f(crs, to);
+                    *reinterpret_cast<float4 *>(s[i]) = bload16f(srs, to);
+                    *reinterpret_cast<float4 *>(c[i] + 4) = bload16f(crs, to + 16);
+                    *reinterpret_cast<float4 *>(s[i] + 4) = bload16f(srs, to + 16);
+                }
+            }
+        };
+        auto fetch_v = [&](int kt, const auto &vi, auto &vr) {
+            constexpr int N = sizeof(vi) / sizeof(vi[0]);
+            const int j0 = kt * BN;
+            const rsrc_t vrs = make_rsrc<2 * D>(vh + (int64_t)j0 * D, sk32 - j0);
 #pragma unroll
-                                for (int u = 1; u <= DT / 2; ++u)
-                                    if (u == tr) rotate_pairs<8>(qv[t], qv[t + u], c, s);
-                            }
+            for (int i = 0; i < N; ++i)
+                if (vi[i].ok) vr[i] = bload16(vrs, 2 * vi[i].o);
+        };
+        // Rotate fetched K items in fp32 at their key positions, round to
+        // bf16 and write them to K buffer b; write fetched V items to V
+        // buffer b.
+        auto stage_k = [&](int b, const auto &ki, const auto &r0, const auto &r1, const auto &c,
+                           const auto &s) {
+            constexpr int N = sizeof(ki) / sizeof(ki[0]);
+            uint16_t *kdst = kbuf(b);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                if (ki[i].mode < 0) continue;
+                // LDS rows have pitch KP; the chunk offsets inside a row are
+                // o - row * D.
+                uint16_t *row = kdst + ki[i].row * (KP - D);
+                uint4 w0 = r0[i], w1 = r1[i];
+                if constexpr (ROT && LAYOUT == 0) {
+                    float lo[8], hi[8], cc[8], ss[8];
+                    unpack8(r0[i], lo);
+                    unpack8(r1[i], hi);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) { cc[u] = c[i][u]; ss[u] = s[i][u]; }
+                    rotate_pairs<8>(lo, hi, cc, ss);
+                    w0 = pack8(lo);
+                    w1 = pack8(hi);
+                } else if constexpr (ROT && LAYOUT == 1) {
+                    // chunk h holds pairs 4h .. 4h+3 of the slot's 8
+                    float x[2][8];
+                    unpack8(r0[i], x[0]);
+                    unpack8(r1[i], x[1]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        float a[4], bb[4], cc[4], ss[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            a[u] = x[h][2 * u]; bb[u] = x[h][2 * u + 1];
+                            cc[u] = c[i][4 * h + u]; ss[u] = s[i][4 * h + u];
                         }
-                    } else {
+                        rotate_pairs<4>(a, bb, cc, ss);
 #pragma unroll
-                        for (int t = 0; t < DT; ++t) {
-                            if (16 * t < p.rot_dim) {
-                                const int f0 = 8 * t + 4 * hh;
-                                float c[4], s[4], a[4], b[4];
-                                *reinterpret_cast<float4 *>(c) = ld4(crow + f0);
-                                *reinterpret_cast<float4 *>(s) = ld4(srow + f0);
+                        for (int u = 0; u < 4; ++u) { x[h][2 * u] = a[u]; x[h][2 * u + 1] = bb[u]; }
+                    }
+                    w0 = pack8(x[0]);
+                    w1 = pack8(x[1]);
+                }
+                if constexpr (ROT && !FULL) {
+                    // slots past rot_dim keep their input bits
+                    const bool rot_slot = ki[i].mode != 0;
+                    w0 = rot_slot ? w0 : r0[i];
+                    w1 = rot_slot ? w1 : r1[i];
+                }
+                *reinterpret_cast<uint4 *>(row + ki[i].o0) = w0;
+                *reinterpret_cast<uint4 *>(row + ki[i].o1) = w1;
+            }
+        };
+        auto stage_v = [&](int b, const auto &vi, const auto &vr) {
+            constexpr int N = sizeof(vi) / sizeof(vi[0]);
+            uint16_t *vdst = vbuf(b);
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) { a[u] = qv[t][2 * u]; b[u] = qv[t][2 * u + 1]; }
-                                rotate_pairs<4>(a, b, c, s);
+            for (int i = 0; i < N; ++i)
+                if (vi[i].ok) *reinterpret_cast<uint4 *>(vdst + vi[i].l) = vr[i];
+        };
+
+        // Plan A registers: one K tile and one V tile of this group in flight.
+        uint4 kr0[KI], kr1[KI];
+        float kc[KI][8], ks[KI][8];
+        uint4 vr[VI];
+        // The first two key tiles, the query rows and their table rows are
+        // all requested before any of them is used, so their latencies
+        // overlap (rows past Sq, or past the table, read as zeros).
+        bf16x8_t qf[DT];
+        {
+            uint4 pr0[KI], pr1[KI];
+            float pc[KI][8], ps[KI][8];
+            if (T(0) < tend) {
+                fetch_k(T(0), kpa, kr0, kr1, kc, ks);
+                fetch_v(T(0), vpa, vr);
+            }
+            if (T(1) < tend) fetch_k(T(1), kpa, pr0, pr1, pc, ps);
+
+            // ---- Q: load, rotate, scale, keep as MFMA B operand ----
+            const int64_t qleft = p.Sq - wq0;
+            const rsrc_t qrs = make_rsrc<2 * D>(qh + wq0 * D, (int)(qleft < 0 ? 0 : (qleft > 32 ? 32 : qleft)));
+            float qv[DT][8];
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) { qv[t][2 * u] = a[u]; qv[t][2 * u + 1] = b[u]; }
-                            }
+            for (int t = 0; t < DT; ++t) unpack8(bload16(qrs, 2 * (l32 * D + 16 * t + 8 * hh)), qv[t]);
+            if constexpr (ROT) {
+                const int64_t tleft = p.table_rows - (p.q_off + wq0);
+                const int trows = (int)(tleft < 0 ? 0 : (tleft > 32 ? 32 : tleft)) * (rh / 4);
+                const rsrc_t qcs = make_rsrc<16>(p.cos_tab + (p.q_off + wq0) * rh, trows);
+                const rsrc_t qss = make_rsrc<16>(p.sin_tab + (p.q_off + wq0) * rh, trows);
+                const int tb = 4 * l32 * rh;   // byte offset of this lane's table row
+                if constexpr (LAYOUT == 0) {
+                    // lane holds dims 16t + 8hh + s; the partner of
+                    // 16t+8hh+s is 16(t + rot/32) + 8hh + s, in the same
+                    // lane (rot_dim is a multiple of 32: tr <= DT/2).
+                    const int tr = p.rot_dim / 32;
+#pragma unroll
+                    for (int t = 0; t < DT / 2; ++t) {
+                        if (t < tr) {
+                            const int f0 = 4 * (16 * t + 8 * hh);
+                            float c[8], s[8];
+                            *reinterpret_cast<float4 *>(c) = bload16f(qcs, tb + f0);
+                            *reinterpret_cast<float4 *>(c + 4) = bload16f(qcs, tb + f0 + 16);
+                            *reinterpret_cast<float4 *>(s) = bload16f(qss, tb + f0);
+                            *reinterpret_cast<float4 *>(s + 4) = bload16f(qss, tb + f0 + 16);
+                            // registers are only indexed with compile-time constants
+#pragma unroll
+                            for (int u = 1; u <= DT / 2; ++u)
+                                if (u == tr) rotate_pairs<8>(qv[t], qv[t + u], c, s);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < DT; ++t) {
+                        if (16 * t < p.rot_dim) {
+                            const int f0 = 4 * (8 * t + 4 * hh);
+                            float c[4], s[4], a[4], b[4];
+                            *reinterpret_cast<float4 *>(c) = bload16f(qcs, tb + f0);
+                            *reinterpret_cast<float4 *>(s) = bload16f(qss, tb + f0);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) { a[u] = qv[t][2 * u]; b[u] = qv[t][2 * u + 1]; }
+                            rotate_pairs<4>(a, b, c, s);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) { qv[t][2 * u] = a[u]; qv[t][2 * u + 1] = b[u]; }
                         }
                     }
                 }
@@ -435,7 +587,14 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                 for (int s = 0; s < 8; ++s) qf[t][s] = (__bf16)(qv[t][s] * p.sl2);
             }
+            if (T(0) < tend) {
+                stage_k(0, kpa, kr0, kr1, kc, ks);
+                stage_v(0, vpa, vr);
+            }
+            if (T(1) < tend) stage_k(1, kpa, pr0, pr1, pc, ps);
         }
+        const int64_t qrow = wq0 + l32;
+        const bool qvalid = qrow < p.Sq;
 
         const int64_t wq_last = (wq0 + 31 < p.Sq ? wq0 + 31 : p.Sq - 1);
         const bool wave_has_rows = wq0 < p.Sq;
@@ -449,134 +608,35 @@ void flash_fwd_bf16_kernel(Params p)
         if (p.causal) {
             const int64_t delta = p.q_off - p.k_off;   // >= 0
             const int64_t x = delta + wq0 + 1 - BN;
-            const int64_t kc = x < 0 ? 0 : x / BN + 1;
-            if (kc < kt_mask) kt_mask = (int)kc;
+            const int64_t kc0 = x < 0 ? 0 : x / BN + 1;
+            if (kc0 < kt_mask) kt_mask = (int)kc0;
             const int64_t c = delta + qrow;
             if (c < lim_base) lim_base = (int)c;
         }
-        // cos/sin rows of this segment's keys start at position k_off
-        const float *ctab = ROT ? p.cos_tab + p.k_off * rh : nullptr;
-        const float *stab = ROT ? p.sin_tab + p.k_off * rh : nullptr;
-        const int sk32 = (int)p.Sk;
-        // table rows from position k_off on (k_off + Sk <= table_rows < 2^31
-        // is not required: the count is capped at the int range)
-        const int64_t trk = p.table_rows - p.k_off;
-        const int tab_rows_k = (int)(trk < 0x7fffffffLL ? trk : 0x7fffffffLL);
-
-        // ---- K/V pipeline registers (one K tile and one V tile in flight) ----
-        uint4 kr0[KI], kr1[KI];
-        float kc[KI][8], ks[KI][8];
-        uint4 vr[VI];
-        // Global loads of key tile kt's K items (with their table rows) and
-        // of value tile kt's V items.  Rows past Sk (and table rows past the
-        // table) read as zeros.
-        auto fetch_k = [&](int kt) {
-            const int j0 = kt * BN;
-            const rsrc_t krs = make_rsrc<2 * D>(kh + (int64_t)j0 * D, sk32 - j0);
-#pragma unroll
-            for (int i = 0; i < KI; ++i) {
-                if (kpa[i].mode < 0) continue;
-                kr0[i] = bload16(krs, 2 * kpa[i].o0);
-                kr1[i] = bload16(krs, 2 * kpa[i].o1);
-            }
-            if constexpr (ROT) {
-                // table rows are rot_dim/2 floats: descriptors count
-                // 16-byte units (rh is a multiple of 16)
-                const int left = tab_rows_k - j0;   // a tile reads at most BN of them
-                const int trows = (left < BN ? left : BN) * (rh / 4);
-                const rsrc_t crs = make_rsrc<16>(ctab + (int64_t)j0 * rh, trows);
-                const rsrc_t srs = make_rsrc<16>(stab + (int64_t)j0 * rh, trows);
-#pragma unroll
-                for (int i = 0; i < KI; ++i) {
-                    if (kpa[i].mode < 0) continue;
-                    const int to = 4 * kpa[i].to;
-                    *reinterpret_cast<float4 *>(kc[i]) = bload16f(crs, to);
-                    *reinterpret_cast<float4 *>(ks[i]) = bload16f(srs, to);
-                    *reinterpret_cast<float4 *>(kc[i] + 4) = bload16f(crs, to + 16);
-                    *reinterpret_cast<float4 *>(ks[i] + 4) = bload16f(srs, to + 16);
-                }
-            }
-        };
-        auto fetch_v = [&](int kt) {
-            const int j0 = kt * BN;
-            const rsrc_t vrs = make_rsrc<2 * D>(vh + (int64_t)j0 * D, sk32 - j0);
-#pragma unroll
-            for (int i = 0; i < VI; ++i)
-                if (vpa[i].ok) vr[i] = bload16(vrs, 2 * vpa[i].o);
-        };
-        // Rotate the fetched K items in fp32 at their key positions, round to
-        // bf16 and write them to K buffer b.
-        auto stage_k = [&](int b) {
-            uint16_t *kdst = kbuf(b);
-#pragma unroll
-            for (int i = 0; i < KI; ++i) {
-                if (kpa[i].mode < 0) continue;
-                // LDS rows have pitch KP; the chunk offsets inside a row are
-                // o - row * D.
-                uint16_t *row = kdst + kpa[i].row * (KP - D);
-                uint4 w0 = kr0[i], w1 = kr1[i];
-                if constexpr (ROT && LAYOUT == 0) {
-                    float lo[8], hi[8];
-                    unpack8(kr0[i], lo);
-                    unpack8(kr1[i], hi);
-                    rotate_pairs<8>(lo, hi, kc[i], ks[i]);
-                    w0 = pack8(lo);
-                    w1 = pack8(hi);
-                } else if constexpr (ROT && LAYOUT == 1) {
-                    // chunk h holds pairs 4h .. 4h+3 of the slot's 8
-                    float x[2][8];
-                    unpack8(kr0[i], x[0]);
-                    unpack8(kr1[i], x[1]);
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        float a[4], bb[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) { a[u] = x[h][2 * u]; bb[u] = x[h][2 * u + 1]; }
-                        rotate_pairs<4>(a, bb, kc[i] + 4 * h, ks[i] + 4 * h);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) { x[h][2 * u] = a[u]; x[h][2 * u + 1] = bb[u]; }
-                    }
-                    w0 = pack8(x[0]);
-                    w1 = pack8(x[1]);
-                }
-                if constexpr (ROT && !FULL) {
-                    // slots past rot_dim keep their input bits
-                    const bool rot_slot = kpa[i].mode != 0;
-                    w0 = rot_slot ? w0 : kr0[i];
-                    w1 = rot_slot ? w1 : kr1[i];
-                }
-                *reinterpret_cast<uint4 *>(row + kpa[i].o0) = w0;
-                *reinterpret_cast<uint4 *>(row + kpa[i].o1) = w1;
-            }
-        };
-        auto stage_v = [&](int b) {
-            uint16_t *vdst = vbuf(b);
-#pragma unroll
-            for (int i = 0; i < VI; ++i)
-                if (vpa[i].ok) *reinterpret_cast<uint4 *>(vdst + vpa[i].l) = vr[i];
-        };
 
         // ---- running state ----
         f32x16_t oacc[DB];
 #pragma unroll
         for (int b = 0; b < DB; ++b) oacc[b] = (f32x16_t){};
-        // Reference max of this lane's query row (base 2, scaled scores),
-        // equal in lanes l and l^32; m_set is false until the row has seen a
-        // visible key; all_set: every row of the wave has.
+        // Reference of this lane's query row (base 2, scaled scores), equal
+        // in lanes l and l^32: probabilities are exp2(S - m_ref).  It stays 0
+        // while the row's scores sit in [-64, 8] (no subtraction needed) and
+        // is raised lazily to the row max when a score exceeds it by more
+        // than the lazy threshold (or a row's first scores all lie below
+        // -64).  m_set: the row has seen a visible key; all_set / ref_zero:
+        // every row of the wave has / has a zero reference.
         float m_ref = 0.f;
-        bool m_set = false, all_set = false;
+        bool m_set = false, all_set = false, ref_zero = true;
         float l_acc[4] = {0.f, 0.f, 0.f, 0.f};   // partial row sums (this lane's keys)
-        // accumulator seed: -m_ref in every element, refreshed when m_ref moves
-        f32x16_t cinit = (f32x16_t){};
 
-        // S' = K Q'^T - m_ref of the tile in K buffer b: NKB 32-key blocks x
-        // 32 queries.  Accumulator element r of block kb2 <-> key
+        // S = K Q'^T of the tile in K buffer b: NKB 32-key blocks x 32
+        // queries.  Accumulator element r of block kb2 <-> key
         // 32kb2 + 8(r/4) + 4hh + r%4 of the tile.
         auto qk = [&](int b, f32x16_t (&s)[NKB]) {
             const uint16_t *kl = kbuf(b);
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2) {
-                s[kb2] = cinit;
+                s[kb2] = (f32x16_t){};
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
                     const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
@@ -585,11 +645,11 @@ void flash_fwd_bf16_kernel(Params p)
                 }
             }
         };
-        // P = exp2(S'), rounded to bf16 in the B-operand layout of
-        // O^T += V^T P^T, and this lane's partial row sums of those bf16
-        // values.  For key sub-step mm of block kb2, slot s holds accumulator
-        // element 8mm + s.
-        auto probs = [&](const f32x16_t (&s)[NKB], bf16x8_t (&pb)[NKB][2], float (&lt)[4]) {
+        // P = exp2(S - m_ref) (SUB) or exp2(S) (every reference zero),
+        // rounded to bf16 in the B-operand layout of O^T += V^T P^T, and this
+        // lane's partial row sums of those bf16 values.  For key sub-step mm
+        // of block kb2, slot s holds accumulator element 8mm + s.
+        auto probs = [&](const f32x16_t (&s)[NKB], bf16x8_t (&pb)[NKB][2], float (&lt)[4], auto SUB) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) lt[u] = 0.f;
 #pragma unroll
@@ -598,9 +658,14 @@ void flash_fwd_bf16_kernel(Params p)
                 for (int mm = 0; mm < 2; ++mm) {
                     uint32_t wv[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        wv[u] = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb2][8 * mm + 2 * u]),
-                                            __builtin_amdgcn_exp2f(s[kb2][8 * mm + 2 * u + 1]));
+                    for (int u = 0; u < 4; ++u) {
+                        float x0 = s[kb2][8 * mm + 2 * u], x1 = s[kb2][8 * mm + 2 * u + 1];
+                        if constexpr (decltype(SUB)::value) {
+                            x0 -= m_ref;
+                            x1 -= m_ref;
+                        }
+                        wv[u] = pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
+                    }
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
                         lt[u] = __builtin_amdgcn_fdot2_f32_bf16(
@@ -608,11 +673,12 @@ void flash_fwd_bf16_kernel(Params p)
                     pb[kb2][mm] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
                 }
         };
+        using sub_on = std::integral_constant<bool, true>;
+        using sub_off = std::integral_constant<bool, false>;
         // The exact path for tile kt: element mask (diagonal or ragged
-        // tile), row max, lazy rescale of the reference (shifting the scores
-        // of this tile and of the next one, already computed), probabilities.
-        auto exact = [&](int kt, f32x16_t (&s)[NKB], f32x16_t (&sn)[NKB], bf16x8_t (&pb)[NKB][2],
-                         float (&lt)[4]) {
+        // tile), row max, lazy raise of the reference (rescaling O and l),
+        // probabilities.
+        auto exact = [&](int kt, f32x16_t (&s)[NKB], bf16x8_t (&pb)[NKB][2], float (&lt)[4]) {
             if (kt >= kt_mask) {
                 // key kt*BN + kk is visible iff kk <= lim (kk: index inside the tile)
                 const int lim0 = lim_base - kt * BN;
@@ -626,7 +692,7 @@ void flash_fwd_bf16_kernel(Params p)
                         if (kk > lim_h) s[kb2][r] = -INFINITY;
                     }
             }
-            // row max of S' (tree), combined with the other half of the column
+            // row max of S (tree), combined with the other half of the column
             float mx[4 * NKB];
 #pragma unroll
             for (int u = 0; u < 4 * NKB; ++u)
@@ -637,32 +703,25 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                 for (int u = 0; u < wd; ++u) mx[u] = fmaxf(mx[u], mx[u + wd]);
             const float rmax = max_with_partner(mx[0]);
-            // raise the reference on a row's first visible key, or when its
-            // scores exceed the reference by more than the lazy threshold
-            const bool need = (!m_set && rmax > -INFINITY) || rmax > LAZY_THRESHOLD;
+            // raise the reference when the row's scores exceed it by more
+            // than the lazy threshold, or when a row's first visible scores
+            // all lie below -64 (they would underflow against 0)
+            const bool need = rmax - m_ref > LAZY_THRESHOLD || (!m_set && rmax > -INFINITY && rmax < -64.f);
             if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float delta = need ? rmax : 0.f;
-                const float alpha = m_set ? __builtin_amdgcn_exp2f(-delta) : 1.f;
-#pragma unroll
-                for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        s[kb2][r] -= delta;
-                        sn[kb2][r] -= delta;
-                    }
+                const float m_new = need ? rmax : m_ref;
+                const float alpha = m_set ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
 #pragma unroll
                 for (int b = 0; b < DB; ++b)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) l_acc[u] *= alpha;
-                m_ref += delta;
-                m_set = m_set || need;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cinit[r] = -m_ref;
+                m_ref = m_new;
+                ref_zero = __builtin_amdgcn_ballot_w64(m_ref != 0.f) == 0;
             }
+            m_set = m_set || rmax > -INFINITY;
             all_set = __builtin_amdgcn_ballot_w64(!m_set) == 0;
-            probs(s, pb, lt);
+            probs(s, pb, lt, sub_on{});
         };
         // O^T += V^T P^T with V from V buffer b.
         auto pv = [&](const bf16x8_t (&pb)[NKB][2], int b) {
@@ -685,96 +744,179 @@ void flash_fwd_bf16_kernel(Params p)
                     }
         };
 
-        // Group g takes tiles kb + g, kb + g + NG, ...: iteration j of the
-        // group handles tile T(j) = kb + j NG + g, whose K sits in K buffer
-        // j & 1 and whose V sits in V buffer j & 1.  Iteration j: fetch
-        // K(j+2) and V(j+1) from HBM; compute the scores of tile j+1 (its K
-        // was staged one iteration earlier) while forming tile j's
-        // probabilities from the scores computed one iteration earlier; add
-        // tile j's P V while rotating and staging K(j+2) and V(j+1) into the
-        // buffers iteration j-1 finished reading.  One barrier per
-        // iteration; every wave of the workgroup runs the same number of
-        // iterations, the first j_end of them computing (a wave's tiles end
-        // at kt_end), the rest only staging.
-        const int n_iter = (int)((ke - kb + NG - 1) / NG);
-        const int t0 = (int)kb + group;
-        const int tend = (int)ke;
-        auto T = [&](int j) { return t0 + j * NG; };
-        const int c_end = kt_end < tend ? kt_end : tend;   // computed tiles: [t0, c_end)
+        // Phase 1 (plan A), iterations [0, j_split), every wave of the group
+        // sharing the staging.  Iteration j (tile T(j)): fetch K(j+2) and
+        // V(j+1) from HBM; compute the scores of tile j+1 (its K was staged
+        // one iteration earlier) on the matrix cores while forming tile j's
+        // probabilities from the scores computed one iteration earlier; then
+        // add tile j's P V while rotating and staging K(j+2) and V(j+1) into
+        // the buffers iteration j-1 finished reading.
+        //
+        // Phase 2 (plan B), [j_split, n_iter): the tiles left are seen only
+        // by the heavy half's rows.  The light half's two waves stage them
+        // alone (K(j+2) and V(j) in iteration j), loading two tiles ahead;
+        // the heavy half's waves only compute, adding tile j-1's P V in the
+        // same matrix-core stream as tile j+1's scores.
+        //
+        // One barrier per iteration; every wave of the workgroup runs the
+        // same number of iterations, plus one at the end.
+        const int c_end = kt_end < tend ? kt_end : tend;   // this wave computes tiles [t0, c_end)
         int j_end = c_end > t0 ? (c_end - t0 + NG - 1) / NG : 0;
         if (j_end > n_iter) j_end = n_iter;
-        if (T(0) < tend) {
-            fetch_k(T(0));
-            fetch_v(T(0));
-            stage_k(0);
-            stage_v(0);
+        int j_split = n_iter;
+        if constexpr (OFFLOAD) {
+            if (rowB < p.Sq) {
+                const int64_t lastA = rowA + 63 < p.Sq ? rowA + 63 : p.Sq - 1;
+                const int light_end = (int)row_visits(p, lastA);   // light rows see tiles < light_end
+                const int js = light_end > t0 ? (light_end - t0 + NG - 1) / NG : 0;
+                if (js < j_split) j_split = js;
+            }
         }
-        if (T(1) < tend) {
-            fetch_k(T(1));
-            stage_k(1);
-        }
+        const bool light = half == 0;
+
         __syncthreads();
+        // scores S[j & 1] of tile j
         f32x16_t S0[NKB], S1[NKB];
         if (j_end > 0) qk(0, S0);
 
         auto fetch_next = [&](int j) {
-            if (T(j + 2) < tend) fetch_k(T(j + 2));
-            if (T(j + 1) < tend) fetch_v(T(j + 1));
+            if (T(j + 2) < tend) fetch_k(T(j + 2), kpa, kr0, kr1, kc, ks);
+            if (T(j + 1) < tend) fetch_v(T(j + 1), vpa, vr);
         };
-        auto step = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
-            __syncthreads();   // K(j+1), V(j) staged; buffers of iteration j-1 free
+        auto stage_next = [&](int j) {
+            stage_k(j & 1, kpa, kr0, kr1, kc, ks);
+            stage_v((j + 1) & 1, vpa, vr);
+        };
+        // tile j's probabilities on the fast path (exact path if needed);
+        // `mfma` issues the matrix-core work they are interleaved with
+        auto softmax = [&](int j, f32x16_t (&sc)[NKB], bf16x8_t (&pb)[NKB][2], auto mfma, auto NMF,
+                           auto NPV) {
             const int kt = T(j);
-            fetch_next(j);
-            // scores of tile j+1 (unused past the last tile) on the matrix
-            // cores, interleaved with tile j's probabilities on the vector ALU
-            qk((j + 1) & 1, sn);
-            bf16x8_t pb[NKB][2];
             float lt[4];
-            probs(sc, pb, lt);
+            constexpr int nmf = decltype(NMF)::value, npv = decltype(NPV)::value;
+            auto block = [&](auto SUB) {
+                mfma();
+                probs(sc, pb, lt, SUB);
+                __builtin_amdgcn_sched_group_barrier(0x100, npv > 0 ? 4 : 2, 0);   // LDS reads
+                sched_mix<0, npv, nmf, 72 / nmf + 1>();
+            };
+            if (ref_zero) block(sub_off{});
+            else block(sub_on{});
             const float lmax = fmaxf(fmaxf(lt[0], lt[1]), fmaxf(lt[2], lt[3]));
-#pragma unroll
-            for (int i = 0; i < NKB * DT; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 64 / (NKB * DT) + 1, 0);   // vector ALU
-            }
             // the fast path's values exist before the branch on them
             asm volatile("" ::"v"(lmax));
             const bool big = !(lmax <= FAST_SUM_LIMIT);
             if (!all_set || kt >= kt_mask || __builtin_amdgcn_ballot_w64(big) != 0)
-                exact(kt, sc, sn, pb, lt);
+                exact(kt, sc, pb, lt);
 #pragma unroll
             for (int u = 0; u < 4; ++u) l_acc[u] += lt[u];
+        };
+        using i_qk = std::integral_constant<int, NKB * DT>;
+        using i_zero = std::integral_constant<int, 0>;
+        // phase-1 iteration
+        auto step_a = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
+            __syncthreads();   // K(j+1), V(j) staged; buffers of iteration j-1 free
+            fetch_next(j);
+            bf16x8_t pb[NKB][2];
+            softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
             // tile j's P V on the matrix cores, interleaved with staging
             pv(pb, j & 1);
-            stage_k(j & 1);
-            stage_v((j + 1) & 1);
+            stage_next(j);
 #pragma unroll
             for (int i = 0; i < 2 * NKB * DB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 64 / (2 * NKB * DB), 0);   // vector ALU
             }
         };
+        // phase-2 iteration of a heavy wave: no staging
+        auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
+            __syncthreads();   // K(j+1), V(j) staged
+            bf16x8_t pb[NKB][2];
+            softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
+            pv(pb, j & 1);
+        };
+
+        // ---- phase 1 ----
         int j = 0;
-        for (; j + 1 < j_end; j += 2) {
-            step(j, S0, S1);
-            step(j + 1, S1, S0);
+        {
+            const int je1 = j_end < j_split ? j_end : j_split;
+            for (; j + 1 < je1; j += 2) {
+                step_a(j, S0, S1);
+                step_a(j + 1, S1, S0);
+            }
+            if (j < je1) {
+                step_a(j, S0, S1);
+                ++j;
+            }
         }
-        if (j < j_end) {
-            step(j, S0, S1);
-            ++j;
-        }
-        for (; j < n_iter; ++j) {
+        for (; j < j_split; ++j) {
             __syncthreads();
             fetch_next(j);
-            stage_k(j & 1);
-            stage_v((j + 1) & 1);
+            stage_next(j);
         }
+        // ---- phase 2 ----
+        if constexpr (OFFLOAD) {
+            if (j_split < n_iter) {
+                if (light) {
+                    // the light pair's 128 threads stage whole tiles: two
+                    // register sets, K(j+2) / V(j+1) staged while K(j+4) /
+                    // V(j+3) load
+                    constexpr int KIB = (Plan::SLOTS + 127) / 128, VIB = (VSLOTS + 127) / 128;
+                    const int ltid = (wave & 1) * 64 + lane;
+                    KItem kpb[KIB];
+                    VItem vpb[VIB];
+#pragma unroll
+                    for (int i = 0; i < KIB; ++i) kpb[i] = k_item(ltid + 128 * i);
+#pragma unroll
+                    for (int i = 0; i < VIB; ++i) vpb[i] = v_item(ltid + 128 * i);
+                    uint4 a0[KIB], a1[KIB], av[VIB], b0[KIB], b1[KIB], bv[VIB];
+                    float ac[KIB][8], as[KIB][8], bc[KIB][8], bs[KIB][8];
+                    auto fetch_b = [&](int jj, auto &r0, auto &r1, auto &c, auto &s, auto &vv) {
+                        if (T(jj + 2) < tend) fetch_k(T(jj + 2), kpb, r0, r1, c, s);
+                        if (T(jj + 1) < tend) fetch_v(T(jj + 1), vpb, vv);
+                    };
+                    auto stage_b = [&](int jj, const auto &r0, const auto &r1, const auto &c, const auto &s,
+                                       const auto &vv) {
+                        stage_k(jj & 1, kpb, r0, r1, c, s);
+                        stage_v((jj + 1) & 1, vpb, vv);
+                    };
+                    fetch_b(j, a0, a1, ac, as, av);
+                    fetch_b(j + 1, b0, b1, bc, bs, bv);
+                    for (; j < n_iter; j += 2) {
+                        __syncthreads();
+                        stage_b(j, a0, a1, ac, as, av);
+                        fetch_b(j + 2, a0, a1, ac, as, av);
+                        if (j + 1 < n_iter) {
+                            __syncthreads();
+                            stage_b(j + 1, b0, b1, bc, bs, bv);
+                            fetch_b(j + 3, b0, b1, bc, bs, bv);
+                        }
+                    }
+                    j = n_iter;
+                } else {
+                    auto run = [&](f32x16_t (&A)[NKB], f32x16_t (&B)[NKB]) {
+                        // iterations [j, j_end); tile j's scores in A
+                        for (; j + 1 < j_end; j += 2) {
+                            step_b(j, A, B);
+                            step_b(j + 1, B, A);
+                        }
+                        if (j < j_end) {
+                            step_b(j, A, B);
+                            ++j;
+                        }
+                    };
+                    if (j & 1) run(S1, S0);
+                    else run(S0, S1);
+                    for (; j < n_iter; ++j) __syncthreads();
+                }
+            }
+        }
+        __syncthreads();   // all tiles consumed
 
         // ---- per-segment epilogue ----
         float l_tot = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
         float m_fin = m_set ? m_ref : -INFINITY;
         float *xfer = reinterpret_cast<float *>(lds);
-        __syncthreads();   // all tiles consumed; LDS reusable
         if constexpr (NG == 2) {
             // group 1 hands its state to group 0 through LDS: per wave, per
             // lane, DB*16 accumulators + m + l, component-major.
