@@ -774,15 +774,18 @@ void flash_fwd_bf16_kernel(Params p)
         }
         const bool light = half == 0;
 
+        // The loads staged in iteration j are issued at the end of
+        // iteration j-1 (here for j = 0), ahead of the barrier.
+        auto fetch_next = [&](int j) {
+            if (T(j + 2) < tend) fetch_k(T(j + 2), kpa, kr0, kr1, kc, ks);
+            if (T(j + 1) < tend) fetch_v(T(j + 1), vpa, vr);
+        };
+        if (j_split > 0) fetch_next(0);
         __syncthreads();
         // scores S[j & 1] of tile j
         f32x16_t S0[NKB], S1[NKB];
         if (j_end > 0) qk(0, S0);
 
-        auto fetch_next = [&](int j) {
-            if (T(j + 2) < tend) fetch_k(T(j + 2), kpa, kr0, kr1, kc, ks);
-            if (T(j + 1) < tend) fetch_v(T(j + 1), vpa, vr);
-        };
         auto stage_next = [&](int j) {
             stage_k(j & 1, kpa, kr0, kr1, kc, ks);
             stage_v((j + 1) & 1, vpa, vr);
@@ -816,7 +819,6 @@ void flash_fwd_bf16_kernel(Params p)
         // phase-1 iteration
         auto step_a = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
             __syncthreads();   // K(j+1), V(j) staged; buffers of iteration j-1 free
-            fetch_next(j);
             bf16x8_t pb[NKB][2];
             softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
             // tile j's P V on the matrix cores, interleaved with staging
@@ -827,6 +829,7 @@ void flash_fwd_bf16_kernel(Params p)
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 64 / (2 * NKB * DB), 0);   // vector ALU
             }
+            if (j + 1 < j_split) fetch_next(j + 1);
         };
         // phase-2 iteration of a heavy wave: no staging
         auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
@@ -851,8 +854,8 @@ void flash_fwd_bf16_kernel(Params p)
         }
         for (; j < j_split; ++j) {
             __syncthreads();
-            fetch_next(j);
             stage_next(j);
+            if (j + 1 < j_split) fetch_next(j + 1);
         }
         // ---- phase 2 ----
         if constexpr (OFFLOAD) {
