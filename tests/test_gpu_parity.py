@@ -356,6 +356,91 @@ def test_fused_edge_cases_full(orc, case):
     assert np.abs(got - want).max() <= (BF16_TOL if dtype == "bf16" else F32_TOL)
 
 
+# Score ranges the random N(0,1) workloads never reach.  The kernel takes
+# probabilities against a per-row reference that stays 0 while a row's
+# scores (log2 units) sit in [-64, 8] and is raised to the row max
+# otherwise; these cases force every branch of that rule.  With large
+# scores, rounding the rotated, scaled rows to bf16 moves a score by about
+# |score| * 2^-9, which alone exceeds the bf16 bar at |score| ~ 100; so these
+# cases use no rotation, integer-valued q and k, and softmax scale ln 2
+# (fp32(ln 2) * fp32(log2 e) == 1 exactly), which make every score an exact
+# integer on both sides.
+LN2 = 0.6931471805599453
+
+
+def exact_score_inputs(w, lim, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-lim, lim + 1, size=(w.B, w.H, w.Sq, w.D)).astype(np.float32)
+    k = rng.integers(-lim, lim + 1, size=(w.B, w.H, w.Sk, w.D)).astype(np.float32)
+    v = wl.round_to(rng.standard_normal((w.B, w.H, w.Sk, w.D)).astype(np.float32), "bf16")
+    return q, k, v
+
+
+def run_fused_scaled(w, q, k, v, scale):
+    out = torch.full_like(q, float("nan"))
+    api.flash_attn_fwd(q, k, v, None, None, q_pos_offset=w.q_off, k_pos_offset=w.k_off, rot_dim=0,
+                       layout=w.layout, causal=w.causal, softmax_scale=scale, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+SCORE_RANGE_CASES = [
+    # (name, B, H, Sq, Sk, D, causal, integer range of q and k)
+    ("large_scores_causal_d64", 1, 2, 300, 300, 64, True, 3),
+    ("large_scores_d128", 1, 2, 200, 260, 128, False, 2),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_RANGE_CASES, ids=lambda c: c[0])
+def test_fused_large_scores(orc, case):
+    """Integer q, k in [-lim, lim] give scores of tens to hundreds (log2
+    units): the reference is raised, probabilities are taken against it and
+    O, l are rescaled.  Every output vs the oracle, max |err| <= 2e-2."""
+    name, B, H, Sq, Sk, D, causal, lim = case
+    w = wl.AttentionWorkload(name, B, H, Sq, Sk, D, "bf16", 0, "neox", rot_dim=0, causal=causal)
+    q, k, v = exact_score_inputs(w, lim, 4321 + Sq)
+    got = to64(run_fused_scaled(w, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), LN2))
+    want = orc.attention(q, k, v, rot_dim=0, causal=causal, scale=LN2)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= BF16_TOL
+
+
+def test_fused_first_scores_far_below_zero(orc):
+    """Queries along +e0 and the first 64 keys along -e0 give every row's
+    first key tile scores near -144 (log2 units), below the range a zero
+    reference covers; later keys score near 0.  Rows 0..63 see only the
+    first tile, later rows see both, so the reference first drops to about
+    -140 and then rises by about 140.  Every output vs the oracle, max |err|
+    <= 2e-2."""
+    B, H, S, D = 1, 2, 256, 64
+    w = wl.AttentionWorkload("first_scores_far_below_zero", B, H, S, S, D, "bf16", 0, "neox", rot_dim=0,
+                             causal=True)
+    q, k, v = exact_score_inputs(w, 1, 987)
+    q[..., 0] = 12.0
+    k[:, :, :64, :] = 0.0
+    k[:, :, :64, 0] = -12.0
+    k[:, :, :64, 1] = np.arange(64) % 5   # distinct scores inside the first tile
+    q[..., 1] = 1.0
+    got = to64(run_fused_scaled(w, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), LN2))
+    want = orc.attention(q, k, v, rot_dim=0, causal=True, scale=LN2)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= BF16_TOL
+
+
+def test_fused_small_scores(orc):
+    """q and k scaled by 1/20: every score near 0, the reference stays 0 for
+    the whole launch (fast path only after each wave's first tile).  Every
+    output vs the oracle, max |err| <= 2e-2."""
+    w = wl.AttentionWorkload("small_scores_neox_1x2x260x64", 1, 2, 260, 260, 64, "bf16", 77, "neox",
+                             base=1e4, causal=True)
+    q, k, v = wl.attention_inputs(w)
+    q, k = wl.round_to(q / 20, "bf16"), wl.round_to(k / 20, "bf16")
+    got = to64(run_fused(w, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")))
+    want = orc.attention(q, k, v, rot_dim=w.rot, base=w.base, layout=w.layout, causal=True)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= BF16_TOL
+
+
 def test_fused_deterministic_and_unfused_agree():
     """Two runs are bit-identical; the fused kernel agrees with the unfused
     path (rope_apply on copies of Q and K, then the kernel with rotation
