@@ -254,6 +254,11 @@ __device__ __forceinline__ float4 bload16f(rsrc_t r, int byte_off)
 {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+__device__ __forceinline__ uint4 bload8(rsrc_t r, int byte_off)
+{
+    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+    return make_uint4(v.x, v.y, 0, 0);
+}
 
 // Per-thread staging plan for K tiles (fixed across tiles).  A slot is two
 // 8-dim chunks of one key row, D/16 slots per row:
@@ -285,33 +290,42 @@ struct VItem {
 // exact path (true row max, lazy rescale).
 constexpr float FAST_SUM_LIMIT = 8192.0f;
 
-// D: head dim; BN: keys per tile (32 or 64); NG: key groups per workgroup;
-// FULL: rot_dim == D (every K slot rotates); BAL: the balanced schedule (a
-// separate instantiation, so the default kernel does not carry its
-// share-walking code).
-template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, bool BAL>
+// D: head dim; BN: keys per tile (32 or 64); NG: groups of 4 waves per
+// workgroup; FULL: rot_dim == D (every K slot rotates); BAL: the balanced
+// schedule (a separate instantiation, so the default kernel does not carry
+// its share-walking code); RS (row split, NG = 2): the two groups take two
+// different 128-row query tiles and consume the same key tiles, so each
+// staged tile serves 256 rows; otherwise the groups take the same rows and
+// alternate key tiles.
+template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, bool BAL, bool RS>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_bf16_kernel(Params p)
 {
+    static_assert(!RS || (NG == 2 && !BAL), "row split: two groups, default schedule");
     using Plan = KPlan<D, LAYOUT, ROT, BN>;
     constexpr int NKB = BN / 32;                    // 32-key blocks per tile
     constexpr int KP = D + KPAD;                    // K LDS row pitch
     constexpr int K_ELEMS = BN * KP, V_ELEMS = BN * VP;
-    constexpr int KI = Plan::ITEMS;                 // K slots per thread per tile
+    // staging threads per tile: a group, or (row split) the workgroup, whose
+    // threads then take half slots (8 dims: NeoX 4 + 4 partner dims)
+    constexpr int NST = RS ? 512 : 256;
+    constexpr int KUNITS = RS ? 2 * Plan::SLOTS : Plan::SLOTS;   // K staging units per tile
+    constexpr int KI = (KUNITS + NST - 1) / NST;    // K units per thread per tile
     constexpr int VSLOTS = BN * (D / 8);            // V 16-byte chunks per tile
-    constexpr int VI = (VSLOTS + 255) / 256;        // per thread (the last may be empty)
+    constexpr int VI = (VSLOTS + NST - 1) / NST;    // per thread (the last may be empty)
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
     constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
     // the light half's waves stage the heavy half's exclusive tiles alone
     // (two key groups only: with one group at D = 128 there are no spare
     // registers for the deeper loads)
-    constexpr bool OFFLOAD = NG == 2 && !BAL;
+    constexpr bool OFFLOAD = NG == 2 && !BAL && !RS;
+    constexpr int NBUF = RS ? 1 : NG;               // buffer sets (one per key stream)
 
-    // [group][buffer] K tiles, then [group][buffer] V tiles.  K runs one tile
-    // ahead of V: while tile t's probabilities are formed, the scores of
-    // tile t+NG are computed from the other K buffer.
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NG * 2 * (K_ELEMS + V_ELEMS)];
+    // [stream][buffer] K tiles, then [stream][buffer] V tiles.  K runs one
+    // tile ahead of V: while tile t's probabilities are formed, the scores of
+    // the next tile are computed from the other K buffer.
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF * 2 * (K_ELEMS + V_ELEMS)];
 
     const int tid = threadIdx.x;
     // group and wave are uniform across a wave; saying so keeps every
@@ -322,8 +336,9 @@ void flash_fwd_bf16_kernel(Params p)
     const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);   // wave inside the group
     const int l32 = lane & 31, hh = lane >> 5;
     const int rh = p.rot_dim / 2;   // table row stride
-    auto kbuf = [&](int b) { return lds + (group * 2 + b) * K_ELEMS; };
-    auto vbuf = [&](int b) { return lds + NG * 2 * K_ELEMS + (group * 2 + b) * V_ELEMS; };
+    const int stream = RS ? 0 : group;
+    auto kbuf = [&](int b) { return lds + (stream * 2 + b) * K_ELEMS; };
+    auto vbuf = [&](int b) { return lds + NBUF * 2 * K_ELEMS + (stream * 2 + b) * V_ELEMS; };
 
     // ---------------- staging plans ----------------
     // A K item is one slot of a key row: mode -1 no slot, 0 copy, 1 NeoX
@@ -332,6 +347,38 @@ void flash_fwd_bf16_kernel(Params p)
     // tile's block of table rows.  A V item is one 16-byte chunk.
     auto k_item = [&](int item) {
         KItem it;
+        if constexpr (RS) {
+            // half slot: two 4-dim chunks (NeoX: dims 4h and their partners
+            // 4h + rot/2; GPT-J: 8 consecutive dims, 4 whole pairs; past
+            // rot_dim: 8 consecutive dims, copied) and 4 cos/sin values
+            constexpr int HPR = D / 8;   // half slots per row
+            const int row = item / HPR, h = item % HPR;
+            int d0, d1;
+            it.row = row;
+            if (item >= KUNITS) {
+                it.mode = -1;
+                d0 = d1 = 0;
+            } else if constexpr (Plan::NEOX_SLOT) {
+                const int rhs = p.rot_dim / 8;   // rotated half slots per row
+                if (h < rhs) {
+                    it.mode = 1;
+                    d0 = 4 * h;
+                    d1 = d0 + rh;
+                } else {
+                    it.mode = 0;
+                    d0 = p.rot_dim + 8 * (h - rhs);
+                    d1 = d0 + 4;
+                }
+            } else {
+                it.mode = (ROT && 8 * h < p.rot_dim) ? 2 : 0;
+                d0 = 8 * h;
+                d1 = d0 + 4;
+            }
+            it.o0 = row * D + d0;
+            it.o1 = row * D + d1;
+            it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
+            return it;
+        }
         const int row = item / Plan::SLOTS_PER_ROW;
         const int slot = item % Plan::SLOTS_PER_ROW;
         int d0 = 0, d1 = 0;
@@ -367,13 +414,14 @@ void flash_fwd_bf16_kernel(Params p)
         it.l = row * VP + 8 * (item % (D / 8));    // LDS offset
         return it;
     };
-    // Plan A: the 256 threads of a group share the staging of a tile.
+    // Plan A: the threads of a key stream share the staging of a tile.
+    const int stid = RS ? tid : gtid;
     KItem kpa[KI];
     VItem vpa[VI];
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kpa[i] = k_item(gtid + 256 * i);
+    for (int i = 0; i < KI; ++i) kpa[i] = k_item(stid + NST * i);
 #pragma unroll
-    for (int i = 0; i < VI; ++i) vpa[i] = v_item(gtid + 256 * i);
+    for (int i = 0; i < VI; ++i) vpa[i] = v_item(stid + NST * i);
 
     // V^T operand addressing for ds_read_b64_tr_b16: in each 16-lane group
     // the source lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving
@@ -394,8 +442,12 @@ void flash_fwd_bf16_kernel(Params p)
     // different halves.
     auto segment = [&](int bh, int64_t rowA, int64_t rowB, int64_t kb, int64_t ke, bool full,
                        int64_t seg_v, int64_t w) {
-        const int half = ((wave >> 1) ^ (NG == 2 ? group : 0)) & 1;
-        const int64_t wq0 = (half ? rowB : rowA) + 32 * (wave & 1);   // first row of this wave
+        // key split: wave w of group 0 takes half (w >> 1) & 1, rows 32 (w &
+        // 1) of it, group 1 the other half on each SIMD; row split: group g
+        // takes the 128 rows at rowA / rowB, wave w rows 32 w of them
+        const int half = RS ? group : ((wave >> 1) ^ (NG == 2 ? group : 0)) & 1;
+        const int64_t wq0 = RS ? (group ? rowB : rowA) + 32 * wave
+                               : (half ? rowB : rowA) + 32 * (wave & 1);   // first row of this wave
         const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
         const uint16_t *kh = p.k + (int64_t)bh * p.Sk * D;
         const uint16_t *vh = p.v + (int64_t)bh * p.Sk * D;
@@ -410,10 +462,11 @@ void flash_fwd_bf16_kernel(Params p)
         // Group g takes tiles kb + g, kb + g + NG, ...: iteration j of the
         // group handles tile T(j) = kb + j NG + g, whose K sits in K buffer
         // j & 1 and whose V sits in V buffer j & 1.
-        const int n_iter = (int)((ke - kb + NG - 1) / NG);
-        const int t0 = (int)kb + group;
+        constexpr int TS = RS ? 1 : NG;   // tile stride of a key stream
+        const int n_iter = (int)((ke - kb + TS - 1) / TS);
+        const int t0 = (int)kb + (RS ? 0 : group);
         const int tend = (int)ke;
-        auto T = [&](int j) { return t0 + j * NG; };
+        auto T = [&](int j) { return t0 + j * TS; };
 
         // ---- K/V loads and staging ----
         // Global loads of key tile kt's K items (with their table rows) and
@@ -426,8 +479,13 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 if (ki[i].mode < 0) continue;
-                r0[i] = bload16(krs, 2 * ki[i].o0);
-                r1[i] = bload16(krs, 2 * ki[i].o1);
+                if constexpr (RS) {   // two 4-dim chunks
+                    r0[i] = bload8(krs, 2 * ki[i].o0);
+                    r1[i] = bload8(krs, 2 * ki[i].o1);
+                } else {
+                    r0[i] = bload16(krs, 2 * ki[i].o0);
+                    r1[i] = bload16(krs, 2 * ki[i].o1);
+                }
             }
             if constexpr (ROT) {
                 // table rows are rot_dim/2 floats; descriptors count 16-byte
@@ -442,8 +500,10 @@ void flash_fwd_bf16_kernel(Params p)
                     const int to = 4 * ki[i].to;
                     *reinterpret_cast<float4 *>(c[i]) = bload16f(crs, to);
                     *reinterpret_cast<float4 *>(s[i]) = bload16f(srs, to);
-                    *reinterpret_cast<float4 *>(c[i] + 4) = bload16f(crs, to + 16);
-                    *reinterpret_cast<float4 *>(s[i] + 4) = bload16f(srs, to + 16);
+                    if constexpr (!RS) {
+                        *reinterpret_cast<float4 *>(c[i] + 4) = bload16f(crs, to + 16);
+                        *reinterpret_cast<float4 *>(s[i] + 4) = bload16f(srs, to + 16);
+                    }
                 }
             }
         };
@@ -468,6 +528,48 @@ void flash_fwd_bf16_kernel(Params p)
                 // LDS rows have pitch KP; the chunk offsets inside a row are
                 // o - row * D.
                 uint16_t *row = kdst + ki[i].row * (KP - D);
+                if constexpr (RS) {
+                    // half slot: 4-dim chunks (NeoX lo / partner hi, or the
+                    // two pairs of pairs of a GPT-J half slot)
+                    uint2 w0 = make_uint2(r0[i].x, r0[i].y), w1 = make_uint2(r1[i].x, r1[i].y);
+                    if constexpr (ROT) {
+                        float a[4], b[4], cc[4], ss[4];
+                        const uint32_t u0[2] = {r0[i].x, r0[i].y}, u1[2] = {r1[i].x, r1[i].y};
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            if constexpr (LAYOUT == 0) {
+                                a[2 * u] = rope::bf16lo_to_f32(u0[u]); a[2 * u + 1] = rope::bf16hi_to_f32(u0[u]);
+                                b[2 * u] = rope::bf16lo_to_f32(u1[u]); b[2 * u + 1] = rope::bf16hi_to_f32(u1[u]);
+                            } else {   // pairs (lo, hi) of each dword
+                                a[u] = rope::bf16lo_to_f32(u0[u]); b[u] = rope::bf16hi_to_f32(u0[u]);
+                                a[2 + u] = rope::bf16lo_to_f32(u1[u]); b[2 + u] = rope::bf16hi_to_f32(u1[u]);
+                            }
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) { cc[u] = c[i][u]; ss[u] = s[i][u]; }
+                        rotate_pairs<4>(a, b, cc, ss);
+                        uint2 x0, x1;
+                        if constexpr (LAYOUT == 0) {
+                            x0 = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                            x1 = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+                        } else {
+                            x0 = make_uint2(pack_bf16x2(a[0], b[0]), pack_bf16x2(a[1], b[1]));
+                            x1 = make_uint2(pack_bf16x2(a[2], b[2]), pack_bf16x2(a[3], b[3]));
+                        }
+                        if constexpr (FULL) {
+                            w0 = x0;
+                            w1 = x1;
+                        } else {
+                            // half slots past rot_dim keep their input bits
+                            const bool rot_slot = ki[i].mode != 0;
+                            w0 = rot_slot ? x0 : w0;
+                            w1 = rot_slot ? x1 : w1;
+                        }
+                    }
+                    *reinterpret_cast<uint2 *>(row + ki[i].o0) = w0;
+                    *reinterpret_cast<uint2 *>(row + ki[i].o1) = w1;
+                    continue;
+                }
                 uint4 w0 = r0[i], w1 = r1[i];
                 if constexpr (ROT && LAYOUT == 0) {
                     float lo[8], hi[8], cc[8], ss[8];
@@ -761,14 +863,14 @@ void flash_fwd_bf16_kernel(Params p)
         // One barrier per iteration; every wave of the workgroup runs the
         // same number of iterations, plus one at the end.
         const int c_end = kt_end < tend ? kt_end : tend;   // this wave computes tiles [t0, c_end)
-        int j_end = c_end > t0 ? (c_end - t0 + NG - 1) / NG : 0;
+        int j_end = c_end > t0 ? (c_end - t0 + TS - 1) / TS : 0;
         if (j_end > n_iter) j_end = n_iter;
         int j_split = n_iter;
         if constexpr (OFFLOAD) {
             if (rowB < p.Sq) {
                 const int64_t lastA = rowA + 63 < p.Sq ? rowA + 63 : p.Sq - 1;
                 const int light_end = (int)row_visits(p, lastA);   // light rows see tiles < light_end
-                const int js = light_end > t0 ? (light_end - t0 + NG - 1) / NG : 0;
+                const int js = light_end > t0 ? (light_end - t0 + TS - 1) / TS : 0;
                 if (js < j_split) j_split = js;
             }
         }
@@ -920,7 +1022,7 @@ void flash_fwd_bf16_kernel(Params p)
         float l_tot = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
         float m_fin = m_set ? m_ref : -INFINITY;
         float *xfer = reinterpret_cast<float *>(lds);
-        if constexpr (NG == 2) {
+        if constexpr (NG == 2 && !RS) {
             // group 1 hands its state to group 0 through LDS: per wave, per
             // lane, DB*16 accumulators + m + l, component-major.
             if (group == 1) {
@@ -965,7 +1067,7 @@ void flash_fwd_bf16_kernel(Params p)
         };
 
         if (full) {
-            if (group == 0) write_out();
+            if (RS || group == 0) write_out();
         } else if (group == 0) {
             // Split query tile: publish this segment's state; the merge
             // kernel that follows on the stream combines the segments.
@@ -990,6 +1092,16 @@ void flash_fwd_bf16_kernel(Params p)
         const int bh = blockIdx.x % p.BH;
         const int64_t rank = blockIdx.x / p.BH;
         int64_t rowA, rowB;
+        if constexpr (RS) {
+            // two 128-row query tiles: with the causal mask tiles r and
+            // n - 1 - r, otherwise 2r and 2r + 1
+            const int64_t tb = p.causal ? p.n_qtiles - 1 - rank : 2 * rank + 1;
+            rowA = (p.causal ? rank : 2 * rank) * BM;
+            rowB = (tb != rank && tb < p.n_qtiles) ? tb * BM : p.Sq;
+            const int64_t lastr = (rowB < p.Sq ? rowB : rowA) + BM - 1;   // rowB > rowA when present
+            segment(bh, rowA, rowB, 0, row_visits(p, lastr < p.Sq ? lastr : p.Sq - 1), true, 0, 0);
+            return;
+        }
         if (p.causal) {
             const int64_t hb = p.n_half - 1 - rank;
             rowA = 64 * rank;
@@ -1173,14 +1285,20 @@ int launch(const FlashArgs &a, hipStream_t stream)
         p.sk_G = 0;   // no (or too small a) workspace: one workgroup per query tile
     else
         p.ws_part = static_cast<float *>(a.workspace);
-    const int64_t blocks = p.sk_G > 0 ? p.sk_G
-                           : (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
-    if (p.sk_G > 0)
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true>), dim3((unsigned)blocks),
+    // D = 128, default schedule: row split (two query tiles per workgroup)
+    constexpr bool RSPLIT = D == 128;
+    if (p.sk_G > 0) {
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true, false>), dim3((unsigned)p.sk_G),
                            dim3(256 * NG), 0, stream, p);
-    else
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, false>), dim3((unsigned)blocks),
+    } else if constexpr (RSPLIT) {
+        const int64_t blocks = (int64_t)p.BH * ((p.n_qtiles + 1) / 2);
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, 2, BN, false, true>), dim3((unsigned)blocks),
+                           dim3(512), 0, stream, p);
+    } else {
+        const int64_t blocks = (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, false, false>), dim3((unsigned)blocks),
                            dim3(256 * NG), 0, stream, p);
+    }
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     if (p.sk_G > 0) {
         hipLaunchKernelGGL((flash_merge_kernel<D>), dim3((unsigned)(p.BH * p.n_qtiles)), dim3(256), 0,
