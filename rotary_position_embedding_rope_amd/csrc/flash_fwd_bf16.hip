@@ -379,8 +379,22 @@ void flash_fwd_bf16_kernel(Params p)
             it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
             return it;
         }
-        const int row = item / Plan::SLOTS_PER_ROW;
-        const int slot = item % Plan::SLOTS_PER_ROW;
+        int row = item / Plan::SLOTS_PER_ROW;
+        int slot = item % Plan::SLOTS_PER_ROW;
+        if constexpr (D == 64) {
+            // 16 consecutive items (one pass of a 128-bit LDS write) take 4
+            // slots of 4 rows chosen so that their chunks cover the 64 banks
+            // once (row pitch 36 dwords): rows r + {0, 4, 8, 12} when the
+            // chunks sit at dword 4 slot (+16), rows r + {0, 1, 8, 9} when
+            // they sit at dword 8 slot (+4).  A wave still covers 16 whole
+            // rows, so the global loads are unchanged.
+            const int q = item >> 4, k = item & 15;
+            slot = k & 3;
+            if constexpr (Plan::NEOX_SLOT && FULL)
+                row = 16 * (q >> 2) + (q & 3) + 4 * (k >> 2);
+            else
+                row = 16 * (q >> 2) + 2 * (q & 3) + ((k >> 2) & 1) + 8 * (k >> 3);
+        }
         int d0 = 0, d1 = 0;
         it.row = row;
         if (item >= Plan::SLOTS) {
@@ -408,7 +422,10 @@ void flash_fwd_bf16_kernel(Params p)
     };
     auto v_item = [&](int item) {
         VItem it;
-        const int row = item / (D / 8);
+        int row = item / (D / 8);
+        // D = 64: the two rows of one 16-lane write pass are r and r + 2
+        // (pitch 80 dwords: 32 banks apart), not r and r + 1
+        if constexpr (D == 64) row = (row & ~3) | ((row & 1) << 1) | ((row >> 1) & 1);
         it.ok = item < VSLOTS;
         it.o = row * D + 8 * (item % (D / 8));     // element offset inside the tile
         it.l = row * VP + 8 * (item % (D / 8));    // LDS offset
