@@ -305,14 +305,18 @@ void flash_fwd_bf16_kernel(Params p)
     using Plan = KPlan<D, LAYOUT, ROT, BN>;
     constexpr int NKB = BN / 32;                    // 32-key blocks per tile
     constexpr int KP = D + KPAD;                    // K LDS row pitch
-    constexpr int K_ELEMS = BN * KP, V_ELEMS = BN * VP;
+    // D = 64 with a key split: value tiles go from HBM straight into LDS
+    // (buffer loads with the LDS bit), unpadded and swizzled (dma_v); else
+    // through registers into rows of pitch VP
+    constexpr bool VDMA = D == 64 && !RS;
+    constexpr int K_ELEMS = BN * KP, V_ELEMS = VDMA ? BN * D : BN * VP;
     // staging threads per tile: a group, or (row split) the workgroup, whose
     // threads then take half slots (8 dims: NeoX 4 + 4 partner dims)
     constexpr int NST = RS ? 512 : 256;
     constexpr int KUNITS = RS ? 2 * Plan::SLOTS : Plan::SLOTS;   // K staging units per tile
     constexpr int KI = (KUNITS + NST - 1) / NST;    // K units per thread per tile
     constexpr int VSLOTS = BN * (D / 8);            // V 16-byte chunks per tile
-    constexpr int VI = (VSLOTS + NST - 1) / NST;    // per thread (the last may be empty)
+    constexpr int VI = VDMA ? 1 : (VSLOTS + NST - 1) / NST;   // per thread (the last may be empty; unused with VDMA)
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
     constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
@@ -321,11 +325,12 @@ void flash_fwd_bf16_kernel(Params p)
     // registers for the deeper loads)
     constexpr bool OFFLOAD = NG == 2 && !BAL && !RS;
     constexpr int NBUF = RS ? 1 : NG;               // buffer sets (one per key stream)
+    constexpr int NVB = 2;                          // V buffers per set
 
     // [stream][buffer] K tiles, then [stream][buffer] V tiles.  K runs one
     // tile ahead of V: while tile t's probabilities are formed, the scores of
     // the next tile are computed from the other K buffer.
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF * 2 * (K_ELEMS + V_ELEMS)];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF * (2 * K_ELEMS + NVB * V_ELEMS)];
 
     const int tid = threadIdx.x;
     // group and wave are uniform across a wave; saying so keeps every
@@ -338,7 +343,8 @@ void flash_fwd_bf16_kernel(Params p)
     const int rh = p.rot_dim / 2;   // table row stride
     const int stream = RS ? 0 : group;
     auto kbuf = [&](int b) { return lds + (stream * 2 + b) * K_ELEMS; };
-    auto vbuf = [&](int b) { return lds + NBUF * 2 * K_ELEMS + (stream * 2 + b) * V_ELEMS; };
+    auto vbuf = [&](int b) { return lds + NBUF * 2 * K_ELEMS + (stream * NVB + b) * V_ELEMS; };
+    auto vslot = [&](int j) { return j & 1; };   // V buffer of tile T(j)
 
     // ---------------- staging plans ----------------
     // A K item is one slot of a key row: mode -1 no slot, 0 copy, 1 NeoX
@@ -446,6 +452,12 @@ void flash_fwd_bf16_kernel(Params p)
     const int g16 = lane >> 4, lp = lane & 15;
     const int tr_row = lp >> 2, tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
     const int tr_key = 4 * (g16 >> 1) + tr_row;   // + 32kb + 16mm (+ 8)
+    // VDMA layout: column offset of dims 32 bd + tr_col in a key row whose
+    // chunks are swizzled by 4 ((key >> 1) & 1) (the key's low bits are tr_row)
+    int vcol[D / 32];
+#pragma unroll
+    for (int bd = 0; bd < D / 32; ++bd)
+        vcol[bd] = 8 * ((4 * bd + (tr_col >> 3)) ^ (4 * ((tr_row >> 1) & 1))) + (tr_col & 7);
     const rope::bf16x2_t ones = __builtin_bit_cast(rope::bf16x2_t, 0x3f803f80u);   // (1, 1)
 
     // One segment: key tiles [kb, ke) of the 128 query rows made of two
@@ -531,6 +543,28 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < N; ++i)
                 if (vi[i].ok) vr[i] = bload16(vrs, 2 * vi[i].o);
+        };
+        // VDMA: blocks [blk0, blk0 + NBLK) of value tile kt straight into V
+        // buffer b.  A block is 8 rows = 1 KB of LDS, written by one buffer
+        // load of the wave: lane q (LDS bytes 16q .. 16q+15 of the block)
+        // takes row q/8 of the block and 16-byte chunk (q%8) ^ 4((q/16)&1)
+        // of that row, so that the 4 keys a transposing read of P V fetches
+        // at once sit in 4 different 16-bank groups.  Rows past Sk (and
+        // tiles past the segment) are written as zeros.  The loads complete
+        // asynchronously: the issuing wave waits for them (vmcnt) before the
+        // barrier that hands the tile over.
+        auto dma_v = [&](int kt, int b, int blk0, auto NBLK) {
+            const int j0 = kt * BN;
+            const int rows = kt < tend ? sk32 - j0 : 0;
+            const rsrc_t vrs = make_rsrc<2 * D>(vh + (int64_t)j0 * D, rows);
+            const int r = lane >> 3, c = (lane & 7) ^ (4 * ((r >> 1) & 1));
+#pragma unroll
+            for (int i = 0; i < decltype(NBLK)::value; ++i) {
+                const int blk = blk0 + i;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    vrs, (__attribute__((address_space(3))) void *)(vbuf(b) + blk * 8 * D), 16,
+                    2 * ((8 * blk + r) * D + 8 * c), 0, 0, 0);
+            }
         };
         // Rotate fetched K items in fp32 at their key positions, round to
         // bf16 and write them to K buffer b; write fetched V items to V
@@ -648,7 +682,8 @@ void flash_fwd_bf16_kernel(Params p)
             float pc[KI][8], ps[KI][8];
             if (T(0) < tend) {
                 fetch_k(T(0), kpa, kr0, kr1, kc, ks);
-                fetch_v(T(0), vpa, vr);
+                if constexpr (VDMA) dma_v(T(0), 0, 2 * wave, std::integral_constant<int, 2>{});
+                else fetch_v(T(0), vpa, vr);
             }
             if (T(1) < tend) fetch_k(T(1), kpa, pr0, pr1, pc, ps);
 
@@ -708,7 +743,7 @@ void flash_fwd_bf16_kernel(Params p)
             }
             if (T(0) < tend) {
                 stage_k(0, kpa, kr0, kr1, kc, ks);
-                stage_v(0, vpa, vr);
+                if constexpr (!VDMA) stage_v(0, vpa, vr);
             }
             if (T(1) < tend) stage_k(1, kpa, pr0, pr1, pc, ps);
         }
@@ -852,10 +887,11 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                     for (int bd = 0; bd < DB; ++bd) {
                         const int key0 = 32 * kb2 + 16 * mm + tr_key;
-                        const uint16_t *src = v_lds + key0 * VP + 32 * bd + tr_col;
+                        constexpr int RP = VDMA ? D : VP;   // row pitch
+                        const uint16_t *src = v_lds + key0 * RP + (VDMA ? vcol[bd] : 32 * bd + tr_col);
                         const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
                         const s16x4_t x1 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * VP));
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * RP));
                         const bf16x8_t a = __builtin_bit_cast(
                             bf16x8_t, (short __attribute__((ext_vector_type(8)))){
                                           x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
@@ -864,18 +900,19 @@ void flash_fwd_bf16_kernel(Params p)
         };
 
         // Phase 1 (plan A), iterations [0, j_split), every wave of the group
-        // sharing the staging.  Iteration j (tile T(j)): fetch K(j+2) and
-        // V(j+1) from HBM; compute the scores of tile j+1 (its K was staged
-        // one iteration earlier) on the matrix cores while forming tile j's
-        // probabilities from the scores computed one iteration earlier; then
-        // add tile j's P V while rotating and staging K(j+2) and V(j+1) into
-        // the buffers iteration j-1 finished reading.
+        // sharing the staging.  Iteration j (tile T(j)): load V(j+1) (straight
+        // into LDS with VDMA); compute the scores of tile j+1 (its K was
+        // staged one iteration earlier) on the matrix cores while forming
+        // tile j's probabilities from the scores computed one iteration
+        // earlier; then add tile j's P V while rotating and staging K(j+2)
+        // (and, without VDMA, V(j+1)) into the buffers iteration j-1 finished
+        // reading; then fetch K(j+3) (and V(j+2)) into registers.
         //
         // Phase 2 (plan B), [j_split, n_iter): the tiles left are seen only
-        // by the heavy half's rows.  The light half's two waves stage them
-        // alone (K(j+2) and V(j) in iteration j), loading two tiles ahead;
-        // the heavy half's waves only compute, adding tile j-1's P V in the
-        // same matrix-core stream as tile j+1's scores.
+        // by the heavy half's rows.  The light half's two waves stage their
+        // K tiles (K(j+2) in iteration j), loading two tiles ahead; the heavy
+        // half's waves compute and load the V tiles (V(j+1) in iteration j)
+        // straight into LDS.
         //
         // One barrier per iteration; every wave of the workgroup runs the
         // same number of iterations, plus one at the end.
@@ -897,8 +934,29 @@ void flash_fwd_bf16_kernel(Params p)
         // iteration j-1 (here for j = 0), ahead of the barrier.
         auto fetch_next = [&](int j) {
             if (T(j + 2) < tend) fetch_k(T(j + 2), kpa, kr0, kr1, kc, ks);
-            if (T(j + 1) < tend) fetch_v(T(j + 1), vpa, vr);
+            if constexpr (!VDMA)
+                if (T(j + 1) < tend) fetch_v(T(j + 1), vpa, vr);
         };
+        // VDMA: right after the barrier that starts iteration j each wave
+        // loads its share of V(j+1) into V buffer (j+1) & 1, whose V(j-1) was
+        // read in iteration j-1; before the barrier that ends iteration j it
+        // waits for all its vector-memory loads (vmcnt 0), so the tile is
+        // complete when iteration j+1 reads it.  4 waves share a tile: 2
+        // blocks each; 2 waves: 4 blocks each.
+        auto wait_vm0 = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0); expcnt, lgkmcnt: no wait
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto dma_next = [&](int j, int blk0, auto NBLK) {
+            if constexpr (VDMA) dma_v(T(j + 1), (j + 1) & 1, blk0, NBLK);
+        };
+        auto wait_dma = [&]() {
+            if constexpr (VDMA) wait_vm0();
+        };
+        using blk2 = std::integral_constant<int, 2>;
+        using blk4 = std::integral_constant<int, 4>;
+        wait_dma();   // V(0)
         if (j_split > 0) fetch_next(0);
         __syncthreads();
         // scores S[j & 1] of tile j
@@ -907,7 +965,7 @@ void flash_fwd_bf16_kernel(Params p)
 
         auto stage_next = [&](int j) {
             stage_k(j & 1, kpa, kr0, kr1, kc, ks);
-            stage_v((j + 1) & 1, vpa, vr);
+            if constexpr (!VDMA) stage_v((j + 1) & 1, vpa, vr);
         };
         // tile j's probabilities on the fast path (exact path if needed);
         // `mfma` issues the matrix-core work they are interleaved with
@@ -938,24 +996,29 @@ void flash_fwd_bf16_kernel(Params p)
         // phase-1 iteration
         auto step_a = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
             __syncthreads();   // K(j+1), V(j) staged; buffers of iteration j-1 free
+            dma_next(j, 2 * wave, blk2{});
             bf16x8_t pb[NKB][2];
             softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
             // tile j's P V on the matrix cores, interleaved with staging
-            pv(pb, j & 1);
+            pv(pb, vslot(j));
             stage_next(j);
 #pragma unroll
             for (int i = 0; i < 2 * NKB * DB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 64 / (2 * NKB * DB), 0);   // vector ALU
             }
+            wait_dma();   // V(j+1)
             if (j + 1 < j_split) fetch_next(j + 1);
         };
-        // phase-2 iteration of a heavy wave: no staging
-        auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
+        // phase-2 iteration of a heavy wave: the pair loads V(j+1) (4
+        // blocks per wave, from block pblk)
+        auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB], int pblk) {
             __syncthreads();   // K(j+1), V(j) staged
+            dma_next(j, pblk, blk4{});
             bf16x8_t pb[NKB][2];
             softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
-            pv(pb, j & 1);
+            pv(pb, vslot(j));
+            wait_dma();   // V(j+1)
         };
 
         // ---- phase 1 ----
@@ -973,66 +1036,68 @@ void flash_fwd_bf16_kernel(Params p)
         }
         for (; j < j_split; ++j) {
             __syncthreads();
+            dma_next(j, 2 * wave, blk2{});
             stage_next(j);
+            wait_dma();
             if (j + 1 < j_split) fetch_next(j + 1);
         }
         // ---- phase 2 ----
         if constexpr (OFFLOAD) {
             if (j_split < n_iter) {
+                // Iteration j stages K(j+2) and loads V(j+1), as in phase 1.
+                // The light pair's 128 threads stage the K tiles, with their
+                // rotation, two register sets deep (K(j+2) staged while
+                // K(j+4) loads); the heavy pair's 128 threads load the V
+                // tiles straight into LDS.
+                constexpr int KIB = (Plan::SLOTS + 127) / 128;
+                const int ptid = (wave & 1) * 64 + lane;   // thread index inside the pair
                 if (light) {
-                    // the light pair's 128 threads stage whole tiles: two
-                    // register sets, K(j+2) / V(j+1) staged while K(j+4) /
-                    // V(j+3) load
-                    constexpr int KIB = (Plan::SLOTS + 127) / 128, VIB = (VSLOTS + 127) / 128;
-                    const int ltid = (wave & 1) * 64 + lane;
                     KItem kpb[KIB];
-                    VItem vpb[VIB];
 #pragma unroll
-                    for (int i = 0; i < KIB; ++i) kpb[i] = k_item(ltid + 128 * i);
-#pragma unroll
-                    for (int i = 0; i < VIB; ++i) vpb[i] = v_item(ltid + 128 * i);
-                    uint4 a0[KIB], a1[KIB], av[VIB], b0[KIB], b1[KIB], bv[VIB];
+                    for (int i = 0; i < KIB; ++i) kpb[i] = k_item(ptid + 128 * i);
+                    uint4 a0[KIB], a1[KIB], b0[KIB], b1[KIB];
                     float ac[KIB][8], as[KIB][8], bc[KIB][8], bs[KIB][8];
-                    auto fetch_b = [&](int jj, auto &r0, auto &r1, auto &c, auto &s, auto &vv) {
+                    auto fetch_b = [&](int jj, auto &r0, auto &r1, auto &c, auto &s) {
                         if (T(jj + 2) < tend) fetch_k(T(jj + 2), kpb, r0, r1, c, s);
-                        if (T(jj + 1) < tend) fetch_v(T(jj + 1), vpb, vv);
                     };
-                    auto stage_b = [&](int jj, const auto &r0, const auto &r1, const auto &c, const auto &s,
-                                       const auto &vv) {
-                        stage_k(jj & 1, kpb, r0, r1, c, s);
-                        stage_v((jj + 1) & 1, vpb, vv);
-                    };
-                    fetch_b(j, a0, a1, ac, as, av);
-                    fetch_b(j + 1, b0, b1, bc, bs, bv);
+                    fetch_b(j, a0, a1, ac, as);
+                    fetch_b(j + 1, b0, b1, bc, bs);
                     for (; j < n_iter; j += 2) {
                         __syncthreads();
-                        stage_b(j, a0, a1, ac, as, av);
-                        fetch_b(j + 2, a0, a1, ac, as, av);
+                        stage_k(j & 1, kpb, a0, a1, ac, as);
+                        fetch_b(j + 2, a0, a1, ac, as);
                         if (j + 1 < n_iter) {
                             __syncthreads();
-                            stage_b(j + 1, b0, b1, bc, bs, bv);
-                            fetch_b(j + 3, b0, b1, bc, bs, bv);
+                            stage_k((j + 1) & 1, kpb, b0, b1, bc, bs);
+                            fetch_b(j + 3, b0, b1, bc, bs);
                         }
                     }
                     j = n_iter;
                 } else {
+                    static_assert(VDMA, "phase 2 loads value tiles straight into LDS");
+                    const int pblk = 4 * (wave & 1);
                     auto run = [&](f32x16_t (&A)[NKB], f32x16_t (&B)[NKB]) {
                         // iterations [j, j_end); tile j's scores in A
                         for (; j + 1 < j_end; j += 2) {
-                            step_b(j, A, B);
-                            step_b(j + 1, B, A);
+                            step_b(j, A, B, pblk);
+                            step_b(j + 1, B, A, pblk);
                         }
                         if (j < j_end) {
-                            step_b(j, A, B);
+                            step_b(j, A, B, pblk);
                             ++j;
                         }
                     };
                     if (j & 1) run(S1, S0);
                     else run(S0, S1);
-                    for (; j < n_iter; ++j) __syncthreads();
+                    for (; j < n_iter; ++j) {
+                        __syncthreads();
+                        dma_next(j, pblk, blk4{});
+                        wait_dma();
+                    }
                 }
             }
         }
+        wait_dma();   // the value loads of tiles past the segment
         __syncthreads();   // all tiles consumed
 
         // ---- per-segment epilogue ----
