@@ -72,9 +72,9 @@ class Oracle:
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         lib.oracle_rope.argtypes = [_dp, _dp, i64, i32, i32, _dp, dbl, i32]
         lib.oracle_trig.argtypes = [dbl, i32, i64, _dp, _dp]
-        lib.oracle_attention.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i64, i64, i32, i32,
+        lib.oracle_attention.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i64, i64, i64, i32, i32,
                                          i64, i64, i32, dbl, i32, i32, dbl]
-        lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, i64, i64, i64, i64, i32, i32,
+        lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, i64, i64, i64, i64, i64, i32, i32,
                                               i64, i64, i32, dbl, i32, i32, dbl,
                                               _i64p, i64, _dp]
         lib.oracle_threads.argtypes = []
@@ -124,19 +124,21 @@ class Oracle:
                   scale: float = 0.0) -> np.ndarray:
         """Forward of softmax attention over rotated Q/K.
 
-        ``q`` ``[B,H,Sq,D]``, ``k`` ``[B,H,Sk,D]``, ``v`` ``[B,H,Sk,Dv]``; 2-D or
-        3-D inputs are promoted.  ``rot_dim=0`` disables the rotation.
+        ``q`` ``[B,H,Sq,D]``, ``k`` ``[B,Hkv,Sk,D]``, ``v`` ``[B,Hkv,Sk,Dv]``
+        (``Hkv`` divides ``H``; query head h reads key/value head
+        h // (H // Hkv)); 2-D or 3-D inputs are promoted.  ``rot_dim=0``
+        disables the rotation.
         """
         q, k, v = (_f64(a) for a in (q, k, v))
         nd = q.ndim
         while q.ndim < 4:
             q, k, v = q[None], k[None], v[None]
         B, H, Sq, D = q.shape
-        Sk, Dv = k.shape[2], v.shape[3]
+        Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
         rot = D if rot_dim is None else int(rot_dim)
         o = np.empty((B, H, Sq, Dv))
         self._check(self._lib.oracle_attention(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Sq, Sk, D, Dv, int(q_off), int(k_off),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, Sq, Sk, D, Dv, int(q_off), int(k_off),
             rot, float(base), _LAYOUTS[layout], int(bool(causal)), float(scale)))
         return o.reshape(o.shape[4 - nd:])
 
@@ -146,12 +148,12 @@ class Oracle:
         """Output rows ``(b, h, i)`` of the same forward; returns ``[len(rows), Dv]``."""
         q, k, v = (_f64(a) for a in (q, k, v))
         B, H, Sq, D = q.shape
-        Sk, Dv = k.shape[2], v.shape[3]
+        Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
         rot = D if rot_dim is None else int(rot_dim)
         r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
         out = np.empty((r.shape[0], Dv))
         self._check(self._lib.oracle_attention_rows(
-            _ptr(q), _ptr(k), _ptr(v), B, H, Sq, Sk, D, Dv, int(q_off), int(k_off), rot,
+            _ptr(q), _ptr(k), _ptr(v), B, H, Hkv, Sq, Sk, D, Dv, int(q_off), int(k_off), rot,
             float(base), _LAYOUTS[layout], int(bool(causal)), float(scale),
             r.ctypes.data_as(_i64p), r.shape[0], _ptr(out)))
         return out

@@ -165,31 +165,37 @@ static void attend_row(const double *qr, const double *kr, const double *v,
     for (int e = 0; e < Dv; ++e) out[e] /= l;
 }
 
-static int attn_args_ok(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int D, int Dv,
+static int attn_args_ok(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
                         int rot_dim, double base, int layout)
 {
     if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || Dv <= 0) return 0;
+    if (Hkv <= 0 || H % Hkv != 0) return 0;
     if (rot_dim == 0) return D > 0 && D % 2 == 0;
     return rope_args_ok(D, rot_dim, base, layout);
 }
 
-/* Full attention forward.  q [B,H,Sq,D], k [B,H,Sk,D], v [B,H,Sk,Dv],
- * o [B,H,Sq,Dv], all contiguous fp64.  Query i has position q_off + i and key
- * j position k_off + j; Q and K are rotated at those positions (rot_dim == 0:
- * no rotation), V is never rotated ([RF] section 1).  scale <= 0 selects
- * 1/sqrt(D).  A query with no visible key is rejected ([RF] section 5). */
+/* Full attention forward.  q [B,H,Sq,D], k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv],
+ * o [B,H,Sq,Dv], all contiguous fp64.  Query head h of batch b attends to key
+ * and value head h / (H / Hkv) of batch b (Hkv divides H; Hkv == H is plain
+ * multi-head attention, fewer key heads are shared by consecutive query
+ * heads: [TR] "Inputs the agent should gather first", item 3, and "Required
+ * reasoning process", step 10, for the two head counts).  Query i has
+ * position q_off + i and key j position k_off + j; Q and K are rotated at
+ * those positions (rot_dim == 0: no rotation), V is never rotated ([RF]
+ * section 1).  scale <= 0 selects 1/sqrt(D).  A query with no visible key is
+ * rejected ([RF] section 5). */
 int oracle_attention(const double *q, const double *k, const double *v, double *o,
-                     int64_t B, int64_t H, int64_t Sq, int64_t Sk, int D, int Dv,
+                     int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
                      int64_t q_off, int64_t k_off, int rot_dim, double base,
                      int layout, int causal, double scale)
 {
-    if (!attn_args_ok(B, H, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!attn_args_ok(B, H, Hkv, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
     if (!q || !k || !v || !o) return OR_ERR_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     for (int64_t i = 0; i < Sq; ++i)
         if (visible_keys(i, Sk, q_off, k_off, causal) == 0) return OR_ERR_EMPTY_ROW;
 
-    const int64_t nq = B * H * Sq, nk = B * H * Sk;
+    const int64_t nq = B * H * Sq, nk = B * Hkv * Sk, group = H / Hkv;
     double *qr = malloc(sizeof(double) * (size_t)(nq * D));
     double *kr = malloc(sizeof(double) * (size_t)(nk * D));
     if (!qr || !kr) { free(qr); free(kr); return OR_ERR_NOMEM; }
@@ -213,8 +219,9 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
 #pragma omp for schedule(dynamic, 16)
             for (int64_t r = 0; r < nq; ++r) {
                 int64_t bh = r / Sq, i = r % Sq;
+                int64_t kvh = bh / group;   /* (b * H + h) / group = b * Hkv + h / group */
                 int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
-                attend_row(qr + r * D, kr + bh * Sk * D, v + bh * Sk * Dv, n, D, Dv,
+                attend_row(qr + r * D, kr + kvh * Sk * D, v + kvh * Sk * Dv, n, D, Dv,
                            scale, scores, o + r * Dv);
             }
             free(scores);
@@ -230,12 +237,12 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
  * o_rows ([n_rows, Dv]) receives output row (b, h, i).  Each selected row
  * rotates its own query and visible keys. */
 int oracle_attention_rows(const double *q, const double *k, const double *v,
-                          int64_t B, int64_t H, int64_t Sq, int64_t Sk, int D, int Dv,
+                          int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
                           int64_t q_off, int64_t k_off, int rot_dim, double base,
                           int layout, int causal, double scale,
                           const int64_t *rows, int64_t n_rows, double *o_rows)
 {
-    if (!attn_args_ok(B, H, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!attn_args_ok(B, H, Hkv, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
     if (!q || !k || !v || (n_rows > 0 && (!rows || !o_rows)) || n_rows < 0) return OR_ERR_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     for (int64_t r = 0; r < n_rows; ++r) {
@@ -256,13 +263,13 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
 #pragma omp for schedule(dynamic, 1)
             for (int64_t r = 0; r < n_rows; ++r) {
                 int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
-                int64_t bh = b * H + h;
+                int64_t bh = b * H + h, kvh = b * Hkv + h / (H / Hkv);
                 int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
                 rotate_row(q + (bh * Sq + i) * D, qr, D, rot_dim, (double)(q_off + i), base, layout);
                 for (int64_t j = 0; j < n; ++j)
-                    rotate_row(k + (bh * Sk + j) * D, kr + j * D, D, rot_dim,
+                    rotate_row(k + (kvh * Sk + j) * D, kr + j * D, D, rot_dim,
                                (double)(k_off + j), base, layout);
-                attend_row(qr, kr, v + bh * Sk * Dv, n, D, Dv, scale, scores, o_rows + r * Dv);
+                attend_row(qr, kr, v + kvh * Sk * Dv, n, D, Dv, scale, scores, o_rows + r * Dv);
             }
         }
         free(qr);

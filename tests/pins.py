@@ -351,4 +351,43 @@ def pin_rows_match_full(orc):
     assert np.array_equal(got, np.stack([full[b, h, i] for b, h, i in rows]))
 
 
+def pin_gqa_vs_torch_sdpa(orc):
+    """Fewer key/value heads than query heads: query head h reads key/value
+    head h // (H // Hkv) ([TR] "Inputs the agent should gather first", item 3,
+    and "Required reasoning process", step 10, for the two head counts).
+    torch's scaled_dot_product_attention with enable_gqa=True, in fp64 on the
+    CPU with the explicit offset mask, agrees at 1e-12; so does the
+    sampled-row entry point, bit for bit with the full forward."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(43)
+    B, H, Hkv, Sq, Sk, D = 2, 6, 2, 5, 9, 8
+    q = rng.standard_normal((B, H, Sq, D))
+    k, v = rng.standard_normal((B, Hkv, Sk, D)), rng.standard_normal((B, Hkv, Sk, D))
+    q_off, k_off = 6, 2
+    qr = orc.rope(q, q_off + np.arange(Sq), layout="neox")
+    kr = orc.rope(k, k_off + np.arange(Sk), layout="neox")
+    mask = torch.tensor(offset_mask(Sq, Sk, q_off, k_off))
+    want = F.scaled_dot_product_attention(torch.tensor(qr), torch.tensor(kr), torch.tensor(v),
+                                          attn_mask=mask, dropout_p=0.0, enable_gqa=True).numpy()
+    got = orc.attention(q, k, v, q_off=q_off, k_off=k_off, layout="neox")
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    rows = [(0, 1, 3), (1, 4, 2), (0, 0, 0), (1, 5, 4)]
+    sel = orc.attention_rows(q, k, v, rows, q_off=q_off, k_off=k_off, layout="neox")
+    assert np.array_equal(sel, np.stack([got[b, h, i] for b, h, i in rows]))
+
+
+def pin_gqa_head_count_must_divide(orc):
+    """A key/value head count that does not divide the query head count is
+    rejected."""
+    rng = np.random.default_rng(47)
+    q = rng.standard_normal((1, 4, 3, 8))
+    k, v = rng.standard_normal((1, 3, 3, 8)), rng.standard_normal((1, 3, 3, 8))
+    try:
+        orc.attention(q, k, v, layout="neox")
+    except Exception:
+        return
+    raise AssertionError("head counts 4 / 3 accepted")
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

@@ -28,6 +28,9 @@ MUTATIONS = {
     "pv_index": ("out[e] += scores[j] * v[j * Dv + e];", "out[e] += scores[j] * v[j * Dv];"),
     "not_normalised": ("for (int e = 0; e < Dv; ++e) out[e] /= l;", ""),
     "query_rotated_at_key_offset": ("(double)(q_off + r % Sq)", "(double)(k_off + r % Sq)"),
+    "kv_heads_interleaved": ("int64_t kvh = bh / group;", "int64_t kvh = (bh / H) * Hkv + (bh % H) % Hkv;"),
+    "kv_heads_interleaved_rows": ("kvh = b * Hkv + h / (H / Hkv);", "kvh = b * Hkv + h % Hkv;"),
+    "kv_head_count_unchecked": ("if (Hkv <= 0 || H % Hkv != 0) return 0;", "if (Hkv <= 0) return 0;"),
 }
 
 
