@@ -238,8 +238,10 @@ def cpu_baseline(wl, w, seconds):
     while True:
         b, h = heads[done % len(heads)]
         sl = (slice(b, b + 1), slice(h, h + 1))
-        orc.attention(np.ascontiguousarray(q[sl]), np.ascontiguousarray(k[sl]),
-                      np.ascontiguousarray(v[sl]), q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot,
+        g = h // (w.H // w.Hkv)   # the key/value head of query head h
+        skv = (slice(b, b + 1), slice(g, g + 1))
+        orc.attention(np.ascontiguousarray(q[sl]), np.ascontiguousarray(k[skv]),
+                      np.ascontiguousarray(v[skv]), q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot,
                       base=w.base, layout=w.layout, causal=w.causal)
         done += 1
         if time.perf_counter() - t0 >= seconds:

@@ -134,7 +134,12 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  *
  *   q, o        [B, H, Sq, head_dim], contiguous, element type `dtype`;
  *               o is written whole and must not alias q, k or v.
- *   k, v        [B, H, Sk, head_dim], contiguous.
+ *   k, v        [B, H_kv, Sk, head_dim], contiguous.  H_kv >= 1 divides H;
+ *               query head h reads key/value head h / (H / H_kv): H_kv == H
+ *               is multi-head attention, H_kv < H grouped-query attention
+ *               (the two head counts of [TR] "Inputs the agent should gather
+ *               first", item 3; [RF] section 7 names GQA as the lever on
+ *               cache bytes).  H % H_kv != 0 is ROPE_ERR_SHAPE.
  *   cos_tab,    fp32 [table_rows, rot_dim/2]; need
  *   sin_tab     table_rows >= max(q_pos_offset + Sq, k_pos_offset + Sk)
  *               (else ROPE_ERR_TABLE_RANGE).
@@ -162,7 +167,7 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  *               result up to floating-point rounding order).
  */
 int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
-                        int B, int H, int64_t Sq, int64_t Sk, int head_dim,
+                        int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
                         int64_t q_pos_offset, int64_t k_pos_offset,
                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
                         int rot_dim, int layout, int causal, float softmax_scale,

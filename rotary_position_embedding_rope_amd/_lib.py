@@ -38,7 +38,7 @@ def load() -> ctypes.CDLL:
     lib.rope_apply.argtypes = [vp, i64, i64, i32, vp, i64, i64, i32, vp, i64, vp, vp, i64,
                                i32, i32, i32, i32, vp]
     lib.rope_apply.restype = i32
-    lib.rope_flash_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i32, i64, i64,
+    lib.rope_flash_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i64, i64,
                                         vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     lib.rope_flash_attn_fwd.restype = i32
     lib.rope_flash_attn_workspace_size.argtypes = [i32, i32, i64, i64, i32, i64, i64, i32, i32]

@@ -131,7 +131,9 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    q_pos_offset: int = 0, k_pos_offset: int = 0, rot_dim: int | None = None,
                    layout="neox", causal: bool = True, softmax_scale: float = 0.0,
                    out: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
-    """Fused RoPE + attention forward on ``[B, H, S, D]`` tensors.
+    """Fused RoPE + attention forward: ``q`` ``[B, H, Sq, D]``, ``k`` and
+    ``v`` ``[B, H_kv, Sk, D]`` with H_kv dividing H (query head h reads
+    key/value head h // (H // H_kv)).
 
     ``rot_dim=0`` (or no tables) runs plain attention.  Returns ``out``
     (allocated like ``q`` when not given).  ``workspace``: None (one
@@ -144,9 +146,9 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if t.dim() != 4 or not t.is_contiguous() or t.dtype != q.dtype:
             raise ValueError("q, k, v must be contiguous [B, H, S, D] tensors of one dtype")
     B, H, Sq, D = q.shape
-    Sk = k.shape[2]
-    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, H, Sk, D] matching q")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Sk, D) or v.shape != k.shape or Hkv < 1 or H % Hkv != 0:
+        raise ValueError("k and v must be [B, H_kv, Sk, D] with H_kv dividing q's H")
     if rot_dim is None:
         rot_dim = D if cos is not None else 0
     if rot_dim > 0:
@@ -167,7 +169,7 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
     _check(lib.rope_flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   B, H, Sq, Sk, D, int(q_pos_offset), int(k_pos_offset),
+                                   B, H, Hkv, Sq, Sk, D, int(q_pos_offset), int(k_pos_offset),
                                    cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),
                                    float(softmax_scale), _dtype(q), wp, wb, _stream(q)),
            "rope_flash_attn_fwd")
@@ -193,7 +195,7 @@ def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int =
     rot = (D if cos is not None else 0) if rot_dim is None else int(rot_dim)
     wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, k.shape[2], D,
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, k.shape[1], Sq, k.shape[2], D,
             int(q_pos_offset), int(k_pos_offset), cos.data_ptr() if rot else None,
             sin.data_ptr() if rot else None, cos.shape[0] if rot else 0, rot, _layout(layout),
             int(bool(causal)), float(softmax_scale), _dtype(q), wp, wb, _stream(q))

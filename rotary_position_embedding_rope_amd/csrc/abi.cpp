@@ -129,19 +129,20 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
     if (st != ROPE_OK) return -st;
     if (dtype != ROPE_BF16) return 0;
     FlashArgs a = {};
-    a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
+    a.B = B; a.H = H; a.H_kv = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
     a.q_off = q_pos_offset; a.k_off = k_pos_offset; a.causal = causal ? 1 : 0; a.dtype = dtype;
     return rope_flash_bf16_workspace_bytes(a);
 }
 
 int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
-                        int B, int H, int64_t Sq, int64_t Sk, int head_dim,
+                        int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
                         int64_t q_pos_offset, int64_t k_pos_offset,
                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
                         int rot_dim, int layout, int causal, float softmax_scale,
                         int dtype, void *workspace, int64_t workspace_bytes, void *stream)
 {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ROPE_ERR_SHAPE;
+    if (H_kv < 1 || H % H_kv != 0) return ROPE_ERR_SHAPE;
     if (Sq > 2147483647 || Sk > 2147483647) return ROPE_ERR_SHAPE;
     if (head_dim < 2 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
@@ -170,7 +171,7 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
 
     FlashArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
-    a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
+    a.B = B; a.H = H; a.H_kv = H_kv; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
     a.q_off = q_pos_offset; a.k_off = k_pos_offset;
     a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.table_rows = table_rows;
     a.rot_dim = rot_dim; a.layout = layout; a.causal = causal ? 1 : 0;

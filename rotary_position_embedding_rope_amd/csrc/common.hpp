@@ -59,7 +59,7 @@ int rope_launch_apply(const RopeApplyArgs &a, hipStream_t stream);
 struct FlashArgs {
     const void *q, *k, *v;
     void *o;
-    int B, H;
+    int B, H, H_kv;   // query heads, key/value heads (H_kv divides H)
     int64_t Sq, Sk;
     int head_dim;
     int64_t q_off, k_off;

@@ -79,6 +79,7 @@ struct Params {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     int BH;
+    int kv_group;       // query heads per key/value head: K/V head of bh is bh / kv_group
     int64_t Sq, Sk, q_off, k_off;
     const float *cos_tab, *sin_tab;
     int64_t table_rows;
@@ -478,8 +479,9 @@ void flash_fwd_bf16_kernel(Params p)
         const int64_t wq0 = RS ? (group ? rowB : rowA) + 32 * wave
                                : (half ? rowB : rowA) + 32 * (wave & 1);   // first row of this wave
         const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
-        const uint16_t *kh = p.k + (int64_t)bh * p.Sk * D;
-        const uint16_t *vh = p.v + (int64_t)bh * p.Sk * D;
+        // (b H + h) / G = b H_kv + h / G: the key/value head of query head h
+        const uint16_t *kh = p.k + (int64_t)(bh / p.kv_group) * p.Sk * D;
+        const uint16_t *vh = p.v + (int64_t)(bh / p.kv_group) * p.Sk * D;
         const int sk32 = (int)p.Sk;
         // cos/sin rows of this segment's keys start at position k_off; table
         // rows from there on, capped at the int range
@@ -1311,6 +1313,7 @@ void plan(const FlashArgs &a, Params &p)
 {
     constexpr int BN = Shape<D>::BN, NG = Shape<D>::NG;
     p.BH = a.B * a.H;
+    p.kv_group = a.H / a.H_kv;
     p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
     p.causal = a.causal;
     p.n_qtiles = (a.Sq + BM - 1) / BM;

@@ -23,6 +23,7 @@ struct F32Params {
     const float *q, *k, *v;
     float *o;
     int BH;
+    int kv_group;   // query heads per key/value head: K/V head of bh is bh / kv_group
     int64_t Sq, Sk, q_off, k_off;
     const float *cos_tab, *sin_tab;
     int rot_dim;
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(256) void flash_fwd_f32_kernel(F32Params p)
     const int qtile = p.causal ? p.n_qtiles - 1 - rank : rank;
     const int64_t q0 = (int64_t)qtile * BM;
     const float *qh = p.q + (int64_t)bh * p.Sq * D;
-    const float *kh = p.k + (int64_t)bh * p.Sk * D;
-    const float *vh = p.v + (int64_t)bh * p.Sk * D;
+    const float *kh = p.k + (int64_t)(bh / p.kv_group) * p.Sk * D;
+    const float *vh = p.v + (int64_t)(bh / p.kv_group) * p.Sk * D;
     const int64_t q_valid = p.Sq - q0 < BM ? p.Sq - q0 : BM;
 
     // Q tile: copy, rotate in LDS, take this lane's slice.
@@ -161,6 +162,7 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.v = static_cast<const float *>(a.v);
     p.o = static_cast<float *>(a.o);
     p.BH = a.B * a.H;
+    p.kv_group = a.H / a.H_kv;
     p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
     p.cos_tab = a.cos_tab; p.sin_tab = a.sin_tab; p.rot_dim = a.rot_dim;
     p.sl2 = a.scale * 1.4426950408889634f;

@@ -57,7 +57,8 @@ def round_to(x, dtype: str) -> np.ndarray:
 
 @dataclass(frozen=True)
 class AttentionWorkload:
-    """One fused RoPE + attention forward: q [B,H,Sq,D], k/v [B,H,Sk,D]."""
+    """One fused RoPE + attention forward: q [B,H,Sq,D], k/v [B,H_kv,Sk,D]
+    (H_kv None: H; otherwise it divides H)."""
 
     name: str
     B: int
@@ -73,6 +74,11 @@ class AttentionWorkload:
     q_off: int = 0
     k_off: int = 0
     causal: bool = True
+    H_kv: int | None = None
+
+    @property
+    def Hkv(self) -> int:
+        return self.H if self.H_kv is None else self.H_kv
 
     @property
     def rot(self) -> int:
@@ -95,7 +101,8 @@ class AttentionWorkload:
         return 4 * self.D * self.visible_pairs()
 
     def label(self) -> str:
-        return f"{self.B}x{self.H}x{self.Sq}x{self.Sk}x{self.D}"
+        kv = "" if self.Hkv == self.H else f"({self.Hkv}kv)"
+        return f"{self.B}x{self.H}{kv}x{self.Sq}x{self.Sk}x{self.D}"
 
 
 @dataclass(frozen=True)
@@ -139,7 +146,13 @@ PREFILL_OFFSET = AttentionWorkload("chunked_prefill_neox_bf16_1x32x2048q_16384k_
 RAGGED_ROPE = RopeApplyWorkload("ragged_rope_neox_bf16_8192tok_32q8kv_rot64of128", 8192, 16,
                                 32768, 32, 8, 128, 64, "neox", "bf16", 8)
 
-ATTENTION_WORKLOADS = (TINY_F32, SMALL_BF16) + SWEEP_BF16 + (PREFILL_OFFSET,)
+# the chunked prefill with 8 key/value heads for the 32 query heads (the
+# head counts of the ragged RoPE workload): grouped-query attention
+PREFILL_GQA = AttentionWorkload("chunked_prefill_gqa_neox_bf16_1x32q8kv_2048q_16384k_128", 1, 32,
+                                2048, 16384, 128, "bf16", 9, "neox", base=500000.0,
+                                q_off=14336, k_off=0, H_kv=8)
+
+ATTENTION_WORKLOADS = (TINY_F32, SMALL_BF16) + SWEEP_BF16 + (PREFILL_OFFSET, PREFILL_GQA)
 
 
 # ---------------------------------------------------------------------------
@@ -150,8 +163,8 @@ def attention_inputs(w: AttentionWorkload):
     """(q, k, v) as fp32 arrays holding values exact in ``w.dtype``."""
     rng = np.random.default_rng(w.seed)
     q = rng.standard_normal((w.B, w.H, w.Sq, w.D))
-    k = rng.standard_normal((w.B, w.H, w.Sk, w.D))
-    v = rng.standard_normal((w.B, w.H, w.Sk, w.D))
+    k = rng.standard_normal((w.B, w.Hkv, w.Sk, w.D))
+    v = rng.standard_normal((w.B, w.Hkv, w.Sk, w.D))
     return tuple(round_to(a.astype(np.float32), w.dtype) for a in (q, k, v))
 
 

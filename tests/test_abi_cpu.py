@@ -127,11 +127,12 @@ def test_rope_apply_noop_needs_no_device(lib, over):
 
 
 def fwd_args(**over):
-    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, B=1, H=8, Sq=4096, Sk=4096, D=64, qo=0, ko=0,
-             cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX, causal=1,
-             scale=0.0, dtype=_lib.BF16, ws=None, wsb=0)
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, B=1, H=8, Hkv=None, Sq=4096, Sk=4096, D=64, qo=0,
+             ko=0, cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX,
+             causal=1, scale=0.0, dtype=_lib.BF16, ws=None, wsb=0)
     a.update(over)
-    return [a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["qo"],
+    hkv = a["H"] if a["Hkv"] is None else a["Hkv"]
+    return [a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], hkv, a["Sq"], a["Sk"], a["D"], a["qo"],
             a["ko"], a["cos"], a["sin"], a["rows"], a["rot"], a["layout"], a["causal"], a["scale"],
             a["dtype"], a["ws"], a["wsb"], None]
 
@@ -141,6 +142,9 @@ def fwd_args(**over):
     (dict(H=-1), _lib.ERR_SHAPE),
     (dict(Sq=0), _lib.ERR_SHAPE),
     (dict(Sk=0), _lib.ERR_SHAPE),
+    (dict(Hkv=0), _lib.ERR_SHAPE),
+    (dict(Hkv=3), _lib.ERR_SHAPE),               # 3 does not divide 8
+    (dict(Hkv=16), _lib.ERR_SHAPE),
     (dict(D=63), _lib.ERR_SHAPE),
     (dict(rot=66), _lib.ERR_SHAPE),
     (dict(rot=-2), _lib.ERR_SHAPE),

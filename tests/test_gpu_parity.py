@@ -276,7 +276,9 @@ def oracle_rows(orc, w, q, k, v, rows, rot=None):
     for b, h in heads:
         idx = [i for bb, hh, i in rows if (bb, hh) == (b, h)]
         sl = (slice(b, b + 1), slice(h, h + 1))
-        res = orc.attention_rows(q[sl], k[sl], v[sl], [(0, 0, i) for i in idx], q_off=w.q_off,
+        g = h // (w.H // w.Hkv)
+        skv = (slice(b, b + 1), slice(g, g + 1))
+        res = orc.attention_rows(q[sl], k[skv], v[skv], [(0, 0, i) for i in idx], q_off=w.q_off,
                                  k_off=w.k_off, rot_dim=rot, base=w.base, layout=w.layout,
                                  causal=w.causal)
         for i, r in zip(idx, res):
@@ -311,7 +313,8 @@ def test_fused_bf16_full(orc, w):
     assert np.array_equal(got[:, :, 0], v[:, :, 0].astype(np.float64))
 
 
-@pytest.mark.parametrize("w", list(wl.SWEEP_BF16) + [wl.PREFILL_OFFSET], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", list(wl.SWEEP_BF16) + [wl.PREFILL_OFFSET, wl.PREFILL_GQA],
+                         ids=lambda w: w.name)
 def test_fused_full_size_sampled(orc, w):
     """Full-size workloads in the benchmark's launch configuration: sampled
     output rows (first/last rows, tile edges, random) vs the oracle row by
@@ -341,6 +344,32 @@ EDGE_CASES = [
     (1, 2, 320, 320, 64, "bf16", "neox", 64, 0, 0, True),       # odd number of 64-row halves
     (1, 1, 448, 600, 64, "bf16", "gptj", 64, 152, 0, True),     # offset mask, D=64, paired halves
 ]
+
+
+GQA_CASES = [
+    # (B, H, H_kv, Sq, Sk, D, dtype, layout, rot, q_off, k_off, causal)
+    (2, 8, 2, 300, 300, 64, "bf16", "neox", 64, 0, 0, True),      # 4 query heads per key head
+    (1, 8, 2, 448, 448, 64, "bf16", "gptj", 64, 0, 0, True),      # paired halves, both phases
+    (1, 4, 1, 200, 260, 128, "bf16", "gptj", 128, 0, 0, False),   # one key/value head, D=128
+    (1, 8, 4, 150, 400, 128, "bf16", "neox", 128, 250, 0, True),  # offset mask, D=128
+    (1, 6, 3, 70, 70, 64, "f32", "neox", 64, 0, 0, True),         # fp32 kernel
+    (2, 4, 2, 97, 97, 128, "f32", "gptj", 64, 3, 3, True),        # fp32, partial rotation
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_gqa_full(orc, case):
+    """Fewer key/value heads than query heads: every output vs the oracle."""
+    B, H, Hkv, Sq, Sk, D, dtype, layout, rot, qo, ko, causal = case
+    w = wl.AttentionWorkload("gqa", B, H, Sq, Sk, D, dtype, 4321 + Sq, layout, base=1e4,
+                             rot_dim=rot, q_off=qo, k_off=ko, causal=causal, H_kv=Hkv)
+    q, k, v = wl.attention_inputs(w)
+    assert k.shape == (B, Hkv, Sk, D)
+    got = to64(run_fused(w, to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)))
+    want = orc.attention(q, k, v, q_off=qo, k_off=ko, rot_dim=rot, base=w.base, layout=layout,
+                         causal=causal)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= (BF16_TOL if dtype == "bf16" else F32_TOL)
 
 
 @pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "x".join(map(str, c)))
@@ -472,6 +501,8 @@ BALANCED = [
     wl.AttentionWorkload("balanced_neox_1x8x2048x128", 1, 8, 2048, 2048, 128, "bf16", 23, "neox"),
     wl.AttentionWorkload("balanced_offset_gptj_1x8x1500x2600x128", 1, 8, 1500, 2600, 128, "bf16", 24,
                          "gptj", q_off=1100, k_off=0),
+    wl.AttentionWorkload("balanced_gqa_neox_1x8q2kv_2048x64", 1, 8, 2048, 2048, 64, "bf16", 25,
+                         "neox", H_kv=2),
 ]
 
 

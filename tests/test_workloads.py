@@ -23,6 +23,15 @@ def test_attention_inputs_deterministic_and_exact():
     assert abs(float(a[0].std()) - 1.0) < 0.02
 
 
+def test_gqa_inputs():
+    w = wl.PREFILL_GQA
+    assert (w.H, w.Hkv) == (32, 8)
+    small = wl.AttentionWorkload("g", 1, 6, 5, 7, 8, "bf16", 3, "neox", H_kv=2)
+    q, k, v = wl.attention_inputs(small)
+    assert q.shape == (1, 6, 5, 8) and k.shape == v.shape == (1, 2, 7, 8)
+    assert wl.SMALL_BF16.Hkv == wl.SMALL_BF16.H
+
+
 def test_ragged_workload():
     w = wl.RAGGED_ROPE
     d = wl.rope_apply_inputs(w)
