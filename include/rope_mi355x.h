@@ -183,6 +183,60 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
                                        int64_t q_pos_offset, int64_t k_pos_offset, int causal,
                                        int dtype);
 
+/*
+ * rope_decode_attn_fwd -- one decode step over a key/value cache: rotate the
+ * new query and key of each request at its cache position, append the
+ * rotated key and the unrotated value to the cache, and attend over the
+ * cache with the offset mask, never rotating a cached key again ([RF]
+ * section 2 for this decoder flow, section 6 for the offset mask; [TR]
+ * "Performance requirements" for doing the decode rotation inside the
+ * attention launch).
+ *
+ * Request b's new token sits at position L = cache_lens[b], the number of
+ * keys already cached: rows 0..L-1 of the cache hold keys rotated at their
+ * positions (by earlier steps, or by rope_apply after a prefill).  The call
+ * writes rope(k_new[b], L) to k_cache[b, :, L] and v_new[b] to
+ * v_cache[b, :, L], and
+ *   o[b, h] = softmax(scale * rope(q[b, h], L) . k_cache[b, h / (H/H_kv), 0..L])
+ *             . v_cache[b, h / (H/H_kv), 0..L]
+ * (all L + 1 keys are visible to the new query).
+ *
+ *   q, o        [B, H, head_dim] bf16, one new query per request; o is
+ *               written whole and must not alias the other arrays.
+ *   k_new,      [B, H_kv, head_dim] bf16; H_kv divides H, H / H_kv <= 8.
+ *   v_new
+ *   k_cache,    [B, H_kv, S_max, head_dim] bf16, contiguous; written at row
+ *   v_cache     L of each (b, head) only.
+ *   cache_lens  device int32 [B].  A value outside [0, S_max), or (rot_dim >
+ *               0) outside [0, table_rows), is detected on the device: that
+ *               request's o rows are set to NaN and its cache is neither read
+ *               nor written.
+ *   cos_tab,    fp32 [table_rows, rot_dim/2] (see rope_tables_build).
+ *   sin_tab
+ *   rot_dim     0 (no rotation; tables may be NULL) or even, 2..head_dim.
+ *   head_dim    64 or 128;  layout ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16.
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
+ *   workspace   device scratch of at least rope_decode_workspace_size()
+ *               bytes, 16-byte aligned, contents irrelevant: fp32 partial
+ *               states of ranges of cached positions, merged by a second
+ *               kernel enqueued right after on the same stream.  Calls that
+ *               share a workspace must not run concurrently.
+ * Requires 16-byte-aligned q, k_new, v_new, caches, o (else ROPE_ERR_ALIGN).
+ */
+int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
+                         void *k_cache, void *v_cache, const int32_t *cache_lens, void *o,
+                         int B, int H, int H_kv, int64_t S_max, int head_dim,
+                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                         int rot_dim, int layout, float softmax_scale, int dtype,
+                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * rope_decode_workspace_size -- bytes of workspace rope_decode_attn_fwd needs
+ * for these shapes, or minus a status code for shapes it would reject.
+ * Makes no device allocation.
+ */
+int64_t rope_decode_workspace_size(int B, int H, int H_kv, int64_t S_max, int head_dim);
+
 #ifdef __cplusplus
 }
 #endif

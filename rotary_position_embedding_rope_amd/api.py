@@ -228,3 +228,88 @@ def prepare_rope_apply(q, k, positions, cos, sin, rot_dim: int | None = None, la
         if status != _lib.OK:
             raise RopeError(status, "rope_apply")
     return launch
+
+
+def decode_workspace(q: torch.Tensor, k_cache: torch.Tensor) -> torch.Tensor:
+    """Workspace for decode_attn_fwd on these shapes, cached per device and
+    grown on demand.  Calls sharing it must be serialised (one stream)."""
+    lib = _lib.load()
+    B, H, D = q.shape
+    need = lib.rope_decode_workspace_size(B, H, k_cache.shape[1], k_cache.shape[2], D)
+    if need < 0:
+        raise RopeError(-need, "rope_decode_workspace_size")
+    key = ("decode", q.device)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
+                 softmax_scale, out, workspace):
+    _require_cuda(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, out)
+    for t in (q, k_new, v_new, k_cache, v_cache, out):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("q, k_new, v_new, caches and out must be contiguous bfloat16")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, D] (one new query per request)")
+    B, H, D = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("k_cache must be [B, H_kv, S_max, D]")
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
+        raise ValueError("v_cache like k_cache, k_new/v_new [B, H_kv, D]")
+    if out.shape != q.shape:
+        raise ValueError("out must be like q")
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,) or not cache_lens.is_contiguous():
+        raise ValueError("cache_lens must be a contiguous int32 [B] vector")
+    rot = (D if cos is not None else 0) if rot_dim is None else int(rot_dim)
+    if rot > 0:
+        if cos is None or sin is None or cos.dtype != torch.float32 or cos.shape != sin.shape \
+                or not cos.is_contiguous() or not sin.is_contiguous() or cos.dim() != 2 \
+                or cos.shape[1] != rot // 2:
+            raise ValueError("cos/sin must be contiguous float32 [rows, rot_dim/2]")
+        cp, sp, rows = cos.data_ptr(), sin.data_ptr(), cos.shape[0]
+    else:
+        cp, sp, rows = None, None, 0
+    if workspace is None:
+        workspace = decode_workspace(q, k_cache)
+    return (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            cache_lens.data_ptr(), out.data_ptr(), B, H, Hkv, S_max, D, cp, sp, rows, rot,
+            _layout(layout), float(softmax_scale), _lib.BF16, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(q))
+
+
+def decode_attn_fwd(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, cache_lens: torch.Tensor,
+                    cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,
+                    rot_dim: int | None = None, layout="neox", softmax_scale: float = 0.0,
+                    out: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
+    """One decode step: ``q`` ``[B, H, D]``, ``k_new``/``v_new`` ``[B, H_kv, D]``
+    at positions ``cache_lens`` (int32 ``[B]``); appends rope(k_new) and v_new
+    to ``k_cache``/``v_cache`` ``[B, H_kv, S_max, D]`` and returns the
+    attention output ``[B, H, D]`` over the L + 1 cached keys."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
+                        softmax_scale, out, workspace)
+    _check(lib.rope_decode_attn_fwd(*args), "rope_decode_attn_fwd")
+    return out
+
+
+def prepare_decode_attn_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, cos=None,
+                            sin=None, rot_dim: int | None = None, layout="neox",
+                            softmax_scale: float = 0.0, workspace=None):
+    """Validate once and return a zero-argument callable that enqueues the
+    decode step on fixed buffers (each call appends at the same positions)."""
+    args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
+                        softmax_scale, out, workspace)
+    fn = _lib.load().rope_decode_attn_fwd
+
+    def launch():
+        status = fn(*args)
+        if status != _lib.OK:
+            raise RopeError(status, "rope_decode_attn_fwd")
+    return launch

@@ -184,4 +184,68 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
     return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
 }
 
+namespace {
+
+int check_decode_shape(int B, int H, int H_kv, int64_t S_max, int head_dim)
+{
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || S_max < 1) return ROPE_ERR_SHAPE;
+    if (S_max > 2147483647) return ROPE_ERR_SHAPE;
+    if (head_dim < 2 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return ROPE_ERR_UNSUPPORTED;
+    if (H / H_kv > 8) return ROPE_ERR_UNSUPPORTED;
+    const int64_t ranges = rope_decode_ranges(S_max);
+    if ((int64_t)B * H_kv * ranges > kMaxGrid || (int64_t)B * H > kMaxGrid) return ROPE_ERR_SHAPE;
+    return ROPE_OK;
+}
+
+int64_t decode_workspace_bytes(int B, int H, int64_t S_max, int head_dim)
+{
+    return (int64_t)B * H * rope_decode_ranges(S_max) * (head_dim + 2) * 4;
+}
+
+}  // namespace
+
+int64_t rope_decode_workspace_size(int B, int H, int H_kv, int64_t S_max, int head_dim)
+{
+    const int st = check_decode_shape(B, H, H_kv, S_max, head_dim);
+    if (st != ROPE_OK) return -st;
+    return decode_workspace_bytes(B, H, S_max, head_dim);
+}
+
+int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
+                         void *k_cache, void *v_cache, const int32_t *cache_lens, void *o,
+                         int B, int H, int H_kv, int64_t S_max, int head_dim,
+                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                         int rot_dim, int layout, float softmax_scale, int dtype,
+                         void *workspace, int64_t workspace_bytes, void *stream)
+{
+    const int st = check_decode_shape(B, H, H_kv, S_max, head_dim);
+    if (st != ROPE_OK) return st;
+    if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return ROPE_ERR_SHAPE;
+    if (!valid_layout(layout)) return ROPE_ERR_UNSUPPORTED;
+    if (dtype != ROPE_BF16) return ROPE_ERR_UNSUPPORTED;
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !o || !workspace)
+        return ROPE_ERR_NULL;
+    if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
+    if (rot_dim > 0 && table_rows < 1) return ROPE_ERR_TABLE_RANGE;
+    if (o == q || o == k_new || o == v_new || o == k_cache || o == v_cache) return ROPE_ERR_SHAPE;
+    if (workspace_bytes < decode_workspace_bytes(B, H, S_max, head_dim)) return ROPE_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(workspace, 16) || !aligned(cache_lens, 4))
+        return ROPE_ERR_ALIGN;
+    if (rot_dim > 0 && (!aligned(cos_tab, 4) || !aligned(sin_tab, 4))) return ROPE_ERR_ALIGN;
+
+    DecodeArgs a;
+    a.q = q; a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+    a.cache_lens = cache_lens; a.o = o;
+    a.B = B; a.H = H; a.H_kv = H_kv; a.S_max = S_max; a.head_dim = head_dim;
+    a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.table_rows = rot_dim > 0 ? table_rows : 0;
+    a.rot_dim = rot_dim; a.layout = layout;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    a.workspace = workspace;
+    const int rc = rope_launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+    return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
+}
+
 }  // extern "C"

@@ -76,3 +76,21 @@ int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream);
 // device (0: the launch needs none).
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a);
 int rope_launch_flash_f32(const FlashArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q, *k_new, *v_new;   // [B, H, D], [B, H_kv, D], [B, H_kv, D]
+    void *k_cache, *v_cache;         // [B, H_kv, S_max, D]
+    const int32_t *cache_lens;       // [B]
+    void *o;                         // [B, H, D]
+    int B, H, H_kv;
+    int64_t S_max;
+    int head_dim;
+    const float *cos_tab, *sin_tab;
+    int64_t table_rows;
+    int rot_dim, layout;
+    float scale;                     // already resolved (> 0)
+    void *workspace;                 // rope_decode_workspace_bytes() bytes
+};
+int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
+// Cached-position ranges per (request, key/value head): one workgroup each.
+int64_t rope_decode_ranges(int64_t S_max);

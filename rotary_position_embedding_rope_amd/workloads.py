@@ -106,6 +106,40 @@ class AttentionWorkload:
 
 
 @dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step over a key/value cache: B requests, one new token
+    each at position lens[b] (keys already cached); q [B,H,D], new k/v
+    [B,H_kv,D], caches [B,H_kv,S_max,D] bf16."""
+
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    D: int
+    S_max: int
+    seed: int
+    layout: str = "neox"
+    base: float = 10000.0
+    rot_dim: int | None = None
+    min_len: int = 0              # cached lengths drawn uniformly from [min_len, S_max - 1]
+
+    @property
+    def rot(self) -> int:
+        return self.D if self.rot_dim is None else self.rot_dim
+
+    def lens(self) -> np.ndarray:
+        rng = np.random.default_rng(self.seed)
+        return rng.integers(self.min_len, self.S_max, size=self.B).astype(np.int32)
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes one step must move: the cached K and V rows read once, the new
+        q, k, v read, the new K and V rows written, the output written (bf16)."""
+        cached = int(self.lens().astype(np.int64).sum())
+        return 2 * (2 * cached * self.H_kv * self.D + self.B * (self.H + 2 * self.H_kv) * self.D
+                    + 2 * self.B * self.H_kv * self.D + self.B * self.H * self.D)
+
+
+@dataclass(frozen=True)
 class RopeApplyWorkload:
     """Standalone in-place RoPE over a ragged continuous batch."""
 
@@ -154,6 +188,12 @@ PREFILL_GQA = AttentionWorkload("chunked_prefill_gqa_neox_bf16_1x32q8kv_2048q_16
 
 ATTENTION_WORKLOADS = (TINY_F32, SMALL_BF16) + SWEEP_BF16 + (PREFILL_OFFSET, PREFILL_GQA)
 
+# a decode step of a continuous batch: 16 requests with cached lengths
+# uniform in [1024, 32767], the head counts and dims of the ragged RoPE
+# workload
+DECODE = DecodeWorkload("decode_gqa_neox_bf16_16req_32q8kv_128_ctx1k-32k", 16, 32, 8, 128, 32768, 10,
+                        base=500000.0, min_len=1024)
+
 
 # ---------------------------------------------------------------------------
 # generators
@@ -197,3 +237,19 @@ def rope_apply_inputs(w: RopeApplyWorkload):
         "q": round_to(q, w.dtype),
         "k": round_to(k, w.dtype),
     }
+
+
+def decode_inputs(w: DecodeWorkload, with_cache: bool = True):
+    """dict with 'lens' (int32 [B]), 'q' [B,H,D], 'k_new', 'v_new' [B,H_kv,D]
+    and (with_cache) 'k_raw', 'v_cache' [B,H_kv,S_max,D]: the unrotated keys
+    and the values of the cached positions (fp32 arrays exact in bf16)."""
+    rng = np.random.default_rng(w.seed + 1)
+    d = {"lens": w.lens()}
+    for name, shape in (("q", (w.B, w.H, w.D)), ("k_new", (w.B, w.H_kv, w.D)),
+                        ("v_new", (w.B, w.H_kv, w.D))):
+        d[name] = round_to(rng.standard_normal(shape).astype(np.float32), "bf16")
+    if with_cache:
+        shape = (w.B, w.H_kv, w.S_max, w.D)
+        d["k_raw"] = round_to(rng.standard_normal(shape).astype(np.float32), "bf16")
+        d["v_cache"] = round_to(rng.standard_normal(shape).astype(np.float32), "bf16")
+    return d

@@ -196,3 +196,52 @@ def test_workspace_size_rejects(lib, args, want):
 def test_workspace_size_fp32_needs_none(lib):
     # the fp32 kernel has no balanced schedule: no device query, zero bytes
     assert lib.rope_flash_attn_workspace_size(1, 2, 128, 128, 64, 0, 0, 1, _lib.F32) == 0
+
+
+def decode_args(**over):
+    a = dict(q=FAKE, kn=FAKE2, vn=FAKE3, kc=FAKE4, vc=FAKE4 + 0x100000, lens=FAKE + 0x8000,
+             o=FAKE4 + 0x200000, B=16, H=32, Hkv=8, S=32768, D=128, cos=FAKE4 + 0x1000,
+             sin=FAKE4 + 0x2000, rows=32768, rot=128, layout=_lib.NEOX, scale=0.0,
+             dtype=_lib.BF16, ws=FAKE4 + 0x300000, wsb=1 << 30)
+    a.update(over)
+    return [a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["lens"], a["o"], a["B"], a["H"],
+            a["Hkv"], a["S"], a["D"], a["cos"], a["sin"], a["rows"], a["rot"], a["layout"],
+            a["scale"], a["dtype"], a["ws"], a["wsb"], None]
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(B=0), _lib.ERR_SHAPE),
+    (dict(Hkv=0), _lib.ERR_SHAPE),
+    (dict(Hkv=5), _lib.ERR_SHAPE),                 # 5 does not divide 32
+    (dict(S=0), _lib.ERR_SHAPE),
+    (dict(D=63), _lib.ERR_SHAPE),
+    (dict(rot=130), _lib.ERR_SHAPE),
+    (dict(rot=-2), _lib.ERR_SHAPE),
+    (dict(scale=float("nan")), _lib.ERR_SHAPE),
+    (dict(wsb=1024), _lib.ERR_SHAPE),              # workspace too small
+    (dict(o=FAKE), _lib.ERR_SHAPE),                # o aliases q
+    (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
+    (dict(Hkv=2), _lib.ERR_UNSUPPORTED),           # 16 query heads per key/value head
+    (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
+    (dict(layout=7), _lib.ERR_UNSUPPORTED),
+    (dict(q=None), _lib.ERR_NULL),
+    (dict(lens=None), _lib.ERR_NULL),
+    (dict(ws=None), _lib.ERR_NULL),
+    (dict(cos=None), _lib.ERR_NULL),
+    (dict(rows=0), _lib.ERR_TABLE_RANGE),
+    (dict(kc=FAKE4 + 8), _lib.ERR_ALIGN),
+    (dict(lens=FAKE + 2), _lib.ERR_ALIGN),
+    (dict(ws=FAKE4 + 0x300004), _lib.ERR_ALIGN),
+])
+def test_decode_rejects(lib, over, want):
+    assert lib.rope_decode_attn_fwd(*decode_args(**over)) == want
+
+
+def test_decode_workspace_size(lib):
+    # 16 requests x 32 heads x 64 ranges of 512 positions x (128 + 2) floats
+    assert lib.rope_decode_workspace_size(16, 32, 8, 32768, 128) == 16 * 32 * 64 * 130 * 4
+    assert lib.rope_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4
+    assert lib.rope_decode_workspace_size(1, 6, 4, 100, 128) == -_lib.ERR_SHAPE
+    assert lib.rope_decode_workspace_size(1, 32, 2, 100, 128) == -_lib.ERR_UNSUPPORTED
+    # no rotation: tables may be NULL (a bad shape is still reported)
+    assert lib.rope_decode_attn_fwd(*decode_args(rot=0, cos=None, sin=None, rows=0, B=0)) == _lib.ERR_SHAPE
