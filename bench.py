@@ -63,7 +63,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
-    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "copy"], default="all",
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "copy"], default="all",
                     help="restrict the timed kernels (for profiler runs); 'copy' runs only a "
                          "plain 256 MiB device copy, the calibration for HBM byte counters")
     ap.add_argument("--sweep", action="store_true",
@@ -168,6 +169,45 @@ def bench_rope_apply(torch, api, wl, steps, sets):
                      "traffic": recorded_traffic("rope_apply_ragged_8192tok_traffic.md", "rope_apply.hip"),
                      "algorithmic_bytes": nbytes},
     }
+
+
+def bench_decode(torch, api, wl, steps, warmup):
+    """The decode step of the continuous batch (wl.DECODE): HBM bytes the
+    step must move over the time of one step (both kernels of the step)."""
+    w = wl.DECODE
+    dev = torch.device("cuda:0")
+    d = wl.decode_inputs(w, with_cache=False)
+    q, k_new, v_new = (torch.from_numpy(d[n]).to(torch.bfloat16).to(dev) for n in ("q", "k_new", "v_new"))
+    lens = torch.from_numpy(d["lens"]).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    shape = (w.B, w.H_kv, w.S_max, w.D)
+    k_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    for b in range(w.B):   # one request at a time keeps the fp32 temporaries small
+        k_cache[b] = torch.randn(shape[1:], generator=g, device=dev)
+        v_cache[b] = torch.randn(shape[1:], generator=g, device=dev)
+    cos, sin = api.tables_build(w.base, w.rot, w.S_max, device=dev)
+    out = torch.empty_like(q)
+    launch = api.prepare_decode_attn_fwd(q, k_new, v_new, k_cache, v_cache, lens, out, cos, sin,
+                                         w.rot, w.layout)
+    stream = torch.cuda.current_stream(dev)
+    ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
+    nbytes = w.algorithmic_bytes()
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
+        "ms_per_step": round(kernel_ms, 5), "wall_ms_per_step": round(ms_step, 5),
+        "single_step_p10_ms": round(durs[len(durs) // 10], 5),
+        "single_step_p90_ms": round(durs[(9 * len(durs)) // 10], 5),
+        "cached_tokens": int(d["lens"].astype("int64").sum()),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic(f"decode_bf16_{w.name}_traffic.md", "decode_bf16.hip"),
+                     "algorithmic_bytes": nbytes},
+    }
+    del k_cache, v_cache
+    return res
 
 
 def comparators(torch, api, wl, w, r, steps, warmup):
@@ -304,6 +344,8 @@ def main():
         del r
     if args.only in ("all", "rope_apply"):
         result["rope_apply"] = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets)
+    if args.only in ("all", "decode"):
+        result["decode"] = bench_decode(torch, api, wl, args.decode_steps, max(args.warmup // 4, 3))
     if args.sweep:
         for x in wl.ATTENTION_WORKLOADS:
             if x.dtype != "bf16":

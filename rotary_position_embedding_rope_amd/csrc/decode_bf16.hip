@@ -10,22 +10,25 @@
 // rotation inside the attention launch).
 //
 // The work is bound by reading the cache once, so the kernel is laid out for
-// HBM streaming rather than for the matrix cores: a workgroup takes one
-// request, one key/value head and a contiguous range of CW cached positions
-// for all G query heads that share the key/value head, reads each 16-byte
-// chunk of K and V once with coalesced buffer loads, and forms scores and
-// P V on the vector ALU in fp32.  Ranges of one (request, key/value head) are
-// combined by a second kernel (running max and sum rescaling, the merge rule
-// of section 5 of the same page).
+// HBM streaming: a workgroup takes one request, one key/value head and a
+// contiguous range of CW cached positions for all G query heads that share
+// the key/value head, and reads each 16-byte chunk of K and V once with
+// coalesced buffer loads, two passes ahead of the one being computed.
+// Scores come from the matrix cores, P V from the vector ALU in fp32.
+// Ranges of one (request, key/value head) are combined by a second kernel
+// (running max and sum rescaling, the merge rule of section 5 of the same
+// page).
 #include "common.hpp"
 
 namespace {
 
 using rope::bf16_to_f32;
+using rope::bf16x8_t;
 using rope::f32_to_bf16;
+using rope::f32x4_t;
 
-constexpr int SUB = 128;          // keys per pass of the workgroup
-constexpr int NSUB = 4;           // passes per workgroup
+constexpr int SUB = 64;           // keys per pass of the workgroup
+constexpr int NSUB = 8;           // passes per workgroup
 constexpr int CW = SUB * NSUB;    // cached positions per workgroup
 constexpr int GMAX = 8;           // query heads per key/value head, at most
 
@@ -79,6 +82,22 @@ __device__ __forceinline__ void pair_dims(int i, int rot_dim, int &a, int &b)
     }
 }
 
+// Orders the LDS accesses of the lanes of one wave around it: writes before
+// it are seen by reads after it in any lane of the wave (lanes are separate
+// threads; without this the compiler may move a read across another lane's
+// write).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint4 pick(bool c, uint4 a, uint4 b)
+{
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 // Sum over groups of W consecutive lanes (W a power of two up to 64): every
 // lane of a group ends with the group's sum.
 template <int W>
@@ -100,20 +119,33 @@ __device__ __forceinline__ float group_max(float x)
 // [c CW, (c + 1) CW) of the L + 1 keys the new query sees (the last one is the
 // new key, taken from LDS and, by the workgroup whose range holds it,
 // appended to the cache).  GT: G rounded up to a power of two.
+//
+// A pass takes SUB keys, 16 per wave.  Scores come from the matrix cores:
+// S (16 keys x 16 query slots) = K Q'^T over D/32 steps of
+// v_mfma_f32_16x16x32_bf16, K straight from the loads in the A-operand
+// layout (lane l: key l%16, dims 8(l/16) .. +7 of each 32-dim step), Q'
+// (rotated, scaled, rounded to bf16) as the B operand, query slots past G
+// zero.  P V runs on the vector ALU, each key row split over D/8 lanes.  The
+// loads of passes s+1 and s+2 are in flight while pass s is computed.  Each
+// wave runs its own online softmax over its keys; the four waves are merged
+// once at the end.
 template <int D, int LAYOUT, bool ROT, int GT>
 __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 {
-    constexpr int LPR = D / 8;          // lanes per key row (16 bytes each)
-    constexpr int KPI = 64 / LPR;       // keys per wave load
-    constexpr int KPW = SUB / 4;        // keys per wave and pass
-    constexpr int NI = KPW / KPI;       // loads per wave and pass, for K and for V
-    static_assert(GT <= LPR && GT <= GMAX, "a lane of each row group writes one query's score");
+    constexpr int LPR = D / 8;          // lanes per value row (16 bytes each)
+    constexpr int KPI = 64 / LPR;       // value rows per wave load
+    constexpr int KPW = SUB / 4;        // keys per wave and pass (16)
+    constexpr int NV = KPW / KPI;       // value loads per wave and pass
+    constexpr int NT = D / 32;          // score MFMA steps (and key loads) per pass
+    static_assert(KPW == 16, "one 16-key score block per wave and pass");
+    static_assert(GT <= 16 && GT <= GMAX, "query slots of the score block");
 
     __shared__ __attribute__((aligned(16))) float q_lds[GT][D];    // rotated, scaled queries
-    __shared__ float s_lds[GT][SUB];                               // scores, then probabilities
+    __shared__ __attribute__((aligned(16))) float p_lds[4][GT][KPW];   // per wave: probabilities
+    __shared__ float a_lds[4][GT];                                 // per wave: rescale factors
+    __shared__ float ml_lds[4][2][GT];                             // per wave: max and sum
     __shared__ __attribute__((aligned(16))) uint16_t knew_lds[D];  // new key, rotated, bf16
     __shared__ __attribute__((aligned(16))) uint16_t vnew_lds[D];
-    __shared__ float m_run[GT], l_run[GT], alpha_lds[GT];
     __shared__ __attribute__((aligned(16))) float o_lds[4][GT][D];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -129,6 +161,32 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
     const int n = L + 1;                      // visible keys, the new one included
     const int k0 = c * CW;
     if (k0 >= n) return;
+
+    // ---- loads of one pass (issued early) ----
+    const int64_t slice = (int64_t)bk * p.S_max;   // row of (b, kvh, position 0)
+    const int kl = lane % 16, kq = lane / 16;      // score layout: key, dim quarter
+    const int vrow = lane / LPR, vsub = lane % LPR; // value layout: row, 16-byte chunk
+    auto issue = [&](int s, uint4 (&kd)[NT], uint4 (&vd)[NV]) {
+        const int ks = k0 + s * SUB;
+        // cached rows [ks, min(L, ks + SUB)); the row at L reads as zero here
+        const int rows = L - ks < SUB ? L - ks : SUB;
+        const rsrc_t krs = make_rsrc<2 * D>(p.k_cache + (slice + ks) * D, rows);
+        const rsrc_t vrs = make_rsrc<2 * D>(p.v_cache + (slice + ks) * D, rows);
+        const int kkey = wave * KPW + kl;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) kd[t] = bload16(krs, 2 * (kkey * D + 32 * t + 8 * kq));
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int key = wave * KPW + i * KPI + vrow;
+            vd[i] = bload16(vrs, 2 * (key * D + 8 * vsub));
+        }
+    };
+    // three register sets: the loads of passes s+1 and s+2 are in flight
+    // while pass s is computed
+    uint4 kd0[NT], vd0[NV], kd1[NT], vd1[NV], kd2[NT], vd2[NV];
+    auto valid = [&](int s) { return s < NSUB && k0 + s * SUB < n; };
+    issue(0, kd0, vd0);
+    if (valid(1)) issue(1, kd1, vd1);
 
     // ---- the new query rows and key at position L ----
     const int rh = p.rot_dim / 2;
@@ -149,9 +207,10 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
         q_lds[g][da] = ya * p.sl2;
         q_lds[g][db] = yb * p.sl2;
     }
+    for (int idx = G * D + tid; idx < GT * D; idx += 256) q_lds[idx / D][idx % D] = 0.f;
     const bool last = n - k0 <= CW;           // this range holds position L
     if (last) {
-        const int64_t crow_off = ((int64_t)bk * p.S_max + L) * D;
+        const int64_t crow_off = (slice + L) * D;
         for (int i = tid; i < D / 2; i += 256) {
             int da, db;
             pair_dims<LAYOUT>(i, ROT ? p.rot_dim : 0, da, db);
@@ -175,104 +234,85 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             p.v_cache[crow_off + d] = v;
         }
     }
-    if (tid < GT) {
-        m_run[tid] = -INFINITY;
-        l_run[tid] = 0.f;
-    }
     __syncthreads();
 
-    const int sub = lane % LPR;               // 16-byte chunk of the row this lane reads
+    // Q' as the B operand: lane l holds query slot l%16, dims 32t + 8(l/16) + j
+    bf16x8_t qb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            qb[t][jj] = (__bf16)(kl < GT ? q_lds[kl][32 * t + 8 * kq + jj] : 0.f);
+    }
+
     float oacc[GT][8];
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[g][e] = 0.f;
 
-    const int64_t slice = (int64_t)bk * p.S_max;   // row of (b, kvh, position 0)
-    for (int s = 0; s < NSUB; ++s) {
+    // Each wave keeps its own running max and sum over its keys, for query
+    // slot kl in lanes kl, kl+16, kl+32, kl+48 (MFMA layout); the waves'
+    // states are merged once, at the end, so the passes need no barrier.
+    float m_run = -INFINITY, l_run = 0.f;
+    auto pass = [&](int s, const uint4 (&kd)[NT], const uint4 (&vd)[NV]) {
         const int ks = k0 + s * SUB;
-        if (ks >= n) break;
-        // cached rows [ks, min(L, ks + SUB)); the row at L reads as zero here
-        const int rows = L - ks < SUB ? L - ks : SUB;
-        const rsrc_t krs = make_rsrc<2 * D>(p.k_cache + (slice + ks) * D, rows);
-        const rsrc_t vrs = make_rsrc<2 * D>(p.v_cache + (slice + ks) * D, rows);
-        uint4 kd[NI], vd[NI];
+        // scores of the wave's 16 keys for all query slots
+        const int kpos = ks + wave * KPW + kl;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const bool knew = kpos == L;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int key = wave * KPW + i * KPI + lane / LPR;
-            kd[i] = bload16(krs, 2 * (key * D + 8 * sub));
+        for (int t = 0; t < NT; ++t) {
+            // the new key's chunk is read every time and picked by value (a
+            // conditional pointer would send the loaded rows through memory)
+            const uint4 kn = *reinterpret_cast<const uint4 *>(knew_lds + 32 * t + 8 * kq);
+            const uint4 w = pick(knew, kn, kd[t]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qb[t], acc,
+                                                          0, 0, 0);
         }
+        // accumulator element r of lane l: key 4(l/16) + r of the block, query slot l%16
+        float sc[4];
+        float mb = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int key = wave * KPW + i * KPI + lane / LPR;
-            vd[i] = bload16(vrs, 2 * (key * D + 8 * sub));
+        for (int r = 0; r < 4; ++r) {
+            sc[r] = ks + wave * KPW + 4 * kq + r < n ? acc[r] : -INFINITY;
+            mb = fmaxf(mb, sc[r]);
         }
-        // scores of the wave's keys, one per lane group
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float m_new = fmaxf(m_run, mb);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // no visible key yet: all p are 0
+        float ps = 0.f, pr[4];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int key = wave * KPW + i * KPI + lane / LPR;
-            const int pos = ks + key;
-            uint4 w = kd[i];
-            if (pos == L) w = *reinterpret_cast<const uint4 *>(knew_lds + 8 * sub);
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-            float kf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = rope::bf16lo_to_f32(u[e]);
-                kf[2 * e + 1] = rope::bf16hi_to_f32(u[e]);
-            }
-#pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                const float4 qa = *reinterpret_cast<const float4 *>(&q_lds[g][8 * sub]);
-                const float4 qb = *reinterpret_cast<const float4 *>(&q_lds[g][8 * sub + 4]);
-                float acc = qa.x * kf[0];
-                acc = fmaf(qa.y, kf[1], acc);
-                acc = fmaf(qa.z, kf[2], acc);
-                acc = fmaf(qa.w, kf[3], acc);
-                acc = fmaf(qb.x, kf[4], acc);
-                acc = fmaf(qb.y, kf[5], acc);
-                acc = fmaf(qb.z, kf[6], acc);
-                acc = fmaf(qb.w, kf[7], acc);
-                acc = group_sum<LPR>(acc);
-                if (sub == g && g < G) s_lds[g][key] = pos < n ? acc : -INFINITY;
-            }
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = __builtin_amdgcn_exp2f(sc[r] - m_use);
+            ps += pr[r];
         }
-        __syncthreads();
-        // running max and sum per query: wave w takes queries w and w + 4
-#pragma unroll
-        for (int gg = 0; gg < (GT + 3) / 4; ++gg) {
-            const int g = wave + 4 * gg;
-            if (g < G) {
-                const float s0 = s_lds[g][lane], s1 = s_lds[g][lane + 64];
-                const float cmax = group_max<64>(fmaxf(s0, s1));
-                const float m_old = m_run[g];
-                const float m_new = fmaxf(m_old, cmax);   // finite: the pass has a visible key
-                const float p0 = __builtin_amdgcn_exp2f(s0 - m_new), p1 = __builtin_amdgcn_exp2f(s1 - m_new);
-                s_lds[g][lane] = p0;
-                s_lds[g][lane + 64] = p1;
-                const float psum = group_sum<64>(p0 + p1);
-                if (lane == 0) {
-                    const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);   // 0 on the first pass
-                    alpha_lds[g] = alpha;
-                    l_run[g] = l_run[g] * alpha + psum;
-                    m_run[g] = m_new;
-                }
-            }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 before the first visible key
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        // probabilities and rescale factors to the value layout, through the
+        // wave's own LDS (no other wave reads them)
+        wave_sync();   // the previous pass's reads are done
+        if (kl < GT) {
+            *reinterpret_cast<float4 *>(&p_lds[wave][kl][4 * kq]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+            if (kq == 0) a_lds[wave][kl] = alpha;
         }
-        __syncthreads();
+        wave_sync();
         // O += P V for the wave's keys, after rescaling to the new maxima
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-            const float a = g < G ? alpha_lds[g] : 0.f;
+            const float a = a_lds[wave][g];
 #pragma unroll
             for (int e = 0; e < 8; ++e) oacc[g][e] *= a;
         }
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int key = wave * KPW + i * KPI + lane / LPR;
-            const int pos = ks + key;
-            uint4 w = vd[i];
-            if (pos == L) w = *reinterpret_cast<const uint4 *>(vnew_lds + 8 * sub);
+        for (int i = 0; i < NV; ++i) {
+            const int key = i * KPI + vrow;   // within the wave's block
+            const uint4 vn = *reinterpret_cast<const uint4 *>(vnew_lds + 8 * vsub);
+            const uint4 w = pick(ks + wave * KPW + key == L, vn, vd[i]);
             const uint32_t u[4] = {w.x, w.y, w.z, w.w};
             float vf[8];
 #pragma unroll
@@ -282,15 +322,25 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             }
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                const float pg = g < G ? s_lds[g][key] : 0.f;
+                const float pg = p_lds[wave][g][key];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) oacc[g][e] = fmaf(pg, vf[e], oacc[g][e]);
             }
         }
-        __syncthreads();   // s_lds is rewritten by the next pass
+    };
+    for (int s = 0; s < NSUB; s += 3) {
+        if (!valid(s)) break;
+        if (valid(s + 2)) issue(s + 2, kd2, vd2);
+        pass(s, kd0, vd0);
+        if (!valid(s + 1)) break;
+        if (valid(s + 3)) issue(s + 3, kd0, vd0);
+        pass(s + 1, kd1, vd1);
+        if (!valid(s + 2)) break;
+        if (valid(s + 4)) issue(s + 4, kd1, vd1);
+        pass(s + 2, kd2, vd2);
     }
 
-    // ---- the range's partial state: O summed over lane groups and waves ----
+    // ---- the range's partial state: the four waves' states merged ----
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
@@ -308,15 +358,28 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             dst[1] = make_float4(oacc[g][4], oacc[g][5], oacc[g][6], oacc[g][7]);
         }
     }
+    if (kq == 0 && kl < GT) {
+        ml_lds[wave][0][kl] = m_run;
+        ml_lds[wave][1][kl] = l_run;
+    }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, d = idx % D;
-        const float v = (o_lds[0][g][d] + o_lds[1][g][d]) + (o_lds[2][g][d] + o_lds[3][g][d]);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][0][g]);   // finite: wave 0 sees key k0
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = __builtin_amdgcn_exp2f(ml_lds[w][0][g] - M);   // 0 for a wave with no visible key
+            o = fmaf(o_lds[w][g][d], f, o);
+            l = fmaf(ml_lds[w][1][g], f, l);
+        }
         float *dst = p.part + (((int64_t)b * p.H + kvh * G + g) * p.n_chunks + c) * (D + 2);
-        dst[2 + d] = v;
+        dst[2 + d] = o;
         if (d == 0) {
-            dst[0] = m_run[g];
-            dst[1] = l_run[g];
+            dst[0] = M;
+            dst[1] = l;
         }
     }
 }
