@@ -217,10 +217,16 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
  *   head_dim    64 or 128;  layout ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16.
  *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
  *   workspace   device scratch of at least rope_decode_workspace_size()
- *               bytes, 16-byte aligned, contents irrelevant: fp32 partial
- *               states of ranges of cached positions, merged by a second
- *               kernel enqueued right after on the same stream.  Calls that
- *               share a workspace must not run concurrently.
+ *               bytes, 16-byte aligned, contents irrelevant: the fp32
+ *               partial states of the pieces each (request, key/value head)
+ *               is cut into (the cache passes are shared out evenly over a
+ *               fixed set of workgroups) and a table of where they lie,
+ *               merged by a second kernel enqueued right after on the same
+ *               stream.  Calls that share a workspace must not run
+ *               concurrently.
+ * Shapes past 2^31 - 1 passes of 64 cached positions over all (request,
+ * key/value head) pairs, i.e. B * H_kv * (S_max / 64 + 1), are rejected with
+ * ROPE_ERR_SHAPE.
  * Requires 16-byte-aligned q, k_new, v_new, caches, o (else ROPE_ERR_ALIGN).
  */
 int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
@@ -232,8 +238,10 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
 
 /*
  * rope_decode_workspace_size -- bytes of workspace rope_decode_attn_fwd needs
- * for these shapes, or minus a status code for shapes it would reject.
- * Makes no device allocation.
+ * for these shapes, or minus a status code for shapes it would reject:
+ * (B * H_kv + 1024) * (H / H_kv) * (head_dim + 2) * 4 rounded up to a
+ * multiple of 256, plus B * H_kv * 8; the same on every device, independent
+ * of S_max.  Makes no device allocation and no HIP call.
  */
 int64_t rope_decode_workspace_size(int B, int H, int H_kv, int64_t S_max, int head_dim);
 

@@ -193,14 +193,10 @@ int check_decode_shape(int B, int H, int H_kv, int64_t S_max, int head_dim)
     if (head_dim < 2 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return ROPE_ERR_UNSUPPORTED;
     if (H / H_kv > 8) return ROPE_ERR_UNSUPPORTED;
-    const int64_t ranges = rope_decode_ranges(S_max);
-    if ((int64_t)B * H_kv * ranges > kMaxGrid || (int64_t)B * H > kMaxGrid) return ROPE_ERR_SHAPE;
+    // pass counts are 32-bit on the device; one merge workgroup per (request, head)
+    if (rope_decode_max_passes(B, H_kv, S_max) > 2147483647 || (int64_t)B * H > kMaxGrid)
+        return ROPE_ERR_SHAPE;
     return ROPE_OK;
-}
-
-int64_t decode_workspace_bytes(int B, int H, int64_t S_max, int head_dim)
-{
-    return (int64_t)B * H * rope_decode_ranges(S_max) * (head_dim + 2) * 4;
 }
 
 }  // namespace
@@ -209,7 +205,7 @@ int64_t rope_decode_workspace_size(int B, int H, int H_kv, int64_t S_max, int he
 {
     const int st = check_decode_shape(B, H, H_kv, S_max, head_dim);
     if (st != ROPE_OK) return -st;
-    return decode_workspace_bytes(B, H, S_max, head_dim);
+    return rope_decode_workspace_bytes(B, H, H_kv, head_dim);
 }
 
 int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
@@ -230,7 +226,7 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
     if (rot_dim > 0 && table_rows < 1) return ROPE_ERR_TABLE_RANGE;
     if (o == q || o == k_new || o == v_new || o == k_cache || o == v_cache) return ROPE_ERR_SHAPE;
-    if (workspace_bytes < decode_workspace_bytes(B, H, S_max, head_dim)) return ROPE_ERR_SHAPE;
+    if (workspace_bytes < rope_decode_workspace_bytes(B, H, H_kv, head_dim)) return ROPE_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
         !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(workspace, 16) || !aligned(cache_lens, 4))
         return ROPE_ERR_ALIGN;

@@ -92,5 +92,11 @@ struct DecodeArgs {
     void *workspace;                 // rope_decode_workspace_bytes() bytes
 };
 int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
-// Cached-position ranges per (request, key/value head): one workgroup each.
-int64_t rope_decode_ranges(int64_t S_max);
+// Workspace bytes of one decode step (any device).
+int64_t rope_decode_workspace_bytes(int B, int H, int H_kv, int head_dim);
+// Passes of 64 cached positions the step may walk: an upper bound the host
+// checks so that device-side pass counts fit in 32 bits.
+int64_t rope_decode_max_passes(int B, int H_kv, int64_t S_max);
+
+// Compute units of the current device (cached per device; 0 on error).
+int rope_device_cu_count();

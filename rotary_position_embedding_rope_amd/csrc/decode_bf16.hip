@@ -10,14 +10,18 @@
 // rotation inside the attention launch).
 //
 // The work is bound by reading the cache once, so the kernel is laid out for
-// HBM streaming: a workgroup takes one request, one key/value head and a
-// contiguous range of CW cached positions for all G query heads that share
-// the key/value head, and reads each 16-byte chunk of K and V once with
-// coalesced buffer loads, two passes ahead of the one being computed.
-// Scores come from the matrix cores, P V from the vector ALU in fp32.
-// Ranges of one (request, key/value head) are combined by a second kernel
-// (running max and sum rescaling, the merge rule of section 5 of the same
-// page).
+// HBM streaming.  The cached positions of every (request, key/value head)
+// slice are cut into passes of 64 keys; the passes of all slices, in slice
+// order, are split into equal contiguous runs, one per workgroup of a grid
+// sized to the machine (stream-K style), so every workgroup moves the same
+// number of bytes whatever the mix of lengths, and its loads stay two passes
+// ahead of its arithmetic across slice boundaries.  A workgroup serves all G
+// query heads that share the slice's key/value head and reads each 16-byte
+// chunk of K and V once, with coalesced buffer loads.  Scores come from the
+// matrix cores, P V from the vector ALU in fp32.  Each workgroup leaves one
+// partial state per slice it touched; a second kernel combines the partial
+// states of a slice (running max and sum rescaling, the merge rule of
+// section 5 of the same page).
 #include "common.hpp"
 
 namespace {
@@ -28,9 +32,9 @@ using rope::f32_to_bf16;
 using rope::f32x4_t;
 
 constexpr int SUB = 64;           // keys per pass of the workgroup
-constexpr int NSUB = 8;           // passes per workgroup
-constexpr int CW = SUB * NSUB;    // cached positions per workgroup
 constexpr int GMAX = 8;           // query heads per key/value head, at most
+constexpr int WG_PER_CU = 2;      // resident workgroups per compute unit (<= 256 registers)
+constexpr int NW_MAX = 1024;      // chunk workgroups at most (the workspace is sized for it)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int RSRC_FLAGS = 0x00020000;   // untyped 32-bit buffer (gfx9 family)
@@ -43,12 +47,29 @@ struct DecodeParams {
     uint16_t *v_cache;          // [B, Hkv, S_max, D]
     const int32_t *lens;        // [B]
     const float *cos_tab, *sin_tab;   // [table_rows, rot_dim / 2]
-    float *part;                // [B * H][n_chunks][D + 2]: m, l, O (unnormalised)
+    float *part;                // [B * Hkv + nw][G][D + 2]: m, l, O (unnormalised)
+    int2 *seg;                  // [B * Hkv]: first workgroup and number of pieces
     uint16_t *o;                // [B, H, D]
     int64_t table_rows, S_max;
-    int B, H, Hkv, G, rot_dim, n_chunks;
+    int B, H, Hkv, G, rot_dim, nw;
     float sl2;                  // softmax scale * log2(e)
 };
+
+// Passes of request with cached length L: the L + 1 keys the new query sees,
+// 64 at a time; none for a length outside the cache (or the table).
+template <bool ROT>
+__device__ __forceinline__ int passes_of(const DecodeParams &p, int L)
+{
+    if (L < 0 || (int64_t)L >= p.S_max || (ROT && (int64_t)L >= p.table_rows)) return 0;
+    return L / SUB + 1;
+}
+
+// Workgroup w of nw owns global passes [w P / nw, (w + 1) P / nw); the one
+// that owns pass x is the largest w with w P / nw <= x.
+__device__ __forceinline__ int owner_of(int64_t x, int64_t P, int nw)
+{
+    return (int)(((x + 1) * nw - 1) / P);
+}
 
 // A buffer resource over `rows` rows of ROW_BYTES from base: loads past them
 // (and with rows <= 0, all loads) return zeros and touch no memory.
@@ -98,37 +119,24 @@ __device__ __forceinline__ uint4 pick(bool c, uint4 a, uint4 b)
     return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
-// Sum over groups of W consecutive lanes (W a power of two up to 64): every
-// lane of a group ends with the group's sum.
-template <int W>
-__device__ __forceinline__ float group_sum(float x)
-{
-#pragma unroll
-    for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m);
-    return x;
-}
-template <int W>
-__device__ __forceinline__ float group_max(float x)
-{
-#pragma unroll
-    for (int m = 1; m < W; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
-// One workgroup: request b, key/value head kvh, cached positions
-// [c CW, (c + 1) CW) of the L + 1 keys the new query sees (the last one is the
-// new key, taken from LDS and, by the workgroup whose range holds it,
-// appended to the cache).  GT: G rounded up to a power of two.
+// A run of passes.  The workgroup walks its passes in order with two cursors
+// (one for the loads, two passes ahead, one for the arithmetic); a slice's
+// passes inside the run form a piece, computed with the slice's rotated
+// queries and finished by writing the piece's partial state to slot
+// slice + w.  These slots are distinct: a workgroup touches each slice at most
+// once and later slices only through later workgroups.  The workgroup that
+// owns a slice's first pass records where its pieces lie; the one that owns
+// its last pass (the pass holding position L) rotates and appends the new key
+// and value.  GT: G rounded up to a power of two.
 //
 // A pass takes SUB keys, 16 per wave.  Scores come from the matrix cores:
 // S (16 keys x 16 query slots) = K Q'^T over D/32 steps of
 // v_mfma_f32_16x16x32_bf16, K straight from the loads in the A-operand
 // layout (lane l: key l%16, dims 8(l/16) .. +7 of each 32-dim step), Q'
 // (rotated, scaled, rounded to bf16) as the B operand, query slots past G
-// zero.  P V runs on the vector ALU, each key row split over D/8 lanes.  The
-// loads of passes s+1 and s+2 are in flight while pass s is computed.  Each
+// zero.  P V runs on the vector ALU, each key row split over D/8 lanes.  Each
 // wave runs its own online softmax over its keys; the four waves are merged
-// once at the end.
+// once per piece.
 template <int D, int LAYOUT, bool ROT, int GT>
 __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 {
@@ -147,29 +155,95 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
     __shared__ __attribute__((aligned(16))) uint16_t knew_lds[D];  // new key, rotated, bf16
     __shared__ __attribute__((aligned(16))) uint16_t vnew_lds[D];
     __shared__ __attribute__((aligned(16))) float o_lds[4][GT][D];
+    __shared__ int red_lds[4];
+    __shared__ int found_lds[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = blockIdx.x % p.n_chunks;
-    const int bk = blockIdx.x / p.n_chunks;   // b * Hkv + kvh
-    const int b = bk / p.Hkv, kvh = bk % p.Hkv;
+    const int w = blockIdx.x;
     const int G = p.G;
-    const int L = p.lens[b];
-    // a length outside the cache (or the table) leaves the request to the
-    // merge kernel, which writes NaN rows; nothing is read or written here
-    if (L < 0 || (int64_t)L >= p.S_max || (ROT && (int64_t)L >= p.table_rows)) return;
-    const int n = L + 1;                      // visible keys, the new one included
-    const int k0 = c * CW;
-    if (k0 >= n) return;
 
-    // ---- loads of one pass (issued early) ----
-    const int64_t slice = (int64_t)bk * p.S_max;   // row of (b, kvh, position 0)
+    // ---- the run: total passes, then the slice holding the first one ----
+    int mine = 0;
+    for (int b = tid; b < p.B; b += 256) mine += passes_of<ROT>(p, p.lens[b]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mine += __shfl_xor(mine, m);
+    if (lane == 0) red_lds[wave] = mine;
+    if (tid == 0) found_lds[0] = -1;
+    __syncthreads();
+    const int64_t P = (int64_t)p.Hkv *
+                      __builtin_amdgcn_readfirstlane(red_lds[0] + red_lds[1] + red_lds[2] + red_lds[3]);
+    // with fewer passes than workgroups only the first P take part, so every
+    // run is non-empty and a slice's pieces lie in consecutive workgroups
+    const int nw = P < p.nw ? (int)P : p.nw;
+    if (w >= nw) return;
+    const int64_t lo = (int64_t)w * P / nw, hi = (int64_t)(w + 1) * P / nw;
+    if (wave == 0) {
+        // request b covers global passes [Hkv pre(b), Hkv pre(b + 1)), pre = passes before b
+        int64_t base = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int b = b0 + lane;
+            const int np = b < p.B ? passes_of<ROT>(p, p.lens[b]) : 0;
+            int inc = np;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const int y = __shfl_up(inc, m);
+                if (lane >= m) inc += y;
+            }
+            const int64_t start = base + (int64_t)p.Hkv * (inc - np);
+            const bool hit = np > 0 && lo >= start && lo < start + (int64_t)p.Hkv * np;
+            const uint64_t bal = __ballot(hit);
+            if (bal) {
+                if (hit) {
+                    found_lds[0] = b;
+                    found_lds[1] = (int)(lo - start);   // < Hkv * np: fits
+                }
+                break;
+            }
+            base += (int64_t)p.Hkv * __shfl(inc, 63);
+        }
+    }
+    __syncthreads();
+
+    struct Cursor {
+        int b, kvh, s, np, L;   // request, key/value head, pass in the slice, passes, length
+        int64_t pstart;         // global index of the slice's first pass
+    };
+    Cursor c0;
+    c0.b = __builtin_amdgcn_readfirstlane(found_lds[0]);
+    if (c0.b < 0) return;   // not reached: lo < P lies in some request
+    {
+        const int off = __builtin_amdgcn_readfirstlane(found_lds[1]);
+        c0.L = p.lens[c0.b];
+        c0.np = passes_of<ROT>(p, c0.L);
+        if (c0.np <= 0) return;   // not reached either
+        c0.kvh = off / c0.np;
+        c0.s = off % c0.np;
+        c0.pstart = lo - c0.s;
+    }
+    // the next pass in slice order (only called while one exists)
+    auto advance = [&](Cursor &c) {
+        if (++c.s < c.np) return;
+        c.pstart += c.np;
+        c.s = 0;
+        if (++c.kvh < p.Hkv) return;
+        c.kvh = 0;
+        while (c.b + 1 < p.B) {
+            ++c.b;
+            c.L = p.lens[c.b];
+            c.np = passes_of<ROT>(p, c.L);
+            if (c.np > 0) break;
+        }
+    };
+
+    // ---- loads of one pass (issued two passes early) ----
     const int kl = lane % 16, kq = lane / 16;      // score layout: key, dim quarter
     const int vrow = lane / LPR, vsub = lane % LPR; // value layout: row, 16-byte chunk
-    auto issue = [&](int s, uint4 (&kd)[NT], uint4 (&vd)[NV]) {
-        const int ks = k0 + s * SUB;
+    auto issue = [&](const Cursor &c, uint4 (&kd)[NT], uint4 (&vd)[NV]) {
+        const int ks = c.s * SUB;
+        const int64_t slice = ((int64_t)c.b * p.Hkv + c.kvh) * p.S_max;
         // cached rows [ks, min(L, ks + SUB)); the row at L reads as zero here
-        const int rows = L - ks < SUB ? L - ks : SUB;
+        const int rows = c.L - ks < SUB ? c.L - ks : SUB;
         const rsrc_t krs = make_rsrc<2 * D>(p.k_cache + (slice + ks) * D, rows);
         const rsrc_t vrs = make_rsrc<2 * D>(p.v_cache + (slice + ks) * D, rows);
         const int kkey = wave * KPW + kl;
@@ -181,82 +255,84 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             vd[i] = bload16(vrs, 2 * (key * D + 8 * vsub));
         }
     };
-    // three register sets: the loads of passes s+1 and s+2 are in flight
-    // while pass s is computed
-    uint4 kd0[NT], vd0[NV], kd1[NT], vd1[NV], kd2[NT], vd2[NV];
-    auto valid = [&](int s) { return s < NSUB && k0 + s * SUB < n; };
-    issue(0, kd0, vd0);
-    if (valid(1)) issue(1, kd1, vd1);
 
-    // ---- the new query rows and key at position L ----
-    const int rh = p.rot_dim / 2;
-    const float *crow = ROT ? p.cos_tab + (int64_t)L * rh : nullptr;
-    const float *srow = ROT ? p.sin_tab + (int64_t)L * rh : nullptr;
-    for (int idx = tid; idx < G * (D / 2); idx += 256) {
-        const int g = idx / (D / 2), i = idx % (D / 2);
-        int da, db;
-        pair_dims<LAYOUT>(i, ROT ? p.rot_dim : 0, da, db);
-        const uint16_t *qr = p.q + ((int64_t)b * p.H + kvh * G + g) * D;
-        const float xa = bf16_to_f32(qr[da]), xb = bf16_to_f32(qr[db]);
-        float ya = xa, yb = xb;
-        if (ROT && i < rh) {
-            const float cs = crow[i], sn = srow[i];
-            ya = xa * cs - xb * sn;
-            yb = xa * sn + xb * cs;
-        }
-        q_lds[g][da] = ya * p.sl2;
-        q_lds[g][db] = yb * p.sl2;
-    }
-    for (int idx = G * D + tid; idx < GT * D; idx += 256) q_lds[idx / D][idx % D] = 0.f;
-    const bool last = n - k0 <= CW;           // this range holds position L
-    if (last) {
-        const int64_t crow_off = (slice + L) * D;
-        for (int i = tid; i < D / 2; i += 256) {
+    bf16x8_t qb[NT];
+    float oacc[GT][8];
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // ---- start of a piece: the slice's queries (and new key) at position L ----
+    auto setup = [&](const Cursor &c) {
+        __syncthreads();   // the previous piece is done with the LDS
+        const int rh = p.rot_dim / 2;
+        const int L = c.L;
+        const int bk = c.b * p.Hkv + c.kvh;
+        const float *crow = ROT ? p.cos_tab + (int64_t)L * rh : nullptr;
+        const float *srow = ROT ? p.sin_tab + (int64_t)L * rh : nullptr;
+        for (int idx = tid; idx < G * (D / 2); idx += 256) {
+            const int g = idx / (D / 2), i = idx % (D / 2);
             int da, db;
             pair_dims<LAYOUT>(i, ROT ? p.rot_dim : 0, da, db);
-            const uint16_t *kr = p.k_new + (int64_t)bk * D;
-            const float xa = bf16_to_f32(kr[da]), xb = bf16_to_f32(kr[db]);
+            const uint16_t *qr = p.q + ((int64_t)c.b * p.H + c.kvh * G + g) * D;
+            const float xa = bf16_to_f32(qr[da]), xb = bf16_to_f32(qr[db]);
             float ya = xa, yb = xb;
             if (ROT && i < rh) {
                 const float cs = crow[i], sn = srow[i];
                 ya = xa * cs - xb * sn;
                 yb = xa * sn + xb * cs;
             }
-            const uint16_t ba = f32_to_bf16(ya), bb = f32_to_bf16(yb);
-            knew_lds[da] = ba;
-            knew_lds[db] = bb;
-            p.k_cache[crow_off + da] = ba;
-            p.k_cache[crow_off + db] = bb;
+            q_lds[g][da] = ya * p.sl2;
+            q_lds[g][db] = yb * p.sl2;
         }
-        for (int d = tid; d < D; d += 256) {
-            const uint16_t v = p.v_new[(int64_t)bk * D + d];
-            vnew_lds[d] = v;
-            p.v_cache[crow_off + d] = v;
+        for (int idx = G * D + tid; idx < GT * D; idx += 256) q_lds[idx / D][idx % D] = 0.f;
+        if (c.pstart + c.np - 1 < hi) {   // this run holds the slice's last pass
+            const int64_t crow_off = ((int64_t)bk * p.S_max + L) * D;
+            for (int i = tid; i < D / 2; i += 256) {
+                int da, db;
+                pair_dims<LAYOUT>(i, ROT ? p.rot_dim : 0, da, db);
+                const uint16_t *kr = p.k_new + (int64_t)bk * D;
+                const float xa = bf16_to_f32(kr[da]), xb = bf16_to_f32(kr[db]);
+                float ya = xa, yb = xb;
+                if (ROT && i < rh) {
+                    const float cs = crow[i], sn = srow[i];
+                    ya = xa * cs - xb * sn;
+                    yb = xa * sn + xb * cs;
+                }
+                const uint16_t ba = f32_to_bf16(ya), bb = f32_to_bf16(yb);
+                knew_lds[da] = ba;
+                knew_lds[db] = bb;
+                p.k_cache[crow_off + da] = ba;
+                p.k_cache[crow_off + db] = bb;
+            }
+            for (int d = tid; d < D; d += 256) {
+                const uint16_t v = p.v_new[(int64_t)bk * D + d];
+                vnew_lds[d] = v;
+                p.v_cache[crow_off + d] = v;
+            }
         }
-    }
-    __syncthreads();
-
-    // Q' as the B operand: lane l holds query slot l%16, dims 32t + 8(l/16) + j
-    bf16x8_t qb[NT];
+        if (c.s == 0 && tid == 0)   // this run holds the slice's first pass
+            p.seg[bk] = make_int2(w, owner_of(c.pstart + c.np - 1, P, nw) - w + 1);
+        __syncthreads();
+        // Q' as the B operand: lane l holds query slot l%16, dims 32t + 8(l/16) + j
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            qb[t][jj] = (__bf16)(kl < GT ? q_lds[kl][32 * t + 8 * kq + jj] : 0.f);
-    }
-
-    float oacc[GT][8];
+            for (int jj = 0; jj < 8; ++jj)
+                qb[t][jj] = (__bf16)(kl < GT ? q_lds[kl][32 * t + 8 * kq + jj] : 0.f);
+        }
 #pragma unroll
-    for (int g = 0; g < GT; ++g)
+        for (int g = 0; g < GT; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[g][e] = 0.f;
+            for (int e = 0; e < 8; ++e) oacc[g][e] = 0.f;
+        m_run = -INFINITY;
+        l_run = 0.f;
+    };
 
     // Each wave keeps its own running max and sum over its keys, for query
     // slot kl in lanes kl, kl+16, kl+32, kl+48 (MFMA layout); the waves'
-    // states are merged once, at the end, so the passes need no barrier.
-    float m_run = -INFINITY, l_run = 0.f;
-    auto pass = [&](int s, const uint4 (&kd)[NT], const uint4 (&vd)[NV]) {
-        const int ks = k0 + s * SUB;
+    // states are merged once per piece, so the passes need no barrier.
+    auto pass = [&](const Cursor &c, const uint4 (&kd)[NT], const uint4 (&vd)[NV]) {
+        const int ks = c.s * SUB;
+        const int L = c.L, n = L + 1;
         // scores of the wave's 16 keys for all query slots
         const int kpos = ks + wave * KPW + kl;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -266,8 +342,8 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             // the new key's chunk is read every time and picked by value (a
             // conditional pointer would send the loaded rows through memory)
             const uint4 kn = *reinterpret_cast<const uint4 *>(knew_lds + 32 * t + 8 * kq);
-            const uint4 w = pick(knew, kn, kd[t]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qb[t], acc,
+            const uint4 wv = pick(knew, kn, kd[t]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv), qb[t], acc,
                                                           0, 0, 0);
         }
         // accumulator element r of lane l: key 4(l/16) + r of the block, query slot l%16
@@ -312,8 +388,8 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
         for (int i = 0; i < NV; ++i) {
             const int key = i * KPI + vrow;   // within the wave's block
             const uint4 vn = *reinterpret_cast<const uint4 *>(vnew_lds + 8 * vsub);
-            const uint4 w = pick(ks + wave * KPW + key == L, vn, vd[i]);
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            const uint4 wv = pick(ks + wave * KPW + key == L, vn, vd[i]);
+            const uint32_t u[4] = {wv.x, wv.y, wv.z, wv.w};
             float vf[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -328,71 +404,108 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             }
         }
     };
-    for (int s = 0; s < NSUB; s += 3) {
-        if (!valid(s)) break;
-        if (valid(s + 2)) issue(s + 2, kd2, vd2);
-        pass(s, kd0, vd0);
-        if (!valid(s + 1)) break;
-        if (valid(s + 3)) issue(s + 3, kd0, vd0);
-        pass(s + 1, kd1, vd1);
-        if (!valid(s + 2)) break;
-        if (valid(s + 4)) issue(s + 4, kd1, vd1);
-        pass(s + 2, kd2, vd2);
-    }
 
-    // ---- the range's partial state: the four waves' states merged ----
+    // ---- end of a piece: the four waves' states merged into slot slice + w ----
+    auto finish = [&](const Cursor &c) {
 #pragma unroll
-    for (int g = 0; g < GT; ++g)
+        for (int g = 0; g < GT; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = oacc[g][e];
+            for (int e = 0; e < 8; ++e) {
+                float x = oacc[g][e];
 #pragma unroll
-            for (int m = LPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
-            oacc[g][e] = x;
+                for (int m = LPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
+                oacc[g][e] = x;
+            }
+        if (lane < LPR) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                float4 *dst = reinterpret_cast<float4 *>(&o_lds[wave][g][8 * lane]);
+                dst[0] = make_float4(oacc[g][0], oacc[g][1], oacc[g][2], oacc[g][3]);
+                dst[1] = make_float4(oacc[g][4], oacc[g][5], oacc[g][6], oacc[g][7]);
+            }
         }
-    if (lane < LPR) {
-#pragma unroll
-        for (int g = 0; g < GT; ++g) {
-            float4 *dst = reinterpret_cast<float4 *>(&o_lds[wave][g][8 * lane]);
-            dst[0] = make_float4(oacc[g][0], oacc[g][1], oacc[g][2], oacc[g][3]);
-            dst[1] = make_float4(oacc[g][4], oacc[g][5], oacc[g][6], oacc[g][7]);
+        if (kq == 0 && kl < GT) {
+            ml_lds[wave][0][kl] = m_run;
+            ml_lds[wave][1][kl] = l_run;
         }
+        __syncthreads();
+        const int64_t slot = (int64_t)c.b * p.Hkv + c.kvh + w;
+        for (int idx = tid; idx < G * D; idx += 256) {
+            const int g = idx / D, d = idx % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_lds[v][0][g]);   // finite: wave 0's first key is visible
+            float o = 0.f, l = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float f = __builtin_amdgcn_exp2f(ml_lds[v][0][g] - M);   // 0 for a wave with no visible key
+                o = fmaf(o_lds[v][g][d], f, o);
+                l = fmaf(ml_lds[v][1][g], f, l);
+            }
+            float *dst = p.part + (slot * G + g) * (D + 2);
+            dst[2 + d] = o;
+            if (d == 0) {
+                dst[0] = M;
+                dst[1] = l;
+            }
+        }
+    };
+
+    const int npass = (int)(hi - lo);
+    auto step = [&](int t, Cursor &c, const uint4 (&kd)[NT], const uint4 (&vd)[NV]) {
+        if (t == 0 || c.s == 0) setup(c);
+        pass(c, kd, vd);
+        if (t == npass - 1 || c.s == c.np - 1) finish(c);
+        if (t + 1 < npass) advance(c);
+    };
+
+    // three register sets: the loads of passes t+1 and t+2 are in flight
+    // while pass t is computed
+    uint4 kd0[NT], vd0[NV], kd1[NT], vd1[NV], kd2[NT], vd2[NV];
+    Cursor ci = c0, cc = c0;
+    issue(ci, kd0, vd0);
+    if (npass > 1) {
+        advance(ci);
+        issue(ci, kd1, vd1);
     }
-    if (kq == 0 && kl < GT) {
-        ml_lds[wave][0][kl] = m_run;
-        ml_lds[wave][1][kl] = l_run;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int g = idx / D, d = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][0][g]);   // finite: wave 0 sees key k0
-        float o = 0.f, l = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = __builtin_amdgcn_exp2f(ml_lds[w][0][g] - M);   // 0 for a wave with no visible key
-            o = fmaf(o_lds[w][g][d], f, o);
-            l = fmaf(ml_lds[w][1][g], f, l);
+    for (int t = 0; t < npass; t += 3) {
+        if (t + 2 < npass) {
+            advance(ci);
+            issue(ci, kd2, vd2);
         }
-        float *dst = p.part + (((int64_t)b * p.H + kvh * G + g) * p.n_chunks + c) * (D + 2);
-        dst[2 + d] = o;
-        if (d == 0) {
-            dst[0] = M;
-            dst[1] = l;
+        step(t, cc, kd0, vd0);
+        if (t + 1 >= npass) break;
+        if (t + 3 < npass) {
+            advance(ci);
+            issue(ci, kd0, vd0);
         }
+        step(t + 1, cc, kd1, vd1);
+        if (t + 2 >= npass) break;
+        if (t + 4 < npass) {
+            advance(ci);
+            issue(ci, kd1, vd1);
+        }
+        step(t + 2, cc, kd2, vd2);
     }
 }
 
-// Output row (b, h): the ranges' partial states merged (maxima aligned, sums
-// and rows rescaled), O / l rounded to bf16.  A request whose length lies
-// outside the cache or the table gets a row of NaN.
+// Output row (b, h): the partial states of the pieces of its slice merged
+// (maxima aligned, sums and rows rescaled), O / l rounded to bf16.  A request
+// whose length lies outside the cache or the table gets a row of NaN.
+//
+// D/2 lanes take one piece (two dims each, 8-byte loads), so 256 threads read
+// RP = 512/D pieces at a time; each thread walks its pieces U at a time with
+// all U loads issued before any is used, keeping a running (max, sum, row)
+// that it rescales whenever a larger piece maximum arrives.  The RP running
+// states are then merged through LDS by the same rule.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int rot)
 {
-    constexpr int CL = 256 / D;   // ranges summed in parallel per dim
-    __shared__ float red[256];
-    __shared__ float mx;
+    constexpr int LR = D / 2;        // lanes per piece
+    constexpr int RP = 256 / LR;     // pieces read at a time
+    constexpr int U = 8;             // pieces per thread in flight
+    __shared__ float2 red_o[RP][LR];
+    __shared__ float red_m[RP], red_l[RP];
     const int bh = blockIdx.x, b = bh / p.H, tid = threadIdx.x;
     const int L = p.lens[b];
     uint16_t *orow = p.o + (int64_t)bh * D;
@@ -400,80 +513,115 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int r
         for (int d = tid; d < D; d += 256) orow[d] = 0x7fc0;   // bf16 quiet NaN
         return;
     }
-    const int nc = (L + 1 + CW - 1) / CW;
-    const float *part = p.part + (int64_t)bh * p.n_chunks * (D + 2);
-    // largest range maximum
-    float m = -INFINITY;
-    for (int c = tid; c < nc; c += 256) m = fmaxf(m, part[(int64_t)c * (D + 2)]);
-    red[tid] = m;
-    __syncthreads();
-    if (tid < 64) {
-        float x = fmaxf(fmaxf(red[tid], red[tid + 64]), fmaxf(red[tid + 128], red[tid + 192]));
-        x = group_max<64>(x);
-        if (tid == 0) mx = x;
-    }
-    __syncthreads();
-    const float M = mx;
-    // thread (d, j) sums dim d over ranges j, j + CL, ...; the sums l ride along
-    const int d = tid % D, j = tid / D;
-    float acc = 0.f, lsum = 0.f;
-    for (int c = j; c < nc; c += CL) {
-        const float *pc = part + (int64_t)c * (D + 2);
-        const float w = __builtin_amdgcn_exp2f(pc[0] - M);
-        acc = fmaf(pc[2 + d], w, acc);
-        lsum = fmaf(pc[1], w, lsum);
-    }
-    __syncthreads();
-    red[tid] = acc;
-    __syncthreads();
-    if (j == 0) {
-        float o = 0.f;
+    const int h = bh % p.H, sl = b * p.Hkv + h / p.G;
+    const int2 sg = p.seg[sl];   // first workgroup, pieces (>= 1, each with a finite max)
+    const int nc = sg.y;
+    const float *part = p.part + (((int64_t)sl + sg.x) * p.G + h % p.G) * (D + 2);
+    const int64_t pstride = (int64_t)p.G * (D + 2);   // from one piece to the next
+    const int r0 = tid / LR, d2 = tid % LR;
+    float M = -INFINITY, l = 0.f;
+    float2 acc = make_float2(0.f, 0.f);
+    for (int c0 = r0; c0 < nc; c0 += RP * U) {
+        float mc[U], lc[U];
+        float2 oc[U];
 #pragma unroll
-        for (int jj = 0; jj < CL; ++jj) o += red[jj * D + d];
-        acc = o;
+        for (int u = 0; u < U; ++u) {
+            // pieces past nc re-read the last one and are given no weight
+            const int c = c0 + u * RP < nc ? c0 + u * RP : nc - 1;
+            const float *pc = part + c * pstride;
+            mc[u] = pc[0];
+            lc[u] = pc[1];
+            oc[u] = *reinterpret_cast<const float2 *>(pc + 2 + 2 * d2);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + u * RP >= nc) break;
+            const float mn = fmaxf(M, mc[u]);
+            const float a = __builtin_amdgcn_exp2f(M - mn);   // 0 while M is -inf
+            const float w = __builtin_amdgcn_exp2f(mc[u] - mn);
+            acc.x = fmaf(oc[u].x, w, acc.x * a);
+            acc.y = fmaf(oc[u].y, w, acc.y * a);
+            l = fmaf(lc[u], w, l * a);
+            M = mn;
+        }
+    }
+    red_o[r0][d2] = acc;
+    if (d2 == 0) {
+        red_m[r0] = M;
+        red_l[r0] = l;
     }
     __syncthreads();
-    red[tid] = lsum;   // the same l sum in every dim lane of range group j
-    __syncthreads();
-    if (j == 0) {
-        float l = 0.f;
+    if (tid < LR) {
+        float Mx = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < CL; ++jj) l += red[jj * D];
-        orow[d] = f32_to_bf16(acc / l);
+        for (int r = 0; r < RP; ++r) Mx = fmaxf(Mx, red_m[r]);   // finite: piece 0 is read by r0 = 0
+        float ox = 0.f, oy = 0.f, ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            const float f = __builtin_amdgcn_exp2f(red_m[r] - Mx);   // 0 for a group with no piece
+            ox = fmaf(red_o[r][tid].x, f, ox);
+            oy = fmaf(red_o[r][tid].y, f, oy);
+            ls = fmaf(red_l[r], f, ls);
+        }
+        const uint32_t pk = (uint32_t)f32_to_bf16(ox / ls) | ((uint32_t)f32_to_bf16(oy / ls) << 16);
+        reinterpret_cast<uint32_t *>(orow)[tid] = pk;
     }
 }
 
 template <int D, int LAYOUT, bool ROT>
-int launch_gt(const DecodeParams &p, unsigned grid, hipStream_t stream)
+int launch_gt(const DecodeParams &p, hipStream_t stream)
 {
+    const dim3 grid((unsigned)p.nw);
     if (p.G <= 1)
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 1>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 1>), grid, dim3(256), 0, stream, p);
     else if (p.G <= 2)
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 2>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 2>), grid, dim3(256), 0, stream, p);
     else if (p.G <= 4)
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 4>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 4>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 8>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 8>), grid, dim3(256), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 
 template <int D>
 int launch_d(const DecodeParams &p, int layout, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.n_chunks);
     int rc;
-    if (p.rot_dim == 0) rc = launch_gt<D, 0, false>(p, grid, stream);
-    else if (layout == 0) rc = launch_gt<D, 0, true>(p, grid, stream);
-    else rc = launch_gt<D, 1, true>(p, grid, stream);
+    if (p.rot_dim == 0) rc = launch_gt<D, 0, false>(p, stream);
+    else if (layout == 0) rc = launch_gt<D, 0, true>(p, stream);
+    else rc = launch_gt<D, 1, true>(p, stream);
     if (rc != ROPE_LAUNCH_OK) return rc;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p,
                        p.rot_dim);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 
+// Workgroups of the chunk kernel on the current device (0 on error).
+int decode_workgroups()
+{
+    const int n = WG_PER_CU * rope_device_cu_count();
+    return n < NW_MAX ? n : NW_MAX;
+}
+
+// Partial states for up to NW_MAX workgroups, then the piece table from a
+// 256-byte boundary.
+int64_t part_bytes(int B, int H, int H_kv, int head_dim)
+{
+    const int64_t n = ((int64_t)B * H_kv + NW_MAX) * (H / H_kv) * (head_dim + 2) * 4;
+    return (n + 255) / 256 * 256;
+}
+
 }  // namespace
 
-int64_t rope_decode_ranges(int64_t S_max) { return (S_max + CW - 1) / CW; }
+int64_t rope_decode_max_passes(int B, int H_kv, int64_t S_max)
+{
+    return (int64_t)B * H_kv * (S_max / SUB + 1);
+}
+
+int64_t rope_decode_workspace_bytes(int B, int H, int H_kv, int head_dim)
+{
+    return part_bytes(B, H, H_kv, head_dim) + (int64_t)B * H_kv * 8;
+}
 
 int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream)
 {
@@ -486,7 +634,11 @@ int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream)
     p.lens = a.cache_lens;
     p.cos_tab = a.cos_tab;
     p.sin_tab = a.sin_tab;
+    p.nw = decode_workgroups();
+    if (p.nw <= 0) return ROPE_LAUNCH_ERR;
     p.part = static_cast<float *>(a.workspace);
+    p.seg = reinterpret_cast<int2 *>(static_cast<char *>(a.workspace) +
+                                     part_bytes(a.B, a.H, a.H_kv, a.head_dim));
     p.o = static_cast<uint16_t *>(a.o);
     p.table_rows = a.table_rows;
     p.S_max = a.S_max;
@@ -495,7 +647,6 @@ int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream)
     p.Hkv = a.H_kv;
     p.G = a.H / a.H_kv;
     p.rot_dim = a.rot_dim;
-    p.n_chunks = (int)rope_decode_ranges(a.S_max);
     p.sl2 = a.scale * 1.4426950408889634f;
     return a.head_dim == 64 ? launch_d<64>(p, a.layout, stream) : launch_d<128>(p, a.layout, stream);
 }

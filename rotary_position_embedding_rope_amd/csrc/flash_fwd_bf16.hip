@@ -1292,19 +1292,6 @@ template <> struct Shape<128> {
     static constexpr int NG = ROPE_FLASH_D128_NG, BN = ROPE_FLASH_D128_BN;
 };
 
-std::atomic<int> g_cu_count[64];
-
-int device_cu_count()
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = g_cu_count[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        g_cu_count[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 // Host half of the schedule: visit-law coefficients, and the balanced
 // share count (0 = one workgroup per query tile).
@@ -1334,7 +1321,7 @@ void plan(const FlashArgs &a, Params &p)
     if (!a.causal) return;
     // balance only when the largest query tile does clearly more than the
     // average and there is enough work to share
-    const int cus = device_cu_count();
+    const int cus = rope_device_cu_count();
     const int G = cus * (NG == 2 ? 1 : 2);
     const int64_t U = (int64_t)p.BH * p.u_head;
     const int64_t vmax = tile_visits(p, p.n_qtiles - 1) > tile_visits(p, 0) ? tile_visits(p, p.n_qtiles - 1)
@@ -1419,4 +1406,20 @@ int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a)
     }
     plan<128>(a, p);
     return workspace_bytes<128>(p);
+}
+
+namespace {
+std::atomic<int> g_cu_count[64];
+}  // namespace
+
+int rope_device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }

@@ -390,4 +390,36 @@ def pin_gqa_head_count_must_divide(orc):
     raise AssertionError("head counts 4 / 3 accepted")
 
 
+def pin_decode_step_forms(orc):
+    """One decoded token at cache length L: its query sits at position L and
+    sees the L cached keys and its own ([RF] sections 2 and 6: rotate the new
+    token at its cache position, keep rotated keys in the cache).  Both forms
+    the decode tests use must equal a reference built from complex-number
+    rotation and scipy's softmax, with query head h reading key/value head
+    h // (H // Hkv):
+      (a) the oracle's attention of the one query at q_off = L over the raw
+          keys 0..L, each rotated at its own position;
+      (b) the oracle's attention without rotation of the query rotated at L
+          over keys that were rotated once when they were cached."""
+    rng = np.random.default_rng(53)
+    H, Hkv, D = 4, 2, 8
+    for layout in ("gptj", "neox"):
+        for L in (0, 1, 6, 13):
+            q = rng.standard_normal((1, H, 1, D))
+            k = rng.standard_normal((1, Hkv, L + 1, D))
+            v = rng.standard_normal((1, Hkv, L + 1, D))
+            pos = np.arange(L + 1)
+            kr = rope_complex(k, pos, 100.0, D, layout)
+            qr = rope_complex(q, [L], 100.0, D, layout)
+            want = np.stack([dense_reference(qr[0, h], kr[0, h // 2], v[0, h // 2],
+                                             np.ones((1, L + 1), bool), 1 / math.sqrt(D))
+                             for h in range(H)])[None]
+            a = orc.attention(q, k, v, q_off=L, k_off=0, base=100.0, layout=layout)
+            np.testing.assert_allclose(a, want, rtol=0, atol=1e-12)
+            b = orc.attention(orc.rope(q, [L], base=100.0, layout=layout),
+                              orc.rope(k, pos, base=100.0, layout=layout), v, q_off=L, k_off=0,
+                              rot_dim=0)
+            np.testing.assert_allclose(b, want, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

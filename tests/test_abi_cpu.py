@@ -219,6 +219,8 @@ def decode_args(**over):
     (dict(rot=-2), _lib.ERR_SHAPE),
     (dict(scale=float("nan")), _lib.ERR_SHAPE),
     (dict(wsb=1024), _lib.ERR_SHAPE),              # workspace too small
+    (dict(wsb=2397183), _lib.ERR_SHAPE),           # one byte short
+    (dict(B=1 << 20, S=1 << 24, wsb=1 << 62), _lib.ERR_SHAPE),   # pass counts past 32 bits
     (dict(o=FAKE), _lib.ERR_SHAPE),                # o aliases q
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(Hkv=2), _lib.ERR_UNSUPPORTED),           # 16 query heads per key/value head
@@ -238,9 +240,15 @@ def test_decode_rejects(lib, over, want):
 
 
 def test_decode_workspace_size(lib):
-    # 16 requests x 32 heads x 64 ranges of 512 positions x (128 + 2) floats
-    assert lib.rope_decode_workspace_size(16, 32, 8, 32768, 128) == 16 * 32 * 64 * 130 * 4
-    assert lib.rope_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4
+    # partial states (m, l, D floats) for each of G query heads in B * Hkv + 1024
+    # slots, rounded up to 256 bytes, then one (workgroup, count) pair per slice
+    def want(B, H, Hkv, D):
+        n = (B * Hkv + 1024) * (H // Hkv) * (D + 2) * 4
+        return (n + 255) // 256 * 256 + B * Hkv * 8
+    assert lib.rope_decode_workspace_size(16, 32, 8, 32768, 128) == want(16, 32, 8, 128) == 2397184
+    assert lib.rope_decode_workspace_size(1, 1, 1, 1, 64) == want(1, 1, 1, 64)
+    # the size does not depend on the cache length
+    assert lib.rope_decode_workspace_size(16, 32, 8, 1, 128) == want(16, 32, 8, 128)
     assert lib.rope_decode_workspace_size(1, 6, 4, 100, 128) == -_lib.ERR_SHAPE
     assert lib.rope_decode_workspace_size(1, 32, 2, 100, 128) == -_lib.ERR_UNSUPPORTED
     # no rotation: tables may be NULL (a bad shape is still reported)

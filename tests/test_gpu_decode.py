@@ -80,10 +80,17 @@ def expected(orc, w, d, b):
     return o[0, :, 0, :]
 
 
-def check_step(orc, w, d, k_cache_in, dev, out):
+def check_step(orc, w, d, k_cache_in, dev, out, bad=()):
+    """Every request against the oracle; requests listed in `bad` (lengths
+    outside the cache or the table) must give NaN rows and an untouched cache."""
     got = to64(out)
     kc, vc = to64(dev["k_cache"]), to64(dev["v_cache"])
     for b in range(w.B):
+        if b in bad:
+            assert np.isnan(got[b]).all(), b
+            assert np.array_equal(kc[b], k_cache_in[b].astype(np.float64)), b
+            assert np.array_equal(vc[b], d["v_cache"][b].astype(np.float64)), b
+            continue
         L = int(d["lens"][b])
         want = expected(orc, w, d, b)
         assert np.isfinite(got[b]).all()
@@ -123,6 +130,41 @@ def test_decode_step(orc, case):
         cos, sin = api.tables_build(w.base, rot, S_max, device=DEV)
     out = run(w, dev, cos, sin)
     check_step(orc, w, d, k_cache_in, dev, out)
+
+
+# Many requests of mixed lengths: the passes of all (request, key/value head)
+# slices are split evenly over the chunk kernel's workgroups, so slices are
+# cut into pieces at arbitrary passes and a workgroup's run crosses slice and
+# request boundaries, empty requests and requests with bad lengths included.
+MIXED_CASES = [
+    # (B, H, H_kv, D, S_max, layout, rot, seed)
+    (70, 8, 2, 128, 2000, "neox", 128, 1),
+    (40, 4, 4, 64, 3000, "gptj", 64, 2),
+    (24, 16, 2, 128, 4000, "neox", 128, 3),    # 8 query heads per key/value head
+    (33, 6, 3, 64, 1500, "neox", 32, 4),
+]
+
+
+@pytest.mark.parametrize("case", MIXED_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_mixed_batch(orc, case):
+    B, H, Hkv, D, S_max, layout, rot, seed = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, S_max, size=B)
+    lens[rng.choice(B, size=4, replace=False)] = [0, 1, S_max - 1, 64]
+    bad = {int(b) for b in rng.choice(np.flatnonzero(lens != S_max - 1), size=3, replace=False)}
+    w = wl.DecodeWorkload("decode_mixed", B, H, Hkv, D, S_max, 200 + seed, layout=layout, base=1e4,
+                          rot_dim=rot)
+    good = [0 if b in bad else int(L) for b, L in enumerate(lens)]
+    d, k_cache_in, dev = prepare(orc, w, good)
+    cos = sin = None
+    if rot > 0:
+        cos, sin = api.tables_build(w.base, rot, S_max, device=DEV)
+    dev_lens = np.array(good, dtype=np.int32)
+    for i, b in enumerate(sorted(bad)):
+        dev_lens[b] = (-1, S_max, S_max + 5)[i % 3]
+    dev["lens"] = torch.from_numpy(dev_lens).to(DEV)
+    out = run(w, dev, cos, sin)
+    check_step(orc, w, d, k_cache_in, dev, out, bad=bad)
 
 
 def test_decode_lengths_outside_the_cache(orc):
