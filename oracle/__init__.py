@@ -71,11 +71,11 @@ class Oracle:
         lib = ctypes.CDLL(self.path)
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         lib.oracle_rope.argtypes = [_dp, _dp, i64, i32, i32, _dp, dbl, i32]
-        lib.oracle_trig.argtypes = [dbl, i32, i64, _dp, _dp]
+        lib.oracle_trig.argtypes = [dbl, i32, i64, dbl, _dp, _dp]
         lib.oracle_attention.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i64, i64, i64, i32, i32,
-                                         i64, i64, i32, dbl, i32, i32, dbl]
+                                         i64, i64, i32, dbl, dbl, i32, i32, dbl]
         lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, i64, i64, i64, i64, i64, i32, i32,
-                                              i64, i64, i32, dbl, i32, i32, dbl,
+                                              i64, i64, i32, dbl, dbl, i32, i32, dbl,
                                               _i64p, i64, _dp]
         lib.oracle_threads.argtypes = []
         for fn in (lib.oracle_rope, lib.oracle_trig, lib.oracle_attention,
@@ -111,23 +111,26 @@ class Oracle:
                                           _ptr(pos), float(base), _LAYOUTS[layout]))
         return out.reshape(x.shape)
 
-    def trig(self, base: float, rot_dim: int, n_pos: int):
-        """fp64 (cos, sin) of p * theta_i, each ``[n_pos, rot_dim/2]``."""
+    def trig(self, base: float, rot_dim: int, n_pos: int, pos_div: float = 1.0):
+        """fp64 (cos, sin) of (p / pos_div) * theta_i, each ``[n_pos, rot_dim/2]``
+        (``pos_div`` > 1: position interpolation)."""
         half = rot_dim // 2
         c = np.empty((n_pos, half))
         s = np.empty((n_pos, half))
-        self._check(self._lib.oracle_trig(float(base), int(rot_dim), int(n_pos), _ptr(c), _ptr(s)))
+        self._check(self._lib.oracle_trig(float(base), int(rot_dim), int(n_pos), float(pos_div),
+                                          _ptr(c), _ptr(s)))
         return c, s
 
     def attention(self, q, k, v, q_off: int = 0, k_off: int = 0, rot_dim: int | None = None,
                   base: float = 10000.0, layout="gptj", causal: bool = True,
-                  scale: float = 0.0) -> np.ndarray:
+                  scale: float = 0.0, pos_div: float = 1.0) -> np.ndarray:
         """Forward of softmax attention over rotated Q/K.
 
         ``q`` ``[B,H,Sq,D]``, ``k`` ``[B,Hkv,Sk,D]``, ``v`` ``[B,Hkv,Sk,Dv]``
         (``Hkv`` divides ``H``; query head h reads key/value head
         h // (H // Hkv)); 2-D or 3-D inputs are promoted.  ``rot_dim=0``
-        disables the rotation.
+        disables the rotation; ``pos_div`` divides the positions the rotation
+        angles use (position interpolation), not the mask's.
         """
         q, k, v = (_f64(a) for a in (q, k, v))
         nd = q.ndim
@@ -139,12 +142,12 @@ class Oracle:
         o = np.empty((B, H, Sq, Dv))
         self._check(self._lib.oracle_attention(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, Sq, Sk, D, Dv, int(q_off), int(k_off),
-            rot, float(base), _LAYOUTS[layout], int(bool(causal)), float(scale)))
+            rot, float(base), float(pos_div), _LAYOUTS[layout], int(bool(causal)), float(scale)))
         return o.reshape(o.shape[4 - nd:])
 
     def attention_rows(self, q, k, v, rows, q_off: int = 0, k_off: int = 0,
                        rot_dim: int | None = None, base: float = 10000.0, layout="gptj",
-                       causal: bool = True, scale: float = 0.0) -> np.ndarray:
+                       causal: bool = True, scale: float = 0.0, pos_div: float = 1.0) -> np.ndarray:
         """Output rows ``(b, h, i)`` of the same forward; returns ``[len(rows), Dv]``."""
         q, k, v = (_f64(a) for a in (q, k, v))
         B, H, Sq, D = q.shape
@@ -154,7 +157,7 @@ class Oracle:
         out = np.empty((r.shape[0], Dv))
         self._check(self._lib.oracle_attention_rows(
             _ptr(q), _ptr(k), _ptr(v), B, H, Hkv, Sq, Sk, D, Dv, int(q_off), int(k_off), rot,
-            float(base), _LAYOUTS[layout], int(bool(causal)), float(scale),
+            float(base), float(pos_div), _LAYOUTS[layout], int(bool(causal)), float(scale),
             r.ctypes.data_as(_i64p), r.shape[0], _ptr(out)))
         return out
 

@@ -30,6 +30,10 @@
  *   - Softmax scale defaults to 1/sqrt(head_dim) (head_dim, not rot_dim).
  *   - Offset mask: query i sits at q_off + i, key j at k_off + j; with causal
  *     set, key j is visible to query i iff k_off + j <= q_off + i.
+ *   - Position interpolation ([RF] section 3: positions divided by an
+ *     extension factor) rotates a row at position p by the angle
+ *     (p / pos_div) theta_i; the mask still compares the integer positions.
+ *     pos_div = 1 is plain RoPE.
  *
  * Build: gcc -O2 -std=c99 -fopenmp -ffp-contract=off -shared -fPIC -lm
  */
@@ -111,18 +115,22 @@ int oracle_rope(const double *x, double *y, int64_t n_rows, int head_dim,
     return OR_OK;
 }
 
-/* The exact trig a cos/sin table approximates: cos_out[p][i] = cos(p theta_i),
- * sin_out[p][i] = sin(p theta_i), rows of rot_dim/2 values.  [RF] section 2
- * (angles formed in fp64); [TR] "Correctness requirements" (table build). */
-int oracle_trig(double base, int rot_dim, int64_t n_pos, double *cos_out, double *sin_out)
+/* The exact trig a cos/sin table approximates: cos_out[p][i] = cos(a),
+ * sin_out[p][i] = sin(a) with a = (p / pos_div) theta_i, rows of rot_dim/2
+ * values.  [RF] section 2 (angles formed in fp64), section 3 (position
+ * interpolation divides the position); [TR] "Correctness requirements"
+ * (table build). */
+int oracle_trig(double base, int rot_dim, int64_t n_pos, double pos_div, double *cos_out,
+                double *sin_out)
 {
     if (rot_dim <= 0 || rot_dim % 2 != 0 || !(base > 0.0) || n_pos < 0) return OR_ERR_ARG;
+    if (!(pos_div > 0.0) || !isfinite(pos_div)) return OR_ERR_ARG;
     if (n_pos > 0 && (!cos_out || !sin_out)) return OR_ERR_ARG;
     const int half = rot_dim / 2;
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < n_pos; ++p)
         for (int i = 0; i < half; ++i) {
-            double ang = (double)p * pair_frequency(base, i, rot_dim);
+            double ang = ((double)p / pos_div) * pair_frequency(base, i, rot_dim);
             cos_out[p * half + i] = cos(ang);
             sin_out[p * half + i] = sin(ang);
         }
@@ -182,14 +190,16 @@ static int attn_args_ok(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t S
  * reasoning process", step 10, for the two head counts).  Query i has
  * position q_off + i and key j position k_off + j; Q and K are rotated at
  * those positions (rot_dim == 0: no rotation), V is never rotated ([RF]
- * section 1).  scale <= 0 selects 1/sqrt(D).  A query with no visible key is
- * rejected ([RF] section 5). */
+ * section 1); with position interpolation the rotation angles use the
+ * positions divided by pos_div ([RF] section 3).  scale <= 0 selects
+ * 1/sqrt(D).  A query with no visible key is rejected ([RF] section 5). */
 int oracle_attention(const double *q, const double *k, const double *v, double *o,
                      int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
-                     int64_t q_off, int64_t k_off, int rot_dim, double base,
+                     int64_t q_off, int64_t k_off, int rot_dim, double base, double pos_div,
                      int layout, int causal, double scale)
 {
     if (!attn_args_ok(B, H, Hkv, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!(pos_div > 0.0) || !isfinite(pos_div)) return OR_ERR_ARG;
     if (!q || !k || !v || !o) return OR_ERR_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     for (int64_t i = 0; i < Sq; ++i)
@@ -203,10 +213,12 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
     /* Rotate every Q and K row once, at its absolute position. */
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nq; ++r)
-        rotate_row(q + r * D, qr + r * D, D, rot_dim, (double)(q_off + r % Sq), base, layout);
+        rotate_row(q + r * D, qr + r * D, D, rot_dim, (double)(q_off + r % Sq) / pos_div, base,
+                   layout);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nk; ++r)
-        rotate_row(k + r * D, kr + r * D, D, rot_dim, (double)(k_off + r % Sk), base, layout);
+        rotate_row(k + r * D, kr + r * D, D, rot_dim, (double)(k_off + r % Sk) / pos_div, base,
+                   layout);
 
     int status = OR_OK;
 #pragma omp parallel
@@ -238,11 +250,12 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
  * rotates its own query and visible keys. */
 int oracle_attention_rows(const double *q, const double *k, const double *v,
                           int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
-                          int64_t q_off, int64_t k_off, int rot_dim, double base,
+                          int64_t q_off, int64_t k_off, int rot_dim, double base, double pos_div,
                           int layout, int causal, double scale,
                           const int64_t *rows, int64_t n_rows, double *o_rows)
 {
     if (!attn_args_ok(B, H, Hkv, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!(pos_div > 0.0) || !isfinite(pos_div)) return OR_ERR_ARG;
     if (!q || !k || !v || (n_rows > 0 && (!rows || !o_rows)) || n_rows < 0) return OR_ERR_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     for (int64_t r = 0; r < n_rows; ++r) {
@@ -265,10 +278,11 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
                 int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
                 int64_t bh = b * H + h, kvh = b * Hkv + h / (H / Hkv);
                 int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
-                rotate_row(q + (bh * Sq + i) * D, qr, D, rot_dim, (double)(q_off + i), base, layout);
+                rotate_row(q + (bh * Sq + i) * D, qr, D, rot_dim, (double)(q_off + i) / pos_div, base,
+                           layout);
                 for (int64_t j = 0; j < n; ++j)
                     rotate_row(k + (kvh * Sk + j) * D, kr + j * D, D, rot_dim,
-                               (double)(k_off + j), base, layout);
+                               (double)(k_off + j) / pos_div, base, layout);
                 attend_row(qr, kr, v + kvh * Sk * Dv, n, D, Dv, scale, scores, o_rows + r * Dv);
             }
         }

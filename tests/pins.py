@@ -422,4 +422,37 @@ def pin_decode_step_forms(orc):
             np.testing.assert_allclose(b, want, rtol=0, atol=1e-12)
 
 
+def pin_position_interpolation(orc):
+    """Position interpolation divides every position by the extension factor
+    before the angle is formed ([RF] section 3).  The table at factor s holds
+    at row s*m exactly the plain table's row m; at a fractional factor it
+    equals numpy's cos/sin of (p/s) theta_i; and attention with the factor
+    equals complex-number rotation at the divided positions plus SciPy's
+    softmax, the mask still comparing the undivided positions."""
+    for base, rot in ((10000.0, 64), (500000.0, 128)):
+        c1, s1 = orc.trig(base, rot, 50)
+        c4, s4 = orc.trig(base, rot, 200, pos_div=4.0)
+        assert np.array_equal(c4[::4], c1) and np.array_equal(s4[::4], s1)
+        cf, sf = orc.trig(base, rot, 300, pos_div=2.5)
+        ang = (np.arange(300)[:, None] / 2.5) * np.power(base, -2.0 * np.arange(rot // 2) / rot)[None]
+        np.testing.assert_allclose(cf, np.cos(ang), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sf, np.sin(ang), rtol=0, atol=1e-12)
+        assert not np.allclose(cf[1:], orc.trig(base, rot, 300)[0][1:])
+    rng = np.random.default_rng(59)
+    Sq, Sk, D, q_off, k_off, s = 5, 11, 8, 9, 3, 3.0
+    for layout in ("gptj", "neox"):
+        q = rng.standard_normal((1, 2, Sq, D))
+        k, v = rng.standard_normal((1, 2, Sk, D)), rng.standard_normal((1, 2, Sk, D))
+        qr = rope_complex(q, (q_off + np.arange(Sq)) / s, 100.0, D, layout)
+        kr = rope_complex(k, (k_off + np.arange(Sk)) / s, 100.0, D, layout)
+        allowed = offset_mask(Sq, Sk, q_off, k_off)
+        want = np.stack([dense_reference(qr[0, h], kr[0, h], v[0, h], allowed, 1 / math.sqrt(D))
+                         for h in range(2)])[None]
+        got = orc.attention(q, k, v, q_off=q_off, k_off=k_off, base=100.0, layout=layout, pos_div=s)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+        rows = orc.attention_rows(q, k, v, [(0, 1, 0), (0, 0, 4)], q_off=q_off, k_off=k_off,
+                                  base=100.0, layout=layout, pos_div=s)
+        np.testing.assert_allclose(rows, np.stack([want[0, 1, 0], want[0, 0, 4]]), rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

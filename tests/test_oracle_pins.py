@@ -30,6 +30,9 @@ MUTATIONS = {
     "query_rotated_at_key_offset": ("(double)(q_off + r % Sq)", "(double)(k_off + r % Sq)"),
     "kv_heads_interleaved": ("int64_t kvh = bh / group;", "int64_t kvh = (bh / H) * Hkv + (bh % H) % Hkv;"),
     "kv_heads_interleaved_rows": ("kvh = b * Hkv + h / (H / Hkv);", "kvh = b * Hkv + h % Hkv;"),
+    "pos_div_multiplies": ("((double)p / pos_div)", "((double)p * pos_div)"),
+    "pos_div_ignored_for_queries": ("(double)(q_off + r % Sq) / pos_div", "(double)(q_off + r % Sq)"),
+    "pos_div_ignored_for_row_keys": ("(double)(k_off + j) / pos_div", "(double)(k_off + j)"),
     "kv_head_count_unchecked": ("if (Hkv <= 0 || H % Hkv != 0) return 0;", "if (Hkv <= 0) return 0;"),
 }
 
