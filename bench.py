@@ -142,12 +142,15 @@ def bench_fused(torch, api, wl, w, steps, warmup, balance=False):
                 p10=durs[len(durs) // 10], p50=durs[len(durs) // 2], p90=durs[(9 * len(durs)) // 10])
 
 
-def bench_rope_apply(torch, api, wl, steps, sets):
-    w = wl.RAGGED_ROPE
+def bench_rope_apply(torch, api, wl, steps, sets, w=None):
+    """rope_apply on a ragged batch (wl.RAGGED_ROPE unless given), cycling
+    `sets` independent Q/K buffers so the last-level cache cannot hold them."""
+    w = w or wl.RAGGED_ROPE
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     dev = torch.device("cuda:0")
     d = wl.rope_apply_inputs(w)
-    q0 = torch.from_numpy(d["q"]).to(torch.bfloat16).to(dev)
-    k0 = torch.from_numpy(d["k"]).to(torch.bfloat16).to(dev)
+    q0 = torch.from_numpy(d["q"]).to(tdt).to(dev)
+    k0 = torch.from_numpy(d["k"]).to(tdt).to(dev)
     pos = torch.from_numpy(d["positions"]).to(dev)
     cos, sin = api.tables_build(w.base, w.rot_dim, w.table_rows, device=dev)
     bufs = [(q0.clone(), k0.clone()) for _ in range(sets)]
@@ -157,7 +160,9 @@ def bench_rope_apply(torch, api, wl, steps, sets):
                                              rotate=lambda i: launches[i % sets]())
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (kernel_ms * 1e-3) / 1e9
-    set_mb = (q0.numel() + k0.numel()) * 2 / 2 ** 20
+    set_mb = (q0.numel() + k0.numel()) * q0.element_size() / 2 ** 20
+    traffic = (recorded_traffic("rope_apply_ragged_8192tok_traffic.md", "rope_apply.hip")
+               if w is wl.RAGGED_ROPE else None)
     return {
         "workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
         "ms_per_launch": round(kernel_ms, 5), "wall_ms_per_launch": round(ms_step, 5),
@@ -165,8 +170,7 @@ def bench_rope_apply(torch, api, wl, steps, sets):
         "single_launch_p90_ms": round(durs[(9 * len(durs)) // 10], 5),
         "buffer_sets": sets, "cycled_mib": round(set_mb * sets, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": recorded_traffic("rope_apply_ragged_8192tok_traffic.md", "rope_apply.hip"),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": nbytes},
     }
 
@@ -344,6 +348,10 @@ def main():
         del r
     if args.only in ("all", "rope_apply"):
         result["rope_apply"] = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets)
+        # the same batch with fp16 storage (same bytes, same kernel family)
+        rf = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets, w=wl.RAGGED_ROPE_F16)
+        result["rope_apply"]["f16"] = {k: rf[k] for k in ("workload", "value", "unit", "ms_per_launch")}
+        result["rope_apply"]["f16"]["frac"] = rf["roofline"]["frac"]
     if args.only in ("all", "decode"):
         result["decode"] = bench_decode(torch, api, wl, args.decode_steps, max(args.warmup // 4, 3))
     if args.sweep:

@@ -19,9 +19,11 @@
  *     argument is validated before any HIP call is made, so argument errors
  *     are reported without a device and nothing is enqueued on error.
  *     ROPE_ERR_HIP reports a failed kernel launch (hipGetLastError).
- *   - Element types: ROPE_BF16 (bfloat16 storage) or ROPE_F32.  All rotation
- *     and softmax arithmetic is fp32; cos/sin tables are always fp32
- *     ([TR] "Kernel design rules": fp32 trig, upcast after load, cast at store).
+ *   - Element types: ROPE_BF16 (bfloat16 storage), ROPE_F32, and for
+ *     rope_apply also ROPE_F16 (IEEE binary16 storage, [TR] "Inputs the agent
+ *     should gather first", item 5).  All rotation and softmax arithmetic is
+ *     fp32; cos/sin tables are always fp32 ([TR] "Kernel design rules": fp32
+ *     trig, upcast after load, cast at store, rounding to nearest even).
  *   - Pairing layouts ([TR] "Inputs the agent should gather first", item 1):
  *       ROPE_NEOX: half split, pair (i, i + rot_dim/2), i < rot_dim/2;
  *       ROPE_GPTJ: adjacent pairs (2i, 2i+1), i < rot_dim/2.
@@ -49,12 +51,13 @@ extern "C" {
 /* element types */
 #define ROPE_BF16 0
 #define ROPE_F32 1
+#define ROPE_F16 2   /* rope_apply only */
 
 /* status codes */
 #define ROPE_OK 0
 #define ROPE_ERR_NULL 1          /* a required pointer is NULL */
 #define ROPE_ERR_SHAPE 2         /* odd or out-of-range dims, non-positive sizes, bad strides */
-#define ROPE_ERR_BASE 3          /* base <= 0 (or not finite) */
+#define ROPE_ERR_BASE 3          /* base or position divisor <= 0 (or not finite) */
 #define ROPE_ERR_UNSUPPORTED 4   /* dtype / head_dim / rot_dim / layout combination not built */
 #define ROPE_ERR_EMPTY_ROW 5     /* causal with q_pos_offset < k_pos_offset: a query sees no key */
 #define ROPE_ERR_TABLE_RANGE 6   /* table_rows too small for the positions the call uses */
@@ -85,6 +88,23 @@ int rope_tables_build(double base, int rot_dim, int64_t max_pos,
                       float *cos_out, float *sin_out, void *stream);
 
 /*
+ * rope_tables_build_scaled -- the same tables under position interpolation
+ * ([RF] section 3: positions are divided by an extension factor before the
+ * angle is formed): row p holds cos((p / pos_divisor) theta_i) and
+ * sin((p / pos_divisor) theta_i), the quotient and the angle in fp64, each
+ * value rounded once to fp32.  pos_divisor = 1 gives exactly the tables of
+ * rope_tables_build.  A larger base (NTK-aware scaling, [RF] section 3) is
+ * the base argument itself.  Every kernel that reads a table (rope_apply,
+ * rope_flash_attn_fwd, rope_decode_attn_fwd) then rotates at the divided
+ * positions; masks and cache rows keep the integer positions.
+ *
+ *   pos_divisor > 0, finite                          (else ROPE_ERR_BASE)
+ *   other arguments as rope_tables_build.
+ */
+int rope_tables_build_scaled(double base, int rot_dim, int64_t max_pos, double pos_divisor,
+                             float *cos_out, float *sin_out, void *stream);
+
+/*
  * rope_apply -- standalone RoPE on Q and K of a ragged continuous batch, in
  * place, both tensors in one launch ([TR] "Required reasoning process"
  * steps 2-10 and "Performance requirements": per-token positions, GQA head
@@ -107,7 +127,7 @@ int rope_tables_build(double base, int rot_dim, int64_t max_pos,
  *   cos_tab,    fp32 [table_rows, rot_dim/2] (see rope_tables_build).
  *   sin_tab
  *   head_dim    even, 2..1024; rot_dim even, 2..head_dim.
- *   layout      ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16 or ROPE_F32.
+ *   layout      ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16, ROPE_F32 or ROPE_F16.
  * n_tokens == 0, or h_q == h_kv == 0, is a no-op returning ROPE_OK.
  * Any alignment is accepted; 16-byte-aligned rows whose rotated span is a
  * whole number of 16-byte vectors take the vectorised path.

@@ -11,11 +11,12 @@ from pathlib import Path
 LIBRARY = Path(__file__).resolve().parent / "librope_mi355x.so"
 
 NEOX, GPTJ = 0, 1
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
 OK, ERR_NULL, ERR_SHAPE, ERR_BASE, ERR_UNSUPPORTED, ERR_EMPTY_ROW, ERR_TABLE_RANGE, ERR_HIP, ERR_ALIGN = range(9)
 
 # every symbol include/rope_mi355x.h declares
-EXPORTS = ("rope_status_str", "rope_tables_build", "rope_apply", "rope_flash_attn_fwd",
+EXPORTS = ("rope_status_str", "rope_tables_build", "rope_tables_build_scaled", "rope_apply",
+           "rope_flash_attn_fwd",
            "rope_flash_attn_workspace_size", "rope_decode_attn_fwd", "rope_decode_workspace_size")
 
 _lib = None
@@ -35,6 +36,8 @@ def load() -> ctypes.CDLL:
     lib.rope_status_str.restype = ctypes.c_char_p
     lib.rope_tables_build.argtypes = [f64, i32, i64, vp, vp, vp]
     lib.rope_tables_build.restype = i32
+    lib.rope_tables_build_scaled.argtypes = [f64, i32, i64, f64, vp, vp, vp]
+    lib.rope_tables_build_scaled.restype = i32
     lib.rope_apply.argtypes = [vp, i64, i64, i32, vp, i64, i64, i32, vp, i64, vp, vp, i64,
                                i32, i32, i32, i32, vp]
     lib.rope_apply.restype = i32

@@ -42,7 +42,9 @@ def _dtype(t: torch.Tensor) -> int:
         return _lib.BF16
     if t.dtype == torch.float32:
         return _lib.F32
-    raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32 expected")
+    if t.dtype == torch.float16:
+        return _lib.F16   # rope_apply only; the other entry points report it as unsupported
+    raise TypeError(f"unsupported dtype {t.dtype}; bfloat16, float16 or float32 expected")
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -55,13 +57,19 @@ def _require_cuda(*ts: torch.Tensor) -> None:
             raise ValueError("tensors must live on the GPU")
 
 
-def tables_build(base: float, rot_dim: int, max_pos: int, device="cuda"):
-    """fp32 (cos, sin) tables ``[max_pos, rot_dim/2]`` built on the device."""
+def tables_build(base: float, rot_dim: int, max_pos: int, device="cuda", pos_divisor: float = 1.0):
+    """fp32 (cos, sin) tables ``[max_pos, rot_dim/2]`` built on the device;
+    ``pos_divisor`` > 1 builds them for position interpolation."""
     lib = _lib.load()
     cos = torch.empty((max_pos, rot_dim // 2), dtype=torch.float32, device=device)
     sin = torch.empty_like(cos)
-    _check(lib.rope_tables_build(float(base), int(rot_dim), int(max_pos), cos.data_ptr(),
-                                 sin.data_ptr(), _stream(cos)), "rope_tables_build")
+    if pos_divisor == 1.0:
+        _check(lib.rope_tables_build(float(base), int(rot_dim), int(max_pos), cos.data_ptr(),
+                                     sin.data_ptr(), _stream(cos)), "rope_tables_build")
+    else:
+        _check(lib.rope_tables_build_scaled(float(base), int(rot_dim), int(max_pos),
+                                            float(pos_divisor), cos.data_ptr(), sin.data_ptr(),
+                                            _stream(cos)), "rope_tables_build_scaled")
     return cos, sin
 
 

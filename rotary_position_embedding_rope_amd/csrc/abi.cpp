@@ -16,9 +16,11 @@ constexpr int64_t kMaxGrid = 2147483647;   // blocks per 1-D grid
 
 bool aligned(const void *p, unsigned bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
 
-int elt_size(int dtype) { return dtype == ROPE_BF16 ? 2 : 4; }
+int elt_size(int dtype) { return dtype == ROPE_F32 ? 4 : 2; }
 
+// dtypes of the fused forward; rope_apply also takes ROPE_F16
 bool valid_dtype(int dtype) { return dtype == ROPE_BF16 || dtype == ROPE_F32; }
+bool valid_apply_dtype(int dtype) { return valid_dtype(dtype) || dtype == ROPE_F16; }
 bool valid_layout(int layout) { return layout == ROPE_NEOX || layout == ROPE_GPTJ; }
 
 // Rows (t, h) of one tensor must not overlap: stride_head >= head_dim when
@@ -44,7 +46,7 @@ const char *rope_status_str(int status)
     case ROPE_OK: return "ok";
     case ROPE_ERR_NULL: return "a required pointer is NULL";
     case ROPE_ERR_SHAPE: return "invalid shape, dimension, offset or stride";
-    case ROPE_ERR_BASE: return "base must be positive and finite";
+    case ROPE_ERR_BASE: return "base (and position divisor) must be positive and finite";
     case ROPE_ERR_UNSUPPORTED: return "unsupported dtype / head_dim / rot_dim / layout combination";
     case ROPE_ERR_EMPTY_ROW: return "a query row sees no key (causal with q_pos_offset < k_pos_offset)";
     case ROPE_ERR_TABLE_RANGE: return "cos/sin table has too few rows for the positions used";
@@ -57,12 +59,19 @@ const char *rope_status_str(int status)
 int rope_tables_build(double base, int rot_dim, int64_t max_pos, float *cos_out,
                       float *sin_out, void *stream)
 {
+    return rope_tables_build_scaled(base, rot_dim, max_pos, 1.0, cos_out, sin_out, stream);
+}
+
+int rope_tables_build_scaled(double base, int rot_dim, int64_t max_pos, double pos_divisor,
+                             float *cos_out, float *sin_out, void *stream)
+{
     if (!(base > 0.0) || !std::isfinite(base)) return ROPE_ERR_BASE;
+    if (!(pos_divisor > 0.0) || !std::isfinite(pos_divisor)) return ROPE_ERR_BASE;
     if (rot_dim < 2 || rot_dim > 1024 || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (max_pos < 1 || max_pos > 2147483647) return ROPE_ERR_SHAPE;
     if (!cos_out || !sin_out) return ROPE_ERR_NULL;
     if (!aligned(cos_out, 4) || !aligned(sin_out, 4)) return ROPE_ERR_ALIGN;
-    return rope_launch_tables(base, rot_dim, max_pos, cos_out, sin_out,
+    return rope_launch_tables(base, rot_dim, max_pos, pos_divisor, cos_out, sin_out,
                               static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK
                ? ROPE_OK
                : ROPE_ERR_HIP;
@@ -78,7 +87,7 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
     if (rot_dim < 2 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (n_tokens < 0 || n_tokens > 2147483647 || h_q < 0 || h_kv < 0 || h_q + h_kv > 65536)
         return ROPE_ERR_SHAPE;
-    if (!valid_layout(layout) || !valid_dtype(dtype)) return ROPE_ERR_UNSUPPORTED;
+    if (!valid_layout(layout) || !valid_apply_dtype(dtype)) return ROPE_ERR_UNSUPPORTED;
     if (!strides_ok(q_stride_tok, q_stride_head, h_q, head_dim, n_tokens) ||
         !strides_ok(k_stride_tok, k_stride_head, h_kv, head_dim, n_tokens))
         return ROPE_ERR_SHAPE;

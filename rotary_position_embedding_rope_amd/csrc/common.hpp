@@ -25,6 +25,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     bf16x2_t v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
 }
+// IEEE binary16 halves of a 32-bit word; two fp32 values rounded to nearest
+// even binary16 and packed (low half first).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f16lo_to_f32(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16hi_to_f32(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float x)
 {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
@@ -38,7 +51,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x)
 
 // Host launchers, one per kernel family.  Arguments are validated by abi.cpp
 // before these are called; each returns ROPE_LAUNCH_OK or ROPE_LAUNCH_ERR.
-int rope_launch_tables(double base, int rot_dim, int64_t max_pos, float *cos_out,
+int rope_launch_tables(double base, int rot_dim, int64_t max_pos, double pos_div, float *cos_out,
                        float *sin_out, hipStream_t stream);
 
 struct RopeApplyArgs {

@@ -32,6 +32,28 @@ using rope::bf16hi_to_f32;
 using rope::bf16lo_to_f32;
 using rope::pack_bf16x2;
 
+// Storage types: uint16_t holds bf16 bit patterns, _Float16 is IEEE binary16,
+// float is fp32.  Widening is exact; narrowing rounds to nearest even.
+template <typename T> struct Elt;
+template <> struct Elt<uint16_t> {
+    static __device__ __forceinline__ float lo(uint32_t w) { return bf16lo_to_f32(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return bf16hi_to_f32(w); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+    static __device__ __forceinline__ float get(uint16_t v) { return rope::bf16_to_f32(v); }
+    static __device__ __forceinline__ uint16_t put(float x) { return rope::f32_to_bf16(x); }
+};
+template <> struct Elt<_Float16> {
+    static __device__ __forceinline__ float lo(uint32_t w) { return rope::f16lo_to_f32(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return rope::f16hi_to_f32(w); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return rope::pack_f16x2(a, b); }
+    static __device__ __forceinline__ float get(_Float16 v) { return (float)v; }
+    static __device__ __forceinline__ _Float16 put(float x) { return (_Float16)x; }
+};
+template <> struct Elt<float> {
+    static __device__ __forceinline__ float get(float v) { return v; }
+    static __device__ __forceinline__ float put(float x) { return x; }
+};
+
 // V contiguous elements of T <-> float[V].
 template <typename T, int V>
 struct Access {
@@ -42,37 +64,31 @@ struct Access {
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[2 * i] = bf16lo_to_f32(ws[i]);
-                x[2 * i + 1] = bf16hi_to_f32(ws[i]);
+                x[2 * i] = Elt<T>::lo(ws[i]);
+                x[2 * i + 1] = Elt<T>::hi(ws[i]);
             }
         } else if constexpr (sizeof(T) == 4 && V == 4) {
             const float4 w = *reinterpret_cast<const float4 *>(p);
             x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
         } else {
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                if constexpr (sizeof(T) == 2) x[i] = rope::bf16_to_f32(p[i]);
-                else x[i] = p[i];
-            }
+            for (int i = 0; i < V; ++i) x[i] = Elt<T>::get(p[i]);
         }
     }
     static __device__ __forceinline__ void store(T *p, const float (&x)[V])
     {
         if constexpr (sizeof(T) == 2 && V == 8) {
             uint4 w;
-            w.x = pack_bf16x2(x[0], x[1]);
-            w.y = pack_bf16x2(x[2], x[3]);
-            w.z = pack_bf16x2(x[4], x[5]);
-            w.w = pack_bf16x2(x[6], x[7]);
+            w.x = Elt<T>::pack(x[0], x[1]);
+            w.y = Elt<T>::pack(x[2], x[3]);
+            w.z = Elt<T>::pack(x[4], x[5]);
+            w.w = Elt<T>::pack(x[6], x[7]);
             *reinterpret_cast<uint4 *>(p) = w;
         } else if constexpr (sizeof(T) == 4 && V == 4) {
             *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
         } else {
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                if constexpr (sizeof(T) == 2) p[i] = rope::f32_to_bf16(x[i]);
-                else p[i] = x[i];
-            }
+            for (int i = 0; i < V; ++i) p[i] = Elt<T>::put(x[i]);
         }
     }
 };
@@ -200,7 +216,7 @@ __device__ __forceinline__ void unpack16(const u32x4_t w, float (&x)[16 / sizeof
 {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo_to_f32(w[i]); x[2 * i + 1] = bf16hi_to_f32(w[i]); }
+        for (int i = 0; i < 4; ++i) { x[2 * i] = Elt<T>::lo(w[i]); x[2 * i + 1] = Elt<T>::hi(w[i]); }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
@@ -212,7 +228,7 @@ __device__ __forceinline__ u32x4_t pack16(const float (&y)[16 / sizeof(T)])
     u32x4_t w;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) w[i] = Elt<T>::pack(y[2 * i], y[2 * i + 1]);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(y[i]);
@@ -366,13 +382,11 @@ int dispatch_rows(const RopeApplyArgs &a, int L, hipStream_t stream)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-}  // namespace
-
-int rope_launch_apply(const RopeApplyArgs &a, hipStream_t stream)
+template <typename T>
+int launch_typed(const RopeApplyArgs &a, hipStream_t stream)
 {
-    const bool bf16 = a.dtype == 0;
-    const int elt = bf16 ? 2 : 4;
-    const int V = 16 / elt;
+    constexpr int elt = (int)sizeof(T);
+    constexpr int V = 16 / elt;
     const int half = a.rot_dim / 2;
     const bool neox = a.layout == 0;
     // 16-byte path: row starts 16-byte aligned for every token/head, and the
@@ -391,25 +405,35 @@ int rope_launch_apply(const RopeApplyArgs &a, hipStream_t stream)
         const int L = a.rot_dim / V;
         const bool pow2 = L >= 2 && L <= 32 && (L & (L - 1)) == 0;
         if (pow2) {
-            const int rc = bf16 ? (neox ? dispatch_rows<uint16_t, 0>(a, L, stream)
-                                        : dispatch_rows<uint16_t, 1>(a, L, stream))
-                                : (neox ? dispatch_rows<float, 0>(a, L, stream)
-                                        : dispatch_rows<float, 1>(a, L, stream));
+            const int rc = neox ? dispatch_rows<T, 0>(a, L, stream) : dispatch_rows<T, 1>(a, L, stream);
             if (rc >= 0) return rc;
         }
     }
-    if (bf16) {
+    if constexpr (elt == 2) {
         if (neox) {
-            if (vec) return vt ? launch<uint16_t, 0, 8, true>(a, stream) : launch<uint16_t, 0, 8, false>(a, stream);
-            return launch<uint16_t, 0, 1, false>(a, stream);
+            if (vec) return vt ? launch<T, 0, 8, true>(a, stream) : launch<T, 0, 8, false>(a, stream);
+            return launch<T, 0, 1, false>(a, stream);
         }
-        if (vec) return vt ? launch<uint16_t, 1, 8, true>(a, stream) : launch<uint16_t, 1, 8, false>(a, stream);
-        return launch<uint16_t, 1, 2, false>(a, stream);
+        if (vec) return vt ? launch<T, 1, 8, true>(a, stream) : launch<T, 1, 8, false>(a, stream);
+        return launch<T, 1, 2, false>(a, stream);
+    } else {
+        if (neox) {
+            if (vec) return vt ? launch<T, 0, 4, true>(a, stream) : launch<T, 0, 4, false>(a, stream);
+            return launch<T, 0, 1, false>(a, stream);
+        }
+        if (vec) return launch<T, 1, 4, false>(a, stream);   // 2 frequencies per chunk
+        return launch<T, 1, 2, false>(a, stream);
     }
-    if (neox) {
-        if (vec) return vt ? launch<float, 0, 4, true>(a, stream) : launch<float, 0, 4, false>(a, stream);
-        return launch<float, 0, 1, false>(a, stream);
+}
+
+}  // namespace
+
+int rope_launch_apply(const RopeApplyArgs &a, hipStream_t stream)
+{
+    switch (a.dtype) {
+    case 0: return launch_typed<uint16_t>(a, stream);
+    case 1: return launch_typed<float>(a, stream);
+    case 2: return launch_typed<_Float16>(a, stream);
+    default: return ROPE_LAUNCH_ERR;
     }
-    if (vec) return launch<float, 1, 4, false>(a, stream);   // 2 frequencies per chunk
-    return launch<float, 1, 2, false>(a, stream);
 }

@@ -42,12 +42,15 @@ def bf16_to_f32(bits) -> np.ndarray:
 
 
 def round_to(x, dtype: str) -> np.ndarray:
-    """fp32 array holding ``x`` rounded to ``dtype`` ('f32' or 'bf16')."""
+    """fp32 array holding ``x`` rounded to ``dtype`` ('f32', 'bf16' or 'f16'),
+    nearest even."""
     f = np.asarray(x, dtype=np.float32)
     if dtype == "f32":
         return np.ascontiguousarray(f)
     if dtype == "bf16":
         return bf16_to_f32(bf16_bits(f))
+    if dtype == "f16":
+        return np.ascontiguousarray(f.astype(np.float16).astype(np.float32))
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -161,7 +164,7 @@ class RopeApplyWorkload:
     def algorithmic_bytes(self) -> int:
         """Bytes the op must move: rotated span read+written for every head,
         one cos and one sin row per token, one int32 position per token."""
-        elt = 2 if self.dtype == "bf16" else 4
+        elt = 4 if self.dtype == "f32" else 2
         per_tok = 2 * (self.H_q + self.H_kv) * self.rot_dim * elt + 2 * (self.rot_dim // 2) * 4 + 4
         return self.n_tokens * per_tok
 
@@ -179,6 +182,9 @@ PREFILL_OFFSET = AttentionWorkload("chunked_prefill_neox_bf16_1x32x2048q_16384k_
                                    q_off=14336, k_off=0)
 RAGGED_ROPE = RopeApplyWorkload("ragged_rope_neox_bf16_8192tok_32q8kv_rot64of128", 8192, 16,
                                 32768, 32, 8, 128, 64, "neox", "bf16", 8)
+# the same batch with fp16 storage
+RAGGED_ROPE_F16 = RopeApplyWorkload("ragged_rope_neox_f16_8192tok_32q8kv_rot64of128", 8192, 16,
+                                    32768, 32, 8, 128, 64, "neox", "f16", 11)
 
 # the chunked prefill with 8 key/value heads for the 32 query heads (the
 # head counts of the ragged RoPE workload): grouped-query attention

@@ -47,6 +47,7 @@ def test_status_codes_match_header():
     assert codes["ROPE_ERR_HIP"] == _lib.ERR_HIP and codes["ROPE_ERR_ALIGN"] == _lib.ERR_ALIGN
     assert codes["ROPE_NEOX"] == _lib.NEOX and codes["ROPE_GPTJ"] == _lib.GPTJ
     assert codes["ROPE_BF16"] == _lib.BF16 and codes["ROPE_F32"] == _lib.F32
+    assert codes["ROPE_F16"] == _lib.F16
 
 
 def test_status_strings(lib):
@@ -75,6 +76,13 @@ def test_status_strings(lib):
 ])
 def test_tables_build_rejects(lib, base, rot, maxpos, c, s, want):
     assert lib.rope_tables_build(base, rot, maxpos, c, s, None) == want
+    # the scaled build validates the same way (divisor 1 is the plain table)
+    assert lib.rope_tables_build_scaled(base, rot, maxpos, 1.0, c, s, None) == want
+
+
+@pytest.mark.parametrize("div", [0.0, -2.0, float("inf"), float("nan")])
+def test_tables_build_scaled_rejects_divisor(lib, div):
+    assert lib.rope_tables_build_scaled(1e4, 64, 10, div, FAKE, FAKE2, None) == _lib.ERR_BASE
 
 
 # --------------------------------------------------------------------------
@@ -103,6 +111,8 @@ def apply_args(**over):
     (dict(qst=31 * 128), _lib.ERR_SHAPE),      # token rows overlap
     (dict(layout=2), _lib.ERR_UNSUPPORTED),
     (dict(dtype=5), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=_lib.F16, q=None), _lib.ERR_NULL),   # fp16 is accepted: validation goes on
+    (dict(dtype=_lib.F16, q=FAKE + 1), _lib.ERR_ALIGN),
     (dict(q=None), _lib.ERR_NULL),
     (dict(k=None), _lib.ERR_NULL),
     (dict(pos=None), _lib.ERR_NULL),
@@ -156,6 +166,7 @@ def fwd_args(**over):
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(rot=48), _lib.ERR_UNSUPPORTED),
     (dict(dtype=3), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=_lib.F16), _lib.ERR_UNSUPPORTED),   # fp16 storage: rope_apply only
     (dict(layout=7), _lib.ERR_UNSUPPORTED),
     (dict(q=None), _lib.ERR_NULL),
     (dict(v=None), _lib.ERR_NULL),
@@ -225,6 +236,7 @@ def decode_args(**over):
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(Hkv=2), _lib.ERR_UNSUPPORTED),           # 16 query heads per key/value head
     (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=_lib.F16), _lib.ERR_UNSUPPORTED),
     (dict(layout=7), _lib.ERR_UNSUPPORTED),
     (dict(q=None), _lib.ERR_NULL),
     (dict(lens=None), _lib.ERR_NULL),
