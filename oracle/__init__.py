@@ -77,9 +77,14 @@ class Oracle:
         lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, i64, i64, i64, i64, i64, i32, i32,
                                               i64, i64, i32, dbl, dbl, i32, i32, dbl,
                                               _i64p, i64, _dp]
+        lib.oracle_attention_lse.argtypes = [_dp, _dp, _dp, i64, i64, i64, i64, i64, i32,
+                                             i64, i64, i32, dbl, dbl, i32, i32, dbl]
+        lib.oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, i64, i64, i64, i64,
+                                             i64, i32, i32, i64, i64, i32, dbl, dbl, i32, i32, dbl]
         lib.oracle_threads.argtypes = []
         for fn in (lib.oracle_rope, lib.oracle_trig, lib.oracle_attention,
-                   lib.oracle_attention_rows, lib.oracle_threads):
+                   lib.oracle_attention_rows, lib.oracle_attention_lse, lib.oracle_attention_bwd,
+                   lib.oracle_threads):
             fn.restype = ctypes.c_int
         self._lib = lib
 
@@ -160,6 +165,37 @@ class Oracle:
             float(base), float(pos_div), _LAYOUTS[layout], int(bool(causal)), float(scale),
             r.ctypes.data_as(_i64p), r.shape[0], _ptr(out)))
         return out
+
+
+    def attention_lse(self, q, k, q_off: int = 0, k_off: int = 0, rot_dim: int | None = None,
+                      base: float = 10000.0, layout="gptj", causal: bool = True,
+                      scale: float = 0.0, pos_div: float = 1.0) -> np.ndarray:
+        """Natural-log log-sum-exp of each query row's scores, ``[B, H, Sq]``."""
+        q, k = _f64(q), _f64(k)
+        B, H, Sq, D = q.shape
+        Hkv, Sk = k.shape[1], k.shape[2]
+        rot = D if rot_dim is None else int(rot_dim)
+        out = np.empty((B, H, Sq))
+        self._check(self._lib.oracle_attention_lse(
+            _ptr(q), _ptr(k), _ptr(out), B, H, Hkv, Sq, Sk, D, int(q_off), int(k_off), rot,
+            float(base), float(pos_div), _LAYOUTS[layout], int(bool(causal)), float(scale)))
+        return out
+
+    def attention_bwd(self, q, k, v, dout, q_off: int = 0, k_off: int = 0,
+                      rot_dim: int | None = None, base: float = 10000.0, layout="gptj",
+                      causal: bool = True, scale: float = 0.0, pos_div: float = 1.0):
+        """Gradients (dq, dk, dv) of ``attention`` for the upstream gradient
+        ``dout`` (same shape as the output); 4-D inputs."""
+        q, k, v, dout = (_f64(a) for a in (q, k, v, dout))
+        B, H, Sq, D = q.shape
+        Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
+        rot = D if rot_dim is None else int(rot_dim)
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        self._check(self._lib.oracle_attention_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, Sq, Sk,
+            D, Dv, int(q_off), int(k_off), rot, float(base), float(pos_div), _LAYOUTS[layout],
+            int(bool(causal)), float(scale)))
+        return dq, dk, dv
 
 
 _DEFAULT: Oracle | None = None

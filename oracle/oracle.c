@@ -292,3 +292,174 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
     }
     return status;
 }
+
+/* Row-wise log-sum-exp of the same forward's scores, natural log:
+ * lse[b, h, i] = log sum_j exp(s_ij) over the visible keys, the quantity a
+ * blocked forward keeps (running max plus log of the running sum) so that a
+ * backward pass can recompute p_ij = exp(s_ij - lse_i) ([RF] section 5: the
+ * (m, l) state; its last row of questions: backward recomputes P from saved
+ * row statistics). */
+int oracle_attention_lse(const double *q, const double *k, double *lse,
+                         int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D,
+                         int64_t q_off, int64_t k_off, int rot_dim, double base, double pos_div,
+                         int layout, int causal, double scale)
+{
+    if (!attn_args_ok(B, H, Hkv, Sq, Sk, D, 1, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!(pos_div > 0.0) || !isfinite(pos_div)) return OR_ERR_ARG;
+    if (!q || !k || !lse) return OR_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int64_t i = 0; i < Sq; ++i)
+        if (visible_keys(i, Sk, q_off, k_off, causal) == 0) return OR_ERR_EMPTY_ROW;
+    const int64_t nq = B * H * Sq, group = H / Hkv;
+    int status = OR_OK;
+#pragma omp parallel
+    {
+        double *qr = malloc(sizeof(double) * (size_t)D);
+        double *kr = malloc(sizeof(double) * (size_t)D);
+        if (!qr || !kr) {
+#pragma omp atomic write
+            status = OR_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nq; ++r) {
+                int64_t bh = r / Sq, i = r % Sq, kvh = bh / group;
+                int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
+                rotate_row(q + r * D, qr, D, rot_dim, (double)(q_off + i) / pos_div, base, layout);
+                double m = -INFINITY;
+                for (int64_t j = 0; j < n; ++j) {
+                    rotate_row(k + (kvh * Sk + j) * D, kr, D, rot_dim, (double)(k_off + j) / pos_div,
+                               base, layout);
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += qr[d] * kr[d];
+                    s *= scale;
+                    if (s > m) m = s;
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    rotate_row(k + (kvh * Sk + j) * D, kr, D, rot_dim, (double)(k_off + j) / pos_div,
+                               base, layout);
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += qr[d] * kr[d];
+                    l += exp(s * scale - m);
+                }
+                lse[r] = m + log(l);
+            }
+        }
+        free(qr);
+        free(kr);
+    }
+    return status;
+}
+
+/* Gradients of the same forward, o = attention(q, k, v), for an upstream
+ * gradient dout [B, H, Sq, Dv], by the chain rule through each step of the
+ * forward ([RF] section 5's last questions: the backward recomputes the
+ * probabilities and needs, per query row, the sum of p times its upstream
+ * score gradient):
+ *   qr_i = R(q_pos_i) q_i, kr_j = R(k_pos_j) k_j    (rotation; V unrotated)
+ *   s_ij = scale qr_i . kr_j,  p_ij = softmax over the visible j
+ *   dv_j   = sum_i p_ij dout_i
+ *   dp_ij  = dout_i . v_j
+ *   ds_ij  = p_ij (dp_ij - sum_j' p_ij' dp_ij')
+ *   dqr_i  = scale sum_j ds_ij kr_j,   dq_i = R(q_pos_i)^T dqr_i
+ *   dkr_j  = scale sum_i ds_ij qr_i,   dk_j = R(k_pos_j)^T dkr_j
+ * R(pos)^T is the rotation by the opposite angle.  A key/value head's dk and
+ * dv sum over every query head that reads it and every query row.  Work is
+ * split over (batch, key/value head), so no two threads write one row. */
+int oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dout,
+                         double *dq, double *dk, double *dv,
+                         int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
+                         int64_t q_off, int64_t k_off, int rot_dim, double base, double pos_div,
+                         int layout, int causal, double scale)
+{
+    if (!attn_args_ok(B, H, Hkv, Sq, Sk, D, Dv, rot_dim, base, layout)) return OR_ERR_ARG;
+    if (!(pos_div > 0.0) || !isfinite(pos_div)) return OR_ERR_ARG;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return OR_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int64_t i = 0; i < Sq; ++i)
+        if (visible_keys(i, Sk, q_off, k_off, causal) == 0) return OR_ERR_EMPTY_ROW;
+
+    const int64_t nq = B * H * Sq, nk = B * Hkv * Sk, group = H / Hkv;
+    double *qr = malloc(sizeof(double) * (size_t)(nq * D));
+    double *kr = malloc(sizeof(double) * (size_t)(nk * D));
+    if (!qr || !kr) { free(qr); free(kr); return OR_ERR_NOMEM; }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nq; ++r)
+        rotate_row(q + r * D, qr + r * D, D, rot_dim, (double)(q_off + r % Sq) / pos_div, base,
+                   layout);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nk; ++r)
+        rotate_row(k + r * D, kr + r * D, D, rot_dim, (double)(k_off + r % Sk) / pos_div, base,
+                   layout);
+
+    int status = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * (size_t)Sk);
+        double *dp = malloc(sizeof(double) * (size_t)Sk);
+        double *dqr = malloc(sizeof(double) * (size_t)D);
+        double *dkr = malloc(sizeof(double) * (size_t)(Sk * D));
+        if (!p || !dp || !dqr || !dkr) {
+#pragma omp atomic write
+            status = OR_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t kvh = 0; kvh < B * Hkv; ++kvh) {
+                const int64_t b = kvh / Hkv;
+                const double *krh = kr + kvh * Sk * D, *vh = v + kvh * Sk * Dv;
+                double *dvh = dv + kvh * Sk * Dv;
+                memset(dkr, 0, sizeof(double) * (size_t)(Sk * D));
+                memset(dvh, 0, sizeof(double) * (size_t)(Sk * Dv));
+                for (int64_t g = 0; g < group; ++g) {
+                    const int64_t bh = b * H + (kvh % Hkv) * group + g;
+                    for (int64_t i = 0; i < Sq; ++i) {
+                        const int64_t r = bh * Sq + i;
+                        const double *qri = qr + r * D, *doi = dout + r * Dv;
+                        const int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
+                        double m = -INFINITY;
+                        for (int64_t j = 0; j < n; ++j) {
+                            double s = 0.0;
+                            for (int d = 0; d < D; ++d) s += qri[d] * krh[j * D + d];
+                            p[j] = s * scale;
+                            if (p[j] > m) m = p[j];
+                        }
+                        double l = 0.0;
+                        for (int64_t j = 0; j < n; ++j) {
+                            p[j] = exp(p[j] - m);
+                            l += p[j];
+                        }
+                        double pdp = 0.0;
+                        for (int64_t j = 0; j < n; ++j) {
+                            p[j] /= l;
+                            double t = 0.0;
+                            for (int e = 0; e < Dv; ++e) t += doi[e] * vh[j * Dv + e];
+                            dp[j] = t;
+                            pdp += p[j] * t;
+                        }
+                        for (int d = 0; d < D; ++d) dqr[d] = 0.0;
+                        for (int64_t j = 0; j < n; ++j) {
+                            const double ds = p[j] * (dp[j] - pdp);
+                            for (int d = 0; d < D; ++d) {
+                                dqr[d] += scale * ds * krh[j * D + d];
+                                dkr[j * D + d] += scale * ds * qri[d];
+                            }
+                            for (int e = 0; e < Dv; ++e) dvh[j * Dv + e] += p[j] * doi[e];
+                        }
+                        rotate_row(dqr, dq + r * D, D, rot_dim, -(double)(q_off + i) / pos_div, base,
+                                   layout);
+                    }
+                }
+                for (int64_t j = 0; j < Sk; ++j)
+                    rotate_row(dkr + j * D, dk + (kvh * Sk + j) * D, D, rot_dim,
+                               -(double)(k_off + j) / pos_div, base, layout);
+            }
+        }
+        free(p);
+        free(dp);
+        free(dqr);
+        free(dkr);
+    }
+    free(qr);
+    free(kr);
+    return status;
+}

@@ -455,4 +455,101 @@ def pin_position_interpolation(orc):
         np.testing.assert_allclose(rows, np.stack([want[0, 1, 0], want[0, 0, 4]]), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# backward pins
+
+
+def _loss_grad_fd(orc, q, k, v, dout, h=1e-5, **kw):
+    """Central differences of L = sum(dout * attention(q, k, v)) with respect
+    to every element of q, k and v."""
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.empty_like(args[which])
+        it = np.nditer(args[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            lp = np.sum(dout * orc.attention(*plus, **kw))
+            lm = np.sum(dout * orc.attention(*minus, **kw))
+            g[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def pin_bwd_finite_differences(orc):
+    """The gradients equal central finite differences of the forward (the
+    pinned oracle forward) for the loss sum(dout * o): GQA, offsets with the
+    causal mask, partial rotation, both pairings, interpolated positions and
+    no mask ([RF] section 5: the backward is the derivative of the same
+    forward)."""
+    rng = np.random.default_rng(61)
+    cases = [
+        dict(shape=(1, 2, 1, 4, 6, 8), kw=dict(q_off=2, k_off=0, rot_dim=8, layout="neox")),
+        dict(shape=(1, 4, 2, 3, 5, 8), kw=dict(q_off=4, k_off=1, rot_dim=4, layout="gptj", base=100.0)),
+        dict(shape=(2, 2, 2, 3, 3, 6), kw=dict(rot_dim=6, layout="neox", causal=False, pos_div=2.5)),
+    ]
+    for c in cases:
+        B, H, Hkv, Sq, Sk, D = c["shape"]
+        q = rng.standard_normal((B, H, Sq, D))
+        k = rng.standard_normal((B, Hkv, Sk, D))
+        v = rng.standard_normal((B, Hkv, Sk, D))
+        dout = rng.standard_normal((B, H, Sq, D))
+        got = orc.attention_bwd(q, k, v, dout, **c["kw"])
+        want = _loss_grad_fd(orc, q, k, v, dout, **c["kw"])
+        for g, w in zip(got, want):
+            np.testing.assert_allclose(g, w, rtol=0, atol=2e-8)
+
+
+def _torch_rope(x, pos, base, rot, layout):
+    """RoPE in torch fp64 from complex multiplication (built without the
+    oracle's pair indexing)."""
+    import torch
+    half = rot // 2
+    theta = base ** (-2.0 * torch.arange(half, dtype=torch.float64) / rot)
+    ang = pos[:, None].to(torch.float64) * theta[None, :]
+    w = torch.polar(torch.ones_like(ang), ang)
+    if layout == "gptj":
+        z = torch.complex(x[..., 0:rot:2], x[..., 1:rot:2]) * w
+        rotated = torch.stack([z.real, z.imag], dim=-1).flatten(-2)
+    else:
+        z = torch.complex(x[..., :half], x[..., half:rot]) * w
+        rotated = torch.cat([z.real, z.imag], dim=-1)
+    return torch.cat([rotated, x[..., rot:]], dim=-1)
+
+
+def pin_bwd_vs_torch_autograd(orc):
+    """fp64 torch autograd through a forward written independently (complex
+    rotation, explicit matmul, offset mask, torch.softmax, key/value heads
+    repeated for GQA) agrees with the oracle's gradients at 1e-11, and its
+    log-sum-exp rows with the oracle's at 1e-12."""
+    import torch
+    rng = np.random.default_rng(67)
+    for layout, rot, causal in (("neox", 8, True), ("gptj", 16, True), ("neox", 16, False)):
+        B, H, Hkv, Sq, Sk, D, q_off, k_off, base = 2, 4, 2, 6, 9, 16, 5, 2, 500.0
+        arrays = [rng.standard_normal(s) for s in ((B, H, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, D),
+                                                   (B, H, Sq, D))]
+        q, k, v, dout = (torch.tensor(a, requires_grad=i < 3) for i, a in enumerate(arrays))
+        qr = _torch_rope(q, torch.arange(Sq) + q_off, base, rot, layout)
+        kr = _torch_rope(k, torch.arange(Sk) + k_off, base, rot, layout)
+        krr = kr.repeat_interleave(H // Hkv, dim=1)
+        vr = v.repeat_interleave(H // Hkv, dim=1)
+        s = qr @ krr.transpose(-1, -2) / math.sqrt(D)
+        if causal:
+            allowed = torch.from_numpy(offset_mask(Sq, Sk, q_off, k_off))
+            s = s.masked_fill(~allowed, float("-inf"))
+        o = torch.softmax(s, dim=-1) @ vr
+        (o * dout).sum().backward()
+        kw = dict(q_off=q_off, k_off=k_off, rot_dim=rot, base=base, layout=layout, causal=causal)
+        got = orc.attention_bwd(*arrays, **kw)
+        for g, t in zip(got, (q.grad, k.grad, v.grad)):
+            np.testing.assert_allclose(g, t.numpy(), rtol=0, atol=1e-11)
+        lse = torch.logsumexp(s, dim=-1).detach().numpy()
+        np.testing.assert_allclose(orc.attention_lse(arrays[0], arrays[1], **kw), lse, rtol=0,
+                                   atol=1e-12)
+
+
 ALL_PINS = [v for name, v in sorted(globals().items()) if name.startswith("pin_")]

@@ -33,6 +33,15 @@ MUTATIONS = {
     "pos_div_multiplies": ("((double)p / pos_div)", "((double)p * pos_div)"),
     "pos_div_ignored_for_queries": ("(double)(q_off + r % Sq) / pos_div", "(double)(q_off + r % Sq)"),
     "pos_div_ignored_for_row_keys": ("(double)(k_off + j) / pos_div", "(double)(k_off + j)"),
+    "bwd_q_unrotated_forward": ("-(double)(q_off + i) / pos_div", "(double)(q_off + i) / pos_div"),
+    "bwd_k_unrotated_forward": ("-(double)(k_off + j) / pos_div", "(double)(k_off + j) / pos_div"),
+    "bwd_no_row_correction": ("p[j] * (dp[j] - pdp)", "p[j] * dp[j]"),
+    "bwd_dk_unscaled": ("dkr[j * D + d] += scale * ds * qri[d];", "dkr[j * D + d] += ds * qri[d];"),
+    "bwd_dq_uses_query": ("dqr[d] += scale * ds * krh[j * D + d];", "dqr[d] += scale * ds * qri[d];"),
+    "bwd_unnormalised_p": ("                            p[j] /= l;\n", ""),
+    "bwd_dv_from_dp": ("dvh[j * Dv + e] += p[j] * doi[e];", "dvh[j * Dv + e] += dp[j] * doi[e];"),
+    "bwd_heads_interleaved": ("(kvh % Hkv) * group + g;", "(kvh % Hkv) + g * Hkv;"),
+    "lse_without_log": ("lse[r] = m + log(l);", "lse[r] = m + l;"),
     "kv_head_count_unchecked": ("if (Hkv <= 0 || H % Hkv != 0) return 0;", "if (Hkv <= 0) return 0;"),
 }
 
