@@ -154,6 +154,13 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  *
  *   q, o        [B, H, Sq, head_dim], contiguous, element type `dtype`;
  *               o is written whole and must not alias q, k or v.
+ *   lse         optional fp32 [B, H, Sq], 4-byte aligned, not aliasing the
+ *               other arrays: when non-NULL, lse[b, h, i] receives the
+ *               natural-log log-sum-exp of query row i's scaled scores over
+ *               its visible keys, the saved row normalisation from which
+ *               rope_flash_attn_bwd recomputes the probabilities ([RF]
+ *               section 5: backward reconstructs P from Q/K and saved row
+ *               statistics).
  *   k, v        [B, H_kv, Sk, head_dim], contiguous.  H_kv >= 1 divides H;
  *               query head h reads key/value head h / (H / H_kv): H_kv == H
  *               is multi-head attention, H_kv < H grouped-query attention
@@ -186,7 +193,7 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  *               NULL / too small: one workgroup per query tile (same
  *               result up to floating-point rounding order).
  */
-int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
+int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
                         int64_t q_pos_offset, int64_t k_pos_offset,
                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
@@ -202,6 +209,52 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
 int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int head_dim,
                                        int64_t q_pos_offset, int64_t k_pos_offset, int causal,
                                        int dtype);
+
+/*
+ * rope_flash_attn_bwd -- gradients of rope_flash_attn_fwd: given q, k, v,
+ * the forward's output o and row statistics lse, and the upstream gradient
+ * dout, write dq, dk and dv ([RF] section 5: the backward recomputes the
+ * probabilities from Q, K and the saved row normalisation instead of storing
+ * them; section 8, item 4).  With Q' = R(q_pos) Q, K' = R(k_pos) K and
+ * P = exp(scale Q' K'^T - lse) under the same mask as the forward:
+ *   dv = P^T dout,  dS = P * (dout V^T - rowsum(dout * o)),
+ *   dq = R(q_pos)^T (scale dS K'),  dk = R(k_pos)^T (scale dS^T Q'),
+ * R^T being the rotation by the opposite angle; dk and dv of a key/value
+ * head sum over the query heads that read it.  V is never rotated.
+ *
+ *   q, o, dout  [B, H, Sq, head_dim] bf16, contiguous; o and lse from
+ *               rope_flash_attn_fwd with the same arguments.
+ *   k, v        [B, H_kv, Sk, head_dim] bf16, contiguous (H_kv divides H).
+ *   lse         fp32 [B, H, Sq], 4-byte aligned.
+ *   dq          [B, H, Sq, head_dim] bf16, written whole.
+ *   dk, dv      [B, H_kv, Sk, head_dim] bf16, written whole (keys no query
+ *               sees get zeros).
+ *   The three outputs must not alias each other or any input
+ *   (ROPE_ERR_SHAPE).
+ *   other arguments as rope_flash_attn_fwd; dtype ROPE_BF16, head_dim 64 or
+ *   128, rot_dim 0 or a multiple of 32 (else ROPE_ERR_UNSUPPORTED).
+ *   workspace   device scratch of at least rope_flash_attn_bwd_workspace_size()
+ *               bytes, 16-byte aligned, contents irrelevant (per-row
+ *               rowsum(dout * o)).  Calls that share a workspace must not run
+ *               concurrently.
+ * Three kernels are enqueued on `stream`: the row sums, dk/dv, then dq.
+ * Accumulation is fp32; the rotated Q/K, dout, V, P and dS enter the matrix
+ * cores rounded to bf16.
+ */
+int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                        const float *lse, void *dq, void *dk, void *dv,
+                        int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
+                        int64_t q_pos_offset, int64_t k_pos_offset,
+                        const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                        int rot_dim, int layout, int causal, float softmax_scale, int dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * rope_flash_attn_bwd_workspace_size -- bytes of workspace rope_flash_attn_bwd
+ * needs: B * H * Sq * 4 rounded up to a multiple of 256, or minus a status
+ * code for shapes or types it would reject.  No HIP call.
+ */
+int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_dim, int dtype);
 
 /*
  * rope_decode_attn_fwd -- one decode step over a key/value cache: rotate the

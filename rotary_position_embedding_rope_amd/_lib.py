@@ -16,7 +16,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_BASE, ERR_UNSUPPORTED, ERR_EMPTY_ROW, ERR_TABLE_RAN
 
 # every symbol include/rope_mi355x.h declares
 EXPORTS = ("rope_status_str", "rope_tables_build", "rope_tables_build_scaled", "rope_apply",
-           "rope_flash_attn_fwd",
+           "rope_flash_attn_fwd", "rope_flash_attn_bwd", "rope_flash_attn_bwd_workspace_size",
            "rope_flash_attn_workspace_size", "rope_decode_attn_fwd", "rope_decode_workspace_size")
 
 _lib = None
@@ -41,11 +41,16 @@ def load() -> ctypes.CDLL:
     lib.rope_apply.argtypes = [vp, i64, i64, i32, vp, i64, i64, i32, vp, i64, vp, vp, i64,
                                i32, i32, i32, i32, vp]
     lib.rope_apply.restype = i32
-    lib.rope_flash_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i64, i64,
+    lib.rope_flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i64, i64,
                                         vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     lib.rope_flash_attn_fwd.restype = i32
     lib.rope_flash_attn_workspace_size.argtypes = [i32, i32, i64, i64, i32, i64, i64, i32, i32]
     lib.rope_flash_attn_workspace_size.restype = i64
+    lib.rope_flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32,
+                                        i64, i64, vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
+    lib.rope_flash_attn_bwd.restype = i32
+    lib.rope_flash_attn_bwd_workspace_size.argtypes = [i32, i32, i64, i32, i32]
+    lib.rope_flash_attn_bwd_workspace_size.restype = i64
     lib.rope_decode_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32,
                                          vp, vp, i64, i32, i32, f32, i32, vp, i64, vp]
     lib.rope_decode_attn_fwd.restype = i32

@@ -138,10 +138,13 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,
                    q_pos_offset: int = 0, k_pos_offset: int = 0, rot_dim: int | None = None,
                    layout="neox", causal: bool = True, softmax_scale: float = 0.0,
-                   out: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
+                   out: torch.Tensor | None = None, workspace=None,
+                   lse: torch.Tensor | None = None) -> torch.Tensor:
     """Fused RoPE + attention forward: ``q`` ``[B, H, Sq, D]``, ``k`` and
     ``v`` ``[B, H_kv, Sk, D]`` with H_kv dividing H (query head h reads
-    key/value head h // (H // H_kv)).
+    key/value head h // (H // H_kv)).  ``lse``: optional float32
+    ``[B, H, Sq]`` tensor that receives each query row's log-sum-exp (the
+    row statistics flash_attn_bwd needs).
 
     ``rot_dim=0`` (or no tables) runs plain attention.  Returns ``out``
     (allocated like ``q`` when not given).  ``workspace``: None (one
@@ -172,11 +175,15 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    if lse is not None and (lse.shape != (B, H, Sq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor on q's device")
     if isinstance(workspace, str):
         workspace = workspace_for(q, Sk, q_pos_offset, k_pos_offset, causal)
     wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
     _check(lib.rope_flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None,
                                    B, H, Hkv, Sq, Sk, D, int(q_pos_offset), int(k_pos_offset),
                                    cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),
                                    float(softmax_scale), _dtype(q), wp, wb, _stream(q)),
@@ -190,20 +197,22 @@ def default_scale(head_dim: int) -> float:
 
 def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int = 0,
                            k_pos_offset: int = 0, rot_dim: int | None = None, layout="neox",
-                           causal: bool = True, softmax_scale: float = 0.0, workspace=None):
+                           causal: bool = True, softmax_scale: float = 0.0, workspace=None,
+                           lse=None):
     """Validate once and return a zero-argument callable that enqueues the
     fused forward on fixed buffers (for repeated launches in timing loops;
     the buffers must stay alive and unchanged in shape)."""
     if isinstance(workspace, str):
         workspace = workspace_for(q, k.shape[2], q_pos_offset, k_pos_offset, causal)
     flash_attn_fwd(q, k, v, cos, sin, q_pos_offset, k_pos_offset, rot_dim, layout, causal,
-                   softmax_scale, out, workspace)   # validates and runs once
+                   softmax_scale, out, workspace, lse)   # validates and runs once
     lib = _lib.load()
     B, H, Sq, D = q.shape
     rot = (D if cos is not None else 0) if rot_dim is None else int(rot_dim)
     wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, k.shape[1], Sq, k.shape[2], D,
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, B, H, k.shape[1], Sq, k.shape[2], D,
             int(q_pos_offset), int(k_pos_offset), cos.data_ptr() if rot else None,
             sin.data_ptr() if rot else None, cos.shape[0] if rot else 0, rot, _layout(layout),
             int(bool(causal)), float(softmax_scale), _dtype(q), wp, wb, _stream(q))
@@ -320,4 +329,88 @@ def prepare_decode_attn_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, 
         status = fn(*args)
         if status != _lib.OK:
             raise RopeError(status, "rope_decode_attn_fwd")
+    return launch
+
+
+def bwd_workspace(q: torch.Tensor) -> torch.Tensor:
+    """Workspace for flash_attn_bwd on q's shape, cached per device and grown
+    on demand.  Calls sharing it must be serialised (one stream)."""
+    lib = _lib.load()
+    B, H, Sq, D = q.shape
+    need = lib.rope_flash_attn_bwd_workspace_size(B, H, Sq, D, _dtype(q))
+    if need < 0:
+        raise RopeError(-need, "rope_flash_attn_bwd_workspace_size")
+    key = ("bwd", q.device)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset, rot_dim,
+              layout, causal, softmax_scale, workspace):
+    _require_cuda(q, k, v, o, lse, dout, dq, dk, dv, cos, sin)
+    for t in (q, k, v, o, dout, dq, dk, dv):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o, dout and the gradients must be contiguous 4-D tensors of "
+                             "one dtype on one device")
+    B, H, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Sk, D) or v.shape != k.shape or Hkv < 1 or H % Hkv != 0:
+        raise ValueError("k and v must be [B, H_kv, Sk, D] with H_kv dividing q's H")
+    if o.shape != q.shape or dout.shape != q.shape or dq.shape != q.shape or dk.shape != k.shape \
+            or dv.shape != k.shape:
+        raise ValueError("o, dout, dq must be shaped like q; dk, dv like k")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    if rot_dim is None:
+        rot_dim = D if cos is not None else 0
+    if rot_dim > 0:
+        if cos is None or sin is None or cos.dtype != torch.float32 or not cos.is_contiguous() \
+                or cos.shape != sin.shape or not sin.is_contiguous() or cos.dim() != 2 \
+                or cos.shape[1] != rot_dim // 2:
+            raise ValueError("rotation needs contiguous float32 cos/sin [rows, rot_dim/2]")
+        cp, sp, rows = cos.data_ptr(), sin.data_ptr(), cos.shape[0]
+    else:
+        cp, sp, rows = None, None, 0
+    ws = bwd_workspace(q) if workspace is None else workspace
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Sq, Sk, D, int(q_pos_offset),
+            int(k_pos_offset), cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),
+            float(softmax_scale), _dtype(q), ws.data_ptr(), ws.numel() * ws.element_size(),
+            _stream(q))
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, cos=None, sin=None, q_pos_offset: int = 0,
+                   k_pos_offset: int = 0, rot_dim: int | None = None, layout="neox",
+                   causal: bool = True, softmax_scale: float = 0.0, dq=None, dk=None, dv=None,
+                   workspace=None):
+    """Gradients (dq, dk, dv) of flash_attn_fwd for the upstream gradient
+    ``dout``, from the forward's output ``o`` and row statistics ``lse``
+    (pass the same rotation and mask arguments as to the forward)."""
+    lib = _lib.load()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset,
+                     rot_dim, layout, causal, softmax_scale, workspace)
+    _check(lib.rope_flash_attn_bwd(*args), "rope_flash_attn_bwd")
+    return dq, dk, dv
+
+
+def prepare_flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cos=None, sin=None,
+                           q_pos_offset: int = 0, k_pos_offset: int = 0, rot_dim: int | None = None,
+                           layout="neox", causal: bool = True, softmax_scale: float = 0.0,
+                           workspace=None):
+    """Validate once and return a zero-argument callable that enqueues the
+    backward on fixed buffers."""
+    args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset,
+                     rot_dim, layout, causal, softmax_scale, workspace)
+    fn = _lib.load().rope_flash_attn_bwd
+
+    def launch():
+        status = fn(*args)
+        if status != _lib.OK:
+            raise RopeError(status, "rope_flash_attn_bwd")
     return launch

@@ -143,7 +143,7 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
     return rope_flash_bf16_workspace_bytes(a);
 }
 
-int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
+int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
                         int64_t q_pos_offset, int64_t k_pos_offset,
                         const float *cos_tab, const float *sin_tab, int64_t table_rows,
@@ -167,6 +167,9 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
     if (!q || !k || !v || !o) return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
     if (o == q || o == k || o == v) return ROPE_ERR_SHAPE;
+    if (lse && ((const void *)lse == q || (const void *)lse == k || (const void *)lse == v ||
+                (void *)lse == o))
+        return ROPE_ERR_SHAPE;
     if (causal && q_pos_offset < k_pos_offset) return ROPE_ERR_EMPTY_ROW;
     if (rot_dim > 0) {
         const int64_t need_q = q_pos_offset + Sq, need_k = k_pos_offset + Sk;
@@ -175,6 +178,7 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
     }
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
         return ROPE_ERR_ALIGN;
+    if (lse && !aligned(lse, 4)) return ROPE_ERR_ALIGN;
     if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return ROPE_ERR_SHAPE;
     if (workspace && !aligned(workspace, 16)) return ROPE_ERR_ALIGN;
 
@@ -186,11 +190,73 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o,
     a.rot_dim = rot_dim; a.layout = layout; a.causal = causal ? 1 : 0;
     a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     a.dtype = dtype;
+    a.lse = lse;
     a.workspace = workspace;
     a.workspace_bytes = workspace ? workspace_bytes : 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int rc = dtype == ROPE_BF16 ? rope_launch_flash_bf16(a, s) : rope_launch_flash_f32(a, s);
     return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_dim, int dtype)
+{
+    if (B < 1 || H < 1 || Sq < 1 || Sq > 2147483647) return -ROPE_ERR_SHAPE;
+    if (head_dim < 2 || head_dim % 2 != 0) return -ROPE_ERR_SHAPE;
+    if (dtype != ROPE_BF16 || (head_dim != 64 && head_dim != 128)) return -ROPE_ERR_UNSUPPORTED;
+    return rope_flash_bwd_workspace_bytes(B, H, Sq);
+}
+
+int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                        const float *lse, void *dq, void *dk, void *dv,
+                        int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
+                        int64_t q_pos_offset, int64_t k_pos_offset,
+                        const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                        int rot_dim, int layout, int causal, float softmax_scale, int dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ROPE_ERR_SHAPE;
+    if (H_kv < 1 || H % H_kv != 0) return ROPE_ERR_SHAPE;
+    if (Sq > 2147483647 || Sk > 2147483647) return ROPE_ERR_SHAPE;
+    if (head_dim < 2 || head_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
+    if (q_pos_offset < 0 || k_pos_offset < 0) return ROPE_ERR_SHAPE;
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return ROPE_ERR_SHAPE;
+    if (!valid_layout(layout) || dtype != ROPE_BF16) return ROPE_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return ROPE_ERR_UNSUPPORTED;
+    if (rot_dim % 32 != 0) return ROPE_ERR_UNSUPPORTED;
+    // grids of 128-row tiles; the key/value kernel walks (Sq / 32 + 1) * (H / H_kv) steps
+    if ((int64_t)B * H * ((Sq + 127) / 128) > kMaxGrid || (int64_t)B * H_kv * ((Sk + 127) / 128) > kMaxGrid ||
+        (Sq / 32 + 1) * (int64_t)(H / H_kv) > 2147483647)
+        return ROPE_ERR_SHAPE;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ROPE_ERR_NULL;
+    if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
+    const void *ins[6] = {q, k, v, o, dout, lse};
+    void *outs[3] = {dq, dk, dv};
+    for (void *x : outs)
+        for (const void *y : ins)
+            if (x == y) return ROPE_ERR_SHAPE;
+    if (dq == dk || dq == dv || dk == dv) return ROPE_ERR_SHAPE;
+    if (causal && q_pos_offset < k_pos_offset) return ROPE_ERR_EMPTY_ROW;
+    if (rot_dim > 0) {
+        if (table_rows < q_pos_offset + Sq || table_rows < k_pos_offset + Sk) return ROPE_ERR_TABLE_RANGE;
+        if (!aligned(cos_tab, 16) || !aligned(sin_tab, 16)) return ROPE_ERR_ALIGN;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4))
+        return ROPE_ERR_ALIGN;
+    if (workspace_bytes < rope_flash_bwd_workspace_bytes(B, H, Sq)) return ROPE_ERR_SHAPE;
+
+    FlashBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.B = B; a.H = H; a.H_kv = H_kv; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
+    a.q_off = q_pos_offset; a.k_off = k_pos_offset;
+    a.cos_tab = cos_tab; a.sin_tab = sin_tab;
+    a.rot_dim = rot_dim; a.layout = layout; a.causal = causal ? 1 : 0;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    a.workspace = workspace;
+    return rope_launch_flash_bwd_bf16(a, static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK ? ROPE_OK
+                                                                                              : ROPE_ERR_HIP;
 }
 
 namespace {

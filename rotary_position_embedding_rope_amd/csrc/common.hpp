@@ -81,6 +81,7 @@ struct FlashArgs {
     int rot_dim, layout, causal;
     float scale;   // already resolved (> 0)
     int dtype;
+    float *lse;                // [B, H, Sq] log-sum-exp of each query row, or NULL
     void *workspace;           // zero-filled scratch for the balanced schedule, or NULL
     int64_t workspace_bytes;
 };
@@ -89,6 +90,22 @@ int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream);
 // device (0: the launch needs none).
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a);
 int rope_launch_flash_f32(const FlashArgs &a, hipStream_t stream);
+
+struct FlashBwdArgs {
+    const void *q, *k, *v, *o, *dout;   // q, o, dout [B, H, Sq, D]; k, v [B, H_kv, Sk, D]
+    const float *lse;                   // [B, H, Sq] from the forward
+    void *dq, *dk, *dv;
+    int B, H, H_kv;
+    int64_t Sq, Sk;
+    int head_dim;
+    int64_t q_off, k_off;
+    const float *cos_tab, *sin_tab;
+    int rot_dim, layout, causal;
+    float scale;                        // already resolved (> 0)
+    void *workspace;                    // rope_flash_bwd_workspace_bytes() bytes
+};
+int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream);
+int64_t rope_flash_bwd_workspace_bytes(int B, int H, int64_t Sq);
 
 struct DecodeArgs {
     const void *q, *k_new, *v_new;   // [B, H, D], [B, H_kv, D], [B, H_kv, D]

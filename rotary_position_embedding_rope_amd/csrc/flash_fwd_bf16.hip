@@ -74,10 +74,12 @@ constexpr int BM = 32 * WAVES_PER_GROUP;   // queries per workgroup
 constexpr int KPAD = 8;                     // K LDS row pitch = D + 8 bf16
 constexpr int VP = 160;                     // V LDS row pitch (bf16): 80 dwords, == 16 mod 64 banks
 constexpr float LAZY_THRESHOLD = 8.0f;      // log2 headroom before the reference max is raised
+constexpr float LN2 = 0.6931471805599453f;
 
 struct Params {
     const uint16_t *q, *k, *v;
     uint16_t *o;
+    float *lse;         // [BH, Sq] natural-log log-sum-exp of each row's scores, or null
     int BH;
     int kv_group;       // query heads per key/value head: K/V head of bh is bh / kv_group
     int64_t Sq, Sk, q_off, k_off;
@@ -1148,6 +1150,8 @@ void flash_fwd_bf16_kernel(Params p)
                     wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
                     *reinterpret_cast<uint2 *>(orow + d0) = wv;
                 }
+            // scores are in log2 units against the reference m_fin
+            if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_fin + log2f(l_tot)) * LN2;
         };
 
         if (full) {
@@ -1265,6 +1269,7 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(Params p)
             wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
             *reinterpret_cast<uint2 *>(orow + d0) = wv;
         }
+    if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_acc + log2f(l_sum)) * LN2;
 }
 
 #ifndef ROPE_FLASH_D64_NG
@@ -1348,6 +1353,7 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.k = static_cast<const uint16_t *>(a.k);
     p.v = static_cast<const uint16_t *>(a.v);
     p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
     p.cos_tab = a.cos_tab; p.sin_tab = a.sin_tab; p.rot_dim = a.rot_dim;
     p.table_rows = a.table_rows;
     p.sl2 = a.scale * 1.4426950408889634f;

@@ -22,6 +22,7 @@ constexpr int BN = 32;
 struct F32Params {
     const float *q, *k, *v;
     float *o;
+    float *lse;     // [BH, Sq] natural-log log-sum-exp of each row's scores, or null
     int BH;
     int kv_group;   // query heads per key/value head: K/V head of bh is bh / kv_group
     int64_t Sq, Sk, q_off, k_off;
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(256) void flash_fwd_f32_kernel(F32Params p)
         float *orow = p.o + ((int64_t)bh * p.Sq + qi) * D + part * DP;
 #pragma unroll
         for (int d = 0; d < DP; ++d) orow[d] = acc[d] * inv;
+        if (p.lse && part == 0) p.lse[(int64_t)bh * p.Sq + qi] = (m_run + log2f(l_run)) * 0.6931471805599453f;
     }
 }
 
@@ -161,6 +163,7 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.k = static_cast<const float *>(a.k);
     p.v = static_cast<const float *>(a.v);
     p.o = static_cast<float *>(a.o);
+    p.lse = a.lse;
     p.BH = a.B * a.H;
     p.kv_group = a.H / a.H_kv;
     p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;

@@ -137,12 +137,12 @@ def test_rope_apply_noop_needs_no_device(lib, over):
 
 
 def fwd_args(**over):
-    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, B=1, H=8, Hkv=None, Sq=4096, Sk=4096, D=64, qo=0,
-             ko=0, cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX,
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=None, B=1, H=8, Hkv=None, Sq=4096, Sk=4096, D=64,
+             qo=0, ko=0, cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX,
              causal=1, scale=0.0, dtype=_lib.BF16, ws=None, wsb=0)
     a.update(over)
     hkv = a["H"] if a["Hkv"] is None else a["Hkv"]
-    return [a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], hkv, a["Sq"], a["Sk"], a["D"], a["qo"],
+    return [a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], hkv, a["Sq"], a["Sk"], a["D"], a["qo"],
             a["ko"], a["cos"], a["sin"], a["rows"], a["rot"], a["layout"], a["causal"], a["scale"],
             a["dtype"], a["ws"], a["wsb"], None]
 
@@ -162,6 +162,8 @@ def fwd_args(**over):
     (dict(scale=float("nan")), _lib.ERR_SHAPE),
     (dict(scale=float("inf")), _lib.ERR_SHAPE),
     (dict(o=FAKE), _lib.ERR_SHAPE),             # o aliases q
+    (dict(lse=FAKE4), _lib.ERR_SHAPE),          # lse aliases o
+    (dict(lse=FAKE4 + 0x9002), _lib.ERR_ALIGN),
     (dict(D=192, rot=192), _lib.ERR_UNSUPPORTED),   # D/2 = 96 is not a power of two
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(rot=48), _lib.ERR_UNSUPPORTED),
@@ -265,3 +267,61 @@ def test_decode_workspace_size(lib):
     assert lib.rope_decode_workspace_size(1, 32, 2, 100, 128) == -_lib.ERR_UNSUPPORTED
     # no rotation: tables may be NULL (a bad shape is still reported)
     assert lib.rope_decode_attn_fwd(*decode_args(rot=0, cos=None, sin=None, rows=0, B=0)) == _lib.ERR_SHAPE
+
+
+# --------------------------------------------------------------------------
+# rope_flash_attn_bwd
+
+
+def bwd_args(**over):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, do=FAKE4 + 0x100000, lse=FAKE4 + 0x200000,
+             dq=FAKE4 + 0x300000, dk=FAKE4 + 0x400000, dv=FAKE4 + 0x500000, B=1, H=8, Hkv=8,
+             Sq=4096, Sk=4096, D=64, qo=0, ko=0, cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096,
+             rot=64, layout=_lib.NEOX, causal=1, scale=0.0, dtype=_lib.BF16,
+             ws=FAKE4 + 0x600000, wsb=1 << 20)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "H", "Hkv", "Sq",
+                           "Sk", "D", "qo", "ko", "cos", "sin", "rows", "rot", "layout", "causal",
+                           "scale", "dtype", "ws", "wsb")] + [None]
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(B=0), _lib.ERR_SHAPE),
+    (dict(Hkv=3), _lib.ERR_SHAPE),
+    (dict(Sk=0), _lib.ERR_SHAPE),
+    (dict(D=63), _lib.ERR_SHAPE),
+    (dict(rot=66), _lib.ERR_SHAPE),
+    (dict(qo=-1), _lib.ERR_SHAPE),
+    (dict(scale=float("nan")), _lib.ERR_SHAPE),
+    (dict(dq=FAKE), _lib.ERR_SHAPE),              # dq aliases q
+    (dict(dk=FAKE4 + 0x200000), _lib.ERR_SHAPE),  # dk aliases lse
+    (dict(dv=FAKE4 + 0x300000), _lib.ERR_SHAPE),  # dv aliases dq
+    (dict(wsb=1024), _lib.ERR_SHAPE),             # workspace too small (4096 rows x 8 heads x 4 B)
+    (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=_lib.F16), _lib.ERR_UNSUPPORTED),
+    (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
+    (dict(rot=48), _lib.ERR_UNSUPPORTED),
+    (dict(layout=3), _lib.ERR_UNSUPPORTED),
+    (dict(lse=None), _lib.ERR_NULL),
+    (dict(do=None), _lib.ERR_NULL),
+    (dict(dv=None), _lib.ERR_NULL),
+    (dict(ws=None), _lib.ERR_NULL),
+    (dict(cos=None), _lib.ERR_NULL),
+    (dict(qo=0, ko=1, rows=8192), _lib.ERR_EMPTY_ROW),
+    (dict(rows=4095), _lib.ERR_TABLE_RANGE),
+    (dict(lse=FAKE4 + 0x200002), _lib.ERR_ALIGN),
+    (dict(dk=FAKE4 + 0x400008), _lib.ERR_ALIGN),
+    (dict(ws=FAKE4 + 0x600004), _lib.ERR_ALIGN),
+])
+def test_bwd_rejects(lib, over, want):
+    assert lib.rope_flash_attn_bwd(*bwd_args(**over)) == want
+
+
+def test_bwd_workspace_size(lib):
+    assert lib.rope_flash_attn_bwd_workspace_size(1, 8, 4096, 64, _lib.BF16) == 8 * 4096 * 4
+    assert lib.rope_flash_attn_bwd_workspace_size(2, 3, 5, 128, _lib.BF16) == 256
+    assert lib.rope_flash_attn_bwd_workspace_size(1, 8, 0, 64, _lib.BF16) == -_lib.ERR_SHAPE
+    assert lib.rope_flash_attn_bwd_workspace_size(1, 8, 16, 64, _lib.F32) == -_lib.ERR_UNSUPPORTED
+    # the smallest accepted workspace is accepted: validation then reaches the device
+    # (not called here); one byte less is rejected
+    assert lib.rope_flash_attn_bwd(*bwd_args(wsb=8 * 4096 * 4 - 1)) == _lib.ERR_SHAPE

@@ -1,0 +1,191 @@
+"""GPU parity of the backward (rope_flash_attn_bwd) and of the forward's row
+statistics (lse) against the fp64 oracle.
+
+Bars:
+  * lse: |err_i| <= 2^-8 * scale * |q_i| * max_j |k_j| + 2^-8.  The kernel's
+    scores use Q' * scale * log2(e) and K' rounded to bf16 (relative 2^-9
+    each, so a score moves by at most 2^-8 * scale * |q'||k'|, and rotation
+    keeps norms); the running sum adds bf16-rounded probabilities (2^-9
+    relative, well inside the last 2^-8).
+  * gradients: per tensor, max |err| <= 2e-2 * max |ref| and
+    rms(err) <= 1e-2 * rms(ref).  Every operand of the backward's products
+    (Q', K', V, dO, P, dS) enters the matrix cores rounded to bf16 (2^-9
+    relative), and P is rebuilt from scores that carry the forward's score
+    error (up to 2^-8 * scale * |q||k|, about 0.03 for unit-normal rows of
+    64 dims, so P_ij is off by up to ~3% and by ~1% in RMS); the error the
+    2e-2 forward bar covers.  A gradient element that is a single term (one
+    query row: dk_j = scale ds_j q'_j) keeps that per-element error, so the
+    RMS bar is 1%; sums over many rows average it down.  Both bars add 1e-5
+    absolute for gradients that vanish in exact arithmetic (a single visible
+    key: P = 1 and dS = dO.v - dO.o = 0), where only the fp32 rounding of the
+    two dot products (|dO||v| ~ 10 times 2^-24 per term) remains.
+  * full size: sampled dq rows against the oracle (a row of dq needs only its
+    own query, every key it sees and its upstream gradient), and two exact
+    identities for dk and dv: sum_j dv_j = sum_i dout_i (each row of P sums
+    to 1) and sum_j R(k_pos_j) dk_j = 0 (each row of dS sums to 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rotary_position_embedding_rope_amd import api
+from rotary_position_embedding_rope_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+MAX_REL = 2e-2
+RMS_REL = 1e-2
+ATOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(DEV)
+
+
+def to64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run(w, q, k, v, dout, rot=None, causal=True, pos_div=1.0):
+    """Forward (with lse) and backward on the GPU; returns numpy arrays."""
+    rot = w.rot if rot is None else rot
+    cos = sin = None
+    if rot > 0:
+        cos, sin = api.tables_build(w.base, rot, w.table_rows, device=DEV, pos_divisor=pos_div)
+    tq, tk, tv, tdo = bf16(q), bf16(k), bf16(v), bf16(dout)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    o = api.flash_attn_fwd(tq, tk, tv, cos, sin, w.q_off, w.k_off, rot, w.layout, causal, lse=lse)
+    dq, dk, dv = api.flash_attn_bwd(tq, tk, tv, o, lse, tdo, cos, sin, w.q_off, w.k_off, rot,
+                                    w.layout, causal)
+    torch.cuda.synchronize()
+    return to64(o), to64(lse), to64(dq), to64(dk), to64(dv)
+
+
+def check_grad(got, want, name):
+    err = np.abs(got - want)
+    scale = np.abs(want).max()
+    rms_e, rms_r = np.sqrt(np.mean(err ** 2)), np.sqrt(np.mean(want ** 2))
+    assert err.max() <= MAX_REL * scale + ATOL, (name, float(err.max()), float(scale))
+    assert rms_e <= RMS_REL * rms_r + ATOL, (name, float(rms_e), float(rms_r))
+    return float(err.max() / scale), float(rms_e / rms_r)
+
+
+def lse_bound(q, k, D):
+    scale = 1.0 / np.sqrt(D)
+    qn = np.linalg.norm(q.astype(np.float64), axis=-1)             # [B, H, Sq]
+    kn = np.linalg.norm(k.astype(np.float64), axis=-1).max(axis=-1)  # [B, Hkv]
+    G = q.shape[1] // k.shape[1]
+    kmax = np.repeat(kn, G, axis=1)[..., None]
+    return 2.0 ** -8 * scale * qn * kmax + 2.0 ** -8
+
+
+def inputs(w, seed_extra=0):
+    q, k, v = wl.attention_inputs(w)
+    rng = np.random.default_rng(w.seed + 1000 + seed_extra)
+    dout = wl.round_to(rng.standard_normal(q.shape), "bf16")
+    return q, k, v, dout
+
+
+# (name, B, H, Hkv, Sq, Sk, D, layout, rot, q_off, causal)
+CASES = [
+    ("causal_neox_64", 1, 2, 2, 256, 256, 64, "neox", 64, 0, True),
+    ("causal_gptj_128", 1, 2, 2, 200, 200, 128, "gptj", 128, 0, True),
+    ("gqa_4to1_64", 1, 8, 2, 160, 160, 64, "neox", 64, 0, True),
+    ("chunked_offset_128", 1, 4, 2, 96, 416, 128, "neox", 128, 320, True),
+    ("partial_rot_128", 2, 2, 1, 130, 130, 128, "neox", 64, 0, True),
+    ("partial_rot32_64_gptj", 1, 3, 3, 70, 70, 64, "gptj", 32, 0, True),
+    ("rot96_128_gptj", 1, 2, 2, 64, 64, 128, "gptj", 96, 0, True),
+    ("no_rotation_64", 1, 2, 1, 100, 100, 64, "neox", 0, 0, True),
+    ("not_causal_64", 1, 2, 2, 77, 150, 64, "neox", 64, 0, False),
+    ("not_causal_128_gqa", 2, 4, 1, 33, 65, 128, "gptj", 128, 0, False),
+    ("one_query_row", 1, 2, 2, 1, 300, 64, "neox", 64, 299, True),
+    ("one_key", 1, 2, 1, 40, 1, 128, "neox", 128, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_backward_full(orc, case):
+    name, B, H, Hkv, Sq, Sk, D, layout, rot, q_off, causal = case
+    w = wl.AttentionWorkload(name, B, H, Sq, Sk, D, "bf16", 500 + Sq + D, layout, base=1e4,
+                             q_off=q_off, H_kv=Hkv)
+    q, k, v, dout = inputs(w)
+    o, lse, dq, dk, dv = run(w, q, k, v, dout, rot=rot, causal=causal)
+    kw = dict(q_off=q_off, k_off=0, rot_dim=rot, base=w.base, layout=layout, causal=causal)
+    lse_ref = orc.attention_lse(q, k, **kw)
+    assert (np.abs(lse - lse_ref) <= lse_bound(q, k, D)).all()
+    rq, rk, rv = orc.attention_bwd(q, k, v, dout, **kw)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+def test_keys_no_query_sees_get_zero_gradients(orc):
+    """Causal with the keys running past the last query's position: those
+    keys' dk and dv are exactly zero."""
+    w = wl.AttentionWorkload("unseen_keys", 1, 2, 64, 300, 64, "bf16", 77, "neox", base=1e4,
+                             q_off=100, H_kv=2)
+    q, k, v, dout = inputs(w)
+    _, _, dq, dk, dv = run(w, q, k, v, dout)
+    # query rows sit at 100..163: keys 164.. are seen by no query
+    assert not dk[:, :, 164:].any() and not dv[:, :, 164:].any()
+    rq, rk, rv = orc.attention_bwd(q, k, v, dout, q_off=100, base=w.base, layout="neox")
+    check_grad(dk, rk, "dk")
+    check_grad(dq, rq, "dq")
+
+
+def test_backward_interpolated_positions(orc):
+    """Position interpolation tables: the backward rotates and un-rotates at
+    the divided positions, like the forward."""
+    w = wl.AttentionWorkload("pi_bwd", 1, 4, 150, 150, 64, "bf16", 79, "gptj", base=5e5, H_kv=2)
+    q, k, v, dout = inputs(w)
+    _, _, dq, dk, dv = run(w, q, k, v, dout, pos_div=4.0)
+    rq, rk, rv = orc.attention_bwd(q, k, v, dout, base=w.base, layout="gptj", pos_div=4.0)
+    for g, r, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        check_grad(g, r, n)
+
+
+def test_backward_deterministic():
+    """No atomics: two runs give the same bits."""
+    w = wl.SMALL_BF16
+    q, k, v, dout = inputs(w)
+    a = run(w, q, k, v, dout)
+    b = run(w, q, k, v, dout)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("w", [wl.HEADLINE, wl.PREFILL_GQA], ids=lambda w: w.name)
+def test_backward_full_size_sampled(orc, w):
+    """The bench workloads' shapes: sampled dq rows against the oracle, and
+    the two exact identities for dk and dv."""
+    q, k, v, dout = inputs(w)
+    o, lse, dq, dk, dv = run(w, q, k, v, dout)
+    rng = np.random.default_rng(5)
+    rows = [0, w.Sq - 1] + list(rng.integers(0, w.Sq, size=6))
+    for i in rows:
+        h = int(rng.integers(0, w.H))
+        sl = slice(h, h + 1)
+        kv = h // (w.H // w.Hkv)
+        rq, _, _ = orc.attention_bwd(q[:, sl, i:i + 1], k[:, kv:kv + 1], v[:, kv:kv + 1],
+                                     dout[:, sl, i:i + 1], q_off=w.q_off + i, k_off=w.k_off,
+                                     base=w.base, layout=w.layout)
+        err = np.abs(dq[:, sl, i:i + 1] - rq).max()
+        assert err <= MAX_REL * max(np.abs(rq).max(), np.abs(dq).max() * 0.1), (i, h, float(err))
+    G = w.H // w.Hkv
+    # sum over keys of dv equals the sum over rows of dout (per kv head: all its query heads)
+    sdv = dv.sum(axis=2)
+    sdo = dout.reshape(w.B, w.Hkv, G, w.Sq, w.D).sum(axis=(2, 3))
+    tol = 2e-2 * np.abs(dv).sum(axis=2).max()
+    assert np.abs(sdv - sdo).max() <= tol
+    # sum over keys of the rotated dk is zero
+    kpos = w.k_off + np.arange(w.Sk)
+    rot_dk = orc.rope(dk, np.broadcast_to(kpos, dk.shape[:3]), base=w.base, layout=w.layout)
+    s = rot_dk.sum(axis=2)
+    assert np.abs(s).max() <= 2e-2 * np.abs(dk).sum(axis=2).max()
