@@ -64,7 +64,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "copy"], default="all",
+    ap.add_argument("--bwd-steps", type=int, default=30)
+    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "backward", "copy"],
+                    default="all",
                     help="restrict the timed kernels (for profiler runs); 'copy' runs only a "
                          "plain 256 MiB device copy, the calibration for HBM byte counters")
     ap.add_argument("--sweep", action="store_true",
@@ -172,6 +174,37 @@ def bench_rope_apply(torch, api, wl, steps, sets, w=None):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": nbytes},
+    }
+
+
+def bench_backward(torch, api, wl, steps, warmup):
+    """The backward of the fused forward on the bench workload: one step is
+    the three kernels of rope_flash_attn_bwd (row sums, dK/dV, dQ), inputs
+    and the forward's output and row statistics resident in HBM."""
+    w = wl.HEADLINE
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in wl.attention_inputs(w))
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 1000)
+    dout = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+    cos, sin = api.tables_build(w.base, w.rot, w.table_rows, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    o = api.flash_attn_fwd(q, k, v, cos, sin, w.q_off, w.k_off, w.rot, w.layout, w.causal, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    launch = api.prepare_flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, w.q_off, w.k_off,
+                                        w.rot, w.layout, w.causal)
+    stream = torch.cuda.current_stream(dev)
+    ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
+    flops = w.bwd_flops()
+    tf = flops / (kernel_ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "value": round(tf, 2), "unit": "TFLOP/s",
+        "ms_per_step": round(kernel_ms, 5), "wall_ms_per_step": round(ms_step, 5),
+        "single_step_p10_ms": round(durs[len(durs) // 10], 5),
+        "single_step_p90_ms": round(durs[(9 * len(durs)) // 10], 5),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": flops},
     }
 
 
@@ -352,6 +385,8 @@ def main():
         rf = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets, w=wl.RAGGED_ROPE_F16)
         result["rope_apply"]["f16"] = {k: rf[k] for k in ("workload", "value", "unit", "ms_per_launch")}
         result["rope_apply"]["f16"]["frac"] = rf["roofline"]["frac"]
+    if args.only in ("all", "backward"):
+        result["backward"] = bench_backward(torch, api, wl, args.bwd_steps, max(args.warmup // 4, 3))
     if args.only in ("all", "decode"):
         result["decode"] = bench_decode(torch, api, wl, args.decode_steps, max(args.warmup // 4, 3))
     if args.sweep:

@@ -107,10 +107,10 @@ struct Unit {
     float4 c0, c1, s0, s1;      // cos / sin of the unit's frequencies
 };
 
-template <int D, int LAYOUT, int ROTD, int ROWS>
+template <int D, int LAYOUT, int ROTD, int ROWS, int NTH>
 struct Stager {
     using G = Geo<D, LAYOUT, ROTD>;
-    static constexpr int NU = (ROWS * G::UPR + 255) / 256;
+    static constexpr int NU = (ROWS * G::UPR + NTH - 1) / NTH;
     Unit u[NU];
 
     // rows [0, valid) of src (row r at src + r D, position pos0 + r); the
@@ -120,7 +120,7 @@ struct Stager {
     {
 #pragma unroll
         for (int n = 0; n < NU; ++n) {
-            const int id = tid + 256 * n;
+            const int id = tid + NTH * n;
             const int r = id / G::UPR, k = id % G::UPR;
             Unit &x = u[n];
             x.a = x.b = make_uint4(0, 0, 0, 0);
@@ -154,7 +154,7 @@ struct Stager {
     {
 #pragma unroll
         for (int n = 0; n < NU; ++n) {
-            const int id = tid + 256 * n;
+            const int id = tid + NTH * n;
             if (id >= ROWS * G::UPR) continue;
             const int r = id / G::UPR, k = id % G::UPR;
             const Unit &x = u[n];
@@ -360,25 +360,52 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const
     if (c == 0 && r < rows) delta[r] = acc;
 }
 
+// The halves of a workgroup: NH = 2 for D = 64 (8 waves, two per SIMD: the
+// halves take alternate 32-row steps and are summed at the end), NH = 1 for
+// D = 128 (its accumulators leave room for one wave per SIMD).
+template <int D> struct Halves { static constexpr int NH = D == 64 ? 2 : 1; };
+
+// Half 1's accumulators added into half 0's through LDS (`buf`, at least
+// 4 waves x 64 lanes x 16 floats), one block of 16 at a time; ends with the
+// sum in half 0.
+template <int DB>
+__device__ __forceinline__ void fold_halves(f32x16_t (&acc)[DB], float *buf, int half, int wv, int lane)
+{
+#pragma unroll
+    for (int bd = 0; bd < DB; ++bd) {
+        __syncthreads();
+        if (half == 1)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) buf[(wv * 16 + r) * 64 + lane] = acc[bd][r];
+        __syncthreads();
+        if (half == 0)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[bd][r] += buf[(wv * 16 + r) * 64 + lane];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV: 128 keys of one (batch, key/value head) per workgroup.
 template <int D, int LAYOUT, int ROTD>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
+__global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dkv_kernel(BwdParams p)
 {
+    constexpr int NH = Halves<D>::NH, NTH = 256 * NH, ROWS = TILE * NH;
     constexpr int P = D + 8;   // LDS row pitch (bf16)
     constexpr int NS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][TILE * P];
-    __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][TILE * P];
-    __shared__ __attribute__((aligned(16))) float lse_lds[2][TILE];
-    __shared__ __attribute__((aligned(16))) float dl_lds[2][TILE];
+    static_assert(2 * ROWS * P * 2 >= 4 * 64 * 16 * 4 || NH == 1, "LDS for the fold");
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][ROWS * P];
+    __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][ROWS * P];
+    __shared__ __attribute__((aligned(16))) float lse_lds[2][ROWS];
+    __shared__ __attribute__((aligned(16))) float dl_lds[2][ROWS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = wave >> 2, wv = wave & 3;   // this wave's half and its place in it
     const int l32 = lane & 31, hh = lane >> 5;
     const int BKV = p.B * p.Hkv;
     const int bkv = blockIdx.x % BKV;                  // a head's workgroups share an XCD
     const int kt = blockIdx.x / BKV;                   // the first key tiles see the most queries
     const int b = bkv / p.Hkv, kvh = bkv % p.Hkv;
-    const int64_t key = (int64_t)kt * WG_ROWS + wave * WROWS + l32;   // this lane's key
+    const int64_t key = (int64_t)kt * WG_ROWS + wv * WROWS + l32;   // this lane's key
     const bool kvalid = key < p.Sk;
     const int g16 = lane >> 4, lp = lane & 15;
     const int tr_row0 = 4 * (g16 >> 1) + (lp >> 2), tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
@@ -397,22 +424,22 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
     if (p.causal) {
         i0 = p.k_off + (int64_t)kt * WG_ROWS - p.q_off;
         if (i0 < 0) i0 = 0;
-        i0 = i0 / TILE * TILE;
+        i0 = i0 / ROWS * ROWS;
     }
-    const int nsteps = i0 < p.Sq ? (int)((p.Sq - i0 + TILE - 1) / TILE) : 0;
+    const int nsteps = i0 < p.Sq ? (int)((p.Sq - i0 + ROWS - 1) / ROWS) : 0;
     const int total = nsteps * p.kv_group;
 
-    Stager<D, LAYOUT, ROTD, TILE> qst;
-    Stager<D, 0, 0, TILE> dost;
-    float lse_r = 0.f, dl_r = 0.f;   // thread tid < TILE: row tid of the tile
+    Stager<D, LAYOUT, ROTD, ROWS, NTH> qst;
+    Stager<D, 0, 0, ROWS, NTH> dost;
+    float lse_r = 0.f, dl_r = 0.f;   // thread tid < ROWS: row tid of the tile
     auto fetch = [&](int t) {
         const int g = t / nsteps;
-        const int64_t i = i0 + (int64_t)(t % nsteps) * TILE;
+        const int64_t i = i0 + (int64_t)(t % nsteps) * ROWS;
         const int64_t bh = (int64_t)b * p.H + kvh * p.kv_group + g;
-        const int valid = p.Sq - i < TILE ? (int)(p.Sq - i) : TILE;
+        const int valid = p.Sq - i < ROWS ? (int)(p.Sq - i) : ROWS;
         qst.fetch(p.q + (bh * p.Sq + i) * D, valid, p.q_off + i, p.cos_tab, p.sin_tab, tid);
         dost.fetch(p.dout + (bh * p.Sq + i) * D, valid, 0, nullptr, nullptr, tid);
-        if (tid < TILE) {
+        if (tid < ROWS) {
             const bool ok = tid < valid;
             lse_r = ok ? p.lse[bh * p.Sq + i + tid] * LOG2E : INFINITY;   // invalid rows: P = 0
             dl_r = ok ? p.delta[bh * p.Sq + i + tid] : 0.f;
@@ -421,7 +448,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
     auto store = [&](int buf) {
         qst.template store<P>(q_lds[buf], p.sl2, tid);
         dost.template store<P>(do_lds[buf], 1.f, tid);
-        if (tid < TILE) {
+        if (tid < ROWS) {
             lse_lds[buf][tid] = lse_r;
             dl_lds[buf][tid] = dl_r;
         }
@@ -435,21 +462,24 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
     }
     for (int t = 0; t < total; ++t) {
         const int buf = t & 1;
-        const int64_t i = i0 + (int64_t)(t % nsteps) * TILE;
+        // this half's 32 rows of the tile
+        const int64_t i = i0 + (int64_t)(t % nsteps) * ROWS + TILE * half;
+        const uint16_t *qt_lds = q_lds[buf] + TILE * half * P, *dot_lds = do_lds[buf] + TILE * half * P;
+        const float *lse_h = lse_lds[buf] + TILE * half, *dl_h = dl_lds[buf] + TILE * half;
         // S (queries x keys) and dP = dO V^T: a lane owns key column l32
         f32x16_t s = {}, dp = {};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(q_lds[buf] + l32 * P + 16 * st + 8 * hh);
+            const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(qt_lds + l32 * P + 16 * st + 8 * hh);
             s = mfma(aq, kb[st], s);
-            const bf16x8_t ao = *reinterpret_cast<const bf16x8_t *>(do_lds[buf] + l32 * P + 16 * st + 8 * hh);
+            const bf16x8_t ao = *reinterpret_cast<const bf16x8_t *>(dot_lds + l32 * P + 16 * st + 8 * hh);
             dp = mfma(ao, vb[st], dp);
         }
         float pv[16], dsv[16];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const float4 l4 = *reinterpret_cast<const float4 *>(&lse_lds[buf][8 * ii + 4 * hh]);
-            const float4 d4 = *reinterpret_cast<const float4 *>(&dl_lds[buf][8 * ii + 4 * hh]);
+            const float4 l4 = *reinterpret_cast<const float4 *>(lse_h + 8 * ii + 4 * hh);
+            const float4 d4 = *reinterpret_cast<const float4 *>(dl_h + 8 * ii + 4 * hh);
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -466,8 +496,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
             const bf16x8_t bp = acc_operand(pv, mm), bs = acc_operand(dsv, mm);
 #pragma unroll
             for (int bd = 0; bd < DB; ++bd) {
-                dv[bd] = mfma(tr_operand<P>(do_lds[buf], mm, bd, tr_row0, tr_col), bp, dv[bd]);
-                dk[bd] = mfma(tr_operand<P>(q_lds[buf], mm, bd, tr_row0, tr_col), bs, dk[bd]);
+                dv[bd] = mfma(tr_operand<P>(dot_lds, mm, bd, tr_row0, tr_col), bp, dv[bd]);
+                dk[bd] = mfma(tr_operand<P>(qt_lds, mm, bd, tr_row0, tr_col), bs, dk[bd]);
             }
         }
         if (t + 1 < total) store(buf ^ 1);
@@ -475,7 +505,12 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
         __syncthreads();
     }
 
-    if (!kvalid) return;
+    if constexpr (NH == 2) {
+        float *xbuf = reinterpret_cast<float *>(&q_lds[0][0]);
+        fold_halves<DB>(dk, xbuf, half, wv, lane);
+        fold_halves<DB>(dv, xbuf, half, wv, lane);
+    }
+    if (half != 0 || !kvalid) return;
     // dK' = scale dS^T Q' = ln 2 * (dS^T (scale log2(e) Q')), then back to K's frame
     unrotate<D, LAYOUT, ROTD>(dk, p.k_off + key, p.cos_tab, p.sin_tab, hh);
     store_row<D>(p.dk + ((int64_t)bkv * p.Sk + key) * D, dk, LN2, hh);
@@ -485,19 +520,21 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p)
 // ---------------------------------------------------------------------------
 // dQ: 128 query rows of one (batch, head) per workgroup.
 template <int D, int LAYOUT, int ROTD>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p)
+__global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dq_kernel(BwdParams p)
 {
+    constexpr int NH = Halves<D>::NH, NTH = 256 * NH, ROWS = TILE * NH;
     constexpr int P = D + 8;
     constexpr int NS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][TILE * P];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TILE * P];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][ROWS * P];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][ROWS * P];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = wave >> 2, wv = wave & 3;
     const int l32 = lane & 31, hh = lane >> 5;
     const int BH = p.B * p.H;
     const int bh = blockIdx.x % BH;
     const int qt = p.n_qtiles - 1 - blockIdx.x / BH;   // with the causal mask the last tiles are heaviest
-    const int64_t qi = (int64_t)qt * WG_ROWS + wave * WROWS + l32;   // this lane's query row
+    const int64_t qi = (int64_t)qt * WG_ROWS + wv * WROWS + l32;   // this lane's query row
     const bool qvalid = qi < p.Sq;
     const int64_t bkv = bh / p.kv_group;
     const int g16 = lane >> 4, lp = lane & 15;
@@ -520,14 +557,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p)
         const int64_t vis = p.q_off + last - p.k_off + 1;
         nk = vis < nk ? vis : nk;
     }
-    const int total = nk > 0 ? (int)((nk + TILE - 1) / TILE) : 0;
+    const int total = nk > 0 ? (int)((nk + ROWS - 1) / ROWS) : 0;
 
-    Stager<D, LAYOUT, ROTD, TILE> kst;
-    Stager<D, 0, 0, TILE> vst;
+    Stager<D, LAYOUT, ROTD, ROWS, NTH> kst;
+    Stager<D, 0, 0, ROWS, NTH> vst;
     const uint16_t *kh = p.k + bkv * p.Sk * D, *vh = p.v + bkv * p.Sk * D;
     auto fetch = [&](int t) {
-        const int64_t j = (int64_t)t * TILE;
-        const int valid = p.Sk - j < TILE ? (int)(p.Sk - j) : TILE;
+        const int64_t j = (int64_t)t * ROWS;
+        const int valid = p.Sk - j < ROWS ? (int)(p.Sk - j) : ROWS;
         kst.fetch(kh + j * D, valid, p.k_off + j, p.cos_tab, p.sin_tab, tid);
         vst.fetch(vh + j * D, valid, 0, nullptr, nullptr, tid);
     };
@@ -544,14 +581,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p)
     }
     for (int t = 0; t < total; ++t) {
         const int buf = t & 1;
-        const int64_t j0 = (int64_t)t * TILE;
+        // this half's 32 keys of the tile
+        const int64_t j0 = (int64_t)t * ROWS + TILE * half;
+        const uint16_t *kt_lds = k_lds[buf] + TILE * half * P, *vt_lds = v_lds[buf] + TILE * half * P;
         // S^T (keys x queries) and dP^T = V dO^T: a lane owns query column l32
         f32x16_t s = {}, dp = {};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(k_lds[buf] + l32 * P + 16 * st + 8 * hh);
+            const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(kt_lds + l32 * P + 16 * st + 8 * hh);
             s = mfma(ak, qb[st], s);
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(v_lds[buf] + l32 * P + 16 * st + 8 * hh);
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(vt_lds + l32 * P + 16 * st + 8 * hh);
             dp = mfma(av, ob[st], dp);
         }
         float dsv[16];
@@ -568,14 +607,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p)
             const bf16x8_t bs = acc_operand(dsv, mm);
 #pragma unroll
             for (int bd = 0; bd < DB; ++bd)
-                dq[bd] = mfma(tr_operand<P>(k_lds[buf], mm, bd, tr_row0, tr_col), bs, dq[bd]);
+                dq[bd] = mfma(tr_operand<P>(kt_lds, mm, bd, tr_row0, tr_col), bs, dq[bd]);
         }
         if (t + 1 < total) store(buf ^ 1);
         if (t + 2 < total) fetch(t + 2);
         __syncthreads();
     }
 
-    if (!qvalid) return;
+    if constexpr (NH == 2) fold_halves<DB>(dq, reinterpret_cast<float *>(&k_lds[0][0]), half, wv, lane);
+    if (half != 0 || !qvalid) return;
     // dQ' = scale dS K', then back to Q's frame
     unrotate<D, LAYOUT, ROTD>(dq, p.q_off + qi, p.cos_tab, p.sin_tab, hh);
     store_row<D>(p.dq + ((int64_t)bh * p.Sq + qi) * D, dq, p.scale, hh);
@@ -589,11 +629,12 @@ int launch_all(const BwdParams &p, hipStream_t stream)
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
                        p.o, p.dout, p.delta, rows);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
+    constexpr int NTH = 256 * Halves<D>::NH;
     hipLaunchKernelGGL((bwd_dkv_kernel<D, LAYOUT, ROTD>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.n_ktiles)),
-                       dim3(256), 0, stream, p);
+                       dim3(NTH), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     hipLaunchKernelGGL((bwd_dq_kernel<D, LAYOUT, ROTD>), dim3((unsigned)((int64_t)p.B * p.H * p.n_qtiles)),
-                       dim3(256), 0, stream, p);
+                       dim3(NTH), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 

@@ -103,6 +103,11 @@ class AttentionWorkload:
         """Algorithmic flops: 4*D per visible pair (QK^T and PV, 2 each)."""
         return 4 * self.D * self.visible_pairs()
 
+    def bwd_flops(self) -> int:
+        """Algorithmic flops of the backward: 10*D per visible pair (the
+        scores rebuilt, dP = dO V^T, dV, dK and dQ, 2*D each)."""
+        return 10 * self.D * self.visible_pairs()
+
     def label(self) -> str:
         kv = "" if self.Hkv == self.H else f"({self.Hkv}kv)"
         return f"{self.B}x{self.H}{kv}x{self.Sq}x{self.Sk}x{self.D}"
