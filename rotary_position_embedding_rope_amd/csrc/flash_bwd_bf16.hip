@@ -384,26 +384,37 @@ __device__ __forceinline__ void fold_halves(f32x16_t (&acc)[DB], float *buf, int
     }
 }
 
+// LDS of a workgroup: two double-buffered [ROWS][D + 8] bf16 tiles and two
+// double-buffered rows of ROWS floats.
+template <int D>
+struct Lds {
+    static constexpr int ROWS = TILE * Halves<D>::NH, P = D + 8;
+    static constexpr int TILE_ELEMS = ROWS * P;
+    static constexpr int BYTES = 4 * TILE_ELEMS * 2 + 4 * ROWS * 4;
+    static_assert(2 * TILE_ELEMS * 2 >= 4 * 64 * 16 * 4 || Halves<D>::NH == 1, "LDS for the fold");
+};
+
 // ---------------------------------------------------------------------------
-// dK, dV: 128 keys of one (batch, key/value head) per workgroup.
+// dK, dV: 128 keys of one (batch, key/value head) per workgroup; blk orders
+// the tiles heaviest first (with the causal mask the first keys see the most
+// queries).
 template <int D, int LAYOUT, int ROTD>
-__global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dkv_kernel(BwdParams p)
+__device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned char *smem)
 {
     constexpr int NH = Halves<D>::NH, NTH = 256 * NH, ROWS = TILE * NH;
     constexpr int P = D + 8;   // LDS row pitch (bf16)
-    constexpr int NS = D / 16, DB = D / 32;
-    static_assert(2 * ROWS * P * 2 >= 4 * 64 * 16 * 4 || NH == 1, "LDS for the fold");
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][ROWS * P];
-    __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][ROWS * P];
-    __shared__ __attribute__((aligned(16))) float lse_lds[2][ROWS];
-    __shared__ __attribute__((aligned(16))) float dl_lds[2][ROWS];
+    constexpr int NS = D / 16, DB = D / 32, TE = Lds<D>::TILE_ELEMS;
+    uint16_t(*q_lds)[TE] = reinterpret_cast<uint16_t(*)[TE]>(smem);
+    uint16_t(*do_lds)[TE] = reinterpret_cast<uint16_t(*)[TE]>(smem + 2 * TE * 2);
+    float(*lse_lds)[ROWS] = reinterpret_cast<float(*)[ROWS]>(smem + 4 * TE * 2);
+    float(*dl_lds)[ROWS] = reinterpret_cast<float(*)[ROWS]>(smem + 4 * TE * 2 + 2 * ROWS * 4);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = wave >> 2, wv = wave & 3;   // this wave's half and its place in it
     const int l32 = lane & 31, hh = lane >> 5;
     const int BKV = p.B * p.Hkv;
-    const int bkv = blockIdx.x % BKV;                  // a head's workgroups share an XCD
-    const int kt = blockIdx.x / BKV;                   // the first key tiles see the most queries
+    const int bkv = blk % BKV;
+    const int kt = blk / BKV;
     const int b = bkv / p.Hkv, kvh = bkv % p.Hkv;
     const int64_t key = (int64_t)kt * WG_ROWS + wv * WROWS + l32;   // this lane's key
     const bool kvalid = key < p.Sk;
@@ -475,6 +486,13 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dkv_kernel(BwdParams 
             const bf16x8_t ao = *reinterpret_cast<const bf16x8_t *>(dot_lds + l32 * P + 16 * st + 8 * hh);
             dp = mfma(ao, vb[st], dp);
         }
+        // the mask only where the diagonal crosses the wave's 32 x 32 block:
+        // row offset r sees this lane's key iff r >= thr
+        int thr = -1;
+        if (p.causal && p.k_off + kt * (int64_t)WG_ROWS + wv * WROWS + WROWS - 1 > p.q_off + i) {
+            const int64_t t64 = p.k_off + key - p.q_off - i;
+            thr = t64 < -1 ? -1 : (t64 > WROWS ? WROWS : (int)t64);
+        }
         float pv[16], dsv[16];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -483,9 +501,8 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dkv_kernel(BwdParams 
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t qi = i + 8 * ii + 4 * hh + j;
-                const bool ok = !p.causal || p.k_off + key <= p.q_off + qi;
-                const float pr = ok ? __builtin_amdgcn_exp2f(s[4 * ii + j] - lv[j]) : 0.f;
+                const float e = __builtin_amdgcn_exp2f(s[4 * ii + j] - lv[j]);
+                const float pr = 8 * ii + 4 * hh + j >= thr ? e : 0.f;
                 pv[4 * ii + j] = pr;
                 dsv[4 * ii + j] = pr * (dp[4 * ii + j] - dv4[j]);
             }
@@ -506,7 +523,7 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dkv_kernel(BwdParams 
     }
 
     if constexpr (NH == 2) {
-        float *xbuf = reinterpret_cast<float *>(&q_lds[0][0]);
+        float *xbuf = reinterpret_cast<float *>(smem);
         fold_halves<DB>(dk, xbuf, half, wv, lane);
         fold_halves<DB>(dv, xbuf, half, wv, lane);
     }
@@ -518,22 +535,23 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dkv_kernel(BwdParams 
 }
 
 // ---------------------------------------------------------------------------
-// dQ: 128 query rows of one (batch, head) per workgroup.
+// dQ: 128 query rows of one (batch, head) per workgroup; blk orders the tiles
+// heaviest first (with the causal mask the last rows see the most keys).
 template <int D, int LAYOUT, int ROTD>
-__global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dq_kernel(BwdParams p)
+__device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned char *smem)
 {
     constexpr int NH = Halves<D>::NH, NTH = 256 * NH, ROWS = TILE * NH;
     constexpr int P = D + 8;
-    constexpr int NS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][ROWS * P];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][ROWS * P];
+    constexpr int NS = D / 16, DB = D / 32, TE = Lds<D>::TILE_ELEMS;
+    uint16_t(*k_lds)[TE] = reinterpret_cast<uint16_t(*)[TE]>(smem);
+    uint16_t(*v_lds)[TE] = reinterpret_cast<uint16_t(*)[TE]>(smem + 2 * TE * 2);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = wave >> 2, wv = wave & 3;
     const int l32 = lane & 31, hh = lane >> 5;
     const int BH = p.B * p.H;
-    const int bh = blockIdx.x % BH;
-    const int qt = p.n_qtiles - 1 - blockIdx.x / BH;   // with the causal mask the last tiles are heaviest
+    const int bh = blk % BH;
+    const int qt = p.n_qtiles - 1 - blk / BH;
     const int64_t qi = (int64_t)qt * WG_ROWS + wv * WROWS + l32;   // this lane's query row
     const bool qvalid = qi < p.Sq;
     const int64_t bkv = bh / p.kv_group;
@@ -593,12 +611,20 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dq_kernel(BwdParams p
             const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(vt_lds + l32 * P + 16 * st + 8 * hh);
             dp = mfma(av, ob[st], dp);
         }
+        // key offset c of the block is visible iff c <= lim: the mask only
+        // where the diagonal or the end of the keys crosses the wave's block
+        int lim = WROWS;
+        if (j0 + WROWS > p.Sk ||
+            (p.causal && p.k_off + j0 + WROWS - 1 > p.q_off + (int64_t)qt * WG_ROWS + wv * WROWS)) {
+            int64_t l64 = p.Sk - 1 - j0;
+            if (p.causal && p.q_off + qi - p.k_off - j0 < l64) l64 = p.q_off + qi - p.k_off - j0;
+            lim = l64 < -1 ? -1 : (l64 > WROWS ? WROWS : (int)l64);
+        }
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t kj = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = kj < p.Sk && (!p.causal || p.k_off + kj <= p.q_off + qi);
-            const float pr = ok ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;
+            const float e = __builtin_amdgcn_exp2f(s[r] - lse2);
+            const float pr = 8 * (r >> 2) + 4 * hh + (r & 3) <= lim ? e : 0.f;
             dsv[r] = pr * (dp[r] - dl);
         }
         // dQ^T += K'^T dS
@@ -614,11 +640,30 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_dq_kernel(BwdParams p
         __syncthreads();
     }
 
-    if constexpr (NH == 2) fold_halves<DB>(dq, reinterpret_cast<float *>(&k_lds[0][0]), half, wv, lane);
+    if constexpr (NH == 2) fold_halves<DB>(dq, reinterpret_cast<float *>(smem), half, wv, lane);
     if (half != 0 || !qvalid) return;
     // dQ' = scale dS K', then back to Q's frame
     unrotate<D, LAYOUT, ROTD>(dq, p.q_off + qi, p.cos_tab, p.sin_tab, hh);
     store_row<D>(p.dq + ((int64_t)bh * p.Sq + qi) * D, dq, p.scale, hh);
+}
+
+// dK/dV and dQ workgroups in one launch: the two lists, each heaviest first,
+// interleaved, so that light tiles of one fill in around heavy tiles of the
+// other (with the causal mask the heavy dK/dV tiles are the light dQ tiles).
+template <int D, int LAYOUT, int ROTD>
+__global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_main_kernel(BwdParams p, int n_dkv, int n_dq)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<D>::BYTES];
+    const int blk = blockIdx.x;
+    const int m = n_dkv < n_dq ? n_dkv : n_dq;
+    if (blk < 2 * m) {
+        if (blk & 1) dq_block<D, LAYOUT, ROTD>(p, blk >> 1, smem);
+        else dkv_block<D, LAYOUT, ROTD>(p, blk >> 1, smem);
+    } else if (n_dkv > n_dq) {
+        dkv_block<D, LAYOUT, ROTD>(p, blk - m, smem);
+    } else {
+        dq_block<D, LAYOUT, ROTD>(p, blk - m, smem);
+    }
 }
 
 template <int D, int LAYOUT, int ROTD>
@@ -630,11 +675,9 @@ int launch_all(const BwdParams &p, hipStream_t stream)
                        p.o, p.dout, p.delta, rows);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     constexpr int NTH = 256 * Halves<D>::NH;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, LAYOUT, ROTD>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.n_ktiles)),
-                       dim3(NTH), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, LAYOUT, ROTD>), dim3((unsigned)((int64_t)p.B * p.H * p.n_qtiles)),
-                       dim3(NTH), 0, stream, p);
+    const int n_dkv = p.B * p.Hkv * p.n_ktiles, n_dq = p.B * p.H * p.n_qtiles;
+    hipLaunchKernelGGL((bwd_main_kernel<D, LAYOUT, ROTD>), dim3((unsigned)(n_dkv + n_dq)), dim3(NTH), 0, stream,
+                       p, n_dkv, n_dq);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 
