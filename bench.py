@@ -133,7 +133,8 @@ def time_launches(torch, launch, steps, warmup, stream, rotate=None):
 
 def bench_fused(torch, api, wl, w, steps, warmup, balance=False):
     dev = torch.device("cuda:0")
-    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in wl.attention_inputs(w))
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    q, k, v = (torch.from_numpy(a).to(tdt).to(dev) for a in wl.attention_inputs(w))
     cos, sin = api.tables_build(w.base, w.rot, w.table_rows, device=dev)
     out = torch.empty_like(q)
     launch = api.prepare_flash_attn_fwd(q, k, v, out, cos, sin, w.q_off, w.k_off, w.rot, w.layout,
@@ -379,6 +380,15 @@ def main():
         for key in ("q", "k", "v", "out"):
             r.pop(key)
         del r
+    if args.only in ("all", "fused"):
+        # the same workload with fp16 storage (the fp16 matrix cores)
+        wf = wl.HEADLINE_F16
+        rf = bench_fused(torch, api, wl, wf, args.steps, args.warmup)
+        tf = wf.flops() / (rf["kernel_ms"] * 1e-3) / 1e12
+        result["fused_f16"] = {"workload": wf.name, "value": round(tf, 2), "unit": "TFLOP/s",
+                               "kernel_ms": round(rf["kernel_ms"], 5),
+                               "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del rf
     if args.only in ("all", "rope_apply"):
         result["rope_apply"] = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets)
         # the same batch with fp16 storage (same bytes, same kernel family)

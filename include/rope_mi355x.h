@@ -19,9 +19,10 @@
  *     argument is validated before any HIP call is made, so argument errors
  *     are reported without a device and nothing is enqueued on error.
  *     ROPE_ERR_HIP reports a failed kernel launch (hipGetLastError).
- *   - Element types: ROPE_BF16 (bfloat16 storage), ROPE_F32, and for
- *     rope_apply also ROPE_F16 (IEEE binary16 storage, [TR] "Inputs the agent
- *     should gather first", item 5).  All rotation and softmax arithmetic is
+ *   - Element types: ROPE_BF16 (bfloat16 storage), ROPE_F32 and ROPE_F16
+ *     (IEEE binary16 storage, [TR] "Inputs the agent should gather first",
+ *     item 5) for rope_apply and the fused forward; the backward and the
+ *     decode step take ROPE_BF16.  All rotation and softmax arithmetic is
  *     fp32; cos/sin tables are always fp32 ([TR] "Kernel design rules": fp32
  *     trig, upcast after load, cast at store, rounding to nearest even).
  *   - Pairing layouts ([TR] "Inputs the agent should gather first", item 1):
@@ -51,7 +52,7 @@ extern "C" {
 /* element types */
 #define ROPE_BF16 0
 #define ROPE_F32 1
-#define ROPE_F16 2   /* rope_apply only */
+#define ROPE_F16 2   /* rope_apply and rope_flash_attn_fwd */
 
 /* status codes */
 #define ROPE_OK 0
@@ -178,8 +179,10 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  *               leave query 0 with no visible key: ROPE_ERR_EMPTY_ROW
  *               ([RF] section 5 rejects such rows).
  * Requires 16-byte-aligned q, k, v, o (else ROPE_ERR_ALIGN).
- * Accumulation and softmax are fp32; for ROPE_BF16 the rotated Q/K and the
- * probabilities enter the matrix cores rounded to bf16.
+ * dtype ROPE_BF16, ROPE_F16 (the same kernels on the fp16 matrix cores) or
+ * ROPE_F32.  Accumulation and softmax are fp32; for the 16-bit types the
+ * rotated Q/K and the probabilities enter the matrix cores rounded to the
+ * storage type.
  *
  *   workspace   optional device scratch, workspace_bytes long, 16-byte
  *               aligned, contents irrelevant.  With at least

@@ -18,9 +18,9 @@ bool aligned(const void *p, unsigned bytes) { return (reinterpret_cast<uintptr_t
 
 int elt_size(int dtype) { return dtype == ROPE_F32 ? 4 : 2; }
 
-// dtypes of the fused forward; rope_apply also takes ROPE_F16
-bool valid_dtype(int dtype) { return dtype == ROPE_BF16 || dtype == ROPE_F32; }
-bool valid_apply_dtype(int dtype) { return valid_dtype(dtype) || dtype == ROPE_F16; }
+// dtypes of the fused forward and rope_apply
+bool valid_dtype(int dtype) { return dtype == ROPE_BF16 || dtype == ROPE_F32 || dtype == ROPE_F16; }
+bool valid_apply_dtype(int dtype) { return valid_dtype(dtype); }
 bool valid_layout(int layout) { return layout == ROPE_NEOX || layout == ROPE_GPTJ; }
 
 // Rows (t, h) of one tensor must not overlap: stride_head >= head_dim when
@@ -136,7 +136,7 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
 {
     const int st = check_fwd_shape(B, H, Sq, Sk, head_dim, q_pos_offset, k_pos_offset, causal, dtype);
     if (st != ROPE_OK) return -st;
-    if (dtype != ROPE_BF16) return 0;
+    if (dtype == ROPE_F32) return 0;
     FlashArgs a = {};
     a.B = B; a.H = H; a.H_kv = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
     a.q_off = q_pos_offset; a.k_off = k_pos_offset; a.causal = causal ? 1 : 0; a.dtype = dtype;
@@ -194,7 +194,7 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     a.workspace = workspace;
     a.workspace_bytes = workspace ? workspace_bytes : 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int rc = dtype == ROPE_BF16 ? rope_launch_flash_bf16(a, s) : rope_launch_flash_f32(a, s);
+    const int rc = dtype == ROPE_F32 ? rope_launch_flash_f32(a, s) : rope_launch_flash_bf16(a, s);
     return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
 }
 

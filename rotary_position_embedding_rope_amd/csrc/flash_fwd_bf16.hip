@@ -176,19 +176,59 @@ __device__ inline int64_t share_of(int64_t x, int64_t U, int G)
     return w;
 }
 
+// The 16-bit storage types: bf16 and IEEE fp16.  Each gives the widening of
+// the low / high half of a 32-bit word, the rounding (to nearest even) of two
+// floats into one word, the matrix-core product of its type and the sum of a
+// word's two halves into an fp32 accumulator (one v_dot2 against (1, 1)).
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <typename E> struct Ty;
+template <> struct Ty<__bf16> {
+    using v8 = bf16x8_t;
+    static __device__ __forceinline__ float lo(uint32_t w) { return rope::bf16lo_to_f32(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return rope::bf16hi_to_f32(w); }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+    static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(rope::bf16x2_t, w),
+                                               __builtin_bit_cast(rope::bf16x2_t, 0x3f803f80u), acc, false);
+    }
+};
+template <> struct Ty<_Float16> {
+    using v8 = f16x8_t;
+    static __device__ __forceinline__ float lo(uint32_t w) { return rope::f16lo_to_f32(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return rope::f16hi_to_f32(w); }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return rope::pack_f16x2(a, b); }
+    static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u),
+                                      acc, false);
+    }
+};
+
+template <typename E>
 __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8])
 {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        x[2 * i] = rope::bf16lo_to_f32(ws[i]);
-        x[2 * i + 1] = rope::bf16hi_to_f32(ws[i]);
+        x[2 * i] = Ty<E>::lo(ws[i]);
+        x[2 * i + 1] = Ty<E>::hi(ws[i]);
     }
 }
+template <typename E>
 __device__ __forceinline__ uint4 pack8(const float (&x)[8])
 {
-    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                      pack_bf16x2(x[6], x[7]));
+    return make_uint4(Ty<E>::pack2(x[0], x[1]), Ty<E>::pack2(x[2], x[3]), Ty<E>::pack2(x[4], x[5]),
+                      Ty<E>::pack2(x[6], x[7]));
 }
 
 // Rotate pairs (a[i], b[i]) by (c[i], s[i]): a' = a c - b s, b' = a s + b c.
@@ -300,10 +340,12 @@ constexpr float FAST_SUM_LIMIT = 8192.0f;
 // different 128-row query tiles and consume the same key tiles, so each
 // staged tile serves 256 rows; otherwise the groups take the same rows and
 // alternate key tiles.
-template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, bool BAL, bool RS>
+template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, bool BAL, bool RS, typename E>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_bf16_kernel(Params p)
 {
+    using TT = Ty<E>;
+    using v8 = typename TT::v8;
     static_assert(!RS || (NG == 2 && !BAL), "row split: two groups, default schedule");
     using Plan = KPlan<D, LAYOUT, ROT, BN>;
     constexpr int NKB = BN / 32;                    // 32-key blocks per tile
@@ -461,7 +503,6 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
     for (int bd = 0; bd < D / 32; ++bd)
         vcol[bd] = 8 * ((4 * bd + (tr_col >> 3)) ^ (4 * ((tr_row >> 1) & 1))) + (tr_col & 7);
-    const rope::bf16x2_t ones = __builtin_bit_cast(rope::bf16x2_t, 0x3f803f80u);   // (1, 1)
 
     // One segment: key tiles [kb, ke) of the 128 query rows made of two
     // 64-row halves starting at rowA and rowB (rowB >= Sq: no second half)
@@ -593,11 +634,11 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                         for (int u = 0; u < 2; ++u) {
                             if constexpr (LAYOUT == 0) {
-                                a[2 * u] = rope::bf16lo_to_f32(u0[u]); a[2 * u + 1] = rope::bf16hi_to_f32(u0[u]);
-                                b[2 * u] = rope::bf16lo_to_f32(u1[u]); b[2 * u + 1] = rope::bf16hi_to_f32(u1[u]);
+                                a[2 * u] = TT::lo(u0[u]); a[2 * u + 1] = TT::hi(u0[u]);
+                                b[2 * u] = TT::lo(u1[u]); b[2 * u + 1] = TT::hi(u1[u]);
                             } else {   // pairs (lo, hi) of each dword
-                                a[u] = rope::bf16lo_to_f32(u0[u]); b[u] = rope::bf16hi_to_f32(u0[u]);
-                                a[2 + u] = rope::bf16lo_to_f32(u1[u]); b[2 + u] = rope::bf16hi_to_f32(u1[u]);
+                                a[u] = TT::lo(u0[u]); b[u] = TT::hi(u0[u]);
+                                a[2 + u] = TT::lo(u1[u]); b[2 + u] = TT::hi(u1[u]);
                             }
                         }
 #pragma unroll
@@ -605,11 +646,11 @@ void flash_fwd_bf16_kernel(Params p)
                         rotate_pairs<4>(a, b, cc, ss);
                         uint2 x0, x1;
                         if constexpr (LAYOUT == 0) {
-                            x0 = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-                            x1 = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+                            x0 = make_uint2(TT::pack2(a[0], a[1]), TT::pack2(a[2], a[3]));
+                            x1 = make_uint2(TT::pack2(b[0], b[1]), TT::pack2(b[2], b[3]));
                         } else {
-                            x0 = make_uint2(pack_bf16x2(a[0], b[0]), pack_bf16x2(a[1], b[1]));
-                            x1 = make_uint2(pack_bf16x2(a[2], b[2]), pack_bf16x2(a[3], b[3]));
+                            x0 = make_uint2(TT::pack2(a[0], b[0]), TT::pack2(a[1], b[1]));
+                            x1 = make_uint2(TT::pack2(a[2], b[2]), TT::pack2(a[3], b[3]));
                         }
                         if constexpr (FULL) {
                             w0 = x0;
@@ -628,18 +669,18 @@ void flash_fwd_bf16_kernel(Params p)
                 uint4 w0 = r0[i], w1 = r1[i];
                 if constexpr (ROT && LAYOUT == 0) {
                     float lo[8], hi[8], cc[8], ss[8];
-                    unpack8(r0[i], lo);
-                    unpack8(r1[i], hi);
+                    unpack8<E>(r0[i], lo);
+                    unpack8<E>(r1[i], hi);
 #pragma unroll
                     for (int u = 0; u < 8; ++u) { cc[u] = c[i][u]; ss[u] = s[i][u]; }
                     rotate_pairs<8>(lo, hi, cc, ss);
-                    w0 = pack8(lo);
-                    w1 = pack8(hi);
+                    w0 = pack8<E>(lo);
+                    w1 = pack8<E>(hi);
                 } else if constexpr (ROT && LAYOUT == 1) {
                     // chunk h holds pairs 4h .. 4h+3 of the slot's 8
                     float x[2][8];
-                    unpack8(r0[i], x[0]);
-                    unpack8(r1[i], x[1]);
+                    unpack8<E>(r0[i], x[0]);
+                    unpack8<E>(r1[i], x[1]);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         float a[4], bb[4], cc[4], ss[4];
@@ -652,8 +693,8 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                         for (int u = 0; u < 4; ++u) { x[h][2 * u] = a[u]; x[h][2 * u + 1] = bb[u]; }
                     }
-                    w0 = pack8(x[0]);
-                    w1 = pack8(x[1]);
+                    w0 = pack8<E>(x[0]);
+                    w1 = pack8<E>(x[1]);
                 }
                 if constexpr (ROT && !FULL) {
                     // slots past rot_dim keep their input bits
@@ -680,7 +721,7 @@ void flash_fwd_bf16_kernel(Params p)
         // The first two key tiles, the query rows and their table rows are
         // all requested before any of them is used, so their latencies
         // overlap (rows past Sq, or past the table, read as zeros).
-        bf16x8_t qf[DT];
+        v8 qf[DT];
         {
             uint4 pr0[KI], pr1[KI];
             float pc[KI][8], ps[KI][8];
@@ -696,7 +737,7 @@ void flash_fwd_bf16_kernel(Params p)
             const rsrc_t qrs = make_rsrc<2 * D>(qh + wq0 * D, (int)(qleft < 0 ? 0 : (qleft > 32 ? 32 : qleft)));
             float qv[DT][8];
 #pragma unroll
-            for (int t = 0; t < DT; ++t) unpack8(bload16(qrs, 2 * (l32 * D + 16 * t + 8 * hh)), qv[t]);
+            for (int t = 0; t < DT; ++t) unpack8<E>(bload16(qrs, 2 * (l32 * D + 16 * t + 8 * hh)), qv[t]);
             if constexpr (ROT) {
                 const int64_t tleft = p.table_rows - (p.q_off + wq0);
                 const int trows = (int)(tleft < 0 ? 0 : (tleft > 32 ? 32 : tleft)) * (rh / 4);
@@ -743,7 +784,7 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
 #pragma unroll
-                for (int s = 0; s < 8; ++s) qf[t][s] = (__bf16)(qv[t][s] * p.sl2);
+                for (int s = 0; s < 8; ++s) qf[t][s] = (E)(qv[t][s] * p.sl2);
             }
             if (T(0) < tend) {
                 stage_k(0, kpa, kr0, kr1, kc, ks);
@@ -797,9 +838,9 @@ void flash_fwd_bf16_kernel(Params p)
                 s[kb2] = (f32x16_t){};
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+                    const v8 a = *reinterpret_cast<const v8 *>(
                         kl + (kb2 * 32 + l32) * KP + 16 * t + 8 * hh);
-                    s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb2], 0, 0, 0);
+                    s[kb2] = TT::mfma(a, qf[t], s[kb2]);
                 }
             }
         };
@@ -807,7 +848,7 @@ void flash_fwd_bf16_kernel(Params p)
         // rounded to bf16 in the B-operand layout of O^T += V^T P^T, and this
         // lane's partial row sums of those bf16 values.  For key sub-step mm
         // of block kb2, slot s holds accumulator element 8mm + s.
-        auto probs = [&](const f32x16_t (&s)[NKB], bf16x8_t (&pb)[NKB][2], float (&lt)[4], auto SUB) {
+        auto probs = [&](const f32x16_t (&s)[NKB], v8 (&pb)[NKB][2], float (&lt)[4], auto SUB) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) lt[u] = 0.f;
 #pragma unroll
@@ -822,13 +863,12 @@ void flash_fwd_bf16_kernel(Params p)
                             x0 -= m_ref;
                             x1 -= m_ref;
                         }
-                        wv[u] = pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
+                        wv[u] = TT::pack2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
                     }
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        lt[u] = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(rope::bf16x2_t, wv[u]), ones, lt[u], false);
-                    pb[kb2][mm] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+                        lt[u] = TT::sum2(wv[u], lt[u]);
+                    pb[kb2][mm] = __builtin_bit_cast(v8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
                 }
         };
         using sub_on = std::integral_constant<bool, true>;
@@ -836,7 +876,7 @@ void flash_fwd_bf16_kernel(Params p)
         // The exact path for tile kt: element mask (diagonal or ragged
         // tile), row max, lazy raise of the reference (rescaling O and l),
         // probabilities.
-        auto exact = [&](int kt, f32x16_t (&s)[NKB], bf16x8_t (&pb)[NKB][2], float (&lt)[4]) {
+        auto exact = [&](int kt, f32x16_t (&s)[NKB], v8 (&pb)[NKB][2], float (&lt)[4]) {
             if (kt >= kt_mask) {
                 // key kt*BN + kk is visible iff kk <= lim (kk: index inside the tile)
                 const int lim0 = lim_base - kt * BN;
@@ -882,7 +922,7 @@ void flash_fwd_bf16_kernel(Params p)
             probs(s, pb, lt, sub_on{});
         };
         // O^T += V^T P^T with V from V buffer b.
-        auto pv = [&](const bf16x8_t (&pb)[NKB][2], int b) {
+        auto pv = [&](const v8 (&pb)[NKB][2], int b) {
             const uint16_t *v_lds = vbuf(b);
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2)
@@ -896,10 +936,10 @@ void flash_fwd_bf16_kernel(Params p)
                         const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
                         const s16x4_t x1 =
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * RP));
-                        const bf16x8_t a = __builtin_bit_cast(
-                            bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+                        const v8 a = __builtin_bit_cast(
+                            v8, (short __attribute__((ext_vector_type(8)))){
                                           x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-                        oacc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb2][mm], oacc[bd], 0, 0, 0);
+                        oacc[bd] = TT::mfma(a, pb[kb2][mm], oacc[bd]);
                     }
         };
 
@@ -973,7 +1013,7 @@ void flash_fwd_bf16_kernel(Params p)
         };
         // tile j's probabilities on the fast path (exact path if needed);
         // `mfma` issues the matrix-core work they are interleaved with
-        auto softmax = [&](int j, f32x16_t (&sc)[NKB], bf16x8_t (&pb)[NKB][2], auto mfma, auto NMF,
+        auto softmax = [&](int j, f32x16_t (&sc)[NKB], v8 (&pb)[NKB][2], auto mfma, auto NMF,
                            auto NPV) {
             const int kt = T(j);
             float lt[4];
@@ -1001,7 +1041,7 @@ void flash_fwd_bf16_kernel(Params p)
         auto step_a = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
             __syncthreads();   // K(j+1), V(j) staged; buffers of iteration j-1 free
             dma_next(j, 2 * wave, blk2{});
-            bf16x8_t pb[NKB][2];
+            v8 pb[NKB][2];
             softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
             // tile j's P V on the matrix cores, interleaved with staging
             pv(pb, vslot(j));
@@ -1019,7 +1059,7 @@ void flash_fwd_bf16_kernel(Params p)
         auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB], int pblk) {
             __syncthreads();   // K(j+1), V(j) staged
             dma_next(j, pblk, blk4{});
-            bf16x8_t pb[NKB][2];
+            v8 pb[NKB][2];
             softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
             pv(pb, vslot(j));
             wait_dma();   // V(j+1)
@@ -1146,8 +1186,8 @@ void flash_fwd_bf16_kernel(Params p)
                 for (int g = 0; g < 4; ++g) {
                     const int d0 = 32 * b + 8 * g + 4 * hh;
                     uint2 wv;
-                    wv.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-                    wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+                    wv.x = TT::pack2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
+                    wv.y = TT::pack2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
                     *reinterpret_cast<uint2 *>(orow + d0) = wv;
                 }
             // scores are in log2 units against the reference m_fin
@@ -1224,9 +1264,10 @@ void flash_fwd_bf16_kernel(Params p)
 // writes its output rows.  One 4-wave workgroup per (batch*head, query tile);
 // tiles that were not split return at once.  Runs after the main kernel on
 // the same stream, so every partial state is visible.
-template <int D>
+template <int D, typename E>
 __global__ __launch_bounds__(256) void flash_merge_kernel(Params p)
 {
+    using TT = Ty<E>;
     constexpr int DB = D / 32, NC = DB * 16 + 2;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -1265,8 +1306,8 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(Params p)
         for (int g = 0; g < 4; ++g) {
             const int d0 = 32 * b + 8 * g + 4 * hh;
             uint2 wv;
-            wv.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-            wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+            wv.x = TT::pack2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
+            wv.y = TT::pack2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
             *reinterpret_cast<uint2 *>(orow + d0) = wv;
         }
     if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_acc + log2f(l_sum)) * LN2;
@@ -1344,7 +1385,7 @@ int64_t workspace_bytes(const Params &p)
     return (int64_t)p.sk_G * 2 * 4 * NC * 64 * 4;   // two partial states per share
 }
 
-template <int D, int LAYOUT, bool ROT, bool FULL>
+template <int D, int LAYOUT, bool ROT, bool FULL, typename E>
 int launch(const FlashArgs &a, hipStream_t stream)
 {
     constexpr int NG = Shape<D>::NG, BN = Shape<D>::BN;
@@ -1366,41 +1407,43 @@ int launch(const FlashArgs &a, hipStream_t stream)
     // D = 128, default schedule: row split (two query tiles per workgroup)
     constexpr bool RSPLIT = D == 128;
     if (p.sk_G > 0) {
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true, false>), dim3((unsigned)p.sk_G),
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true, false, E>), dim3((unsigned)p.sk_G),
                            dim3(256 * NG), 0, stream, p);
     } else if constexpr (RSPLIT) {
         const int64_t blocks = (int64_t)p.BH * ((p.n_qtiles + 1) / 2);
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, 2, BN, false, true>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, 2, BN, false, true, E>), dim3((unsigned)blocks),
                            dim3(512), 0, stream, p);
     } else {
         const int64_t blocks = (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, false, false>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, false, false, E>), dim3((unsigned)blocks),
                            dim3(256 * NG), 0, stream, p);
     }
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     if (p.sk_G > 0) {
-        hipLaunchKernelGGL((flash_merge_kernel<D>), dim3((unsigned)(p.BH * p.n_qtiles)), dim3(256), 0,
+        hipLaunchKernelGGL((flash_merge_kernel<D, E>), dim3((unsigned)(p.BH * p.n_qtiles)), dim3(256), 0,
                            stream, p);
         if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     }
     return ROPE_LAUNCH_OK;
 }
 
-template <int D>
+template <int D, typename E>
 int launch_d(const FlashArgs &a, hipStream_t stream)
 {
-    if (a.rot_dim == 0) return launch<D, 1, false, false>(a, stream);
+    if (a.rot_dim == 0) return launch<D, 1, false, false, E>(a, stream);
     const bool full = a.rot_dim == D;
     if (a.layout == 0)
-        return full ? launch<D, 0, true, true>(a, stream) : launch<D, 0, true, false>(a, stream);
-    return full ? launch<D, 1, true, true>(a, stream) : launch<D, 1, true, false>(a, stream);
+        return full ? launch<D, 0, true, true, E>(a, stream) : launch<D, 0, true, false, E>(a, stream);
+    return full ? launch<D, 1, true, true, E>(a, stream) : launch<D, 1, true, false, E>(a, stream);
 }
 
 }  // namespace
 
+// dtype 0 (bf16) or 2 (fp16): the same kernels over either 16-bit type
 int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream)
 {
-    return a.head_dim == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
+    if (a.dtype == 2) return a.head_dim == 64 ? launch_d<64, _Float16>(a, stream) : launch_d<128, _Float16>(a, stream);
+    return a.head_dim == 64 ? launch_d<64, __bf16>(a, stream) : launch_d<128, __bf16>(a, stream);
 }
 
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a)

@@ -182,6 +182,8 @@ SWEEP_BF16 = tuple(
     for (b, s), seed in zip(((1, 1024), (1, 2048), (1, 4096), (2, 1024), (4, 1024)), range(2, 7))
 )
 HEADLINE = SWEEP_BF16[2]   # 1x8x4096x64 bf16 NeoX causal
+# the same shape with fp16 storage
+HEADLINE_F16 = AttentionWorkload("causal_neox_f16_1x8x4096x64", 1, 8, 4096, 4096, 64, "f16", 4, "neox")
 PREFILL_OFFSET = AttentionWorkload("chunked_prefill_neox_bf16_1x32x2048q_16384k_128", 1, 32, 2048,
                                    16384, 128, "bf16", 7, "neox", base=500000.0,
                                    q_off=14336, k_off=0)

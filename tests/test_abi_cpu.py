@@ -168,7 +168,7 @@ def fwd_args(**over):
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(rot=48), _lib.ERR_UNSUPPORTED),
     (dict(dtype=3), _lib.ERR_UNSUPPORTED),
-    (dict(dtype=_lib.F16), _lib.ERR_UNSUPPORTED),   # fp16 storage: rope_apply only
+    (dict(dtype=_lib.F16, q=None), _lib.ERR_NULL),  # fp16 accepted: validation goes on
     (dict(layout=7), _lib.ERR_UNSUPPORTED),
     (dict(q=None), _lib.ERR_NULL),
     (dict(v=None), _lib.ERR_NULL),

@@ -109,6 +109,23 @@ CASES = [
     ("one_key", 1, 2, 1, 40, 1, 128, "neox", 128, 0, False),
 ]
 
+# both offsets non-zero: queries at 700.., keys at 250.. (name, Sq, Sk, D, layout, q_off, k_off)
+KOFF_CASES = [("koff_neox_64", 90, 530, 64, "neox", 700, 250),
+              ("koff_gptj_128_gqa", 70, 300, 128, "gptj", 400, 133)]
+
+
+@pytest.mark.parametrize("case", KOFF_CASES, ids=lambda c: c[0])
+def test_backward_key_offset(orc, case):
+    name, Sq, Sk, D, layout, q_off, k_off = case
+    w = wl.AttentionWorkload(name, 1, 4, Sq, Sk, D, "bf16", 900 + Sq, layout, base=1e4,
+                             q_off=q_off, k_off=k_off, H_kv=2)
+    q, k, v, dout = inputs(w)
+    o, lse, dq, dk, dv = run(w, q, k, v, dout)
+    kw = dict(q_off=q_off, k_off=k_off, base=w.base, layout=layout)
+    assert (np.abs(lse - orc.attention_lse(q, k, **kw)) <= lse_bound(q, k, D)).all()
+    for g, r, n in zip((dq, dk, dv), orc.attention_bwd(q, k, v, dout, **kw), ("dq", "dk", "dv")):
+        check_grad(g, r, n)
+
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_backward_full(orc, case):
