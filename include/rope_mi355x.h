@@ -19,10 +19,9 @@
  *     argument is validated before any HIP call is made, so argument errors
  *     are reported without a device and nothing is enqueued on error.
  *     ROPE_ERR_HIP reports a failed kernel launch (hipGetLastError).
- *   - Element types: ROPE_BF16 (bfloat16 storage), ROPE_F32 and ROPE_F16
- *     (IEEE binary16 storage, [TR] "Inputs the agent should gather first",
- *     item 5) for rope_apply and the fused forward; the backward and the
- *     decode step take ROPE_BF16.  All rotation and softmax arithmetic is
+ *   - Element types: ROPE_BF16 (bfloat16 storage) and ROPE_F16 (IEEE
+ *     binary16 storage, [TR] "Inputs the agent should gather first", item 5)
+ *     everywhere; ROPE_F32 for rope_apply and the fused forward.  All rotation and softmax arithmetic is
  *     fp32; cos/sin tables are always fp32 ([TR] "Kernel design rules": fp32
  *     trig, upcast after load, cast at store, rounding to nearest even).
  *   - Pairing layouts ([TR] "Inputs the agent should gather first", item 1):
@@ -52,7 +51,7 @@ extern "C" {
 /* element types */
 #define ROPE_BF16 0
 #define ROPE_F32 1
-#define ROPE_F16 2   /* rope_apply and rope_flash_attn_fwd */
+#define ROPE_F16 2
 
 /* status codes */
 #define ROPE_OK 0
@@ -225,24 +224,26 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
  * R^T being the rotation by the opposite angle; dk and dv of a key/value
  * head sum over the query heads that read it.  V is never rotated.
  *
- *   q, o, dout  [B, H, Sq, head_dim] bf16, contiguous; o and lse from
+ *   q, o, dout  [B, H, Sq, head_dim], contiguous; o and lse from
  *               rope_flash_attn_fwd with the same arguments.
- *   k, v        [B, H_kv, Sk, head_dim] bf16, contiguous (H_kv divides H).
+ *   k, v        [B, H_kv, Sk, head_dim], contiguous (H_kv divides H).
  *   lse         fp32 [B, H, Sq], 4-byte aligned.
- *   dq          [B, H, Sq, head_dim] bf16, written whole.
- *   dk, dv      [B, H_kv, Sk, head_dim] bf16, written whole (keys no query
+ *   dq          [B, H, Sq, head_dim], written whole.
+ *   dk, dv      [B, H_kv, Sk, head_dim], written whole (keys no query
  *               sees get zeros).
  *   The three outputs must not alias each other or any input
  *   (ROPE_ERR_SHAPE).
- *   other arguments as rope_flash_attn_fwd; dtype ROPE_BF16, head_dim 64 or
- *   128, rot_dim 0 or a multiple of 32 (else ROPE_ERR_UNSUPPORTED).
+ *   other arguments as rope_flash_attn_fwd; dtype ROPE_BF16 or ROPE_F16 (all
+ *   tensors of that type), head_dim 64 or 128, rot_dim 0 or a multiple of 32
+ *   (else ROPE_ERR_UNSUPPORTED).
  *   workspace   device scratch of at least rope_flash_attn_bwd_workspace_size()
  *               bytes, 16-byte aligned, contents irrelevant (per-row
  *               rowsum(dout * o)).  Calls that share a workspace must not run
  *               concurrently.
- * Three kernels are enqueued on `stream`: the row sums, dk/dv, then dq.
+ * Two kernels are enqueued on `stream`: the row sums, then dk/dv and dq
+ * in one launch.
  * Accumulation is fp32; the rotated Q/K, dout, V, P and dS enter the matrix
- * cores rounded to bf16.
+ * cores rounded to the storage type.
  */
 int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                         const float *lse, void *dq, void *dk, void *dv,
@@ -277,11 +278,11 @@ int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_di
  *             . v_cache[b, h / (H/H_kv), 0..L]
  * (all L + 1 keys are visible to the new query).
  *
- *   q, o        [B, H, head_dim] bf16, one new query per request; o is
+ *   q, o        [B, H, head_dim], one new query per request; o is
  *               written whole and must not alias the other arrays.
- *   k_new,      [B, H_kv, head_dim] bf16; H_kv divides H, H / H_kv <= 8.
+ *   k_new,      [B, H_kv, head_dim]; H_kv divides H, H / H_kv <= 8.
  *   v_new
- *   k_cache,    [B, H_kv, S_max, head_dim] bf16, contiguous; written at row
+ *   k_cache,    [B, H_kv, S_max, head_dim], contiguous; written at row
  *   v_cache     L of each (b, head) only.
  *   cache_lens  device int32 [B].  A value outside [0, S_max), or (rot_dim >
  *               0) outside [0, table_rows), is detected on the device: that
@@ -290,7 +291,8 @@ int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_di
  *   cos_tab,    fp32 [table_rows, rot_dim/2] (see rope_tables_build).
  *   sin_tab
  *   rot_dim     0 (no rotation; tables may be NULL) or even, 2..head_dim.
- *   head_dim    64 or 128;  layout ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16.
+ *   head_dim    64 or 128;  layout ROPE_NEOX or ROPE_GPTJ;  dtype ROPE_BF16
+ *               or ROPE_F16 (q, k_new, v_new, caches and o all of it).
  *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
  *   workspace   device scratch of at least rope_decode_workspace_size()
  *               bytes, 16-byte aligned, contents irrelevant: the fp32

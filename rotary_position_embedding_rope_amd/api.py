@@ -267,8 +267,9 @@ def _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_di
                  softmax_scale, out, workspace):
     _require_cuda(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, out)
     for t in (q, k_new, v_new, k_cache, v_cache, out):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("q, k_new, v_new, caches and out must be contiguous bfloat16")
+        if t.dtype not in (torch.bfloat16, torch.float16) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k_new, v_new, caches and out must be contiguous, all bfloat16 or all "
+                             "float16")
     if q.dim() != 3:
         raise ValueError("q must be [B, H, D] (one new query per request)")
     B, H, D = q.shape
@@ -294,7 +295,7 @@ def _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_di
         workspace = decode_workspace(q, k_cache)
     return (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             cache_lens.data_ptr(), out.data_ptr(), B, H, Hkv, S_max, D, cp, sp, rows, rot,
-            _layout(layout), float(softmax_scale), _lib.BF16, workspace.data_ptr(),
+            _layout(layout), float(softmax_scale), _dtype(q), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _stream(q))
 
 

@@ -202,7 +202,8 @@ int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_di
 {
     if (B < 1 || H < 1 || Sq < 1 || Sq > 2147483647) return -ROPE_ERR_SHAPE;
     if (head_dim < 2 || head_dim % 2 != 0) return -ROPE_ERR_SHAPE;
-    if (dtype != ROPE_BF16 || (head_dim != 64 && head_dim != 128)) return -ROPE_ERR_UNSUPPORTED;
+    if ((dtype != ROPE_BF16 && dtype != ROPE_F16) || (head_dim != 64 && head_dim != 128))
+        return -ROPE_ERR_UNSUPPORTED;
     return rope_flash_bwd_workspace_bytes(B, H, Sq);
 }
 
@@ -221,7 +222,7 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
     if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (q_pos_offset < 0 || k_pos_offset < 0) return ROPE_ERR_SHAPE;
     if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return ROPE_ERR_SHAPE;
-    if (!valid_layout(layout) || dtype != ROPE_BF16) return ROPE_ERR_UNSUPPORTED;
+    if (!valid_layout(layout) || (dtype != ROPE_BF16 && dtype != ROPE_F16)) return ROPE_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return ROPE_ERR_UNSUPPORTED;
     if (rot_dim % 32 != 0) return ROPE_ERR_UNSUPPORTED;
     // grids of 128-row tiles; the key/value kernel walks (Sq / 32 + 1) * (H / H_kv) steps
@@ -254,6 +255,7 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
     a.cos_tab = cos_tab; a.sin_tab = sin_tab;
     a.rot_dim = rot_dim; a.layout = layout; a.causal = causal ? 1 : 0;
     a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    a.dtype = dtype;
     a.workspace = workspace;
     return rope_launch_flash_bwd_bf16(a, static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK ? ROPE_OK
                                                                                               : ROPE_ERR_HIP;
@@ -295,7 +297,7 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
     if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return ROPE_ERR_SHAPE;
     if (!valid_layout(layout)) return ROPE_ERR_UNSUPPORTED;
-    if (dtype != ROPE_BF16) return ROPE_ERR_UNSUPPORTED;
+    if (dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_ERR_UNSUPPORTED;
     if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !o || !workspace)
         return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
@@ -314,6 +316,7 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
     a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.table_rows = rot_dim > 0 ? table_rows : 0;
     a.rot_dim = rot_dim; a.layout = layout;
     a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    a.dtype = dtype;
     a.workspace = workspace;
     const int rc = rope_launch_decode_bf16(a, static_cast<hipStream_t>(stream));
     return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;

@@ -43,6 +43,62 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x)
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// The 16-bit storage types: bf16 and IEEE fp16.  Each gives the widening of
+// the low / high half of a 32-bit word, the rounding (to nearest even) of two
+// floats into one word, the matrix-core products of its type (32x32x16 and
+// 16x16x32), the sum of a word's two halves into an fp32 accumulator (one
+// v_dot2 against (1, 1)) and the bits of a quiet NaN.
+template <typename E> struct Ty;
+template <> struct Ty<__bf16> {
+    using v8 = bf16x8_t;
+    static __device__ __forceinline__ float lo(uint32_t w) { return bf16lo_to_f32(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return bf16hi_to_f32(w); }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+    static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mfma16(v8 a, v8 b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+    }
+    static constexpr uint16_t QNAN = 0x7fc0;
+};
+template <> struct Ty<_Float16> {
+    using v8 = f16x8_t;
+    static __device__ __forceinline__ float lo(uint32_t w) { return f16lo_to_f32(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return f16hi_to_f32(w); }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_f16x2(a, b); }
+    static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mfma16(v8 a, v8 b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u),
+                                      acc, false);
+    }
+    static constexpr uint16_t QNAN = 0x7e00;
+};
+
+// One 16-bit element of type E <-> fp32 (bits held in a uint16_t).
+template <typename E>
+__device__ __forceinline__ float elt_to_f32(uint16_t b) { return Ty<E>::lo((uint32_t)b); }
+template <typename E>
+__device__ __forceinline__ uint16_t f32_to_elt(float x) { return (uint16_t)(Ty<E>::pack2(x, 0.f) & 0xffffu); }
+
+
 }  // namespace rope
 
 // Status values returned by the launchers (mirror include/rope_mi355x.h).
@@ -102,6 +158,7 @@ struct FlashBwdArgs {
     const float *cos_tab, *sin_tab;
     int rot_dim, layout, causal;
     float scale;                        // already resolved (> 0)
+    int dtype;                          // 0 bf16, 2 fp16
     void *workspace;                    // rope_flash_bwd_workspace_bytes() bytes
 };
 int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream);
@@ -119,6 +176,7 @@ struct DecodeArgs {
     int64_t table_rows;
     int rot_dim, layout;
     float scale;                     // already resolved (> 0)
+    int dtype;                       // 0 bf16, 2 fp16
     void *workspace;                 // rope_decode_workspace_bytes() bytes
 };
 int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);

@@ -26,9 +26,9 @@
 
 namespace {
 
-using rope::bf16_to_f32;
-using rope::bf16x8_t;
-using rope::f32_to_bf16;
+using rope::elt_to_f32;
+using rope::f32_to_elt;
+using rope::Ty;
 using rope::f32x4_t;
 
 constexpr int SUB = 64;           // keys per pass of the workgroup
@@ -137,9 +137,10 @@ __device__ __forceinline__ uint4 pick(bool c, uint4 a, uint4 b)
 // zero.  P V runs on the vector ALU, each key row split over D/8 lanes.  Each
 // wave runs its own online softmax over its keys; the four waves are merged
 // once per piece.
-template <int D, int LAYOUT, bool ROT, int GT>
+template <int D, int LAYOUT, bool ROT, int GT, typename E>
 __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 {
+    using V8 = typename Ty<E>::v8;
     constexpr int LPR = D / 8;          // lanes per value row (16 bytes each)
     constexpr int KPI = 64 / LPR;       // value rows per wave load
     constexpr int KPW = SUB / 4;        // keys per wave and pass (16)
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
     __shared__ __attribute__((aligned(16))) float p_lds[4][GT][KPW];   // per wave: probabilities
     __shared__ float a_lds[4][GT];                                 // per wave: rescale factors
     __shared__ float ml_lds[4][2][GT];                             // per wave: max and sum
-    __shared__ __attribute__((aligned(16))) uint16_t knew_lds[D];  // new key, rotated, bf16
+    __shared__ __attribute__((aligned(16))) uint16_t knew_lds[D];  // new key, rotated, rounded to E
     __shared__ __attribute__((aligned(16))) uint16_t vnew_lds[D];
     __shared__ __attribute__((aligned(16))) float o_lds[4][GT][D];
     __shared__ int red_lds[4];
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
         }
     };
 
-    bf16x8_t qb[NT];
+    V8 qb[NT];
     float oacc[GT][8];
     float m_run = -INFINITY, l_run = 0.f;
 
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             int da, db;
             pair_dims<LAYOUT>(i, ROT ? p.rot_dim : 0, da, db);
             const uint16_t *qr = p.q + ((int64_t)c.b * p.H + c.kvh * G + g) * D;
-            const float xa = bf16_to_f32(qr[da]), xb = bf16_to_f32(qr[db]);
+            const float xa = elt_to_f32<E>(qr[da]), xb = elt_to_f32<E>(qr[db]);
             float ya = xa, yb = xb;
             if (ROT && i < rh) {
                 const float cs = crow[i], sn = srow[i];
@@ -290,14 +291,14 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
                 int da, db;
                 pair_dims<LAYOUT>(i, ROT ? p.rot_dim : 0, da, db);
                 const uint16_t *kr = p.k_new + (int64_t)bk * D;
-                const float xa = bf16_to_f32(kr[da]), xb = bf16_to_f32(kr[db]);
+                const float xa = elt_to_f32<E>(kr[da]), xb = elt_to_f32<E>(kr[db]);
                 float ya = xa, yb = xb;
                 if (ROT && i < rh) {
                     const float cs = crow[i], sn = srow[i];
                     ya = xa * cs - xb * sn;
                     yb = xa * sn + xb * cs;
                 }
-                const uint16_t ba = f32_to_bf16(ya), bb = f32_to_bf16(yb);
+                const uint16_t ba = f32_to_elt<E>(ya), bb = f32_to_elt<E>(yb);
                 knew_lds[da] = ba;
                 knew_lds[db] = bb;
                 p.k_cache[crow_off + da] = ba;
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj)
-                qb[t][jj] = (__bf16)(kl < GT ? q_lds[kl][32 * t + 8 * kq + jj] : 0.f);
+                qb[t][jj] = (E)(kl < GT ? q_lds[kl][32 * t + 8 * kq + jj] : 0.f);
         }
 #pragma unroll
         for (int g = 0; g < GT; ++g)
@@ -343,8 +344,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             // conditional pointer would send the loaded rows through memory)
             const uint4 kn = *reinterpret_cast<const uint4 *>(knew_lds + 32 * t + 8 * kq);
             const uint4 wv = pick(knew, kn, kd[t]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv), qb[t], acc,
-                                                          0, 0, 0);
+            acc = Ty<E>::mfma16(__builtin_bit_cast(V8, wv), qb[t], acc);
         }
         // accumulator element r of lane l: key 4(l/16) + r of the block, query slot l%16
         float sc[4];
@@ -393,8 +393,8 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             float vf[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vf[2 * e] = rope::bf16lo_to_f32(u[e]);
-                vf[2 * e + 1] = rope::bf16hi_to_f32(u[e]);
+                vf[2 * e] = Ty<E>::lo(u[e]);
+                vf[2 * e + 1] = Ty<E>::hi(u[e]);
             }
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 // all U loads issued before any is used, keeping a running (max, sum, row)
 // that it rescales whenever a larger piece maximum arrives.  The RP running
 // states are then merged through LDS by the same rule.
-template <int D>
+template <int D, typename E>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int rot)
 {
     constexpr int LR = D / 2;        // lanes per piece
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int r
     const int L = p.lens[b];
     uint16_t *orow = p.o + (int64_t)bh * D;
     if (L < 0 || (int64_t)L >= p.S_max || (rot > 0 && (int64_t)L >= p.table_rows)) {
-        for (int d = tid; d < D; d += 256) orow[d] = 0x7fc0;   // bf16 quiet NaN
+        for (int d = tid; d < D; d += 256) orow[d] = Ty<E>::QNAN;
         return;
     }
     const int h = bh % p.H, sl = b * p.Hkv + h / p.G;
@@ -563,35 +563,35 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int r
             oy = fmaf(red_o[r][tid].y, f, oy);
             ls = fmaf(red_l[r], f, ls);
         }
-        const uint32_t pk = (uint32_t)f32_to_bf16(ox / ls) | ((uint32_t)f32_to_bf16(oy / ls) << 16);
+        const uint32_t pk = Ty<E>::pack2(ox / ls, oy / ls);
         reinterpret_cast<uint32_t *>(orow)[tid] = pk;
     }
 }
 
-template <int D, int LAYOUT, bool ROT>
+template <int D, int LAYOUT, bool ROT, typename E>
 int launch_gt(const DecodeParams &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)p.nw);
     if (p.G <= 1)
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 1>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 1, E>), grid, dim3(256), 0, stream, p);
     else if (p.G <= 2)
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 2>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 2, E>), grid, dim3(256), 0, stream, p);
     else if (p.G <= 4)
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 4>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 4, E>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 8>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((decode_chunk_kernel<D, LAYOUT, ROT, 8, E>), grid, dim3(256), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 
-template <int D>
+template <int D, typename E>
 int launch_d(const DecodeParams &p, int layout, hipStream_t stream)
 {
     int rc;
-    if (p.rot_dim == 0) rc = launch_gt<D, 0, false>(p, stream);
-    else if (layout == 0) rc = launch_gt<D, 0, true>(p, stream);
-    else rc = launch_gt<D, 1, true>(p, stream);
+    if (p.rot_dim == 0) rc = launch_gt<D, 0, false, E>(p, stream);
+    else if (layout == 0) rc = launch_gt<D, 0, true, E>(p, stream);
+    else rc = launch_gt<D, 1, true, E>(p, stream);
     if (rc != ROPE_LAUNCH_OK) return rc;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL((decode_merge_kernel<D, E>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p,
                        p.rot_dim);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
@@ -648,5 +648,8 @@ int rope_launch_decode_bf16(const DecodeArgs &a, hipStream_t stream)
     p.G = a.H / a.H_kv;
     p.rot_dim = a.rot_dim;
     p.sl2 = a.scale * 1.4426950408889634f;
-    return a.head_dim == 64 ? launch_d<64>(p, a.layout, stream) : launch_d<128>(p, a.layout, stream);
+    // dtype 0 (bf16) or 2 (fp16): the same kernels over either 16-bit type
+    if (a.dtype == 2)
+        return a.head_dim == 64 ? launch_d<64, _Float16>(p, a.layout, stream) : launch_d<128, _Float16>(p, a.layout, stream);
+    return a.head_dim == 64 ? launch_d<64, __bf16>(p, a.layout, stream) : launch_d<128, __bf16>(p, a.layout, stream);
 }

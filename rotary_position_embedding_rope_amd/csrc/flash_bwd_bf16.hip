@@ -16,8 +16,9 @@
 // k_off + j; with the causal mask key j is visible iff k_off + j <= q_off + i
 // (section 6).
 //
-// Three kernels, enqueued in order on the caller's stream:
-//   * bwd_delta_kernel: delta = rowsum(dO * O) into the workspace;
+// Two kernels, enqueued in order on the caller's stream: bwd_delta_kernel
+// (delta = rowsum(dO * O) into the workspace), then bwd_main_kernel, whose
+// workgroups are of two kinds:
 //   * bwd_dkv_kernel: a workgroup owns 128 keys of one (batch, key/value
 //     head), 32 per wave; K' (rotated once) and V sit in registers as
 //     matrix-core operands while the workgroup walks the query rows that see
@@ -41,11 +42,8 @@
 
 namespace {
 
-using rope::bf16hi_to_f32;
-using rope::bf16lo_to_f32;
-using rope::bf16x8_t;
 using rope::f32x16_t;
-using rope::pack_bf16x2;
+using rope::Ty;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -68,27 +66,35 @@ struct BwdParams {
     float scale, sl2;                       // softmax scale; scale * log2(e)
 };
 
+// E: the 16-bit storage type (__bf16 or _Float16); V8<E>: 8 of them, the
+// matrix-core operand.
+template <typename E> using V8 = typename Ty<E>::v8;
+
+template <typename E>
 __device__ __forceinline__ void unpack8(const uint4 w, float (&x)[8])
 {
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16lo_to_f32(u[i]);
-        x[2 * i + 1] = bf16hi_to_f32(u[i]);
+        x[2 * i] = Ty<E>::lo(u[i]);
+        x[2 * i + 1] = Ty<E>::hi(u[i]);
     }
 }
+template <typename E>
 __device__ __forceinline__ uint4 pack8(const float (&x)[8])
 {
-    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                      pack_bf16x2(x[6], x[7]));
+    return make_uint4(Ty<E>::pack2(x[0], x[1]), Ty<E>::pack2(x[2], x[3]), Ty<E>::pack2(x[4], x[5]),
+                      Ty<E>::pack2(x[6], x[7]));
 }
-__device__ __forceinline__ bf16x8_t to_bf16x8(const float (&x)[8])
+template <typename E>
+__device__ __forceinline__ V8<E> to_v8(const float (&x)[8])
 {
-    return __builtin_bit_cast(bf16x8_t, pack8(x));
+    return __builtin_bit_cast(V8<E>, pack8<E>(x));
 }
-__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c)
+template <typename E>
+__device__ __forceinline__ f32x16_t mfma(V8<E> a, V8<E> b, f32x16_t c)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    return Ty<E>::mfma(a, b, c);
 }
 
 // Staging of row-major [ROWS][D] bf16 tiles into LDS, in units a thread loads
@@ -107,7 +113,7 @@ struct Unit {
     float4 c0, c1, s0, s1;      // cos / sin of the unit's frequencies
 };
 
-template <int D, int LAYOUT, int ROTD, int ROWS, int NTH>
+template <int D, int LAYOUT, int ROTD, int ROWS, int NTH, typename E>
 struct Stager {
     using G = Geo<D, LAYOUT, ROTD>;
     static constexpr int NU = (ROWS * G::UPR + NTH - 1) / NTH;
@@ -160,11 +166,11 @@ struct Stager {
             const Unit &x = u[n];
             uint16_t *row = lds + r * P;
             float a[8];
-            unpack8(x.a, a);
+            unpack8<E>(x.a, a);
             if (k < G::NROT) {
                 if constexpr (LAYOUT == 0) {
                     float b[8], lo[8], hi[8];
-                    unpack8(x.b, b);
+                    unpack8<E>(x.b, b);
                     const float c[8] = {x.c0.x, x.c0.y, x.c0.z, x.c0.w, x.c1.x, x.c1.y, x.c1.z, x.c1.w};
                     const float s[8] = {x.s0.x, x.s0.y, x.s0.z, x.s0.w, x.s1.x, x.s1.y, x.s1.z, x.s1.w};
 #pragma unroll
@@ -172,8 +178,8 @@ struct Stager {
                         lo[e] = (a[e] * c[e] - b[e] * s[e]) * mul;
                         hi[e] = (a[e] * s[e] + b[e] * c[e]) * mul;
                     }
-                    *reinterpret_cast<uint4 *>(row + 8 * k) = pack8(lo);
-                    *reinterpret_cast<uint4 *>(row + 8 * k + ROTD / 2) = pack8(hi);
+                    *reinterpret_cast<uint4 *>(row + 8 * k) = pack8<E>(lo);
+                    *reinterpret_cast<uint4 *>(row + 8 * k + ROTD / 2) = pack8<E>(hi);
                 } else {
                     const float c[4] = {x.c0.x, x.c0.y, x.c0.z, x.c0.w};
                     const float s[4] = {x.s0.x, x.s0.y, x.s0.z, x.s0.w};
@@ -183,12 +189,12 @@ struct Stager {
                         y[2 * m] = (a[2 * m] * c[m] - a[2 * m + 1] * s[m]) * mul;
                         y[2 * m + 1] = (a[2 * m] * s[m] + a[2 * m + 1] * c[m]) * mul;
                     }
-                    *reinterpret_cast<uint4 *>(row + 8 * k) = pack8(y);
+                    *reinterpret_cast<uint4 *>(row + 8 * k) = pack8<E>(y);
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) a[e] *= mul;
-                *reinterpret_cast<uint4 *>(row + ROTD + 8 * (k - G::NROT)) = pack8(a);
+                *reinterpret_cast<uint4 *>(row + ROTD + 8 * (k - G::NROT)) = pack8<E>(a);
             }
         }
     }
@@ -198,17 +204,17 @@ struct Stager {
 // holds dims 16 s + 8 hh .. + 7 of step s, rotated at pos (NeoX partners sit
 // rot/32 steps later in the same lane; GPT-J pairs are adjacent), multiplied
 // by mul and rounded to bf16.  An invalid row is zero.
-template <int D, int LAYOUT, int ROTD>
+template <int D, int LAYOUT, int ROTD, typename E>
 __device__ __forceinline__ void row_operand(const uint16_t *row, bool valid, int64_t pos, float mul,
                                             const float *cos_tab, const float *sin_tab, int hh,
-                                            bf16x8_t (&out)[D / 16])
+                                            V8<E> (&out)[D / 16])
 {
     constexpr int NS = D / 16;
     float x[NS][8];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const uint4 w = valid ? *reinterpret_cast<const uint4 *>(row + 16 * s + 8 * hh) : make_uint4(0, 0, 0, 0);
-        unpack8(w, x[s]);
+        unpack8<E>(w, x[s]);
     }
     if constexpr (ROTD > 0) {
         if (valid) {
@@ -250,7 +256,7 @@ __device__ __forceinline__ void row_operand(const uint16_t *row, bool valid, int
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[s][e] *= mul;
-        out[s] = to_bf16x8(x[s]);
+        out[s] = to_v8<E>(x[s]);
     }
 }
 
@@ -301,7 +307,7 @@ __device__ __forceinline__ void unrotate(f32x16_t (&acc)[D / 32], int64_t pos, c
 }
 
 // One row (acc layout above), times mul, rounded to bf16, 8-byte stores.
-template <int D>
+template <int D, typename E>
 __device__ __forceinline__ void store_row(uint16_t *row, const f32x16_t (&acc)[D / 32], float mul, int hh)
 {
 #pragma unroll
@@ -309,8 +315,8 @@ __device__ __forceinline__ void store_row(uint16_t *row, const f32x16_t (&acc)[D
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint2 w;
-            w.x = pack_bf16x2(acc[bd][4 * i] * mul, acc[bd][4 * i + 1] * mul);
-            w.y = pack_bf16x2(acc[bd][4 * i + 2] * mul, acc[bd][4 * i + 3] * mul);
+            w.x = Ty<E>::pack2(acc[bd][4 * i] * mul, acc[bd][4 * i + 1] * mul);
+            w.y = Ty<E>::pack2(acc[bd][4 * i + 2] * mul, acc[bd][4 * i + 3] * mul);
             *reinterpret_cast<uint2 *>(row + 32 * bd + 8 * i + 4 * hh) = w;
         }
 }
@@ -319,28 +325,29 @@ __device__ __forceinline__ void store_row(uint16_t *row, const f32x16_t (&acc)[D
 // lane l gets column 32 bd + l % 32 of rows 16 mm + 4 (l / 32) + {0..3} and
 // the same + 8 -- the row order in which a score accumulator's rows 8 i +
 // 4 (l / 32) + j, i = 2 mm, 2 mm + 1, leave as a B operand.
-template <int P>
-__device__ __forceinline__ bf16x8_t tr_operand(const uint16_t *T, int mm, int bd, int tr_row0, int tr_col)
+template <int P, typename E>
+__device__ __forceinline__ V8<E> tr_operand(const uint16_t *T, int mm, int bd, int tr_row0, int tr_col)
 {
     const uint16_t *src = T + (16 * mm + tr_row0) * P + 32 * bd + tr_col;
     const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
     const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * P));
-    return __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+    return __builtin_bit_cast(V8<E>, (short __attribute__((ext_vector_type(8)))){
                                             x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
 }
 
 // rows 8 mm .. 8 mm + 7 of a score accumulator, rounded: the B operand of
 // 16-row step mm
-__device__ __forceinline__ bf16x8_t acc_operand(const float (&v)[16], int mm)
+template <typename E>
+__device__ __forceinline__ V8<E> acc_operand(const float (&v)[16], int mm)
 {
     const float x[8] = {v[8 * mm], v[8 * mm + 1], v[8 * mm + 2], v[8 * mm + 3],
                         v[8 * mm + 4], v[8 * mm + 5], v[8 * mm + 6], v[8 * mm + 7]};
-    return to_bf16x8(x);
+    return to_v8<E>(x);
 }
 
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O), D/8 lanes per row.
-template <int D>
+template <int D, typename E>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const uint16_t *dout, float *delta,
                                                         int64_t rows)
 {
@@ -350,8 +357,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const
     float acc = 0.f;
     if (r < rows) {
         float a[8], b[8];
-        unpack8(*reinterpret_cast<const uint4 *>(o + r * D + 8 * c), a);
-        unpack8(*reinterpret_cast<const uint4 *>(dout + r * D + 8 * c), b);
+        unpack8<E>(*reinterpret_cast<const uint4 *>(o + r * D + 8 * c), a);
+        unpack8<E>(*reinterpret_cast<const uint4 *>(dout + r * D + 8 * c), b);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
     }
@@ -398,7 +405,7 @@ struct Lds {
 // dK, dV: 128 keys of one (batch, key/value head) per workgroup; blk orders
 // the tiles heaviest first (with the causal mask the first keys see the most
 // queries).
-template <int D, int LAYOUT, int ROTD>
+template <int D, int LAYOUT, int ROTD, typename E>
 __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned char *smem)
 {
     constexpr int NH = Halves<D>::NH, NTH = 256 * NH, ROWS = TILE * NH;
@@ -421,11 +428,11 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
     const int g16 = lane >> 4, lp = lane & 15;
     const int tr_row0 = 4 * (g16 >> 1) + (lp >> 2), tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
 
-    bf16x8_t kb[NS], vb[NS];
+    V8<E> kb[NS], vb[NS];
     const uint16_t *krow = p.k + ((int64_t)bkv * p.Sk + key) * D;
     const uint16_t *vrow = p.v + ((int64_t)bkv * p.Sk + key) * D;
-    row_operand<D, LAYOUT, ROTD>(krow, kvalid, p.k_off + key, 1.f, p.cos_tab, p.sin_tab, hh, kb);
-    row_operand<D, 0, 0>(vrow, kvalid, 0, 1.f, nullptr, nullptr, hh, vb);
+    row_operand<D, LAYOUT, ROTD, E>(krow, kvalid, p.k_off + key, 1.f, p.cos_tab, p.sin_tab, hh, kb);
+    row_operand<D, 0, 0, E>(vrow, kvalid, 0, 1.f, nullptr, nullptr, hh, vb);
     f32x16_t dk[DB], dv[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) dk[i] = dv[i] = (f32x16_t){};
@@ -440,8 +447,8 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
     const int nsteps = i0 < p.Sq ? (int)((p.Sq - i0 + ROWS - 1) / ROWS) : 0;
     const int total = nsteps * p.kv_group;
 
-    Stager<D, LAYOUT, ROTD, ROWS, NTH> qst;
-    Stager<D, 0, 0, ROWS, NTH> dost;
+    Stager<D, LAYOUT, ROTD, ROWS, NTH, E> qst;
+    Stager<D, 0, 0, ROWS, NTH, E> dost;
     float lse_r = 0.f, dl_r = 0.f;   // thread tid < ROWS: row tid of the tile
     auto fetch = [&](int t) {
         const int g = t / nsteps;
@@ -481,10 +488,10 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
         f32x16_t s = {}, dp = {};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(qt_lds + l32 * P + 16 * st + 8 * hh);
-            s = mfma(aq, kb[st], s);
-            const bf16x8_t ao = *reinterpret_cast<const bf16x8_t *>(dot_lds + l32 * P + 16 * st + 8 * hh);
-            dp = mfma(ao, vb[st], dp);
+            const V8<E> aq = *reinterpret_cast<const V8<E> *>(qt_lds + l32 * P + 16 * st + 8 * hh);
+            s = mfma<E>(aq, kb[st], s);
+            const V8<E> ao = *reinterpret_cast<const V8<E> *>(dot_lds + l32 * P + 16 * st + 8 * hh);
+            dp = mfma<E>(ao, vb[st], dp);
         }
         // the mask only where the diagonal crosses the wave's 32 x 32 block:
         // row offset r sees this lane's key iff r >= thr
@@ -510,11 +517,11 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
         // dV^T += dO^T P,  dK^T += Q'^T dS
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-            const bf16x8_t bp = acc_operand(pv, mm), bs = acc_operand(dsv, mm);
+            const V8<E> bp = acc_operand<E>(pv, mm), bs = acc_operand<E>(dsv, mm);
 #pragma unroll
             for (int bd = 0; bd < DB; ++bd) {
-                dv[bd] = mfma(tr_operand<P>(dot_lds, mm, bd, tr_row0, tr_col), bp, dv[bd]);
-                dk[bd] = mfma(tr_operand<P>(qt_lds, mm, bd, tr_row0, tr_col), bs, dk[bd]);
+                dv[bd] = mfma<E>(tr_operand<P, E>(dot_lds, mm, bd, tr_row0, tr_col), bp, dv[bd]);
+                dk[bd] = mfma<E>(tr_operand<P, E>(qt_lds, mm, bd, tr_row0, tr_col), bs, dk[bd]);
             }
         }
         if (t + 1 < total) store(buf ^ 1);
@@ -530,14 +537,14 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
     if (half != 0 || !kvalid) return;
     // dK' = scale dS^T Q' = ln 2 * (dS^T (scale log2(e) Q')), then back to K's frame
     unrotate<D, LAYOUT, ROTD>(dk, p.k_off + key, p.cos_tab, p.sin_tab, hh);
-    store_row<D>(p.dk + ((int64_t)bkv * p.Sk + key) * D, dk, LN2, hh);
-    store_row<D>(p.dv + ((int64_t)bkv * p.Sk + key) * D, dv, 1.f, hh);
+    store_row<D, E>(p.dk + ((int64_t)bkv * p.Sk + key) * D, dk, LN2, hh);
+    store_row<D, E>(p.dv + ((int64_t)bkv * p.Sk + key) * D, dv, 1.f, hh);
 }
 
 // ---------------------------------------------------------------------------
 // dQ: 128 query rows of one (batch, head) per workgroup; blk orders the tiles
 // heaviest first (with the causal mask the last rows see the most keys).
-template <int D, int LAYOUT, int ROTD>
+template <int D, int LAYOUT, int ROTD, typename E>
 __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned char *smem)
 {
     constexpr int NH = Halves<D>::NH, NTH = 256 * NH, ROWS = TILE * NH;
@@ -558,10 +565,10 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
     const int g16 = lane >> 4, lp = lane & 15;
     const int tr_row0 = 4 * (g16 >> 1) + (lp >> 2), tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
 
-    bf16x8_t qb[NS], ob[NS];
-    row_operand<D, LAYOUT, ROTD>(p.q + ((int64_t)bh * p.Sq + qi) * D, qvalid, p.q_off + qi, p.sl2, p.cos_tab,
+    V8<E> qb[NS], ob[NS];
+    row_operand<D, LAYOUT, ROTD, E>(p.q + ((int64_t)bh * p.Sq + qi) * D, qvalid, p.q_off + qi, p.sl2, p.cos_tab,
                                  p.sin_tab, hh, qb);
-    row_operand<D, 0, 0>(p.dout + ((int64_t)bh * p.Sq + qi) * D, qvalid, 0, 1.f, nullptr, nullptr, hh, ob);
+    row_operand<D, 0, 0, E>(p.dout + ((int64_t)bh * p.Sq + qi) * D, qvalid, 0, 1.f, nullptr, nullptr, hh, ob);
     const float lse2 = qvalid ? p.lse[(int64_t)bh * p.Sq + qi] * LOG2E : INFINITY;
     const float dl = qvalid ? p.delta[(int64_t)bh * p.Sq + qi] : 0.f;
     f32x16_t dq[DB];
@@ -577,8 +584,8 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
     }
     const int total = nk > 0 ? (int)((nk + ROWS - 1) / ROWS) : 0;
 
-    Stager<D, LAYOUT, ROTD, ROWS, NTH> kst;
-    Stager<D, 0, 0, ROWS, NTH> vst;
+    Stager<D, LAYOUT, ROTD, ROWS, NTH, E> kst;
+    Stager<D, 0, 0, ROWS, NTH, E> vst;
     const uint16_t *kh = p.k + bkv * p.Sk * D, *vh = p.v + bkv * p.Sk * D;
     auto fetch = [&](int t) {
         const int64_t j = (int64_t)t * ROWS;
@@ -606,10 +613,10 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
         f32x16_t s = {}, dp = {};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(kt_lds + l32 * P + 16 * st + 8 * hh);
-            s = mfma(ak, qb[st], s);
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(vt_lds + l32 * P + 16 * st + 8 * hh);
-            dp = mfma(av, ob[st], dp);
+            const V8<E> ak = *reinterpret_cast<const V8<E> *>(kt_lds + l32 * P + 16 * st + 8 * hh);
+            s = mfma<E>(ak, qb[st], s);
+            const V8<E> av = *reinterpret_cast<const V8<E> *>(vt_lds + l32 * P + 16 * st + 8 * hh);
+            dp = mfma<E>(av, ob[st], dp);
         }
         // key offset c of the block is visible iff c <= lim: the mask only
         // where the diagonal or the end of the keys crosses the wave's block
@@ -630,10 +637,10 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
         // dQ^T += K'^T dS
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-            const bf16x8_t bs = acc_operand(dsv, mm);
+            const V8<E> bs = acc_operand<E>(dsv, mm);
 #pragma unroll
             for (int bd = 0; bd < DB; ++bd)
-                dq[bd] = mfma(tr_operand<P>(kt_lds, mm, bd, tr_row0, tr_col), bs, dq[bd]);
+                dq[bd] = mfma<E>(tr_operand<P, E>(kt_lds, mm, bd, tr_row0, tr_col), bs, dq[bd]);
         }
         if (t + 1 < total) store(buf ^ 1);
         if (t + 2 < total) fetch(t + 2);
@@ -644,48 +651,69 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
     if (half != 0 || !qvalid) return;
     // dQ' = scale dS K', then back to Q's frame
     unrotate<D, LAYOUT, ROTD>(dq, p.q_off + qi, p.cos_tab, p.sin_tab, hh);
-    store_row<D>(p.dq + ((int64_t)bh * p.Sq + qi) * D, dq, p.scale, hh);
+    store_row<D, E>(p.dq + ((int64_t)bh * p.Sq + qi) * D, dq, p.scale, hh);
 }
 
 // dK/dV and dQ workgroups in one launch: the two lists, each heaviest first,
 // interleaved, so that light tiles of one fill in around heavy tiles of the
 // other (with the causal mask the heavy dK/dV tiles are the light dQ tiles).
-template <int D, int LAYOUT, int ROTD>
+template <int D, int LAYOUT, int ROTD, typename E>
 __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_main_kernel(BwdParams p, int n_dkv, int n_dq)
 {
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<D>::BYTES];
     const int blk = blockIdx.x;
     const int m = n_dkv < n_dq ? n_dkv : n_dq;
     if (blk < 2 * m) {
-        if (blk & 1) dq_block<D, LAYOUT, ROTD>(p, blk >> 1, smem);
-        else dkv_block<D, LAYOUT, ROTD>(p, blk >> 1, smem);
+        if (blk & 1) dq_block<D, LAYOUT, ROTD, E>(p, blk >> 1, smem);
+        else dkv_block<D, LAYOUT, ROTD, E>(p, blk >> 1, smem);
     } else if (n_dkv > n_dq) {
-        dkv_block<D, LAYOUT, ROTD>(p, blk - m, smem);
+        dkv_block<D, LAYOUT, ROTD, E>(p, blk - m, smem);
     } else {
-        dq_block<D, LAYOUT, ROTD>(p, blk - m, smem);
+        dq_block<D, LAYOUT, ROTD, E>(p, blk - m, smem);
     }
 }
 
-template <int D, int LAYOUT, int ROTD>
+template <int D, int LAYOUT, int ROTD, typename E>
 int launch_all(const BwdParams &p, hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Sq;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_delta_kernel<D, E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
                        p.o, p.dout, p.delta, rows);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     constexpr int NTH = 256 * Halves<D>::NH;
     const int n_dkv = p.B * p.Hkv * p.n_ktiles, n_dq = p.B * p.H * p.n_qtiles;
-    hipLaunchKernelGGL((bwd_main_kernel<D, LAYOUT, ROTD>), dim3((unsigned)(n_dkv + n_dq)), dim3(NTH), 0, stream,
+    hipLaunchKernelGGL((bwd_main_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)(n_dkv + n_dq)), dim3(NTH), 0, stream,
                        p, n_dkv, n_dq);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 
-template <int D, int ROTD>
+template <int D, int ROTD, typename E>
 int launch_rot(const BwdParams &p, int layout, hipStream_t stream)
 {
-    if constexpr (ROTD == 0) return launch_all<D, 0, 0>(p, stream);
-    else return layout == 0 ? launch_all<D, 0, ROTD>(p, stream) : launch_all<D, 1, ROTD>(p, stream);
+    if constexpr (ROTD == 0) return launch_all<D, 0, 0, E>(p, stream);
+    else return layout == 0 ? launch_all<D, 0, ROTD, E>(p, stream) : launch_all<D, 1, ROTD, E>(p, stream);
+}
+
+template <typename E>
+int launch_typed(const BwdParams &p, int head_dim, int rot_dim, int layout, hipStream_t stream)
+{
+    if (head_dim == 64) {
+        switch (rot_dim) {
+        case 0: return launch_rot<64, 0, E>(p, layout, stream);
+        case 32: return launch_rot<64, 32, E>(p, layout, stream);
+        case 64: return launch_rot<64, 64, E>(p, layout, stream);
+        default: return ROPE_LAUNCH_ERR;
+        }
+    }
+    switch (rot_dim) {
+    case 0: return launch_rot<128, 0, E>(p, layout, stream);
+    case 32: return launch_rot<128, 32, E>(p, layout, stream);
+    case 64: return launch_rot<128, 64, E>(p, layout, stream);
+    case 96: return launch_rot<128, 96, E>(p, layout, stream);
+    case 128: return launch_rot<128, 128, E>(p, layout, stream);
+    default: return ROPE_LAUNCH_ERR;
+    }
 }
 
 }  // namespace
@@ -716,20 +744,7 @@ int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream)
     p.n_ktiles = (int)((a.Sk + WG_ROWS - 1) / WG_ROWS);
     p.scale = a.scale;
     p.sl2 = a.scale * LOG2E;
-    if (a.head_dim == 64) {
-        switch (a.rot_dim) {
-        case 0: return launch_rot<64, 0>(p, a.layout, stream);
-        case 32: return launch_rot<64, 32>(p, a.layout, stream);
-        case 64: return launch_rot<64, 64>(p, a.layout, stream);
-        default: return ROPE_LAUNCH_ERR;
-        }
-    }
-    switch (a.rot_dim) {
-    case 0: return launch_rot<128, 0>(p, a.layout, stream);
-    case 32: return launch_rot<128, 32>(p, a.layout, stream);
-    case 64: return launch_rot<128, 64>(p, a.layout, stream);
-    case 96: return launch_rot<128, 96>(p, a.layout, stream);
-    case 128: return launch_rot<128, 128>(p, a.layout, stream);
-    default: return ROPE_LAUNCH_ERR;
-    }
+    // dtype 0 (bf16) or 2 (fp16): the same kernels over either 16-bit type
+    return a.dtype == 2 ? launch_typed<_Float16>(p, a.head_dim, a.rot_dim, a.layout, stream)
+                        : launch_typed<__bf16>(p, a.head_dim, a.rot_dim, a.layout, stream);
 }

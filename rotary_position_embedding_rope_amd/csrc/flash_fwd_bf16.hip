@@ -176,43 +176,7 @@ __device__ inline int64_t share_of(int64_t x, int64_t U, int G)
     return w;
 }
 
-// The 16-bit storage types: bf16 and IEEE fp16.  Each gives the widening of
-// the low / high half of a 32-bit word, the rounding (to nearest even) of two
-// floats into one word, the matrix-core product of its type and the sum of a
-// word's two halves into an fp32 accumulator (one v_dot2 against (1, 1)).
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-template <typename E> struct Ty;
-template <> struct Ty<__bf16> {
-    using v8 = bf16x8_t;
-    static __device__ __forceinline__ float lo(uint32_t w) { return rope::bf16lo_to_f32(w); }
-    static __device__ __forceinline__ float hi(uint32_t w) { return rope::bf16hi_to_f32(w); }
-    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
-    static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
-    {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(rope::bf16x2_t, w),
-                                               __builtin_bit_cast(rope::bf16x2_t, 0x3f803f80u), acc, false);
-    }
-};
-template <> struct Ty<_Float16> {
-    using v8 = f16x8_t;
-    static __device__ __forceinline__ float lo(uint32_t w) { return rope::f16lo_to_f32(w); }
-    static __device__ __forceinline__ float hi(uint32_t w) { return rope::f16hi_to_f32(w); }
-    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return rope::pack_f16x2(a, b); }
-    static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float sum2(uint32_t w, float acc)
-    {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u),
-                                      acc, false);
-    }
-};
+using rope::Ty;
 
 template <typename E>
 __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8])

@@ -238,7 +238,7 @@ def decode_args(**over):
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(Hkv=2), _lib.ERR_UNSUPPORTED),           # 16 query heads per key/value head
     (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
-    (dict(dtype=_lib.F16), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=_lib.F16, q=None), _lib.ERR_NULL),    # fp16 accepted
     (dict(layout=7), _lib.ERR_UNSUPPORTED),
     (dict(q=None), _lib.ERR_NULL),
     (dict(lens=None), _lib.ERR_NULL),
@@ -298,7 +298,7 @@ def bwd_args(**over):
     (dict(dv=FAKE4 + 0x300000), _lib.ERR_SHAPE),  # dv aliases dq
     (dict(wsb=1024), _lib.ERR_SHAPE),             # workspace too small (4096 rows x 8 heads x 4 B)
     (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
-    (dict(dtype=_lib.F16), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=_lib.F16, lse=None), _lib.ERR_NULL),  # fp16 accepted
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(rot=48), _lib.ERR_UNSUPPORTED),
     (dict(layout=3), _lib.ERR_UNSUPPORTED),

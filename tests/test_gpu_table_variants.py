@@ -212,10 +212,62 @@ def test_fused_fp16(orc, case):
     assert err <= F16_TOL, err
 
 
-def test_decode_and_backward_reject_fp16():
-    q = torch.zeros((1, 2, 128, 64), dtype=torch.float16, device=DEV)
-    with pytest.raises(api.RopeError):
-        api.bwd_workspace(q)
+# fp16 backward: the bf16 bars with fp16's 2^-11 in place of bf16's rounding:
+# max |err| <= 5e-3 max |ref| + 1e-5, rms(err) <= 2.5e-3 rms(ref) + 1e-5.
+@pytest.mark.parametrize("case", [(1, 4, 2, 160, 160, 64, "neox", 64, 0),
+                                  (1, 2, 1, 96, 400, 128, "gptj", 128, 304)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_backward_fp16(orc, case):
+    B, H, Hkv, Sq, Sk, D, layout, rot, q_off = case
+    w = wl.AttentionWorkload("f16_bwd", B, H, Sq, Sk, D, "f16", 60 + Sq, layout, base=1e4,
+                             q_off=q_off, H_kv=Hkv)
+    q, k, v = wl.attention_inputs(w)
+    dout = wl.round_to(np.random.default_rng(61).standard_normal(q.shape), "f16")
+    c, s = api.tables_build(w.base, rot, w.table_rows, device=DEV)
+    tq, tk, tv, tdo = (to_dev(a, "f16") for a in (q, k, v, dout))
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    o = api.flash_attn_fwd(tq, tk, tv, c, s, q_pos_offset=q_off, rot_dim=rot, layout=layout, lse=lse)
+    grads = api.flash_attn_bwd(tq, tk, tv, o, lse, tdo, c, s, q_pos_offset=q_off, rot_dim=rot,
+                               layout=layout)
+    torch.cuda.synchronize()
+    refs = orc.attention_bwd(q, k, v, dout, q_off=q_off, rot_dim=rot, base=w.base, layout=layout)
+    for g, r in zip(grads, refs):
+        assert g.dtype == torch.float16
+        err = np.abs(to64(g) - r)
+        assert err.max() <= 5e-3 * np.abs(r).max() + 1e-5
+        assert np.sqrt(np.mean(err ** 2)) <= 2.5e-3 * np.sqrt(np.mean(r ** 2)) + 1e-5
+
+
+def test_decode_fp16(orc):
+    """One fp16 decode step against the oracle (bar 5e-3, as the fp16 fused
+    forward), the appended key within one fp16 ulp, the value exact."""
+    B, H, Hkv, D, S_max = 4, 8, 2, 128, 1500
+    w = wl.DecodeWorkload("decode_f16", B, H, Hkv, D, S_max, 81, layout="neox", base=1e4, rot_dim=D)
+    d = wl.decode_inputs(w)
+    lens = np.array([0, 511, 512, 1499], dtype=np.int32)
+    qd, kn, vn = (wl.round_to(d[n], "f16") for n in ("q", "k_new", "v_new"))
+    kraw, vc = wl.round_to(d["k_raw"], "f16"), wl.round_to(d["v_cache"], "f16")
+    kc = kraw.copy()
+    for b, L in enumerate(lens):
+        kc[b, :, :L] = wl.round_to(orc.rope(kraw[b, :, :L], np.arange(L), base=w.base,
+                                            layout="neox").astype(np.float32), "f16")
+    tk, tv = to_dev(kc, "f16"), to_dev(vc, "f16")
+    c, s = api.tables_build(w.base, D, S_max, device=DEV)
+    out = api.decode_attn_fwd(to_dev(qd, "f16"), to_dev(kn, "f16"), to_dev(vn, "f16"), tk, tv,
+                              torch.from_numpy(lens).to(DEV), c, s, layout="neox")
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16
+    got, kcg, vcg = to64(out), to64(tk), to64(tv)
+    for b, L in enumerate(lens):
+        L = int(L)
+        kk = np.concatenate([kraw[b, :, :L], kn[b][:, None]], axis=1)
+        vv = np.concatenate([vc[b, :, :L], vn[b][:, None]], axis=1)
+        want = orc.attention(qd[b][None, :, None], kk[None], vv[None], q_off=L, base=w.base,
+                             layout="neox")[0, :, 0]
+        assert np.abs(got[b] - want).max() <= F16_TOL, b
+        knew = orc.rope(kn[b][:, None], [L], base=w.base, layout="neox")[:, 0]
+        assert (np.abs(kcg[b, :, L] - knew) <= ulp(knew, "f16")).all()
+        assert np.array_equal(vcg[b, :, L], vn[b].astype(np.float64))
 
 
 # --------------------------------------------------------------------------
