@@ -484,8 +484,17 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
         const int64_t i = i0 + (int64_t)(t % nsteps) * ROWS + TILE * half;
         const uint16_t *qt_lds = q_lds[buf] + TILE * half * P, *dot_lds = do_lds[buf] + TILE * half * P;
         const float *lse_h = lse_lds[buf] + TILE * half, *dl_h = dl_lds[buf] + TILE * half;
-        // S (queries x keys) and dP = dO V^T: a lane owns key column l32
-        f32x16_t s = {}, dp = {};
+        // S - lse (queries x keys) and dP - delta = dO V^T - delta, the
+        // accumulators seeded with the row statistics: a lane owns key
+        // column l32, its accumulator element 4 ii + j row 8 ii + 4 hh + j
+        f32x16_t s, dp;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const float4 l4 = *reinterpret_cast<const float4 *>(lse_h + 8 * ii + 4 * hh);
+            const float4 d4 = *reinterpret_cast<const float4 *>(dl_h + 8 * ii + 4 * hh);
+            s[4 * ii] = -l4.x; s[4 * ii + 1] = -l4.y; s[4 * ii + 2] = -l4.z; s[4 * ii + 3] = -l4.w;
+            dp[4 * ii] = -d4.x; dp[4 * ii + 1] = -d4.y; dp[4 * ii + 2] = -d4.z; dp[4 * ii + 3] = -d4.w;
+        }
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             const V8<E> aq = *reinterpret_cast<const V8<E> *>(qt_lds + l32 * P + 16 * st + 8 * hh);
@@ -493,27 +502,20 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
             const V8<E> ao = *reinterpret_cast<const V8<E> *>(dot_lds + l32 * P + 16 * st + 8 * hh);
             dp = mfma<E>(ao, vb[st], dp);
         }
-        // the mask only where the diagonal crosses the wave's 32 x 32 block:
-        // row offset r sees this lane's key iff r >= thr
-        int thr = -1;
-        if (p.causal && p.k_off + kt * (int64_t)WG_ROWS + wv * WROWS + WROWS - 1 > p.q_off + i) {
-            const int64_t t64 = p.k_off + key - p.q_off - i;
-            thr = t64 < -1 ? -1 : (t64 > WROWS ? WROWS : (int)t64);
-        }
         float pv[16], dsv[16];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const float4 l4 = *reinterpret_cast<const float4 *>(lse_h + 8 * ii + 4 * hh);
-            const float4 d4 = *reinterpret_cast<const float4 *>(dl_h + 8 * ii + 4 * hh);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(s[r]);
+        // the mask only where the diagonal crosses the wave's 32 x 32 block
+        // (a wave-uniform test): row offset r sees this lane's key iff r >= thr
+        if (p.causal && p.k_off + kt * (int64_t)WG_ROWS + wv * WROWS + WROWS - 1 > p.q_off + i) {
+            const int64_t t64 = p.k_off + key - p.q_off - i;
+            const int thr = t64 < -1 ? -1 : (t64 > WROWS ? WROWS : (int)t64);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f(s[4 * ii + j] - lv[j]);
-                const float pr = 8 * ii + 4 * hh + j >= thr ? e : 0.f;
-                pv[4 * ii + j] = pr;
-                dsv[4 * ii + j] = pr * (dp[4 * ii + j] - dv4[j]);
-            }
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + 4 * hh + (r & 3) < thr) pv[r] = 0.f;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsv[r] = pv[r] * dp[r];
         // dV^T += dO^T P,  dK^T += Q'^T dS
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
@@ -609,8 +611,14 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
         // this half's 32 keys of the tile
         const int64_t j0 = (int64_t)t * ROWS + TILE * half;
         const uint16_t *kt_lds = k_lds[buf] + TILE * half * P, *vt_lds = v_lds[buf] + TILE * half * P;
-        // S^T (keys x queries) and dP^T = V dO^T: a lane owns query column l32
-        f32x16_t s = {}, dp = {};
+        // S^T - lse and dP^T - delta (keys x queries), the accumulators
+        // seeded with this lane's row statistics: a lane owns query column l32
+        f32x16_t s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = -lse2;
+            dp[r] = -dl;
+        }
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             const V8<E> ak = *reinterpret_cast<const V8<E> *>(kt_lds + l32 * P + 16 * st + 8 * hh);
@@ -618,22 +626,23 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
             const V8<E> av = *reinterpret_cast<const V8<E> *>(vt_lds + l32 * P + 16 * st + 8 * hh);
             dp = mfma<E>(av, ob[st], dp);
         }
+        float pr[16], dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r]);
         // key offset c of the block is visible iff c <= lim: the mask only
         // where the diagonal or the end of the keys crosses the wave's block
-        int lim = WROWS;
+        // (a wave-uniform test)
         if (j0 + WROWS > p.Sk ||
             (p.causal && p.k_off + j0 + WROWS - 1 > p.q_off + (int64_t)qt * WG_ROWS + wv * WROWS)) {
             int64_t l64 = p.Sk - 1 - j0;
             if (p.causal && p.q_off + qi - p.k_off - j0 < l64) l64 = p.q_off + qi - p.k_off - j0;
-            lim = l64 < -1 ? -1 : (l64 > WROWS ? WROWS : (int)l64);
-        }
-        float dsv[16];
+            const int lim = l64 < -1 ? -1 : (l64 > WROWS ? WROWS : (int)l64);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[r] - lse2);
-            const float pr = 8 * (r >> 2) + 4 * hh + (r & 3) <= lim ? e : 0.f;
-            dsv[r] = pr * (dp[r] - dl);
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + 4 * hh + (r & 3) > lim) pr[r] = 0.f;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsv[r] = pr[r] * dp[r];
         // dQ^T += K'^T dS
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
