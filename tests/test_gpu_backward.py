@@ -206,3 +206,32 @@ def test_backward_full_size_sampled(orc, w):
     rot_dk = orc.rope(dk, np.broadcast_to(kpos, dk.shape[:3]), base=w.base, layout=w.layout)
     s = rot_dk.sum(axis=2)
     assert np.abs(s).max() <= 2e-2 * np.abs(dk).sum(axis=2).max()
+
+
+def test_lse_balanced_schedule(orc):
+    """The balanced (split query tile) schedule writes each row's log-sum-exp
+    from the merge of its pieces: the same bar as the default schedule."""
+    w = wl.AttentionWorkload("causal_neox_bf16_1x8x2048x64", 1, 8, 2048, 2048, 64, "bf16", 3, "neox")
+    q, k, v = wl.attention_inputs(w)
+    tq, tk, tv = bf16(q), bf16(k), bf16(v)
+    c, s = api.tables_build(w.base, w.rot, w.table_rows, device=DEV)
+    ws = api.workspace_for(tq, w.Sk, 0, 0, True)
+    assert ws is not None   # this shape runs the balanced schedule (see the parity tests)
+    lse = torch.full((1, 8, 2048), float("nan"), dtype=torch.float32, device=DEV)
+    api.flash_attn_fwd(tq, tk, tv, c, s, layout="neox", lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    want = orc.attention_lse(q, k, base=w.base, layout="neox")
+    assert (np.abs(to64(lse) - want) <= lse_bound(q, k, 64)).all()
+
+
+def test_lse_fp32_forward(orc):
+    """The fp32 forward's log-sum-exp: fp32 scores, so within 1e-5."""
+    w = wl.TINY_F32
+    q, k, v = wl.attention_inputs(w)
+    t = [torch.from_numpy(a).to(DEV) for a in (q, k, v)]
+    c, s = api.tables_build(w.base, w.rot, w.table_rows, device=DEV)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    api.flash_attn_fwd(*t, c, s, layout=w.layout, lse=lse)
+    torch.cuda.synchronize()
+    want = orc.attention_lse(q, k, base=w.base, layout=w.layout)
+    assert np.abs(to64(lse) - want).max() <= 1e-5

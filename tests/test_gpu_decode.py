@@ -142,6 +142,7 @@ MIXED_CASES = [
     (40, 4, 4, 64, 3000, "gptj", 64, 2),
     (24, 16, 2, 128, 4000, "neox", 128, 3),    # 8 query heads per key/value head
     (33, 6, 3, 64, 1500, "neox", 32, 4),
+    (300, 2, 1, 64, 200, "gptj", 64, 5),      # more requests than the scans' 256 / 64 chunks
 ]
 
 
