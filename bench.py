@@ -180,8 +180,9 @@ def bench_rope_apply(torch, api, wl, steps, sets, w=None):
 
 def bench_backward(torch, api, wl, steps, warmup):
     """The backward of the fused forward on the bench workload: one step is
-    the three kernels of rope_flash_attn_bwd (row sums, dK/dV, dQ), inputs
-    and the forward's output and row statistics resident in HBM."""
+    the two kernels of rope_flash_attn_bwd (the row sums dO.O, then the
+    merged dK/dV and dQ launch), inputs and the forward's output and row
+    statistics resident in HBM."""
     w = wl.HEADLINE
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in wl.attention_inputs(w))
@@ -204,7 +205,9 @@ def bench_backward(torch, api, wl, steps, warmup):
         "single_step_p10_ms": round(durs[len(durs) // 10], 5),
         "single_step_p90_ms": round(durs[(9 * len(durs)) // 10], 5),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(f"flash_bwd_bf16_{w.name}_traffic.md",
+                                                 "flash_bwd_bf16.hip"),
                      "algorithmic_flops": flops},
     }
 
