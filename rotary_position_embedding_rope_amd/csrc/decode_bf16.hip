@@ -83,6 +83,26 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, int byte_off)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+__device__ __forceinline__ void bload(rsrc_t r, int byte_off, uint4 &x) { x = bload16(r, byte_off); }
+__device__ __forceinline__ void bload(rsrc_t r, int byte_off, uint2 &x)
+{
+    x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// The value-side shape of the chunk kernel.  Each lane of the P V product
+// holds DPL dims of one value row for all query slots: 8 dims (16-byte
+// loads), except with 8 query heads at D = 128, where 8 x 8 fp32 sums per
+// lane would leave room for only one workgroup per compute unit; there a
+// lane takes 4 dims (8-byte loads) and the loads run one pass ahead instead
+// of two, which brings the kernel under 256 registers.
+template <int D, int GT>
+struct ChunkShape {
+    static constexpr bool WIDE = GT == 8 && D == 128;
+    static constexpr int DPL = WIDE ? 4 : 8;     // value dims per lane
+    static constexpr int NSET = WIDE ? 2 : 3;    // register sets of loads (passes in flight + 1)
+};
+template <int DPL> struct VChunk { using type = uint4; };
+template <> struct VChunk<4> { using type = uint2; };
 
 // The two dims of rotation pair i (i < rot_dim / 2): NeoX pairs dim i with
 // i + rot_dim/2, GPT-J pairs 2i with 2i + 1; pair indices past rot_dim/2
@@ -118,6 +138,10 @@ __device__ __forceinline__ uint4 pick(bool c, uint4 a, uint4 b)
 {
     return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
+__device__ __forceinline__ uint2 pick(bool c, uint2 a, uint2 b)
+{
+    return make_uint2(c ? a.x : b.x, c ? a.y : b.y);
+}
 
 // A run of passes.  The workgroup walks its passes in order with two cursors
 // (one for the loads, two passes ahead, one for the arithmetic); a slice's
@@ -134,14 +158,17 @@ __device__ __forceinline__ uint4 pick(bool c, uint4 a, uint4 b)
 // v_mfma_f32_16x16x32_bf16, K straight from the loads in the A-operand
 // layout (lane l: key l%16, dims 8(l/16) .. +7 of each 32-dim step), Q'
 // (rotated, scaled, rounded to bf16) as the B operand, query slots past G
-// zero.  P V runs on the vector ALU, each key row split over D/8 lanes.  Each
+// zero.  P V runs on the vector ALU, each key row split over D/DPL lanes.  Each
 // wave runs its own online softmax over its keys; the four waves are merged
 // once per piece.
 template <int D, int LAYOUT, bool ROT, int GT, typename E>
 __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 {
     using V8 = typename Ty<E>::v8;
-    constexpr int LPR = D / 8;          // lanes per value row (16 bytes each)
+    using Shape = ChunkShape<D, GT>;
+    constexpr int DPL = Shape::DPL;
+    using VC = typename VChunk<DPL>::type;
+    constexpr int LPR = D / DPL;        // lanes per value row (DPL dims each)
     constexpr int KPI = 64 / LPR;       // value rows per wave load
     constexpr int KPW = SUB / 4;        // keys per wave and pass (16)
     constexpr int NV = KPW / KPI;       // value loads per wave and pass
@@ -240,7 +267,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
     // ---- loads of one pass (issued two passes early) ----
     const int kl = lane % 16, kq = lane / 16;      // score layout: key, dim quarter
     const int vrow = lane / LPR, vsub = lane % LPR; // value layout: row, 16-byte chunk
-    auto issue = [&](const Cursor &c, uint4 (&kd)[NT], uint4 (&vd)[NV]) {
+    auto issue = [&](const Cursor &c, uint4 (&kd)[NT], VC (&vd)[NV]) {
         const int ks = c.s * SUB;
         const int64_t slice = ((int64_t)c.b * p.Hkv + c.kvh) * p.S_max;
         // cached rows [ks, min(L, ks + SUB)); the row at L reads as zero here
@@ -253,12 +280,12 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int key = wave * KPW + i * KPI + vrow;
-            vd[i] = bload16(vrs, 2 * (key * D + 8 * vsub));
+            bload(vrs, 2 * (key * D + DPL * vsub), vd[i]);
         }
     };
 
     V8 qb[NT];
-    float oacc[GT][8];
+    float oacc[GT][DPL];
     float m_run = -INFINITY, l_run = 0.f;
 
     // ---- start of a piece: the slice's queries (and new key) at position L ----
@@ -323,7 +350,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 #pragma unroll
         for (int g = 0; g < GT; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[g][e] = 0.f;
+            for (int e = 0; e < DPL; ++e) oacc[g][e] = 0.f;
         m_run = -INFINITY;
         l_run = 0.f;
     };
@@ -331,7 +358,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
     // Each wave keeps its own running max and sum over its keys, for query
     // slot kl in lanes kl, kl+16, kl+32, kl+48 (MFMA layout); the waves'
     // states are merged once per piece, so the passes need no barrier.
-    auto pass = [&](const Cursor &c, const uint4 (&kd)[NT], const uint4 (&vd)[NV]) {
+    auto pass = [&](const Cursor &c, const uint4 (&kd)[NT], const VC (&vd)[NV]) {
         const int ks = c.s * SUB;
         const int L = c.L, n = L + 1;
         // scores of the wave's 16 keys for all query slots
@@ -382,17 +409,17 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
         for (int g = 0; g < GT; ++g) {
             const float a = a_lds[wave][g];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[g][e] *= a;
+            for (int e = 0; e < DPL; ++e) oacc[g][e] *= a;
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int key = i * KPI + vrow;   // within the wave's block
-            const uint4 vn = *reinterpret_cast<const uint4 *>(vnew_lds + 8 * vsub);
-            const uint4 wv = pick(ks + wave * KPW + key == L, vn, vd[i]);
-            const uint32_t u[4] = {wv.x, wv.y, wv.z, wv.w};
-            float vf[8];
+            const VC vn = *reinterpret_cast<const VC *>(vnew_lds + DPL * vsub);
+            const VC wv = pick(ks + wave * KPW + key == L, vn, vd[i]);
+            const uint32_t *u = reinterpret_cast<const uint32_t *>(&wv);
+            float vf[DPL];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < DPL / 2; ++e) {
                 vf[2 * e] = Ty<E>::lo(u[e]);
                 vf[2 * e + 1] = Ty<E>::hi(u[e]);
             }
@@ -400,7 +427,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
             for (int g = 0; g < GT; ++g) {
                 const float pg = p_lds[wave][g][key];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) oacc[g][e] = fmaf(pg, vf[e], oacc[g][e]);
+                for (int e = 0; e < DPL; ++e) oacc[g][e] = fmaf(pg, vf[e], oacc[g][e]);
             }
         }
     };
@@ -410,7 +437,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
 #pragma unroll
         for (int g = 0; g < GT; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < DPL; ++e) {
                 float x = oacc[g][e];
 #pragma unroll
                 for (int m = LPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
@@ -419,9 +446,10 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
         if (lane < LPR) {
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                float4 *dst = reinterpret_cast<float4 *>(&o_lds[wave][g][8 * lane]);
-                dst[0] = make_float4(oacc[g][0], oacc[g][1], oacc[g][2], oacc[g][3]);
-                dst[1] = make_float4(oacc[g][4], oacc[g][5], oacc[g][6], oacc[g][7]);
+                float4 *dst = reinterpret_cast<float4 *>(&o_lds[wave][g][DPL * lane]);
+#pragma unroll
+                for (int e = 0; e < DPL; e += 4)
+                    dst[e / 4] = make_float4(oacc[g][e], oacc[g][e + 1], oacc[g][e + 2], oacc[g][e + 3]);
             }
         }
         if (kq == 0 && kl < GT) {
@@ -452,17 +480,39 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeParams p)
     };
 
     const int npass = (int)(hi - lo);
-    auto step = [&](int t, Cursor &c, const uint4 (&kd)[NT], const uint4 (&vd)[NV]) {
+    auto step = [&](int t, Cursor &c, const uint4 (&kd)[NT], const VC (&vd)[NV]) {
         if (t == 0 || c.s == 0) setup(c);
         pass(c, kd, vd);
         if (t == npass - 1 || c.s == c.np - 1) finish(c);
         if (t + 1 < npass) advance(c);
     };
 
+    Cursor ci = c0, cc = c0;
+    if constexpr (Shape::NSET == 2) {
+        // two register sets: the loads of pass t+1 are in flight while pass t
+        // is computed
+        uint4 kd0[NT], kd1[NT];
+        VC vd0[NV], vd1[NV];
+        issue(ci, kd0, vd0);
+        for (int t = 0; t < npass; t += 2) {
+            if (t + 1 < npass) {
+                advance(ci);
+                issue(ci, kd1, vd1);
+            }
+            step(t, cc, kd0, vd0);
+            if (t + 1 >= npass) break;
+            if (t + 2 < npass) {
+                advance(ci);
+                issue(ci, kd0, vd0);
+            }
+            step(t + 1, cc, kd1, vd1);
+        }
+        return;
+    }
     // three register sets: the loads of passes t+1 and t+2 are in flight
     // while pass t is computed
-    uint4 kd0[NT], vd0[NV], kd1[NT], vd1[NV], kd2[NT], vd2[NV];
-    Cursor ci = c0, cc = c0;
+    uint4 kd0[NT], kd1[NT], kd2[NT];
+    VC vd0[NV], vd1[NV], vd2[NV];
     issue(ci, kd0, vd0);
     if (npass > 1) {
         advance(ci);

@@ -115,6 +115,7 @@ DECODE_CASES = [
     (3, 8, 1, 64, 900, "gptj", 32, [5, 300, 899]),                         # 8 per head, partial rot
     (2, 6, 2, 128, 600, "neox", 64, [77, 599]),                            # 3 per head
     (2, 16, 8, 128, 300, "neox", 0, [0, 299]),                             # no rotation
+    (3, 16, 2, 128, 800, "gptj", 64, [0, 300, 799]),                       # 8 per head at D = 128
     (4, 32, 8, 128, 2100, "neox", 128, [2047, 2048, 2049, 2099]),          # bench head counts
 ]
 
