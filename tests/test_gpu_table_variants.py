@@ -238,10 +238,12 @@ def test_backward_fp16(orc, case):
         assert np.sqrt(np.mean(err ** 2)) <= 2.5e-3 * np.sqrt(np.mean(r ** 2)) + 1e-5
 
 
-def test_decode_fp16(orc):
+@pytest.mark.parametrize("H", [8, 16], ids=["4q_per_kv", "8q_per_kv"])
+def test_decode_fp16(orc, H):
     """One fp16 decode step against the oracle (bar 5e-3, as the fp16 fused
-    forward), the appended key within one fp16 ulp, the value exact."""
-    B, H, Hkv, D, S_max = 4, 8, 2, 128, 1500
+    forward), the appended key within one fp16 ulp, the value exact.  Eight
+    query heads per key/value head take the 4-dims-per-lane value layout."""
+    B, Hkv, D, S_max = 4, 2, 128, 1500
     w = wl.DecodeWorkload("decode_f16", B, H, Hkv, D, S_max, 81, layout="neox", base=1e4, rot_dim=D)
     d = wl.decode_inputs(w)
     lens = np.array([0, 511, 512, 1499], dtype=np.int32)
