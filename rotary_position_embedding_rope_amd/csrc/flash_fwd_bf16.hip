@@ -631,12 +631,18 @@ void flash_fwd_bf16_kernel(Params p)
                     continue;
                 }
                 uint4 w0 = r0[i], w1 = r1[i];
+                // slots past rot_dim rotate by angle 0 (cos 1, sin 0), which
+                // gives back their input values
+                const bool rot_slot = FULL || ki[i].mode != 0;
                 if constexpr (ROT && LAYOUT == 0) {
                     float lo[8], hi[8], cc[8], ss[8];
                     unpack8<E>(r0[i], lo);
                     unpack8<E>(r1[i], hi);
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) { cc[u] = c[i][u]; ss[u] = s[i][u]; }
+                    for (int u = 0; u < 8; ++u) {
+                        cc[u] = rot_slot ? c[i][u] : 1.f;
+                        ss[u] = rot_slot ? s[i][u] : 0.f;
+                    }
                     rotate_pairs<8>(lo, hi, cc, ss);
                     w0 = pack8<E>(lo);
                     w1 = pack8<E>(hi);
@@ -651,7 +657,8 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             a[u] = x[h][2 * u]; bb[u] = x[h][2 * u + 1];
-                            cc[u] = c[i][4 * h + u]; ss[u] = s[i][4 * h + u];
+                            cc[u] = rot_slot ? c[i][4 * h + u] : 1.f;
+                            ss[u] = rot_slot ? s[i][4 * h + u] : 0.f;
                         }
                         rotate_pairs<4>(a, bb, cc, ss);
 #pragma unroll
@@ -659,12 +666,6 @@ void flash_fwd_bf16_kernel(Params p)
                     }
                     w0 = pack8<E>(x[0]);
                     w1 = pack8<E>(x[1]);
-                }
-                if constexpr (ROT && !FULL) {
-                    // slots past rot_dim keep their input bits
-                    const bool rot_slot = ki[i].mode != 0;
-                    w0 = rot_slot ? w0 : r0[i];
-                    w1 = rot_slot ? w1 : r1[i];
                 }
                 *reinterpret_cast<uint4 *>(row + ki[i].o0) = w0;
                 *reinterpret_cast<uint4 *>(row + ki[i].o1) = w1;

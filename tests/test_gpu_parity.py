@@ -343,6 +343,11 @@ EDGE_CASES = [
     (1, 1, 65, 65, 128, "f32", "gptj", 0, 0, 0, False),         # fp32, no rotation
     (1, 2, 320, 320, 64, "bf16", "neox", 64, 0, 0, True),       # odd number of 64-row halves
     (1, 1, 448, 600, 64, "bf16", "gptj", 64, 152, 0, True),     # offset mask, D=64, paired halves
+    # partial rotation at D = 64 over many key tiles (both phases of a
+    # workgroup): the slots past rot_dim go through the rotation at angle 0
+    (1, 3, 1000, 1000, 64, "bf16", "neox", 32, 7, 7, True),
+    (1, 2, 700, 900, 64, "bf16", "gptj", 32, 200, 0, True),
+    (1, 2, 333, 333, 64, "bf16", "gptj", 32, 0, 0, False),
 ]
 
 
