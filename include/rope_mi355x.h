@@ -238,10 +238,11 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
  *   (else ROPE_ERR_UNSUPPORTED).
  *   workspace   device scratch of at least rope_flash_attn_bwd_workspace_size()
  *               bytes, 16-byte aligned, contents irrelevant (per-row
- *               rowsum(dout * o)).  Calls that share a workspace must not run
- *               concurrently.
- * Two kernels are enqueued on `stream`: the row sums, then dk/dv and dq
- * in one launch.
+ *               rowsum(dout * o); with rotation, also q rotated and scaled
+ *               and k rotated, once, in the storage type).  Calls that share
+ *               a workspace must not run concurrently.
+ * Kernels enqueued on `stream`: with rot_dim > 0 the rotation of q and k
+ * into the workspace, then the row sums, then dk/dv and dq in one launch.
  * Accumulation is fp32; the rotated Q/K, dout, V, P and dS enter the matrix
  * cores rounded to the storage type.
  */
@@ -255,10 +256,14 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
 
 /*
  * rope_flash_attn_bwd_workspace_size -- bytes of workspace rope_flash_attn_bwd
- * needs: B * H * Sq * 4 rounded up to a multiple of 256, or minus a status
- * code for shapes or types it would reject.  No HIP call.
+ * needs for these shapes: B * H * Sq * 4 rounded up to a multiple of 256,
+ * plus, when rot_dim > 0, B * H * Sq * head_dim * 2 and
+ * B * H_kv * Sk * head_dim * 2, each rounded up to a multiple of 256.
+ * Minus a status code for shapes or types it would reject (H_kv must divide
+ * H, 0 <= rot_dim <= head_dim).  No HIP call.
  */
-int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_dim, int dtype);
+int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
+                                           int rot_dim, int dtype);
 
 /*
  * rope_decode_attn_fwd -- one decode step over a key/value cache: rotate the

@@ -49,7 +49,7 @@ def load() -> ctypes.CDLL:
     lib.rope_flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32,
                                         i64, i64, vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     lib.rope_flash_attn_bwd.restype = i32
-    lib.rope_flash_attn_bwd_workspace_size.argtypes = [i32, i32, i64, i32, i32]
+    lib.rope_flash_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i64, i64, i32, i32, i32]
     lib.rope_flash_attn_bwd_workspace_size.restype = i64
     lib.rope_decode_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32,
                                          vp, vp, i64, i32, i32, f32, i32, vp, i64, vp]

@@ -333,12 +333,13 @@ def prepare_decode_attn_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, 
     return launch
 
 
-def bwd_workspace(q: torch.Tensor) -> torch.Tensor:
-    """Workspace for flash_attn_bwd on q's shape, cached per device and grown
-    on demand.  Calls sharing it must be serialised (one stream)."""
+def bwd_workspace(q: torch.Tensor, k: torch.Tensor, rot_dim: int) -> torch.Tensor:
+    """Workspace for flash_attn_bwd on q's and k's shapes, cached per device
+    and grown on demand.  Calls sharing it must be serialised (one stream)."""
     lib = _lib.load()
     B, H, Sq, D = q.shape
-    need = lib.rope_flash_attn_bwd_workspace_size(B, H, Sq, D, _dtype(q))
+    need = lib.rope_flash_attn_bwd_workspace_size(B, H, k.shape[1], Sq, k.shape[2], D, int(rot_dim),
+                                                  _dtype(q))
     if need < 0:
         raise RopeError(-need, "rope_flash_attn_bwd_workspace_size")
     key = ("bwd", q.device)
@@ -375,7 +376,7 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_o
         cp, sp, rows = cos.data_ptr(), sin.data_ptr(), cos.shape[0]
     else:
         cp, sp, rows = None, None, 0
-    ws = bwd_workspace(q) if workspace is None else workspace
+    ws = bwd_workspace(q, k, rot_dim) if workspace is None else workspace
     return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Sq, Sk, D, int(q_pos_offset),
             int(k_pos_offset), cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),

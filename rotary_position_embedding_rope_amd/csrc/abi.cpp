@@ -198,13 +198,16 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
 }
 
-int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int64_t Sq, int head_dim, int dtype)
+int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
+                                           int rot_dim, int dtype)
 {
-    if (B < 1 || H < 1 || Sq < 1 || Sq > 2147483647) return -ROPE_ERR_SHAPE;
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0) return -ROPE_ERR_SHAPE;
+    if (Sq < 1 || Sk < 1 || Sq > 2147483647 || Sk > 2147483647) return -ROPE_ERR_SHAPE;
     if (head_dim < 2 || head_dim % 2 != 0) return -ROPE_ERR_SHAPE;
+    if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return -ROPE_ERR_SHAPE;
     if ((dtype != ROPE_BF16 && dtype != ROPE_F16) || (head_dim != 64 && head_dim != 128))
         return -ROPE_ERR_UNSUPPORTED;
-    return rope_flash_bwd_workspace_bytes(B, H, Sq);
+    return rope_flash_bwd_workspace_bytes(B, H, H_kv, Sq, Sk, head_dim, rot_dim);
 }
 
 int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -229,6 +232,9 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
     if ((int64_t)B * H * ((Sq + 127) / 128) > kMaxGrid || (int64_t)B * H_kv * ((Sk + 127) / 128) > kMaxGrid ||
         (Sq / 32 + 1) * (int64_t)(H / H_kv) > 2147483647)
         return ROPE_ERR_SHAPE;
+    // the rotation pre-pass: one block per 32-row tile of q and of k
+    if (rot_dim > 0 && (int64_t)B * H * ((Sq + 31) / 32) + (int64_t)B * H_kv * ((Sk + 31) / 32) > kMaxGrid)
+        return ROPE_ERR_SHAPE;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
     const void *ins[6] = {q, k, v, o, dout, lse};
@@ -245,7 +251,8 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4))
         return ROPE_ERR_ALIGN;
-    if (workspace_bytes < rope_flash_bwd_workspace_bytes(B, H, Sq)) return ROPE_ERR_SHAPE;
+    if (workspace_bytes < rope_flash_bwd_workspace_bytes(B, H, H_kv, Sq, Sk, head_dim, rot_dim))
+        return ROPE_ERR_SHAPE;
 
     FlashBwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;

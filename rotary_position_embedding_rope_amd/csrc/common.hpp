@@ -162,7 +162,7 @@ struct FlashBwdArgs {
     void *workspace;                    // rope_flash_bwd_workspace_bytes() bytes
 };
 int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream);
-int64_t rope_flash_bwd_workspace_bytes(int B, int H, int64_t Sq);
+int64_t rope_flash_bwd_workspace_bytes(int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim, int rot_dim);
 
 struct DecodeArgs {
     const void *q, *k_new, *v_new;   // [B, H, D], [B, H_kv, D], [B, H_kv, D]

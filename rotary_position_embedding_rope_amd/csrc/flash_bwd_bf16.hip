@@ -16,18 +16,20 @@
 // k_off + j; with the causal mask key j is visible iff k_off + j <= q_off + i
 // (section 6).
 //
-// Two kernels, enqueued in order on the caller's stream: bwd_delta_kernel
-// (delta = rowsum(dO * O) into the workspace), then bwd_main_kernel, whose
-// workgroups are of two kinds:
+// Kernels, enqueued in order on the caller's stream: with rotation,
+// bwd_rotate_kernel (Q' = rope(Q) * scale * log2(e) and K' = rope(K), once,
+// rounded, into the workspace); bwd_delta_kernel (delta = rowsum(dO * O)
+// into the workspace); then bwd_main_kernel, whose workgroups are of two
+// kinds:
 //   * bwd_dkv_kernel: a workgroup owns 128 keys of one (batch, key/value
-//     head), 32 per wave; K' (rotated once) and V sit in registers as
+//     head), 32 per wave; K' and V sit in registers as
 //     matrix-core operands while the workgroup walks the query rows that see
-//     them, 32 at a time, for every query head of the group: Q' (rotated and
-//     scaled by scale * log2(e)) and dO are staged in LDS, one tile ahead, and
+//     them, 32 at a time, for every query head of the group: Q' and dO are
+//     staged in LDS as plain copies, one tile ahead, and
 //     dK^T, dV^T accumulate in registers, so the head-group sum needs no
 //     atomics;
 //   * bwd_dq_kernel: a workgroup owns 128 query rows of one head, 32 per
-//     wave; Q' and dO sit in registers while K' (rotated at staging) and V
+//     wave; Q' and dO sit in registers while K' and V
 //     tiles of 32 keys stream through LDS, one tile ahead; dQ^T accumulates
 //     in registers.
 // Every product is v_mfma_f32_32x32x16_bf16.  Score tiles are laid out so
@@ -35,9 +37,9 @@
 // one column (a key in the dK/dV kernel, a query in the dQ kernel), and P and
 // dS leave the accumulator in the B-operand layout of the transposed product;
 // the matching A operand (dO^T, Q'^T or K'^T) comes from ds_read_b64_tr_b16
-// reads of the row-major LDS tile.  The rotation angle's table rows are read
-// at the positions of the rows a thread stages or owns; the un-rotation of
-// dQ' and dK' happens in registers before the single bf16 store.
+// reads of the row-major LDS tile.  The un-rotation of dQ' and dK' happens in
+// registers, with the table rows of the positions a lane owns, before the
+// single bf16 store.
 #include "common.hpp"
 
 namespace {
@@ -154,17 +156,19 @@ struct Stager {
         }
     }
 
-    // the fetched units, rotated and multiplied by mul, into lds (row pitch P)
+    // the fetched units of rows [0, rows), rotated and multiplied by mul,
+    // to dst (row pitch P)
     template <int P>
-    __device__ __forceinline__ void store(uint16_t *lds, float mul, int tid) const
+    __device__ __forceinline__ void store(uint16_t *dst, float mul, int tid, int rows = ROWS) const
     {
 #pragma unroll
         for (int n = 0; n < NU; ++n) {
             const int id = tid + NTH * n;
             if (id >= ROWS * G::UPR) continue;
             const int r = id / G::UPR, k = id % G::UPR;
+            if (r >= rows) continue;
             const Unit &x = u[n];
-            uint16_t *row = lds + r * P;
+            uint16_t *row = dst + r * P;
             float a[8];
             unpack8<E>(x.a, a);
             if (k < G::NROT) {
@@ -367,6 +371,30 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const
     if (c == 0 && r < rows) delta[r] = acc;
 }
 
+// The rotated operands, once: row i of q rotated at q_off + i, multiplied by
+// scale log2(e) and rounded to E; row j of k rotated at k_off + j and
+// rounded.  One 32-row tile of one head per workgroup, query tiles first.
+// The main kernel then stages these rows as plain copies, instead of
+// rotating a query tile again for every key tile that sees it (and a key
+// tile for every query tile).
+template <int D, int LAYOUT, int ROTD, typename E>
+__global__ __launch_bounds__(256) void bwd_rotate_kernel(BwdParams p, const uint16_t *q, const uint16_t *k,
+                                                         uint16_t *qr, uint16_t *kr)
+{
+    const int64_t tq = (p.Sq + TILE - 1) / TILE, tk = (p.Sk + TILE - 1) / TILE;
+    const int64_t nq = (int64_t)p.B * p.H * tq;
+    int64_t blk = blockIdx.x;
+    const bool isq = blk < nq;
+    if (!isq) blk -= nq;
+    const int64_t t = isq ? tq : tk, S = isq ? p.Sq : p.Sk;
+    const int64_t head = blk / t, i = (blk % t) * TILE;
+    const int64_t off = (head * S + i) * D;
+    const int rows = S - i < TILE ? (int)(S - i) : TILE;
+    Stager<D, LAYOUT, ROTD, TILE, 256, E> st;
+    st.fetch((isq ? q : k) + off, rows, (isq ? p.q_off : p.k_off) + i, p.cos_tab, p.sin_tab, threadIdx.x);
+    st.template store<D>((isq ? qr : kr) + off, isq ? p.sl2 : 1.f, threadIdx.x, rows);
+}
+
 // The halves of a workgroup: NH = 2 for D = 64 (8 waves, two per SIMD: the
 // halves take alternate 32-row steps and are summed at the end), NH = 1 for
 // D = 128 (its accumulators leave room for one wave per SIMD).
@@ -431,7 +459,7 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
     V8<E> kb[NS], vb[NS];
     const uint16_t *krow = p.k + ((int64_t)bkv * p.Sk + key) * D;
     const uint16_t *vrow = p.v + ((int64_t)bkv * p.Sk + key) * D;
-    row_operand<D, LAYOUT, ROTD, E>(krow, kvalid, p.k_off + key, 1.f, p.cos_tab, p.sin_tab, hh, kb);
+    row_operand<D, 0, 0, E>(krow, kvalid, 0, 1.f, nullptr, nullptr, hh, kb);   // rotated beforehand
     row_operand<D, 0, 0, E>(vrow, kvalid, 0, 1.f, nullptr, nullptr, hh, vb);
     f32x16_t dk[DB], dv[DB];
 #pragma unroll
@@ -447,7 +475,7 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
     const int nsteps = i0 < p.Sq ? (int)((p.Sq - i0 + ROWS - 1) / ROWS) : 0;
     const int total = nsteps * p.kv_group;
 
-    Stager<D, LAYOUT, ROTD, ROWS, NTH, E> qst;
+    Stager<D, 0, 0, ROWS, NTH, E> qst;   // rotated and scaled beforehand (or scaled at staging)
     Stager<D, 0, 0, ROWS, NTH, E> dost;
     float lse_r = 0.f, dl_r = 0.f;   // thread tid < ROWS: row tid of the tile
     auto fetch = [&](int t) {
@@ -455,7 +483,7 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
         const int64_t i = i0 + (int64_t)(t % nsteps) * ROWS;
         const int64_t bh = (int64_t)b * p.H + kvh * p.kv_group + g;
         const int valid = p.Sq - i < ROWS ? (int)(p.Sq - i) : ROWS;
-        qst.fetch(p.q + (bh * p.Sq + i) * D, valid, p.q_off + i, p.cos_tab, p.sin_tab, tid);
+        qst.fetch(p.q + (bh * p.Sq + i) * D, valid, 0, nullptr, nullptr, tid);
         dost.fetch(p.dout + (bh * p.Sq + i) * D, valid, 0, nullptr, nullptr, tid);
         if (tid < ROWS) {
             const bool ok = tid < valid;
@@ -464,7 +492,7 @@ __device__ __forceinline__ void dkv_block(const BwdParams &p, int blk, unsigned 
         }
     };
     auto store = [&](int buf) {
-        qst.template store<P>(q_lds[buf], p.sl2, tid);
+        qst.template store<P>(q_lds[buf], ROTD > 0 ? 1.f : p.sl2, tid);
         dost.template store<P>(do_lds[buf], 1.f, tid);
         if (tid < ROWS) {
             lse_lds[buf][tid] = lse_r;
@@ -568,8 +596,8 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
     const int tr_row0 = 4 * (g16 >> 1) + (lp >> 2), tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
 
     V8<E> qb[NS], ob[NS];
-    row_operand<D, LAYOUT, ROTD, E>(p.q + ((int64_t)bh * p.Sq + qi) * D, qvalid, p.q_off + qi, p.sl2, p.cos_tab,
-                                 p.sin_tab, hh, qb);
+    row_operand<D, 0, 0, E>(p.q + ((int64_t)bh * p.Sq + qi) * D, qvalid, 0, ROTD > 0 ? 1.f : p.sl2, nullptr,
+                            nullptr, hh, qb);
     row_operand<D, 0, 0, E>(p.dout + ((int64_t)bh * p.Sq + qi) * D, qvalid, 0, 1.f, nullptr, nullptr, hh, ob);
     const float lse2 = qvalid ? p.lse[(int64_t)bh * p.Sq + qi] * LOG2E : INFINITY;
     const float dl = qvalid ? p.delta[(int64_t)bh * p.Sq + qi] : 0.f;
@@ -586,13 +614,13 @@ __device__ __forceinline__ void dq_block(const BwdParams &p, int blk, unsigned c
     }
     const int total = nk > 0 ? (int)((nk + ROWS - 1) / ROWS) : 0;
 
-    Stager<D, LAYOUT, ROTD, ROWS, NTH, E> kst;
+    Stager<D, 0, 0, ROWS, NTH, E> kst;   // rotated beforehand
     Stager<D, 0, 0, ROWS, NTH, E> vst;
     const uint16_t *kh = p.k + bkv * p.Sk * D, *vh = p.v + bkv * p.Sk * D;
     auto fetch = [&](int t) {
         const int64_t j = (int64_t)t * ROWS;
         const int valid = p.Sk - j < ROWS ? (int)(p.Sk - j) : ROWS;
-        kst.fetch(kh + j * D, valid, p.k_off + j, p.cos_tab, p.sin_tab, tid);
+        kst.fetch(kh + j * D, valid, 0, nullptr, nullptr, tid);
         vst.fetch(vh + j * D, valid, 0, nullptr, nullptr, tid);
     };
     auto store = [&](int buf) {
@@ -683,9 +711,18 @@ __global__ __launch_bounds__(256 * Halves<D>::NH) void bwd_main_kernel(BwdParams
 }
 
 template <int D, int LAYOUT, int ROTD, typename E>
-int launch_all(const BwdParams &p, hipStream_t stream)
+int launch_all(BwdParams p, uint16_t *qr, uint16_t *kr, hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    if constexpr (ROTD > 0) {
+        const int64_t nblk = (int64_t)p.B * p.H * ((p.Sq + TILE - 1) / TILE) +
+                             (int64_t)p.B * p.Hkv * ((p.Sk + TILE - 1) / TILE);
+        hipLaunchKernelGGL((bwd_rotate_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)nblk), dim3(256), 0, stream, p,
+                           p.q, p.k, qr, kr);
+        if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
+        p.q = qr;
+        p.k = kr;
+    }
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<D, E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
                        p.o, p.dout, p.delta, rows);
@@ -698,38 +735,48 @@ int launch_all(const BwdParams &p, hipStream_t stream)
 }
 
 template <int D, int ROTD, typename E>
-int launch_rot(const BwdParams &p, int layout, hipStream_t stream)
+int launch_rot(const BwdParams &p, int layout, uint16_t *qr, uint16_t *kr, hipStream_t stream)
 {
-    if constexpr (ROTD == 0) return launch_all<D, 0, 0, E>(p, stream);
-    else return layout == 0 ? launch_all<D, 0, ROTD, E>(p, stream) : launch_all<D, 1, ROTD, E>(p, stream);
+    if constexpr (ROTD == 0) return launch_all<D, 0, 0, E>(p, qr, kr, stream);
+    else
+        return layout == 0 ? launch_all<D, 0, ROTD, E>(p, qr, kr, stream)
+                           : launch_all<D, 1, ROTD, E>(p, qr, kr, stream);
 }
 
 template <typename E>
-int launch_typed(const BwdParams &p, int head_dim, int rot_dim, int layout, hipStream_t stream)
+int launch_typed(const BwdParams &p, int head_dim, int rot_dim, int layout, uint16_t *qr, uint16_t *kr,
+                 hipStream_t stream)
 {
     if (head_dim == 64) {
         switch (rot_dim) {
-        case 0: return launch_rot<64, 0, E>(p, layout, stream);
-        case 32: return launch_rot<64, 32, E>(p, layout, stream);
-        case 64: return launch_rot<64, 64, E>(p, layout, stream);
+        case 0: return launch_rot<64, 0, E>(p, layout, qr, kr, stream);
+        case 32: return launch_rot<64, 32, E>(p, layout, qr, kr, stream);
+        case 64: return launch_rot<64, 64, E>(p, layout, qr, kr, stream);
         default: return ROPE_LAUNCH_ERR;
         }
     }
     switch (rot_dim) {
-    case 0: return launch_rot<128, 0, E>(p, layout, stream);
-    case 32: return launch_rot<128, 32, E>(p, layout, stream);
-    case 64: return launch_rot<128, 64, E>(p, layout, stream);
-    case 96: return launch_rot<128, 96, E>(p, layout, stream);
-    case 128: return launch_rot<128, 128, E>(p, layout, stream);
+    case 0: return launch_rot<128, 0, E>(p, layout, qr, kr, stream);
+    case 32: return launch_rot<128, 32, E>(p, layout, qr, kr, stream);
+    case 64: return launch_rot<128, 64, E>(p, layout, qr, kr, stream);
+    case 96: return launch_rot<128, 96, E>(p, layout, qr, kr, stream);
+    case 128: return launch_rot<128, 128, E>(p, layout, qr, kr, stream);
     default: return ROPE_LAUNCH_ERR;
     }
 }
 
 }  // namespace
 
-int64_t rope_flash_bwd_workspace_bytes(int B, int H, int64_t Sq)
+// The row sums dO.O (fp32), then, with rotation, the rotated copies of q and
+// k (E), each from a 256-byte boundary.
+namespace {
+int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+}
+int64_t rope_flash_bwd_workspace_bytes(int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim, int rot_dim)
 {
-    return ((int64_t)B * H * Sq * 4 + 255) / 256 * 256;
+    int64_t n = round256((int64_t)B * H * Sq * 4);
+    if (rot_dim > 0) n += round256((int64_t)B * H * Sq * head_dim * 2) + round256((int64_t)B * H_kv * Sk * head_dim * 2);
+    return n;
 }
 
 int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream)
@@ -742,6 +789,10 @@ int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream)
     p.dout = static_cast<const uint16_t *>(a.dout);
     p.lse = a.lse;
     p.delta = static_cast<float *>(a.workspace);
+    char *const ws = static_cast<char *>(a.workspace);
+    const int64_t q_at = round256((int64_t)a.B * a.H * a.Sq * 4);
+    uint16_t *const qr = reinterpret_cast<uint16_t *>(ws + q_at);
+    uint16_t *const kr = reinterpret_cast<uint16_t *>(ws + q_at + round256((int64_t)a.B * a.H * a.Sq * a.head_dim * 2));
     p.dq = static_cast<uint16_t *>(a.dq);
     p.dk = static_cast<uint16_t *>(a.dk);
     p.dv = static_cast<uint16_t *>(a.dv);
@@ -754,6 +805,6 @@ int rope_launch_flash_bwd_bf16(const FlashBwdArgs &a, hipStream_t stream)
     p.scale = a.scale;
     p.sl2 = a.scale * LOG2E;
     // dtype 0 (bf16) or 2 (fp16): the same kernels over either 16-bit type
-    return a.dtype == 2 ? launch_typed<_Float16>(p, a.head_dim, a.rot_dim, a.layout, stream)
-                        : launch_typed<__bf16>(p, a.head_dim, a.rot_dim, a.layout, stream);
+    return a.dtype == 2 ? launch_typed<_Float16>(p, a.head_dim, a.rot_dim, a.layout, qr, kr, stream)
+                        : launch_typed<__bf16>(p, a.head_dim, a.rot_dim, a.layout, qr, kr, stream);
 }

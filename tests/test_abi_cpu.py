@@ -318,10 +318,18 @@ def test_bwd_rejects(lib, over, want):
 
 
 def test_bwd_workspace_size(lib):
-    assert lib.rope_flash_attn_bwd_workspace_size(1, 8, 4096, 64, _lib.BF16) == 8 * 4096 * 4
-    assert lib.rope_flash_attn_bwd_workspace_size(2, 3, 5, 128, _lib.BF16) == 256
-    assert lib.rope_flash_attn_bwd_workspace_size(1, 8, 0, 64, _lib.BF16) == -_lib.ERR_SHAPE
-    assert lib.rope_flash_attn_bwd_workspace_size(1, 8, 16, 64, _lib.F32) == -_lib.ERR_UNSUPPORTED
+    f = lib.rope_flash_attn_bwd_workspace_size
+    # row sums only without rotation
+    assert f(1, 8, 8, 4096, 4096, 64, 0, _lib.BF16) == 8 * 4096 * 4
+    assert f(2, 3, 3, 5, 5, 128, 0, _lib.BF16) == 256
+    # with rotation: the rotated q and k copies too, each from a 256-byte boundary
+    assert f(1, 8, 8, 4096, 4096, 64, 64, _lib.BF16) == 8 * 4096 * 4 + 2 * 8 * 4096 * 64 * 2
+    assert f(2, 4, 2, 5, 7, 128, 32, _lib.F16) == 256 + 2 * 4 * 5 * 128 * 2 + 2 * 2 * 7 * 128 * 2
+    assert f(1, 2, 1, 3, 3, 64, 64, _lib.BF16) == 256 + 768 + 512
+    assert f(1, 8, 8, 0, 16, 64, 0, _lib.BF16) == -_lib.ERR_SHAPE
+    assert f(1, 8, 3, 16, 16, 64, 0, _lib.BF16) == -_lib.ERR_SHAPE     # H_kv must divide H
+    assert f(1, 8, 8, 16, 16, 64, 66, _lib.BF16) == -_lib.ERR_SHAPE    # rot_dim past head_dim
+    assert f(1, 8, 8, 16, 16, 64, 0, _lib.F32) == -_lib.ERR_UNSUPPORTED
     # the smallest accepted workspace is accepted: validation then reaches the device
     # (not called here); one byte less is rejected
     assert lib.rope_flash_attn_bwd(*bwd_args(wsb=8 * 4096 * 4 - 1)) == _lib.ERR_SHAPE
