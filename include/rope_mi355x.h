@@ -241,8 +241,9 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
  *               rowsum(dout * o); with rotation, also q rotated and scaled
  *               and k rotated, once, in the storage type).  Calls that share
  *               a workspace must not run concurrently.
- * Kernels enqueued on `stream`: with rot_dim > 0 the rotation of q and k
- * into the workspace, then the row sums, then dk/dv and dq in one launch.
+ * Two kernels are enqueued on `stream`: the row sums (with rot_dim > 0 in
+ * the same launch as the rotation of q and k into the workspace), then
+ * dk/dv and dq in one launch.
  * Accumulation is fp32; the rotated Q/K, dout, V, P and dS enter the matrix
  * cores rounded to the storage type.
  */

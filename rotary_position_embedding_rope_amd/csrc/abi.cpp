@@ -232,8 +232,10 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
     if ((int64_t)B * H * ((Sq + 127) / 128) > kMaxGrid || (int64_t)B * H_kv * ((Sk + 127) / 128) > kMaxGrid ||
         (Sq / 32 + 1) * (int64_t)(H / H_kv) > 2147483647)
         return ROPE_ERR_SHAPE;
-    // the rotation pre-pass: one block per 32-row tile of q and of k
-    if (rot_dim > 0 && (int64_t)B * H * ((Sq + 31) / 32) + (int64_t)B * H_kv * ((Sk + 31) / 32) > kMaxGrid)
+    // the pre-pass: one block per 32-row tile of q and of k, then one per 16
+    // (D = 128) or 32 rows of the row sums
+    if (rot_dim > 0 && (int64_t)B * H * ((Sq + 31) / 32) + (int64_t)B * H_kv * ((Sk + 31) / 32) +
+                               ((int64_t)B * H * Sq + 15) / 16 > kMaxGrid)
         return ROPE_ERR_SHAPE;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;

@@ -16,11 +16,11 @@
 // k_off + j; with the causal mask key j is visible iff k_off + j <= q_off + i
 // (section 6).
 //
-// Kernels, enqueued in order on the caller's stream: with rotation,
-// bwd_rotate_kernel (Q' = rope(Q) * scale * log2(e) and K' = rope(K), once,
-// rounded, into the workspace); bwd_delta_kernel (delta = rowsum(dO * O)
-// into the workspace); then bwd_main_kernel, whose workgroups are of two
-// kinds:
+// Two kernels, enqueued in order on the caller's stream: bwd_rotate_kernel
+// (Q' = rope(Q) * scale * log2(e) and K' = rope(K), once, rounded, into the
+// workspace, and delta = rowsum(dO * O) into the workspace; without rotation
+// bwd_delta_kernel computes delta alone); then bwd_main_kernel, whose
+// workgroups are of two kinds:
 //   * bwd_dkv_kernel: a workgroup owns 128 keys of one (batch, key/value
 //     head), 32 per wave; K' and V sit in registers as
 //     matrix-core operands while the workgroup walks the query rows that see
@@ -352,11 +352,11 @@ __device__ __forceinline__ V8<E> acc_operand(const float (&v)[16], int mm)
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O), D/8 lanes per row.
 template <int D, typename E>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const uint16_t *dout, float *delta,
-                                                        int64_t rows)
+__device__ __forceinline__ void delta_rows(const uint16_t *o, const uint16_t *dout, float *delta, int64_t rows,
+                                           int64_t blk)
 {
     constexpr int LPR = D / 8, RPB = 256 / LPR;
-    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int64_t r = blk * RPB + threadIdx.x / LPR;
     const int c = threadIdx.x % LPR;
     float acc = 0.f;
     if (r < rows) {
@@ -371,19 +371,32 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const
     if (c == 0 && r < rows) delta[r] = acc;
 }
 
+template <int D, typename E>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *o, const uint16_t *dout, float *delta,
+                                                        int64_t rows)
+{
+    delta_rows<D, E>(o, dout, delta, rows, blockIdx.x);
+}
+
 // The rotated operands, once: row i of q rotated at q_off + i, multiplied by
 // scale log2(e) and rounded to E; row j of k rotated at k_off + j and
 // rounded.  One 32-row tile of one head per workgroup, query tiles first.
 // The main kernel then stages these rows as plain copies, instead of
 // rotating a query tile again for every key tile that sees it (and a key
 // tile for every query tile).
+// The same launch computes the row sums: blocks past the rotation tiles run
+// bwd_delta_kernel's rows.
 template <int D, int LAYOUT, int ROTD, typename E>
 __global__ __launch_bounds__(256) void bwd_rotate_kernel(BwdParams p, const uint16_t *q, const uint16_t *k,
                                                          uint16_t *qr, uint16_t *kr)
 {
     const int64_t tq = (p.Sq + TILE - 1) / TILE, tk = (p.Sk + TILE - 1) / TILE;
-    const int64_t nq = (int64_t)p.B * p.H * tq;
+    const int64_t nq = (int64_t)p.B * p.H * tq, nrot = nq + (int64_t)p.B * p.Hkv * tk;
     int64_t blk = blockIdx.x;
+    if (blk >= nrot) {
+        delta_rows<D, E>(p.o, p.dout, p.delta, (int64_t)p.B * p.H * p.Sq, blk - nrot);
+        return;
+    }
     const bool isq = blk < nq;
     if (!isq) blk -= nq;
     const int64_t t = isq ? tq : tk, S = isq ? p.Sq : p.Sk;
@@ -714,19 +727,22 @@ template <int D, int LAYOUT, int ROTD, typename E>
 int launch_all(BwdParams p, uint16_t *qr, uint16_t *kr, hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t ndelta = (rows + RPB - 1) / RPB;
     if constexpr (ROTD > 0) {
-        const int64_t nblk = (int64_t)p.B * p.H * ((p.Sq + TILE - 1) / TILE) +
+        // rotation tiles, then the row sums, in one launch
+        const int64_t nrot = (int64_t)p.B * p.H * ((p.Sq + TILE - 1) / TILE) +
                              (int64_t)p.B * p.Hkv * ((p.Sk + TILE - 1) / TILE);
-        hipLaunchKernelGGL((bwd_rotate_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)nblk), dim3(256), 0, stream, p,
-                           p.q, p.k, qr, kr);
+        hipLaunchKernelGGL((bwd_rotate_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)(nrot + ndelta)), dim3(256), 0,
+                           stream, p, p.q, p.k, qr, kr);
         if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
         p.q = qr;
         p.k = kr;
+    } else {
+        hipLaunchKernelGGL((bwd_delta_kernel<D, E>), dim3((unsigned)ndelta), dim3(256), 0, stream, p.o, p.dout,
+                           p.delta, rows);
+        if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     }
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D, E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                       p.o, p.dout, p.delta, rows);
-    if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     constexpr int NTH = 256 * Halves<D>::NH;
     const int n_dkv = p.B * p.Hkv * p.n_ktiles, n_dq = p.B * p.H * p.n_qtiles;
     hipLaunchKernelGGL((bwd_main_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)(n_dkv + n_dq)), dim3(NTH), 0, stream,
