@@ -180,8 +180,8 @@ def bench_rope_apply(torch, api, wl, steps, sets, w=None):
 
 def bench_backward(torch, api, wl, steps, warmup):
     """The backward of the fused forward on the bench workload: one step is
-    the three kernels of rope_flash_attn_bwd (Q and K rotated once into the
-    workspace, the row sums dO.O, then the merged dK/dV and dQ launch),
+    the two kernels of rope_flash_attn_bwd (Q and K rotated once into the
+    workspace with the row sums dO.O, then the merged dK/dV and dQ launch),
     inputs and the forward's output and row statistics resident in HBM."""
     w = wl.HEADLINE
     dev = torch.device("cuda:0")
