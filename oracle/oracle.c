@@ -49,6 +49,9 @@ enum { OR_OK = 0, OR_ERR_ARG = 1, OR_ERR_EMPTY_ROW = 2, OR_ERR_NOMEM = 3 };
 /* Threads an OpenMP region of the oracle uses (reported with its timings). */
 int oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Threads later parallel regions use (n >= 1); for single-thread timings. */
+void oracle_set_threads(int n) { if (n >= 1) omp_set_num_threads(n); }
+
 /* theta_i = base^(-2i/rot_dim): one frequency per rotated pair; the first
  * frequency is 1 for every base.  [RF] section 1; [TR] "Correctness
  * requirements" (table build). */
@@ -364,8 +367,14 @@ int oracle_attention_lse(const double *q, const double *k, double *lse,
  *   dqr_i  = scale sum_j ds_ij kr_j,   dq_i = R(q_pos_i)^T dqr_i
  *   dkr_j  = scale sum_i ds_ij qr_i,   dk_j = R(k_pos_j)^T dkr_j
  * R(pos)^T is the rotation by the opposite angle.  A key/value head's dk and
- * dv sum over every query head that reads it and every query row.  Work is
- * split over (batch, key/value head), so no two threads write one row. */
+ * dv sum over every query head that reads it and every query row.
+ *
+ * Two passes, so that each thread owns the rows it writes:
+ *   1. per query row i: its softmax statistics (max m_i, sum l_i), the row
+ *      correction c_i = sum_j p_ij dp_ij, and dq_i;
+ *   2. per key row j of a key/value head: dk_j and dv_j, summing over the
+ *      query rows of every query head that reads it, with p_ij rebuilt as
+ *      exp(s_ij - m_i) / l_i from the same scores and statistics. */
 int oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dout,
                          double *dq, double *dk, double *dv,
                          int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int D, int Dv,
@@ -382,7 +391,13 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v, cons
     const int64_t nq = B * H * Sq, nk = B * Hkv * Sk, group = H / Hkv;
     double *qr = malloc(sizeof(double) * (size_t)(nq * D));
     double *kr = malloc(sizeof(double) * (size_t)(nk * D));
-    if (!qr || !kr) { free(qr); free(kr); return OR_ERR_NOMEM; }
+    double *row_m = malloc(sizeof(double) * (size_t)nq);
+    double *row_l = malloc(sizeof(double) * (size_t)nq);
+    double *row_c = malloc(sizeof(double) * (size_t)nq);
+    if (!qr || !kr || !row_m || !row_l || !row_c) {
+        free(qr); free(kr); free(row_m); free(row_l); free(row_c);
+        return OR_ERR_NOMEM;
+    }
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < nq; ++r)
         rotate_row(q + r * D, qr + r * D, D, rot_dim, (double)(q_off + r % Sq) / pos_div, base,
@@ -393,73 +408,102 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v, cons
                    layout);
 
     int status = OR_OK;
+    /* Pass 1: per query row, its statistics, its correction and dq. */
 #pragma omp parallel
     {
         double *p = malloc(sizeof(double) * (size_t)Sk);
         double *dp = malloc(sizeof(double) * (size_t)Sk);
         double *dqr = malloc(sizeof(double) * (size_t)D);
-        double *dkr = malloc(sizeof(double) * (size_t)(Sk * D));
-        if (!p || !dp || !dqr || !dkr) {
+        if (!p || !dp || !dqr) {
 #pragma omp atomic write
             status = OR_ERR_NOMEM;
         } else {
-#pragma omp for schedule(dynamic, 1)
-            for (int64_t kvh = 0; kvh < B * Hkv; ++kvh) {
-                const int64_t b = kvh / Hkv;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nq; ++r) {
+                const int64_t bh = r / Sq, i = r % Sq;
+                const int64_t kvh = bh / group;   /* (b * H + h) / group = b * Hkv + h / group */
                 const double *krh = kr + kvh * Sk * D, *vh = v + kvh * Sk * Dv;
-                double *dvh = dv + kvh * Sk * Dv;
-                memset(dkr, 0, sizeof(double) * (size_t)(Sk * D));
-                memset(dvh, 0, sizeof(double) * (size_t)(Sk * Dv));
-                for (int64_t g = 0; g < group; ++g) {
-                    const int64_t bh = b * H + (kvh % Hkv) * group + g;
-                    for (int64_t i = 0; i < Sq; ++i) {
-                        const int64_t r = bh * Sq + i;
-                        const double *qri = qr + r * D, *doi = dout + r * Dv;
-                        const int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
-                        double m = -INFINITY;
-                        for (int64_t j = 0; j < n; ++j) {
-                            double s = 0.0;
-                            for (int d = 0; d < D; ++d) s += qri[d] * krh[j * D + d];
-                            p[j] = s * scale;
-                            if (p[j] > m) m = p[j];
-                        }
-                        double l = 0.0;
-                        for (int64_t j = 0; j < n; ++j) {
-                            p[j] = exp(p[j] - m);
-                            l += p[j];
-                        }
-                        double pdp = 0.0;
-                        for (int64_t j = 0; j < n; ++j) {
-                            p[j] /= l;
-                            double t = 0.0;
-                            for (int e = 0; e < Dv; ++e) t += doi[e] * vh[j * Dv + e];
-                            dp[j] = t;
-                            pdp += p[j] * t;
-                        }
-                        for (int d = 0; d < D; ++d) dqr[d] = 0.0;
-                        for (int64_t j = 0; j < n; ++j) {
-                            const double ds = p[j] * (dp[j] - pdp);
-                            for (int d = 0; d < D; ++d) {
-                                dqr[d] += scale * ds * krh[j * D + d];
-                                dkr[j * D + d] += scale * ds * qri[d];
-                            }
-                            for (int e = 0; e < Dv; ++e) dvh[j * Dv + e] += p[j] * doi[e];
-                        }
-                        rotate_row(dqr, dq + r * D, D, rot_dim, -(double)(q_off + i) / pos_div, base,
-                                   layout);
-                    }
+                const double *qri = qr + r * D, *doi = dout + r * Dv;
+                const int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
+                double m = -INFINITY;
+                for (int64_t j = 0; j < n; ++j) {
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += qri[d] * krh[j * D + d];
+                    p[j] = s * scale;
+                    if (p[j] > m) m = p[j];
                 }
-                for (int64_t j = 0; j < Sk; ++j)
-                    rotate_row(dkr + j * D, dk + (kvh * Sk + j) * D, D, rot_dim,
-                               -(double)(k_off + j) / pos_div, base, layout);
+                double l = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    p[j] = exp(p[j] - m);
+                    l += p[j];
+                }
+                double pdp = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    p[j] /= l;
+                    double t = 0.0;
+                    for (int e = 0; e < Dv; ++e) t += doi[e] * vh[j * Dv + e];
+                    dp[j] = t;
+                    pdp += p[j] * t;
+                }
+                for (int d = 0; d < D; ++d) dqr[d] = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    const double ds = p[j] * (dp[j] - pdp);
+                    for (int d = 0; d < D; ++d) dqr[d] += scale * ds * krh[j * D + d];
+                }
+                rotate_row(dqr, dq + r * D, D, rot_dim, -(double)(q_off + i) / pos_div, base,
+                           layout);
+                row_m[r] = m;
+                row_l[r] = l;
+                row_c[r] = pdp;
             }
         }
         free(p);
         free(dp);
         free(dqr);
-        free(dkr);
+    }
+    /* Pass 2: per key row, dk and dv over every query row that sees it. */
+    if (status == OR_OK) {
+#pragma omp parallel
+        {
+            double *dkr = malloc(sizeof(double) * (size_t)D);
+            if (!dkr) {
+#pragma omp atomic write
+                status = OR_ERR_NOMEM;
+            } else {
+#pragma omp for schedule(dynamic, 16)
+                for (int64_t kr_row = 0; kr_row < nk; ++kr_row) {
+                    const int64_t kvh = kr_row / Sk, j = kr_row % Sk, b = kvh / Hkv;
+                    const double *krj = kr + kr_row * D, *vj = v + kr_row * Dv;
+                    double *dvj = dv + kr_row * Dv;
+                    for (int d = 0; d < D; ++d) dkr[d] = 0.0;
+                    for (int e = 0; e < Dv; ++e) dvj[e] = 0.0;
+                    for (int64_t g = 0; g < group; ++g) {
+                        const int64_t bh = b * H + (kvh % Hkv) * group + g;
+                        for (int64_t i = 0; i < Sq; ++i) {
+                            if (j >= visible_keys(i, Sk, q_off, k_off, causal)) continue;
+                            const int64_t r = bh * Sq + i;
+                            const double *qri = qr + r * D, *doi = dout + r * Dv;
+                            double s = 0.0;
+                            for (int d = 0; d < D; ++d) s += qri[d] * krj[d];
+                            const double pij = exp(s * scale - row_m[r]) / row_l[r];
+                            double dpij = 0.0;
+                            for (int e = 0; e < Dv; ++e) dpij += doi[e] * vj[e];
+                            const double ds = pij * (dpij - row_c[r]);
+                            for (int d = 0; d < D; ++d) dkr[d] += scale * ds * qri[d];
+                            for (int e = 0; e < Dv; ++e) dvj[e] += pij * doi[e];
+                        }
+                    }
+                    rotate_row(dkr, dk + kr_row * D, D, rot_dim, -(double)(k_off + j) / pos_div, base,
+                               layout);
+                }
+            }
+            free(dkr);
+        }
     }
     free(qr);
     free(kr);
+    free(row_m);
+    free(row_l);
+    free(row_c);
     return status;
 }

@@ -36,11 +36,18 @@ MUTATIONS = {
     "bwd_q_unrotated_forward": ("-(double)(q_off + i) / pos_div", "(double)(q_off + i) / pos_div"),
     "bwd_k_unrotated_forward": ("-(double)(k_off + j) / pos_div", "(double)(k_off + j) / pos_div"),
     "bwd_no_row_correction": ("p[j] * (dp[j] - pdp)", "p[j] * dp[j]"),
-    "bwd_dk_unscaled": ("dkr[j * D + d] += scale * ds * qri[d];", "dkr[j * D + d] += ds * qri[d];"),
+    "bwd_no_row_correction_keys": ("pij * (dpij - row_c[r])", "pij * dpij"),
+    "bwd_dk_unscaled": ("dkr[d] += scale * ds * qri[d];", "dkr[d] += ds * qri[d];"),
     "bwd_dq_uses_query": ("dqr[d] += scale * ds * krh[j * D + d];", "dqr[d] += scale * ds * qri[d];"),
-    "bwd_unnormalised_p": ("                            p[j] /= l;\n", ""),
-    "bwd_dv_from_dp": ("dvh[j * Dv + e] += p[j] * doi[e];", "dvh[j * Dv + e] += dp[j] * doi[e];"),
+    "bwd_unnormalised_p": ("                    p[j] /= l;\n", ""),
+    "bwd_keys_unnormalised_p": ("exp(s * scale - row_m[r]) / row_l[r]", "exp(s * scale - row_m[r])"),
+    "bwd_keys_unscaled_scores": ("exp(s * scale - row_m[r])", "exp(s - row_m[r])"),
+    "bwd_dv_from_dp": ("dvj[e] += pij * doi[e];", "dvj[e] += dpij * doi[e];"),
     "bwd_heads_interleaved": ("(kvh % Hkv) * group + g;", "(kvh % Hkv) + g * Hkv;"),
+    "bwd_rows_heads_interleaved": ("const int64_t kvh = bh / group;   /* (b * H + h)",
+                                   "const int64_t kvh = (bh / H) * Hkv + (bh % H) % Hkv;   /* (b * H + h)"),
+    "bwd_keys_mask_off_by_one": ("if (j >= visible_keys(i, Sk, q_off, k_off, causal)) continue;",
+                                 "if (j > visible_keys(i, Sk, q_off, k_off, causal)) continue;"),
     "lse_without_log": ("lse[r] = m + log(l);", "lse[r] = m + l;"),
     "kv_head_count_unchecked": ("if (Hkv <= 0 || H % Hkv != 0) return 0;", "if (Hkv <= 0) return 0;"),
 }
