@@ -82,6 +82,8 @@ class Oracle:
         lib.oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, i64, i64, i64, i64,
                                              i64, i32, i32, i64, i64, i32, dbl, dbl, i32, i32, dbl]
         lib.oracle_threads.argtypes = []
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         for fn in (lib.oracle_rope, lib.oracle_trig, lib.oracle_attention,
                    lib.oracle_attention_rows, lib.oracle_attention_lse, lib.oracle_attention_bwd,
                    lib.oracle_threads):
@@ -91,6 +93,10 @@ class Oracle:
     def threads(self) -> int:
         """OpenMP threads the oracle's parallel regions use."""
         return int(self._lib.oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Use ``n`` OpenMP threads from now on (for single-thread timings)."""
+        self._lib.oracle_set_threads(int(n))
 
     @staticmethod
     def _check(status: int) -> None:
