@@ -8,8 +8,6 @@ device memory and streams.
 """
 from __future__ import annotations
 
-import math
-
 import torch
 
 from . import _lib
@@ -43,7 +41,7 @@ def _dtype(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return _lib.F32
     if t.dtype == torch.float16:
-        return _lib.F16   # rope_apply only; the other entry points report it as unsupported
+        return _lib.F16
     raise TypeError(f"unsupported dtype {t.dtype}; bfloat16, float16 or float32 expected")
 
 
@@ -191,10 +189,6 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out
 
 
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)
-
-
 def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int = 0,
                            k_pos_offset: int = 0, rot_dim: int | None = None, layout="neox",
                            causal: bool = True, softmax_scale: float = 0.0, workspace=None,
@@ -222,6 +216,9 @@ def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int =
         status = fn(*args)
         if status != _lib.OK:
             raise RopeError(status, "rope_flash_attn_fwd")
+    # the callable holds the workspace it launches on: a later call that grows
+    # the per-device cache cannot free it under a prepared launch
+    launch.workspace = workspace
     return launch
 
 
@@ -293,7 +290,7 @@ def _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_di
         cp, sp, rows = None, None, 0
     if workspace is None:
         workspace = decode_workspace(q, k_cache)
-    return (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+    return workspace, (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             cache_lens.data_ptr(), out.data_ptr(), B, H, Hkv, S_max, D, cp, sp, rows, rot,
             _layout(layout), float(softmax_scale), _dtype(q), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _stream(q))
@@ -311,8 +308,8 @@ def decode_attn_fwd(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
-    args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
-                        softmax_scale, out, workspace)
+    _, args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
+                           softmax_scale, out, workspace)
     _check(lib.rope_decode_attn_fwd(*args), "rope_decode_attn_fwd")
     return out
 
@@ -322,14 +319,15 @@ def prepare_decode_attn_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, 
                             softmax_scale: float = 0.0, workspace=None):
     """Validate once and return a zero-argument callable that enqueues the
     decode step on fixed buffers (each call appends at the same positions)."""
-    args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
-                        softmax_scale, out, workspace)
+    ws, args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
+                            softmax_scale, out, workspace)
     fn = _lib.load().rope_decode_attn_fwd
 
     def launch():
         status = fn(*args)
         if status != _lib.OK:
             raise RopeError(status, "rope_decode_attn_fwd")
+    launch.workspace = ws   # kept alive as long as the callable (see prepare_flash_attn_fwd)
     return launch
 
 
@@ -377,7 +375,7 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_o
     else:
         cp, sp, rows = None, None, 0
     ws = bwd_workspace(q, k, rot_dim) if workspace is None else workspace
-    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+    return ws, (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Sq, Sk, D, int(q_pos_offset),
             int(k_pos_offset), cp, sp, rows, int(rot_dim), _layout(layout), int(bool(causal)),
             float(softmax_scale), _dtype(q), ws.data_ptr(), ws.numel() * ws.element_size(),
@@ -395,8 +393,8 @@ def flash_attn_bwd(q, k, v, o, lse, dout, cos=None, sin=None, q_pos_offset: int 
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset,
-                     rot_dim, layout, causal, softmax_scale, workspace)
+    _, args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset,
+                        rot_dim, layout, causal, softmax_scale, workspace)
     _check(lib.rope_flash_attn_bwd(*args), "rope_flash_attn_bwd")
     return dq, dk, dv
 
@@ -407,12 +405,13 @@ def prepare_flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cos=None, sin=None
                            workspace=None):
     """Validate once and return a zero-argument callable that enqueues the
     backward on fixed buffers."""
-    args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset,
-                     rot_dim, layout, causal, softmax_scale, workspace)
+    ws, args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cos, sin, q_pos_offset, k_pos_offset,
+                         rot_dim, layout, causal, softmax_scale, workspace)
     fn = _lib.load().rope_flash_attn_bwd
 
     def launch():
         status = fn(*args)
         if status != _lib.OK:
             raise RopeError(status, "rope_flash_attn_bwd")
+    launch.workspace = ws   # kept alive as long as the callable (see prepare_flash_attn_fwd)
     return launch

@@ -6,15 +6,64 @@
 // allocates device memory or synchronises.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "common.hpp"
 #include "rope_mi355x.h"
 
 namespace {
 
-constexpr int64_t kMaxGrid = 2147483647;   // blocks per 1-D grid
+// Bound on the block counts the launchers form in 32-bit arithmetic; each
+// launcher also checks its exact grid against the 2^32 - 1 work-item limit
+// of one launch (ROPE_ERR_SHAPE when it does not fit).
+constexpr int64_t kMaxGrid = 2147483647;
 
 bool aligned(const void *p, unsigned bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+// Launcher status -> API status.
+int api_status(int rc)
+{
+    return rc == ROPE_LAUNCH_OK ? ROPE_OK : (rc == ROPE_LAUNCH_SHAPE ? ROPE_ERR_SHAPE : ROPE_ERR_HIP);
+}
+
+// Bytes of a dense tensor with these dims and element size (saturating at
+// INT64_MAX, so an absurd shape still compares as "large").
+int64_t bytes_of(std::initializer_list<int64_t> dims, int64_t elt)
+{
+    int64_t n = elt;
+    for (int64_t d : dims) {
+        if (d <= 0) return 0;
+        if (n > INT64_MAX / d) return INT64_MAX;
+        n *= d;
+    }
+    return n;
+}
+
+// Whether two byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (!a || !b || na <= 0 || nb <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t xe = (uint64_t)na > UINTPTR_MAX - x ? UINTPTR_MAX : x + (uintptr_t)na;
+    const uintptr_t ye = (uint64_t)nb > UINTPTR_MAX - y ? UINTPTR_MAX : y + (uintptr_t)nb;
+    return x < ye && y < xe;
+}
+
+struct Span {
+    const void *p;
+    int64_t n;
+};
+// Whether any written range overlaps another written range or a read range.
+bool any_overlap(std::initializer_list<Span> writes, std::initializer_list<Span> reads)
+{
+    for (auto w = writes.begin(); w != writes.end(); ++w) {
+        for (auto w2 = w + 1; w2 != writes.end(); ++w2)
+            if (overlaps(w->p, w->n, w2->p, w2->n)) return true;
+        for (const Span &r : reads)
+            if (overlaps(w->p, w->n, r.p, r.n)) return true;
+    }
+    return false;
+}
 
 int elt_size(int dtype) { return dtype == ROPE_F32 ? 4 : 2; }
 
@@ -71,10 +120,10 @@ int rope_tables_build_scaled(double base, int rot_dim, int64_t max_pos, double p
     if (max_pos < 1 || max_pos > 2147483647) return ROPE_ERR_SHAPE;
     if (!cos_out || !sin_out) return ROPE_ERR_NULL;
     if (!aligned(cos_out, 4) || !aligned(sin_out, 4)) return ROPE_ERR_ALIGN;
-    return rope_launch_tables(base, rot_dim, max_pos, pos_divisor, cos_out, sin_out,
-                              static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK
-               ? ROPE_OK
-               : ROPE_ERR_HIP;
+    if (overlaps(cos_out, bytes_of({max_pos, rot_dim / 2}, 4), sin_out, bytes_of({max_pos, rot_dim / 2}, 4)))
+        return ROPE_ERR_SHAPE;
+    return api_status(rope_launch_tables(base, rot_dim, max_pos, pos_divisor, cos_out, sin_out,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
@@ -106,8 +155,7 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
     a.positions = positions; a.n_tokens = n_tokens;
     a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.table_rows = table_rows;
     a.head_dim = head_dim; a.rot_dim = rot_dim; a.layout = layout; a.dtype = dtype;
-    return rope_launch_apply(a, static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK ? ROPE_OK
-                                                                                     : ROPE_ERR_HIP;
+    return api_status(rope_launch_apply(a, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -166,10 +214,15 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     if ((int64_t)B * H > kMaxGrid || (int64_t)B * H * tiles > kMaxGrid) return ROPE_ERR_SHAPE;
     if (!q || !k || !v || !o) return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
-    if (o == q || o == k || o == v) return ROPE_ERR_SHAPE;
-    if (lse && ((const void *)lse == q || (const void *)lse == k || (const void *)lse == v ||
-                (void *)lse == o))
-        return ROPE_ERR_SHAPE;
+    {
+        // o, lse and the workspace are written: none may overlap another or an input
+        const int64_t es = elt_size(dtype);
+        const int64_t nq = bytes_of({B, H, Sq, head_dim}, es), nk = bytes_of({B, H_kv, Sk, head_dim}, es);
+        const int64_t nt = rot_dim > 0 ? bytes_of({table_rows, rot_dim / 2}, 4) : 0;
+        if (any_overlap({{o, nq}, {lse, lse ? bytes_of({B, H, Sq}, 4) : 0}, {workspace, workspace_bytes}},
+                        {{q, nq}, {k, nk}, {v, nk}, {cos_tab, nt}, {sin_tab, nt}}))
+            return ROPE_ERR_SHAPE;
+    }
     if (causal && q_pos_offset < k_pos_offset) return ROPE_ERR_EMPTY_ROW;
     if (rot_dim > 0) {
         const int64_t need_q = q_pos_offset + Sq, need_k = k_pos_offset + Sk;
@@ -194,8 +247,7 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     a.workspace = workspace;
     a.workspace_bytes = workspace ? workspace_bytes : 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int rc = dtype == ROPE_F32 ? rope_launch_flash_f32(a, s) : rope_launch_flash_bf16(a, s);
-    return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
+    return api_status(dtype == ROPE_F32 ? rope_launch_flash_f32(a, s) : rope_launch_flash_bf16(a, s));
 }
 
 int64_t rope_flash_attn_bwd_workspace_size(int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
@@ -239,12 +291,16 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
         return ROPE_ERR_SHAPE;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
-    const void *ins[6] = {q, k, v, o, dout, lse};
-    void *outs[3] = {dq, dk, dv};
-    for (void *x : outs)
-        for (const void *y : ins)
-            if (x == y) return ROPE_ERR_SHAPE;
-    if (dq == dk || dq == dv || dk == dv) return ROPE_ERR_SHAPE;
+    {
+        // dq, dk, dv and the workspace are written: none may overlap another or an input
+        const int64_t es = elt_size(dtype);
+        const int64_t nq = bytes_of({B, H, Sq, head_dim}, es), nk = bytes_of({B, H_kv, Sk, head_dim}, es);
+        const int64_t nt = rot_dim > 0 ? bytes_of({table_rows, rot_dim / 2}, 4) : 0;
+        if (any_overlap({{dq, nq}, {dk, nk}, {dv, nk}, {workspace, workspace_bytes}},
+                        {{q, nq}, {k, nk}, {v, nk}, {o, nq}, {dout, nq}, {lse, bytes_of({B, H, Sq}, 4)},
+                         {cos_tab, nt}, {sin_tab, nt}}))
+            return ROPE_ERR_SHAPE;
+    }
     if (causal && q_pos_offset < k_pos_offset) return ROPE_ERR_EMPTY_ROW;
     if (rot_dim > 0) {
         if (table_rows < q_pos_offset + Sq || table_rows < k_pos_offset + Sk) return ROPE_ERR_TABLE_RANGE;
@@ -266,8 +322,7 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
     a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     a.dtype = dtype;
     a.workspace = workspace;
-    return rope_launch_flash_bwd_bf16(a, static_cast<hipStream_t>(stream)) == ROPE_LAUNCH_OK ? ROPE_OK
-                                                                                              : ROPE_ERR_HIP;
+    return api_status(rope_launch_flash_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -311,7 +366,18 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
         return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
     if (rot_dim > 0 && table_rows < 1) return ROPE_ERR_TABLE_RANGE;
-    if (o == q || o == k_new || o == v_new || o == k_cache || o == v_cache) return ROPE_ERR_SHAPE;
+    {
+        // o, the caches (rows L are written) and the workspace: none may
+        // overlap another or an input
+        const int64_t es = elt_size(dtype);
+        const int64_t nq = bytes_of({B, H, head_dim}, es), nn = bytes_of({B, H_kv, head_dim}, es);
+        const int64_t nc = bytes_of({B, H_kv, S_max, head_dim}, es);
+        const int64_t nt = rot_dim > 0 ? bytes_of({table_rows, rot_dim / 2}, 4) : 0;
+        if (any_overlap({{o, nq}, {k_cache, nc}, {v_cache, nc}, {workspace, workspace_bytes}},
+                        {{q, nq}, {k_new, nn}, {v_new, nn}, {cache_lens, bytes_of({B}, 4)}, {cos_tab, nt},
+                         {sin_tab, nt}}))
+            return ROPE_ERR_SHAPE;
+    }
     if (workspace_bytes < rope_decode_workspace_bytes(B, H, H_kv, head_dim)) return ROPE_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
         !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(workspace, 16) || !aligned(cache_lens, 4))
@@ -327,8 +393,7 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
     a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     a.dtype = dtype;
     a.workspace = workspace;
-    const int rc = rope_launch_decode_bf16(a, static_cast<hipStream_t>(stream));
-    return rc == ROPE_LAUNCH_OK ? ROPE_OK : ROPE_ERR_HIP;
+    return api_status(rope_launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

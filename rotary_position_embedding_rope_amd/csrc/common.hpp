@@ -103,10 +103,20 @@ __device__ __forceinline__ uint16_t f32_to_elt(float x) { return (uint16_t)(Ty<E
 
 // Status values returned by the launchers (mirror include/rope_mi355x.h).
 #define ROPE_LAUNCH_OK 0
+#define ROPE_LAUNCH_SHAPE 2   // the grid would not fit one launch: nothing was enqueued
 #define ROPE_LAUNCH_ERR 7
 
+// A 1-D launch holds at most 2^32 - 1 work-items in all (grid blocks times
+// block threads); launchers check every grid of a call before the first
+// launch and return ROPE_LAUNCH_SHAPE when one does not fit.
+inline bool rope_grid_fits(int64_t blocks, int threads)
+{
+    return blocks >= 1 && threads >= 1 && blocks <= (int64_t)0xffffffffLL / threads;
+}
+
 // Host launchers, one per kernel family.  Arguments are validated by abi.cpp
-// before these are called; each returns ROPE_LAUNCH_OK or ROPE_LAUNCH_ERR.
+// before these are called; each returns ROPE_LAUNCH_OK, ROPE_LAUNCH_SHAPE
+// (before any launch) or ROPE_LAUNCH_ERR.
 int rope_launch_tables(double base, int rot_dim, int64_t max_pos, double pos_div, float *cos_out,
                        float *sin_out, hipStream_t stream);
 

@@ -636,6 +636,7 @@ int launch_gt(const DecodeParams &p, hipStream_t stream)
 template <int D, typename E>
 int launch_d(const DecodeParams &p, int layout, hipStream_t stream)
 {
+    if (!rope_grid_fits(p.nw, 256) || !rope_grid_fits((int64_t)p.B * p.H, 256)) return ROPE_LAUNCH_SHAPE;
     int rc;
     if (p.rot_dim == 0) rc = launch_gt<D, 0, false, E>(p, stream);
     else if (layout == 0) rc = launch_gt<D, 0, true, E>(p, stream);

@@ -729,10 +729,14 @@ int launch_all(BwdParams p, uint16_t *qr, uint16_t *kr, hipStream_t stream)
     const int64_t rows = (int64_t)p.B * p.H * p.Sq;
     constexpr int RPB = 256 / (D / 8);
     const int64_t ndelta = (rows + RPB - 1) / RPB;
+    constexpr int NTH = 256 * Halves<D>::NH;
+    const int64_t n_dkv = (int64_t)p.B * p.Hkv * p.n_ktiles, n_dq = (int64_t)p.B * p.H * p.n_qtiles;
+    const int64_t nrot = ROTD > 0 ? (int64_t)p.B * p.H * ((p.Sq + TILE - 1) / TILE) +
+                                        (int64_t)p.B * p.Hkv * ((p.Sk + TILE - 1) / TILE)
+                                  : 0;
+    if (!rope_grid_fits(nrot + ndelta, 256) || !rope_grid_fits(n_dkv + n_dq, NTH)) return ROPE_LAUNCH_SHAPE;
     if constexpr (ROTD > 0) {
         // rotation tiles, then the row sums, in one launch
-        const int64_t nrot = (int64_t)p.B * p.H * ((p.Sq + TILE - 1) / TILE) +
-                             (int64_t)p.B * p.Hkv * ((p.Sk + TILE - 1) / TILE);
         hipLaunchKernelGGL((bwd_rotate_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)(nrot + ndelta)), dim3(256), 0,
                            stream, p, p.q, p.k, qr, kr);
         if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
@@ -743,10 +747,8 @@ int launch_all(BwdParams p, uint16_t *qr, uint16_t *kr, hipStream_t stream)
                            p.delta, rows);
         if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     }
-    constexpr int NTH = 256 * Halves<D>::NH;
-    const int n_dkv = p.B * p.Hkv * p.n_ktiles, n_dq = p.B * p.H * p.n_qtiles;
     hipLaunchKernelGGL((bwd_main_kernel<D, LAYOUT, ROTD, E>), dim3((unsigned)(n_dkv + n_dq)), dim3(NTH), 0, stream,
-                       p, n_dkv, n_dq);
+                       p, (int)n_dkv, (int)n_dq);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 

@@ -1371,6 +1371,14 @@ int launch(const FlashArgs &a, hipStream_t stream)
         p.ws_part = static_cast<float *>(a.workspace);
     // D = 128, default schedule: row split (two query tiles per workgroup)
     constexpr bool RSPLIT = D == 128;
+    {
+        int64_t blocks = p.sk_G;
+        if (p.sk_G == 0)
+            blocks = RSPLIT ? (int64_t)p.BH * ((p.n_qtiles + 1) / 2)
+                            : (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
+        if (!rope_grid_fits(blocks, 512) || (p.sk_G > 0 && !rope_grid_fits((int64_t)p.BH * p.n_qtiles, 256)))
+            return ROPE_LAUNCH_SHAPE;
+    }
     if (p.sk_G > 0) {
         hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true, false, E>), dim3((unsigned)p.sk_G),
                            dim3(256 * NG), 0, stream, p);

@@ -172,6 +172,7 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.causal = a.causal;
     p.n_qtiles = (int)((a.Sq + BM - 1) / BM);
     const int64_t blocks = (int64_t)p.BH * p.n_qtiles;
+    if (!rope_grid_fits(blocks, 256)) return ROPE_LAUNCH_SHAPE;
     hipLaunchKernelGGL((flash_fwd_f32_kernel<D, LAYOUT, ROT>), dim3((unsigned)blocks), dim3(256),
                        0, stream, p);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;

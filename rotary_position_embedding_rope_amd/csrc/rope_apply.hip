@@ -203,6 +203,7 @@ int launch(const RopeApplyArgs &a, hipStream_t stream)
     g.tokens_per_block = 256 / per_token;
     const int threads = g.tokens_per_block * per_token;
     const int64_t blocks = (a.n_tokens + g.tokens_per_block - 1) / g.tokens_per_block;
+    if (!rope_grid_fits(blocks, threads)) return ROPE_LAUNCH_SHAPE;
     hipLaunchKernelGGL((rope_apply_kernel<T, LAYOUT, V, VT>), dim3((unsigned)blocks),
                        dim3(threads), 0, stream, a, g);
     return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
@@ -357,7 +358,7 @@ int launch_rows(const RopeApplyArgs &a, hipStream_t stream)
     const int hpt = (heads + slots - 1) / slots;
     const int64_t groups = a.n_tokens * slots;
     const int64_t blocks = (groups * L + 255) / 256;
-    if (blocks > 2147483647) return -1;
+    if (!rope_grid_fits(blocks, 256)) return -1;   // the general kernel checks its own grid
     if ((slots * L) % 64 == 0)
         hipLaunchKernelGGL((rope_apply_rows_kernel<T, LAYOUT, L, kRowsBatch, true>), dim3((unsigned)blocks),
                            dim3(256), 0, stream, a, a.q_stride_head, a.k_stride_head, slots, hpt, groups);

@@ -11,11 +11,16 @@ from rotary_position_embedding_rope_amd import _lib
 ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "rope_mi355x.h"
 
-FAKE = 0x10000          # a 16-byte-aligned non-NULL address; never dereferenced
-FAKE2 = 0x20000
-FAKE3 = 0x30000
-FAKE4 = 0x40000
-MISALIGNED = 0x10002
+
+
+def slot(i, off=0):
+    """A fake device address, never dereferenced: slots are 4 TiB apart, so
+    the tensors of one call never overlap unless a test places them so."""
+    return (i << 42) + off
+
+
+FAKE, FAKE2 = slot(1), slot(2)
+MISALIGNED = slot(1, 2)
 
 
 @pytest.fixture(scope="module")
@@ -90,8 +95,8 @@ def test_tables_build_scaled_rejects_divisor(lib, div):
 
 
 def apply_args(**over):
-    a = dict(q=FAKE, qst=40 * 128, qsh=128, hq=32, k=FAKE2, kst=8 * 128, ksh=128, hkv=8,
-             pos=FAKE3, n=8192, cos=FAKE4, sin=FAKE4 + 0x1000, rows=32768, D=128, rot=64,
+    a = dict(q=slot(1), qst=40 * 128, qsh=128, hq=32, k=slot(2), kst=8 * 128, ksh=128, hkv=8,
+             pos=slot(3), n=8192, cos=slot(4), sin=slot(5), rows=32768, D=128, rot=64,
              layout=_lib.NEOX, dtype=_lib.BF16)
     a.update(over)
     return [a["q"], a["qst"], a["qsh"], a["hq"], a["k"], a["kst"], a["ksh"], a["hkv"], a["pos"],
@@ -112,15 +117,17 @@ def apply_args(**over):
     (dict(layout=2), _lib.ERR_UNSUPPORTED),
     (dict(dtype=5), _lib.ERR_UNSUPPORTED),
     (dict(dtype=_lib.F16, q=None), _lib.ERR_NULL),   # fp16 is accepted: validation goes on
-    (dict(dtype=_lib.F16, q=FAKE + 1), _lib.ERR_ALIGN),
+    (dict(dtype=_lib.F16, q=slot(1, 1)), _lib.ERR_ALIGN),
     (dict(q=None), _lib.ERR_NULL),
     (dict(k=None), _lib.ERR_NULL),
     (dict(pos=None), _lib.ERR_NULL),
     (dict(cos=None), _lib.ERR_NULL),
     (dict(rows=0), _lib.ERR_TABLE_RANGE),
-    (dict(q=FAKE + 1), _lib.ERR_ALIGN),
-    (dict(pos=FAKE3 + 2), _lib.ERR_ALIGN),
-    (dict(cos=FAKE4 + 2), _lib.ERR_ALIGN),
+    (dict(q=slot(1, 1)), _lib.ERR_ALIGN),
+    (dict(pos=slot(3, 2)), _lib.ERR_ALIGN),
+    (dict(cos=slot(4, 2)), _lib.ERR_ALIGN),
+    # 2^31 - 1 tokens x 40 heads: the grid would pass 2^32 - 1 work-items
+    (dict(n=2147483647), _lib.ERR_SHAPE),
 ])
 def test_rope_apply_rejects(lib, over, want):
     assert lib.rope_apply(*apply_args(**over)) == want
@@ -137,8 +144,8 @@ def test_rope_apply_noop_needs_no_device(lib, over):
 
 
 def fwd_args(**over):
-    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=None, B=1, H=8, Hkv=None, Sq=4096, Sk=4096, D=64,
-             qo=0, ko=0, cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096, rot=64, layout=_lib.NEOX,
+    a = dict(q=slot(1), k=slot(2), v=slot(3), o=slot(4), lse=None, B=1, H=8, Hkv=None, Sq=4096, Sk=4096,
+             D=64, qo=0, ko=0, cos=slot(5), sin=slot(6), rows=4096, rot=64, layout=_lib.NEOX,
              causal=1, scale=0.0, dtype=_lib.BF16, ws=None, wsb=0)
     a.update(over)
     hkv = a["H"] if a["Hkv"] is None else a["Hkv"]
@@ -161,9 +168,12 @@ def fwd_args(**over):
     (dict(qo=-1), _lib.ERR_SHAPE),
     (dict(scale=float("nan")), _lib.ERR_SHAPE),
     (dict(scale=float("inf")), _lib.ERR_SHAPE),
-    (dict(o=FAKE), _lib.ERR_SHAPE),             # o aliases q
-    (dict(lse=FAKE4), _lib.ERR_SHAPE),          # lse aliases o
-    (dict(lse=FAKE4 + 0x9002), _lib.ERR_ALIGN),
+    (dict(o=slot(1)), _lib.ERR_SHAPE),             # o aliases q
+    (dict(o=slot(1, 0x1000)), _lib.ERR_SHAPE),     # o overlaps q at an offset
+    (dict(o=slot(3, -16)), _lib.ERR_SHAPE),        # o's last bytes overlap v
+    (dict(lse=slot(4)), _lib.ERR_SHAPE),           # lse aliases o
+    (dict(lse=slot(4, 0x3ffffc)), _lib.ERR_SHAPE), # lse starts inside o (4 MiB)
+    (dict(lse=slot(7, 2)), _lib.ERR_ALIGN),
     (dict(D=192, rot=192), _lib.ERR_UNSUPPORTED),   # D/2 = 96 is not a power of two
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(rot=48), _lib.ERR_UNSUPPORTED),
@@ -176,11 +186,15 @@ def fwd_args(**over):
     (dict(qo=0, ko=1, rows=8192), _lib.ERR_EMPTY_ROW),
     (dict(rows=4095), _lib.ERR_TABLE_RANGE),
     (dict(qo=14336, Sq=2048, Sk=16384, rows=16383), _lib.ERR_TABLE_RANGE),
-    (dict(cos=FAKE4 + 0x1004), _lib.ERR_ALIGN),
-    (dict(k=FAKE2 + 8), _lib.ERR_ALIGN),
+    (dict(cos=slot(5, 4)), _lib.ERR_ALIGN),
+    (dict(k=slot(2, 8)), _lib.ERR_ALIGN),
     (dict(ws=None, wsb=1024), _lib.ERR_SHAPE),        # bytes without a buffer
-    (dict(ws=FAKE4 + 0x8000, wsb=-1), _lib.ERR_SHAPE),
-    (dict(ws=FAKE4 + 0x8004, wsb=4096), _lib.ERR_ALIGN),
+    (dict(ws=slot(8), wsb=-1), _lib.ERR_SHAPE),
+    (dict(ws=slot(8, 4), wsb=4096), _lib.ERR_ALIGN),
+    (dict(ws=slot(4, 0x100), wsb=4096), _lib.ERR_SHAPE),   # workspace inside o
+    (dict(ws=slot(2, 0x100), wsb=4096), _lib.ERR_SHAPE),   # workspace inside k
+    # 16 M workgroups of 512 threads: past the 2^32 - 1 work-items of one launch
+    (dict(B=2048, H=1024, Sq=1024, Sk=1024), _lib.ERR_SHAPE),
 ])
 def test_flash_rejects(lib, over, want):
     assert lib.rope_flash_attn_fwd(*fwd_args(**over)) == want
@@ -212,10 +226,9 @@ def test_workspace_size_fp32_needs_none(lib):
 
 
 def decode_args(**over):
-    a = dict(q=FAKE, kn=FAKE2, vn=FAKE3, kc=FAKE4, vc=FAKE4 + 0x100000, lens=FAKE + 0x8000,
-             o=FAKE4 + 0x200000, B=16, H=32, Hkv=8, S=32768, D=128, cos=FAKE4 + 0x1000,
-             sin=FAKE4 + 0x2000, rows=32768, rot=128, layout=_lib.NEOX, scale=0.0,
-             dtype=_lib.BF16, ws=FAKE4 + 0x300000, wsb=1 << 30)
+    a = dict(q=slot(1), kn=slot(2), vn=slot(3), kc=slot(4), vc=slot(5), lens=slot(6),
+             o=slot(7), B=16, H=32, Hkv=8, S=32768, D=128, cos=slot(8), sin=slot(9), rows=32768,
+             rot=128, layout=_lib.NEOX, scale=0.0, dtype=_lib.BF16, ws=slot(10), wsb=1 << 30)
     a.update(over)
     return [a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["lens"], a["o"], a["B"], a["H"],
             a["Hkv"], a["S"], a["D"], a["cos"], a["sin"], a["rows"], a["rot"], a["layout"],
@@ -234,7 +247,10 @@ def decode_args(**over):
     (dict(wsb=1024), _lib.ERR_SHAPE),              # workspace too small
     (dict(wsb=2397183), _lib.ERR_SHAPE),           # one byte short
     (dict(B=1 << 20, S=1 << 24, wsb=1 << 62), _lib.ERR_SHAPE),   # pass counts past 32 bits
-    (dict(o=FAKE), _lib.ERR_SHAPE),                # o aliases q
+    (dict(o=slot(1)), _lib.ERR_SHAPE),             # o aliases q
+    (dict(o=slot(4, 1 << 20)), _lib.ERR_SHAPE),    # o inside the key cache
+    (dict(vc=slot(4, 1 << 29)), _lib.ERR_SHAPE),   # the caches overlap
+    (dict(ws=slot(5, 64)), _lib.ERR_SHAPE),        # workspace inside the value cache
     (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
     (dict(Hkv=2), _lib.ERR_UNSUPPORTED),           # 16 query heads per key/value head
     (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
@@ -245,9 +261,9 @@ def decode_args(**over):
     (dict(ws=None), _lib.ERR_NULL),
     (dict(cos=None), _lib.ERR_NULL),
     (dict(rows=0), _lib.ERR_TABLE_RANGE),
-    (dict(kc=FAKE4 + 8), _lib.ERR_ALIGN),
-    (dict(lens=FAKE + 2), _lib.ERR_ALIGN),
-    (dict(ws=FAKE4 + 0x300004), _lib.ERR_ALIGN),
+    (dict(kc=slot(4, 8)), _lib.ERR_ALIGN),
+    (dict(lens=slot(6, 2)), _lib.ERR_ALIGN),
+    (dict(ws=slot(10, 4)), _lib.ERR_ALIGN),
 ])
 def test_decode_rejects(lib, over, want):
     assert lib.rope_decode_attn_fwd(*decode_args(**over)) == want
@@ -274,11 +290,11 @@ def test_decode_workspace_size(lib):
 
 
 def bwd_args(**over):
-    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, do=FAKE4 + 0x100000, lse=FAKE4 + 0x200000,
-             dq=FAKE4 + 0x300000, dk=FAKE4 + 0x400000, dv=FAKE4 + 0x500000, B=1, H=8, Hkv=8,
-             Sq=4096, Sk=4096, D=64, qo=0, ko=0, cos=FAKE4 + 0x1000, sin=FAKE4 + 0x2000, rows=4096,
+    a = dict(q=slot(1), k=slot(2), v=slot(3), o=slot(4), do=slot(5), lse=slot(6), dq=slot(7),
+             dk=slot(8), dv=slot(9), B=1, H=8, Hkv=8, Sq=4096, Sk=4096, D=64, qo=0, ko=0,
+             cos=slot(10), sin=slot(11), rows=4096,
              rot=64, layout=_lib.NEOX, causal=1, scale=0.0, dtype=_lib.BF16,
-             ws=FAKE4 + 0x600000, wsb=1 << 20)
+             ws=slot(12), wsb=1 << 24)
     a.update(over)
     return [a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "H", "Hkv", "Sq",
                            "Sk", "D", "qo", "ko", "cos", "sin", "rows", "rot", "layout", "causal",
@@ -293,9 +309,12 @@ def bwd_args(**over):
     (dict(rot=66), _lib.ERR_SHAPE),
     (dict(qo=-1), _lib.ERR_SHAPE),
     (dict(scale=float("nan")), _lib.ERR_SHAPE),
-    (dict(dq=FAKE), _lib.ERR_SHAPE),              # dq aliases q
-    (dict(dk=FAKE4 + 0x200000), _lib.ERR_SHAPE),  # dk aliases lse
-    (dict(dv=FAKE4 + 0x300000), _lib.ERR_SHAPE),  # dv aliases dq
+    (dict(dq=slot(1)), _lib.ERR_SHAPE),           # dq aliases q
+    (dict(dq=slot(1, 0x100000)), _lib.ERR_SHAPE), # dq overlaps q at an offset
+    (dict(dk=slot(6)), _lib.ERR_SHAPE),           # dk aliases lse
+    (dict(dv=slot(7)), _lib.ERR_SHAPE),           # dv aliases dq
+    (dict(dv=slot(8, 0x200)), _lib.ERR_SHAPE),    # dv overlaps dk
+    (dict(ws=slot(9, 0x3fff00)), _lib.ERR_SHAPE), # workspace overlaps dv's end
     (dict(wsb=1024), _lib.ERR_SHAPE),             # workspace too small (4096 rows x 8 heads x 4 B)
     (dict(dtype=_lib.F32), _lib.ERR_UNSUPPORTED),
     (dict(dtype=_lib.F16, lse=None), _lib.ERR_NULL),  # fp16 accepted
@@ -309,9 +328,9 @@ def bwd_args(**over):
     (dict(cos=None), _lib.ERR_NULL),
     (dict(qo=0, ko=1, rows=8192), _lib.ERR_EMPTY_ROW),
     (dict(rows=4095), _lib.ERR_TABLE_RANGE),
-    (dict(lse=FAKE4 + 0x200002), _lib.ERR_ALIGN),
-    (dict(dk=FAKE4 + 0x400008), _lib.ERR_ALIGN),
-    (dict(ws=FAKE4 + 0x600004), _lib.ERR_ALIGN),
+    (dict(lse=slot(6, 2)), _lib.ERR_ALIGN),
+    (dict(dk=slot(8, 8)), _lib.ERR_ALIGN),
+    (dict(ws=slot(12, 4)), _lib.ERR_ALIGN),
 ])
 def test_bwd_rejects(lib, over, want):
     assert lib.rope_flash_attn_bwd(*bwd_args(**over)) == want
@@ -330,6 +349,10 @@ def test_bwd_workspace_size(lib):
     assert f(1, 8, 3, 16, 16, 64, 0, _lib.BF16) == -_lib.ERR_SHAPE     # H_kv must divide H
     assert f(1, 8, 8, 16, 16, 64, 66, _lib.BF16) == -_lib.ERR_SHAPE    # rot_dim past head_dim
     assert f(1, 8, 8, 16, 16, 64, 0, _lib.F32) == -_lib.ERR_UNSUPPORTED
-    # the smallest accepted workspace is accepted: validation then reaches the device
-    # (not called here); one byte less is rejected
-    assert lib.rope_flash_attn_bwd(*bwd_args(wsb=8 * 4096 * 4 - 1)) == _lib.ERR_SHAPE
+    # one byte less than the size the library asks for is rejected, with and
+    # without the rotated copies (a call with the full size would reach the
+    # device, so it is not made here)
+    for rot in (64, 0):
+        need = f(1, 8, 8, 4096, 4096, 64, rot, _lib.BF16)
+        assert need == 8 * 4096 * 4 + (2 * 8 * 4096 * 64 * 2 if rot else 0)
+        assert lib.rope_flash_attn_bwd(*bwd_args(rot=rot, wsb=need - 1)) == _lib.ERR_SHAPE
