@@ -19,10 +19,11 @@ Bars:
     absolute for gradients that vanish in exact arithmetic (a single visible
     key: P = 1 and dS = dO.v - dO.o = 0), where only the fp32 rounding of the
     two dot products (|dO||v| ~ 10 times 2^-24 per term) remains.
-  * full size: sampled dq rows against the oracle (a row of dq needs only its
-    own query, every key it sees and its upstream gradient), and two exact
-    identities for dk and dv: sum_j dv_j = sum_i dout_i (each row of P sums
-    to 1) and sum_j R(k_pos_j) dk_j = 0 (each row of dS sums to 0).
+  * full size: every element against the oracle (the GQA chunked prefill:
+    every element of its first and last key/value head groups), with the
+    same bars; two exact identities for dk and dv on top: sum_j dv_j =
+    sum_i dout_i (each row of P sums to 1) and sum_j R(k_pos_j) dk_j = 0
+    (each row of dS sums to 0).
 """
 import numpy as np
 import pytest
@@ -178,34 +179,53 @@ def test_backward_deterministic():
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("w", [wl.HEADLINE, wl.PREFILL_GQA], ids=lambda w: w.name)
-def test_backward_full_size_sampled(orc, w):
-    """The bench workloads' shapes: sampled dq rows against the oracle, and
-    the two exact identities for dk and dv."""
-    q, k, v, dout = inputs(w)
-    o, lse, dq, dk, dv = run(w, q, k, v, dout)
-    rng = np.random.default_rng(5)
-    rows = [0, w.Sq - 1] + list(rng.integers(0, w.Sq, size=6))
-    for i in rows:
-        h = int(rng.integers(0, w.H))
-        sl = slice(h, h + 1)
-        kv = h // (w.H // w.Hkv)
-        rq, _, _ = orc.attention_bwd(q[:, sl, i:i + 1], k[:, kv:kv + 1], v[:, kv:kv + 1],
-                                     dout[:, sl, i:i + 1], q_off=w.q_off + i, k_off=w.k_off,
-                                     base=w.base, layout=w.layout)
-        err = np.abs(dq[:, sl, i:i + 1] - rq).max()
-        assert err <= MAX_REL * max(np.abs(rq).max(), np.abs(dq).max() * 0.1), (i, h, float(err))
+def full_size_identities(orc, w, dout, dk, dv):
+    """Two exact identities of the gradients: sum_j dv_j = sum_i dout_i per
+    key/value head (each row of P sums to 1), and sum_j R(k_pos_j) dk_j = 0
+    (each row of dS sums to 0).  Bars scale with the oracle-free sums of
+    |dv| and |dk| the identities are built from."""
     G = w.H // w.Hkv
-    # sum over keys of dv equals the sum over rows of dout (per kv head: all its query heads)
     sdv = dv.sum(axis=2)
     sdo = dout.reshape(w.B, w.Hkv, G, w.Sq, w.D).sum(axis=(2, 3))
-    tol = 2e-2 * np.abs(dv).sum(axis=2).max()
-    assert np.abs(sdv - sdo).max() <= tol
-    # sum over keys of the rotated dk is zero
+    assert np.abs(sdv - sdo).max() <= 2e-2 * np.abs(dv).sum(axis=2).max()
     kpos = w.k_off + np.arange(w.Sk)
     rot_dk = orc.rope(dk, np.broadcast_to(kpos, dk.shape[:3]), base=w.base, layout=w.layout)
-    s = rot_dk.sum(axis=2)
-    assert np.abs(s).max() <= 2e-2 * np.abs(dk).sum(axis=2).max()
+    assert np.abs(rot_dk.sum(axis=2)).max() <= 2e-2 * np.abs(dk).sum(axis=2).max()
+
+
+def test_backward_full_size_headline(orc):
+    """The bench workload (causal 1x8x4096x64, NeoX): lse, dq, dk and dv,
+    every element, against the oracle with the bars above."""
+    w = wl.HEADLINE
+    q, k, v, dout = inputs(w)
+    o, lse, dq, dk, dv = run(w, q, k, v, dout)
+    kw = dict(q_off=w.q_off, k_off=w.k_off, base=w.base, layout=w.layout)
+    assert (np.abs(lse - orc.attention_lse(q, k, **kw)) <= lse_bound(q, k, w.D)).all()
+    for g, r, n in zip((dq, dk, dv), orc.attention_bwd(q, k, v, dout, **kw), ("dq", "dk", "dv")):
+        check_grad(g, r, n)
+    full_size_identities(orc, w, dout, dk, dv)
+
+
+def test_backward_full_size_gqa_prefill(orc):
+    """The GQA chunked prefill (32 query / 8 key-value heads, 2048 queries at
+    14336.. over 16384 keys, D = 128): the whole launch runs on the GPU;
+    the first and the last key/value head, with all query heads that read
+    them, are compared element by element (dq of those 8 query heads, dk and
+    dv of those 2 key/value heads: a key/value head's gradients depend only
+    on its own query heads), and lse of every row."""
+    w = wl.PREFILL_GQA
+    q, k, v, dout = inputs(w)
+    o, lse, dq, dk, dv = run(w, q, k, v, dout)
+    kw = dict(q_off=w.q_off, k_off=w.k_off, base=w.base, layout=w.layout)
+    assert (np.abs(lse - orc.attention_lse(q, k, **kw)) <= lse_bound(q, k, w.D)).all()
+    G = w.H // w.Hkv
+    kvs = [0, w.Hkv - 1]
+    qs = np.concatenate([np.arange(g * G, (g + 1) * G) for g in kvs])
+    rq, rk, rv = orc.attention_bwd(q[:, qs], k[:, kvs], v[:, kvs], dout[:, qs], **kw)
+    check_grad(dq[:, qs], rq, "dq")
+    check_grad(dk[:, kvs], rk, "dk")
+    check_grad(dv[:, kvs], rv, "dv")
+    full_size_identities(orc, w, dout, dk, dv)
 
 
 def test_lse_balanced_schedule(orc):

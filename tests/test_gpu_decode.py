@@ -195,9 +195,11 @@ def test_decode_lengths_outside_the_cache(orc):
     assert np.isnan(got[3]).all() and np.isfinite(got[:3]).all()
 
 
-def test_decode_full_size_sampled(orc):
+def test_decode_full_size(orc):
     """The bench workload's shapes (16 requests, 32/8 heads, 128 dims,
-    lengths up to 32767): requests 0, 7 and 15 against the oracle."""
+    lengths up to 32767): every request's output against the oracle, and
+    every request's appended cache row (the rotated new key within one bf16
+    ulp of the exact rotation, the new value bit-identical)."""
     w = wl.DECODE
     d = wl.decode_inputs(w, with_cache=False)
     g = torch.Generator(device=DEV)
@@ -210,17 +212,42 @@ def test_decode_full_size_sampled(orc):
     cos, sin = api.tables_build(w.base, w.rot, w.S_max, device=DEV)
     out = to64(run(w, dev, cos, sin))
     assert np.isfinite(out).all()
-    for b in (0, 7, 15):
+    for b in range(w.B):
         L = int(d["lens"][b])
-        # the cache holds these values as already-rotated keys: unrotate
-        # nothing, rotate only the query and the new key (the oracle's
-        # attention with keys at their positions would rotate them again),
-        # so the reference rotates q and k_new itself and attends unrotated
+        # the cache holds these values as already-rotated keys: the
+        # reference rotates only the query and the new key (at L) and
+        # attends over the cache rows as they are
         kc = to64(k_cache[b, :, :L + 1])
         vc = to64(v_cache[b, :, :L + 1])
         qr = orc.rope(d["q"][b][:, None, :], [L], base=w.base, layout=w.layout)
         kn = orc.rope(d["k_new"][b][:, None, :], [L], base=w.base, layout=w.layout)[:, 0, :]
-        kc[:, L] = wl.round_to(kn.astype(np.float32), "bf16")
+        assert (np.abs(kc[:, L] - kn) <= ulp_bf16(kn)).all(), b
+        assert np.array_equal(vc[:, L], d["v_new"][b].astype(np.float64)), b
         want = orc.attention(qr[None], kc[None], vc[None], q_off=L, k_off=0, rot_dim=0,
                              causal=True)[0, :, 0, :]
         assert np.abs(out[b] - want).max() <= BF16_TOL, b
+
+
+def test_prepared_launch_keeps_its_workspace():
+    """A prepared launch holds the workspace it was built on: growing the
+    per-device cache afterwards (a larger request) replaces the cache entry
+    but cannot free the buffer the prepared launch writes to."""
+    import weakref
+    w = wl.DecodeWorkload("decode_ws_lifetime", 2, 8, 2, 128, 256, 31, base=1e4)
+    d = wl.decode_inputs(w)
+    d["k_cache"] = d["k_raw"]   # contents do not matter here
+    dev = {n: bf16(d[n]) for n in ("q", "k_new", "v_new", "k_cache", "v_cache")}
+    lens = torch.from_numpy(d["lens"]).to(DEV)
+    cos, sin = api.tables_build(w.base, w.rot, w.S_max, device=DEV)
+    out = torch.empty_like(dev["q"])
+    launch = api.prepare_decode_attn_fwd(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"],
+                                         dev["v_cache"], lens, out, cos, sin)
+    ws = weakref.ref(launch.workspace)
+    need = launch.workspace.numel()
+    big_q = torch.zeros((64, 8, 128), dtype=torch.bfloat16, device=DEV)
+    big_cache = torch.zeros((64, 2, 8, 128), dtype=torch.bfloat16, device=DEV)
+    grown = api.decode_workspace(big_q, big_cache)   # replaces the cache entry
+    assert grown.numel() > need
+    assert ws() is not None and ws().numel() >= need
+    del launch
+    assert ws() is None or ws() is grown

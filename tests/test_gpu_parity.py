@@ -255,37 +255,6 @@ def run_fused(w: wl.AttentionWorkload, q, k, v, rot=None):
     return out
 
 
-def sample_rows(w: wl.AttentionWorkload, n_random=24, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for b in range(w.B):
-        for h in sorted({0, w.H - 1, w.H // 2}):
-            for i in (0, 1, 31, 32, 63, 64, 127, 128, w.Sq // 2, w.Sq - 2, w.Sq - 1):
-                if 0 <= i < w.Sq:
-                    rows.add((b, h, i))
-    for _ in range(n_random):
-        rows.add((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.Sq))))
-    return sorted(rows)
-
-
-def oracle_rows(orc, w, q, k, v, rows, rot=None):
-    """Oracle output for each (b, h, i) in ``rows``, one oracle call per head."""
-    rot = w.rot if rot is None else rot
-    out = {}
-    heads = sorted({(b, h) for b, h, _ in rows})
-    for b, h in heads:
-        idx = [i for bb, hh, i in rows if (bb, hh) == (b, h)]
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        g = h // (w.H // w.Hkv)
-        skv = (slice(b, b + 1), slice(g, g + 1))
-        res = orc.attention_rows(q[sl], k[skv], v[skv], [(0, 0, i) for i in idx], q_off=w.q_off,
-                                 k_off=w.k_off, rot_dim=rot, base=w.base, layout=w.layout,
-                                 causal=w.causal)
-        for i, r in zip(idx, res):
-            out[(b, h, i)] = r
-    return np.stack([out[r] for r in rows])
-
-
 def test_fused_tiny_f32_full(orc):
     """fp32 workload 1x2x128x64, GPT-J, causal: every output vs the oracle,
     max |err| <= 1e-5."""
@@ -313,19 +282,24 @@ def test_fused_bf16_full(orc, w):
     assert np.array_equal(got[:, :, 0], v[:, :, 0].astype(np.float64))
 
 
-@pytest.mark.parametrize("w", list(wl.SWEEP_BF16) + [wl.PREFILL_OFFSET, wl.PREFILL_GQA],
+@pytest.mark.parametrize("w", list(wl.SWEEP_BF16[1:]) + [wl.PREFILL_OFFSET, wl.PREFILL_GQA],
                          ids=lambda w: w.name)
-def test_fused_full_size_sampled(orc, w):
-    """Full-size workloads in the benchmark's launch configuration: sampled
-    output rows (first/last rows, tile edges, random) vs the oracle row by
-    row, max |err| <= 2e-2; every output finite."""
+def test_fused_full_size(orc, w):
+    """Full-size workloads in the benchmark's launch configuration (the
+    1x8xSx64 sweep shapes from 2048 queries up, the 2048 x 16384 chunked
+    prefill with 32 and with 8 key/value heads): every output element vs
+    the dense fp64 oracle, max |err| <= 2e-2; where the causal mask leaves
+    query 0 a single key (square shapes), its output is V[0] exactly."""
     q, k, v = wl.attention_inputs(w)
     out = run_fused(w, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"))
-    assert bool(torch.isfinite(out).all())
-    rows = sample_rows(w)
-    got = np.stack([to64(out[b, h, i]) for (b, h, i) in rows])
-    want = oracle_rows(orc, w, q, k, v, rows)
-    assert np.abs(got - want).max() <= BF16_TOL
+    got = to64(out)
+    assert np.isfinite(got).all()
+    want = orc.attention(q, k, v, q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot, base=w.base,
+                         layout=w.layout, causal=w.causal)
+    err = np.abs(got - want)
+    assert err.max() <= BF16_TOL, (float(err.max()), np.unravel_index(int(err.argmax()), err.shape))
+    if w.q_off == w.k_off and w.Hkv == w.H:
+        assert np.array_equal(got[:, :, 0], v[:, :, 0].astype(np.float64))
 
 
 EDGE_CASES = [
