@@ -13,16 +13,24 @@ synchronisations; rank 0 prints ONE JSON line.
   roofline       the fused kernel: flops per launch / mean launch duration,
                  from one HIP event pair on the launch stream around the K
                  launches, against 2500 TFLOP/s
-  rope_apply     the ragged RoPE workload (8192 tokens, 32 Q + 8 K heads,
-                 rot 64 of 128): algorithmic bytes / mean launch duration
-                 (measured the same way), cycling through enough buffer sets
-                 to defeat the 256 MB last-level cache, against 8 TB/s
-  cpu_baseline   the fp64 CPU oracle on the same workload (whole heads),
-                 timed on this host's cores
+  max_abs_err    the timed kernel's output against the fp64 oracle, in the
+                 same run (every element)
+  configs        every workload the target names, each timed the same way
+                 with its own roofline fraction and same-run oracle error:
+                 the fp32 parity case, the page-shaped 1x8x512x64 GPT-J case,
+                 the 1x8xSx64 NeoX sweep, the ragged rope_apply batch (with
+                 the in-place streaming ceiling of the same bytes on this
+                 GPU) and the 2048 x 16384 chunked prefill with its query
+                 offset (plus its 8-key/value-head variant); the six
+                 page-shaped workloads also carry the comparators below
   comparators    context rows mirroring "RoPE + PoPE Attention Kernels"'
                  benchmark table: the same kernel without rotation ("flash"),
                  and rope_apply on copies of Q/K followed by it ("unfused"),
-                 with peak extra device memory
+                 with peak extra device memory of one forward each
+  cpu_baseline   the fp64 CPU oracle on the same workload (whole heads),
+                 timed on this host's cores; single-thread and rope_apply
+                 oracle rates beside it
+  backward, decode   the backward step and the decode step (context)
 """
 from __future__ import annotations
 
@@ -41,9 +49,10 @@ if str(ROOT) not in sys.path:
 
 METRIC = "fused RoPE+causal attn fwd TFLOP/s (%MFMA peak); rope_apply HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
+PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector peak, published (the fp32 kernel's units)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth, published
 # "RoPE + PoPE Attention Kernels", median runtime table: rope (rotate, then
-# flash) at 1x8x4096x64 on an unnamed CUDA GPU -- context, not a target.
+# flash) on an unnamed CUDA GPU -- context, not a target.
 PAGE_ROPE_MS = {"causal_neox_bf16_1x8x4096x64": 31.984, "causal_neox_bf16_1x8x1024x64": 4.431,
                 "causal_neox_bf16_1x8x2048x64": 8.717, "causal_neox_bf16_2x8x1024x64": 4.749,
                 "causal_neox_bf16_4x8x1024x64": 9.057, "causal_gptj_bf16_1x8x512x64": 1.811}
@@ -62,15 +71,14 @@ def parse_args():
                     help="distinct Q/K buffer sets cycled by the rope_apply timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config list")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--bwd-steps", type=int, default=30)
     ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "backward", "copy"],
                     default="all",
-                    help="restrict the timed kernels (for profiler runs); 'copy' runs only a "
-                         "plain 256 MiB device copy, the calibration for HBM byte counters")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time every attention workload (printed to stderr)")
+                    help="restrict the timed kernels (for profiler runs): 'fused' times only "
+                         "--workload; 'copy' runs only a plain 256 MiB device copy, the "
+                         "calibration for HBM byte counters")
     ap.add_argument("--balance", action="store_true",
                     help="pass a workspace: balanced (split query tile) schedule")
     return ap.parse_args()
@@ -131,25 +139,88 @@ def time_launches(torch, launch, steps, warmup, stream, rotate=None):
     return wall_ms / steps, event_ms / steps, durs
 
 
+def _tdt(torch, dtype):
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+
+
 def bench_fused(torch, api, wl, w, steps, warmup, balance=False):
     dev = torch.device("cuda:0")
-    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
-    q, k, v = (torch.from_numpy(a).to(tdt).to(dev) for a in wl.attention_inputs(w))
+    arrays = wl.attention_inputs(w)
+    q, k, v = (torch.from_numpy(a).to(_tdt(torch, w.dtype)).to(dev) for a in arrays)
     cos, sin = api.tables_build(w.base, w.rot, w.table_rows, device=dev)
     out = torch.empty_like(q)
     launch = api.prepare_flash_attn_fwd(q, k, v, out, cos, sin, w.q_off, w.k_off, w.rot, w.layout,
                                         w.causal, workspace="auto" if balance else None)
     stream = torch.cuda.current_stream(dev)
     ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
-    return dict(q=q, k=k, v=v, cos=cos, sin=sin, out=out, ms_step=ms_step, kernel_ms=kernel_ms,
-                p10=durs[len(durs) // 10], p50=durs[len(durs) // 2], p90=durs[(9 * len(durs)) // 10])
+    return dict(arrays=arrays, q=q, k=k, v=v, cos=cos, sin=sin, out=out, ms_step=ms_step,
+                kernel_ms=kernel_ms, p10=durs[len(durs) // 10], p50=durs[len(durs) // 2],
+                p90=durs[(9 * len(durs)) // 10])
 
 
-def bench_rope_apply(torch, api, wl, steps, sets, w=None):
+def sample_rows(w, n_random=40, seed=0):
+    """(b, h, i) rows for a same-run spot check: tile edges of three heads and
+    random rows."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(w.B):
+        for h in sorted({0, w.H - 1, w.H // 2}):
+            for i in (0, 1, 31, 32, 63, 64, 127, 128, 255, 256, w.Sq // 2, w.Sq - 2, w.Sq - 1):
+                if 0 <= i < w.Sq:
+                    rows.add((b, h, i))
+    for _ in range(n_random):
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.Sq))))
+    return sorted(rows)
+
+
+def fused_error(orc, w, r, full_pairs_limit=2 * 10 ** 8):
+    """Max |GPU - oracle| over every output element (sampled rows for the
+    largest workloads), with what was compared."""
+    import numpy as np
+    q, k, v = r["arrays"]
+    got = r["out"].float().cpu().numpy().astype(np.float64)
+    kw = dict(q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot, base=w.base, layout=w.layout,
+              causal=w.causal)
+    if w.visible_pairs() <= full_pairs_limit:
+        want = orc.attention(q, k, v, **kw)
+        return float(np.abs(got - want).max()), "every element"
+    rows = sample_rows(w)
+    want = orc.attention_rows(q, k, v, rows, **kw)
+    g = np.stack([got[b, h, i] for b, h, i in rows])
+    return float(np.abs(g - want).max()), f"{len(rows)} sampled rows"
+
+
+def fused_entry(torch, api, wl, orc, w, config, steps, warmup, comparators_too=False):
+    r = bench_fused(torch, api, wl, w, steps, warmup)
+    flops = w.flops()
+    tf = flops / (r["kernel_ms"] * 1e-3) / 1e12
+    f32 = w.dtype == "f32"
+    peak = PEAK_F32_VALU_TFLOPS if f32 else PEAK_BF16_TFLOPS
+    err, checked = fused_error(orc, w, r)
+    e = {"config": config, "workload": w.name, "shape": w.label(), "dtype": w.dtype,
+         "ms": round(r["kernel_ms"], 5), "wall_ms": round(r["ms_step"], 5),
+         "single_launch_p10_ms": round(r["p10"], 5), "single_launch_p90_ms": round(r["p90"], 5),
+         "value": round(tf, 2), "unit": "TFLOP/s",
+         "roofline": {"bound": "alu" if f32 else "mfma", "achieved": round(tf, 2), "peak": peak,
+                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                      "traffic": None if f32 else recorded_traffic(f"flash_fwd_bf16_{w.name}_traffic.md",
+                                                                   "flash_fwd_bf16.hip"),
+                      "algorithmic_flops": flops},
+         "max_abs_err": err, "err_checked": checked, "tolerance": 1e-5 if f32 else 2e-2}
+    if comparators_too:
+        e["comparators"] = comparators(torch, api, wl, w, r, max(steps // 2, 10), warmup)
+    return e
+
+
+def bench_rope_apply(torch, api, wl, steps, sets, orc=None, w=None):
     """rope_apply on a ragged batch (wl.RAGGED_ROPE unless given), cycling
-    `sets` independent Q/K buffers so the last-level cache cannot hold them."""
+    `sets` independent Q/K buffers so the last-level cache cannot hold them;
+    with `orc`, a fresh copy is rotated once more and compared with the
+    oracle (every element)."""
+    import numpy as np
     w = w or wl.RAGGED_ROPE
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    tdt = _tdt(torch, w.dtype)
     dev = torch.device("cuda:0")
     d = wl.rope_apply_inputs(w)
     q0 = torch.from_numpy(d["q"]).to(tdt).to(dev)
@@ -166,8 +237,8 @@ def bench_rope_apply(torch, api, wl, steps, sets, w=None):
     set_mb = (q0.numel() + k0.numel()) * q0.element_size() / 2 ** 20
     traffic = (recorded_traffic("rope_apply_ragged_8192tok_traffic.md", "rope_apply.hip")
                if w is wl.RAGGED_ROPE else None)
-    return {
-        "workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
+    res = {
+        "config": 4, "workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
         "ms_per_launch": round(kernel_ms, 5), "wall_ms_per_launch": round(ms_step, 5),
         "single_launch_p10_ms": round(durs[len(durs) // 10], 5),
         "single_launch_p90_ms": round(durs[(9 * len(durs)) // 10], 5),
@@ -176,19 +247,48 @@ def bench_rope_apply(torch, api, wl, steps, sets, w=None):
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": nbytes},
     }
+    del bufs, launches
+    if orc is not None:
+        qf, kf = q0.clone(), k0.clone()
+        api.rope_apply(qf, kf, pos, cos, sin, w.rot_dim, w.layout)
+        torch.cuda.synchronize()
+        err = 0.0
+        for x_in, x_out in ((d["q"], qf), (d["k"], kf)):
+            p = np.broadcast_to(d["positions"][:, None], x_in.shape[:2])
+            want = orc.rope(x_in, p, base=w.base, rot_dim=w.rot_dim, layout=w.layout)
+            got = x_out.float().cpu().numpy().astype(np.float64)
+            err = max(err, float(np.abs(got - want).max()))
+        res["max_abs_err"] = err
+        res["err_checked"] = "every element"
+    return res
 
 
-def bench_backward(torch, api, wl, steps, warmup):
+def streaming_ceiling(torch, nbytes, steps, sets):
+    """An in-place streaming pass over `nbytes` of HBM traffic (nbytes/2 read
+    and written back by torch's own elementwise kernel), cycling `sets`
+    buffers as the rope_apply timing does: what a plain kernel moving the
+    same bytes reaches on this GPU."""
+    dev = torch.device("cuda:0")
+    n = nbytes // 4   # bf16 elements: 2 bytes read + 2 written each
+    bufs = [torch.ones(n, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream(dev)
+    _, ms, _ = time_launches(torch, None, steps, sets, stream, rotate=lambda i: bufs[i % sets].mul_(1.0))
+    del bufs
+    return round(4 * n / (ms * 1e-3) / 1e9, 1)
+
+
+def bench_backward(torch, api, wl, orc, steps, warmup):
     """The backward of the fused forward on the bench workload: one step is
-    the two kernels of rope_flash_attn_bwd (Q and K rotated once into the
+    the kernels of rope_flash_attn_bwd (Q and K rotated once into the
     workspace with the row sums dO.O, then the merged dK/dV and dQ launch),
     inputs and the forward's output and row statistics resident in HBM."""
+    import numpy as np
     w = wl.HEADLINE
     dev = torch.device("cuda:0")
-    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in wl.attention_inputs(w))
-    g = torch.Generator(device=dev)
-    g.manual_seed(w.seed + 1000)
-    dout = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+    arrays = wl.attention_inputs(w)
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in arrays)
+    dout_np = wl.round_to(np.random.default_rng(w.seed + 1000).standard_normal(arrays[0].shape), "bf16")
+    dout = torch.from_numpy(dout_np).to(torch.bfloat16).to(dev)
     cos, sin = api.tables_build(w.base, w.rot, w.table_rows, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     o = api.flash_attn_fwd(q, k, v, cos, sin, w.q_off, w.k_off, w.rot, w.layout, w.causal, lse=lse)
@@ -199,7 +299,7 @@ def bench_backward(torch, api, wl, steps, warmup):
     ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
     flops = w.bwd_flops()
     tf = flops / (kernel_ms * 1e-3) / 1e12
-    return {
+    res = {
         "workload": w.name, "value": round(tf, 2), "unit": "TFLOP/s",
         "ms_per_step": round(kernel_ms, 5), "wall_ms_per_step": round(ms_step, 5),
         "single_step_p10_ms": round(durs[len(durs) // 10], 5),
@@ -210,11 +310,22 @@ def bench_backward(torch, api, wl, steps, warmup):
                                                  "flash_bwd_bf16.hip"),
                      "algorithmic_flops": flops},
     }
+    if orc is not None:
+        refs = orc.attention_bwd(*arrays, dout_np, q_off=w.q_off, k_off=w.k_off, base=w.base,
+                                 layout=w.layout)
+        rel = {}
+        for name, g, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+            got = g.float().cpu().numpy().astype(np.float64)
+            rel[name] = round(float(np.abs(got - ref).max() / np.abs(ref).max()), 6)
+        res["max_rel_err"] = rel
+        res["err_checked"] = "every element (max |err| / max |ref| per tensor; bar 2e-2)"
+    return res
 
 
-def bench_decode(torch, api, wl, steps, warmup):
+def bench_decode(torch, api, wl, orc, steps, warmup):
     """The decode step of the continuous batch (wl.DECODE): HBM bytes the
     step must move over the time of one step (both kernels of the step)."""
+    import numpy as np
     w = wl.DECODE
     dev = torch.device("cuda:0")
     d = wl.decode_inputs(w, with_cache=False)
@@ -247,6 +358,24 @@ def bench_decode(torch, api, wl, steps, warmup):
                      "traffic": recorded_traffic(f"decode_bf16_{w.name}_traffic.md", "decode_bf16.hip"),
                      "algorithmic_bytes": nbytes},
     }
+    if orc is not None:
+        # one more step on the resident caches: each launch appends at the same
+        # rows, so the cache rows below L are the seeded values; requests
+        # 0, 7 and 15 against the oracle (cache rows taken as rotated keys)
+        api.decode_attn_fwd(q, k_new, v_new, k_cache, v_cache, lens, cos, sin, w.rot, w.layout, out=out)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = 0.0
+        for b in (0, 7, 15):
+            L = int(d["lens"][b])
+            kc = k_cache[b, :, :L + 1].float().cpu().numpy().astype(np.float64)
+            vc = v_cache[b, :, :L + 1].float().cpu().numpy().astype(np.float64)
+            qr = orc.rope(d["q"][b][:, None, :], [L], base=w.base, layout=w.layout)
+            want = orc.attention(qr[None], kc[None], vc[None], q_off=L, k_off=0, rot_dim=0,
+                                 causal=True)[0, :, 0, :]
+            err = max(err, float(np.abs(got[b] - want).max()))
+        res["max_abs_err"] = err
+        res["err_checked"] = "every output row of requests 0, 7 and 15"
     del k_cache, v_cache
     return res
 
@@ -265,13 +394,13 @@ def comparators(torch, api, wl, w, r, steps, warmup):
 
     def unfused():
         qt = q.permute(0, 2, 1, 3).reshape(w.B * T, w.H, w.D).contiguous()
-        kt = k.permute(0, 2, 1, 3).reshape(w.B * w.Sk, w.H, w.D).contiguous()
+        kt = k.permute(0, 2, 1, 3).reshape(w.B * w.Sk, w.Hkv, w.D).contiguous()
         pq = torch.arange(w.q_off, w.q_off + T, dtype=torch.int32, device=dev).repeat(w.B)
         api.rope_apply(qt, None, pq, r["cos"], r["sin"], w.rot, w.layout)
         pk = torch.arange(w.k_off, w.k_off + w.Sk, dtype=torch.int32, device=dev).repeat(w.B)
         api.rope_apply(None, kt, pk, r["cos"], r["sin"], w.rot, w.layout)
         qr = qt.reshape(w.B, T, w.H, w.D).permute(0, 2, 1, 3).contiguous()
-        kr = kt.reshape(w.B, w.Sk, w.H, w.D).permute(0, 2, 1, 3).contiguous()
+        kr = kt.reshape(w.B, w.Sk, w.Hkv, w.D).permute(0, 2, 1, 3).contiguous()
         return api.flash_attn_fwd(qr, kr, v, rot_dim=0, causal=w.causal, q_pos_offset=w.q_off,
                                   k_pos_offset=w.k_off)
 
@@ -307,7 +436,9 @@ def copy_calibration(torch, steps, nbytes=256 * 2 ** 20):
 
 
 def cpu_baseline(wl, w, seconds):
-    """The oracle on whole heads of the workload, cycled until `seconds` pass."""
+    """The oracle on whole heads of the workload, cycled until `seconds` pass;
+    beside it the oracle's rope on the ragged batch (GB/s) and single-thread
+    times of the fp32 and the 1x8x512x64 cases."""
     import numpy as np
 
     import oracle
@@ -329,9 +460,39 @@ def cpu_baseline(wl, w, seconds):
             break
     dt = time.perf_counter() - t0
     tflops = 4 * w.D * pairs_per_head * done / dt / 1e12
-    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": orc.threads(), "kind": "oracle",
-            "sample": f"{done} whole heads of {w.name} (fp64 C oracle with OpenMP; "
-                      f"{dt:.1f} s, rope + dense masked softmax per head)"}
+    threads = orc.threads()
+    res = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} whole heads of {w.name} (fp64 C oracle with OpenMP; "
+                     f"{dt:.1f} s, rope + dense masked softmax per head)"}
+
+    def rope_rate():
+        rw = wl.RAGGED_ROPE
+        d = wl.rope_apply_inputs(rw)
+        t = time.perf_counter()
+        for x in (d["q"], d["k"]):
+            orc.rope(x, np.broadcast_to(d["positions"][:, None], x.shape[:2]), base=rw.base,
+                     rot_dim=rw.rot_dim, layout=rw.layout)
+        return rw.algorithmic_bytes() / (time.perf_counter() - t) / 1e9
+
+    def attn_ms(x):
+        a = wl.attention_inputs(x)
+        t = time.perf_counter()
+        orc.attention(*a, q_off=x.q_off, k_off=x.k_off, rot_dim=x.rot, base=x.base, layout=x.layout,
+                      causal=x.causal)
+        return (time.perf_counter() - t) * 1e3
+
+    res["rope_apply"] = {"value": round(rope_rate(), 3), "unit": "GB/s", "cores": threads,
+                         "sample": f"the whole {wl.RAGGED_ROPE.name} batch"}
+    orc.set_threads(1)
+    try:
+        res["single_thread"] = {
+            "rope_apply_gbs": round(rope_rate(), 3),
+            wl.TINY_F32.name + "_ms": round(attn_ms(wl.TINY_F32), 3),
+            wl.SMALL_BF16.name + "_ms": round(attn_ms(wl.SMALL_BF16), 3),
+        }
+    finally:
+        orc.set_threads(threads)
+    return res
 
 
 def main():
@@ -350,6 +511,10 @@ def main():
     if args.only == "copy":
         print(json.dumps(copy_calibration(torch, args.steps)), flush=True)
         return
+    orc = None
+    if args.only == "all":
+        import oracle
+        orc = oracle.load()
     w = {x.name: x for x in wl.ATTENTION_WORKLOADS}[args.workload]
     result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
@@ -377,40 +542,42 @@ def main():
                               "algorithmic_flops": flops}
         if w.name in PAGE_ROPE_MS:
             result["vs_baseline"] = round(PAGE_ROPE_MS[w.name] / r["ms_step"], 2)
-        if args.only == "all" and not args.no_comparators:
-            result["comparators"] = comparators(torch, api, wl, w, r, max(args.steps // 2, 10),
-                                                args.warmup)
-        for key in ("q", "k", "v", "out"):
-            r.pop(key)
+        if orc is not None:
+            result["max_abs_err"], result["err_checked"] = fused_error(orc, w, r)
         del r
-    if args.only in ("all", "fused"):
-        # the same workload with fp16 storage (the fp16 matrix cores)
+    if args.only == "all" and not args.no_configs:
+        configs = [fused_entry(torch, api, wl, orc, wl.TINY_F32, 1, args.steps, args.warmup),
+                   fused_entry(torch, api, wl, orc, wl.SMALL_BF16, 2, args.steps, args.warmup, True)]
+        for x in wl.SWEEP_BF16:
+            configs.append(fused_entry(torch, api, wl, orc, x, 3, args.steps, args.warmup, True))
+        ra = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets, orc)
+        ra["ceiling_gbs"] = streaming_ceiling(torch, wl.RAGGED_ROPE.algorithmic_bytes(), args.rope_steps,
+                                              args.rope_sets)
+        ra["frac_of_ceiling"] = round(ra["value"] / ra["ceiling_gbs"], 4)
+        configs.append(ra)
+        configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_OFFSET, 5, args.steps, args.warmup))
+        configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_GQA, "5-gqa", args.steps, args.warmup))
+        result["configs"] = configs
+        # the headline workload with fp16 storage (the fp16 matrix cores)
         wf = wl.HEADLINE_F16
         rf = bench_fused(torch, api, wl, wf, args.steps, args.warmup)
         tf = wf.flops() / (rf["kernel_ms"] * 1e-3) / 1e12
         result["fused_f16"] = {"workload": wf.name, "value": round(tf, 2), "unit": "TFLOP/s",
                                "kernel_ms": round(rf["kernel_ms"], 5),
-                               "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+                               "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                               "max_abs_err": fused_error(orc, wf, rf)[0]}
         del rf
-    if args.only in ("all", "rope_apply"):
-        result["rope_apply"] = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets)
+    if args.only == "rope_apply" or (args.only == "all" and args.no_configs):
+        result["rope_apply"] = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets, orc)
+    if args.only == "all":
         # the same batch with fp16 storage (same bytes, same kernel family)
         rf = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets, w=wl.RAGGED_ROPE_F16)
-        result["rope_apply"]["f16"] = {k: rf[k] for k in ("workload", "value", "unit", "ms_per_launch")}
-        result["rope_apply"]["f16"]["frac"] = rf["roofline"]["frac"]
+        result["rope_apply_f16"] = {k: rf[k] for k in ("workload", "value", "unit", "ms_per_launch")}
+        result["rope_apply_f16"]["frac"] = rf["roofline"]["frac"]
     if args.only in ("all", "backward"):
-        result["backward"] = bench_backward(torch, api, wl, args.bwd_steps, max(args.warmup // 4, 3))
+        result["backward"] = bench_backward(torch, api, wl, orc, args.bwd_steps, max(args.warmup // 4, 3))
     if args.only in ("all", "decode"):
-        result["decode"] = bench_decode(torch, api, wl, args.decode_steps, max(args.warmup // 4, 3))
-    if args.sweep:
-        for x in wl.ATTENTION_WORKLOADS:
-            if x.dtype != "bf16":
-                continue
-            rx = bench_fused(torch, api, wl, x, args.steps, args.warmup, balance=args.balance)
-            tf = x.flops() / (rx["kernel_ms"] * 1e-3) / 1e12
-            sys.stderr.write(f"sweep {x.name:55s} kernel {rx['kernel_ms'] * 1e3:9.2f} us  "
-                             f"{tf:8.1f} TFLOP/s  {tf / PEAK_BF16_TFLOPS * 100:5.1f}% of peak\n")
-            del rx
+        result["decode"] = bench_decode(torch, api, wl, orc, args.decode_steps, max(args.warmup // 4, 3))
     torch.cuda.synchronize()
     if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_seconds)
