@@ -313,13 +313,19 @@ int oracle_attention_lse(const double *q, const double *k, double *lse,
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     for (int64_t i = 0; i < Sq; ++i)
         if (visible_keys(i, Sk, q_off, k_off, causal) == 0) return OR_ERR_EMPTY_ROW;
-    const int64_t nq = B * H * Sq, group = H / Hkv;
+    const int64_t nq = B * H * Sq, nk = B * Hkv * Sk, group = H / Hkv;
+    /* Rotate every K row once, at its absolute position. */
+    double *kr = malloc(sizeof(double) * (size_t)(nk * D));
+    if (!kr) return OR_ERR_NOMEM;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nk; ++r)
+        rotate_row(k + r * D, kr + r * D, D, rot_dim, (double)(k_off + r % Sk) / pos_div, base,
+                   layout);
     int status = OR_OK;
 #pragma omp parallel
     {
         double *qr = malloc(sizeof(double) * (size_t)D);
-        double *kr = malloc(sizeof(double) * (size_t)D);
-        if (!qr || !kr) {
+        if (!qr) {
 #pragma omp atomic write
             status = OR_ERR_NOMEM;
         } else {
@@ -327,30 +333,27 @@ int oracle_attention_lse(const double *q, const double *k, double *lse,
             for (int64_t r = 0; r < nq; ++r) {
                 int64_t bh = r / Sq, i = r % Sq, kvh = bh / group;
                 int64_t n = visible_keys(i, Sk, q_off, k_off, causal);
+                const double *krh = kr + kvh * Sk * D;
                 rotate_row(q + r * D, qr, D, rot_dim, (double)(q_off + i) / pos_div, base, layout);
                 double m = -INFINITY;
                 for (int64_t j = 0; j < n; ++j) {
-                    rotate_row(k + (kvh * Sk + j) * D, kr, D, rot_dim, (double)(k_off + j) / pos_div,
-                               base, layout);
                     double s = 0.0;
-                    for (int d = 0; d < D; ++d) s += qr[d] * kr[d];
+                    for (int d = 0; d < D; ++d) s += qr[d] * krh[j * D + d];
                     s *= scale;
                     if (s > m) m = s;
                 }
                 double l = 0.0;
                 for (int64_t j = 0; j < n; ++j) {
-                    rotate_row(k + (kvh * Sk + j) * D, kr, D, rot_dim, (double)(k_off + j) / pos_div,
-                               base, layout);
                     double s = 0.0;
-                    for (int d = 0; d < D; ++d) s += qr[d] * kr[d];
+                    for (int d = 0; d < D; ++d) s += qr[d] * krh[j * D + d];
                     l += exp(s * scale - m);
                 }
                 lse[r] = m + log(l);
             }
         }
         free(qr);
-        free(kr);
     }
+    free(kr);
     return status;
 }
 
