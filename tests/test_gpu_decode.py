@@ -240,6 +240,7 @@ def test_prepared_launch_keeps_its_workspace():
     lens = torch.from_numpy(d["lens"]).to(DEV)
     cos, sin = api.tables_build(w.base, w.rot, w.S_max, device=DEV)
     out = torch.empty_like(dev["q"])
+    api._WORKSPACES.pop(("decode", dev["q"].device), None)   # start from an empty cache
     launch = api.prepare_decode_attn_fwd(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"],
                                          dev["v_cache"], lens, out, cos, sin)
     ws = weakref.ref(launch.workspace)
