@@ -40,12 +40,12 @@ def sources() -> list[Path]:
     return sorted(CSRC.glob("*.hip")) + [CSRC / "abi.cpp"]
 
 
-# Per-file extra flags.  The fused attention kernel never produces or tests a
+# Per-file extra flags.  The fused attention kernels never produce or test a
 # NaN (masked scores are -inf, which stays honoured); without
 # -fno-honor-nans every fmaxf on a matrix-core result gets a NaN-quieting
 # v_max_f32 x, x, x in front of it.  Host-side argument validation (abi.cpp)
 # does test for NaN and keeps IEEE semantics.
-FILE_FLAGS = {"flash_fwd_bf16.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {name: ["-fno-honor-nans"] for name in ("flash_fwd_bf16.hip", "flash_fwd_pp.hip")}
 
 
 def _compile(src: Path) -> Path:
