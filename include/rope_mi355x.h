@@ -63,6 +63,7 @@ extern "C" {
 #define ROPE_ERR_TABLE_RANGE 6   /* table_rows too small for the positions the call uses */
 #define ROPE_ERR_HIP 7           /* a HIP launch failed */
 #define ROPE_ERR_ALIGN 8         /* a pointer or stride breaks the required alignment */
+#define ROPE_ERR_SCRATCH 9       /* the call needs more scratch than the library's static array */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *rope_status_str(int status);
@@ -328,6 +329,39 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
  * of S_max.  Makes no device allocation and no HIP call.
  */
 int64_t rope_decode_workspace_size(int B, int H, int H_kv, int64_t S_max, int head_dim);
+
+/*
+ * Bytes of the library's static decode scratch: one array of this size in
+ * each GPU's memory, held from the first rope_decode_attn_fwd_noalloc call on
+ * that GPU until the process ends.
+ */
+#define ROPE_DECODE_SCRATCH_BYTES (8 << 20)
+
+/*
+ * rope_decode_attn_fwd_noalloc -- rope_decode_attn_fwd without a workspace
+ * argument, for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  It allocates nothing (no hipMalloc, hipFree or allocating
+ * library call); the partial states and the piece table live in a static
+ * device array of ROPE_DECODE_SCRATCH_BYTES per GPU, whose address the
+ * first call on a device looks up once (with that device current).
+ *
+ * Arguments, results and errors are those of rope_decode_attn_fwd, plus
+ * ROPE_ERR_SCRATCH, returned before any HIP call, when
+ * rope_decode_workspace_size() for the shapes exceeds
+ * ROPE_DECODE_SCRATCH_BYTES (for head_dim 128, B * H_kv up to 2997 fits
+ * with H / H_kv = 4, up to 990 with H / H_kv = 8).  ROPE_ERR_HIP if the
+ * array's address cannot be obtained.
+ * Nothing in the array needs clearing between calls: every byte a call
+ * reads was written earlier in that call.  All calls on one GPU share the
+ * array, so calls that may overlap in time on one GPU (different streams,
+ * or host threads) race and must be serialised by the caller.
+ */
+int rope_decode_attn_fwd_noalloc(const void *q, const void *k_new, const void *v_new,
+                                 void *k_cache, void *v_cache, const int32_t *cache_lens, void *o,
+                                 int B, int H, int H_kv, int64_t S_max, int head_dim,
+                                 const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                                 int rot_dim, int layout, float softmax_scale, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

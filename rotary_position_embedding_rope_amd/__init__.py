@@ -6,6 +6,7 @@ The HIP library is loaded on first use of an entry point; importing the
 package (for example for ``workloads``) does not touch the GPU.
 """
 _API = ("tables_build", "rope_apply", "flash_attn_fwd", "flash_attn_bwd", "decode_attn_fwd",
+        "decode_attn_fwd_noalloc",
         "prepare_flash_attn_fwd", "prepare_flash_attn_bwd", "prepare_decode_attn_fwd",
         "prepare_rope_apply", "RopeError")
 __all__ = list(_API) + ["workloads"]

@@ -12,12 +12,15 @@ LIBRARY = Path(__file__).resolve().parent / "librope_mi355x.so"
 
 NEOX, GPTJ = 0, 1
 BF16, F32, F16 = 0, 1, 2
-OK, ERR_NULL, ERR_SHAPE, ERR_BASE, ERR_UNSUPPORTED, ERR_EMPTY_ROW, ERR_TABLE_RANGE, ERR_HIP, ERR_ALIGN = range(9)
+OK, ERR_NULL, ERR_SHAPE, ERR_BASE, ERR_UNSUPPORTED, ERR_EMPTY_ROW, ERR_TABLE_RANGE, ERR_HIP, ERR_ALIGN, \
+    ERR_SCRATCH = range(10)
+DECODE_SCRATCH_BYTES = 8 << 20   # ROPE_DECODE_SCRATCH_BYTES
 
 # every symbol include/rope_mi355x.h declares
 EXPORTS = ("rope_status_str", "rope_tables_build", "rope_tables_build_scaled", "rope_apply",
            "rope_flash_attn_fwd", "rope_flash_attn_bwd", "rope_flash_attn_bwd_workspace_size",
-           "rope_flash_attn_workspace_size", "rope_decode_attn_fwd", "rope_decode_workspace_size")
+           "rope_flash_attn_workspace_size", "rope_decode_attn_fwd", "rope_decode_workspace_size",
+           "rope_decode_attn_fwd_noalloc")
 
 _lib = None
 
@@ -56,6 +59,9 @@ def load() -> ctypes.CDLL:
     lib.rope_decode_attn_fwd.restype = i32
     lib.rope_decode_workspace_size.argtypes = [i32, i32, i32, i64, i32]
     lib.rope_decode_workspace_size.restype = i64
+    lib.rope_decode_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32,
+                                                 vp, vp, i64, i32, i32, f32, i32, vp]
+    lib.rope_decode_attn_fwd_noalloc.restype = i32
     _lib = lib
     return lib
 

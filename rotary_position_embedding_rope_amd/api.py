@@ -260,6 +260,9 @@ def decode_workspace(q: torch.Tensor, k_cache: torch.Tensor) -> torch.Tensor:
     return ws
 
 
+_NO_WORKSPACE = object()   # _decode_args marker: the static-scratch entry point takes none
+
+
 def _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
                  softmax_scale, out, workspace):
     _require_cuda(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, out)
@@ -288,6 +291,10 @@ def _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_di
         cp, sp, rows = cos.data_ptr(), sin.data_ptr(), cos.shape[0]
     else:
         cp, sp, rows = None, None, 0
+    if workspace is _NO_WORKSPACE:
+        return None, (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                      cache_lens.data_ptr(), out.data_ptr(), B, H, Hkv, S_max, D, cp, sp, rows, rot,
+                      _layout(layout), float(softmax_scale), _dtype(q), _stream(q))
     if workspace is None:
         workspace = decode_workspace(q, k_cache)
     return workspace, (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -311,6 +318,21 @@ def decode_attn_fwd(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     _, args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
                            softmax_scale, out, workspace)
     _check(lib.rope_decode_attn_fwd(*args), "rope_decode_attn_fwd")
+    return out
+
+
+def decode_attn_fwd_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor, cache_lens: torch.Tensor,
+                            out: torch.Tensor, cos: torch.Tensor | None = None,
+                            sin: torch.Tensor | None = None, rot_dim: int | None = None, layout="neox",
+                            softmax_scale: float = 0.0) -> torch.Tensor:
+    """decode_attn_fwd through rope_decode_attn_fwd_noalloc: the same step on
+    the library's static per-GPU scratch, allocating nothing (``out`` is
+    required).  Calls that may overlap on one GPU must be serialised."""
+    lib = _lib.load()
+    _, args = _decode_args(q, k_new, v_new, k_cache, v_cache, cache_lens, cos, sin, rot_dim, layout,
+                           softmax_scale, out, _NO_WORKSPACE)
+    _check(lib.rope_decode_attn_fwd_noalloc(*args), "rope_decode_attn_fwd_noalloc")
     return out
 
 

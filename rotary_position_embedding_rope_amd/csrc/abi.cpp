@@ -101,6 +101,7 @@ const char *rope_status_str(int status)
     case ROPE_ERR_TABLE_RANGE: return "cos/sin table has too few rows for the positions used";
     case ROPE_ERR_HIP: return "HIP kernel launch failed";
     case ROPE_ERR_ALIGN: return "pointer or stride breaks the required alignment";
+    case ROPE_ERR_SCRATCH: return "the call needs more scratch than the static decode array holds";
     default: return "unknown status";
     }
 }
@@ -327,6 +328,11 @@ int rope_flash_attn_bwd(const void *q, const void *k, const void *v, const void 
 
 namespace {
 
+int decode_checked(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                   const int32_t *cache_lens, void *o, int B, int H, int H_kv, int64_t S_max, int head_dim,
+                   const float *cos_tab, const float *sin_tab, int64_t table_rows, int rot_dim, int layout,
+                   float softmax_scale, int dtype, void *workspace, int64_t workspace_bytes, void *stream);
+
 int check_decode_shape(int B, int H, int H_kv, int64_t S_max, int head_dim)
 {
     if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || S_max < 1) return ROPE_ERR_SHAPE;
@@ -358,14 +364,60 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
 {
     const int st = check_decode_shape(B, H, H_kv, S_max, head_dim);
     if (st != ROPE_OK) return st;
+    if (!workspace) return ROPE_ERR_NULL;
+    return decode_checked(q, k_new, v_new, k_cache, v_cache, cache_lens, o, B, H, H_kv, S_max, head_dim, cos_tab,
+                          sin_tab, table_rows, rot_dim, layout, softmax_scale, dtype, workspace, workspace_bytes,
+                          stream);
+}
+
+int rope_decode_attn_fwd_noalloc(const void *q, const void *k_new, const void *v_new,
+                                 void *k_cache, void *v_cache, const int32_t *cache_lens, void *o,
+                                 int B, int H, int H_kv, int64_t S_max, int head_dim,
+                                 const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                                 int rot_dim, int layout, float softmax_scale, int dtype, void *stream)
+{
+    const int st = check_decode_shape(B, H, H_kv, S_max, head_dim);
+    if (st != ROPE_OK) return st;
+    // before any HIP call: the static array must hold what the shapes need
+    if (rope_decode_workspace_bytes(B, H, H_kv, head_dim) > (int64_t)ROPE_DECODE_SCRATCH_BYTES)
+        return ROPE_ERR_SCRATCH;
+    // workspace nullptr: decode_checked looks up the current device's copy
+    // of the static array after every host-side check has passed
+    return decode_checked(q, k_new, v_new, k_cache, v_cache, cache_lens, o, B, H, H_kv, S_max, head_dim, cos_tab,
+                          sin_tab, table_rows, rot_dim, layout, softmax_scale, dtype, nullptr,
+                          (int64_t)ROPE_DECODE_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// rope_decode_attn_fwd after the shape check: arguments, overlap and
+// alignment checks, then the launch on `workspace`, or (workspace nullptr)
+// on the static decode scratch, whose address is looked up only after the
+// host-side checks
+int decode_checked(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                   const int32_t *cache_lens, void *o, int B, int H, int H_kv, int64_t S_max, int head_dim,
+                   const float *cos_tab, const float *sin_tab, int64_t table_rows, int rot_dim, int layout,
+                   float softmax_scale, int dtype, void *workspace, int64_t workspace_bytes, void *stream)
+{
     if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2 != 0) return ROPE_ERR_SHAPE;
     if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return ROPE_ERR_SHAPE;
     if (!valid_layout(layout)) return ROPE_ERR_UNSUPPORTED;
     if (dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_ERR_UNSUPPORTED;
-    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !o || !workspace)
-        return ROPE_ERR_NULL;
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !o) return ROPE_ERR_NULL;
     if (rot_dim > 0 && (!cos_tab || !sin_tab)) return ROPE_ERR_NULL;
     if (rot_dim > 0 && table_rows < 1) return ROPE_ERR_TABLE_RANGE;
+    if (workspace_bytes < rope_decode_workspace_bytes(B, H, H_kv, head_dim)) return ROPE_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(cache_lens, 4))
+        return ROPE_ERR_ALIGN;
+    if (rot_dim > 0 && (!aligned(cos_tab, 4) || !aligned(sin_tab, 4))) return ROPE_ERR_ALIGN;
+    if (workspace == nullptr) {
+        workspace = rope_decode_static_scratch();
+        if (workspace == nullptr) return ROPE_ERR_HIP;
+    }
+    if (!aligned(workspace, 16)) return ROPE_ERR_ALIGN;
     {
         // o, the caches (rows L are written) and the workspace: none may
         // overlap another or an input
@@ -378,11 +430,6 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
                          {sin_tab, nt}}))
             return ROPE_ERR_SHAPE;
     }
-    if (workspace_bytes < rope_decode_workspace_bytes(B, H, H_kv, head_dim)) return ROPE_ERR_SHAPE;
-    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
-        !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(workspace, 16) || !aligned(cache_lens, 4))
-        return ROPE_ERR_ALIGN;
-    if (rot_dim > 0 && (!aligned(cos_tab, 4) || !aligned(sin_tab, 4))) return ROPE_ERR_ALIGN;
 
     DecodeArgs a;
     a.q = q; a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
@@ -396,4 +443,4 @@ int rope_decode_attn_fwd(const void *q, const void *k_new, const void *v_new,
     return api_status(rope_launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
-}  // extern "C"
+}  // namespace

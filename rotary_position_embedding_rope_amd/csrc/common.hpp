@@ -198,6 +198,10 @@ int64_t rope_decode_workspace_bytes(int B, int H, int H_kv, int head_dim);
 // Passes of 64 cached positions the step may walk: an upper bound the host
 // checks so that device-side pass counts fit in 32 bits.
 int64_t rope_decode_max_passes(int B, int H_kv, int64_t S_max);
+// The current device's copy of the static decode scratch
+// (ROPE_DECODE_SCRATCH_BYTES), looked up on the first call per device;
+// nullptr if HIP cannot give its address.
+void *rope_decode_static_scratch();
 
 // Compute units of the current device (cached per device; 0 on error).
 int rope_device_cu_count();

@@ -22,7 +22,10 @@
 // partial state per slice it touched; a second kernel combines the partial
 // states of a slice (running max and sum rescaling, the merge rule of
 // section 5 of the same page).
+#include <atomic>
+
 #include "common.hpp"
+#include "rope_mi355x.h"
 
 namespace {
 
@@ -663,6 +666,29 @@ int64_t part_bytes(int B, int H, int H_kv, int head_dim)
 }
 
 }  // namespace
+
+// Static scratch of the allocation-free decode entry point: partial states
+// and piece table, one copy per GPU.  Host code never uses this name as an
+// address (on the host it is a stand-in symbol); it asks HIP for the
+// device copy's address and keeps that per device.
+static __device__ __align__(256) unsigned char scratch[ROPE_DECODE_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void *> g_scratch[64];
+}  // namespace
+
+void *rope_decode_static_scratch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        // with `dev` current: its own copy of the array
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
 
 int64_t rope_decode_max_passes(int B, int H_kv, int64_t S_max)
 {

@@ -50,13 +50,14 @@ def test_status_codes_match_header():
     assert codes["ROPE_ERR_EMPTY_ROW"] == _lib.ERR_EMPTY_ROW
     assert codes["ROPE_ERR_TABLE_RANGE"] == _lib.ERR_TABLE_RANGE
     assert codes["ROPE_ERR_HIP"] == _lib.ERR_HIP and codes["ROPE_ERR_ALIGN"] == _lib.ERR_ALIGN
+    assert codes["ROPE_ERR_SCRATCH"] == _lib.ERR_SCRATCH
     assert codes["ROPE_NEOX"] == _lib.NEOX and codes["ROPE_GPTJ"] == _lib.GPTJ
     assert codes["ROPE_BF16"] == _lib.BF16 and codes["ROPE_F32"] == _lib.F32
     assert codes["ROPE_F16"] == _lib.F16
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         assert _lib.status_str(s)
     assert _lib.status_str(99) == "unknown status"
 
@@ -283,6 +284,49 @@ def test_decode_workspace_size(lib):
     assert lib.rope_decode_workspace_size(1, 32, 2, 100, 128) == -_lib.ERR_UNSUPPORTED
     # no rotation: tables may be NULL (a bad shape is still reported)
     assert lib.rope_decode_attn_fwd(*decode_args(rot=0, cos=None, sin=None, rows=0, B=0)) == _lib.ERR_SHAPE
+
+
+def test_decode_scratch_size_matches_header():
+    text = HEADER.read_text()
+    m = re.search(r"#define ROPE_DECODE_SCRATCH_BYTES \((\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DECODE_SCRATCH_BYTES
+
+
+def noalloc_args(**over):
+    a = decode_args(**over)
+    return a[:19] + [a[21]]   # no workspace pointer or size
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(B=0), _lib.ERR_SHAPE),
+    (dict(Hkv=2), _lib.ERR_UNSUPPORTED),
+    (dict(D=96, rot=96), _lib.ERR_UNSUPPORTED),
+    # scratch need past ROPE_DECODE_SCRATCH_BYTES: rejected before any HIP call
+    (dict(B=2998, Hkv=1, H=4), _lib.ERR_SCRATCH),    # one (request, kv head) too many
+    (dict(B=991, Hkv=1, H=8), _lib.ERR_SCRATCH),
+    (dict(B=512, Hkv=8, H=32), _lib.ERR_SCRATCH),    # 4096 (request, kv head) pairs
+    # fits: the host-side argument checks still run before the scratch lookup
+    (dict(B=2997, Hkv=1, H=4, q=None), _lib.ERR_NULL),
+    (dict(B=990, Hkv=1, H=8, q=None), _lib.ERR_NULL),
+    (dict(rot=130), _lib.ERR_SHAPE),
+    (dict(cos=None), _lib.ERR_NULL),
+    (dict(rows=0), _lib.ERR_TABLE_RANGE),
+    (dict(kc=slot(4, 8)), _lib.ERR_ALIGN),
+])
+def test_decode_noalloc_rejects_before_any_device_call(lib, over, want):
+    # shape, scratch size, pointer, table and alignment rejections come before
+    # the scratch lookup (the overlap check, which needs the scratch address,
+    # comes after it)
+    assert lib.rope_decode_attn_fwd_noalloc(*noalloc_args(**over)) == want
+
+
+def test_decode_noalloc_limit_matches_workspace_size(lib):
+    # the entry point accepts exactly the shapes whose workspace fits
+    for G, D, n_fit in [(4, 128, 2997), (8, 128, 990), (4, 64, 6867)]:
+        assert lib.rope_decode_workspace_size(n_fit, G, 1, 100, D) <= _lib.DECODE_SCRATCH_BYTES
+        assert lib.rope_decode_workspace_size(n_fit + 1, G, 1, 100, D) > _lib.DECODE_SCRATCH_BYTES
+        args = noalloc_args(B=n_fit + 1, H=G, Hkv=1, D=D, rot=D)
+        assert lib.rope_decode_attn_fwd_noalloc(*args) == _lib.ERR_SCRATCH
 
 
 # --------------------------------------------------------------------------
