@@ -156,9 +156,11 @@ int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream);
 // device (0: the launch needs none).
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a);
 int rope_launch_flash_f32(const FlashArgs &a, hipStream_t stream);
-// Head dim 128 (bf16 / fp16): the ping-pong kernel; -1 when it does not take
-// the shape (nothing launched).
+// Head dim 128 (bf16 / fp16): the two-team kernel of flash_fwd_pp.hip;
+// -1 when it does not take the shape (nothing launched).
 int rope_launch_flash_pp(const FlashArgs &a, hipStream_t stream);
+// Workspace bytes its split-key schedule would use (0: none).
+int64_t rope_flash_pp_workspace_bytes(const FlashArgs &a);
 
 struct FlashBwdArgs {
     const void *q, *k, *v, *o, *dout;   // q, o, dout [B, H, Sq, D]; k, v [B, H_kv, Sk, D]

@@ -1413,24 +1413,18 @@ int launch_d(const FlashArgs &a, hipStream_t stream)
 }  // namespace
 
 // dtype 0 (bf16) or 2 (fp16): the same kernels over either 16-bit type.
-// Head dim 128 without a balanced-schedule workspace runs the ping-pong
-// kernel (flash_fwd_pp.hip).
+// Head dim 128 runs the two-team kernel of flash_fwd_pp.hip.
 int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream)
 {
-    if (a.head_dim == 128) {
-        const int64_t need = a.workspace ? rope_flash_bf16_workspace_bytes(a) : 0;
-        const bool balanced = need > 0 && a.workspace_bytes >= need;
-        if (!balanced) {
-            const int rc = rope_launch_flash_pp(a, stream);
-            if (rc >= 0) return rc;
-        }
-    }
+    const int rc = rope_launch_flash_pp(a, stream);
+    if (rc >= 0) return rc;
     if (a.dtype == 2) return a.head_dim == 64 ? launch_d<64, _Float16>(a, stream) : launch_d<128, _Float16>(a, stream);
     return a.head_dim == 64 ? launch_d<64, __bf16>(a, stream) : launch_d<128, __bf16>(a, stream);
 }
 
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a)
 {
+    if (a.head_dim == 128 && (a.dtype == 0 || a.dtype == 2)) return rope_flash_pp_workspace_bytes(a);
     Params p;
     if (a.head_dim == 64) {
         plan<64>(a, p);

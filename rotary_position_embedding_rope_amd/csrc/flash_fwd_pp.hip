@@ -60,8 +60,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int PP_D = 128;
-constexpr int PP_KP = PP_D + 8;      // K LDS row pitch (bf16)
 constexpr int PP_NKS = 2;            // K slots
 constexpr int PP_NVS = 3;            // V slots
 #ifndef ROPE_PP_BN
@@ -72,21 +70,38 @@ constexpr int PP_NVS = 3;            // V slots
 #endif
 constexpr int PP_PF = ROPE_PP_PF;   // LDS operand reads in flight ahead of the matrix instruction
 
-// Tile geometry for BN keys per tile (32 or 64).  Each team stages half of
-// a tile's keys; a staging unit is two CH-dim chunks of one key row.
-template <int BN> struct PPShape {
+// Tile geometry for head dim D (64 or 128) and BN keys per tile (32 or 64).
+// Each team stages half of a tile's keys; a staging unit is two CH-dim
+// chunks of one key row.  V rows are D / 8 chunks of 16 bytes, RPB rows to
+// a 1 KB block of the loads straight into LDS.
+template <int D, int BN> struct PPShape {
     static constexpr int NKB = BN / 32;           // 32-key blocks per tile
     static constexpr int HALF = BN / 2;           // keys a team stages per tile
     static constexpr int UPR = 256 / HALF;        // staging units per key row
-    static constexpr int CH = PP_D / (2 * UPR);   // dims per chunk (8 or 4)
-    static constexpr int NTRIG = CH / 4;          // 16-byte cos (and sin) loads per unit
-    static constexpr int VBW = HALF / 16;         // 1 KB value blocks per wave per tile
-    static constexpr int NLOAD = 2 + 2 * NTRIG + VBW;   // vector-memory loads per matrix step
-    static constexpr int K_ELEMS = BN * PP_KP;
-    static constexpr int V_ELEMS = BN * PP_D;
+    static constexpr int CH = D / (2 * UPR);      // dims per chunk (2, 4 or 8)
+    static constexpr int NTRIG = CH >= 4 ? CH / 4 : 1;   // cos (and sin) loads per unit
+    static constexpr int KP = D + 8;              // K LDS row pitch (elements)
+    static constexpr int CPR = D / 8;             // 16-byte chunks per V row
+    static constexpr int RPB = 64 / CPR;          // V rows per 1 KB block
+    static constexpr int VBW = HALF / RPB / 4;    // 1 KB value blocks per wave per tile
+    // vector-memory loads per matrix step (K chunks, cos/sin with rotation, V)
+    template <bool ROT> static constexpr int nload() { return 2 + (ROT ? 2 * NTRIG : 0) + VBW; }
+    static constexpr int K_ELEMS = BN * KP;
+    static constexpr int V_ELEMS = BN * D;
     static constexpr int LDS_BYTES = 2 * (PP_NKS * K_ELEMS + PP_NVS * V_ELEMS);
+    static_assert(CH >= 4 && VBW >= 1, "tile shape");
 };
+// Position of 16-byte chunk c of V row `row` in LDS: c ^ vswz(row).  Every
+// four consecutive keys of a transposing read then fall in different bank
+// groups (D = 128: rows are 256 bytes, so the row's low two bits pick a
+// quarter; D = 64: 128-byte rows, rows 2 and 3 of four take the other half).
+template <int D>
+__device__ __forceinline__ int vswz(int row)
+{
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 constexpr float PP_LAZY = 8.0f;      // log2 headroom before the reference is raised
+constexpr int PP_MAXSEG = 8;         // key segments per pair at most (split schedule)
 constexpr float PP_LN2 = 0.6931471805599453f;
 constexpr int RSRC_FLAGS = 0x00020000;
 
@@ -104,6 +119,11 @@ struct PPParams {
     int causal;
     int n_qt;    // 128-row query tiles
     int n_kt;    // key tiles
+    // split keys: the key tiles of a workgroup's query rows are cut into
+    // segments of seg_tiles tiles (nseg at most); segments of a cut pair
+    // leave fp32 partial states in ws, merged by flash_pp_merge_kernel
+    int seg_tiles, nseg;
+    float *ws;
 };
 
 // A buffer descriptor over `rows` rows of ROW_BYTES from `base` (wave-uniform
@@ -186,12 +206,25 @@ __device__ __forceinline__ int tiles_seen(const PPParams &p, int last)
     return v < p.n_kt ? (int)v : p.n_kt;
 }
 
-template <int BN, int LAYOUT, bool ROT, bool FULL, typename E>
+// Key tiles of the pair of query tiles (2 pr, 2 pr + 1): the larger count
+// of the two.
+template <int BN>
+__device__ __forceinline__ int pair_tiles(const PPParams &p, int pr)
+{
+    const int tB = 2 * pr + 1 < p.n_qt ? 2 * pr + 1 : 2 * pr;
+    const int last = tB * 128 + 127 < p.Sq ? tB * 128 + 127 : p.Sq - 1;
+    return tiles_seen<BN>(p, last);
+}
+
+// PING: ping-pong schedule (team 1 one phase behind team 0, two barriers per
+// key tile); otherwise both teams run each step together (one barrier per
+// tile).  SPLIT: the workgroup takes one key segment of its pair.
+template <int D, int BN, bool PING, bool SPLIT, int LAYOUT, bool ROT, bool FULL, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_pp_kernel(PPParams p)
 {
-    using SH = PPShape<BN>;
-    constexpr int D = PP_D, KP = PP_KP;
+    using SH = PPShape<D, BN>;
+    constexpr int KP = SH::KP;
     constexpr int DT = D / 16;          // k-steps of Q K^T
     constexpr int DB = D / 32;          // 32-dim blocks of O^T
     constexpr int NKB = SH::NKB, CH = SH::CH, UPR = SH::UPR;
@@ -211,13 +244,14 @@ void flash_fwd_pp_kernel(PPParams p)
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int rh = p.rot_dim / 2;   // table row stride (floats)
 
-    // ---- work item: (batch*head, two query tiles) ----
+    // ---- work item: (batch*head, two query tiles, key segment) ----
     const int bh = blockIdx.x % p.BH;
-    const int r = blockIdx.x / p.BH;
+    const int npair = (p.n_qt + 1) / 2;
+    const int r = (blockIdx.x / p.BH) % npair;
+    const int seg = SPLIT ? (int)(blockIdx.x / p.BH / npair) : 0;
     // Each workgroup takes two adjacent query tiles (team 0 the lower one), so
     // both teams walk nearly the same key range; under the causal mask the
     // pairs with the most keys come first.
-    const int npair = (p.n_qt + 1) / 2;
     const int pr = p.causal ? npair - 1 - r : r;
     const int tA = 2 * pr;
     const int tB = 2 * pr + 1;
@@ -229,16 +263,17 @@ void flash_fwd_pp_kernel(PPParams p)
     const int wlast = row0 + 31 < p.Sq ? row0 + 31 : p.Sq - 1;
     // tiles this wave computes, and the workgroup's staging range
     const int w_end = wave_rows ? tiles_seen<BN>(p, wlast) : 0;
-    int k_end;
-    {
-        const int lastA = tA * 128 + 127 < p.Sq ? tA * 128 + 127 : p.Sq - 1;
-        k_end = tiles_seen<BN>(p, lastA);
-        if (tB < p.n_qt) {
-            const int lastB = tB * 128 + 127 < p.Sq ? tB * 128 + 127 : p.Sq - 1;
-            const int kb = tiles_seen<BN>(p, lastB);
-            k_end = kb > k_end ? kb : k_end;
-        }
+    const int k_all = pair_tiles<BN>(p, pr);
+    // this workgroup's key tiles [k_beg, k_end): its segment of the pair's
+    int k_beg = 0, k_end = k_all;
+    bool partial = false;   // the pair is cut: leave a partial state
+    if constexpr (SPLIT) {
+        k_beg = seg * p.seg_tiles;
+        if (k_beg >= k_all) return;   // no segment here (uniform over the workgroup)
+        k_end = k_beg + p.seg_tiles < k_all ? k_beg + p.seg_tiles : k_all;
+        partial = k_all > p.seg_tiles;
     }
+    const int w_stop = w_end < k_end ? w_end : k_end;   // softmax only below this tile
     // first tile needing the element mask (diagonal or ragged end), and the
     // lane's key limit: key j of the segment is visible iff j <= lim_base
     const int qrow = row0 + l32;
@@ -287,7 +322,7 @@ void flash_fwd_pp_kernel(PPParams p)
     float sc[CH], ss[CH];                // their cos / sin
     auto fetch_k = [&](int kt) {
         const int j0 = kt * BN;
-        const rsrc_t krs = make_rsrc<2 * D>(kh + (int64_t)j0 * D, p.Sk - j0);
+        const rsrc_t krs = make_rsrc<2 * D>(kh + (int64_t)j0 * D, kt < k_end ? p.Sk - j0 : 0);
         if constexpr (CH == 8) {
             *reinterpret_cast<uint4 *>(sk0) = bload16(krs, 2 * (krow * D + kd0));
             *reinterpret_cast<uint4 *>(sk1) = bload16(krs, 2 * (krow * D + kd1));
@@ -388,11 +423,9 @@ void flash_fwd_pp_kernel(PPParams p)
         stage_write(kt);
     };
     // V tile kt, this team's half of its keys, straight into LDS: blocks of
-    // 1 KB (4 rows of 256 B), VBW per wave.  LDS chunk q of a row holds the
-    // row's 16-byte chunk q ^ 4 (row & 3), so the four keys a transposing read
-    // fetches at once sit in different bank groups.  Tiles past the range load
-    // nothing (zero records) and fill their slot, which is free by then,
-    // with zeros.
+    // 1 KB (RPB rows), VBW per wave, each row's chunks swizzled by vswz.
+    // Tiles past the range load nothing (zero records) and fill their slot,
+    // which is free by then, with zeros.
     const uint32_t lds_byte0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
     auto dma_v = [&](int kt) {
         const int j0 = kt * BN;
@@ -401,9 +434,9 @@ void flash_fwd_pp_kernel(PPParams p)
         const sgpr4_t vrs = rsrc_words(vh + (int64_t)j0 * D, bytes);
 #pragma unroll
         for (int i = 0; i < SH::VBW; ++i) {
-            const int blk = team * (SH::HALF / 4) + wave * SH::VBW + i;   // 1 KB block of the tile
-            const int rr = 4 * blk + (lane >> 4);                         // key row
-            const int cq = (lane & 15) ^ (4 * (rr & 3));
+            const int blk = team * (SH::HALF / SH::RPB) + wave * SH::VBW + i;   // 1 KB block of the tile
+            const int rr = SH::RPB * blk + lane / SH::CPR;                     // key row
+            const int cq = (lane % SH::CPR) ^ vswz<D>(rr);
             const uint32_t dst = lds_byte0 + 2 * (uint32_t)((vslot(kt) - lds) + blk * 512);
             dma16(vrs, 2 * (rr * D + 8 * cq), __builtin_amdgcn_readfirstlane(dst));
         }
@@ -480,17 +513,19 @@ void flash_fwd_pp_kernel(PPParams p)
             for (int i = 0; i < 8; ++i) qf[t][i] = (E)(qv[t][i] * p.sl2);
     }
 
-    // ---- prologue: K(0) staged, this team's half of K(1) and V(0) in
-    // flight.  Every matrix step then issues the same NLOAD vector-memory
-    // loads per wave (its K half, then its V half; past the key range they
-    // read zero records), so the waits below can count them.
-    fetch_k(0);
-    stage_k(0);
-    fetch_k(1);
-    dma_v(0);
+    // ---- prologue: K(k_beg) staged, this team's half of K(k_beg + 1) and
+    // V(k_beg) in flight.  Every matrix step then issues the same number of
+    // vector-memory loads per wave (nload: its V half, then its K half; past
+    // the key range they read zero records), so the waits below can count
+    // them.
+    fetch_k(k_beg);
+    stage_k(k_beg);
+    fetch_k(k_beg + 1);
+    dma_v(k_beg);
     {
-        // the slot of V(-1), which step 0 multiplies by the zero P(-1)
-        uint4 *z = reinterpret_cast<uint4 *>(vslot(-1));
+        // the slot of V(k_beg - 1), which the first step multiplies by the
+        // zero P(k_beg - 1)
+        uint4 *z = reinterpret_cast<uint4 *>(vslot(k_beg - 1));
 #pragma unroll
         for (int i = 0; i < SH::V_ELEMS / 8 / 512; ++i) z[tid + 512 * i] = make_uint4(0, 0, 0, 0);
     }
@@ -512,18 +547,17 @@ void flash_fwd_pp_kernel(PPParams p)
     // V^T operand addressing (ds_read_b64_tr_b16): in each 16-lane group,
     // lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving lane then
     // holds V[key0 .. key0+3][dim0 + its index].  Key k of the tile maps to
-    // row k, whose 16-byte chunk c sits at c ^ 4 (k & 3).  The lane's key is
-    // tr_key + 32 kb + 16 mm (+ 8), all multiples of 4 apart from tr_key, and
-    // its dim tr_dim + 32 bd: chunk (4 bd + c0) ^ 4 x = 4 (bd ^ x) + c0 with
-    // x = tr_key & 3, so a lane needs one base per 32-dim block and the key
-    // steps are immediate offsets.
+    // row k, whose 16-byte chunk c sits at c ^ vswz(k).  The lane's key is
+    // tr_key + 32 kb + 16 mm (+ 8), all multiples of 8 apart from tr_key,
+    // which leave vswz unchanged, so a lane needs one base per 32-dim block
+    // and the key steps are immediate offsets.
     const int g16 = lane >> 4, lp = lane & 15;
     const int tr_key = 4 * (g16 >> 1) + (lp >> 2);
     const int tr_dim = 4 * (lp & 3) + 16 * (g16 & 1);
     int vbase[DB];   // element offsets inside a V slot
 #pragma unroll
     for (int bd = 0; bd < DB; ++bd)
-        vbase[bd] = tr_key * D + 32 * (bd ^ (tr_key & 3)) + 8 * (tr_dim >> 3) + (tr_dim & 7);
+        vbase[bd] = tr_key * D + 8 * ((4 * bd + (tr_dim >> 3)) ^ vswz<D>(tr_key)) + (tr_dim & 7);
     const int kbase = l32 * KP + 8 * hh;   // K operand: row l32, dims 8 hh (+ 32 kb rows, 16 t dims)
 
     // The operand stream of matrix step k: NPV P V operands (V^T of tile k-1,
@@ -652,8 +686,9 @@ void flash_fwd_pp_kernel(PPParams p)
     // reference where needed (rescaling O and l) first.
     float m_lim = PP_LAZY;   // m_ref + PP_LAZY
     auto softmax_step = [&](int k) {
-        if (k >= w_end) {
-            // past this wave's keys: P = 0, so the next P V product adds nothing
+        if (k >= w_stop) {
+            // past this wave's keys or the segment: P = 0, so the next P V
+            // product adds nothing
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -699,37 +734,70 @@ void flash_fwd_pp_kernel(PPParams p)
         for (int u = 0; u < 4; ++u) l_acc[u] += lt[u];
     };
 
-    __syncthreads();   // K(0) staged, the slot of V(-1) zeroed
+    __syncthreads();   // K(k_beg) staged, the slot of V(k_beg - 1) zeroed
 
-    // Both teams run the same sequence, matrix step k, barrier, softmax k,
-    // barrier; team 1 passes one barrier first, so it runs one phase behind:
-    // phase 2k holds team 0's matrix step k and team 1's softmax k-1, phase
-    // 2k+1 team 0's softmax k and team 1's matrix step k.  K(k+1) is staged
-    // in phases 2k (team 0's half) and 2k+1 (team 1's) and first read in
-    // phase 2k+2.  V(k), loaded by the matrix steps k-1, is first read in
-    // phase 2k+2; waiting at the end of matrix step k until at most the
-    // NLOAD loads of that step are outstanding completes V(k) by the end of
-    // phase 2k (team 0) or 2k+1 (team 1).
+    // Ping-pong: both teams run the same sequence, matrix step k, barrier,
+    // softmax k, barrier; team 1 passes one barrier first, so it runs one
+    // phase behind: phase 2k holds team 0's matrix step k and team 1's
+    // softmax k-1, phase 2k+1 team 0's softmax k and team 1's matrix step k.
+    // K(k+1) is staged in phases 2k (team 0's half) and 2k+1 (team 1's) and
+    // first read in phase 2k+2.  V(k), loaded by the matrix steps k-1, is
+    // first read in phase 2k+2; waiting at the end of matrix step k until at
+    // most the loads of that step are outstanding completes V(k) by the
+    // end of phase 2k (team 0) or 2k+1 (team 1).
+    // Together (not PING): every wave runs matrix step k, waits, passes one
+    // barrier, then runs softmax k; the barrier hands over K(k+1) and V(k),
+    // and the reads of K(k) and V(k-1) all precede it, so their slots may be
+    // refilled in step k+1.
     auto wait_older_loads = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(SH::NLOAD | (7 << 4) | (15 << 8));   // vmcnt(NLOAD)
+        __builtin_amdgcn_s_waitcnt(SH::template nload<ROT>() | (7 << 4) | (15 << 8));   // vmcnt(loads of one step)
         __builtin_amdgcn_sched_barrier(0);
     };
-    prefetch_pv(0);
-    if (team == 1) lds_barrier();
-    for (int k = 0; k <= k_end; ++k) {
-        mfma_step(k);
-        wait_older_loads();
-        lds_barrier();
-        prefetch_pv(k + 1);   // V(k): complete since the phase before
-        softmax_step(k);
-        lds_barrier();
+    prefetch_pv(k_beg);
+    if constexpr (PING) {
+        if (team == 1) lds_barrier();
+        for (int k = k_beg; k <= k_end; ++k) {
+            mfma_step(k);
+            wait_older_loads();
+            lds_barrier();
+            prefetch_pv(k + 1);   // V(k): complete since the phase before
+            softmax_step(k);
+            lds_barrier();
+        }
+        if (team == 0) lds_barrier();
+    } else {
+        for (int k = k_beg; k <= k_end; ++k) {
+            mfma_step(k);
+            wait_older_loads();
+            lds_barrier();
+            prefetch_pv(k + 1);   // V(k): complete before the barrier
+            softmax_step(k);
+        }
     }
-    if (team == 0) lds_barrier();
 
-    // ---- epilogue: O / l, one store per element; lse on request ----
     if (!wave_rows || qrow >= p.Sq) return;
     const float l_tot = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
+    if (SPLIT && partial) {
+        // ---- partial state of this segment: unnormalised O, reference m
+        // (-inf when no key of the segment was visible) and row sum l, as
+        // [D + 2][256 rows] fp32 for the merge kernel's coalesced reads
+        const int rr = team * 128 + 32 * wave + l32;
+        float *blk = p.ws + (((int64_t)bh * npair + pr) * p.nseg + seg) * (int64_t)(D + 2) * 256;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) blk[(32 * b + 8 * g + 4 * hh + e) * 256 + rr] = oacc[b][4 * g + e];
+        if (hh == 0) {
+            blk[D * 256 + rr] = m_set ? m_ref : -INFINITY;
+            blk[(D + 1) * 256 + rr] = l_tot;
+        }
+        return;
+    }
+
+    // ---- epilogue: O / l, one store per element; lse on request ----
     const float inv = 1.f / l_tot;
     uint16_t *orow = p.o + ((int64_t)bh * p.Sq + qrow) * D;
 #pragma unroll
@@ -745,18 +813,96 @@ void flash_fwd_pp_kernel(PPParams p)
     if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = ((m_set ? m_ref : -INFINITY) + log2f(l_tot)) * PP_LN2;
 }
 
-template <int LAYOUT, bool ROT, bool FULL, typename E>
-int launch(const FlashArgs &a, hipStream_t stream)
+// Merges the segments of every cut pair: one workgroup per (batch*head,
+// pair, 8-dim chunk of the output), one thread per query row.  With M the
+// largest reference of the row's segments,
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, which is exact in real
+// arithmetic (each segment's O_s and l_s are measured against its own
+// reference m_s).  All loads of a thread are independent and issued
+// together (at most PP_MAXSEG segments).  Runs after the main kernel on the
+// same stream.
+template <int D, int BN, typename E>
+__global__ __launch_bounds__(256) void flash_pp_merge_kernel(PPParams p)
+{
+    using TT = Ty<E>;
+    constexpr int NC = D / 8;
+    const int bh = blockIdx.x % p.BH;
+    const int npair = (p.n_qt + 1) / 2;
+    const int pr = (blockIdx.x / p.BH) / NC;
+    const int c8 = 8 * ((blockIdx.x / p.BH) % NC);
+    const int k_all = pair_tiles<BN>(p, pr);
+    if (k_all <= p.seg_tiles) return;   // written by the main kernel
+    const int ns = (k_all + p.seg_tiles - 1) / p.seg_tiles;
+    const int t = threadIdx.x;
+    const int qrow = (t < 128 ? 2 * pr : 2 * pr + 1) * 128 + (t & 127);
+    if (qrow >= p.Sq) return;
+    const float *blk0 = p.ws + ((int64_t)bh * npair + pr) * p.nseg * (int64_t)(D + 2) * 256 + t;
+    const int64_t sstride = (int64_t)(D + 2) * 256;
+    float m[PP_MAXSEG], l[PP_MAXSEG], o[PP_MAXSEG][8];
+#pragma unroll
+    for (int sg = 0; sg < PP_MAXSEG; ++sg) {
+        m[sg] = -INFINITY;
+        l[sg] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[sg][e] = 0.f;
+        if (sg < ns) {
+            const float *b = blk0 + sg * sstride;
+            m[sg] = b[D * 256];
+            l[sg] = b[(D + 1) * 256];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[sg][e] = b[(c8 + e) * 256];
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sg = 0; sg < PP_MAXSEG; ++sg) M = fmaxf(M, m[sg]);
+    float lsum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sg = 0; sg < PP_MAXSEG; ++sg) {
+        // segments without a visible key (m = -inf, l = 0, O = 0) add nothing
+        const float w = m[sg] > -INFINITY ? __builtin_amdgcn_exp2f(m[sg] - M) : 0.f;
+        lsum += w * l[sg];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * o[sg][e];
+    }
+    const float inv = 1.f / lsum;
+    uint4 wv;
+    wv.x = TT::pack2(acc[0] * inv, acc[1] * inv);
+    wv.y = TT::pack2(acc[2] * inv, acc[3] * inv);
+    wv.z = TT::pack2(acc[4] * inv, acc[5] * inv);
+    wv.w = TT::pack2(acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<uint4 *>(p.o + ((int64_t)bh * p.Sq + qrow) * D + c8) = wv;
+    if (p.lse && c8 == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (M + log2f(lsum)) * PP_LN2;
+}
+
+#ifndef ROPE_PP_PING64
+#define ROPE_PP_PING64 1
+#endif
+// Schedule per head dim: ping-pong (true) or together.
+template <int D> constexpr bool pp_ping() { return D == 128 ? true : (ROPE_PP_PING64 != 0); }
+
+// Host half: kernel parameters, and the split plan (seg_tiles = 0: none).
+// Pairs of 128-row query tiles see k_all(pr) key tiles; when the pairs are
+// fewer than the CUs, the smallest segment length C is chosen whose segment
+// count, sum over pairs of ceil(k_all / C), still fits one workgroup per CU.
+struct PPPlan {
+    PPParams p;
+    int64_t ws_bytes;   // workspace the split needs (0: no split)
+};
+
+template <int D>
+PPPlan pp_plan(const FlashArgs &a)
 {
     constexpr int BN = ROPE_PP_BN;
-    PPParams p;
+    PPPlan pl;
+    PPParams &p = pl.p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
     p.v = static_cast<const uint16_t *>(a.v);
     p.o = static_cast<uint16_t *>(a.o);
     p.lse = a.lse;
     p.BH = a.B * a.H;
-    p.kv_group = a.H / a.H_kv;
+    p.kv_group = a.H_kv > 0 ? a.H / a.H_kv : 1;
     p.Sq = (int)a.Sq;
     p.Sk = (int)a.Sk;
     p.q_off = a.q_off;
@@ -769,28 +915,97 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.causal = a.causal;
     p.n_qt = (int)((a.Sq + 127) / 128);
     p.n_kt = (int)((a.Sk + BN - 1) / BN);
-    const int64_t blocks = (int64_t)p.BH * ((p.n_qt + 1) / 2);
-    if (!rope_grid_fits(blocks, 512)) return ROPE_LAUNCH_SHAPE;
-    hipLaunchKernelGGL((flash_fwd_pp_kernel<BN, LAYOUT, ROT, FULL, E>), dim3((unsigned)blocks), dim3(512), 0, stream,
-                       p);
-    return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
+    p.seg_tiles = 0;
+    p.nseg = 1;
+    p.ws = nullptr;
+    pl.ws_bytes = 0;
+    const int npair = (p.n_qt + 1) / 2;
+    const int cus = rope_device_cu_count();
+    const int64_t pairs = (int64_t)p.BH * npair;
+    if (cus <= 0 || pairs >= cus) return pl;
+    auto k_all = [&](int pr) {
+        const int tB = 2 * pr + 1 < p.n_qt ? 2 * pr + 1 : 2 * pr;
+        const int64_t last = tB * 128 + 127 < a.Sq ? tB * 128 + 127 : a.Sq - 1;
+        if (!a.causal) return p.n_kt;
+        const int64_t v = (a.q_off + last - a.k_off) / BN + 1;
+        return (int)(v < p.n_kt ? v : p.n_kt);
+    };
+    int kmax = 0;
+    for (int pr = 0; pr < npair; ++pr) kmax = k_all(pr) > kmax ? k_all(pr) : kmax;
+    int C = kmax;
+    for (int c = (kmax + PP_MAXSEG - 1) / PP_MAXSEG; c < kmax; ++c) {
+        int64_t n = 0;
+        for (int pr = 0; pr < npair; ++pr) n += (k_all(pr) + c - 1) / c;
+        if (n * p.BH <= cus) {
+            C = c;
+            break;
+        }
+    }
+    if (C >= kmax) return pl;
+    p.seg_tiles = C;
+    p.nseg = (kmax + C - 1) / C;
+    pl.ws_bytes = pairs * p.nseg * (int64_t)(D + 2) * 256 * 4;
+    return pl;
 }
 
-template <typename E>
-int launch_e(const FlashArgs &a, hipStream_t stream)
+template <int D, bool SPLIT, int LAYOUT, bool ROT, bool FULL, typename E>
+int launch(const PPParams &p, hipStream_t stream)
 {
-    if (a.rot_dim == 0) return launch<1, false, false, E>(a, stream);
-    const bool full = a.rot_dim == PP_D;
-    if (a.layout == 0) return full ? launch<0, true, true, E>(a, stream) : launch<0, true, false, E>(a, stream);
-    return full ? launch<1, true, true, E>(a, stream) : launch<1, true, false, E>(a, stream);
+    constexpr int BN = ROPE_PP_BN;
+    const int npair = (p.n_qt + 1) / 2;
+    const int64_t blocks = (int64_t)p.BH * npair * (SPLIT ? p.nseg : 1);
+    if (!rope_grid_fits(blocks, 512) || !rope_grid_fits((int64_t)p.BH * npair * (D / 8), 256))
+        return ROPE_LAUNCH_SHAPE;
+    hipLaunchKernelGGL((flash_fwd_pp_kernel<D, BN, pp_ping<D>(), SPLIT, LAYOUT, ROT, FULL, E>), dim3((unsigned)blocks),
+                       dim3(512), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
+    if (SPLIT) {
+        hipLaunchKernelGGL((flash_pp_merge_kernel<D, BN, E>), dim3((unsigned)((int64_t)p.BH * npair * (D / 8))),
+                           dim3(256), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
+    }
+    return ROPE_LAUNCH_OK;
+}
+
+template <int D, bool SPLIT, typename E>
+int launch_r(const PPParams &p, int layout, hipStream_t stream)
+{
+    if (p.rot_dim == 0) return launch<D, SPLIT, 1, false, false, E>(p, stream);
+    const bool full = p.rot_dim == D;
+    if (layout == 0)
+        return full ? launch<D, SPLIT, 0, true, true, E>(p, stream) : launch<D, SPLIT, 0, true, false, E>(p, stream);
+    return full ? launch<D, SPLIT, 1, true, true, E>(p, stream) : launch<D, SPLIT, 1, true, false, E>(p, stream);
+}
+
+template <int D, typename E>
+int launch_d(const FlashArgs &a, hipStream_t stream)
+{
+    PPPlan pl = pp_plan<D>(a);
+    const bool split = pl.ws_bytes > 0 && a.workspace != nullptr && a.workspace_bytes >= pl.ws_bytes;
+    if (split) {
+        pl.p.ws = static_cast<float *>(a.workspace);
+        return launch_r<D, true, E>(pl.p, a.layout, stream);
+    }
+    pl.p.seg_tiles = 0;
+    pl.p.nseg = 1;
+    return launch_r<D, false, E>(pl.p, a.layout, stream);
 }
 
 }  // namespace
 
-// Head dim 128, 16-bit storage: the ping-pong kernel.  Returns -1 (nothing
-// launched) for shapes it does not take.
+// Head dim 128, 16-bit storage.  Returns -1 (nothing launched) for shapes
+// it does not take.  (The kernel also compiles for head dim 64, where it
+// measured slower than the row-split kernel of flash_fwd_bf16.hip on the
+// causal 1x8xSx64 shapes: with the softmax twice the matrix work per tile,
+// neither schedule hides it.)
 int rope_launch_flash_pp(const FlashArgs &a, hipStream_t stream)
 {
-    if (a.head_dim != PP_D || (a.dtype != 0 && a.dtype != 2)) return -1;
-    return a.dtype == 2 ? launch_e<_Float16>(a, stream) : launch_e<__bf16>(a, stream);
+    if (a.head_dim != 128 || (a.dtype != 0 && a.dtype != 2)) return -1;
+    return a.dtype == 2 ? launch_d<128, _Float16>(a, stream) : launch_d<128, __bf16>(a, stream);
+}
+
+int64_t rope_flash_pp_workspace_bytes(const FlashArgs &a)
+{
+    if (a.head_dim != 128 || (a.dtype != 0 && a.dtype != 2)) return 0;
+    return pp_plan<128>(a).ws_bytes;
 }
