@@ -79,8 +79,6 @@ def parse_args():
                     help="restrict the timed kernels (for profiler runs): 'fused' times only "
                          "--workload; 'copy' runs only a plain 256 MiB device copy, the "
                          "calibration for HBM byte counters")
-    ap.add_argument("--balance", action="store_true",
-                    help="pass a workspace: balanced (split query tile) schedule")
     return ap.parse_args()
 
 
@@ -143,14 +141,14 @@ def _tdt(torch, dtype):
     return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
-def bench_fused(torch, api, wl, w, steps, warmup, balance=False):
+def bench_fused(torch, api, wl, w, steps, warmup):
     dev = torch.device("cuda:0")
     arrays = wl.attention_inputs(w)
     q, k, v = (torch.from_numpy(a).to(_tdt(torch, w.dtype)).to(dev) for a in arrays)
     cos, sin = api.tables_build(w.base, w.rot, w.table_rows, device=dev)
     out = torch.empty_like(q)
     launch = api.prepare_flash_attn_fwd(q, k, v, out, cos, sin, w.q_off, w.k_off, w.rot, w.layout,
-                                        w.causal, workspace="auto" if balance else None)
+                                        w.causal)   # the library's default (cached) workspace
     stream = torch.cuda.current_stream(dev)
     ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
     return dict(arrays=arrays, q=q, k=k, v=v, cos=cos, sin=sin, out=out, ms_step=ms_step,
@@ -525,7 +523,7 @@ def main():
                          "accumulate": "fp32", "device": torch.cuda.get_device_name(0)}}
 
     if args.only in ("all", "fused"):
-        r = bench_fused(torch, api, wl, w, args.steps, args.warmup, balance=args.balance)
+        r = bench_fused(torch, api, wl, w, args.steps, args.warmup)
         flops = w.flops()
         value = flops / (r["ms_step"] * 1e-3) / 1e12
         achieved = flops / (r["kernel_ms"] * 1e-3) / 1e12

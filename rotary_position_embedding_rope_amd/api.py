@@ -113,7 +113,7 @@ _WORKSPACES: dict = {}
 
 def workspace_for(q: torch.Tensor, Sk: int, q_pos_offset: int, k_pos_offset: int,
                   causal: bool) -> torch.Tensor | None:
-    """Workspace for the balanced schedule of this forward, cached per device
+    """Workspace for the split-key schedule of this forward, cached per device
     and grown on demand (None when the library would use none).  Calls
     sharing it must be serialised, which holds on one stream."""
     lib = _lib.load()
@@ -136,7 +136,7 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,
                    q_pos_offset: int = 0, k_pos_offset: int = 0, rot_dim: int | None = None,
                    layout="neox", causal: bool = True, softmax_scale: float = 0.0,
-                   out: torch.Tensor | None = None, workspace=None,
+                   out: torch.Tensor | None = None, workspace="auto",
                    lse: torch.Tensor | None = None) -> torch.Tensor:
     """Fused RoPE + attention forward: ``q`` ``[B, H, Sq, D]``, ``k`` and
     ``v`` ``[B, H_kv, Sk, D]`` with H_kv dividing H (query head h reads
@@ -145,10 +145,11 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     row statistics flash_attn_bwd needs).
 
     ``rot_dim=0`` (or no tables) runs plain attention.  Returns ``out``
-    (allocated like ``q`` when not given).  ``workspace``: None (one
-    workgroup per query tile, the default), "auto" (the balanced schedule
-    with a cached buffer sized by the library) or a uint8 tensor of at least
-    the library's requested size."""
+    (allocated like ``q`` when not given).  ``workspace``: "auto" (the
+    default: a per-device cached buffer of the size the library asks for,
+    none when it asks for none; head dim 128 with fewer query-tile pairs than
+    CUs then splits the key range across workgroups), None (never split) or
+    a uint8 tensor of at least the library's requested size."""
     lib = _lib.load()
     _require_cuda(q, k, v, cos, sin)
     for t in (q, k, v):
@@ -191,7 +192,7 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 def prepare_flash_attn_fwd(q, k, v, out, cos=None, sin=None, q_pos_offset: int = 0,
                            k_pos_offset: int = 0, rot_dim: int | None = None, layout="neox",
-                           causal: bool = True, softmax_scale: float = 0.0, workspace=None,
+                           causal: bool = True, softmax_scale: float = 0.0, workspace="auto",
                            lse=None):
     """Validate once and return a zero-argument callable that enqueues the
     fused forward on fixed buffers (for repeated launches in timing loops;

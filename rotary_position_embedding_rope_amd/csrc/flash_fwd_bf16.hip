@@ -72,7 +72,6 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 constexpr int WAVES_PER_GROUP = 4;
 constexpr int BM = 32 * WAVES_PER_GROUP;   // queries per workgroup
 constexpr int KPAD = 8;                     // K LDS row pitch = D + 8 bf16
-constexpr int VP = 160;                     // V LDS row pitch (bf16): 80 dwords, == 16 mod 64 banks
 constexpr float LAZY_THRESHOLD = 8.0f;      // log2 headroom before the reference max is raised
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -91,31 +90,10 @@ struct Params {
     int64_t n_qtiles;
     int64_t n_half;     // 64-row halves of the query range
     int64_t n_kt;       // key tiles
-    // Key tiles visited by query tile t: causal and t < n_qtiles - 1:
-    // min(n_kt, va * t + vb); the last query tile: v_last; non-causal: n_kt.
-    int64_t va, vb, v_last;
     int tile_n;         // keys per tile
-    // Balanced schedule (sk_G > 0): the BH * u_head (query tile, key tile)
-    // visits are cut into sk_G equal contiguous shares, one per workgroup.
-    int sk_G;
-    int64_t u_head;     // visits per (batch, head)
-    // xcd_order: heads are laid out XCD by XCD in the visit order (head
-    // slot hs = (bh % 8) * (BH / 8) + bh / 8) and block b takes share
-    // (b % 8) * (sk_G / 8) + b / 8, so blocks that the dispatcher sends to one
-    // XCD (b mod 8) work on that XCD's heads and their K/V share one L2.
-    int xcd_order;
-    float *ws_part;     // partial states: [sk_G][2 slots][4 waves][NC][64 lanes]
 };
 
 // ---- schedule arithmetic (host and device) ----
-
-__host__ __device__ inline int64_t tile_visits(const Params &p, int64_t t)
-{
-    if (!p.causal) return p.n_kt;
-    if (t == p.n_qtiles - 1) return p.v_last;
-    const int64_t v = p.va * t + p.vb;
-    return v < p.n_kt ? v : p.n_kt;
-}
 
 // Key tiles seen by query rows up to `last` (all key tiles when not causal).
 __host__ __device__ inline int64_t row_visits(const Params &p, int64_t last)
@@ -123,57 +101,6 @@ __host__ __device__ inline int64_t row_visits(const Params &p, int64_t last)
     if (!p.causal) return p.n_kt;
     const int64_t v = (p.q_off + last - p.k_off) / p.tile_n + 1;
     return v < p.n_kt ? v : p.n_kt;
-}
-
-// Sum of tile_visits(t) over t < T, in closed form (T <= n_qtiles).
-__host__ __device__ inline int64_t visits_before(const Params &p, int64_t T)
-{
-    if (!p.causal) return T * p.n_kt;
-    const int64_t tf = T < p.n_qtiles - 1 ? T : p.n_qtiles - 1;   // tiles on the linear law
-    const int64_t ts = p.n_kt <= p.vb ? 0 : (p.n_kt - p.vb + p.va - 1) / p.va;  // first saturated tile
-    const int64_t m = tf < ts ? tf : ts;
-    int64_t s = p.va * m * (m - 1) / 2 + p.vb * m + (tf - m) * p.n_kt;
-    if (T == p.n_qtiles) s += p.v_last;
-    return s;
-}
-
-// Largest query tile T with visits_before(T) <= r (r < u_head).
-__device__ inline int64_t find_tile(const Params &p, int64_t r)
-{
-    int64_t lo = 0, hi = p.n_qtiles - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) / 2;
-        if (visits_before(p, mid) <= r) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-__device__ inline int64_t share_start(int64_t w, int64_t U, int G) { return (w * U) / G; }
-
-__device__ inline int head_of_slot(const Params &p, int64_t hs)
-{
-    if (!p.xcd_order) return (int)hs;
-    const int per = p.BH / 8;
-    return (int)((hs % per) * 8 + hs / per);
-}
-__device__ inline int64_t slot_of_head(const Params &p, int bh)
-{
-    if (!p.xcd_order) return bh;
-    return (int64_t)(bh % 8) * (p.BH / 8) + bh / 8;
-}
-__device__ inline int64_t share_of_block(const Params &p, int64_t b)
-{
-    if (!p.xcd_order) return b;
-    return (b % 8) * (p.sk_G / 8) + b / 8;
-}
-
-// The workgroup whose share contains visit x.
-__device__ inline int64_t share_of(int64_t x, int64_t U, int G)
-{
-    int64_t w = (x * G) / U;   // share_start(w) <= x
-    while (w + 1 < G && share_start(w + 1, U, G) <= x) ++w;
-    return w;
 }
 
 using rope::Ty;
@@ -261,11 +188,6 @@ __device__ __forceinline__ float4 bload16f(rsrc_t r, int byte_off)
 {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
-__device__ __forceinline__ uint4 bload8(rsrc_t r, int byte_off)
-{
-    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
-    return make_uint4(v.x, v.y, 0, 0);
-}
 
 // Per-thread staging plan for K tiles (fixed across tiles).  A slot is two
 // 8-dim chunks of one key row, D/16 slots per row:
@@ -285,10 +207,6 @@ struct KPlan {
 struct KItem {
     int row, mode, o0, o1, to;
 };
-struct VItem {
-    int o, l;
-    bool ok;
-};
 
 // Row sums of one tile's probabilities (this lane's keys) up to this bound
 // are taken without looking at the row max: every probability is then at
@@ -297,43 +215,28 @@ struct VItem {
 // exact path (true row max, lazy rescale).
 constexpr float FAST_SUM_LIMIT = 8192.0f;
 
-// D: head dim; BN: keys per tile (32 or 64); NG: groups of 4 waves per
-// workgroup; FULL: rot_dim == D (every K slot rotates); BAL: the balanced
-// schedule (a separate instantiation, so the default kernel does not carry
-// its share-walking code); RS (row split, NG = 2): the two groups take two
-// different 128-row query tiles and consume the same key tiles, so each
-// staged tile serves 256 rows; otherwise the groups take the same rows and
-// alternate key tiles.
-template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, bool BAL, bool RS, typename E>
+// D: head dim (64); BN: keys per tile (64); NG: groups of 4 waves per
+// workgroup (2): the groups take the same rows and alternate key tiles;
+// FULL: rot_dim == D (every K slot rotates).
+template <int D, int LAYOUT, bool ROT, bool FULL, int NG, int BN, typename E>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_bf16_kernel(Params p)
 {
     using TT = Ty<E>;
     using v8 = typename TT::v8;
-    static_assert(!RS || (NG == 2 && !BAL), "row split: two groups, default schedule");
+    static_assert(D == 64 && NG == 2 && BN == 64, "built for head dim 64, two key groups, 64-key tiles");
     using Plan = KPlan<D, LAYOUT, ROT, BN>;
     constexpr int NKB = BN / 32;                    // 32-key blocks per tile
     constexpr int KP = D + KPAD;                    // K LDS row pitch
-    // D = 64 with a key split: value tiles go from HBM straight into LDS
-    // (buffer loads with the LDS bit), unpadded and swizzled (dma_v); else
-    // through registers into rows of pitch VP
-    constexpr bool VDMA = D == 64 && !RS;
-    constexpr int K_ELEMS = BN * KP, V_ELEMS = VDMA ? BN * D : BN * VP;
-    // staging threads per tile: a group, or (row split) the workgroup, whose
-    // threads then take half slots (8 dims: NeoX 4 + 4 partner dims)
-    constexpr int NST = RS ? 512 : 256;
-    constexpr int KUNITS = RS ? 2 * Plan::SLOTS : Plan::SLOTS;   // K staging units per tile
-    constexpr int KI = (KUNITS + NST - 1) / NST;    // K units per thread per tile
-    constexpr int VSLOTS = BN * (D / 8);            // V 16-byte chunks per tile
-    constexpr int VI = VDMA ? 1 : (VSLOTS + NST - 1) / NST;   // per thread (the last may be empty; unused with VDMA)
+    // value tiles go from HBM straight into LDS (buffer loads with the LDS
+    // bit), unpadded and swizzled (dma_v)
+    constexpr int K_ELEMS = BN * KP, V_ELEMS = BN * D;
+    constexpr int NST = 256;                        // staging threads per tile: a group
+    constexpr int KI = (Plan::SLOTS + NST - 1) / NST;   // K slots per thread per tile
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
     constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
-    // the light half's waves stage the heavy half's exclusive tiles alone
-    // (two key groups only: with one group at D = 128 there are no spare
-    // registers for the deeper loads)
-    constexpr bool OFFLOAD = NG == 2 && !BAL && !RS;
-    constexpr int NBUF = RS ? 1 : NG;               // buffer sets (one per key stream)
+    constexpr int NBUF = NG;                        // buffer sets (one per key stream)
     constexpr int NVB = 2;                          // V buffers per set
 
     // [stream][buffer] K tiles, then [stream][buffer] V tiles.  K runs one
@@ -350,7 +253,7 @@ void flash_fwd_bf16_kernel(Params p)
     const int wave = __builtin_amdgcn_readfirstlane(gtid >> 6);   // wave inside the group
     const int l32 = lane & 31, hh = lane >> 5;
     const int rh = p.rot_dim / 2;   // table row stride
-    const int stream = RS ? 0 : group;
+    const int stream = group;
     auto kbuf = [&](int b) { return lds + (stream * 2 + b) * K_ELEMS; };
     auto vbuf = [&](int b) { return lds + NBUF * 2 * K_ELEMS + (stream * NVB + b) * V_ELEMS; };
     auto vslot = [&](int j) { return j & 1; };   // V buffer of tile T(j)
@@ -362,38 +265,6 @@ void flash_fwd_bf16_kernel(Params p)
     // tile's block of table rows.  A V item is one 16-byte chunk.
     auto k_item = [&](int item) {
         KItem it;
-        if constexpr (RS) {
-            // half slot: two 4-dim chunks (NeoX: dims 4h and their partners
-            // 4h + rot/2; GPT-J: 8 consecutive dims, 4 whole pairs; past
-            // rot_dim: 8 consecutive dims, copied) and 4 cos/sin values
-            constexpr int HPR = D / 8;   // half slots per row
-            const int row = item / HPR, h = item % HPR;
-            int d0, d1;
-            it.row = row;
-            if (item >= KUNITS) {
-                it.mode = -1;
-                d0 = d1 = 0;
-            } else if constexpr (Plan::NEOX_SLOT) {
-                const int rhs = p.rot_dim / 8;   // rotated half slots per row
-                if (h < rhs) {
-                    it.mode = 1;
-                    d0 = 4 * h;
-                    d1 = d0 + rh;
-                } else {
-                    it.mode = 0;
-                    d0 = p.rot_dim + 8 * (h - rhs);
-                    d1 = d0 + 4;
-                }
-            } else {
-                it.mode = (ROT && 8 * h < p.rot_dim) ? 2 : 0;
-                d0 = 8 * h;
-                d1 = d0 + 4;
-            }
-            it.o0 = row * D + d0;
-            it.o1 = row * D + d1;
-            it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
-            return it;
-        }
         int row = item / Plan::SLOTS_PER_ROW;
         int slot = item % Plan::SLOTS_PER_ROW;
         if constexpr (D == 64) {
@@ -435,25 +306,10 @@ void flash_fwd_bf16_kernel(Params p)
         it.to = row * rh + (LAYOUT == 0 ? d0 : d0 / 2);
         return it;
     };
-    auto v_item = [&](int item) {
-        VItem it;
-        int row = item / (D / 8);
-        // D = 64: the two rows of one 16-lane write pass are r and r + 2
-        // (pitch 80 dwords: 32 banks apart), not r and r + 1
-        if constexpr (D == 64) row = (row & ~3) | ((row & 1) << 1) | ((row >> 1) & 1);
-        it.ok = item < VSLOTS;
-        it.o = row * D + 8 * (item % (D / 8));     // element offset inside the tile
-        it.l = row * VP + 8 * (item % (D / 8));    // LDS offset
-        return it;
-    };
     // Plan A: the threads of a key stream share the staging of a tile.
-    const int stid = RS ? tid : gtid;
     KItem kpa[KI];
-    VItem vpa[VI];
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kpa[i] = k_item(stid + NST * i);
-#pragma unroll
-    for (int i = 0; i < VI; ++i) vpa[i] = v_item(stid + NST * i);
+    for (int i = 0; i < KI; ++i) kpa[i] = k_item(gtid + NST * i);
 
     // V^T operand addressing for ds_read_b64_tr_b16: in each 16-lane group
     // the source lane 4j + b points at V[key0 + j][dim0 + 4b]; the receiving
@@ -461,7 +317,7 @@ void flash_fwd_bf16_kernel(Params p)
     const int g16 = lane >> 4, lp = lane & 15;
     const int tr_row = lp >> 2, tr_col = 4 * (lp & 3) + 16 * (g16 & 1);
     const int tr_key = 4 * (g16 >> 1) + tr_row;   // + 32kb + 16mm (+ 8)
-    // VDMA layout: column offset of dims 32 bd + tr_col in a key row whose
+    // V layout: column offset of dims 32 bd + tr_col in a key row whose
     // chunks are swizzled by 4 ((key >> 1) & 1) (the key's low bits are tr_row)
     int vcol[D / 32];
 #pragma unroll
@@ -470,21 +326,13 @@ void flash_fwd_bf16_kernel(Params p)
 
     // One segment: key tiles [kb, ke) of the 128 query rows made of two
     // 64-row halves starting at rowA and rowB (rowB >= Sq: no second half)
-    // of head `bh`.  `full` when the segment covers every key tile those rows
-    // see; otherwise (balanced schedule, rowB = rowA + 64) its state is merged
-    // with the other segments of that query tile through the workspace
-    // (seg_v: global index of its first visit, w: this workgroup's share).
+    // of head `bh`, every key tile those rows see.
     // Wave w of group 0 takes half (w >> 1) & 1, rows 32 (w & 1) of it; group
     // 1 takes the other half on each SIMD, so a SIMD's two waves work on
     // different halves.
-    auto segment = [&](int bh, int64_t rowA, int64_t rowB, int64_t kb, int64_t ke, bool full,
-                       int64_t seg_v, int64_t w) {
-        // key split: wave w of group 0 takes half (w >> 1) & 1, rows 32 (w &
-        // 1) of it, group 1 the other half on each SIMD; row split: group g
-        // takes the 128 rows at rowA / rowB, wave w rows 32 w of them
-        const int half = RS ? group : ((wave >> 1) ^ (NG == 2 ? group : 0)) & 1;
-        const int64_t wq0 = RS ? (group ? rowB : rowA) + 32 * wave
-                               : (half ? rowB : rowA) + 32 * (wave & 1);   // first row of this wave
+    auto segment = [&](int bh, int64_t rowA, int64_t rowB, int64_t kb, int64_t ke) {
+        const int half = ((wave >> 1) ^ group) & 1;
+        const int64_t wq0 = (half ? rowB : rowA) + 32 * (wave & 1);   // first row of this wave
         const uint16_t *qh = p.q + (int64_t)bh * p.Sq * D;
         // (b H + h) / G = b H_kv + h / G: the key/value head of query head h
         const uint16_t *kh = p.k + (int64_t)(bh / p.kv_group) * p.Sk * D;
@@ -500,9 +348,9 @@ void flash_fwd_bf16_kernel(Params p)
         // Group g takes tiles kb + g, kb + g + NG, ...: iteration j of the
         // group handles tile T(j) = kb + j NG + g, whose K sits in K buffer
         // j & 1 and whose V sits in V buffer j & 1.
-        constexpr int TS = RS ? 1 : NG;   // tile stride of a key stream
+        constexpr int TS = NG;   // tile stride of a key stream
         const int n_iter = (int)((ke - kb + TS - 1) / TS);
-        const int t0 = (int)kb + (RS ? 0 : group);
+        const int t0 = (int)kb + group;
         const int tend = (int)ke;
         auto T = [&](int j) { return t0 + j * TS; };
 
@@ -517,13 +365,8 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 if (ki[i].mode < 0) continue;
-                if constexpr (RS) {   // two 4-dim chunks
-                    r0[i] = bload8(krs, 2 * ki[i].o0);
-                    r1[i] = bload8(krs, 2 * ki[i].o1);
-                } else {
-                    r0[i] = bload16(krs, 2 * ki[i].o0);
-                    r1[i] = bload16(krs, 2 * ki[i].o1);
-                }
+                r0[i] = bload16(krs, 2 * ki[i].o0);
+                r1[i] = bload16(krs, 2 * ki[i].o1);
             }
             if constexpr (ROT) {
                 // table rows are rot_dim/2 floats; descriptors count 16-byte
@@ -538,22 +381,12 @@ void flash_fwd_bf16_kernel(Params p)
                     const int to = 4 * ki[i].to;
                     *reinterpret_cast<float4 *>(c[i]) = bload16f(crs, to);
                     *reinterpret_cast<float4 *>(s[i]) = bload16f(srs, to);
-                    if constexpr (!RS) {
-                        *reinterpret_cast<float4 *>(c[i] + 4) = bload16f(crs, to + 16);
-                        *reinterpret_cast<float4 *>(s[i] + 4) = bload16f(srs, to + 16);
-                    }
+                    *reinterpret_cast<float4 *>(c[i] + 4) = bload16f(crs, to + 16);
+                    *reinterpret_cast<float4 *>(s[i] + 4) = bload16f(srs, to + 16);
                 }
             }
         };
-        auto fetch_v = [&](int kt, const auto &vi, auto &vr) {
-            constexpr int N = sizeof(vi) / sizeof(vi[0]);
-            const int j0 = kt * BN;
-            const rsrc_t vrs = make_rsrc<2 * D>(vh + (int64_t)j0 * D, sk32 - j0);
-#pragma unroll
-            for (int i = 0; i < N; ++i)
-                if (vi[i].ok) vr[i] = bload16(vrs, 2 * vi[i].o);
-        };
-        // VDMA: blocks [blk0, blk0 + NBLK) of value tile kt straight into V
+        // Blocks [blk0, blk0 + NBLK) of value tile kt straight into V
         // buffer b.  A block is 8 rows = 1 KB of LDS, written by one buffer
         // load of the wave: lane q (LDS bytes 16q .. 16q+15 of the block)
         // takes row q/8 of the block and 16-byte chunk (q%8) ^ 4((q/16)&1)
@@ -588,48 +421,6 @@ void flash_fwd_bf16_kernel(Params p)
                 // LDS rows have pitch KP; the chunk offsets inside a row are
                 // o - row * D.
                 uint16_t *row = kdst + ki[i].row * (KP - D);
-                if constexpr (RS) {
-                    // half slot: 4-dim chunks (NeoX lo / partner hi, or the
-                    // two pairs of pairs of a GPT-J half slot)
-                    uint2 w0 = make_uint2(r0[i].x, r0[i].y), w1 = make_uint2(r1[i].x, r1[i].y);
-                    if constexpr (ROT) {
-                        float a[4], b[4], cc[4], ss[4];
-                        const uint32_t u0[2] = {r0[i].x, r0[i].y}, u1[2] = {r1[i].x, r1[i].y};
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            if constexpr (LAYOUT == 0) {
-                                a[2 * u] = TT::lo(u0[u]); a[2 * u + 1] = TT::hi(u0[u]);
-                                b[2 * u] = TT::lo(u1[u]); b[2 * u + 1] = TT::hi(u1[u]);
-                            } else {   // pairs (lo, hi) of each dword
-                                a[u] = TT::lo(u0[u]); b[u] = TT::hi(u0[u]);
-                                a[2 + u] = TT::lo(u1[u]); b[2 + u] = TT::hi(u1[u]);
-                            }
-                        }
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) { cc[u] = c[i][u]; ss[u] = s[i][u]; }
-                        rotate_pairs<4>(a, b, cc, ss);
-                        uint2 x0, x1;
-                        if constexpr (LAYOUT == 0) {
-                            x0 = make_uint2(TT::pack2(a[0], a[1]), TT::pack2(a[2], a[3]));
-                            x1 = make_uint2(TT::pack2(b[0], b[1]), TT::pack2(b[2], b[3]));
-                        } else {
-                            x0 = make_uint2(TT::pack2(a[0], b[0]), TT::pack2(a[1], b[1]));
-                            x1 = make_uint2(TT::pack2(a[2], b[2]), TT::pack2(a[3], b[3]));
-                        }
-                        if constexpr (FULL) {
-                            w0 = x0;
-                            w1 = x1;
-                        } else {
-                            // half slots past rot_dim keep their input bits
-                            const bool rot_slot = ki[i].mode != 0;
-                            w0 = rot_slot ? x0 : w0;
-                            w1 = rot_slot ? x1 : w1;
-                        }
-                    }
-                    *reinterpret_cast<uint2 *>(row + ki[i].o0) = w0;
-                    *reinterpret_cast<uint2 *>(row + ki[i].o1) = w1;
-                    continue;
-                }
                 uint4 w0 = r0[i], w1 = r1[i];
                 // slots past rot_dim rotate by angle 0 (cos 1, sin 0), which
                 // gives back their input values
@@ -671,18 +462,10 @@ void flash_fwd_bf16_kernel(Params p)
                 *reinterpret_cast<uint4 *>(row + ki[i].o1) = w1;
             }
         };
-        auto stage_v = [&](int b, const auto &vi, const auto &vr) {
-            constexpr int N = sizeof(vi) / sizeof(vi[0]);
-            uint16_t *vdst = vbuf(b);
-#pragma unroll
-            for (int i = 0; i < N; ++i)
-                if (vi[i].ok) *reinterpret_cast<uint4 *>(vdst + vi[i].l) = vr[i];
-        };
 
-        // Plan A registers: one K tile and one V tile of this group in flight.
+        // Plan A registers: one K tile of this group in flight.
         uint4 kr0[KI], kr1[KI];
         float kc[KI][8], ks[KI][8];
-        uint4 vr[VI];
         // The first two key tiles, the query rows and their table rows are
         // all requested before any of them is used, so their latencies
         // overlap (rows past Sq, or past the table, read as zeros).
@@ -692,8 +475,7 @@ void flash_fwd_bf16_kernel(Params p)
             float pc[KI][8], ps[KI][8];
             if (T(0) < tend) {
                 fetch_k(T(0), kpa, kr0, kr1, kc, ks);
-                if constexpr (VDMA) dma_v(T(0), 0, 2 * wave, std::integral_constant<int, 2>{});
-                else fetch_v(T(0), vpa, vr);
+                dma_v(T(0), 0, 2 * wave, std::integral_constant<int, 2>{});
             }
             if (T(1) < tend) fetch_k(T(1), kpa, pr0, pr1, pc, ps);
 
@@ -751,10 +533,7 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                 for (int s = 0; s < 8; ++s) qf[t][s] = (E)(qv[t][s] * p.sl2);
             }
-            if (T(0) < tend) {
-                stage_k(0, kpa, kr0, kr1, kc, ks);
-                if constexpr (!VDMA) stage_v(0, vpa, vr);
-            }
+            if (T(0) < tend) stage_k(0, kpa, kr0, kr1, kc, ks);
             if (T(1) < tend) stage_k(1, kpa, pr0, pr1, pc, ps);
         }
         const int64_t qrow = wq0 + l32;
@@ -896,11 +675,10 @@ void flash_fwd_bf16_kernel(Params p)
 #pragma unroll
                     for (int bd = 0; bd < DB; ++bd) {
                         const int key0 = 32 * kb2 + 16 * mm + tr_key;
-                        constexpr int RP = VDMA ? D : VP;   // row pitch
-                        const uint16_t *src = v_lds + key0 * RP + (VDMA ? vcol[bd] : 32 * bd + tr_col);
+                        const uint16_t *src = v_lds + key0 * D + vcol[bd];
                         const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
                         const s16x4_t x1 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * RP));
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * D));
                         const v8 a = __builtin_bit_cast(
                             v8, (short __attribute__((ext_vector_type(8)))){
                                           x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
@@ -909,13 +687,12 @@ void flash_fwd_bf16_kernel(Params p)
         };
 
         // Phase 1 (plan A), iterations [0, j_split), every wave of the group
-        // sharing the staging.  Iteration j (tile T(j)): load V(j+1) (straight
-        // into LDS with VDMA); compute the scores of tile j+1 (its K was
-        // staged one iteration earlier) on the matrix cores while forming
-        // tile j's probabilities from the scores computed one iteration
-        // earlier; then add tile j's P V while rotating and staging K(j+2)
-        // (and, without VDMA, V(j+1)) into the buffers iteration j-1 finished
-        // reading; then fetch K(j+3) (and V(j+2)) into registers.
+        // sharing the staging.  Iteration j (tile T(j)): load V(j+1) straight
+        // into LDS; compute the scores of tile j+1 (its K was staged one
+        // iteration earlier) on the matrix cores while forming tile j's
+        // probabilities from the scores computed one iteration earlier; then
+        // add tile j's P V while rotating and staging K(j+2) into the buffer
+        // iteration j-1 finished reading; then fetch K(j+3) into registers.
         //
         // Phase 2 (plan B), [j_split, n_iter): the tiles left are seen only
         // by the heavy half's rows.  The light half's two waves stage their
@@ -929,13 +706,11 @@ void flash_fwd_bf16_kernel(Params p)
         int j_end = c_end > t0 ? (c_end - t0 + TS - 1) / TS : 0;
         if (j_end > n_iter) j_end = n_iter;
         int j_split = n_iter;
-        if constexpr (OFFLOAD) {
-            if (rowB < p.Sq) {
-                const int64_t lastA = rowA + 63 < p.Sq ? rowA + 63 : p.Sq - 1;
-                const int light_end = (int)row_visits(p, lastA);   // light rows see tiles < light_end
-                const int js = light_end > t0 ? (light_end - t0 + TS - 1) / TS : 0;
-                if (js < j_split) j_split = js;
-            }
+        if (rowB < p.Sq) {
+            const int64_t lastA = rowA + 63 < p.Sq ? rowA + 63 : p.Sq - 1;
+            const int light_end = (int)row_visits(p, lastA);   // light rows see tiles < light_end
+            const int js = light_end > t0 ? (light_end - t0 + TS - 1) / TS : 0;
+            if (js < j_split) j_split = js;
         }
         const bool light = half == 0;
 
@@ -943,10 +718,8 @@ void flash_fwd_bf16_kernel(Params p)
         // iteration j-1 (here for j = 0), ahead of the barrier.
         auto fetch_next = [&](int j) {
             if (T(j + 2) < tend) fetch_k(T(j + 2), kpa, kr0, kr1, kc, ks);
-            if constexpr (!VDMA)
-                if (T(j + 1) < tend) fetch_v(T(j + 1), vpa, vr);
         };
-        // VDMA: right after the barrier that starts iteration j each wave
+        // Right after the barrier that starts iteration j each wave
         // loads its share of V(j+1) into V buffer (j+1) & 1, whose V(j-1) was
         // read in iteration j-1; before the barrier that ends iteration j it
         // waits for all its vector-memory loads (vmcnt 0), so the tile is
@@ -957,12 +730,8 @@ void flash_fwd_bf16_kernel(Params p)
             __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0); expcnt, lgkmcnt: no wait
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto dma_next = [&](int j, int blk0, auto NBLK) {
-            if constexpr (VDMA) dma_v(T(j + 1), (j + 1) & 1, blk0, NBLK);
-        };
-        auto wait_dma = [&]() {
-            if constexpr (VDMA) wait_vm0();
-        };
+        auto dma_next = [&](int j, int blk0, auto NBLK) { dma_v(T(j + 1), (j + 1) & 1, blk0, NBLK); };
+        auto wait_dma = [&]() { wait_vm0(); };
         using blk2 = std::integral_constant<int, 2>;
         using blk4 = std::integral_constant<int, 4>;
         wait_dma();   // V(0)
@@ -972,10 +741,7 @@ void flash_fwd_bf16_kernel(Params p)
         f32x16_t S0[NKB], S1[NKB];
         if (j_end > 0) qk(0, S0);
 
-        auto stage_next = [&](int j) {
-            stage_k(j & 1, kpa, kr0, kr1, kc, ks);
-            if constexpr (!VDMA) stage_v((j + 1) & 1, vpa, vr);
-        };
+        auto stage_next = [&](int j) { stage_k(j & 1, kpa, kr0, kr1, kc, ks); };
         // tile j's probabilities on the fast path (exact path if needed);
         // `mfma` issues the matrix-core work they are interleaved with
         auto softmax = [&](int j, f32x16_t (&sc)[NKB], v8 (&pb)[NKB][2], auto mfma, auto NMF,
@@ -1051,7 +817,7 @@ void flash_fwd_bf16_kernel(Params p)
             if (j + 1 < j_split) fetch_next(j + 1);
         }
         // ---- phase 2 ----
-        if constexpr (OFFLOAD) {
+        {
             if (j_split < n_iter) {
                 // Iteration j stages K(j+2) and loads V(j+1), as in phase 1.
                 // The light pair's 128 threads stage the K tiles, with their
@@ -1083,7 +849,6 @@ void flash_fwd_bf16_kernel(Params p)
                     }
                     j = n_iter;
                 } else {
-                    static_assert(VDMA, "phase 2 loads value tiles straight into LDS");
                     const int pblk = 4 * (wave & 1);
                     auto run = [&](f32x16_t (&A)[NKB], f32x16_t (&B)[NKB]) {
                         // iterations [j, j_end); tile j's scores in A
@@ -1113,7 +878,7 @@ void flash_fwd_bf16_kernel(Params p)
         float l_tot = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
         float m_fin = m_set ? m_ref : -INFINITY;
         float *xfer = reinterpret_cast<float *>(lds);
-        if constexpr (NG == 2 && !RS) {
+        {
             // group 1 hands its state to group 0 through LDS: per wave, per
             // lane, DB*16 accumulators + m + l, component-major.
             if (group == 1) {
@@ -1159,201 +924,35 @@ void flash_fwd_bf16_kernel(Params p)
             if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_fin + log2f(l_tot)) * LN2;
         };
 
-        if (full) {
-            if (RS || group == 0) write_out();
-        } else if (group == 0) {
-            // Split query tile: publish this segment's state; the merge
-            // kernel that follows on the stream combines the segments.
-            const int64_t U = (int64_t)p.BH * p.u_head;
-            const int my_slot = seg_v == share_start(w, U, p.sk_G) ? 0 : 1;
-            float *dst = p.ws_part + (((w * 2 + my_slot) * 4 + wave) * NC) * 64 + lane;
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dst[(b * 16 + r) * 64] = oacc[b][r];
-            dst[(DB * 16) * 64] = m_fin;
-            dst[(DB * 16 + 1) * 64] = l_tot;
-        }
-        __syncthreads();   // LDS is reused by the next segment
+        if (group == 0) write_out();
     };
 
-    if constexpr (!BAL) {
-        // A head's workgroups share an XCD (block index modulo the head
-        // count).  Causal: workgroup r takes 64-row half-tiles r and
-        // n_half - 1 - r, a light and a heavy one, so every workgroup sees
-        // about the same number of key tiles.  Otherwise: 128 consecutive rows.
-        const int bh = blockIdx.x % p.BH;
-        const int64_t rank = blockIdx.x / p.BH;
-        int64_t rowA, rowB;
-        if constexpr (RS) {
-            // two 128-row query tiles: with the causal mask tiles r and
-            // n - 1 - r, otherwise 2r and 2r + 1
-            const int64_t tb = p.causal ? p.n_qtiles - 1 - rank : 2 * rank + 1;
-            rowA = (p.causal ? rank : 2 * rank) * BM;
-            rowB = (tb != rank && tb < p.n_qtiles) ? tb * BM : p.Sq;
-            const int64_t lastr = (rowB < p.Sq ? rowB : rowA) + BM - 1;   // rowB > rowA when present
-            segment(bh, rowA, rowB, 0, row_visits(p, lastr < p.Sq ? lastr : p.Sq - 1), true, 0, 0);
-            return;
-        }
-        if (p.causal) {
-            const int64_t hb = p.n_half - 1 - rank;
-            rowA = 64 * rank;
-            rowB = hb > rank ? 64 * hb : p.Sq;
-        } else {
-            rowA = rank * BM;
-            rowB = rowA + 64;
-        }
-        const int64_t last = (rowB < p.Sq ? rowB : rowA) + 63;
-        segment(bh, rowA, rowB, 0, row_visits(p, last < p.Sq ? last : p.Sq - 1), true, 0, 0);
+    // A head's workgroups share an XCD (block index modulo the head count).
+    // Causal: workgroup r takes 64-row half-tiles r and n_half - 1 - r, a
+    // light and a heavy one, so every workgroup sees about the same number
+    // of key tiles.  Otherwise: 128 consecutive rows.
+    const int bh = blockIdx.x % p.BH;
+    const int64_t rank = blockIdx.x / p.BH;
+    int64_t rowA, rowB;
+    if (p.causal) {
+        const int64_t hb = p.n_half - 1 - rank;
+        rowA = 64 * rank;
+        rowB = hb > rank ? 64 * hb : p.Sq;
     } else {
-        // balanced share [v0, v1) of the (batch*head, query tile, key tile) visits
-        const int64_t U = (int64_t)p.BH * p.u_head;
-        const int64_t w = share_of_block(p, blockIdx.x);
-        const int64_t v1 = share_start(w + 1, U, p.sk_G);
-        for (int64_t v = share_start(w, U, p.sk_G); v < v1;) {
-            const int64_t hs = v / p.u_head;
-            const int bh = head_of_slot(p, hs);
-            const int64_t r = v - hs * p.u_head;
-            const int64_t qtile = find_tile(p, r);
-            const int64_t base = visits_before(p, qtile);
-            const int64_t nt = tile_visits(p, qtile);
-            const int64_t kb = r - base;
-            const int64_t ke = (nt < kb + (v1 - v)) ? nt : kb + (v1 - v);
-            segment(bh, qtile * BM, qtile * BM + 64, kb, ke, kb == 0 && ke == nt, v, w);
-            v += ke - kb;
-        }
+        rowA = rank * BM;
+        rowB = rowA + 64;
     }
+    const int64_t last = (rowB < p.Sq ? rowB : rowA) + 63;
+    segment(bh, rowA, rowB, 0, row_visits(p, last < p.Sq ? last : p.Sq - 1));
 }
 
-// Combines the segments of every split query tile, in share order, and
-// writes its output rows.  One 4-wave workgroup per (batch*head, query tile);
-// tiles that were not split return at once.  Runs after the main kernel on
-// the same stream, so every partial state is visible.
-template <int D, typename E>
-__global__ __launch_bounds__(256) void flash_merge_kernel(Params p)
-{
-    using TT = Ty<E>;
-    constexpr int DB = D / 32, NC = DB * 16 + 2;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int bh = blockIdx.x / p.n_qtiles;
-    const int64_t qtile = blockIdx.x % p.n_qtiles;
-    const int64_t U = (int64_t)p.BH * p.u_head;
-    const int64_t X0 = slot_of_head(p, bh) * p.u_head + visits_before(p, qtile);
-    const int64_t X1 = X0 + tile_visits(p, qtile);
-    const int64_t w_first = share_of(X0, U, p.sk_G), w_last = share_of(X1 - 1, U, p.sk_G);
-    if (w_first == w_last) return;   // written by the main kernel
-    const int64_t qrow = qtile * BM + wave * 32 + l32;
-    f32x16_t oacc[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) oacc[b] = (f32x16_t){};
-    float m_acc = -INFINITY, l_sum = 0.f;
-    for (int64_t w2 = w_first; w2 <= w_last; ++w2) {
-        const int slot2 = share_start(w2, U, p.sk_G) >= X0 ? 0 : 1;
-        const float *src = p.ws_part + (((w2 * 2 + slot2) * 4 + wave) * NC) * 64 + lane;
-        const float m2 = src[(DB * 16) * 64], l2 = src[(DB * 16 + 1) * 64];
-        const float m = fmaxf(m_acc, m2);
-        const float a1 = m_acc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_acc - m);
-        const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[b][r] = oacc[b][r] * a1 + src[(b * 16 + r) * 64] * a2;
-        l_sum = l_sum * a1 + l2 * a2;
-        m_acc = m;
-    }
-    if (qrow >= p.Sq) return;
-    const float inv = 1.f / l_sum;
-    uint16_t *orow = p.o + ((int64_t)bh * p.Sq + qrow) * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * b + 8 * g + 4 * hh;
-            uint2 wv;
-            wv.x = TT::pack2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-            wv.y = TT::pack2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-            *reinterpret_cast<uint2 *>(orow + d0) = wv;
-        }
-    if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_acc + log2f(l_sum)) * LN2;
-}
+// Tile shape: two key groups (8 waves, two per SIMD) of 64-key tiles.
+constexpr int D64_NG = 2, D64_BN = 64;
 
-#ifndef ROPE_FLASH_D64_NG
-#define ROPE_FLASH_D64_NG 2
-#endif
-#ifndef ROPE_FLASH_D64_BN
-#define ROPE_FLASH_D64_BN 64
-#endif
-#ifndef ROPE_FLASH_D128_NG
-#define ROPE_FLASH_D128_NG 1
-#endif
-#ifndef ROPE_FLASH_D128_BN
-#define ROPE_FLASH_D128_BN 32
-#endif
-
-// Tile shape per head dim: key groups per workgroup and keys per tile.
-// D = 64: two groups (8 waves, two per SIMD) of 64-key tiles.  D = 128: one
-// group of 32-key tiles (within 256 registers per wave), two workgroups per
-// CU.
-template <int D> struct Shape;
-template <> struct Shape<64> {
-    static constexpr int NG = ROPE_FLASH_D64_NG, BN = ROPE_FLASH_D64_BN;
-};
-template <> struct Shape<128> {
-    static constexpr int NG = ROPE_FLASH_D128_NG, BN = ROPE_FLASH_D128_BN;
-};
-
-
-// Host half of the schedule: visit-law coefficients, and the balanced
-// share count (0 = one workgroup per query tile).
-template <int D>
-void plan(const FlashArgs &a, Params &p)
-{
-    constexpr int BN = Shape<D>::BN, NG = Shape<D>::NG;
-    p.BH = a.B * a.H;
-    p.kv_group = a.H / a.H_kv;
-    p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
-    p.causal = a.causal;
-    p.n_qtiles = (a.Sq + BM - 1) / BM;
-    p.n_half = (a.Sq + 63) / 64;
-    p.tile_n = BN;
-    p.n_kt = (a.Sk + BN - 1) / BN;
-    const int64_t delta = a.q_off - a.k_off;   // >= 0 when causal (validated)
-    p.va = BM / BN;
-    p.vb = (BM - 1 + delta) / BN + 1;
-    {
-        const int64_t je = a.q_off + a.Sq - 1 - a.k_off;
-        p.v_last = a.causal ? (je / BN + 1 < p.n_kt ? je / BN + 1 : p.n_kt) : p.n_kt;
-    }
-    p.u_head = visits_before(p, p.n_qtiles);
-    p.sk_G = 0;
-    p.xcd_order = 0;
-    p.ws_part = nullptr;
-    if (!a.causal) return;
-    // balance only when the largest query tile does clearly more than the
-    // average and there is enough work to share
-    const int cus = rope_device_cu_count();
-    const int G = cus * (NG == 2 ? 1 : 2);
-    const int64_t U = (int64_t)p.BH * p.u_head;
-    const int64_t vmax = tile_visits(p, p.n_qtiles - 1) > tile_visits(p, 0) ? tile_visits(p, p.n_qtiles - 1)
-                                                                            : tile_visits(p, 0);
-    if (G <= 0 || U < 4 * (int64_t)G || vmax * p.n_qtiles * 10 < p.u_head * 11) return;
-    p.sk_G = G;
-    p.xcd_order = (p.BH % 8 == 0 && G % 8 == 0) ? 1 : 0;
-}
-
-template <int D>
-int64_t workspace_bytes(const Params &p)
-{
-    if (p.sk_G == 0) return 0;
-    constexpr int NC = (D / 32) * 16 + 2;
-    return (int64_t)p.sk_G * 2 * 4 * NC * 64 * 4;   // two partial states per share
-}
-
-template <int D, int LAYOUT, bool ROT, bool FULL, typename E>
+template <int LAYOUT, bool ROT, bool FULL, typename E>
 int launch(const FlashArgs &a, hipStream_t stream)
 {
-    constexpr int NG = Shape<D>::NG, BN = Shape<D>::BN;
+    constexpr int D = 64, NG = D64_NG, BN = D64_BN;
     Params p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
@@ -1363,75 +962,48 @@ int launch(const FlashArgs &a, hipStream_t stream)
     p.cos_tab = a.cos_tab; p.sin_tab = a.sin_tab; p.rot_dim = a.rot_dim;
     p.table_rows = a.table_rows;
     p.sl2 = a.scale * 1.4426950408889634f;
-    plan<D>(a, p);
-    const int64_t need = workspace_bytes<D>(p);
-    if (need == 0 || a.workspace == nullptr || a.workspace_bytes < need)
-        p.sk_G = 0;   // no (or too small a) workspace: one workgroup per query tile
-    else
-        p.ws_part = static_cast<float *>(a.workspace);
-    // D = 128, default schedule: row split (two query tiles per workgroup)
-    constexpr bool RSPLIT = D == 128;
-    {
-        int64_t blocks = p.sk_G;
-        if (p.sk_G == 0)
-            blocks = RSPLIT ? (int64_t)p.BH * ((p.n_qtiles + 1) / 2)
-                            : (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
-        if (!rope_grid_fits(blocks, 512) || (p.sk_G > 0 && !rope_grid_fits((int64_t)p.BH * p.n_qtiles, 256)))
-            return ROPE_LAUNCH_SHAPE;
-    }
-    if (p.sk_G > 0) {
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, true, false, E>), dim3((unsigned)p.sk_G),
-                           dim3(256 * NG), 0, stream, p);
-    } else if constexpr (RSPLIT) {
-        const int64_t blocks = (int64_t)p.BH * ((p.n_qtiles + 1) / 2);
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, 2, BN, false, true, E>), dim3((unsigned)blocks),
-                           dim3(512), 0, stream, p);
-    } else {
-        const int64_t blocks = (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
-        hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, false, false, E>), dim3((unsigned)blocks),
-                           dim3(256 * NG), 0, stream, p);
-    }
-    if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
-    if (p.sk_G > 0) {
-        hipLaunchKernelGGL((flash_merge_kernel<D, E>), dim3((unsigned)(p.BH * p.n_qtiles)), dim3(256), 0,
-                           stream, p);
-        if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
-    }
-    return ROPE_LAUNCH_OK;
+    p.BH = a.B * a.H;
+    p.kv_group = a.H / a.H_kv;
+    p.Sq = a.Sq; p.Sk = a.Sk; p.q_off = a.q_off; p.k_off = a.k_off;
+    p.causal = a.causal;
+    p.n_qtiles = (a.Sq + BM - 1) / BM;
+    p.n_half = (a.Sq + 63) / 64;
+    p.tile_n = BN;
+    p.n_kt = (a.Sk + BN - 1) / BN;
+    const int64_t blocks = (int64_t)p.BH * (p.causal ? (p.n_half + 1) / 2 : p.n_qtiles);
+    if (!rope_grid_fits(blocks, 256 * NG)) return ROPE_LAUNCH_SHAPE;
+    hipLaunchKernelGGL((flash_fwd_bf16_kernel<D, LAYOUT, ROT, FULL, NG, BN, E>), dim3((unsigned)blocks),
+                       dim3(256 * NG), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? ROPE_LAUNCH_OK : ROPE_LAUNCH_ERR;
 }
 
-template <int D, typename E>
-int launch_d(const FlashArgs &a, hipStream_t stream)
+template <typename E>
+int launch_e(const FlashArgs &a, hipStream_t stream)
 {
-    if (a.rot_dim == 0) return launch<D, 1, false, false, E>(a, stream);
-    const bool full = a.rot_dim == D;
-    if (a.layout == 0)
-        return full ? launch<D, 0, true, true, E>(a, stream) : launch<D, 0, true, false, E>(a, stream);
-    return full ? launch<D, 1, true, true, E>(a, stream) : launch<D, 1, true, false, E>(a, stream);
+    if (a.rot_dim == 0) return launch<1, false, false, E>(a, stream);
+    const bool full = a.rot_dim == 64;
+    if (a.layout == 0) return full ? launch<0, true, true, E>(a, stream) : launch<0, true, false, E>(a, stream);
+    return full ? launch<1, true, true, E>(a, stream) : launch<1, true, false, E>(a, stream);
 }
 
 }  // namespace
 
 // dtype 0 (bf16) or 2 (fp16): the same kernels over either 16-bit type.
-// Head dim 128 runs the two-team kernel of flash_fwd_pp.hip.
+// Head dim 64 runs the kernel above, 128 the two-team kernel of
+// flash_fwd_pp.hip.
 int rope_launch_flash_bf16(const FlashArgs &a, hipStream_t stream)
 {
     const int rc = rope_launch_flash_pp(a, stream);
     if (rc >= 0) return rc;
-    if (a.dtype == 2) return a.head_dim == 64 ? launch_d<64, _Float16>(a, stream) : launch_d<128, _Float16>(a, stream);
-    return a.head_dim == 64 ? launch_d<64, __bf16>(a, stream) : launch_d<128, __bf16>(a, stream);
+    if (a.head_dim != 64) return ROPE_LAUNCH_SHAPE;
+    return a.dtype == 2 ? launch_e<_Float16>(a, stream) : launch_e<__bf16>(a, stream);
 }
 
+// Only the split-key schedule of the head-dim-128 kernel uses a workspace.
 int64_t rope_flash_bf16_workspace_bytes(const FlashArgs &a)
 {
     if (a.head_dim == 128 && (a.dtype == 0 || a.dtype == 2)) return rope_flash_pp_workspace_bytes(a);
-    Params p;
-    if (a.head_dim == 64) {
-        plan<64>(a, p);
-        return workspace_bytes<64>(p);
-    }
-    plan<128>(a, p);
-    return workspace_bytes<128>(p);
+    return 0;
 }
 
 namespace {

@@ -228,20 +228,20 @@ def test_backward_full_size_gqa_prefill(orc):
     full_size_identities(orc, w, dout, dk, dv)
 
 
-def test_lse_balanced_schedule(orc):
-    """The balanced (split query tile) schedule writes each row's log-sum-exp
-    from the merge of its pieces: the same bar as the default schedule."""
-    w = wl.AttentionWorkload("causal_neox_bf16_1x8x2048x64", 1, 8, 2048, 2048, 64, "bf16", 3, "neox")
+def test_lse_split_schedule(orc):
+    """The split-key schedule (head dim 128) writes each row's log-sum-exp
+    from the merge of its segments: the same bar as the default schedule."""
+    w = wl.AttentionWorkload("causal_neox_bf16_1x8x2048x128", 1, 8, 2048, 2048, 128, "bf16", 3, "neox")
     q, k, v = wl.attention_inputs(w)
     tq, tk, tv = bf16(q), bf16(k), bf16(v)
     c, s = api.tables_build(w.base, w.rot, w.table_rows, device=DEV)
     ws = api.workspace_for(tq, w.Sk, 0, 0, True)
-    assert ws is not None   # this shape runs the balanced schedule (see the parity tests)
+    assert ws is not None   # this shape runs the split schedule (see the parity tests)
     lse = torch.full((1, 8, 2048), float("nan"), dtype=torch.float32, device=DEV)
     api.flash_attn_fwd(tq, tk, tv, c, s, layout="neox", lse=lse, workspace=ws)
     torch.cuda.synchronize()
     want = orc.attention_lse(q, k, base=w.base, layout="neox")
-    assert (np.abs(to64(lse) - want) <= lse_bound(q, k, 64)).all()
+    assert (np.abs(to64(lse) - want) <= lse_bound(q, k, 128)).all()
 
 
 def test_lse_fp32_forward(orc):

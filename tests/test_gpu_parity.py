@@ -471,54 +471,55 @@ def test_fused_deterministic_and_unfused_agree():
 
 
 # --------------------------------------------------------------------------
-# balanced (split query tile) schedule
+# split-key schedule (head dim 128, fewer query-tile pairs than CUs)
 
 
-BALANCED = [
-    wl.AttentionWorkload("balanced_neox_1x8x2048x64", 1, 8, 2048, 2048, 64, "bf16", 21, "neox"),
-    wl.AttentionWorkload("balanced_gptj_2x4x2000x64", 2, 4, 2000, 2000, 64, "bf16", 22, "gptj"),
-    wl.AttentionWorkload("balanced_neox_1x8x2048x128", 1, 8, 2048, 2048, 128, "bf16", 23, "neox"),
-    wl.AttentionWorkload("balanced_offset_gptj_1x8x1500x2600x128", 1, 8, 1500, 2600, 128, "bf16", 24,
+SPLIT_KEYS = [
+    wl.AttentionWorkload("split_neox_1x8x2048x128", 1, 8, 2048, 2048, 128, "bf16", 23, "neox"),
+    wl.AttentionWorkload("split_offset_gptj_1x8x1500x2600x128", 1, 8, 1500, 2600, 128, "bf16", 24,
                          "gptj", q_off=1100, k_off=0),
-    wl.AttentionWorkload("balanced_gqa_neox_1x8q2kv_2048x64", 1, 8, 2048, 2048, 64, "bf16", 25,
+    wl.AttentionWorkload("split_gqa_neox_1x8q2kv_1000x128", 1, 8, 1000, 1000, 128, "bf16", 25,
                          "neox", H_kv=2),
+    wl.AttentionWorkload("split_noncausal_gptj_2x2x300x700x128", 2, 2, 300, 700, 128, "bf16", 26,
+                         "gptj", causal=False),
 ]
 
 
-def test_balanced_schedule_is_used():
-    """The square causal workloads above request a workspace (the split
-    schedule runs); a balanced one (chunked prefill) does not."""
+def test_split_schedule_is_used():
+    """The head-dim-128 workloads above request a workspace (the split
+    schedule runs); the chunked prefill (256 query-tile pairs) and head dim
+    64 do not."""
     from rotary_position_embedding_rope_amd import _lib
     lib = _lib.load()
-    for w in BALANCED[:3] + [wl.HEADLINE]:
-        assert lib.rope_flash_attn_workspace_size(w.B, w.H, w.Sq, w.Sk, w.D, w.q_off, w.k_off, 1,
+    for w in SPLIT_KEYS:
+        assert lib.rope_flash_attn_workspace_size(w.B, w.H, w.Sq, w.Sk, w.D, w.q_off, w.k_off, int(w.causal),
                                                   _lib.BF16) > 0, w.name
-    w = wl.PREFILL_OFFSET
-    assert lib.rope_flash_attn_workspace_size(w.B, w.H, w.Sq, w.Sk, w.D, w.q_off, w.k_off, 1,
-                                              _lib.BF16) == 0
+    for w in (wl.PREFILL_OFFSET, wl.HEADLINE):
+        assert lib.rope_flash_attn_workspace_size(w.B, w.H, w.Sq, w.Sk, w.D, w.q_off, w.k_off, 1,
+                                                  _lib.BF16) == 0, w.name
 
 
-@pytest.mark.parametrize("w", BALANCED, ids=lambda w: w.name)
-def test_balanced_schedule_full(orc, w):
-    """Split query tiles merged through the workspace: every output vs the
-    oracle (2e-2), the same with no workspace (one workgroup per query
-    tile), two calls in a row bit-identical (the merge order is fixed)."""
+@pytest.mark.parametrize("w", SPLIT_KEYS, ids=lambda w: w.name)
+def test_split_schedule_full(orc, w):
+    """Key segments merged through the workspace: every output vs the oracle
+    (2e-2), the same with no workspace (one workgroup per query-tile pair),
+    two calls in a row bit-identical (the merge order is fixed)."""
     q, k, v = wl.attention_inputs(w)
     tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
     c, s = tables(w.base, w.rot, w.table_rows)
-    ws = api.workspace_for(tq, w.Sk, w.q_off, w.k_off, True)
+    ws = api.workspace_for(tq, w.Sk, w.q_off, w.k_off, w.causal)
     assert ws is not None
     ws.fill_(0x7f)   # contents are irrelevant: stale bytes must not matter
     outs = []
     for use_ws in (ws, ws, None):
         out = torch.full_like(tq, float("nan"))
-        api.flash_attn_fwd(tq, tk, tv, c, s, w.q_off, w.k_off, w.rot, w.layout, True, out=out,
+        api.flash_attn_fwd(tq, tk, tv, c, s, w.q_off, w.k_off, w.rot, w.layout, w.causal, out=out,
                            workspace=use_ws)
         torch.cuda.synchronize()
         outs.append(out)
     assert torch.equal(outs[0], outs[1])
     want = orc.attention(q, k, v, q_off=w.q_off, k_off=w.k_off, rot_dim=w.rot, base=w.base,
-                         layout=w.layout, causal=True)
+                         layout=w.layout, causal=w.causal)
     for out in outs:
         got = to64(out)
         assert np.isfinite(got).all()
