@@ -101,6 +101,17 @@ def recorded_traffic(profile: str, source: str):
     return float(m_b.group(1))
 
 
+def fused_traffic(w):
+    """Recorded HBM bytes per launch of the fused forward kernel that runs w
+    (head dim 128 in 16-bit storage: flash_fwd_pp.hip, else
+    flash_fwd_bf16.hip), or None."""
+    if w.dtype == "f32":
+        return None
+    if w.D == 128:
+        return recorded_traffic(f"flash_fwd_pp_{w.name}_traffic.md", "flash_fwd_pp.hip")
+    return recorded_traffic(f"flash_fwd_bf16_{w.name}_traffic.md", "flash_fwd_bf16.hip")
+
+
 def time_launches(torch, launch, steps, warmup, stream, rotate=None):
     """Warm up, then the timed region: `steps` launches back to back on
     `stream`, between device synchronisations, with one HIP event pair on the
@@ -202,8 +213,7 @@ def fused_entry(torch, api, wl, orc, w, config, steps, warmup, comparators_too=F
          "value": round(tf, 2), "unit": "TFLOP/s",
          "roofline": {"bound": "alu" if f32 else "mfma", "achieved": round(tf, 2), "peak": peak,
                       "unit": "TFLOP/s", "frac": round(tf / peak, 4),
-                      "traffic": None if f32 else recorded_traffic(f"flash_fwd_bf16_{w.name}_traffic.md",
-                                                                   "flash_fwd_bf16.hip"),
+                      "traffic": fused_traffic(w),
                       "algorithmic_flops": flops},
          "max_abs_err": err, "err_checked": checked, "tolerance": 1e-5 if f32 else 2e-2}
     if comparators_too:
@@ -535,8 +545,7 @@ def main():
                                "single_launch_p90": round(r["p90"], 5)}
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                              "traffic": recorded_traffic(f"flash_fwd_bf16_{w.name}_traffic.md",
-                                                          "flash_fwd_bf16.hip"),
+                              "traffic": fused_traffic(w),
                               "algorithmic_flops": flops}
         if w.name in PAGE_ROPE_MS:
             result["vs_baseline"] = round(PAGE_ROPE_MS[w.name] / r["ms_step"], 2)
