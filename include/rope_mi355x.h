@@ -205,7 +205,8 @@ int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
 
 /*
  * rope_flash_attn_workspace_size -- bytes of workspace rope_flash_attn_fwd
- * can use for these shapes on the current device (0: it would use none).
+ * can use for these shapes on the current device, whatever H_kv (0: it
+ * would use none).
  * Returns minus a status code for arguments rope_flash_attn_fwd would reject
  * on shape grounds.  Makes no device allocation.
  */

@@ -187,7 +187,9 @@ int64_t rope_flash_attn_workspace_size(int B, int H, int64_t Sq, int64_t Sk, int
     if (st != ROPE_OK) return -st;
     if (dtype == ROPE_F32) return 0;
     FlashArgs a = {};
-    a.B = B; a.H = H; a.H_kv = H; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
+    // H_kv 0: enough for any key/value head count (the head grouping of the
+    // split schedule depends on it)
+    a.B = B; a.H = H; a.H_kv = 0; a.Sq = Sq; a.Sk = Sk; a.head_dim = head_dim;
     a.q_off = q_pos_offset; a.k_off = k_pos_offset; a.causal = causal ? 1 : 0; a.dtype = dtype;
     return rope_flash_bf16_workspace_bytes(a);
 }

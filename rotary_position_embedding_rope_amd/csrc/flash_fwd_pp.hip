@@ -9,13 +9,20 @@
 // pairs and formula: "Write Triton Rope Kernel", "Required reasoning
 // process" steps 1 and 6; V is never rotated.
 //
-// Work decomposition.  A workgroup of 512 threads owns two 128-row query
-// tiles of one (batch, head): team 0 (waves 0-3) tile 2r, team 1 (waves
-// 4-7) tile 2r + 1, so both teams walk nearly the same key range; with the
-// causal mask the pairs with the most keys are launched first.  A wave owns
-// 32 query rows.  Both teams walk the same key tiles (BN = 64 keys by
-// default, 32 also compiles), so each key tile is loaded, rotated and staged
-// in LDS once for 256 query rows.
+// Work decomposition.  A workgroup of 512 threads owns 256 query rows that
+// read the same key/value head: G query heads of one key/value head (G the
+// largest of 1, 2, 4, 8 dividing the query heads per key/value head) times
+// a block of 256 / G consecutive query rows, the same rows in each head, so
+// every wave walks nearly the same key range.  Waves 8/G apart take
+// consecutive heads; a wave owns 32 query rows.  With G = 1 that is two
+// 128-row query tiles of one head (team 0 = waves 0-3 the lower one); with
+// grouped-query attention a staged key tile serves G query heads at once
+// ("Write Triton Rope Kernel", "Inputs the agent should gather first", item
+// 3: query and key head counts differ and share one table).  Under the
+// causal mask the row blocks with the most keys are launched first.  All
+// waves walk the same key tiles (BN = 64 keys by default, 32 also
+// compiles), so each key tile is loaded, rotated and staged in LDS once
+// for 256 query rows.
 //
 // Ping-pong.  The two waves of one SIMD belong to different teams.  Time is
 // cut into phases separated by workgroup barriers; in each phase one team
@@ -101,7 +108,7 @@ __device__ __forceinline__ int vswz(int row)
     return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 constexpr float PP_LAZY = 8.0f;      // log2 headroom before the reference is raised
-constexpr int PP_MAXSEG = 8;         // key segments per pair at most (split schedule)
+constexpr int PP_MAXSEG = 8;         // key segments per row block at most (split schedule)
 constexpr float PP_LN2 = 0.6931471805599453f;
 constexpr int RSRC_FLAGS = 0x00020000;
 
@@ -117,11 +124,13 @@ struct PPParams {
     int rot_dim;
     float sl2;
     int causal;
-    int n_qt;    // 128-row query tiles
+    int g_log2;  // log2 G: G query heads of one key/value head per workgroup
+    int n_hg;    // head groups: BH / G
+    int n_rb;    // row blocks of 256 / G query rows
     int n_kt;    // key tiles
     // split keys: the key tiles of a workgroup's query rows are cut into
-    // segments of seg_tiles tiles (nseg at most); segments of a cut pair
-    // leave fp32 partial states in ws, merged by flash_pp_merge_kernel
+    // segments of seg_tiles tiles (nseg at most); segments of a cut row
+    // block leave fp32 partial states in ws, merged by flash_pp_merge_kernel
     int seg_tiles, nseg;
     float *ws;
 };
@@ -206,19 +215,19 @@ __device__ __forceinline__ int tiles_seen(const PPParams &p, int last)
     return v < p.n_kt ? (int)v : p.n_kt;
 }
 
-// Key tiles of the pair of query tiles (2 pr, 2 pr + 1): the larger count
-// of the two.
+// Key tiles of row block rb (rows rb R .. rb R + R - 1, R = 256 / G): those
+// its last row sees.
 template <int BN>
-__device__ __forceinline__ int pair_tiles(const PPParams &p, int pr)
+__device__ __forceinline__ int block_tiles(const PPParams &p, int rb)
 {
-    const int tB = 2 * pr + 1 < p.n_qt ? 2 * pr + 1 : 2 * pr;
-    const int last = tB * 128 + 127 < p.Sq ? tB * 128 + 127 : p.Sq - 1;
+    const int R = 256 >> p.g_log2;
+    const int last = rb * R + R - 1 < p.Sq ? rb * R + R - 1 : p.Sq - 1;
     return tiles_seen<BN>(p, last);
 }
 
 // PING: ping-pong schedule (team 1 one phase behind team 0, two barriers per
 // key tile); otherwise both teams run each step together (one barrier per
-// tile).  SPLIT: the workgroup takes one key segment of its pair.
+// tile).  SPLIT: the workgroup takes one key segment of its row block.
 template <int D, int BN, bool PING, bool SPLIT, int LAYOUT, bool ROT, bool FULL, typename E>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_pp_kernel(PPParams p)
@@ -244,29 +253,28 @@ void flash_fwd_pp_kernel(PPParams p)
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int rh = p.rot_dim / 2;   // table row stride (floats)
 
-    // ---- work item: (batch*head, two query tiles, key segment) ----
-    const int bh = blockIdx.x % p.BH;
-    const int npair = (p.n_qt + 1) / 2;
-    const int r = (blockIdx.x / p.BH) % npair;
-    const int seg = SPLIT ? (int)(blockIdx.x / p.BH / npair) : 0;
-    // Each workgroup takes two adjacent query tiles (team 0 the lower one), so
-    // both teams walk nearly the same key range; under the causal mask the
-    // pairs with the most keys come first.
-    const int pr = p.causal ? npair - 1 - r : r;
-    const int tA = 2 * pr;
-    const int tB = 2 * pr + 1;
-    const int my_t = team ? tB : tA;
-    const bool team_rows = team == 0 || tB < p.n_qt;
-    // this wave's first query row (wave-uniform: keeps the descriptors scalar)
-    const int row0 = __builtin_amdgcn_readfirstlane(my_t * 128 + 32 * wave);
-    const bool wave_rows = team_rows && row0 < p.Sq;
+    // ---- work item: (head group, row block, key segment) ----
+    // Block index mod n_hg selects the head group, so one key/value head's
+    // workgroups share an XCD (and its L2) when n_hg is a multiple of 8.
+    const int hg = blockIdx.x % p.n_hg;
+    const int r = (blockIdx.x / p.n_hg) % p.n_rb;
+    const int seg = SPLIT ? (int)(blockIdx.x / p.n_hg / p.n_rb) : 0;
+    const int rb = p.causal ? p.n_rb - 1 - r : r;   // the most keys first
+    const int item = hg * p.n_rb + rb;
+    // wave gw of the workgroup: head gw >> (3 - g_log2) of the group, rows
+    // 32 (gw mod 8/G) of the block (wave-uniform: keeps descriptors scalar)
+    const int gw = 4 * team + wave;
+    const int wlog = 3 - p.g_log2;
+    const int bh = __builtin_amdgcn_readfirstlane((hg << p.g_log2) + (gw >> wlog));   // batch*head
+    const int row0 = __builtin_amdgcn_readfirstlane(rb * (256 >> p.g_log2) + 32 * (gw & ((1 << wlog) - 1)));
+    const bool wave_rows = row0 < p.Sq;
     const int wlast = row0 + 31 < p.Sq ? row0 + 31 : p.Sq - 1;
     // tiles this wave computes, and the workgroup's staging range
     const int w_end = wave_rows ? tiles_seen<BN>(p, wlast) : 0;
-    const int k_all = pair_tiles<BN>(p, pr);
-    // this workgroup's key tiles [k_beg, k_end): its segment of the pair's
+    const int k_all = block_tiles<BN>(p, rb);
+    // this workgroup's key tiles [k_beg, k_end): its segment of the row block's
     int k_beg = 0, k_end = k_all;
-    bool partial = false;   // the pair is cut: leave a partial state
+    bool partial = false;   // the row block is cut: leave a partial state
     if constexpr (SPLIT) {
         k_beg = seg * p.seg_tiles;
         if (k_beg >= k_all) return;   // no segment here (uniform over the workgroup)
@@ -782,8 +790,8 @@ void flash_fwd_pp_kernel(PPParams p)
         // ---- partial state of this segment: unnormalised O, reference m
         // (-inf when no key of the segment was visible) and row sum l, as
         // [D + 2][256 rows] fp32 for the merge kernel's coalesced reads
-        const int rr = team * 128 + 32 * wave + l32;
-        float *blk = p.ws + (((int64_t)bh * npair + pr) * p.nseg + seg) * (int64_t)(D + 2) * 256;
+        const int rr = 32 * gw + l32;
+        float *blk = p.ws + ((int64_t)item * p.nseg + seg) * (int64_t)(D + 2) * 256;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -813,8 +821,9 @@ void flash_fwd_pp_kernel(PPParams p)
     if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = ((m_set ? m_ref : -INFINITY) + log2f(l_tot)) * PP_LN2;
 }
 
-// Merges the segments of every cut pair: one workgroup per (batch*head,
-// pair, 8-dim chunk of the output), one thread per query row.  With M the
+// Merges the segments of every cut row block: one workgroup per (head group,
+// row block, 8-dim chunk of the output), one thread per query row (thread t:
+// head t / R of the group, row t mod R of the block, R = 256 / G).  With M the
 // largest reference of the row's segments,
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, which is exact in real
 // arithmetic (each segment's O_s and l_s are measured against its own
@@ -826,17 +835,18 @@ __global__ __launch_bounds__(256) void flash_pp_merge_kernel(PPParams p)
 {
     using TT = Ty<E>;
     constexpr int NC = D / 8;
-    const int bh = blockIdx.x % p.BH;
-    const int npair = (p.n_qt + 1) / 2;
-    const int pr = (blockIdx.x / p.BH) / NC;
-    const int c8 = 8 * ((blockIdx.x / p.BH) % NC);
-    const int k_all = pair_tiles<BN>(p, pr);
+    const int hg = blockIdx.x % p.n_hg;
+    const int rb = (blockIdx.x / p.n_hg) / NC;
+    const int c8 = 8 * ((blockIdx.x / p.n_hg) % NC);
+    const int k_all = block_tiles<BN>(p, rb);
     if (k_all <= p.seg_tiles) return;   // written by the main kernel
     const int ns = (k_all + p.seg_tiles - 1) / p.seg_tiles;
     const int t = threadIdx.x;
-    const int qrow = (t < 128 ? 2 * pr : 2 * pr + 1) * 128 + (t & 127);
+    const int rlog = 8 - p.g_log2;   // log2 R
+    const int bh = (hg << p.g_log2) + (t >> rlog);
+    const int qrow = (rb << rlog) + (t & ((1 << rlog) - 1));
     if (qrow >= p.Sq) return;
-    const float *blk0 = p.ws + ((int64_t)bh * npair + pr) * p.nseg * (int64_t)(D + 2) * 256 + t;
+    const float *blk0 = p.ws + ((int64_t)hg * p.n_rb + rb) * p.nseg * (int64_t)(D + 2) * 256 + t;
     const int64_t sstride = (int64_t)(D + 2) * 256;
     float m[PP_MAXSEG], l[PP_MAXSEG], o[PP_MAXSEG][8];
 #pragma unroll
@@ -882,16 +892,27 @@ __global__ __launch_bounds__(256) void flash_pp_merge_kernel(PPParams p)
 template <int D> constexpr bool pp_ping() { return D == 128 ? true : (ROPE_PP_PING64 != 0); }
 
 // Host half: kernel parameters, and the split plan (seg_tiles = 0: none).
-// Pairs of 128-row query tiles see k_all(pr) key tiles; when the pairs are
-// fewer than the CUs, the smallest segment length C is chosen whose segment
-// count, sum over pairs of ceil(k_all / C), still fits one workgroup per CU.
+// Row block rb (of each head group) sees k_all(rb) key tiles; when the work
+// items (head groups times row blocks) are fewer than the CUs, the smallest
+// segment length C is chosen whose segment count, n_hg times the sum over
+// row blocks of ceil(k_all / C), still fits one workgroup per CU.
 struct PPPlan {
     PPParams p;
     int64_t ws_bytes;   // workspace the split needs (0: no split)
 };
 
+// log2 of G, the query heads per workgroup: the largest of 1, 2, 4, 8 that
+// divides the query heads per key/value head.
+inline int pp_group_log2(int kv_group)
+{
+    int g = 0;
+    while (g < 3 && kv_group % (2 << g) == 0) ++g;
+    return g;
+}
+
+// g_log2 < 0: G from the head counts of `a`.
 template <int D>
-PPPlan pp_plan(const FlashArgs &a)
+PPPlan pp_plan(const FlashArgs &a, int g_log2 = -1)
 {
     constexpr int BN = ROPE_PP_BN;
     PPPlan pl;
@@ -913,30 +934,31 @@ PPPlan pp_plan(const FlashArgs &a)
     p.rot_dim = a.rot_dim;
     p.sl2 = a.scale * 1.4426950408889634f;
     p.causal = a.causal;
-    p.n_qt = (int)((a.Sq + 127) / 128);
+    p.g_log2 = g_log2 >= 0 ? g_log2 : pp_group_log2(p.kv_group);
+    const int R = 256 >> p.g_log2;   // query rows per head in a workgroup
+    p.n_hg = p.BH >> p.g_log2;
+    p.n_rb = (int)((a.Sq + R - 1) / R);
     p.n_kt = (int)((a.Sk + BN - 1) / BN);
     p.seg_tiles = 0;
     p.nseg = 1;
     p.ws = nullptr;
     pl.ws_bytes = 0;
-    const int npair = (p.n_qt + 1) / 2;
     const int cus = rope_device_cu_count();
-    const int64_t pairs = (int64_t)p.BH * npair;
-    if (cus <= 0 || pairs >= cus) return pl;
-    auto k_all = [&](int pr) {
-        const int tB = 2 * pr + 1 < p.n_qt ? 2 * pr + 1 : 2 * pr;
-        const int64_t last = tB * 128 + 127 < a.Sq ? tB * 128 + 127 : a.Sq - 1;
+    const int64_t items = (int64_t)p.n_hg * p.n_rb;
+    if (cus <= 0 || items >= cus) return pl;
+    auto k_all = [&](int rb) {
+        const int64_t last = (int64_t)rb * R + R - 1 < a.Sq ? (int64_t)rb * R + R - 1 : a.Sq - 1;
         if (!a.causal) return p.n_kt;
         const int64_t v = (a.q_off + last - a.k_off) / BN + 1;
         return (int)(v < p.n_kt ? v : p.n_kt);
     };
     int kmax = 0;
-    for (int pr = 0; pr < npair; ++pr) kmax = k_all(pr) > kmax ? k_all(pr) : kmax;
+    for (int rb = 0; rb < p.n_rb; ++rb) kmax = k_all(rb) > kmax ? k_all(rb) : kmax;
     int C = kmax;
     for (int c = (kmax + PP_MAXSEG - 1) / PP_MAXSEG; c < kmax; ++c) {
         int64_t n = 0;
-        for (int pr = 0; pr < npair; ++pr) n += (k_all(pr) + c - 1) / c;
-        if (n * p.BH <= cus) {
+        for (int rb = 0; rb < p.n_rb; ++rb) n += (k_all(rb) + c - 1) / c;
+        if (n * p.n_hg <= cus) {
             C = c;
             break;
         }
@@ -944,7 +966,7 @@ PPPlan pp_plan(const FlashArgs &a)
     if (C >= kmax) return pl;
     p.seg_tiles = C;
     p.nseg = (kmax + C - 1) / C;
-    pl.ws_bytes = pairs * p.nseg * (int64_t)(D + 2) * 256 * 4;
+    pl.ws_bytes = items * p.nseg * (int64_t)(D + 2) * 256 * 4;
     return pl;
 }
 
@@ -952,16 +974,15 @@ template <int D, bool SPLIT, int LAYOUT, bool ROT, bool FULL, typename E>
 int launch(const PPParams &p, hipStream_t stream)
 {
     constexpr int BN = ROPE_PP_BN;
-    const int npair = (p.n_qt + 1) / 2;
-    const int64_t blocks = (int64_t)p.BH * npair * (SPLIT ? p.nseg : 1);
-    if (!rope_grid_fits(blocks, 512) || !rope_grid_fits((int64_t)p.BH * npair * (D / 8), 256))
-        return ROPE_LAUNCH_SHAPE;
+    const int64_t items = (int64_t)p.n_hg * p.n_rb;
+    const int64_t blocks = items * (SPLIT ? p.nseg : 1);
+    if (!rope_grid_fits(blocks, 512) || !rope_grid_fits(items * (D / 8), 256)) return ROPE_LAUNCH_SHAPE;
     hipLaunchKernelGGL((flash_fwd_pp_kernel<D, BN, pp_ping<D>(), SPLIT, LAYOUT, ROT, FULL, E>), dim3((unsigned)blocks),
                        dim3(512), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     if (SPLIT) {
-        hipLaunchKernelGGL((flash_pp_merge_kernel<D, BN, E>), dim3((unsigned)((int64_t)p.BH * npair * (D / 8))),
-                           dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((flash_pp_merge_kernel<D, BN, E>), dim3((unsigned)(items * (D / 8))), dim3(256), 0,
+                           stream, p);
         if (hipGetLastError() != hipSuccess) return ROPE_LAUNCH_ERR;
     }
     return ROPE_LAUNCH_OK;
@@ -1004,8 +1025,17 @@ int rope_launch_flash_pp(const FlashArgs &a, hipStream_t stream)
     return a.dtype == 2 ? launch_d<128, _Float16>(a, stream) : launch_d<128, __bf16>(a, stream);
 }
 
+// H_kv == 0: the key/value head count is not known yet; the bytes then
+// cover every head grouping a divisor of H can give.
 int64_t rope_flash_pp_workspace_bytes(const FlashArgs &a)
 {
     if (a.head_dim != 128 || (a.dtype != 0 && a.dtype != 2)) return 0;
-    return pp_plan<128>(a).ws_bytes;
+    if (a.H_kv > 0) return pp_plan<128>(a).ws_bytes;
+    int64_t most = 0;
+    for (int g = 0; g <= 3; ++g)
+        if (a.H % (1 << g) == 0) {
+            const int64_t b = pp_plan<128>(a, g).ws_bytes;
+            most = b > most ? b : most;
+        }
+    return most;
 }

@@ -351,6 +351,39 @@ def test_fused_gqa_full(orc, case):
     assert np.abs(got - want).max() <= (BF16_TOL if dtype == "bf16" else F32_TOL)
 
 
+# Head dim 128 puts G query heads of one key/value head in a workgroup (G
+# the largest of 1, 2, 4, 8 dividing H / H_kv), each over the same block of
+# 256 / G query rows, so one staged key tile serves G heads.
+HEAD_GROUP_CASES = [
+    # (B, H, H_kv, Sq, Sk, layout, q_off, causal)
+    (1, 8, 4, 300, 300, "neox", 0, True),      # 2 query heads per key head: G = 2, 128-row blocks
+    (1, 8, 1, 200, 333, "gptj", 133, True),    # 8 per key head: G = 8, 32-row blocks, offset mask
+    (2, 6, 2, 260, 260, "neox", 0, True),      # 3 per key head: G = 1
+    (1, 12, 2, 150, 420, "gptj", 270, True),   # 6 per key head: G = 2
+    (1, 16, 2, 100, 100, "neox", 0, False),    # 8 per key head, no mask
+]
+
+
+@pytest.mark.parametrize("case", HEAD_GROUP_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_head_groups_full(orc, case):
+    """Query heads grouped per key/value head, with the split-key workspace
+    and without it: every output vs the oracle."""
+    B, H, Hkv, Sq, Sk, layout, qo, causal = case
+    w = wl.AttentionWorkload("head_group", B, H, Sq, Sk, 128, "bf16", 777 + Sq + H, layout, base=1e4,
+                             q_off=qo, causal=causal, H_kv=Hkv)
+    q, k, v = wl.attention_inputs(w)
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    c, s = tables(w.base, w.rot, w.table_rows)
+    want = orc.attention(q, k, v, q_off=qo, rot_dim=w.rot, base=w.base, layout=layout, causal=causal)
+    for ws in ("auto", None):
+        out = torch.full_like(tq, float("nan"))
+        api.flash_attn_fwd(tq, tk, tv, c, s, qo, 0, w.rot, layout, causal, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        got = to64(out)
+        assert np.isfinite(got).all(), ws
+        assert np.abs(got - want).max() <= BF16_TOL, ws
+
+
 @pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "x".join(map(str, c)))
 def test_fused_edge_cases_full(orc, case):
     B, H, Sq, Sk, D, dtype, layout, rot, qo, ko, causal = case
