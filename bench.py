@@ -15,6 +15,9 @@ synchronisations; rank 0 prints ONE JSON line.
                  launches, against 2500 TFLOP/s
   max_abs_err    the timed kernel's output against the fp64 oracle, in the
                  same run (every element)
+  clock          the per-XCD shader clocks amd-smi reports while the bench
+                 workload runs back to back (the 2500 TFLOP/s peak assumes
+                 2400 MHz)
   configs        every workload the target names, each timed the same way
                  with its own roofline fraction and same-run oracle error:
                  the fp32 parity case, the page-shaped 1x8x512x64 GPT-J case,
@@ -152,6 +155,44 @@ def _tdt(torch, dtype):
     return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
+def sample_clock(torch, launch, kernel_ms, busy_s=3.0, delay_s=1.0):
+    """The shader clock under this workload: `amd-smi metric --clock` run as
+    a child process `delay_s` into `busy_s` seconds of back-to-back launches
+    (per-XCD gfx clocks, MHz).  None when amd-smi is missing or fails."""
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    got = {}
+
+    def probe():
+        time.sleep(delay_s)
+        try:
+            r = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
+            d = json.loads(r.stdout)
+            clocks = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
+            got["gfx_mhz"] = [clocks[k]["clk"]["value"] for k in sorted(clocks) if k.startswith("gfx_")]
+        except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+            pass
+
+    t = threading.Thread(target=probe)
+    t.start()
+    t0 = time.perf_counter()
+    n = max(1, int(busy_s * 1e3 / kernel_ms))
+    for i in range(n):
+        launch()
+        if i % 256 == 255 and time.perf_counter() - t0 > busy_s:
+            break
+    torch.cuda.synchronize()
+    t.join()
+    if not got.get("gfx_mhz"):
+        return None
+    return {"gfx_mhz": got["gfx_mhz"], "max_mhz": 2400,
+            "sampled": f"amd-smi metric --clock, {delay_s:.1f} s into back-to-back launches of this workload"}
+
+
 def bench_fused(torch, api, wl, w, steps, warmup):
     dev = torch.device("cuda:0")
     arrays = wl.attention_inputs(w)
@@ -162,9 +203,15 @@ def bench_fused(torch, api, wl, w, steps, warmup):
                                         w.causal)   # the library's default (cached) workspace
     stream = torch.cuda.current_stream(dev)
     ms_step, kernel_ms, durs = time_launches(torch, launch, steps, warmup, stream)
-    return dict(arrays=arrays, q=q, k=k, v=v, cos=cos, sin=sin, out=out, ms_step=ms_step,
+    return dict(arrays=arrays, q=q, k=k, v=v, cos=cos, sin=sin, out=out, launch=launch, ms_step=ms_step,
                 kernel_ms=kernel_ms, p10=durs[len(durs) // 10], p50=durs[len(durs) // 2],
                 p90=durs[(9 * len(durs)) // 10])
+
+
+def device_label(torch):
+    props = torch.cuda.get_device_properties(0)
+    name = torch.cuda.get_device_name(0) or "AMD GPU"
+    return f"{name} ({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)"
 
 
 def sample_rows(w, n_random=40, seed=0):
@@ -530,7 +577,7 @@ def main():
               "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
                          "layout": w.layout, "rope_base": w.base, "rot_dim": w.rot,
                          "q_pos_offset": w.q_off, "k_pos_offset": w.k_off, "causal": w.causal,
-                         "accumulate": "fp32", "device": torch.cuda.get_device_name(0)}}
+                         "accumulate": "fp32", "device": device_label(torch)}}
 
     if args.only in ("all", "fused"):
         r = bench_fused(torch, api, wl, w, args.steps, args.warmup)
@@ -549,6 +596,8 @@ def main():
                               "algorithmic_flops": flops}
         if w.name in PAGE_ROPE_MS:
             result["vs_baseline"] = round(PAGE_ROPE_MS[w.name] / r["ms_step"], 2)
+        if args.only == "all":
+            result["clock"] = sample_clock(torch, r["launch"], r["kernel_ms"])
         if orc is not None:
             result["max_abs_err"], result["err_checked"] = fused_error(orc, w, r)
         del r
