@@ -247,7 +247,7 @@ def fused_error(orc, w, r, full_pairs_limit=2 * 10 ** 8):
     return float(np.abs(g - want).max()), f"{len(rows)} sampled rows"
 
 
-def fused_entry(torch, api, wl, orc, w, config, steps, warmup, comparators_too=False):
+def fused_entry(torch, api, wl, orc, w, config, steps, warmup, comparators_too=False, clock=False):
     r = bench_fused(torch, api, wl, w, steps, warmup)
     flops = w.flops()
     tf = flops / (r["kernel_ms"] * 1e-3) / 1e12
@@ -265,6 +265,8 @@ def fused_entry(torch, api, wl, orc, w, config, steps, warmup, comparators_too=F
          "max_abs_err": err, "err_checked": checked, "tolerance": 1e-5 if f32 else 2e-2}
     if comparators_too:
         e["comparators"] = comparators(torch, api, wl, w, r, max(steps // 2, 10), warmup)
+    if clock:
+        e["clock"] = sample_clock(torch, r["launch"], r["kernel_ms"])
     return e
 
 
@@ -611,7 +613,7 @@ def main():
                                               args.rope_sets)
         ra["frac_of_ceiling"] = round(ra["value"] / ra["ceiling_gbs"], 4)
         configs.append(ra)
-        configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_OFFSET, 5, args.steps, args.warmup))
+        configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_OFFSET, 5, args.steps, args.warmup, clock=True))
         configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_GQA, "5-gqa", args.steps, args.warmup))
         result["configs"] = configs
         # the headline workload with fp16 storage (the fp16 matrix cores)
