@@ -35,21 +35,22 @@
 //   * Q: each lane loads its query row's dims straight into the matrix-core
 //     operand layout, rotates them in fp32 at q_off + i, multiplies by
 //     scale*log2(e), rounds to bf16 and keeps the tile in registers.
-//   * K: every visited tile is loaded from HBM once, rotated in fp32 at its
-//     key positions, rounded to bf16 and written to LDS -- rotated once per
-//     staging, never written back to HBM ("RoPE + PoPE Attention Kernels":
-//     recompute instead of materialising rotated [B,H,S,D] tensors).  V is
-//     copied unrotated, row-major, to LDS.  Two LDS buffers per group: tile
-//     t+NG is fetched into registers while tile t is consumed, then written
-//     to the other buffer; one barrier per tile.
-//   * S' = K Q'^T - m on v_mfma_f32_32x32x16_bf16, the accumulator seeded
-//     with the running max: a lane owns one query column, so row max / row
-//     sum are in-lane plus one v_permlane32_swap, and the exponent needs no
-//     per-score arithmetic: P = exp2(S').
-//   * The max is lazily refreshed: only when a row's new scores exceed its
-//     reference by more than 2^8 (or on its first visible key) is the
-//     reference raised and O, l rescaled -- exact in real arithmetic since
-//     numerator and denominator share the reference.
+//   * K: every visited tile is loaded from HBM once (into registers, a tile
+//     ahead), rotated in fp32 at its key positions, rounded to bf16 and
+//     written to LDS -- rotated once per staging, never written back to HBM
+//     ("RoPE + PoPE Attention Kernels": recompute instead of materialising
+//     rotated [B,H,S,D] tensors).  V goes unrotated from HBM straight into
+//     LDS (buffer loads with the LDS bit), row-major with swizzled 16-byte
+//     chunks.  Two K and two V buffers per group; one barrier per tile.
+//   * S = K Q'^T on v_mfma_f32_32x32x16_bf16: a lane owns one query column,
+//     so row max / row sum are in-lane plus one v_permlane32_swap.
+//     P = exp2(S - m) against a per-row reference m that stays 0 while the
+//     row's scores (log2 units) lie in [-64, 8], so the common path needs
+//     no per-score subtraction.
+//   * The reference is raised lazily: only when a row's scores exceed it by
+//     more than 8 (or its first visible scores all lie below -64) is it
+//     raised to the row max and O, l rescaled -- exact in real arithmetic
+//     since numerator and denominator share the reference.
 //   * P is rounded to bf16; its row sums use v_dot2_f32_bf16 on those same
 //     bf16 values, so numerator and denominator see identical weights.  P
 //     leaves the accumulator already in the B-operand layout of
