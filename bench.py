@@ -18,12 +18,19 @@ synchronisations; rank 0 prints ONE JSON line.
   clock          the per-XCD shader clocks amd-smi reports while the bench
                  workload runs back to back (the 2500 TFLOP/s peak assumes
                  2400 MHz)
+  loop_ceiling   the attention inner step alone (scores, exponentials, row
+                 sums, P V on LDS-resident tiles, no global traffic, rotation
+                 or barriers; librope_calib.so) in every built variant; its
+                 best rate per head dim is what a kernel running that step
+                 can reach here, and each bf16 forward roofline carries
+                 frac_of_loop_ceiling beside frac
   configs        every workload the target names, each timed the same way
                  with its own roofline fraction and same-run oracle error:
                  the fp32 parity case, the page-shaped 1x8x512x64 GPT-J case,
                  the 1x8xSx64 NeoX sweep, the ragged rope_apply batch (with
-                 the in-place streaming ceiling of the same bytes on this
-                 GPU) and the 2048 x 16384 chunked prefill with its query
+                 ceiling_gbs: librope_calib.so's in-place stream of the same
+                 rotated spans, read and written once, and the same bytes
+                 contiguous) and the 2048 x 16384 chunked prefill with its query
                  offset (plus its 8-key/value-head variant); the six
                  page-shaped workloads also carry the comparators below
   comparators    context rows mirroring "RoPE + PoPE Attention Kernels"'
@@ -77,11 +84,12 @@ def parse_args():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config list")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--bwd-steps", type=int, default=30)
-    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "backward", "copy"],
+    ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "backward", "copy", "ceilings"],
                     default="all",
                     help="restrict the timed kernels (for profiler runs): 'fused' times only "
                          "--workload; 'copy' runs only a plain 256 MiB device copy, the "
-                         "calibration for HBM byte counters")
+                         "calibration for HBM byte counters; 'ceilings' only the measurement "
+                         "kernels (attention inner step, in-place stream)")
     return ap.parse_args()
 
 
@@ -320,18 +328,62 @@ def bench_rope_apply(torch, api, wl, steps, sets, orc=None, w=None):
     return res
 
 
-def streaming_ceiling(torch, nbytes, steps, sets):
-    """An in-place streaming pass over `nbytes` of HBM traffic (nbytes/2 read
-    and written back by torch's own elementwise kernel), cycling `sets`
-    buffers as the rope_apply timing does: what a plain kernel moving the
-    same bytes reaches on this GPU."""
+def streaming_ceiling(torch, w, steps, sets, row_vecs=None, span_vecs=None):
+    """The in-place stream of librope_calib.so over rope_apply's footprint on
+    workload w: each 16-byte vector of the rotated span of every head row
+    read and written back once (row_vecs / span_vecs: the head row and its
+    rotated span in vectors; equal values stream a contiguous range of the
+    same size), cycling `sets` buffers as the rope_apply timing does.  GB/s
+    of read + written bytes: what a plain kernel moving the same bytes the
+    same way reaches on this GPU."""
+    from rotary_position_embedding_rope_amd import calib
     dev = torch.device("cuda:0")
-    n = nbytes // 4   # bf16 elements: 2 bytes read + 2 written each
-    bufs = [torch.ones(n, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    esz = 2 if w.dtype in ("bf16", "f16") else 4
+    row = row_vecs or w.D * esz // 16
+    span = span_vecs or w.rot_dim * esz // 16
+    n_vec = w.n_tokens * (w.H_q + w.H_kv) * (w.rot_dim * esz // 16)
+    words = -(-n_vec // span) * row * 4
+    bufs = [torch.zeros(words, dtype=torch.int32, device=dev) for _ in range(sets)]
     stream = torch.cuda.current_stream(dev)
-    _, ms, _ = time_launches(torch, None, steps, sets, stream, rotate=lambda i: bufs[i % sets].mul_(1.0))
+    _, ms, _ = time_launches(torch, None, steps, sets, stream,
+                             rotate=lambda i: calib.stream_inplace(bufs[i % sets], n_vec, row, span, stream))
     del bufs
-    return round(4 * n / (ms * 1e-3) / 1e9, 1)
+    return round(32 * n_vec / (ms * 1e-3) / 1e9, 1)
+
+
+def loop_ceilings(torch, iters=512, launches=5):
+    """Every variant of the attention inner-step kernel of librope_calib.so
+    (scores, exponentials, row sums, P V on LDS-resident tiles; no global
+    traffic, rotation or barriers), one workgroup per CU, timed with a HIP
+    event pair around `launches` launches: TFLOP/s, fraction of the bf16
+    peak and ns per 32-row x 64-key wave tile per SIMD.  The best rate per
+    head dim bounds what any kernel running this step reaches here."""
+    import numpy as np
+    from rotary_position_embedding_rope_amd import calib
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    rng = np.random.default_rng(7)
+    rows, best = [], {}
+    for D, wps, pipe in calib.LOOP_VARIANTS:
+        n_k, n_v, n_q, n_out, _ = calib.loop_shapes(D, wps, wgs)
+        kt, vt, qt = (torch.from_numpy(rng.normal(0, 0.25, n).astype(np.float32)).to(torch.bfloat16).to(dev)
+                      for n in (n_k, n_v, n_q))
+        out = torch.empty(n_out, dtype=torch.float32, device=dev)
+
+        def launch():
+            calib.attn_loop(D, wps, pipe, iters, wgs, kt, vt, qt, out, stream=stream)
+
+        _, ms, _ = time_launches(torch, launch, launches, 1, stream)
+        flops = 4.0 * 64 * 32 * D * iters * 4 * wps * wgs
+        tf = flops / (ms * 1e-3) / 1e12
+        ns_tile = ms * 1e6 / (iters * wps)
+        rows.append({"head_dim": D, "waves_per_simd": wps, "pipelined": bool(pipe), "tflops": round(tf, 1),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "ns_per_wave_tile_per_simd": round(ns_tile, 1)})
+        best[D] = max(best.get(D, 0.0), tf)
+        del kt, vt, qt, out
+    return {"variants": rows, "best_tflops": {str(d): round(t, 1) for d, t in best.items()},
+            "iters": iters, "workgroups": wgs}
 
 
 def bench_backward(torch, api, wl, orc, steps, warmup):
@@ -568,6 +620,13 @@ def main():
     if args.only == "copy":
         print(json.dumps(copy_calibration(torch, args.steps)), flush=True)
         return
+    if args.only == "ceilings":
+        out = {"loop_ceiling": loop_ceilings(torch),
+               "stream_half_row_gbs": streaming_ceiling(torch, wl.RAGGED_ROPE, args.rope_steps, args.rope_sets),
+               "stream_contiguous_gbs": streaming_ceiling(torch, wl.RAGGED_ROPE, args.rope_steps, args.rope_sets,
+                                                          row_vecs=8, span_vecs=8)}
+        print(json.dumps(out), flush=True)
+        return
     orc = None
     if args.only == "all":
         import oracle
@@ -600,6 +659,11 @@ def main():
             result["vs_baseline"] = round(PAGE_ROPE_MS[w.name] / r["ms_step"], 2)
         if args.only == "all":
             result["clock"] = sample_clock(torch, r["launch"], r["kernel_ms"])
+            result["loop_ceiling"] = loop_ceilings(torch)
+            best = result["loop_ceiling"]["best_tflops"].get(str(w.D))
+            if best and w.dtype != "f32":
+                result["roofline"]["loop_ceiling_tflops"] = best
+                result["roofline"]["frac_of_loop_ceiling"] = round(achieved / best, 4)
         if orc is not None:
             result["max_abs_err"], result["err_checked"] = fused_error(orc, w, r)
         del r
@@ -609,12 +673,21 @@ def main():
         for x in wl.SWEEP_BF16:
             configs.append(fused_entry(torch, api, wl, orc, x, 3, args.steps, args.warmup, True))
         ra = bench_rope_apply(torch, api, wl, args.rope_steps, args.rope_sets, orc)
-        ra["ceiling_gbs"] = streaming_ceiling(torch, wl.RAGGED_ROPE.algorithmic_bytes(), args.rope_steps,
-                                              args.rope_sets)
+        ra["ceiling_gbs"] = streaming_ceiling(torch, wl.RAGGED_ROPE, args.rope_steps, args.rope_sets)
+        ra["ceiling_contiguous_gbs"] = streaming_ceiling(torch, wl.RAGGED_ROPE, args.rope_steps, args.rope_sets,
+                                                         row_vecs=8, span_vecs=8)
         ra["frac_of_ceiling"] = round(ra["value"] / ra["ceiling_gbs"], 4)
         configs.append(ra)
         configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_OFFSET, 5, args.steps, args.warmup, clock=True))
         configs.append(fused_entry(torch, api, wl, orc, wl.PREFILL_GQA, "5-gqa", args.steps, args.warmup))
+        best = result.get("loop_ceiling", {}).get("best_tflops", {})
+        for e in configs:
+            if e.get("unit") == "TFLOP/s" and e.get("dtype") != "f32":
+                d = {x.name: x for x in wl.ATTENTION_WORKLOADS}.get(e["workload"])
+                ceil = best.get(str(d.D)) if d is not None else None
+                if ceil:
+                    e["roofline"]["loop_ceiling_tflops"] = ceil
+                    e["roofline"]["frac_of_loop_ceiling"] = round(e["value"] / ceil, 4)
         result["configs"] = configs
         # the headline workload with fp16 storage (the fp16 matrix cores)
         wf = wl.HEADLINE_F16

@@ -1,7 +1,10 @@
-"""Compile the HIP sources of this package into ``librope_mi355x.so`` for gfx950.
+"""Compile the HIP sources of this package for gfx950.
 
 Every ``csrc/*.hip`` file and ``csrc/abi.cpp`` is compiled by hipcc in
-parallel, then linked into one shared library next to this file.  Packed fp32
+parallel, then linked into ``librope_mi355x.so`` next to this file (the
+library of include/rope_mi355x.h).  ``calib/calib.hip`` becomes
+``librope_calib.so`` (include/rope_calib.h): measurement kernels the
+benchmark times beside the library's, not part of it.  Packed fp32
 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -18,6 +21,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "librope_mi355x.so"
+CALIB_SOURCE = PKG / "calib" / "calib.hip"
+CALIB_LIBRARY = PKG / "librope_calib.so"
 BUILD_DIR = PKG / "_build"
 
 ARCH = "gfx950"
@@ -61,18 +66,25 @@ def _compile(src: Path) -> Path:
     return obj
 
 
-def build(jobs: int | None = None) -> Path:
-    """Compile and link the library; returns its path.  Always rebuilds."""
-    BUILD_DIR.mkdir(exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=jobs or min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIBRARY.with_name(LIBRARY.name + f".tmp{os.getpid()}")
+def _link(objs: list[Path], library: Path) -> Path:
+    tmp = library.with_name(library.name + f".tmp{os.getpid()}")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, library)
+    return library
+
+
+def build(jobs: int | None = None) -> Path:
+    """Compile and link both libraries; returns the path of the RoPE
+    library.  Always rebuilds."""
+    BUILD_DIR.mkdir(exist_ok=True)
+    srcs = sources() + [CALIB_SOURCE]
+    with ThreadPoolExecutor(max_workers=jobs or min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIBRARY)
+    _link(objs[-1:], CALIB_LIBRARY)
     return LIBRARY
 
 

@@ -1,0 +1,69 @@
+"""The measurement library (librope_calib.so) on the CPU: it loads, exports
+every symbol include/rope_calib.h declares, its status codes match the
+header, and invalid arguments come back as status codes before any HIP call
+(no kernel is launched here)."""
+import re
+from pathlib import Path
+
+import pytest
+
+from rotary_position_embedding_rope_amd import calib
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "rope_calib.h"
+FAKE = 1 << 42   # a fake device address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return calib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    body = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(rope_[a-z_0-9]+)\s*\(", body)))
+    assert names == sorted(calib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_header():
+    codes = dict((m.group(1), int(m.group(2)))
+                 for m in re.finditer(r"#define (ROPE_CALIB_\w+) (\d+)", HEADER.read_text()))
+    assert codes == {"ROPE_CALIB_OK": calib.OK, "ROPE_CALIB_ERR_NULL": calib.ERR_NULL,
+                     "ROPE_CALIB_ERR_SHAPE": calib.ERR_SHAPE, "ROPE_CALIB_ERR_HIP": calib.ERR_HIP}
+
+
+@pytest.mark.parametrize("buf,n,row,span,want", [
+    (None, 16, 16, 8, calib.ERR_NULL),
+    (FAKE, 0, 16, 8, calib.ERR_SHAPE),        # nothing to move
+    (FAKE, 16, 16, 32, calib.ERR_SHAPE),      # span wider than the row
+    (FAKE, 16, 12, 4, calib.ERR_SHAPE),       # row not a power of two
+    (FAKE, 16, 16, 6, calib.ERR_SHAPE),       # span not a power of two
+    (FAKE, 16, 1 << 21, 8, calib.ERR_SHAPE),  # row beyond 2^20 vectors
+    (FAKE + 8, 16, 16, 8, calib.ERR_SHAPE),   # not 16-byte aligned
+    (FAKE, 1 << 40, 16, 8, calib.ERR_SHAPE),  # grid past 2^32 - 1 work-items
+])
+def test_stream_rejects(lib, buf, n, row, span, want):
+    assert lib.rope_calib_stream_inplace(buf, n, row, span, None) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((64, 2, 0, 8, 1, None, FAKE, FAKE, FAKE), calib.ERR_NULL),
+    ((64, 2, 0, 8, 1, FAKE, FAKE, FAKE, None), calib.ERR_NULL),
+    ((64, 2, 0, 7, 1, FAKE, FAKE, FAKE, FAKE), calib.ERR_SHAPE),    # odd iteration count
+    ((64, 2, 0, 0, 1, FAKE, FAKE, FAKE, FAKE), calib.ERR_SHAPE),
+    ((64, 2, 0, 8, 0, FAKE, FAKE, FAKE, FAKE), calib.ERR_SHAPE),    # no workgroup
+    ((96, 2, 0, 8, 1, FAKE, FAKE, FAKE, FAKE), calib.ERR_SHAPE),    # head dim not built
+    ((64, 5, 0, 8, 1, FAKE, FAKE, FAKE, FAKE), calib.ERR_SHAPE),    # more waves than built
+    ((128, 3, 0, 8, 1, FAKE, FAKE, FAKE, FAKE), calib.ERR_SHAPE),
+])
+def test_loop_rejects(lib, args, want):
+    assert lib.rope_calib_attn_loop(*args, None, None) == want
+
+
+def test_variant_list_matches_the_built_kernels():
+    # every (head dim, waves per SIMD) pair the launcher takes, both schedules
+    assert sorted({(d, w) for d, w, _ in calib.LOOP_VARIANTS}) == \
+        [(64, 1), (64, 2), (64, 3), (64, 4), (128, 1), (128, 2)]
+    assert all(sum(1 for v in calib.LOOP_VARIANTS if v[:2] == dw) == 2
+               for dw in {(d, w) for d, w, _ in calib.LOOP_VARIANTS})
