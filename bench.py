@@ -82,6 +82,7 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config list")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi shader-clock sample")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--bwd-steps", type=int, default=30)
     ap.add_argument("--only", choices=["all", "fused", "rope_apply", "decode", "backward", "copy", "ceilings"],
@@ -163,13 +164,25 @@ def _tdt(torch, dtype):
     return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
+CLOCK_OFF = False   # --no-clock
+
+
+def under_profiler() -> bool:
+    """True inside rocprofv3, whose preloaded tool would also load into (and
+    initialise the GPU in) any child process bench.py starts."""
+    return any(k.startswith("ROCPROF") for k in os.environ) or "rocprofiler" in os.environ.get("LD_PRELOAD", "")
+
+
 def sample_clock(torch, launch, kernel_ms, busy_s=3.0, delay_s=1.0):
     """The shader clock under this workload: `amd-smi metric --clock` run as
     a child process `delay_s` into `busy_s` seconds of back-to-back launches
-    (per-XCD gfx clocks, MHz).  None when amd-smi is missing or fails."""
+    (per-XCD gfx clocks, MHz).  None when amd-smi is missing or fails, with
+    --no-clock, and under a profiler (no child process is started there)."""
     import shutil
     import subprocess
     import threading
+    if CLOCK_OFF or under_profiler():
+        return None
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
@@ -606,6 +619,8 @@ def cpu_baseline(wl, w, seconds):
 
 def main():
     args = parse_args()
+    global CLOCK_OFF
+    CLOCK_OFF = args.no_clock
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: this library has no multi-GPU path; "

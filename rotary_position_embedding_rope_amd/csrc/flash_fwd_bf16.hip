@@ -18,11 +18,12 @@
 //     the query range, a light and a heavy one, so all workgroups see about
 //     the same number of key tiles (the causal triangle is folded instead of
 //     leaving the last query tiles as the critical path); otherwise they are
-//     128 consecutive rows.  NG key groups of 4 waves each (NG = 1 or 2) walk
-//     interleaved key tiles and are merged through LDS at the end.  With
-//     NG = 2 every SIMD runs two waves, one per half, so one wave's softmax
-//     overlaps the other's matrix-core work and the heavy half's tiles are
-//     spread over all four SIMDs;
+//     128 consecutive rows.  Two key groups of 4 waves walk interleaved key
+//     tiles over the same rows and are merged through LDS at the end, each
+//     group merging and storing one 32-dim half of O.  Every SIMD runs two
+//     waves, one per half, so one wave's softmax overlaps the other's
+//     matrix-core work and the heavy half's tiles are spread over all four
+//     SIMDs;
 //   * in each group a wave owns 32 query rows; the key loop stops at the
 //     last tile a query of the workgroup can see, tiles past a wave's last
 //     query are skipped by that wave (it keeps staging for the others), and
@@ -32,9 +33,12 @@
 //     count), so a head's K/V stay in one L2.
 //
 // Data path of a group:
-//   * Q: each lane loads its query row's dims straight into the matrix-core
-//     operand layout, rotates them in fp32 at q_off + i, multiplies by
-//     scale*log2(e), rounds to bf16 and keeps the tile in registers.
+//   * Q: in group 0 each lane loads its query row's dims straight into the
+//     matrix-core operand layout, rotates them in fp32 at q_off + i,
+//     multiplies by scale*log2(e), rounds to bf16 and keeps the tile in
+//     registers; it also leaves it in LDS, where the group-1 wave holding
+//     the same rows picks it up after the first barrier (each query row is
+//     loaded and rotated once per workgroup).
 //   * K: every visited tile is loaded from HBM once (into registers, a tile
 //     ahead), rotated in fp32 at its key positions, rounded to bf16 and
 //     written to LDS -- rotated once per staging, never written back to HBM
@@ -236,14 +240,17 @@ void flash_fwd_bf16_kernel(Params p)
     constexpr int KI = (Plan::SLOTS + NST - 1) / NST;   // K slots per thread per tile
     constexpr int DT = D / 16;                      // k-steps of the QK^T product
     constexpr int DB = D / 32;                      // 32-row blocks of O^T
-    constexpr int NC = DB * 16 + 2;                 // per-lane state: O^T accumulators, m, l
     constexpr int NBUF = NG;                        // buffer sets (one per key stream)
     constexpr int NVB = 2;                          // V buffers per set
 
     // [stream][buffer] K tiles, then [stream][buffer] V tiles.  K runs one
     // tile ahead of V: while tile t's probabilities are formed, the scores of
-    // the next tile are computed from the other K buffer.
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF * (2 * K_ELEMS + NVB * V_ELEMS)];
+    // the next tile are computed from the other K buffer.  Then the rotated
+    // query operand of the workgroup's rows, [wave][k-step][lane] 16 bytes
+    // each: group 0 forms it, group 1 (same rows) reads it.
+    constexpr int KV_ELEMS = NBUF * (2 * K_ELEMS + NVB * V_ELEMS);
+    constexpr int QX_ELEMS = WAVES_PER_GROUP * DT * 64 * 8;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[KV_ELEMS + QX_ELEMS];
 
     const int tid = threadIdx.x;
     // group and wave are uniform across a wave; saying so keeps every
@@ -481,58 +488,64 @@ void flash_fwd_bf16_kernel(Params p)
             if (T(1) < tend) fetch_k(T(1), kpa, pr0, pr1, pc, ps);
 
             // ---- Q: load, rotate, scale, keep as MFMA B operand ----
-            const int64_t qleft = p.Sq - wq0;
-            const rsrc_t qrs = make_rsrc<2 * D>(qh + wq0 * D, (int)(qleft < 0 ? 0 : (qleft > 32 ? 32 : qleft)));
-            float qv[DT][8];
+            // Group 0 only: group 1 holds the same rows (its wave w those of
+            // group 0's wave w ^ 2) and reads the operand from LDS after
+            // the first barrier.
+            if (group == 0) {
+                const int64_t qleft = p.Sq - wq0;
+                const rsrc_t qrs = make_rsrc<2 * D>(qh + wq0 * D, (int)(qleft < 0 ? 0 : (qleft > 32 ? 32 : qleft)));
+                float qv[DT][8];
 #pragma unroll
-            for (int t = 0; t < DT; ++t) unpack8<E>(bload16(qrs, 2 * (l32 * D + 16 * t + 8 * hh)), qv[t]);
-            if constexpr (ROT) {
-                const int64_t tleft = p.table_rows - (p.q_off + wq0);
-                const int trows = (int)(tleft < 0 ? 0 : (tleft > 32 ? 32 : tleft)) * (rh / 4);
-                const rsrc_t qcs = make_rsrc<16>(p.cos_tab + (p.q_off + wq0) * rh, trows);
-                const rsrc_t qss = make_rsrc<16>(p.sin_tab + (p.q_off + wq0) * rh, trows);
-                const int tb = 4 * l32 * rh;   // byte offset of this lane's table row
-                if constexpr (LAYOUT == 0) {
-                    // lane holds dims 16t + 8hh + s; the partner of
-                    // 16t+8hh+s is 16(t + rot/32) + 8hh + s, in the same
-                    // lane (rot_dim is a multiple of 32: tr <= DT/2).
-                    const int tr = p.rot_dim / 32;
+                for (int t = 0; t < DT; ++t) unpack8<E>(bload16(qrs, 2 * (l32 * D + 16 * t + 8 * hh)), qv[t]);
+                if constexpr (ROT) {
+                    const int64_t tleft = p.table_rows - (p.q_off + wq0);
+                    const int trows = (int)(tleft < 0 ? 0 : (tleft > 32 ? 32 : tleft)) * (rh / 4);
+                    const rsrc_t qcs = make_rsrc<16>(p.cos_tab + (p.q_off + wq0) * rh, trows);
+                    const rsrc_t qss = make_rsrc<16>(p.sin_tab + (p.q_off + wq0) * rh, trows);
+                    const int tb = 4 * l32 * rh;   // byte offset of this lane's table row
+                    if constexpr (LAYOUT == 0) {
+                        // lane holds dims 16t + 8hh + s; the partner of
+                        // 16t+8hh+s is 16(t + rot/32) + 8hh + s, in the same
+                        // lane (rot_dim is a multiple of 32: tr <= DT/2).
+                        const int tr = p.rot_dim / 32;
 #pragma unroll
-                    for (int t = 0; t < DT / 2; ++t) {
-                        if (t < tr) {
-                            const int f0 = 4 * (16 * t + 8 * hh);
-                            float c[8], s[8];
-                            *reinterpret_cast<float4 *>(c) = bload16f(qcs, tb + f0);
-                            *reinterpret_cast<float4 *>(c + 4) = bload16f(qcs, tb + f0 + 16);
-                            *reinterpret_cast<float4 *>(s) = bload16f(qss, tb + f0);
-                            *reinterpret_cast<float4 *>(s + 4) = bload16f(qss, tb + f0 + 16);
-                            // registers are only indexed with compile-time constants
+                        for (int t = 0; t < DT / 2; ++t) {
+                            if (t < tr) {
+                                const int f0 = 4 * (16 * t + 8 * hh);
+                                float c[8], s[8];
+                                *reinterpret_cast<float4 *>(c) = bload16f(qcs, tb + f0);
+                                *reinterpret_cast<float4 *>(c + 4) = bload16f(qcs, tb + f0 + 16);
+                                *reinterpret_cast<float4 *>(s) = bload16f(qss, tb + f0);
+                                *reinterpret_cast<float4 *>(s + 4) = bload16f(qss, tb + f0 + 16);
+                                // registers are only indexed with compile-time constants
 #pragma unroll
-                            for (int u = 1; u <= DT / 2; ++u)
-                                if (u == tr) rotate_pairs<8>(qv[t], qv[t + u], c, s);
+                                for (int u = 1; u <= DT / 2; ++u)
+                                    if (u == tr) rotate_pairs<8>(qv[t], qv[t + u], c, s);
+                            }
                         }
-                    }
-                } else {
+                    } else {
 #pragma unroll
-                    for (int t = 0; t < DT; ++t) {
-                        if (16 * t < p.rot_dim) {
-                            const int f0 = 4 * (8 * t + 4 * hh);
-                            float c[4], s[4], a[4], b[4];
-                            *reinterpret_cast<float4 *>(c) = bload16f(qcs, tb + f0);
-                            *reinterpret_cast<float4 *>(s) = bload16f(qss, tb + f0);
+                        for (int t = 0; t < DT; ++t) {
+                            if (16 * t < p.rot_dim) {
+                                const int f0 = 4 * (8 * t + 4 * hh);
+                                float c[4], s[4], a[4], b[4];
+                                *reinterpret_cast<float4 *>(c) = bload16f(qcs, tb + f0);
+                                *reinterpret_cast<float4 *>(s) = bload16f(qss, tb + f0);
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) { a[u] = qv[t][2 * u]; b[u] = qv[t][2 * u + 1]; }
-                            rotate_pairs<4>(a, b, c, s);
+                                for (int u = 0; u < 4; ++u) { a[u] = qv[t][2 * u]; b[u] = qv[t][2 * u + 1]; }
+                                rotate_pairs<4>(a, b, c, s);
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) { qv[t][2 * u] = a[u]; qv[t][2 * u + 1] = b[u]; }
+                                for (int u = 0; u < 4; ++u) { qv[t][2 * u] = a[u]; qv[t][2 * u + 1] = b[u]; }
+                            }
                         }
                     }
                 }
-            }
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
+                for (int t = 0; t < DT; ++t) {
 #pragma unroll
-                for (int s = 0; s < 8; ++s) qf[t][s] = (E)(qv[t][s] * p.sl2);
+                    for (int s = 0; s < 8; ++s) qf[t][s] = (E)(qv[t][s] * p.sl2);
+                    *reinterpret_cast<v8 *>(lds + KV_ELEMS + ((wave * DT + t) * 64 + lane) * 8) = qf[t];
+                }
             }
             if (T(0) < tend) stage_k(0, kpa, kr0, kr1, kc, ks);
             if (T(1) < tend) stage_k(1, kpa, pr0, pr1, pc, ps);
@@ -738,6 +751,11 @@ void flash_fwd_bf16_kernel(Params p)
         wait_dma();   // V(0)
         if (j_split > 0) fetch_next(0);
         __syncthreads();
+        if (group == 1) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+                qf[t] = *reinterpret_cast<const v8 *>(lds + KV_ELEMS + (((wave ^ 2) * DT + t) * 64 + lane) * 8);
+        }
         // scores S[j & 1] of tile j
         f32x16_t S0[NKB], S1[NKB];
         if (j_end > 0) qk(0, S0);
@@ -876,56 +894,61 @@ void flash_fwd_bf16_kernel(Params p)
         __syncthreads();   // all tiles consumed
 
         // ---- per-segment epilogue ----
-        float l_tot = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
-        float m_fin = m_set ? m_ref : -INFINITY;
+        // The two groups hold the same rows (group 1's wave w those of group
+        // 0's wave w ^ 2) over alternate key tiles.  Each group merges and
+        // stores one 32-dim block of O (group g block g): it hands the other
+        // block with its (m, l) to the partner wave through LDS, and both
+        // form the merged (m, l) by the same expression, so both halves of a
+        // row divide by the same l.
+        static_assert(DB == 2, "one 32-dim block of O per group");
+        const float l_own = sum_with_partner((l_acc[0] + l_acc[1]) + (l_acc[2] + l_acc[3]));
+        const float m_own = m_set ? m_ref : -INFINITY;
         float *xfer = reinterpret_cast<float *>(lds);
+        const int pair = group == 0 ? wave : (wave ^ 2);   // group 0's wave of these rows
+        constexpr int NX = 16 + 2;                         // floats handed over per lane
         {
-            // group 1 hands its state to group 0 through LDS: per wave, per
-            // lane, DB*16 accumulators + m + l, component-major.
-            if (group == 1) {
-                float *dst = xfer + (wave ^ 2) * NC * 64 + lane;   // the rows of group 0's wave ^ 2
+            float *dst = xfer + ((group * WAVES_PER_GROUP + pair) * NX) * 64 + lane;
 #pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[(b * 16 + r) * 64] = oacc[b][r];
-                dst[(DB * 16) * 64] = m_fin;
-                dst[(DB * 16 + 1) * 64] = l_tot;
-            }
-            __syncthreads();
-            if (group == 0) {
-                const float *src = xfer + wave * NC * 64 + lane;
-                const float mB = src[(DB * 16) * 64], lB = src[(DB * 16 + 1) * 64];
-                const float m = fmaxf(m_fin, mB);
-                const float aA = m_fin == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_fin - m);
-                const float aB = mB == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mB - m);
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[b][r] = oacc[b][r] * aA + src[(b * 16 + r) * 64] * aB;
-                l_tot = l_tot * aA + lB * aB;
-                m_fin = m;
-            }
+            for (int r = 0; r < 16; ++r) dst[r * 64] = group == 0 ? oacc[1][r] : oacc[0][r];
+            dst[16 * 64] = m_own;
+            dst[17 * 64] = l_own;
         }
+        __syncthreads();
+        const float *src = xfer + (((group ^ 1) * WAVES_PER_GROUP + pair) * NX) * 64 + lane;
+        const float m_oth = src[16 * 64], l_oth = src[17 * 64];
+        // A: group 0's state, B: group 1's
+        const float mA = group == 0 ? m_own : m_oth, mB = group == 0 ? m_oth : m_own;
+        const float lA = group == 0 ? l_own : l_oth, lB = group == 0 ? l_oth : l_own;
+        const float m_fin = fmaxf(mA, mB);
+        const float aA = mA == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mA - m_fin);
+        const float aB = mB == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mB - m_fin);
+        const float l_tot = lA * aA + lB * aB;
+        const float a_own = group == 0 ? aA : aB, a_oth = group == 0 ? aB : aA;
 
-        auto write_out = [&]() {
+        // merge block b of O with the partner's, scale by 1/l, round, store
+        auto merge_store = [&](auto B) {
+            constexpr int b = decltype(B)::value;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[b][r] = oacc[b][r] * a_own + src[r * 64] * a_oth;
             if (!qvalid) return;
             const float inv = 1.f / l_tot;
             uint16_t *orow = p.o + ((int64_t)bh * p.Sq + qrow) * D;
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = 32 * b + 8 * g + 4 * hh;
-                    uint2 wv;
-                    wv.x = TT::pack2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-                    wv.y = TT::pack2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-                    *reinterpret_cast<uint2 *>(orow + d0) = wv;
-                }
-            // scores are in log2 units against the reference m_fin
-            if (p.lse && hh == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_fin + log2f(l_tot)) * LN2;
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * b + 8 * g + 4 * hh;
+                uint2 wv;
+                wv.x = TT::pack2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
+                wv.y = TT::pack2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+                *reinterpret_cast<uint2 *>(orow + d0) = wv;
+            }
         };
-
-        if (group == 0) write_out();
+        if (group == 0) {
+            merge_store(std::integral_constant<int, 0>{});
+            // scores are in log2 units against the reference m_fin
+            if (p.lse && hh == 0 && qvalid) p.lse[(int64_t)bh * p.Sq + qrow] = (m_fin + log2f(l_tot)) * LN2;
+        } else {
+            merge_store(std::integral_constant<int, 1>{});
+        }
     };
 
     // A head's workgroups share an XCD (block index modulo the head count).
