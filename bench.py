@@ -40,7 +40,9 @@ synchronisations; rank 0 prints ONE JSON line.
   cpu_baseline   the fp64 CPU oracle on the same workload (whole heads),
                  timed on this host's cores; single-thread and rope_apply
                  oracle rates beside it
-  backward, decode   the backward step and the decode step (context)
+  backward, decode   the backward step and the decode step (context); the
+                 decode step carries ceiling_gbs, librope_calib.so's
+                 read-only stream over the same number of bytes
 """
 from __future__ import annotations
 
@@ -364,6 +366,22 @@ def streaming_ceiling(torch, w, steps, sets, row_vecs=None, span_vecs=None):
     return round(32 * n_vec / (ms * 1e-3) / 1e9, 1)
 
 
+def read_ceiling(torch, nbytes, steps):
+    """librope_calib.so's read-only stream over `nbytes` (one buffer, larger
+    than the 256 MB last-level cache at the decode step's size): GB/s of a
+    plain kernel reading that many bytes once, the decode step's ceiling."""
+    from rotary_position_embedding_rope_amd import calib
+    dev = torch.device("cuda:0")
+    n_vec = nbytes // 16
+    buf = torch.zeros(4 * n_vec, dtype=torch.int32, device=dev)
+    hit = torch.zeros(1, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    _, ms, _ = time_launches(torch, lambda: calib.stream_read(buf, n_vec, 0x7A5C3E1D, hit, stream), steps,
+                             max(steps // 5, 2), stream)
+    del buf
+    return round(16 * n_vec / (ms * 1e-3) / 1e9, 1)
+
+
 def loop_ceilings(torch, iters=512, launches=5):
     """Every variant of the attention inner-step kernel of librope_calib.so
     (scores, exponentials, row sums, P V on LDS-resident tiles; no global
@@ -499,6 +517,8 @@ def bench_decode(torch, api, wl, orc, steps, warmup):
         res["max_abs_err"] = err
         res["err_checked"] = "every output row of requests 0, 7 and 15"
     del k_cache, v_cache
+    res["ceiling_gbs"] = read_ceiling(torch, nbytes, steps)
+    res["frac_of_ceiling"] = round(gbs / res["ceiling_gbs"], 4)
     return res
 
 
@@ -639,7 +659,8 @@ def main():
         out = {"loop_ceiling": loop_ceilings(torch),
                "stream_half_row_gbs": streaming_ceiling(torch, wl.RAGGED_ROPE, args.rope_steps, args.rope_sets),
                "stream_contiguous_gbs": streaming_ceiling(torch, wl.RAGGED_ROPE, args.rope_steps, args.rope_sets,
-                                                          row_vecs=8, span_vecs=8)}
+                                                          row_vecs=8, span_vecs=8),
+               "stream_read_gbs": read_ceiling(torch, wl.DECODE.algorithmic_bytes(), args.decode_steps)}
         print(json.dumps(out), flush=True)
         return
     orc = None

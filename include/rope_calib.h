@@ -47,6 +47,19 @@ extern "C" {
 int rope_calib_stream_inplace(void *buf, int64_t n_vec, int row_vecs, int span_vecs, void *stream);
 
 /*
+ * rope_calib_stream_read -- read n_vec 16-byte vectors of buf once
+ * (non-temporal loads, one vector per thread), the traffic of a decode step
+ * walking its key/value cache ([RF] section 7).  A vector whose four 32-bit
+ * words all equal `key` writes its index to *hit (several such vectors: one
+ * of their indices); *hit is left alone otherwise.  Reads 16 * n_vec bytes.
+ *
+ *   buf     16-byte aligned, n_vec vectors
+ *   n_vec   > 0 (grid within 2^32 - 1 work-items)
+ *   hit     one int64
+ */
+int rope_calib_stream_read(const void *buf, int64_t n_vec, uint32_t key, int64_t *hit, void *stream);
+
+/*
  * rope_calib_attn_loop -- the inner step of a flash-attention forward with
  * nothing around it ([RF] section 5: scores, exponentials, row sums, P V),
  * repeated `iters` times by every wave on one K tile and one V tile held in

@@ -10,7 +10,7 @@ from pathlib import Path
 
 LIBRARY = Path(__file__).resolve().parent.parent / "librope_calib.so"
 OK, ERR_NULL, ERR_SHAPE, ERR_HIP = 0, 1, 2, 7
-EXPORTS = ("rope_calib_stream_inplace", "rope_calib_attn_loop")
+EXPORTS = ("rope_calib_stream_inplace", "rope_calib_stream_read", "rope_calib_attn_loop")
 # (head dim, waves per SIMD, pipelined) variants the loop kernel is built for
 LOOP_VARIANTS = tuple((64, w, p) for w in (1, 2, 3, 4) for p in (0, 1)) + \
     tuple((128, w, p) for w in (1, 2) for p in (0, 1))
@@ -29,6 +29,8 @@ def load() -> ctypes.CDLL:
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.rope_calib_stream_inplace.argtypes = [vp, i64, i32, i32, vp]
     lib.rope_calib_stream_inplace.restype = i32
+    lib.rope_calib_stream_read.argtypes = [vp, i64, ctypes.c_uint32, vp, vp]
+    lib.rope_calib_stream_read.restype = i32
     lib.rope_calib_attn_loop.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.rope_calib_attn_loop.restype = i32
     _lib = lib
@@ -50,6 +52,18 @@ def stream_inplace(buf, n_vec: int, row_vecs: int, span_vecs: int, stream=None) 
     _check(load().rope_calib_stream_inplace(buf.data_ptr(), n_vec, row_vecs, span_vecs,
                                             None if stream is None else stream.cuda_stream),
            "rope_calib_stream_inplace")
+
+
+def stream_read(buf, n_vec: int, key: int, hit, stream=None) -> None:
+    """Read n_vec 16-byte vectors of the device tensor `buf`; a vector of
+    four words equal to `key` writes its index into the int64 tensor `hit`."""
+    if buf.numel() * buf.element_size() < 16 * n_vec:
+        raise ValueError(f"buffer holds {buf.numel() * buf.element_size()} bytes, the read needs {16 * n_vec}")
+    if hit.numel() < 1 or hit.element_size() != 8:
+        raise ValueError("hit must hold one int64")
+    _check(load().rope_calib_stream_read(buf.data_ptr(), n_vec, key & 0xffffffff, hit.data_ptr(),
+                                         None if stream is None else stream.cuda_stream),
+           "rope_calib_stream_read")
 
 
 def loop_shapes(head_dim: int, waves_per_simd: int, workgroups: int):

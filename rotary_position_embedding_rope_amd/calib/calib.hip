@@ -8,6 +8,10 @@
 //    access pattern of an in-place RoPE that rotates part of each head row
 //    ("Write Triton Rope Kernel", "Performance requirements": the op is a
 //    pure stream of the rotated span, read once and written once).
+//  * stream_read_kernel: a read-only stream of 16-byte vectors (non-temporal
+//    loads, one vector per thread), the access of a decode step walking its
+//    key/value cache once ("RoPE and FlashAttention", section 7: decoding
+//    reads the cached keys and values);
 //  * attn_loop_kernel: the inner step of a flash-attention forward with
 //    nothing around it ("RoPE and FlashAttention", section 5: scores, the
 //    exponentials against a reference, row sums, the P V update), on one K
@@ -44,6 +48,18 @@ __global__ __launch_bounds__(256) void stream_inplace_kernel(u32x4 *buf, int64_t
     u32x4 x = __builtin_nontemporal_load(buf + at);
     x += 1u;
     __builtin_nontemporal_store(x, buf + at);
+}
+
+// Read-only stream: each thread loads one vector; a vector equal to `key`
+// (all four words) writes its index to *hit, so the loads cannot be dropped
+// and a test can find a planted vector.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *buf, int64_t n_vec, uint32_t key,
+                                                          int64_t *hit)
+{
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v >= n_vec) return;
+    const u32x4 x = __builtin_nontemporal_load(buf + v);
+    if (x.x == key && x.y == key && x.z == key && x.w == key) *hit = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -247,6 +263,18 @@ extern "C" int rope_calib_stream_inplace(void *buf, int64_t n_vec, int row_vecs,
     if (blocks > 0xffffffffLL / 256) return ROPE_CALIB_ERR_SHAPE;
     hipLaunchKernelGGL(stream_inplace_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<u32x4 *>(buf), n_vec, rl, sl);
+    return hipGetLastError() == hipSuccess ? ROPE_CALIB_OK : ROPE_CALIB_ERR_HIP;
+}
+
+extern "C" int rope_calib_stream_read(const void *buf, int64_t n_vec, uint32_t key, int64_t *hit,
+                                     void *stream)
+{
+    if (!buf || !hit) return ROPE_CALIB_ERR_NULL;
+    if (n_vec <= 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0) return ROPE_CALIB_ERR_SHAPE;
+    const int64_t blocks = (n_vec + 255) / 256;
+    if (blocks > 0xffffffffLL / 256) return ROPE_CALIB_ERR_SHAPE;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(buf), n_vec, key, hit);
     return hipGetLastError() == hipSuccess ? ROPE_CALIB_OK : ROPE_CALIB_ERR_HIP;
 }
 

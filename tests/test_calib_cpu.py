@@ -47,6 +47,17 @@ def test_stream_rejects(lib, buf, n, row, span, want):
     assert lib.rope_calib_stream_inplace(buf, n, row, span, None) == want
 
 
+@pytest.mark.parametrize("buf,n,hit,want", [
+    (None, 16, FAKE, calib.ERR_NULL),
+    (FAKE, 16, None, calib.ERR_NULL),
+    (FAKE, 0, FAKE, calib.ERR_SHAPE),
+    (FAKE + 4, 16, FAKE, calib.ERR_SHAPE),      # not 16-byte aligned
+    (FAKE, 1 << 40, FAKE, calib.ERR_SHAPE),     # grid past 2^32 - 1 work-items
+])
+def test_read_rejects(lib, buf, n, hit, want):
+    assert lib.rope_calib_stream_read(buf, n, 0, hit, None) == want
+
+
 @pytest.mark.parametrize("args,want", [
     ((64, 2, 0, 8, 1, None, FAKE, FAKE, FAKE), calib.ERR_NULL),
     ((64, 2, 0, 8, 1, FAKE, FAKE, FAKE, None), calib.ERR_NULL),

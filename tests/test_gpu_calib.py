@@ -31,6 +31,20 @@ def test_stream_touches_exactly_its_pattern(row, span, n_vec):
     assert np.array_equal(got, want.reshape(-1))
 
 
+@pytest.mark.parametrize("n_vec,at", [(1, 0), (1000, 999), (12345, 4321)])
+def test_stream_read_finds_a_planted_vector(n_vec, at):
+    key = 0x7A5C3E1D
+    words = np.random.default_rng(n_vec).integers(0, 2 ** 31, size=4 * n_vec).astype(np.int32)
+    words[4 * at:4 * at + 4] = key
+    buf = torch.from_numpy(words).to(DEV)
+    hit = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    miss = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    calib.stream_read(buf, n_vec, key, hit)
+    calib.stream_read(buf, n_vec, key ^ 1, miss)   # no vector matches: nothing written
+    torch.cuda.synchronize()
+    assert int(hit.item()) == at and int(miss.item()) == -1
+
+
 def bf16_round(x):
     return wl.round_to(np.asarray(x, dtype=np.float64), "bf16")
 
