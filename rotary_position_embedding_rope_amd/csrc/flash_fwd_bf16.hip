@@ -710,9 +710,10 @@ void flash_fwd_bf16_kernel(Params p)
         //
         // Phase 2 (plan B), [j_split, n_iter): the tiles left are seen only
         // by the heavy half's rows.  The light half's two waves stage their
-        // K tiles (K(j+2) in iteration j), loading two tiles ahead; the heavy
-        // half's waves compute and load the V tiles (V(j+1) in iteration j)
-        // straight into LDS.
+        // K tiles (K(j+2) in iteration j), loading two tiles ahead, and load
+        // the V tiles (V(j+1) in iteration j) straight into LDS; the heavy
+        // half's waves only compute, so their dependency chain holds no
+        // memory operation.
         //
         // One barrier per iteration; every wave of the workgroup runs the
         // same number of iterations, plus one at the end.
@@ -806,13 +807,11 @@ void flash_fwd_bf16_kernel(Params p)
         };
         // phase-2 iteration of a heavy wave: the pair loads V(j+1) (4
         // blocks per wave, from block pblk)
-        auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB], int pblk) {
+        auto step_b = [&](int j, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
             __syncthreads();   // K(j+1), V(j) staged
-            dma_next(j, pblk, blk4{});
             v8 pb[NKB][2];
             softmax(j, sc, pb, [&]() { qk((j + 1) & 1, sn); }, i_qk{}, i_zero{});
             pv(pb, vslot(j));
-            wait_dma();   // V(j+1)
         };
 
         // ---- phase 1 ----
@@ -838,11 +837,10 @@ void flash_fwd_bf16_kernel(Params p)
         // ---- phase 2 ----
         {
             if (j_split < n_iter) {
-                // Iteration j stages K(j+2) and loads V(j+1), as in phase 1.
-                // The light pair's 128 threads stage the K tiles, with their
+                // Iteration j stages K(j+2) and loads V(j+1), as in phase 1,
+                // both by the light pair's 128 threads: the K tiles with their
                 // rotation, two register sets deep (K(j+2) staged while
-                // K(j+4) loads); the heavy pair's 128 threads load the V
-                // tiles straight into LDS.
+                // K(j+4) loads), the V tiles straight into LDS.
                 constexpr int KIB = (Plan::SLOTS + 127) / 128;
                 const int ptid = (wave & 1) * 64 + lane;   // thread index inside the pair
                 if (light) {
@@ -854,39 +852,54 @@ void flash_fwd_bf16_kernel(Params p)
                     auto fetch_b = [&](int jj, auto &r0, auto &r1, auto &c, auto &s) {
                         if (T(jj + 2) < tend) fetch_k(T(jj + 2), kpb, r0, r1, c, s);
                     };
+                    const int pblk = 4 * (wave & 1);
+                    // V(jj+1) straight into LDS (4 blocks per wave), then the
+                    // K loads two tiles ahead; before the next barrier wait
+                    // for all but those K loads (vector-memory operations
+                    // complete in order), so V(jj+1) is complete
+                    constexpr int KB_LOADS = KIB * (2 + (ROT ? 4 : 0));
+                    auto wait_v = [&](int jj) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (T(jj + 2) < tend)
+                            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | (KB_LOADS & 15) | ((KB_LOADS >> 4) << 14));
+                        else
+                            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+                        __builtin_amdgcn_sched_barrier(0);
+                    };
                     fetch_b(j, a0, a1, ac, as);
                     fetch_b(j + 1, b0, b1, bc, bs);
                     for (; j < n_iter; j += 2) {
                         __syncthreads();
+                        dma_next(j, pblk, blk4{});
                         stage_k(j & 1, kpb, a0, a1, ac, as);
+                        __builtin_amdgcn_sched_barrier(0);
                         fetch_b(j + 2, a0, a1, ac, as);
+                        wait_v(j + 2);
                         if (j + 1 < n_iter) {
                             __syncthreads();
+                            dma_next(j + 1, pblk, blk4{});
                             stage_k((j + 1) & 1, kpb, b0, b1, bc, bs);
+                            __builtin_amdgcn_sched_barrier(0);
                             fetch_b(j + 3, b0, b1, bc, bs);
+                            wait_v(j + 3);
                         }
                     }
                     j = n_iter;
                 } else {
-                    const int pblk = 4 * (wave & 1);
                     auto run = [&](f32x16_t (&A)[NKB], f32x16_t (&B)[NKB]) {
                         // iterations [j, j_end); tile j's scores in A
                         for (; j + 1 < j_end; j += 2) {
-                            step_b(j, A, B, pblk);
-                            step_b(j + 1, B, A, pblk);
+                            step_b(j, A, B);
+                            step_b(j + 1, B, A);
                         }
                         if (j < j_end) {
-                            step_b(j, A, B, pblk);
+                            step_b(j, A, B);
                             ++j;
                         }
                     };
                     if (j & 1) run(S1, S0);
                     else run(S0, S1);
-                    for (; j < n_iter; ++j) {
-                        __syncthreads();
-                        dma_next(j, pblk, blk4{});
-                        wait_dma();
-                    }
+                    for (; j < n_iter; ++j) __syncthreads();
                 }
             }
         }
