@@ -186,15 +186,19 @@ int rope_apply(void *q, int64_t q_stride_tok, int64_t q_stride_head, int h_q,
  *
  *   workspace   optional device scratch, workspace_bytes long, 16-byte
  *               aligned, contents irrelevant.  With at least
- *               rope_flash_attn_workspace_size() bytes, causal workloads
- *               whose query tiles see very unequal key counts are cut into
- *               equal shares of work across the GPU; a query tile cut
- *               between shares leaves fp32 partial states (output rows,
- *               running max and sum) in the workspace, and a second kernel
- *               enqueued right after on the same stream merges them.  Calls
- *               that share one workspace must not run concurrently.
- *               NULL / too small: one workgroup per query tile (same
- *               result up to floating-point rounding order).
+ *               rope_flash_attn_workspace_size() bytes, a head-dim-128
+ *               16-bit workload with fewer work items (query-row blocks of
+ *               one head group) than the device has CUs has the key tiles
+ *               of each item cut into segments, one workgroup each; a cut
+ *               item's segments leave fp32 partial states (unnormalised
+ *               output rows, reference max and sum) in the workspace, and a
+ *               second kernel enqueued right after on the same stream
+ *               merges them (each state rescaled to the larger max, as
+ *               [RF] section 5 rescales earlier contributions when the
+ *               running max rises).  Calls that share one workspace
+ *               must not run concurrently.  NULL / too small: one
+ *               workgroup per item (same result up to floating-point
+ *               rounding order).  Head dim 64 and fp32 use no workspace.
  */
 int rope_flash_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         int B, int H, int H_kv, int64_t Sq, int64_t Sk, int head_dim,
