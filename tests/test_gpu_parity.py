@@ -322,6 +322,10 @@ EDGE_CASES = [
     (1, 3, 1000, 1000, 64, "bf16", "neox", 32, 7, 7, True),
     (1, 2, 700, 900, 64, "bf16", "gptj", 32, 200, 0, True),
     (1, 2, 333, 333, 64, "bf16", "gptj", 32, 0, 0, False),
+    # no rotation at D = 64 over many key tiles: the K loads in flight
+    # during phase 2 are the two key chunks alone (no table rows)
+    (1, 2, 1000, 1000, 64, "bf16", "neox", 0, 0, 0, True),
+    (1, 3, 600, 1100, 64, "bf16", "gptj", 0, 500, 0, True),
 ]
 
 
