@@ -190,6 +190,8 @@ F16_TOL = 5e-3
 F16_CASES = [
     # (B, H, Hkv, Sq, Sk, D, layout, rot, q_off, causal)
     (1, 8, 8, 512, 512, 64, "neox", 64, 0, True),
+    (1, 4, 4, 2048, 2048, 64, "neox", 64, 0, True),      # 32 key tiles: long second phase
+    (1, 2, 2, 600, 1500, 64, "gptj", 64, 900, True),     # offset mask over 24 key tiles
     (1, 4, 2, 300, 300, 64, "gptj", 32, 0, True),
     (1, 4, 1, 200, 1100, 128, "neox", 128, 900, True),
     (2, 2, 2, 130, 70, 128, "gptj", 64, 0, False),
